@@ -1,0 +1,167 @@
+/*
+ * pararnn.h -- C ABI of libpararnn.so: parallel-in-time evaluation of
+ * nonlinear RNNs by Newton's method with a parallel linear-recurrence scan,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method (ParaRNN page, TL;DR and abstract; DEER summary page, first and
+ * second paragraphs): the recurrence h_t = f(h_{t-1}, x_t) over a whole
+ * sequence is one nonlinear system; Newton's method linearises every cell at
+ * the current iterate and solves the resulting block bi-diagonal linear
+ * system, which is a linear recurrence, with a parallel scan over the
+ * sequence.  The GRU-style cell has a diagonal Jacobian and the LSTM-style
+ * cell a 2x2 block-diagonal one (ParaRNN page, Fig. 2 caption).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are fp32, dense, row-major.  Sequence tensors are [B, L, H]
+ *    with the channel index fastest ("channel-contiguous").  Per-channel
+ *    weights u are [H], shared over batch and time.  Initial states are
+ *    [B, H].  Output row t is the state after consuming input t; the initial
+ *    state is not emitted.
+ *  - Every pointer named as a tensor is a DEVICE pointer (hipMalloc'd or
+ *    torch-allocated, at least 4-byte aligned).  The caller owns all memory,
+ *    including the workspace; the library never allocates or frees and keeps
+ *    no state between calls.  Outputs must not alias inputs.
+ *  - `ws`/`ws_bytes`: a device scratch buffer of at least
+ *    pararnn_workspace_bytes(...) bytes (256-byte aligned).  Concurrent calls
+ *    on different streams need different workspaces.
+ *  - `stream`: a hipStream_t passed as void* (NULL = the default stream).
+ *    Every call only enqueues work on that stream and returns; it never
+ *    synchronises.  Device-side outputs (including `info`) are valid once
+ *    the stream has been synchronised.
+ *  - Return value: PARARNN_OK, or a negative status.  Argument validation is
+ *    done on the host before anything is enqueued (PARARNN_ERR_INVALID).  A
+ *    failed launch returns PARARNN_ERR_HIP.  Non-convergence of Newton is NOT
+ *    an error: the outputs hold the last iterate and info reports it.
+ */
+#ifndef PARARNN_H
+#define PARARNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    PARARNN_OK = 0,
+    PARARNN_ERR_INVALID = -1,     /* bad pointer, size, tolerance, cap or workspace */
+    PARARNN_ERR_HIP = -2,         /* a HIP launch or runtime call failed */
+    PARARNN_ERR_UNSUPPORTED = -3  /* combination not implemented */
+};
+
+enum { PARARNN_CELL_GRU = 0, PARARNN_CELL_LSTM = 1 };
+
+/* Operation codes for pararnn_workspace_bytes. */
+enum {
+    PARARNN_OP_LINSCAN_DIAG = 0,
+    PARARNN_OP_LINSCAN_BLK2 = 1,
+    PARARNN_OP_GRU_FORWARD = 2,
+    PARARNN_OP_LSTM_FORWARD = 3,
+    PARARNN_OP_GRU_ADJOINT = 4,
+    PARARNN_OP_LSTM_ADJOINT = 5
+};
+
+/*
+ * Bytes of workspace that operation `op` needs at (B, L, H) with Newton
+ * iteration cap `max_iter` (ignored by the scans and the adjoints).
+ * Returns 0 for invalid arguments.
+ */
+size_t pararnn_workspace_bytes(int32_t op, int64_t B, int64_t L, int64_t H,
+                               int32_t max_iter);
+
+/*
+ * Diagonal linear recurrence, solved by a chunked parallel scan
+ * (ParaRNN page, Fig. 2 left: the parallel reduction for diagonal systems;
+ * DEER summary page: associative scan; minimal-RNN article: the recurrence a
+ * parallel scan evaluates once gates do not depend on h):
+ *     h[b,t,j] = a[b,t,j] * h[b,t-1,j] + b[b,t,j],   h[b,-1,j] = h0[b,j]
+ * a, b, h: [B, L, H].  h0: [B, H], or NULL for zeros.
+ */
+int rnn_linscan_diag(int64_t B, int64_t L, int64_t H,
+                     const float *a, const float *b, const float *h0,
+                     float *h, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * 2x2 block linear recurrence (ParaRNN page, Fig. 2: the 2x2 block-diagonal
+ * solver used by ParaLSTM):
+ *     h[b,t,j,:] = A[b,t,j] @ h[b,t-1,j,:] + b[b,t,j,:]
+ * A: [B, L, H, 2, 2] row-major blocks (a00, a01, a10, a11).
+ * b, h: [B, L, H, 2].  h0: [B, H, 2] or NULL.
+ */
+int rnn_linscan_blk2(int64_t B, int64_t L, int64_t H,
+                     const float *A, const float *b, const float *h0,
+                     float *h, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * GRU-style cell with diagonal recurrence (ParaGRU, ParaRNN page Fig. 2):
+ *   z = sigmoid(pz + uz*h), r = sigmoid(pr + ur*h),
+ *   c = tanh(pc + uc*(r*h)),  h' = (1 - z)*h + z*c
+ * evaluated over the whole sequence by Newton's method from h = 0
+ * (ParaRNN TL;DR; DEER summary).  pz, pr, pc: [B, L, H] gate
+ * pre-projections (input projections and biases already applied).
+ * uz, ur, uc: [H].  h0: [B, H] or NULL.  h: [B, L, H] output.
+ * tol >= 0: stop once max|delta| over the sequence tile is <= tol (the only
+ * extra hyper-parameter; DEER summary, second paragraph).  max_iter >= 1.
+ * info: device int32[2] {iterations, converged} or NULL.  iterations is the
+ * largest number of updates any tile applied; converged is 1 only if every
+ * tile met the tolerance.
+ * trace: device float[max_iter] or NULL; receives max|delta| of each
+ * iteration (0 for iterations not run).
+ */
+int pararnn_gru_forward(int64_t B, int64_t L, int64_t H,
+                        const float *pz, const float *pr, const float *pc,
+                        const float *uz, const float *ur, const float *uc,
+                        const float *h0, float *h, float tol, int32_t max_iter,
+                        int32_t *info, float *trace,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * LSTM-style cell with diagonal recurrence (ParaLSTM, ParaRNN page Fig. 2):
+ * per channel the state is (c, h) and the Jacobian a 2x2 block.
+ *   i = sigmoid(pi + ui*h'), f = sigmoid(pf + uf*h'), o = sigmoid(po + uo*h'),
+ *   g = tanh(pg + ug*h'),  c = f*c' + i*g,  h = o*tanh(c)
+ * Newton from (c, h) = 0; max|delta| is taken over both components.
+ * pi, pf, po, pg: [B, L, H]; ui, uf, uo, ug: [H]; h0, c0: [B, H] or NULL;
+ * h, c: [B, L, H] outputs.  tol, max_iter, info, trace as for the GRU.
+ */
+int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H,
+                         const float *pi, const float *pf, const float *po,
+                         const float *pg, const float *ui, const float *uf,
+                         const float *uo, const float *ug, const float *h0,
+                         const float *c0, float *h, float *c, float tol,
+                         int32_t max_iter, int32_t *info, float *trace,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Gradients through the converged solve (DEER summary: forward plus
+ * gradients), by a reverse-time linear scan of the adjoint:
+ *   lambda_t = g_t + J_{t+1}^T lambda_{t+1},  dL/dp_t = (df_t/dp_t)^T lambda_t,
+ *   dL/du = sum_{b,t} lambda_t^T df_t/du,  dL/dh0 = J_0^T lambda_0,
+ * for the loss L = sum g_h*h (+ sum g_c*c for the LSTM), with J and df/dp
+ * evaluated at the forward states (h, c).
+ * cell: PARARNN_CELL_GRU (3 gates z, r, c) or PARARNN_CELL_LSTM (4 gates
+ * i, f, o, g).  p, u, grad_p, grad_u: HOST arrays of 3 or 4 DEVICE pointers.
+ * h (and c for the LSTM): the forward outputs [B, L, H].  grad_h: [B, L, H];
+ * grad_c: [B, L, H] or NULL (LSTM only; NULL means zero).  grad_p[k]:
+ * [B, L, H] outputs (overwritten).  grad_u: NULL, or an array whose entries
+ * are [H] outputs or NULL.  grad_h0, grad_c0: [B, H] outputs or NULL.
+ */
+int pararnn_adjoint_backward(int32_t cell, int64_t B, int64_t L, int64_t H,
+                             const float *const *p, const float *const *u,
+                             const float *h0, const float *c0,
+                             const float *h, const float *c,
+                             const float *grad_h, const float *grad_c,
+                             float *const *grad_p, float *const *grad_u,
+                             float *grad_h0, float *grad_c0,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Short text for a status code (static storage). */
+const char *pararnn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PARARNN_H */

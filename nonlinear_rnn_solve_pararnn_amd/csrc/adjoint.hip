@@ -1,0 +1,339 @@
+// adjoint.hip -- gradients through the converged sequence by a reverse-time
+// linear scan (DEER summary: forward plus gradients).
+//
+// For L = sum_t g_t . s_t the adjoint obeys
+//   lambda_t = g_t + J_{t+1}^T lambda_{t+1},
+// whose coefficient J_{t+1} belongs to the next position.  Writing
+// nu_t = J_t^T lambda_t turns it into a recurrence with position-local terms,
+//   nu_t = J_t^T nu_{t+1} + J_t^T g_t,   lambda_t = g_t + nu_{t+1},
+// an affine map per position scanned from t = L-1 down to 0 (nu_L = 0).
+// Then dL/dp_t = (dF_t/dp_t)^T lambda_t, dL/du = sum_{b,t} of dL/dp_t times
+// the derivative of the pre-activation by u, and dL/ds0 = nu_0.
+// The scan core runs in "position" order; position pos is time L-1-pos.
+#include "cells.hpp"
+#include "launch.hpp"
+#include "scan_core.hpp"
+
+namespace prn {
+
+// Sum of per-workgroup partials of dL/du over chunks and batch rows.
+// partial layout: channel lanes [tile][gate][64]; time lanes [tile][gate].
+struct UReduceArgs {
+    const float *partial;
+    float *gu[4];
+    int ngates;
+    int64_t B, H, nq, ncb;
+    bool channel_lanes;
+};
+
+__global__ __launch_bounds__(256) void reduce_u_kernel(UReduceArgs r) {
+    __shared__ float red[256];
+    const int gate = blockIdx.y;
+    const int64_t j = blockIdx.x;
+    float *out = r.gu[gate];
+    if (out == nullptr) return;
+    const int64_t n = r.nq * r.B;
+    float s = 0.0f;
+    for (int64_t k = threadIdx.x; k < n; k += 256) {
+        // k = q * B + b
+        int64_t idx;
+        if (r.channel_lanes)
+            idx = ((k * r.ncb + j / 64) * r.ngates + gate) * 64 + (j % 64);
+        else
+            idx = (k * r.H + j) * r.ngates + gate;
+        s += r.partial[idx];
+    }
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int d = 128; d > 0; d >>= 1) {
+        if ((int)threadIdx.x < d) red[threadIdx.x] += red[threadIdx.x + d];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[j] = red[0];
+}
+
+// Store per-workgroup dL/du partials of `ngates` gates.
+template <int NW, bool CL, int NG>
+__device__ __forceinline__ void store_u_partials(const TilePos &tp, const float (&su)[NG],
+                                                 float *partial) {
+    __shared__ float red[NW * 64];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+        const float s = wg_channel_sum<NW, CL>(su[q], red);
+        if (w == 0) {
+            if (CL)
+                partial[(tp.tile * NG + q) * 64 + lane] = s;
+            else if (lane == 0)
+                partial[tp.tile * NG + q] = s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- GRU
+struct GruAdjOp {
+    static constexpr int S = 1;
+    const float *pz, *pr, *pc, *uz, *ur, *uc, *h0, *h, *gh;
+    float *gpz, *gpr, *gpc, *gh0;
+    float *partial;  // NULL when no dL/du is wanted
+    int64_t L, H;
+
+    struct Elem {
+        float J, g, dz, dr, dc, xz, xr, xc;  // xz.. = pre-activation derivative by u times dF/dp
+    };
+    __device__ bool active() const { return true; }
+    __device__ float init_state(const TilePos &) const { return 0.0f; }
+
+    template <int C>
+    __device__ Aff1 phase1(const TilePos &tp, Elem (&e)[C]) const {
+        const float wz = tp.ok ? uz[tp.j] : 0.0f, wr = tp.ok ? ur[tp.j] : 0.0f,
+                    wc = tp.ok ? uc[tp.j] : 0.0f;
+        Aff1 acc = {1.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int64_t pos = tp.pos0 + i;
+            if (tp.ok && pos < L) {
+                const int64_t t = L - 1 - pos;
+                const int64_t kk = idx3(tp.b, t, tp.j, L, H);
+                const float hp = t == 0 ? (h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f) : h[kk - H];
+                float J, dz, dr, dc, r;
+                gru_j_dp(hp, pz[kk], pr[kk], pc[kk], wz, wr, wc, J, dz, dr, dc, r);
+                e[i] = {J, gh[kk], dz, dr, dc, dz * hp, dr * hp, dc * r * hp};
+            } else {
+                e[i] = {1.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            acc = {acc.a * e[i].J, fmaf(e[i].J, acc.b, e[i].J * e[i].g)};
+        }
+        return acc;
+    }
+
+    template <int C, int NW, bool CL>
+    __device__ void phase2(const TilePos &tp, Elem (&e)[C], float nu) const {
+        float su[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int64_t pos = tp.pos0 + i;
+            if (tp.ok && pos < L) {
+                const int64_t t = L - 1 - pos;
+                const int64_t kk = idx3(tp.b, t, tp.j, L, H);
+                const float lam = e[i].g + nu;
+                gpz[kk] = e[i].dz * lam;
+                gpr[kk] = e[i].dr * lam;
+                gpc[kk] = e[i].dc * lam;
+                su[0] = fmaf(e[i].xz, lam, su[0]);
+                su[1] = fmaf(e[i].xr, lam, su[1]);
+                su[2] = fmaf(e[i].xc, lam, su[2]);
+                nu = e[i].J * lam;
+                if (t == 0 && gh0 != nullptr) gh0[tp.b * H + tp.j] = nu;
+            }
+        }
+        if (partial != nullptr) store_u_partials<NW, CL, 3>(tp, su, partial);
+    }
+};
+
+// ---------------------------------------------------------------- LSTM
+// State order (c, h) as (x, y).  Map nu -> J^T (g + nu).
+struct LstmAdjOp {
+    static constexpr int S = 2;
+    const float *pi, *pf, *po, *pg, *ui, *uf, *uo, *ug, *h0, *c0, *h, *c, *gh, *gc;
+    float *gpi, *gpf, *gpo, *gpg, *gh0, *gc0;
+    float *partial;
+    int64_t L, H;
+
+    struct Elem {
+        float j00, j01, j10, j11, gcv, ghv;
+        float dci, dcf, dcg, dhi, dhf, dho, dhg, hp;
+    };
+    __device__ bool active() const { return true; }
+    __device__ float2s init_state(const TilePos &) const { return {0.0f, 0.0f}; }
+
+    template <int C>
+    __device__ Aff2 phase1(const TilePos &tp, Elem (&e)[C]) const {
+        float wi = 0.0f, wf = 0.0f, wo = 0.0f, wg = 0.0f;
+        if (tp.ok) {
+            wi = ui[tp.j];
+            wf = uf[tp.j];
+            wo = uo[tp.j];
+            wg = ug[tp.j];
+        }
+        Aff2 acc = MonoidT<2>::id();
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int64_t pos = tp.pos0 + i;
+            Aff2 m;
+            if (tp.ok && pos < L) {
+                const int64_t t = L - 1 - pos;
+                const int64_t kk = idx3(tp.b, t, tp.j, L, H);
+                float hp, cp;
+                if (t == 0) {
+                    hp = h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f;
+                    cp = c0 != nullptr ? c0[tp.b * H + tp.j] : 0.0f;
+                } else {
+                    hp = h[kk - H];
+                    cp = c[kk - H];
+                }
+                const LstmAdj r = lstm_adj(cp, hp, pi[kk], pf[kk], po[kk], pg[kk], wi, wf, wo, wg);
+                e[i] = {r.j00, r.j01, r.j10, r.j11, gc != nullptr ? gc[kk] : 0.0f, gh[kk],
+                        r.dci, r.dcf, r.dcg, r.dhi, r.dhf, r.dho, r.dhg, hp};
+                // J^T and J^T g
+                m = {e[i].j00, e[i].j10, e[i].j01, e[i].j11,
+                     fmaf(e[i].j00, e[i].gcv, e[i].j10 * e[i].ghv),
+                     fmaf(e[i].j01, e[i].gcv, e[i].j11 * e[i].ghv)};
+            } else {
+                e[i] = {1.0f, 0.0f, 0.0f, 1.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+                m = MonoidT<2>::id();
+            }
+            acc = MonoidT<2>::then(acc, m);
+        }
+        return acc;
+    }
+
+    template <int C, int NW, bool CL>
+    __device__ void phase2(const TilePos &tp, Elem (&e)[C], float2s nu) const {
+        float su[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int64_t pos = tp.pos0 + i;
+            if (tp.ok && pos < L) {
+                const int64_t t = L - 1 - pos;
+                const int64_t kk = idx3(tp.b, t, tp.j, L, H);
+                const float lc = e[i].gcv + nu.x, lh = e[i].ghv + nu.y;
+                const float di = fmaf(e[i].dci, lc, e[i].dhi * lh);
+                const float df = fmaf(e[i].dcf, lc, e[i].dhf * lh);
+                const float dO = e[i].dho * lh;
+                const float dg = fmaf(e[i].dcg, lc, e[i].dhg * lh);
+                gpi[kk] = di;
+                gpf[kk] = df;
+                gpo[kk] = dO;
+                gpg[kk] = dg;
+                su[0] = fmaf(di, e[i].hp, su[0]);
+                su[1] = fmaf(df, e[i].hp, su[1]);
+                su[2] = fmaf(dO, e[i].hp, su[2]);
+                su[3] = fmaf(dg, e[i].hp, su[3]);
+                nu = {fmaf(e[i].j00, lc, e[i].j10 * lh), fmaf(e[i].j01, lc, e[i].j11 * lh)};
+                if (t == 0) {
+                    if (gh0 != nullptr) gh0[tp.b * H + tp.j] = nu.y;
+                    if (gc0 != nullptr) gc0[tp.b * H + tp.j] = nu.x;
+                }
+            }
+        }
+        if (partial != nullptr) store_u_partials<NW, CL, 4>(tp, su, partial);
+    }
+};
+
+// ---------------------------------------------------------------- launch
+static_assert(kCfgGruAdj.nw_cl == 4 && kCfgGruAdj.c_cl == 8 && kCfgGruAdj.nw_tl == 4 &&
+                  kCfgGruAdj.c_tl == 8,
+              "GRU adjoint instantiation must match its tile configuration");
+static_assert(kCfgLstmAdj.nw_cl == 4 && kCfgLstmAdj.c_cl == 4 && kCfgLstmAdj.nw_tl == 4 &&
+                  kCfgLstmAdj.c_tl == 4,
+              "LSTM adjoint instantiation must match its tile configuration");
+
+size_t gru_adjoint_ws(int64_t B, int64_t L, int64_t H) {
+    const ScanShape sh = scan_shape(kCfgGruAdj, B, L, H);
+    return scan_ws(kCfgGruAdj, Desc<1>::kAggWords, B, L, H, (sh.channel_lanes ? 64 : 1) * 3).total;
+}
+size_t lstm_adjoint_ws(int64_t B, int64_t L, int64_t H) {
+    const ScanShape sh = scan_shape(kCfgLstmAdj, B, L, H);
+    return scan_ws(kCfgLstmAdj, Desc<2>::kAggWords, B, L, H, (sh.channel_lanes ? 64 : 1) * 4).total;
+}
+
+template <class Op, int S, int NW, int C>
+static hipError_t run_adjoint(const TileCfg &cfg, Op op, int ngates, const AdjArgs &a, char *ws,
+                              hipStream_t s) {
+    const ScanShape sh0 = scan_shape(cfg, a.B, a.L, a.H);
+    const ScanWs w = scan_ws(cfg, Desc<S>::kAggWords, a.B, a.L, a.H, (sh0.channel_lanes ? 64 : 1) * ngates);
+    bool want_u = false;
+    for (int q = 0; q < ngates; ++q) want_u = want_u || a.gu[q] != nullptr;
+    op.partial = want_u ? reinterpret_cast<float *>(ws + w.partial) : nullptr;
+    FillRange fr[4] = {
+        {ws + w.counter, 1, 0, 4},
+        {ws + w.err, 1, 0, 4},
+        {ws + w.agg, (uint64_t)w.sh.ndesc * Desc<S>::kAggWords, kSentinel64, 8},
+        {ws + w.inc, (uint64_t)w.sh.ndesc, kSentinel64, 8},
+    };
+    hipError_t e = fill(fr, 4, s);
+    if (e != hipSuccess) return e;
+    ScanGeo g;
+    g.B = a.B;
+    g.L = a.L;
+    g.H = a.H;
+    g.ncb = w.sh.ncb;
+    g.nq = w.sh.nq;
+    g.counter = reinterpret_cast<uint32_t *>(ws + w.counter);
+    g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
+    g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
+    g.agg_next = nullptr;
+    g.inc_next = nullptr;
+    g.err = reinterpret_cast<uint32_t *>(ws + w.err);
+    if (w.sh.channel_lanes)
+        hipLaunchKernelGGL((chunk_scan_kernel<Op, NW, C, true>), dim3((unsigned)w.sh.ntiles), dim3(NW * 64),
+                           0, s, op, g);
+    else
+        hipLaunchKernelGGL((chunk_scan_kernel<Op, NW, C, false>), dim3((unsigned)w.sh.ntiles),
+                           dim3(NW * 64), 0, s, op, g);
+    e = hipGetLastError();
+    if (e != hipSuccess || !want_u) return e;
+    UReduceArgs r;
+    r.partial = op.partial;
+    for (int q = 0; q < 4; ++q) r.gu[q] = q < ngates ? a.gu[q] : nullptr;
+    r.ngates = ngates;
+    r.B = a.B;
+    r.H = a.H;
+    r.nq = w.sh.nq;
+    r.ncb = w.sh.ncb;
+    r.channel_lanes = w.sh.channel_lanes;
+    hipLaunchKernelGGL(reduce_u_kernel, dim3((unsigned)a.H, (unsigned)ngates), dim3(256), 0, s, r);
+    return hipGetLastError();
+}
+
+hipError_t gru_adjoint(const AdjArgs &a, char *ws, hipStream_t s) {
+    GruAdjOp op;
+    op.pz = a.p[0];
+    op.pr = a.p[1];
+    op.pc = a.p[2];
+    op.uz = a.u[0];
+    op.ur = a.u[1];
+    op.uc = a.u[2];
+    op.h0 = a.h0;
+    op.h = a.h;
+    op.gh = a.gh;
+    op.gpz = a.gp[0];
+    op.gpr = a.gp[1];
+    op.gpc = a.gp[2];
+    op.gh0 = a.gh0;
+    op.partial = nullptr;
+    op.L = a.L;
+    op.H = a.H;
+    return run_adjoint<GruAdjOp, 1, 4, 8>(kCfgGruAdj, op, 3, a, ws, s);
+}
+
+hipError_t lstm_adjoint(const AdjArgs &a, char *ws, hipStream_t s) {
+    LstmAdjOp op;
+    op.pi = a.p[0];
+    op.pf = a.p[1];
+    op.po = a.p[2];
+    op.pg = a.p[3];
+    op.ui = a.u[0];
+    op.uf = a.u[1];
+    op.uo = a.u[2];
+    op.ug = a.u[3];
+    op.h0 = a.h0;
+    op.c0 = a.c0;
+    op.h = a.h;
+    op.c = a.c;
+    op.gh = a.gh;
+    op.gc = a.gc;
+    op.gpi = a.gp[0];
+    op.gpf = a.gp[1];
+    op.gpo = a.gp[2];
+    op.gpg = a.gp[3];
+    op.gh0 = a.gh0;
+    op.gc0 = a.gc0;
+    op.partial = nullptr;
+    op.L = a.L;
+    op.H = a.H;
+    return run_adjoint<LstmAdjOp, 2, 4, 4>(kCfgLstmAdj, op, 4, a, ws, s);
+}
+
+}  // namespace prn

@@ -1,0 +1,177 @@
+// api.hip -- the C ABI declared in include/pararnn.h: host-side argument
+// validation, workspace checks and dispatch to the kernel launchers.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/pararnn.h"
+#include "launch.hpp"
+
+using namespace prn;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 40;
+
+bool dims_ok(int64_t B, int64_t L, int64_t H) {
+    if (B <= 0 || L <= 0 || H <= 0) return false;
+    if (B > kMaxDim || L > kMaxDim || H > kMaxDim) return false;
+    // B*L*H elements must be addressable and the grid must fit in 2^31 blocks
+    const double n = (double)B * (double)L * (double)H;
+    return n < 9.0e15;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_HIP; }
+
+bool grid_ok(int64_t ntiles) { return ntiles > 0 && ntiles < ((int64_t)1 << 31); }
+
+size_t gru_step_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
+    return newton_ws(kCfgGruStep, 1, 1, B, L, H, cap).total;
+}
+size_t lstm_step_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
+    return newton_ws(kCfgLstmStep, 2, 3, B, L, H, cap).total;
+}
+
+// Path for the GRU forward: the fused on-chip kernel while the sequence fits
+// one workgroup's registers, else one launch per Newton iteration.
+// PARARNN_GRU_PATH=fused|step overrides the choice (for testing both).
+enum class GruPath { Fused, Step, Invalid };
+GruPath gru_path(int64_t L) {
+    const char *env = getenv("PARARNN_GRU_PATH");
+    const bool fits = fused_c_for(L) != 0;
+    if (env != nullptr && strcmp(env, "step") == 0) return GruPath::Step;
+    if (env != nullptr && strcmp(env, "fused") == 0) return fits ? GruPath::Fused : GruPath::Invalid;
+    return fits ? GruPath::Fused : GruPath::Step;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pararnn_status_string(int status) {
+    switch (status) {
+        case PARARNN_OK: return "ok";
+        case PARARNN_ERR_INVALID: return "invalid argument";
+        case PARARNN_ERR_HIP: return "HIP error";
+        case PARARNN_ERR_UNSUPPORTED: return "unsupported";
+        default: return "unknown status";
+    }
+}
+
+size_t pararnn_workspace_bytes(int32_t op, int64_t B, int64_t L, int64_t H, int32_t max_iter) {
+    if (!dims_ok(B, L, H)) return 0;
+    switch (op) {
+        case PARARNN_OP_LINSCAN_DIAG: return scan_ws(kCfgLinDiag, 1, B, L, H).total;
+        case PARARNN_OP_LINSCAN_BLK2: return scan_ws(kCfgLinBlk2, 3, B, L, H).total;
+        case PARARNN_OP_GRU_FORWARD:
+            if (max_iter < 1) return 0;
+            return gru_step_ws(B, L, H, max_iter);
+        case PARARNN_OP_LSTM_FORWARD:
+            if (max_iter < 1) return 0;
+            return lstm_step_ws(B, L, H, max_iter);
+        case PARARNN_OP_GRU_ADJOINT: return gru_adjoint_ws(B, L, H);
+        case PARARNN_OP_LSTM_ADJOINT: return lstm_adjoint_ws(B, L, H);
+        default: return 0;
+    }
+}
+
+int rnn_linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const float *b,
+                     const float *h0, float *h, void *ws, size_t ws_bytes, void *stream) {
+    if (!dims_ok(B, L, H) || !a || !b || !h || !ws) return PARARNN_ERR_INVALID;
+    if (!grid_ok(scan_shape(kCfgLinDiag, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+    if (ws_bytes < scan_ws(kCfgLinDiag, 1, B, L, H).total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+    return status_of(linscan_diag(B, L, H, a, b, h0, h, static_cast<char *>(ws),
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int rnn_linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const float *b,
+                     const float *h0, float *h, void *ws, size_t ws_bytes, void *stream) {
+    if (!dims_ok(B, L, H) || !A || !b || !h || !ws) return PARARNN_ERR_INVALID;
+    if (!aligned(A, 16) || !aligned(b, 8) || !aligned(h, 8) || (h0 && !aligned(h0, 8)))
+        return PARARNN_ERR_INVALID;
+    if (!grid_ok(scan_shape(kCfgLinBlk2, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+    if (ws_bytes < scan_ws(kCfgLinBlk2, 3, B, L, H).total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+    return status_of(linscan_blk2(B, L, H, A, b, h0, h, static_cast<char *>(ws),
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int pararnn_gru_forward(int64_t B, int64_t L, int64_t H, const float *pz, const float *pr,
+                        const float *pc, const float *uz, const float *ur, const float *uc,
+                        const float *h0, float *h, float tol, int32_t max_iter, int32_t *info,
+                        float *trace, void *ws, size_t ws_bytes, void *stream) {
+    if (!dims_ok(B, L, H) || !pz || !pr || !pc || !uz || !ur || !uc || !h) return PARARNN_ERR_INVALID;
+    if (!(tol >= 0.0f) || max_iter < 1) return PARARNN_ERR_INVALID;  // rejects NaN too
+    GruFwdArgs a{B, L, H, pz, pr, pc, uz, ur, uc, h0, h, tol, max_iter, info, trace};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (gru_path(L)) {
+        case GruPath::Fused:
+            if (!grid_ok(B * ((H + kFusedChannels - 1) / kFusedChannels))) return PARARNN_ERR_INVALID;
+            return status_of(gru_forward_fused(a, s));
+        case GruPath::Step:
+            if (!ws || ws_bytes < gru_step_ws(B, L, H, max_iter) || !aligned(ws, 256))
+                return PARARNN_ERR_INVALID;
+            if (!grid_ok(scan_shape(kCfgGruStep, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+            return status_of(gru_forward_step(a, static_cast<char *>(ws), s));
+        default: return PARARNN_ERR_UNSUPPORTED;
+    }
+}
+
+int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H, const float *pi, const float *pf,
+                         const float *po, const float *pg, const float *ui, const float *uf,
+                         const float *uo, const float *ug, const float *h0, const float *c0,
+                         float *h, float *c, float tol, int32_t max_iter, int32_t *info,
+                         float *trace, void *ws, size_t ws_bytes, void *stream) {
+    if (!dims_ok(B, L, H) || !pi || !pf || !po || !pg || !ui || !uf || !uo || !ug || !h || !c)
+        return PARARNN_ERR_INVALID;
+    if (!(tol >= 0.0f) || max_iter < 1) return PARARNN_ERR_INVALID;
+    if (!ws || ws_bytes < lstm_step_ws(B, L, H, max_iter) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+    if (!grid_ok(scan_shape(kCfgLstmStep, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+    LstmFwdArgs a{B, L, H, pi, pf, po, pg, ui, uf, uo, ug, h0, c0, h, c, tol, max_iter, info, trace};
+    return status_of(lstm_forward_step(a, static_cast<char *>(ws), static_cast<hipStream_t>(stream)));
+}
+
+int pararnn_adjoint_backward(int32_t cell, int64_t B, int64_t L, int64_t H, const float *const *p,
+                             const float *const *u, const float *h0, const float *c0,
+                             const float *h, const float *c, const float *grad_h,
+                             const float *grad_c, float *const *grad_p, float *const *grad_u,
+                             float *grad_h0, float *grad_c0, void *ws, size_t ws_bytes,
+                             void *stream) {
+    if (cell != PARARNN_CELL_GRU && cell != PARARNN_CELL_LSTM) return PARARNN_ERR_INVALID;
+    if (!dims_ok(B, L, H) || !p || !u || !h || !grad_h || !grad_p || !ws) return PARARNN_ERR_INVALID;
+    const int ng = cell == PARARNN_CELL_GRU ? 3 : 4;
+    AdjArgs a;
+    memset(&a, 0, sizeof(a));
+    a.B = B;
+    a.L = L;
+    a.H = H;
+    for (int q = 0; q < ng; ++q) {
+        if (!p[q] || !u[q] || !grad_p[q]) return PARARNN_ERR_INVALID;
+        a.p[q] = p[q];
+        a.u[q] = u[q];
+        a.gp[q] = grad_p[q];
+        a.gu[q] = grad_u ? grad_u[q] : nullptr;
+    }
+    a.h0 = h0;
+    a.h = h;
+    a.gh = grad_h;
+    a.gh0 = grad_h0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cell == PARARNN_CELL_GRU) {
+        if (grad_c || grad_c0) return PARARNN_ERR_INVALID;
+        if (!grid_ok(scan_shape(kCfgGruAdj, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+        if (ws_bytes < gru_adjoint_ws(B, L, H) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+        return status_of(gru_adjoint(a, static_cast<char *>(ws), s));
+    }
+    if (!c) return PARARNN_ERR_INVALID;
+    a.c0 = c0;
+    a.c = c;
+    a.gc = grad_c;
+    a.gc0 = grad_c0;
+    if (!grid_ok(scan_shape(kCfgLstmAdj, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+    if (ws_bytes < lstm_adjoint_ws(B, L, H) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+    return status_of(lstm_adjoint(a, static_cast<char *>(ws), s));
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// cells.hpp -- fp32 device evaluation of the two diagonal-recurrence cells,
+// their Jacobians with respect to the previous state, and their partials
+// with respect to the gate pre-activations.
+//
+// GRU-style cell (ParaGRU; ParaRNN page, Fig. 2 caption: diagonal
+// Jacobian).  Per channel, with h the previous state:
+//   z = s(pz + uz h), r = s(pr + ur h), c = tanh(pc + uc r h),
+//   F = h + z (c - h)
+//   dF/dh = (1 - z) + z(1-z) uz (c - h) + z (1 - c^2) uc (r + h r(1-r) ur)
+//
+// LSTM-style cell (ParaLSTM; Fig. 2 caption: 2x2 block-diagonal Jacobian).
+// State (c, h), previous (c', h'):
+//   i, f, o = s(p + u h'), g = tanh(pg + ug h'), c = f c' + i g, h = o tanh(c)
+//   kappa = dc/dh' = c' f(1-f) uf + g i(1-i) ui + i (1-g^2) ug
+//   J = [[f, kappa], [o(1-tanh^2 c) f, o(1-o) uo tanh c + o(1-tanh^2 c) kappa]]
+#pragma once
+
+#include "common.hpp"
+
+namespace prn {
+
+__device__ __forceinline__ void gru_f_j(float h, float pz, float pr, float pc, float uz,
+                                        float ur, float uc, float &F, float &J) {
+    const float z = sigmoid(fmaf(uz, h, pz));
+    const float r = sigmoid(fmaf(ur, h, pr));
+    const float c = tanh_fast(fmaf(uc, r * h, pc));
+    const float cmh = c - h;
+    F = fmaf(z, cmh, h);
+    const float omz = 1.0f - z;
+    const float omc2 = fmaf(-c, c, 1.0f);
+    const float drh = fmaf(h * (r - r * r), ur, r);  // d(r h)/dh
+    J = fmaf(z * omc2 * uc, drh, fmaf(z * omz * uz, cmh, omz));
+}
+
+// Jacobian and the partials dF/dpz, dF/dpr, dF/dpc at previous state h; also r.
+__device__ __forceinline__ void gru_j_dp(float h, float pz, float pr, float pc, float uz,
+                                         float ur, float uc, float &J, float &dz, float &dr,
+                                         float &dc, float &r_out) {
+    const float z = sigmoid(fmaf(uz, h, pz));
+    const float r = sigmoid(fmaf(ur, h, pr));
+    const float c = tanh_fast(fmaf(uc, r * h, pc));
+    const float cmh = c - h;
+    const float omz = 1.0f - z;
+    const float zomz = z * omz;
+    const float omc2 = fmaf(-c, c, 1.0f);
+    const float rr = r - r * r;
+    const float drh = fmaf(h * rr, ur, r);
+    dz = zomz * cmh;
+    dc = z * omc2;
+    dr = dc * uc * h * rr;
+    J = fmaf(dc * uc, drh, fmaf(zomz * uz, cmh, omz));
+    r_out = r;
+}
+
+struct Lstm2 {
+    float Fc, Fh;
+    float j00, j01, j10, j11;
+};
+
+__device__ __forceinline__ Lstm2 lstm_f_j(float cp, float hp, float pi, float pf, float po,
+                                          float pg, float ui, float uf, float uo, float ug) {
+    const float i = sigmoid(fmaf(ui, hp, pi));
+    const float f = sigmoid(fmaf(uf, hp, pf));
+    const float o = sigmoid(fmaf(uo, hp, po));
+    const float g = tanh_fast(fmaf(ug, hp, pg));
+    const float c = fmaf(f, cp, i * g);
+    const float tc = tanh_fast(c);
+    const float dtc = fmaf(-tc, tc, 1.0f);
+    const float kappa = fmaf(cp * (f - f * f), uf, fmaf(g * (i - i * i), ui, i * fmaf(-g, g, 1.0f) * ug));
+    const float odtc = o * dtc;
+    Lstm2 r;
+    r.Fc = c;
+    r.Fh = o * tc;
+    r.j00 = f;
+    r.j01 = kappa;
+    r.j10 = odtc * f;
+    r.j11 = fmaf((o - o * o) * uo, tc, odtc * kappa);
+    return r;
+}
+
+// LSTM partials for the adjoint: Jacobian plus dc/dp (i, f, g; dc/dpo = 0)
+// and dh/dp (i, f, o, g).
+struct LstmAdj {
+    float j00, j01, j10, j11;
+    float dci, dcf, dcg;
+    float dhi, dhf, dho, dhg;
+};
+
+__device__ __forceinline__ LstmAdj lstm_adj(float cp, float hp, float pi, float pf, float po,
+                                            float pg, float ui, float uf, float uo, float ug) {
+    const float i = sigmoid(fmaf(ui, hp, pi));
+    const float f = sigmoid(fmaf(uf, hp, pf));
+    const float o = sigmoid(fmaf(uo, hp, po));
+    const float g = tanh_fast(fmaf(ug, hp, pg));
+    const float c = fmaf(f, cp, i * g);
+    const float tc = tanh_fast(c);
+    const float dtc = fmaf(-tc, tc, 1.0f);
+    const float odtc = o * dtc;
+    LstmAdj a;
+    a.dci = g * (i - i * i);
+    a.dcf = cp * (f - f * f);
+    a.dcg = i * fmaf(-g, g, 1.0f);
+    const float kappa = fmaf(a.dcf, uf, fmaf(a.dci, ui, a.dcg * ug));
+    a.j00 = f;
+    a.j01 = kappa;
+    a.j10 = odtc * f;
+    a.j11 = fmaf((o - o * o) * uo, tc, odtc * kappa);
+    a.dhi = odtc * a.dci;
+    a.dhf = odtc * a.dcf;
+    a.dho = (o - o * o) * tc;
+    a.dhg = odtc * a.dcg;
+    return a;
+}
+
+}  // namespace prn

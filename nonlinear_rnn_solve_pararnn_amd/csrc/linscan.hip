@@ -1,0 +1,197 @@
+// linscan.hip -- the exported linear-recurrence scans (diagonal and 2x2
+// block) on the chunked look-back scan of scan_core.hpp, plus the fill
+// kernel used to reset workspaces.
+#include "launch.hpp"
+#include "scan_core.hpp"
+
+namespace prn {
+
+// ---------------------------------------------------------------- fill
+struct FillPack {
+    FillRange r[kMaxFill];
+    int n;
+};
+
+__global__ void fill_kernel(FillPack p) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (int k = 0; k < p.n; ++k) {
+        const FillRange &r = p.r[k];
+        for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < r.count; i += stride) {
+            if (r.bytes == 8)
+                static_cast<uint64_t *>(r.ptr)[i] = r.value;
+            else
+                static_cast<uint32_t *>(r.ptr)[i] = (uint32_t)r.value;
+        }
+    }
+}
+
+hipError_t fill(const FillRange *r, int n, hipStream_t s) {
+    FillPack p;
+    p.n = 0;
+    uint64_t most = 0;
+    for (int k = 0; k < n; ++k) {
+        if (r[k].count == 0 || r[k].ptr == nullptr) continue;
+        p.r[p.n++] = r[k];
+        most = r[k].count > most ? r[k].count : most;
+    }
+    if (p.n == 0) return hipSuccess;
+    uint64_t blocks = (most + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- diag scan
+// h_t = a_t h_{t-1} + b_t per (batch, channel).
+struct LinDiagOp {
+    static constexpr int S = 1;
+    const float *a, *b, *h0;
+    float *h;
+    int64_t L, H;
+
+    struct Elem {
+        float a, b;
+    };
+    __device__ bool active() const { return true; }
+    __device__ float init_state(const TilePos &tp) const {
+        return (h0 != nullptr && tp.ok) ? h0[tp.b * H + tp.j] : 0.0f;
+    }
+    template <int C>
+    __device__ Aff1 phase1(const TilePos &tp, Elem (&e)[C]) const {
+        const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
+        if (tp.ok && tp.pos0 + C <= L) {
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                e[i].a = a[base + i * H];
+                e[i].b = b[base + i * H];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                const bool v = tp.ok && tp.pos0 + i < L;
+                e[i].a = v ? a[base + i * H] : 1.0f;
+                e[i].b = v ? b[base + i * H] : 0.0f;
+            }
+        }
+        Aff1 acc = {1.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < C; ++i) acc = {acc.a * e[i].a, fmaf(e[i].a, acc.b, e[i].b)};
+        return acc;
+    }
+    template <int C, int NW, bool CL>
+    __device__ void phase2(const TilePos &tp, Elem (&e)[C], float x) const {
+        const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            x = fmaf(e[i].a, x, e[i].b);
+            if (tp.ok && tp.pos0 + i < L) h[base + i * H] = x;
+        }
+    }
+};
+
+// ---------------------------------------------------------------- 2x2 scan
+// h_t = A_t h_{t-1} + b_t with A_t a 2x2 block per (batch, channel).
+struct LinBlk2Op {
+    static constexpr int S = 2;
+    const float *A, *b, *h0;
+    float *h;
+    int64_t L, H;
+
+    struct Elem {
+        Aff2 m;
+    };
+    __device__ bool active() const { return true; }
+    __device__ float2s init_state(const TilePos &tp) const {
+        if (h0 != nullptr && tp.ok) {
+            const float2 v = reinterpret_cast<const float2 *>(h0)[tp.b * H + tp.j];
+            return {v.x, v.y};
+        }
+        return {0.0f, 0.0f};
+    }
+    template <int C>
+    __device__ Aff2 phase1(const TilePos &tp, Elem (&e)[C]) const {
+        const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
+        const float4 *A4 = reinterpret_cast<const float4 *>(A);
+        const float2 *b2 = reinterpret_cast<const float2 *>(b);
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            if (tp.ok && tp.pos0 + i < L) {
+                const float4 m = A4[base + i * H];
+                const float2 v = b2[base + i * H];
+                e[i].m = {m.x, m.y, m.z, m.w, v.x, v.y};
+            } else {
+                e[i].m = MonoidT<2>::id();
+            }
+        }
+        Aff2 acc = MonoidT<2>::id();
+#pragma unroll
+        for (int i = 0; i < C; ++i) acc = MonoidT<2>::then(acc, e[i].m);
+        return acc;
+    }
+    template <int C, int NW, bool CL>
+    __device__ void phase2(const TilePos &tp, Elem (&e)[C], float2s x) const {
+        const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
+        float2 *h2 = reinterpret_cast<float2 *>(h);
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            x = MonoidT<2>::apply(e[i].m, x);
+            if (tp.ok && tp.pos0 + i < L) h2[base + i * H] = make_float2(x.x, x.y);
+        }
+    }
+};
+
+template <class Op, int NW, int C, bool CL>
+static hipError_t launch_scan(const Op &op, const ScanGeo &g, int64_t ntiles, hipStream_t s) {
+    hipLaunchKernelGGL((chunk_scan_kernel<Op, NW, C, CL>), dim3((unsigned)ntiles), dim3(NW * 64), 0, s,
+                       op, g);
+    return hipGetLastError();
+}
+
+template <class Op, int S>
+static hipError_t run_scan(const TileCfg &cfg, const Op &op, int64_t B, int64_t L, int64_t H,
+                           char *ws, hipStream_t s) {
+    const ScanWs w = scan_ws(cfg, Desc<S>::kAggWords, B, L, H);
+    FillRange fr[4] = {
+        {ws + w.counter, 1, 0, 4},
+        {ws + w.err, 1, 0, 4},
+        {ws + w.agg, (uint64_t)w.sh.ndesc * Desc<S>::kAggWords, kSentinel64, 8},
+        {ws + w.inc, (uint64_t)w.sh.ndesc, kSentinel64, 8},
+    };
+    hipError_t e = fill(fr, 4, s);
+    if (e != hipSuccess) return e;
+    ScanGeo g;
+    g.B = B;
+    g.L = L;
+    g.H = H;
+    g.ncb = w.sh.ncb;
+    g.nq = w.sh.nq;
+    g.counter = reinterpret_cast<uint32_t *>(ws + w.counter);
+    g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
+    g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
+    g.agg_next = nullptr;
+    g.inc_next = nullptr;
+    g.err = reinterpret_cast<uint32_t *>(ws + w.err);
+    return w.sh.channel_lanes ? launch_scan<Op, 4, (S == 1 ? 16 : 8), true>(op, g, w.sh.ntiles, s)
+                              : launch_scan<Op, 4, (S == 1 ? 16 : 8), false>(op, g, w.sh.ntiles, s);
+}
+
+static_assert(kCfgLinDiag.nw_cl == 4 && kCfgLinDiag.c_cl == 16 && kCfgLinDiag.nw_tl == 4 &&
+                  kCfgLinDiag.c_tl == 16,
+              "diag scan instantiation must match its tile configuration");
+static_assert(kCfgLinBlk2.nw_cl == 4 && kCfgLinBlk2.c_cl == 8 && kCfgLinBlk2.nw_tl == 4 &&
+                  kCfgLinBlk2.c_tl == 8,
+              "blk2 scan instantiation must match its tile configuration");
+
+hipError_t linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const float *b,
+                        const float *h0, float *h, char *ws, hipStream_t s) {
+    LinDiagOp op{a, b, h0, h, L, H};
+    return run_scan<LinDiagOp, 1>(kCfgLinDiag, op, B, L, H, ws, s);
+}
+
+hipError_t linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const float *b,
+                        const float *h0, float *h, char *ws, hipStream_t s) {
+    LinBlk2Op op{A, b, h0, h, L, H};
+    return run_scan<LinBlk2Op, 2>(kCfgLinBlk2, op, B, L, H, ws, s);
+}
+
+}  // namespace prn

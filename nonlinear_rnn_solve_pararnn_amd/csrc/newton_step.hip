@@ -1,0 +1,332 @@
+// newton_step.hip -- Newton's method for the whole sequence with one launch
+// per iteration, for sequences too long to keep on chip (ParaRNN page,
+// Fig. 5 caption: the modality that assembles the system and runs the
+// parallel reduction as separate stages, here fused into one HBM pass).
+//
+// Iteration k (from s^0 = 0):
+//   F_t = f(s^{k-1}_{t-1}), J_t = df/ds there, beta_t = F_t - s^{k-1}_t,
+//   delta_t = J_t delta_{t-1} + beta_t (delta_{-1} = 0)  -- the bi-diagonal
+//   solve, done by the chunked look-back scan,
+//   s^k_t = s^{k-1}_t + delta_t,  e_k = max |delta| (NaN counts as +inf).
+// One launch reads the gate inputs and s^{k-1} and writes s^k in place.  A
+// chunk's first cell needs s^{k-1} at the end of the previous chunk, which
+// that chunk's workgroup may already have overwritten in this launch, so the
+// last state of every chunk is also kept in a small boundary array
+// (alternating between two copies).  Every launch first reads e_{k-1}; once
+// an iteration has met the tolerance every later launch exits at once, so
+// the host can enqueue max_iter launches without waiting for the device.
+#include "cells.hpp"
+#include "launch.hpp"
+#include "scan_core.hpp"
+
+namespace prn {
+
+__device__ __forceinline__ bool newton_active(const uint32_t *maxd, int k, float tol) {
+    // maxd holds |delta| bits; iterations not run hold 0.
+    return k == 1 || !(__uint_as_float(maxd[k - 2]) <= tol);
+}
+
+template <int NW, bool CL>
+__device__ __forceinline__ void wg_max_to(uint32_t mx, uint32_t *dst) {
+    mx = wave_max_u32(clamp_nan_to_inf(mx));
+    if ((threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_max(dst, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- GRU
+struct GruStepOp {
+    static constexpr int S = 1;
+    const float *pz, *pr, *pc, *uz, *ur, *uc, *h0;
+    float *h;
+    const float *bnd_prev;
+    float *bnd_next;
+    uint32_t *maxd;
+    float tol;
+    int k;
+    int64_t B, L, H;
+
+    struct Elem {
+        float J, beta, hc;
+    };
+    __device__ bool active() const { return newton_active(maxd, k, tol); }
+    __device__ float init_state(const TilePos &) const { return 0.0f; }
+
+    template <int C>
+    __device__ Aff1 phase1(const TilePos &tp, Elem (&e)[C]) const {
+        const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
+        float hp = 0.0f;  // s^{k-1} at pos0 - 1
+        float wz = 0.0f, wr = 0.0f, wc = 0.0f;
+        if (tp.ok) {
+            wz = uz[tp.j];
+            wr = ur[tp.j];
+            wc = uc[tp.j];
+            if (tp.pos0 == 0)
+                hp = h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f;
+            else if (k == 1)
+                hp = 0.0f;
+            else if (tp.sub == 0)
+                hp = bnd_prev[(tp.q - 1) * B * H + tp.b * H + tp.j];
+            else
+                hp = h[base - H];
+        }
+        Aff1 acc = {1.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            if (tp.ok && tp.pos0 + i < L) {
+                const int64_t kk = base + i * H;
+                const float hc = k == 1 ? 0.0f : h[kk];
+                float F, J;
+                gru_f_j(hp, pz[kk], pr[kk], pc[kk], wz, wr, wc, F, J);
+                e[i] = {J, F - hc, hc};
+                hp = hc;
+            } else {
+                e[i] = {1.0f, 0.0f, 0.0f};
+            }
+            acc = {acc.a * e[i].J, fmaf(e[i].J, acc.b, e[i].beta)};
+        }
+        return acc;
+    }
+
+    template <int C, int NW, bool CL>
+    __device__ void phase2(const TilePos &tp, Elem (&e)[C], float d) const {
+        const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            if (tp.ok && tp.pos0 + i < L) {
+                d = fmaf(e[i].J, d, e[i].beta);
+                const float hn = e[i].hc + d;
+                h[base + i * H] = hn;
+                const uint32_t ad = abs_bits(d);
+                mx = ad > mx ? ad : mx;
+                if (i == C - 1 && tp.sub == tp.nsub - 1)
+                    bnd_next[tp.q * B * H + tp.b * H + tp.j] = hn;
+            }
+        }
+        wg_max_to<NW, CL>(mx, maxd + (k - 1));
+    }
+};
+
+// ---------------------------------------------------------------- LSTM
+// State (c, h); boundary arrays hold float2 (c, h).
+struct LstmStepOp {
+    static constexpr int S = 2;
+    const float *pi, *pf, *po, *pg, *ui, *uf, *uo, *ug, *h0, *c0;
+    float *h, *c;
+    const float2 *bnd_prev;
+    float2 *bnd_next;
+    uint32_t *maxd;
+    float tol;
+    int k;
+    int64_t B, L, H;
+
+    struct Elem {
+        Aff2 m;       // J and beta
+        float cc, hc; // s^{k-1}
+    };
+    __device__ bool active() const { return newton_active(maxd, k, tol); }
+    __device__ float2s init_state(const TilePos &) const { return {0.0f, 0.0f}; }
+
+    template <int C>
+    __device__ Aff2 phase1(const TilePos &tp, Elem (&e)[C]) const {
+        const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
+        float cp = 0.0f, hp = 0.0f;
+        float wi = 0.0f, wf = 0.0f, wo = 0.0f, wg = 0.0f;
+        if (tp.ok) {
+            wi = ui[tp.j];
+            wf = uf[tp.j];
+            wo = uo[tp.j];
+            wg = ug[tp.j];
+            if (tp.pos0 == 0) {
+                hp = h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f;
+                cp = c0 != nullptr ? c0[tp.b * H + tp.j] : 0.0f;
+            } else if (k == 1) {
+            } else if (tp.sub == 0) {
+                const float2 v = bnd_prev[(tp.q - 1) * B * H + tp.b * H + tp.j];
+                cp = v.x;
+                hp = v.y;
+            } else {
+                cp = c[base - H];
+                hp = h[base - H];
+            }
+        }
+        Aff2 acc = MonoidT<2>::id();
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            if (tp.ok && tp.pos0 + i < L) {
+                const int64_t kk = base + i * H;
+                const float cc = k == 1 ? 0.0f : c[kk];
+                const float hc = k == 1 ? 0.0f : h[kk];
+                const Lstm2 r = lstm_f_j(cp, hp, pi[kk], pf[kk], po[kk], pg[kk], wi, wf, wo, wg);
+                e[i].m = {r.j00, r.j01, r.j10, r.j11, r.Fc - cc, r.Fh - hc};
+                e[i].cc = cc;
+                e[i].hc = hc;
+                cp = cc;
+                hp = hc;
+            } else {
+                e[i].m = MonoidT<2>::id();
+                e[i].cc = 0.0f;
+                e[i].hc = 0.0f;
+            }
+            acc = MonoidT<2>::then(acc, e[i].m);
+        }
+        return acc;
+    }
+
+    template <int C, int NW, bool CL>
+    __device__ void phase2(const TilePos &tp, Elem (&e)[C], float2s d) const {
+        const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            if (tp.ok && tp.pos0 + i < L) {
+                d = MonoidT<2>::apply(e[i].m, d);
+                const float cn = e[i].cc + d.x;
+                const float hn = e[i].hc + d.y;
+                c[base + i * H] = cn;
+                h[base + i * H] = hn;
+                const uint32_t a0 = abs_bits(d.x), a1 = abs_bits(d.y);
+                mx = a0 > mx ? a0 : mx;
+                mx = a1 > mx ? a1 : mx;
+                if (i == C - 1 && tp.sub == tp.nsub - 1)
+                    bnd_next[tp.q * B * H + tp.b * H + tp.j] = make_float2(cn, hn);
+            }
+        }
+        wg_max_to<NW, CL>(mx, maxd + (k - 1));
+    }
+};
+
+// ---------------------------------------------------------------- finalize
+// info = {first k with e_k <= tol, 1} or {cap, 0}; trace[k-1] = e_k.
+__global__ void newton_finalize(const uint32_t *maxd, int cap, float tol, int32_t *info,
+                                float *trace) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    int it = cap, conv = 0;
+    for (int k = 0; k < cap; ++k) {
+        const float e = __uint_as_float(maxd[k]);
+        if (trace) trace[k] = e;
+        if (!conv && e <= tol) {
+            it = k + 1;
+            conv = 1;
+        }
+    }
+    if (info) {
+        info[0] = it;
+        info[1] = conv;
+    }
+}
+
+template <class Op, int NW, int C, bool CL>
+static hipError_t launch_iter(const Op &op, const ScanGeo &g, int64_t ntiles, hipStream_t s) {
+    hipLaunchKernelGGL((chunk_scan_kernel<Op, NW, C, CL>), dim3((unsigned)ntiles), dim3(NW * 64), 0, s,
+                       op, g);
+    return hipGetLastError();
+}
+
+// Runs the launch sequence shared by both cells.  `make_op(k, parity)`
+// returns the op of iteration k.
+template <int S, int NW, int C, class MakeOp>
+static hipError_t newton_loop(const TileCfg &cfg, int64_t B, int64_t L, int64_t H, int32_t cap,
+                              float tol, int32_t *info, float *trace, char *ws, hipStream_t s,
+                              MakeOp make_op) {
+    const NewtonWs w = newton_ws(cfg, S, Desc<S>::kAggWords, B, L, H, cap);
+    FillRange fr[7] = {
+        {ws + w.counters, (uint64_t)cap, 0, 4},
+        {ws + w.err, 1, 0, 4},
+        {ws + w.maxd, (uint64_t)cap, 0, 4},
+        {ws + w.agg[0], (uint64_t)w.sh.ndesc * Desc<S>::kAggWords, kSentinel64, 8},
+        {ws + w.inc[0], (uint64_t)w.sh.ndesc, kSentinel64, 8},
+        {ws + w.agg[1], (uint64_t)w.sh.ndesc * Desc<S>::kAggWords, kSentinel64, 8},
+        {ws + w.inc[1], (uint64_t)w.sh.ndesc, kSentinel64, 8},
+    };
+    hipError_t e = fill(fr, 7, s);
+    if (e != hipSuccess) return e;
+    uint32_t *maxd = reinterpret_cast<uint32_t *>(ws + w.maxd);
+    for (int k = 1; k <= cap; ++k) {
+        const int par = k & 1;
+        ScanGeo g;
+        g.B = B;
+        g.L = L;
+        g.H = H;
+        g.ncb = w.sh.ncb;
+        g.nq = w.sh.nq;
+        g.counter = reinterpret_cast<uint32_t *>(ws + w.counters) + (k - 1);
+        g.agg = reinterpret_cast<uint64_t *>(ws + w.agg[par]);
+        g.inc = reinterpret_cast<uint64_t *>(ws + w.inc[par]);
+        g.agg_next = reinterpret_cast<uint64_t *>(ws + w.agg[par ^ 1]);
+        g.inc_next = reinterpret_cast<uint64_t *>(ws + w.inc[par ^ 1]);
+        g.err = reinterpret_cast<uint32_t *>(ws + w.err);
+        auto op = make_op(k, ws + w.bnd[par ^ 1], ws + w.bnd[par], maxd);
+        e = w.sh.channel_lanes ? launch_iter<decltype(op), NW, C, true>(op, g, w.sh.ntiles, s)
+                               : launch_iter<decltype(op), NW, C, false>(op, g, w.sh.ntiles, s);
+        if (e != hipSuccess) return e;
+    }
+    if (info != nullptr || trace != nullptr) {
+        hipLaunchKernelGGL(newton_finalize, dim3(1), dim3(64), 0, s, maxd, cap, tol, info, trace);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+static_assert(kCfgGruStep.nw_cl == 4 && kCfgGruStep.c_cl == 16 && kCfgGruStep.nw_tl == 4 &&
+                  kCfgGruStep.c_tl == 16,
+              "GRU step instantiation must match its tile configuration");
+static_assert(kCfgLstmStep.nw_cl == 4 && kCfgLstmStep.c_cl == 8 && kCfgLstmStep.nw_tl == 4 &&
+                  kCfgLstmStep.c_tl == 8,
+              "LSTM step instantiation must match its tile configuration");
+
+hipError_t gru_forward_step(const GruFwdArgs &a, char *ws, hipStream_t s) {
+    auto make = [&](int k, char *bprev, char *bnext, uint32_t *maxd) {
+        GruStepOp op;
+        op.pz = a.pz;
+        op.pr = a.pr;
+        op.pc = a.pc;
+        op.uz = a.uz;
+        op.ur = a.ur;
+        op.uc = a.uc;
+        op.h0 = a.h0;
+        op.h = a.h;
+        op.bnd_prev = reinterpret_cast<const float *>(bprev);
+        op.bnd_next = reinterpret_cast<float *>(bnext);
+        op.maxd = maxd;
+        op.tol = a.tol;
+        op.k = k;
+        op.B = a.B;
+        op.L = a.L;
+        op.H = a.H;
+        return op;
+    };
+    return newton_loop<1, 4, 16>(kCfgGruStep, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, ws, s,
+                                 make);
+}
+
+hipError_t lstm_forward_step(const LstmFwdArgs &a, char *ws, hipStream_t s) {
+    auto make = [&](int k, char *bprev, char *bnext, uint32_t *maxd) {
+        LstmStepOp op;
+        op.pi = a.pi;
+        op.pf = a.pf;
+        op.po = a.po;
+        op.pg = a.pg;
+        op.ui = a.ui;
+        op.uf = a.uf;
+        op.uo = a.uo;
+        op.ug = a.ug;
+        op.h0 = a.h0;
+        op.c0 = a.c0;
+        op.h = a.h;
+        op.c = a.c;
+        op.bnd_prev = reinterpret_cast<const float2 *>(bprev);
+        op.bnd_next = reinterpret_cast<float2 *>(bnext);
+        op.maxd = maxd;
+        op.tol = a.tol;
+        op.k = k;
+        op.B = a.B;
+        op.L = a.L;
+        op.H = a.H;
+        return op;
+    };
+    return newton_loop<2, 4, 8>(kCfgLstmStep, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, ws, s,
+                                make);
+}
+
+}  // namespace prn

@@ -1,0 +1,117 @@
+// plan.hpp -- host-side geometry of every launch and the layout of the
+// caller's workspace.  The workspace query and the dispatch both use these
+// functions, so the size reported is exactly the size used.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace prn {
+
+// Tile shapes (waves per workgroup, positions per thread) for the two lane
+// mappings of scan_core.hpp.  The kernels are instantiated with exactly these.
+struct TileCfg {
+    int nw_cl, c_cl;  // channel lanes (H >= 32)
+    int nw_tl, c_tl;  // time lanes (H < 32)
+};
+constexpr TileCfg kCfgLinDiag{4, 16, 4, 16};
+constexpr TileCfg kCfgLinBlk2{4, 8, 4, 8};
+constexpr TileCfg kCfgGruStep{4, 16, 4, 16};
+constexpr TileCfg kCfgLstmStep{4, 8, 4, 8};
+constexpr TileCfg kCfgGruAdj{4, 8, 4, 8};
+constexpr TileCfg kCfgLstmAdj{4, 4, 4, 4};
+constexpr int64_t kChannelLanesMinH = 32;
+
+struct ScanShape {
+    bool channel_lanes;
+    int nw, c;
+    int64_t T;       // positions per chunk
+    int64_t ncb;     // channel blocks per batch row
+    int64_t nq;      // chunks along the sequence
+    int64_t ntiles;  // workgroups per launch
+    int64_t ndesc;   // look-back descriptors (nq * B * H)
+};
+
+inline ScanShape scan_shape(const TileCfg &cfg, int64_t B, int64_t L, int64_t H) {
+    ScanShape s;
+    s.channel_lanes = H >= kChannelLanesMinH;
+    s.nw = s.channel_lanes ? cfg.nw_cl : cfg.nw_tl;
+    s.c = s.channel_lanes ? cfg.c_cl : cfg.c_tl;
+    s.T = s.channel_lanes ? (int64_t)s.nw * s.c : (int64_t)s.nw * 64 * s.c;
+    s.ncb = s.channel_lanes ? (H + 63) / 64 : H;
+    s.nq = (L + s.T - 1) / s.T;
+    s.ntiles = s.nq * B * s.ncb;
+    s.ndesc = s.nq * B * H;
+    return s;
+}
+
+// Bump allocator over the workspace (256-byte aligned sections).
+struct Carve {
+    size_t off = 0;
+    size_t take(size_t bytes) {
+        size_t o = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return o;
+    }
+};
+
+// Workspace of one scan launch: ticket counter and one descriptor set.
+struct ScanWs {
+    ScanShape sh;
+    size_t counter, err, agg, inc, partial, total;
+};
+
+inline ScanWs scan_ws(const TileCfg &cfg, int agg_words, int64_t B, int64_t L, int64_t H,
+                      int64_t partial_floats_per_tile = 0) {
+    ScanWs w;
+    w.sh = scan_shape(cfg, B, L, H);
+    Carve c;
+    w.counter = c.take(4);
+    w.err = c.take(4);
+    w.agg = c.take((size_t)w.sh.ndesc * agg_words * 8);
+    w.inc = c.take((size_t)w.sh.ndesc * 8);
+    w.partial = c.take((size_t)w.sh.ntiles * partial_floats_per_tile * 4);
+    w.total = c.off;
+    return w;
+}
+
+// Workspace of the per-iteration Newton path: a ticket counter and a
+// max|delta| slot per iteration, two descriptor sets used alternately, and
+// two sets of chunk-boundary states (state components `S`).
+struct NewtonWs {
+    ScanShape sh;
+    size_t counters, maxd, err, agg[2], inc[2], bnd[2], total;
+};
+
+inline NewtonWs newton_ws(const TileCfg &cfg, int S, int agg_words, int64_t B, int64_t L,
+                          int64_t H, int32_t cap) {
+    NewtonWs w;
+    w.sh = scan_shape(cfg, B, L, H);
+    Carve c;
+    w.counters = c.take((size_t)cap * 4);
+    w.maxd = c.take((size_t)cap * 4);
+    w.err = c.take(4);
+    for (int k = 0; k < 2; ++k) {
+        w.agg[k] = c.take((size_t)w.sh.ndesc * agg_words * 8);
+        w.inc[k] = c.take((size_t)w.sh.ndesc * 8);
+    }
+    for (int k = 0; k < 2; ++k) w.bnd[k] = c.take((size_t)w.sh.ndesc * S * 4);
+    w.total = c.off;
+    return w;
+}
+
+// Fused on-chip GRU Newton: one workgroup owns all L positions of 16
+// channels of one batch row; 8 waves, each lane one (channel, sub-chunk),
+// 32 sub-chunks of C positions.  Usable while L <= 32 * 16.
+constexpr int kFusedChannels = 16;
+constexpr int kFusedSubchunks = 32;
+constexpr int kFusedMaxC = 16;
+constexpr int64_t kFusedMaxL = (int64_t)kFusedSubchunks * kFusedMaxC;
+
+inline int fused_c_for(int64_t L) {
+    for (int c = 1; c <= kFusedMaxC; c *= 2)
+        if (L <= (int64_t)kFusedSubchunks * c) return c;
+    return 0;
+}
+
+}  // namespace prn

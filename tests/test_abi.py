@@ -1,0 +1,71 @@
+"""Host-only checks of the C-ABI library: it loads, exports every function the
+header declares, and its workspace query (pure host arithmetic) behaves.
+No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nonlinear_rnn_solve_pararnn_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "pararnn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)) - {"if", "sizeof"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.LIB_PATH):
+        from nonlinear_rnn_solve_pararnn_amd import build
+        build.build()
+    return api.load_library()
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared()
+    for n in ("rnn_linscan_diag", "rnn_linscan_blk2", "pararnn_gru_forward",
+              "pararnn_lstm_forward", "pararnn_adjoint_backward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert set(api.EXPORTS) <= set(_declared())
+
+
+def test_workspace_query(lib):
+    for op in range(6):
+        assert api.workspace_bytes(op, 2, 100, 70, 8) > 0
+        assert api.workspace_bytes(op, 0, 100, 70, 8) == 0
+        assert api.workspace_bytes(op, 2, -1, 70, 8) == 0
+    assert api.workspace_bytes(api.OP_GRU_FORWARD, 2, 100, 70, 0) == 0
+    assert api.workspace_bytes(99, 2, 100, 70, 8) == 0
+    # grows with the iteration cap (one counter and one max slot per iteration)
+    assert api.workspace_bytes(api.OP_GRU_FORWARD, 16, 4096, 64, 500) > \
+        api.workspace_bytes(api.OP_GRU_FORWARD, 16, 4096, 64, 2)
+
+
+def test_invalid_arguments_rejected_on_host(lib):
+    # validation happens before any HIP call: NULL pointers / bad sizes
+    n = None
+    assert lib.rnn_linscan_diag(0, 10, 10, n, n, n, n, n, 0, n) == -1
+    assert lib.pararnn_gru_forward(1, 10, 10, *([n] * 8), ctypes.c_float(1e-4), 5, n, n, n, 0, n) == -1
+    assert lib.pararnn_adjoint_backward(7, 1, 10, 10, *([n] * 13), 0, n) == -1
+    assert lib.pararnn_status_string(-1) == b"invalid argument"
+
+
+def test_product_path_does_not_use_the_oracle():
+    """The binding and the kernels never import or link the oracle."""
+    pkg = os.path.join(ROOT, "nonlinear_rnn_solve_pararnn_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "liboracle" not in text and "oracle.c" not in text, f
