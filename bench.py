@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of the Newton / parallel-scan RNN path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the path on one batch of synthetic inputs that already
+reside in HBM.  The headline workload (default) is the diagonal GRU Newton
+forward at B=16, L=512, H=4096 (p = 0.5 N(0,1), u ~ U(-0.5,0.5), h0 = 0,
+tol 1e-4, cap 32): the sequence length the ParaRNN page highlights (Fig. 2
+caption) and the fully fused on-chip Newton kernel.  The other workloads
+(the exported diagonal scan, the LSTM Newton forward, and the long-sequence
+GRU forward plus adjoint) are measured in the same run and reported under
+"workloads".
+
+Printed: one JSON line with the metric, the throughput (Newton-solved state
+elements per second = B*L*H / time), the roofline of the dominant kernel
+(timed with HIP events on the stream the kernel runs on) and the fp64 CPU
+oracle timed on this host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Newton-solved state elements/sec (B·L·H) and achieved HBM GB/s vs peak"
+PEAK_HBM_GBS = 8000.0
+
+# Algorithmic bytes per state element (inputs read once, outputs written once).
+ALG_BYTES = {
+    "c1_linscan": 12,            # a, b in; h out
+    "c2_gru_fused": 16,          # pz, pr, pc in; h out
+    "c3_lstm": 24,               # pi, pf, po, pg in; h, c out
+    "c4_gru_long_fwd_adj": 48,   # fwd: 3 p in, h out; adjoint: g, 3 p, h in, 3 dp out
+}
+DOMINANT = {
+    "c1_linscan": "chunk_scan_kernel<LinDiagOp>",
+    "c2_gru_fused": "gru_fused_kernel<16>",
+    "c3_lstm": "chunk_scan_kernel<LstmStepOp> (one launch per Newton iteration)",
+    "c4_gru_long_fwd_adj": "chunk_scan_kernel<GruStepOp> (one launch per Newton iteration)",
+}
+DESCRIBE = {
+    "c1_linscan": "linear diagonal recurrence h_t = a_t h_{t-1} + b_t, B=16 L=4096 H=1024, "
+                  "a~U(0.5,1), b~N(0,1), h0=0",
+    "c2_gru_fused": "diagonal GRU Newton forward, B=16 L=512 H=4096, p=0.5N(0,1), "
+                    "u~U(-0.5,0.5), h0=0, tol 1e-4, cap 32 (fused on-chip kernel)",
+    "c3_lstm": "diagonal LSTM Newton forward (2x2 block Jacobians), B=8 L=2048 H=2048, "
+               "p~N(0,1), u~U(-0.5,0.5), h0=c0=0, tol 1e-4, cap 32",
+    "c4_gru_long_fwd_adj": "diagonal GRU Newton forward + reverse adjoint, B=16 L=1048576 H=1, "
+                           "p~N(0,1), u~U(-0.5,0.5), g~N(0,1), h0=0, tol 1e-4, cap 32",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Workload:
+    """Inputs on the GPU plus a step() that runs the path once."""
+
+    def __init__(self, name, dev):
+        import torch
+
+        from nonlinear_rnn_solve_pararnn_amd import api, synth
+        self.name = name
+        self.w = synth.WORKLOADS[name]
+        self.host = synth.workload_inputs(name)
+        self.dev = dev
+        t = {k: torch.from_numpy(v).to(dev) for k, v in self.host.items()}
+        self.t = t
+        B, L, H = self.w["B"], self.w["L"], self.w["H"]
+        self.B, self.L, self.H = B, L, H
+        self.elements = B * L * H
+        self.info = torch.zeros(2, dtype=torch.int32, device=dev)
+        if name == "c1_linscan":
+            self.out = torch.empty(B, L, H, device=dev)
+            self.ws = torch.empty(api.workspace_bytes(api.OP_LINSCAN_DIAG, B, L, H),
+                                  dtype=torch.uint8, device=dev)
+            self._step = lambda: api.linscan_diag(t["a"], t["b"], None, out=self.out, ws=self.ws)
+        elif name == "c2_gru_fused":
+            self.out = torch.empty(B, L, H, device=dev)
+            cap = self.w["cap"]
+            self.ws = torch.empty(api.workspace_bytes(api.OP_GRU_FORWARD, B, L, H, cap),
+                                  dtype=torch.uint8, device=dev)
+            args = [t[k] for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
+            # no info/trace in the timed call: the step is exactly one kernel launch
+            self._step = lambda: api.gru_forward(*args, None, tol=self.w["tol"], max_iter=cap,
+                                                 out=self.out, ws=self.ws)
+            self._probe = lambda: api.gru_forward(*args, None, tol=self.w["tol"], max_iter=cap,
+                                                  out=self.out, ws=self.ws, info=self.info)
+        elif name == "c3_lstm":
+            self.out = torch.empty(B, L, H, device=dev)
+            self.out_c = torch.empty(B, L, H, device=dev)
+            cap = self.w["cap"]
+            self.ws = torch.empty(api.workspace_bytes(api.OP_LSTM_FORWARD, B, L, H, cap),
+                                  dtype=torch.uint8, device=dev)
+            args = [t[k] for k in ("pi", "pf", "po", "pg", "ui", "uf", "uo", "ug")]
+            self._step = lambda: api.lstm_forward(*args, None, None, tol=self.w["tol"],
+                                                  max_iter=cap, out_h=self.out, out_c=self.out_c,
+                                                  info=self.info, ws=self.ws)
+        elif name == "c4_gru_long_fwd_adj":
+            self.out = torch.empty(B, L, H, device=dev)
+            cap = self.w["cap"]
+            self.ws = torch.empty(max(api.workspace_bytes(api.OP_GRU_FORWARD, B, L, H, cap),
+                                      api.workspace_bytes(api.OP_GRU_ADJOINT, B, L, H)),
+                                  dtype=torch.uint8, device=dev)
+            args = [t[k] for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
+
+            def step():
+                h = api.gru_forward(*args, None, tol=self.w["tol"], max_iter=cap, out=self.out,
+                                    info=self.info, ws=self.ws)
+                return api.adjoint_backward(api.CELL_GRU, args[:3], args[3:], h, t["g"], None,
+                                            ws=self.ws)
+            self._step = step
+        else:
+            raise KeyError(name)
+
+    def step(self):
+        return self._step()
+
+    def iterations(self):
+        import torch
+        if hasattr(self, "_probe"):
+            self._probe()
+        else:
+            self._step()
+        torch.cuda.synchronize()
+        return [int(x) for x in self.info.cpu().tolist()]
+
+
+def time_workload(wl, steps, warmup):
+    """Returns (ms_per_step from the wall clock around K steps, list of per-step
+    event times in ms on the current stream)."""
+    import torch
+    for _ in range(warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        wl.step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [s.elapsed_time(e) for s, e in ev]
+    return wall, per
+
+
+def cpu_baseline(name, host):
+    """The fp64 oracle's sequential rollout (the definition of the result) on
+    this host, timed over the full workload or a bounded sample of it."""
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.num_threads()
+    if name in ("c2_gru_fused", "c4_gru_long_fwd_adj", "c0_gru_tiny"):
+        args = [host[k].astype(np.float64) for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
+        fn = lambda: oracle.gru_rollout(*args)
+        n = args[0].size
+        what = "fp64 sequential GRU rollout (oracle.gru_rollout) over the full workload"
+    elif name == "c3_lstm":
+        args = [host[k].astype(np.float64) for k in ("pi", "pf", "po", "pg", "ui", "uf", "uo", "ug")]
+        fn = lambda: oracle.lstm_rollout(*args)
+        n = args[0].size
+        what = "fp64 sequential LSTM rollout (oracle.lstm_rollout) over the full workload"
+    else:
+        args = [host["a"].astype(np.float64), host["b"].astype(np.float64)]
+        fn = lambda: oracle.linscan_diag(*args)
+        n = args[0].size
+        what = "fp64 serial linear recurrence (oracle.linscan_diag) over the full workload"
+    fn()  # page-in
+    reps, t = 0, 0.0
+    t0 = time.perf_counter()
+    while t < 2.0 and reps < 20:
+        fn()
+        reps += 1
+        t = time.perf_counter() - t0
+    return {"value": n * reps / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "sample": "%s, %d repetition(s), %.2f s" % (what, reps, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2_gru_fused",
+                    choices=["c1_linscan", "c2_gru_fused", "c3_lstm", "c4_gru_long_fwd_adj"])
+    ap.add_argument("--only", action="store_true",
+                    help="measure only the chosen workload (for profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (for scaling HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each GPU would run the same kernels on its own batch/channel shard); "
+              "run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = 1 << 28  # 1 GiB of fp32
+        a = torch.ones(n, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(args.warmup + args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: %d launches of a %d-byte device copy" % (args.warmup + args.steps, 4 * n))
+        return
+
+    names = [args.workload] if args.only else \
+        [args.workload] + [n for n in ALG_BYTES if n != args.workload]
+    results = {}
+    for name in names:
+        log("workload", name)
+        wl = Workload(name, dev)
+        iters = wl.iterations() if name != "c1_linscan" else None
+        wall_ms, per = time_workload(wl, args.steps, args.warmup)
+        ev_ms = sum(per) / len(per)
+        gbs = ALG_BYTES[name] * wl.elements / (ev_ms * 1e-3) / 1e9
+        results[name] = {
+            "elements": wl.elements,
+            "elements_per_s": wl.elements / (wall_ms * 1e-3),
+            "ms_per_step": wall_ms,
+            "event_ms_per_step": ev_ms,
+            "newton_iterations": iters,
+            "alg_bytes_per_element": ALG_BYTES[name],
+            "effective_GBps": gbs,
+            "hbm_frac": gbs / PEAK_HBM_GBS,
+            "dominant_kernel": DOMINANT[name],
+            "describe": DESCRIBE[name],
+        }
+        log(json.dumps({name: results[name]}))
+        del wl
+        torch.cuda.empty_cache()
+
+    head = results[args.workload]
+    from nonlinear_rnn_solve_pararnn_amd import synth
+    w = synth.WORKLOADS[args.workload]
+    alg_bytes = ALG_BYTES[args.workload] * head["elements"]
+    achieved = alg_bytes / (head["event_ms_per_step"] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                "kernel": head["dominant_kernel"],
+                "alg_bytes_per_launch": alg_bytes,
+                "kernel_us": head["event_ms_per_step"] * 1e3}
+    out = {
+        "metric": METRIC,
+        "value": head["elements_per_s"],
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload + ": " + DESCRIBE[args.workload],
+                   "B": w["B"], "L": w["L"], "H": w["H"], "parallelism": "single GPU"},
+        "newton_iterations": head["newton_iterations"],
+        "effective_GBps": head["effective_GBps"],
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(args.workload, synth.workload_inputs(args.workload))
+    else:
+        out["cpu_baseline"] = None
+    if len(results) > 1:
+        out["workloads"] = {k: v for k, v in results.items() if k != args.workload}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -38,11 +38,23 @@ struct FusedGruArgs {
     uint32_t *trace;
 };
 
-template <int C>
-__global__ __launch_bounds__(kNW * 64) void gru_fused_kernel(FusedGruArgs a) {
+// FULL: every lane's channel exists and every position is inside the
+// sequence (L == 32*C, H a multiple of 16), so no masking is needed.
+//
+// Arithmetic per position and iteration (h the previous state, hc the
+// current one): the exponent arguments of the three gates are formed with
+// inputs and weights pre-scaled by -log2(e) (tanh: -2 log2(e)), so each gate
+// is one fma, one exp2, one add and one reciprocal; then
+//   c = 2 s - 1, F = h + z (c - h),
+//   J = (1-z) + z [ (1-z) uz (c-h) + (1-c^2) uc (r + h r(1-r) ur) ],
+//   beta = F - hc.
+// |delta| is tracked with a float max (which ignores NaN); a NaN anywhere in
+// a thread's chain propagates to its last delta, which is checked once.
+template <int C, bool FULL>
+__global__ __launch_bounds__(kNW * 64, 4) void gru_fused_kernel(FusedGruArgs a) {
     __shared__ Aff1 s_wtot[kNW][kCh];
     __shared__ float s_last[kFusedSubchunks][kCh];
-    __shared__ uint32_t s_wmax[kNW];
+    __shared__ float s_wmax[kNW];
 
     // XCD-aware tile order: workgroups are dispatched round-robin over the 8
     // XCDs, so give each XCD a contiguous run of tiles; neighbouring
@@ -57,22 +69,24 @@ __global__ __launch_bounds__(kNW * 64) void gru_fused_kernel(FusedGruArgs a) {
     const int ch = lane % kCh, sl = lane / kCh;
     const int sub = w * kSubW + sl;
     const int64_t j = cb * kCh + ch;
-    const bool ok = j < a.H;
+    const bool ok = FULL || j < a.H;
     const int64_t t0 = (int64_t)sub * C;
     const int64_t L = a.L, H = a.H;
     const int64_t base = (b * L + t0) * H + j;
 
+    constexpr float kE1 = -kLog2e, kE2 = -2.0f * kLog2e;
     float xz[C], xr[C], xc[C], hv[C], Jv[C], bv[C];
     bool val[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) {
-        val[i] = ok && (t0 + i < L);
-        xz[i] = val[i] ? a.pz[base + i * H] : 0.0f;
-        xr[i] = val[i] ? a.pr[base + i * H] : 0.0f;
-        xc[i] = val[i] ? a.pc[base + i * H] : 0.0f;
+        val[i] = FULL || (ok && (t0 + i < L));
+        xz[i] = val[i] ? kE1 * a.pz[base + i * H] : 0.0f;
+        xr[i] = val[i] ? kE1 * a.pr[base + i * H] : 0.0f;
+        xc[i] = val[i] ? kE2 * a.pc[base + i * H] : 0.0f;
         hv[i] = 0.0f;
     }
-    const float wz = ok ? a.uz[j] : 0.0f, wr = ok ? a.ur[j] : 0.0f, wc = ok ? a.uc[j] : 0.0f;
+    const float uz = ok ? a.uz[j] : 0.0f, ur = ok ? a.ur[j] : 0.0f, uc = ok ? a.uc[j] : 0.0f;
+    const float uzs = kE1 * uz, urs = kE1 * ur, ucs = kE2 * uc;
     const float hinit = (ok && a.h0 != nullptr) ? a.h0[b * H + j] : 0.0f;
 
     int iters = 0;
@@ -87,12 +101,28 @@ __global__ __launch_bounds__(kNW * 64) void gru_fused_kernel(FusedGruArgs a) {
         Aff1 acc = {1.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            float F, J;
-            gru_f_j(hp, xz[i], xr[i], xc[i], wz, wr, wc, F, J);
-            Jv[i] = val[i] ? J : 1.0f;
-            bv[i] = val[i] ? F - hv[i] : 0.0f;
+            const float z = fast_rcp(1.0f + fast_exp2(fmaf(uzs, hp, xz[i])));
+            const float r = fast_rcp(1.0f + fast_exp2(fmaf(urs, hp, xr[i])));
+            const float rh = r * hp;
+            const float sc = fast_rcp(1.0f + fast_exp2(fmaf(ucs, rh, xc[i])));
+            const float c = fmaf(2.0f, sc, -1.0f);
+            const float cmh = c - hp;
+            const float F = fmaf(z, cmh, hp);
+            const float omz = 1.0f - z;
+            const float omc2 = fmaf(-c, c, 1.0f);
+            const float rr = fmaf(-r, r, r);
+            const float drh = fmaf(hp * rr, ur, r);
+            const float inner = fmaf(omz * uz, cmh, (omc2 * uc) * drh);
+            float J = fmaf(z, inner, omz);
+            float beta = F - hv[i];
+            if (!FULL) {
+                J = val[i] ? J : 1.0f;
+                beta = val[i] ? beta : 0.0f;
+            }
+            Jv[i] = J;
+            bv[i] = beta;
             hp = hv[i];
-            acc = {acc.a * Jv[i], fmaf(Jv[i], acc.b, bv[i])};
+            acc = {acc.a * J, fmaf(J, acc.b, beta)};
         }
 
         // scan of the sub-chunk maps of each channel
@@ -110,25 +140,27 @@ __global__ __launch_bounds__(kNW * 64) void gru_fused_kernel(FusedGruArgs a) {
         for (int ww = 0; ww < w; ++ww) pre = MonoidT<1>::then(pre, s_wtot[ww][ch]);
         float d = MonoidT<1>::then(pre, exw).b;  // delta entering the sub-chunk (delta_{-1} = 0)
 
-        uint32_t mx = 0;
+        float mx = 0.0f;
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             d = fmaf(Jv[i], d, bv[i]);
             hv[i] += d;
-            const uint32_t ad = val[i] ? abs_bits(d) : 0u;
-            mx = ad > mx ? ad : mx;
+            mx = fmaxf(mx, fabsf(d));
         }
+        if (d != d) mx = __uint_as_float(kInfBits);
+        if (!ok) mx = 0.0f;
         s_last[sub][ch] = hv[C - 1];
-        mx = wave_max_u32(clamp_nan_to_inf(mx));
+        mx = __uint_as_float(wave_max_u32(__float_as_uint(mx)));
         if (lane == 0) s_wmax[w] = mx;
         __syncthreads();
-        uint32_t m = 0;
+        float m = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < kNW; ++ww) m = s_wmax[ww] > m ? s_wmax[ww] : m;
+        for (int ww = 0; ww < kNW; ++ww) m = fmaxf(m, s_wmax[ww]);
         iters = k;
         if (threadIdx.x == 0 && a.trace != nullptr)
-            __hip_atomic_fetch_max(a.trace + (k - 1), m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (__uint_as_float(m) <= a.tol) {
+            __hip_atomic_fetch_max(a.trace + (k - 1), __float_as_uint(m), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        if (m <= a.tol) {
             conv = true;
             break;
         }
@@ -145,7 +177,11 @@ __global__ __launch_bounds__(kNW * 64) void gru_fused_kernel(FusedGruArgs a) {
 
 template <int C>
 static hipError_t launch_fused(const FusedGruArgs &fa, int64_t nblocks, hipStream_t s) {
-    hipLaunchKernelGGL(gru_fused_kernel<C>, dim3((unsigned)nblocks), dim3(kNW * 64), 0, s, fa);
+    const bool full = fa.L == (int64_t)kFusedSubchunks * C && fa.H % kCh == 0;
+    if (full)
+        hipLaunchKernelGGL((gru_fused_kernel<C, true>), dim3((unsigned)nblocks), dim3(kNW * 64), 0, s, fa);
+    else
+        hipLaunchKernelGGL((gru_fused_kernel<C, false>), dim3((unsigned)nblocks), dim3(kNW * 64), 0, s, fa);
     return hipGetLastError();
 }
 
