@@ -20,12 +20,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpararnn.so")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")  # the C ABI header
 ARCH = os.environ.get("PARARNN_ARCH", "gfx950")
 
 CFLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function",
+    "-munsafe-fp-atomics", "-Wall", "-Wno-unused-function", "-I" + INCLUDE,
 ]
 
 

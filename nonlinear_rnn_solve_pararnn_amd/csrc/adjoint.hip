@@ -222,12 +222,6 @@ struct LstmAdjOp {
 };
 
 // ---------------------------------------------------------------- launch
-static_assert(kCfgGruAdj.nw_cl == 4 && kCfgGruAdj.c_cl == 8 && kCfgGruAdj.nw_tl == 4 &&
-                  kCfgGruAdj.c_tl == 8,
-              "GRU adjoint instantiation must match its tile configuration");
-static_assert(kCfgLstmAdj.nw_cl == 4 && kCfgLstmAdj.c_cl == 4 && kCfgLstmAdj.nw_tl == 4 &&
-                  kCfgLstmAdj.c_tl == 4,
-              "LSTM adjoint instantiation must match its tile configuration");
 
 size_t gru_adjoint_ws(int64_t B, int64_t L, int64_t H) {
     const ScanShape sh = scan_shape(kCfgGruAdj, B, L, H);
@@ -238,7 +232,7 @@ size_t lstm_adjoint_ws(int64_t B, int64_t L, int64_t H) {
     return scan_ws(kCfgLstmAdj, Desc<2>::kAggWords, B, L, H, (sh.channel_lanes ? 64 : 1) * 4).total;
 }
 
-template <class Op, int S, int NW, int C>
+template <class Op, int S, int NWC, int CC, int NWT, int CT>
 static hipError_t run_adjoint(const TileCfg &cfg, Op op, int ngates, const AdjArgs &a, char *ws,
                               hipStream_t s) {
     const ScanShape sh0 = scan_shape(cfg, a.B, a.L, a.H);
@@ -267,11 +261,11 @@ static hipError_t run_adjoint(const TileCfg &cfg, Op op, int ngates, const AdjAr
     g.inc_next = nullptr;
     g.err = reinterpret_cast<uint32_t *>(ws + w.err);
     if (w.sh.channel_lanes)
-        hipLaunchKernelGGL((chunk_scan_kernel<Op, NW, C, true>), dim3((unsigned)w.sh.ntiles), dim3(NW * 64),
-                           0, s, op, g);
+        hipLaunchKernelGGL((chunk_scan_kernel<Op, NWC, CC, true>), dim3((unsigned)w.sh.ntiles),
+                           dim3(NWC * 64), 0, s, op, g);
     else
-        hipLaunchKernelGGL((chunk_scan_kernel<Op, NW, C, false>), dim3((unsigned)w.sh.ntiles),
-                           dim3(NW * 64), 0, s, op, g);
+        hipLaunchKernelGGL((chunk_scan_kernel<Op, NWT, CT, false>), dim3((unsigned)w.sh.ntiles),
+                           dim3(NWT * 64), 0, s, op, g);
     e = hipGetLastError();
     if (e != hipSuccess || !want_u) return e;
     UReduceArgs r;
@@ -305,7 +299,8 @@ hipError_t gru_adjoint(const AdjArgs &a, char *ws, hipStream_t s) {
     op.partial = nullptr;
     op.L = a.L;
     op.H = a.H;
-    return run_adjoint<GruAdjOp, 1, 4, 8>(kCfgGruAdj, op, 3, a, ws, s);
+    constexpr TileCfg c = kCfgGruAdj;
+    return run_adjoint<GruAdjOp, 1, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, op, 3, a, ws, s);
 }
 
 hipError_t lstm_adjoint(const AdjArgs &a, char *ws, hipStream_t s) {
@@ -333,7 +328,8 @@ hipError_t lstm_adjoint(const AdjArgs &a, char *ws, hipStream_t s) {
     op.partial = nullptr;
     op.L = a.L;
     op.H = a.H;
-    return run_adjoint<LstmAdjOp, 2, 4, 4>(kCfgLstmAdj, op, 4, a, ws, s);
+    constexpr TileCfg c = kCfgLstmAdj;
+    return run_adjoint<LstmAdjOp, 2, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, op, 4, a, ws, s);
 }
 
 }  // namespace prn

@@ -4,7 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include "../../include/pararnn.h"
+#include "pararnn.h"
 #include "launch.hpp"
 
 using namespace prn;

@@ -170,43 +170,12 @@ template <> struct Desc<2> {
     }
 };
 
-// Walk back over the predecessors of chunk q (same batch row and channel),
-// composing aggregates until a predecessor's inclusive state is found, and
-// return the state entering chunk q.  Every predecessor holds a smaller
-// dynamic ticket, so it is already resident and will publish: the wait ends.
-// As a guard against a broken invariant the wait is still bounded: after
-// kMaxPolls polls of one predecessor it sets *err (if given) and returns
-// NaN, so the failure shows in the output instead of hanging the device.
-// `stride` is the distance in descriptors between consecutive chunks.
+// Bound on the polls of one unpublished descriptor.  Every predecessor of a
+// chunk holds a smaller dynamic ticket, so it is already resident and will
+// publish and the wait ends; the bound is only a guard against a broken
+// invariant: when it is hit the error word is set and NaN is returned, so
+// the failure shows in the output instead of hanging the device.
 constexpr uint32_t kMaxPolls = 1u << 20;
-
-template <int S>
-__device__ typename MonoidT<S>::State lookback(const uint64_t *agg, const uint64_t *inc,
-                                              int64_t q, int64_t stride, int64_t slot,
-                                              uint32_t *err) {
-    using M = MonoidT<S>;
-    using D = Desc<S>;
-    typename M::Map acc = M::id();  // maps the state after chunk p to the state entering q
-    for (int64_t p = q - 1; p >= 0; --p) {
-        const int64_t d = p * stride + slot;
-        for (uint32_t polls = 0;; ++polls) {
-            typename M::State x;
-            if (D::get_inc(inc + d * D::kIncWords, x)) return M::apply(acc, x);
-            typename M::Map m;
-            if (D::get_agg(agg + d * D::kAggWords, m)) {
-                acc = M::then(m, acc);
-                break;
-            }
-            if (polls >= kMaxPolls) {
-                if (err != nullptr)
-                    __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                return M::apply(acc, nan_state<S>());
-            }
-            __builtin_amdgcn_s_sleep(1);
-        }
-    }
-    return M::zero();  // not reached: chunk 0 always publishes its inclusive state
-}
 
 // ---------------------------------------------------------------- indexing
 __device__ __forceinline__ int64_t idx3(int64_t b, int64_t t, int64_t j, int64_t L, int64_t H) {

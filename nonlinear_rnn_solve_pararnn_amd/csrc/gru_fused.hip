@@ -157,9 +157,13 @@ __global__ __launch_bounds__(kNW * 64, 4) void gru_fused_kernel(FusedGruArgs a) 
 #pragma unroll
         for (int ww = 0; ww < kNW; ++ww) m = fmaxf(m, s_wmax[ww]);
         iters = k;
-        if (threadIdx.x == 0 && a.trace != nullptr)
-            __hip_atomic_fetch_max(a.trace + (k - 1), __float_as_uint(m), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0 && a.trace != nullptr) {
+            // shared by every workgroup: skip the atomic unless it would raise the value
+            const uint32_t cur = __hip_atomic_load(a.trace + (k - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (__float_as_uint(m) > cur)
+                __hip_atomic_fetch_max(a.trace + (k - 1), __float_as_uint(m), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
         if (m <= a.tol) {
             conv = true;
             break;
@@ -170,8 +174,11 @@ __global__ __launch_bounds__(kNW * 64, 4) void gru_fused_kernel(FusedGruArgs a) 
     for (int i = 0; i < C; ++i)
         if (val[i]) a.h[base + i * H] = hv[i];
     if (threadIdx.x == 0 && a.info != nullptr) {
-        __hip_atomic_fetch_max(a.info, iters, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!conv) __hip_atomic_fetch_and(a.info + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // shared by every workgroup: skip atomics that would not change the value
+        if (iters > __hip_atomic_load(a.info, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            __hip_atomic_fetch_max(a.info, iters, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!conv && __hip_atomic_load(a.info + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+            __hip_atomic_store(a.info + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

@@ -147,7 +147,7 @@ static hipError_t launch_scan(const Op &op, const ScanGeo &g, int64_t ntiles, hi
     return hipGetLastError();
 }
 
-template <class Op, int S>
+template <class Op, int S, int NWC, int CC, int NWT, int CT>
 static hipError_t run_scan(const TileCfg &cfg, const Op &op, int64_t B, int64_t L, int64_t H,
                            char *ws, hipStream_t s) {
     const ScanWs w = scan_ws(cfg, Desc<S>::kAggWords, B, L, H);
@@ -171,27 +171,23 @@ static hipError_t run_scan(const TileCfg &cfg, const Op &op, int64_t B, int64_t 
     g.agg_next = nullptr;
     g.inc_next = nullptr;
     g.err = reinterpret_cast<uint32_t *>(ws + w.err);
-    return w.sh.channel_lanes ? launch_scan<Op, 4, (S == 1 ? 16 : 8), true>(op, g, w.sh.ntiles, s)
-                              : launch_scan<Op, 4, (S == 1 ? 16 : 8), false>(op, g, w.sh.ntiles, s);
+    return w.sh.channel_lanes ? launch_scan<Op, NWC, CC, true>(op, g, w.sh.ntiles, s)
+                              : launch_scan<Op, NWT, CT, false>(op, g, w.sh.ntiles, s);
 }
 
-static_assert(kCfgLinDiag.nw_cl == 4 && kCfgLinDiag.c_cl == 16 && kCfgLinDiag.nw_tl == 4 &&
-                  kCfgLinDiag.c_tl == 16,
-              "diag scan instantiation must match its tile configuration");
-static_assert(kCfgLinBlk2.nw_cl == 4 && kCfgLinBlk2.c_cl == 8 && kCfgLinBlk2.nw_tl == 4 &&
-                  kCfgLinBlk2.c_tl == 8,
-              "blk2 scan instantiation must match its tile configuration");
 
 hipError_t linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const float *b,
                         const float *h0, float *h, char *ws, hipStream_t s) {
     LinDiagOp op{a, b, h0, h, L, H};
-    return run_scan<LinDiagOp, 1>(kCfgLinDiag, op, B, L, H, ws, s);
+    constexpr TileCfg c = kCfgLinDiag;
+    return run_scan<LinDiagOp, 1, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, op, B, L, H, ws, s);
 }
 
 hipError_t linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const float *b,
                         const float *h0, float *h, char *ws, hipStream_t s) {
     LinBlk2Op op{A, b, h0, h, L, H};
-    return run_scan<LinBlk2Op, 2>(kCfgLinBlk2, op, B, L, H, ws, s);
+    constexpr TileCfg c = kCfgLinBlk2;
+    return run_scan<LinBlk2Op, 2, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, op, B, L, H, ws, s);
 }
 
 }  // namespace prn

@@ -26,11 +26,25 @@ __device__ __forceinline__ bool newton_active(const uint32_t *maxd, int k, float
     return k == 1 || !(__uint_as_float(maxd[k - 2]) <= tol);
 }
 
-template <int NW, bool CL>
+// Fold the per-thread max|delta| (bits of non-negative floats; NaN above
+// +inf) over the workgroup and merge it into *dst.  All workgroups of an
+// iteration share *dst, so same-address atomics would serialise: only the
+// workgroup's first thread updates it, and only when its value exceeds the
+// value it reads there (maxima only grow, so a stale read can only cause an
+// unnecessary update, never a lost one).
+template <int NW>
 __device__ __forceinline__ void wg_max_to(uint32_t mx, uint32_t *dst) {
+    __shared__ uint32_t s_wmax[NW];
     mx = wave_max_u32(clamp_nan_to_inf(mx));
-    if ((threadIdx.x & 63) == 0)
-        __hip_atomic_fetch_max(dst, mx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) s_wmax[w] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t m = 0;
+        for (int k = 0; k < NW; ++k) m = s_wmax[k] > m ? s_wmax[k] : m;
+        const uint32_t cur = __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (m > cur) __hip_atomic_fetch_max(dst, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 // ---------------------------------------------------------------- GRU
@@ -103,7 +117,7 @@ struct GruStepOp {
                     bnd_next[tp.q * B * H + tp.b * H + tp.j] = hn;
             }
         }
-        wg_max_to<NW, CL>(mx, maxd + (k - 1));
+        wg_max_to<NW>(mx, maxd + (k - 1));
     }
 };
 
@@ -192,7 +206,7 @@ struct LstmStepOp {
                     bnd_next[tp.q * B * H + tp.b * H + tp.j] = make_float2(cn, hn);
             }
         }
-        wg_max_to<NW, CL>(mx, maxd + (k - 1));
+        wg_max_to<NW>(mx, maxd + (k - 1));
     }
 };
 
@@ -225,7 +239,7 @@ static hipError_t launch_iter(const Op &op, const ScanGeo &g, int64_t ntiles, hi
 
 // Runs the launch sequence shared by both cells.  `make_op(k, parity)`
 // returns the op of iteration k.
-template <int S, int NW, int C, class MakeOp>
+template <int S, int NWC, int CC, int NWT, int CT, class MakeOp>
 static hipError_t newton_loop(const TileCfg &cfg, int64_t B, int64_t L, int64_t H, int32_t cap,
                               float tol, int32_t *info, float *trace, char *ws, hipStream_t s,
                               MakeOp make_op) {
@@ -257,8 +271,8 @@ static hipError_t newton_loop(const TileCfg &cfg, int64_t B, int64_t L, int64_t 
         g.inc_next = reinterpret_cast<uint64_t *>(ws + w.inc[par ^ 1]);
         g.err = reinterpret_cast<uint32_t *>(ws + w.err);
         auto op = make_op(k, ws + w.bnd[par ^ 1], ws + w.bnd[par], maxd);
-        e = w.sh.channel_lanes ? launch_iter<decltype(op), NW, C, true>(op, g, w.sh.ntiles, s)
-                               : launch_iter<decltype(op), NW, C, false>(op, g, w.sh.ntiles, s);
+        e = w.sh.channel_lanes ? launch_iter<decltype(op), NWC, CC, true>(op, g, w.sh.ntiles, s)
+                               : launch_iter<decltype(op), NWT, CT, false>(op, g, w.sh.ntiles, s);
         if (e != hipSuccess) return e;
     }
     if (info != nullptr || trace != nullptr) {
@@ -268,12 +282,6 @@ static hipError_t newton_loop(const TileCfg &cfg, int64_t B, int64_t L, int64_t 
     return e;
 }
 
-static_assert(kCfgGruStep.nw_cl == 4 && kCfgGruStep.c_cl == 16 && kCfgGruStep.nw_tl == 4 &&
-                  kCfgGruStep.c_tl == 16,
-              "GRU step instantiation must match its tile configuration");
-static_assert(kCfgLstmStep.nw_cl == 4 && kCfgLstmStep.c_cl == 8 && kCfgLstmStep.nw_tl == 4 &&
-                  kCfgLstmStep.c_tl == 8,
-              "LSTM step instantiation must match its tile configuration");
 
 hipError_t gru_forward_step(const GruFwdArgs &a, char *ws, hipStream_t s) {
     auto make = [&](int k, char *bprev, char *bnext, uint32_t *maxd) {
@@ -296,7 +304,8 @@ hipError_t gru_forward_step(const GruFwdArgs &a, char *ws, hipStream_t s) {
         op.H = a.H;
         return op;
     };
-    return newton_loop<1, 4, 16>(kCfgGruStep, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, ws, s,
+    constexpr TileCfg c = kCfgGruStep;
+    return newton_loop<1, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, ws, s,
                                  make);
 }
 
@@ -325,7 +334,8 @@ hipError_t lstm_forward_step(const LstmFwdArgs &a, char *ws, hipStream_t s) {
         op.H = a.H;
         return op;
     };
-    return newton_loop<2, 4, 8>(kCfgLstmStep, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, ws, s,
+    constexpr TileCfg c = kCfgLstmStep;
+    return newton_loop<2, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, ws, s,
                                 make);
 }
 

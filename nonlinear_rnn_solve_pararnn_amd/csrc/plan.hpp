@@ -14,11 +14,11 @@ struct TileCfg {
     int nw_cl, c_cl;  // channel lanes (H >= 32)
     int nw_tl, c_tl;  // time lanes (H < 32)
 };
-constexpr TileCfg kCfgLinDiag{4, 16, 4, 16};
+constexpr TileCfg kCfgLinDiag{8, 16, 4, 16};
 constexpr TileCfg kCfgLinBlk2{4, 8, 4, 8};
-constexpr TileCfg kCfgGruStep{4, 16, 4, 16};
-constexpr TileCfg kCfgLstmStep{4, 8, 4, 8};
-constexpr TileCfg kCfgGruAdj{4, 8, 4, 8};
+constexpr TileCfg kCfgGruStep{4, 16, 16, 4};
+constexpr TileCfg kCfgLstmStep{16, 8, 4, 8};
+constexpr TileCfg kCfgGruAdj{4, 8, 16, 4};
 constexpr TileCfg kCfgLstmAdj{4, 4, 4, 4};
 constexpr int64_t kChannelLanesMinH = 32;
 

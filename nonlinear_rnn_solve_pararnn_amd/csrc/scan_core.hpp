@@ -45,6 +45,180 @@ struct TilePos {
     bool ok;                // channel exists (j < H)
 };
 
+// ---------------------------------------------------------------- look-back
+// Partial result of looking back over a run of consecutive predecessors,
+// ordered nearest first: either the state entering the run's nearest end is
+// known (found: x), or only the composite map of the whole run is (acc maps
+// the state entering the run's farthest chunk to the state leaving its
+// nearest one).  combine(near, far) is associative, so partials can be
+// folded in any grouping as long as near stays before far.
+template <int S> struct LbPart {
+    typename MonoidT<S>::Map acc;
+    typename MonoidT<S>::State x;
+    int found;
+};
+
+template <int S>
+__device__ __forceinline__ LbPart<S> lb_identity() {
+    return {MonoidT<S>::id(), MonoidT<S>::zero(), 0};
+}
+
+template <int S>
+__device__ __forceinline__ LbPart<S> lb_combine(const LbPart<S> &near, const LbPart<S> &far) {
+    using M = MonoidT<S>;
+    if (near.found) return near;
+    LbPart<S> r;
+    if (far.found) {
+        r.found = 1;
+        r.x = M::apply(near.acc, far.x);
+        r.acc = near.acc;
+    } else {
+        r.found = 0;
+        r.acc = M::then(far.acc, near.acc);
+        r.x = far.x;
+    }
+    return r;
+}
+
+__device__ __forceinline__ float shfl_down_f(float v, int d) { return __shfl_down(v, d, 64); }
+__device__ __forceinline__ Aff1 shfl_down_m(Aff1 m, int d) { return {shfl_down_f(m.a, d), shfl_down_f(m.b, d)}; }
+__device__ __forceinline__ Aff2 shfl_down_m(Aff2 m, int d) {
+    return {shfl_down_f(m.a00, d), shfl_down_f(m.a01, d), shfl_down_f(m.a10, d),
+            shfl_down_f(m.a11, d), shfl_down_f(m.b0, d),  shfl_down_f(m.b1, d)};
+}
+__device__ __forceinline__ float shfl_down_s(float x, int d) { return shfl_down_f(x, d); }
+__device__ __forceinline__ float2s shfl_down_s(float2s x, int d) {
+    return {shfl_down_f(x.x, d), shfl_down_f(x.y, d)};
+}
+
+__device__ __forceinline__ float bcast0_f(float v) { return __shfl(v, 0, 64); }
+__device__ __forceinline__ Aff1 bcast0_m(Aff1 m) { return {bcast0_f(m.a), bcast0_f(m.b)}; }
+__device__ __forceinline__ Aff2 bcast0_m(Aff2 m) {
+    return {bcast0_f(m.a00), bcast0_f(m.a01), bcast0_f(m.a10), bcast0_f(m.a11), bcast0_f(m.b0), bcast0_f(m.b1)};
+}
+__device__ __forceinline__ float bcast0_s(float x) { return bcast0_f(x); }
+__device__ __forceinline__ float2s bcast0_s(float2s x) { return {bcast0_f(x.x), bcast0_f(x.y)}; }
+
+// Descriptors polled per batch by one channel lane (channel lanes), and the
+// window of the holder wave (time lanes: lane i polls predecessor i).
+constexpr int kLbBatch = 4;
+
+// Poll up to R consecutive predecessors p0, p0-1, ... (those >= 0) of one
+// channel, issuing all loads before looking at any, and fold them nearest
+// first until an inclusive state is met.  *next receives the first
+// predecessor not folded (-1 once an inclusive state was found); a
+// predecessor that has published nothing yet stops the fold there, to be
+// polled again by the caller.
+template <int S, int R>
+__device__ __forceinline__ LbPart<S> lb_poll_batch(const ScanGeo &g, int64_t p0, int64_t stride,
+                                                   int64_t slot, int64_t *next) {
+    using M = MonoidT<S>;
+    using D = Desc<S>;
+    typename M::State xs[R];
+    typename M::Map ms[R];
+    int st[R];  // 0 nothing published, 1 aggregate, 2 inclusive, 3 before chunk 0
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        st[k] = 3;
+        const int64_t p = p0 - k;
+        if (p >= 0) {
+            const int64_t d = p * stride + slot;
+            const bool hi = D::get_inc(g.inc + d * D::kIncWords, xs[k]);
+            const bool ha = D::get_agg(g.agg + d * D::kAggWords, ms[k]);
+            st[k] = hi ? 2 : (ha ? 1 : 0);
+        }
+    }
+    LbPart<S> part = lb_identity<S>();
+    *next = p0 - R;
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        if (part.found || *next != p0 - R) continue;
+        if (st[k] == 2) {
+            part = lb_combine<S>(part, LbPart<S>{M::id(), xs[k], 1});
+            *next = -1;
+        } else if (st[k] == 1) {
+            part = lb_combine<S>(part, LbPart<S>{ms[k], M::zero(), 0});
+        } else if (st[k] == 0) {
+            *next = p0 - k;  // not published yet: resume here
+        }
+    }
+    return part;
+}
+
+// State entering chunk q > 0 of one channel: batched, decoupled look-back by
+// one lane.  Every predecessor holds a smaller ticket, so it is resident and
+// publishes; the wait is still bounded (kMaxPolls rounds without progress
+// set the error word and give NaN).
+template <int S>
+__device__ typename MonoidT<S>::State lane_lookback(const ScanGeo &g, int64_t q, int64_t stride,
+                                                    int64_t slot) {
+    using M = MonoidT<S>;
+    typename M::Map acc = M::id();  // state entering the farthest folded chunk -> entering q
+    int64_t p = q - 1;
+    uint32_t idle = 0;
+    for (;;) {
+        int64_t next;
+        const LbPart<S> part = lb_poll_batch<S, kLbBatch>(g, p, stride, slot, &next);
+        if (part.found) return M::apply(acc, part.x);
+        acc = M::then(part.acc, acc);
+        if (next == p) {
+            if (++idle >= kMaxPolls) {
+                if (g.err != nullptr)
+                    __hip_atomic_store(g.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                return nan_state<S>();
+            }
+            __builtin_amdgcn_s_sleep(1);
+        } else {
+            idle = 0;
+        }
+        p = next;
+    }
+}
+
+// State entering chunk q > 0 for a time-lane workgroup (one channel): the
+// holder wave polls a window of 64 predecessors at once (lane i polls
+// q-1-i), folds it with shuffles, and repeats with the next window until an
+// inclusive state is met.  Called by every lane of one wave.
+template <int S>
+__device__ typename MonoidT<S>::State wave_lookback(const ScanGeo &g, int64_t q, int64_t stride,
+                                                    int64_t slot) {
+    using M = MonoidT<S>;
+    using D = Desc<S>;
+    const int lane = threadIdx.x & 63;
+    typename M::Map acc_total = M::id();
+    for (int64_t pbase = q - 1;; pbase -= 64) {
+        const int64_t p = pbase - lane;
+        LbPart<S> part = lb_identity<S>();
+        if (p >= 0) {
+            const int64_t d = p * stride + slot;
+            for (uint32_t polls = 0;; ++polls) {
+                typename M::State x;
+                typename M::Map m;
+                if (D::get_inc(g.inc + d * D::kIncWords, x)) { part = {M::id(), x, 1}; break; }
+                if (D::get_agg(g.agg + d * D::kAggWords, m)) { part = {m, M::zero(), 0}; break; }
+                if (polls >= kMaxPolls) {
+                    if (g.err != nullptr)
+                        __hip_atomic_store(g.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    part = {M::id(), nan_state<S>(), 1};
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            LbPart<S> far;
+            far.acc = shfl_down_m(part.acc, d);
+            far.x = shfl_down_s(part.x, d);
+            far.found = __shfl_down(part.found, d, 64);
+            if (lane + d < 64) part = lb_combine<S>(part, far);
+        }
+        // lane 0 holds the fold of the whole window; broadcast it
+        if (__shfl(part.found, 0, 64)) return M::apply(acc_total, bcast0_s(part.x));
+        acc_total = M::then(bcast0_m(part.acc), acc_total);
+    }
+}
+
 template <class Op, int NW, int C, bool CHANNEL_LANES>
 __global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
     constexpr int S = Op::S;
@@ -114,26 +288,40 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
         tot = M::then(pre, incl);
     }
 
-    // the holder of the chunk aggregate publishes it, looks back, and
-    // publishes the state leaving the chunk
+    // The holder of the chunk aggregate publishes it, finds the state
+    // entering the chunk by look-back (per channel lane, or by the holder's
+    // whole wave for time lanes) and publishes the state leaving the chunk.
     const bool holder = CHANNEL_LANES ? (w == NW - 1) : (tid == NT - 1);
-    if (holder) {
-        State xin = op.init_state(tp);
-        if (tp.ok) {
-            const int64_t stride = g.B * g.H;
-            const int64_t slot = tp.b * g.H + tp.j;
-            const int64_t dsc = tp.q * stride + slot;
-            if (tp.q > 0) {
-                D::put_agg(g.agg + dsc * D::kAggWords, tot);
-                xin = lookback<S>(g.agg, g.inc, tp.q, stride, slot, g.err);
-            }
-            D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin));
-            if (g.agg_next) {
-                for (int k = 0; k < D::kAggWords; ++k) g.agg_next[dsc * D::kAggWords + k] = kSentinel64;
-                for (int k = 0; k < D::kIncWords; ++k) g.inc_next[dsc * D::kIncWords + k] = kSentinel64;
-            }
+    const int cslot = CHANNEL_LANES ? lane : 0;
+    const int64_t stride = g.B * g.H, slot = tp.b * g.H + tp.j;
+    const int64_t dsc = tp.q * stride + slot;
+    if (tp.q == 0) {
+        if (holder) {
+            const State xin = op.init_state(tp);
+            if (tp.ok) D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin));
+            s_carry[cslot] = xin;
         }
-        s_carry[CHANNEL_LANES ? lane : 0] = xin;
+    } else if (CHANNEL_LANES) {
+        if (holder) {
+            State xin = M::zero();
+            if (tp.ok) {
+                D::put_agg(g.agg + dsc * D::kAggWords, tot);
+                xin = lane_lookback<S>(g, tp.q, stride, slot);
+                D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin));
+            }
+            s_carry[cslot] = xin;
+        }
+    } else if (w == NW - 1) {
+        if (holder) D::put_agg(g.agg + dsc * D::kAggWords, tot);
+        const State xin = wave_lookback<S>(g, tp.q, stride, slot);
+        if (holder) {
+            D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin));
+            s_carry[0] = xin;
+        }
+    }
+    if (g.agg_next != nullptr && holder && tp.ok) {
+        for (int k = 0; k < D::kAggWords; ++k) g.agg_next[dsc * D::kAggWords + k] = kSentinel64;
+        for (int k = 0; k < D::kIncWords; ++k) g.inc_next[dsc * D::kIncWords + k] = kSentinel64;
     }
     __syncthreads();
     const State x = M::apply(ex, s_carry[CHANNEL_LANES ? lane : 0]);
