@@ -219,8 +219,10 @@ __device__ typename MonoidT<S>::State wave_lookback(const ScanGeo &g, int64_t q,
     }
 }
 
+// One tile (chunk q of a batch row and channel block, identified by its
+// ticket) of a scan.  Every thread of the workgroup calls this.
 template <class Op, int NW, int C, bool CHANNEL_LANES>
-__global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
+__device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_t ticket) {
     constexpr int S = Op::S;
     using M = MonoidT<S>;
     using D = Desc<S>;
@@ -231,15 +233,8 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
 
     __shared__ Map s_part[CHANNEL_LANES ? NT : NW];
     __shared__ State s_carry[CHANNEL_LANES ? 64 : 1];
-    __shared__ uint32_t s_ticket;
-
-    if (!op.active()) return;  // uniform over the grid (e.g. Newton already converged)
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (tid == 0)
-        s_ticket = __hip_atomic_fetch_add(g.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    const int64_t ticket = s_ticket;
     const int64_t per_q = g.B * g.ncb;
 
     TilePos tp;
@@ -326,6 +321,18 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
     __syncthreads();
     const State x = M::apply(ex, s_carry[CHANNEL_LANES ? lane : 0]);
     op.template phase2<C, NW, CHANNEL_LANES>(tp, e, x);
+}
+
+// One launch of a scan: each workgroup draws one ticket (tiles are handed
+// out in ticket order, which is what makes the look-back wait finite).
+template <class Op, int NW, int C, bool CHANNEL_LANES>
+__global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
+    __shared__ uint32_t s_ticket;
+    if (!op.active()) return;  // uniform over the grid (e.g. Newton already converged)
+    if (threadIdx.x == 0)
+        s_ticket = __hip_atomic_fetch_add(g.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    scan_tile<Op, NW, C, CHANNEL_LANES>(op, g, s_ticket);
 }
 
 // Reduce a per-thread value over the workgroup into one value per channel

@@ -149,3 +149,18 @@ def test_invalid_arguments_raise():
         api.gru_forward(*ins, tol=float("nan"))
     with pytest.raises(api.PararnnError):
         api.gru_forward(*ins, max_iter=0)
+
+
+@pytest.mark.parametrize("path,B,L,H", [("step", 16, 20000, 1), ("step", 4, 3000, 256),
+                                        ("fused", 16, 512, 1024)])
+def test_trace_equals_oracle_newton_trace(orc, monkeypatch, path, B, L, H):
+    """max|delta| of each iteration, reduced over thousands of workgroups on
+    every XCD, equals the oracle's global max (a lost update would show)."""
+    monkeypatch.setenv("PARARNN_GRU_PATH", path)
+    d = synth.gru_inputs(B, L, H, seed=64)
+    cap = 3
+    h, info, tr = _run(d, 0.0, cap, with_h0=False, trace=True)
+    _, it, conv, otr = orc.gru_newton(*gru_args(d), tol=0.0, cap=cap)
+    say(path, "gpu trace", list(tr), "oracle", list(otr))
+    for k in range(cap):
+        assert abs(float(tr[k]) - otr[k]) <= 1e-4 * otr[k] + 1e-6, (k, tr, otr)
