@@ -2,11 +2,11 @@
 // kernel, with the sequence kept on chip between iterations (ParaRNN page,
 // Fig. 2 right and Fig. 5: the fully fused solver is the fastest modality).
 //
-// One workgroup (8 waves) owns all L <= 32*C positions of 16 channels of one
-// batch row.  Lane l of wave w handles channel (l mod 16) and sub-chunk
-// 4w + l/16 of C consecutive positions.  The gate inputs are read from HBM
-// once, the iterate, the Jacobians and the residuals live in registers, and
-// h is written once.  Per iteration:
+// A tile is all L <= 32*C positions of 16 channels of one batch row, owned by
+// one workgroup of 8 waves: lane l of wave w handles channel (l mod 16) and
+// sub-chunk 4w + l/16 of C consecutive positions.  The gate inputs are read
+// from HBM once, the iterate, the Jacobians and the residuals live in
+// registers, and h is written once.  Per iteration:
 //   1. every thread evaluates its C cells at the previous iterate (the state
 //      before its first position comes from the neighbouring sub-chunk
 //      through LDS) and composes its sub-chunk's affine map
@@ -16,16 +16,18 @@
 //   3. every thread applies its carry-in delta, updates h += delta and
 //      forms max|delta|; the workgroup maximum decides convergence of this
 //      tile (each tile stops on its own once its max|delta| <= tol).
+
 #include "cells.hpp"
 #include "launch.hpp"
 
 namespace prn {
 
 namespace {
-constexpr int kCh = kFusedChannels;       // channels per workgroup
-constexpr int kSubW = 64 / kCh;           // sub-chunks per wave
+constexpr int kCh = kFusedChannels;           // channels per tile
+constexpr int kSubW = 64 / kCh;               // sub-chunks per wave
 constexpr int kNW = kFusedSubchunks / kSubW;  // waves per workgroup
 static_assert(kCh * kSubW == 64, "a wave is kCh channels x kSubW sub-chunks");
+constexpr float kE1 = -kLog2e, kE2 = -2.0f * kLog2e;
 }  // namespace
 
 struct FusedGruArgs {
@@ -38,59 +40,54 @@ struct FusedGruArgs {
     uint32_t *trace;
 };
 
-// FULL: every lane's channel exists and every position is inside the
-// sequence (L == 32*C, H a multiple of 16), so no masking is needed.
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations but not for its outstanding global memory operations.  The
+// empty asm statements keep the compiler from moving memory accesses across
+// the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left alone
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// XCD-aware tile order: workgroups are dispatched round-robin over the 8 XCDs,
+// so give each XCD a contiguous run of tiles; neighbouring 16-channel tiles
+// share 128-byte lines and then share one L2.
+__device__ __forceinline__ int64_t xcd_tile(int64_t n, int64_t ntiles) {
+    return (ntiles & 7) == 0 ? (n & 7) * (ntiles >> 3) + (n >> 3) : n;
+}
+
+// Newton iterations on one tile held in registers.  x* are the pre-scaled
+// gate inputs (pz, pr by -log2 e; pc by -2 log2 e), hv receives the solution.
 //
-// Arithmetic per position and iteration (h the previous state, hc the
-// current one): the exponent arguments of the three gates are formed with
-// inputs and weights pre-scaled by -log2(e) (tanh: -2 log2(e)), so each gate
-// is one fma, one exp2, one add and one reciprocal; then
+// Arithmetic per position and iteration (h the previous state, hc the current
+// one): each gate is one fma, one exp2, one add and one reciprocal; then
 //   c = 2 s - 1, F = h + z (c - h),
 //   J = (1-z) + z [ (1-z) uz (c-h) + (1-c^2) uc (r + h r(1-r) ur) ],
 //   beta = F - hc.
-// |delta| is tracked with a float max (which ignores NaN); a NaN anywhere in
-// a thread's chain propagates to its last delta, which is checked once.
-template <int C, bool FULL>
-__global__ __launch_bounds__(kNW * 64, 4) void gru_fused_kernel(FusedGruArgs a) {
-    __shared__ Aff1 s_wtot[kNW][kCh];
-    __shared__ float s_last[kFusedSubchunks][kCh];
-    __shared__ float s_wmax[kNW];
-
-    // XCD-aware tile order: workgroups are dispatched round-robin over the 8
-    // XCDs, so give each XCD a contiguous run of tiles; neighbouring
-    // 16-channel tiles share 128-byte lines and then share one L2.
-    const int64_t nblk = gridDim.x;
-    int64_t tile = blockIdx.x;
-    if ((nblk & 7) == 0) tile = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-    const int64_t b = tile / a.ncb;
-    const int64_t cb = tile - b * a.ncb;
-
+// |delta| is tracked with a float max (which ignores NaN); a NaN anywhere in a
+// thread's chain propagates to its last delta, which is checked once.
+template <int C, int NSUB, int CH, bool FULL>
+__device__ __forceinline__ void newton_on_tile(const float (&xz)[C], const float (&xr)[C],
+                                               const float (&xc)[C], float (&hv)[C],
+                                               const bool (&val)[C], bool ok, float uz, float ur,
+                                               float uc, float hinit, const FusedGruArgs &a,
+                                               int &iters, bool &conv) {
+    constexpr int SUBW = 64 / CH;     // sub-chunks per wave
+    constexpr int NW = NSUB / SUBW;   // waves of the workgroup
+    __shared__ Aff1 s_wtot[NW][CH];
+    __shared__ float s_last[NSUB][CH];
+    __shared__ float s_wmax[NW];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int ch = lane % kCh, sl = lane / kCh;
-    const int sub = w * kSubW + sl;
-    const int64_t j = cb * kCh + ch;
-    const bool ok = FULL || j < a.H;
-    const int64_t t0 = (int64_t)sub * C;
-    const int64_t L = a.L, H = a.H;
-    const int64_t base = (b * L + t0) * H + j;
-
-    constexpr float kE1 = -kLog2e, kE2 = -2.0f * kLog2e;
-    float xz[C], xr[C], xc[C], hv[C], Jv[C], bv[C];
-    bool val[C];
-#pragma unroll
-    for (int i = 0; i < C; ++i) {
-        val[i] = FULL || (ok && (t0 + i < L));
-        xz[i] = val[i] ? kE1 * a.pz[base + i * H] : 0.0f;
-        xr[i] = val[i] ? kE1 * a.pr[base + i * H] : 0.0f;
-        xc[i] = val[i] ? kE2 * a.pc[base + i * H] : 0.0f;
-        hv[i] = 0.0f;
-    }
-    const float uz = ok ? a.uz[j] : 0.0f, ur = ok ? a.ur[j] : 0.0f, uc = ok ? a.uc[j] : 0.0f;
+    const int ch = lane % CH, sl = lane / CH;
+    const int sub = w * SUBW + sl;
     const float uzs = kE1 * uz, urs = kE1 * ur, ucs = kE2 * uc;
-    const float hinit = (ok && a.h0 != nullptr) ? a.h0[b * H + j] : 0.0f;
-
-    int iters = 0;
-    bool conv = false;
+    float Jv[C], bv[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) hv[i] = 0.0f;
+    iters = 0;
+    conv = false;
     for (int k = 1; k <= a.cap; ++k) {
         float hp = 0.0f;
         if (sub == 0)
@@ -128,14 +125,14 @@ __global__ __launch_bounds__(kNW * 64, 4) void gru_fused_kernel(FusedGruArgs a) 
         // scan of the sub-chunk maps of each channel
         Aff1 incl = acc;
 #pragma unroll
-        for (int d = 1; d < kSubW; d <<= 1) {
-            const Aff1 o = MonoidT<1>::shfl_up(incl, d * kCh);
+        for (int d = 1; d < SUBW; d <<= 1) {
+            const Aff1 o = MonoidT<1>::shfl_up(incl, d * CH);
             if (sl >= d) incl = MonoidT<1>::then(o, incl);
         }
-        Aff1 exw = MonoidT<1>::shfl_up(incl, kCh);
+        Aff1 exw = MonoidT<1>::shfl_up(incl, CH);
         if (sl == 0) exw = MonoidT<1>::id();
-        if (sl == kSubW - 1) s_wtot[w][ch] = incl;
-        __syncthreads();
+        if (sl == SUBW - 1) s_wtot[w][ch] = incl;
+        lds_barrier();
         Aff1 pre = MonoidT<1>::id();
         for (int ww = 0; ww < w; ++ww) pre = MonoidT<1>::then(pre, s_wtot[ww][ch]);
         float d = MonoidT<1>::then(pre, exw).b;  // delta entering the sub-chunk (delta_{-1} = 0)
@@ -152,10 +149,10 @@ __global__ __launch_bounds__(kNW * 64, 4) void gru_fused_kernel(FusedGruArgs a) 
         s_last[sub][ch] = hv[C - 1];
         mx = __uint_as_float(wave_max_u32(__float_as_uint(mx)));
         if (lane == 0) s_wmax[w] = mx;
-        __syncthreads();
+        lds_barrier();
         float m = 0.0f;
 #pragma unroll
-        for (int ww = 0; ww < kNW; ++ww) m = fmaxf(m, s_wmax[ww]);
+        for (int ww = 0; ww < NW; ++ww) m = fmaxf(m, s_wmax[ww]);
         iters = k;
         if (threadIdx.x == 0 && a.trace != nullptr) {
             // shared by every workgroup: skip the atomic unless it would raise the value
@@ -169,10 +166,11 @@ __global__ __launch_bounds__(kNW * 64, 4) void gru_fused_kernel(FusedGruArgs a) 
             break;
         }
     }
+    // s_last and s_wmax are rewritten by the next tile's first iteration
+    lds_barrier();
+}
 
-#pragma unroll
-    for (int i = 0; i < C; ++i)
-        if (val[i]) a.h[base + i * H] = hv[i];
+__device__ __forceinline__ void report_tile(const FusedGruArgs &a, int iters, bool conv) {
     if (threadIdx.x == 0 && a.info != nullptr) {
         // shared by every workgroup: skip atomics that would not change the value
         if (iters > __hip_atomic_load(a.info, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
@@ -182,13 +180,49 @@ __global__ __launch_bounds__(kNW * 64, 4) void gru_fused_kernel(FusedGruArgs a) 
     }
 }
 
+// One tile per workgroup.  FULL: every lane's channel exists and every
+// position is inside the sequence (L == 32*C, H a multiple of 16).
+template <int C, bool FULL>
+__global__ __launch_bounds__(kNW * 64, 4) void gru_fused_kernel(FusedGruArgs a) {
+    const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t b = tile / a.ncb;
+    const int64_t cb = tile - b * a.ncb;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int ch = lane % kCh, sl = lane / kCh;
+    const int sub = w * kSubW + sl;
+    const int64_t j = cb * kCh + ch;
+    const bool ok = FULL || j < a.H;
+    const int64_t t0 = (int64_t)sub * C;
+    const int64_t L = a.L, H = a.H;
+    const int64_t base = (b * L + t0) * H + j;
+
+    float xz[C], xr[C], xc[C], hv[C];
+    bool val[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        val[i] = FULL || (ok && (t0 + i < L));
+        xz[i] = val[i] ? kE1 * a.pz[base + i * H] : 0.0f;
+        xr[i] = val[i] ? kE1 * a.pr[base + i * H] : 0.0f;
+        xc[i] = val[i] ? kE2 * a.pc[base + i * H] : 0.0f;
+    }
+    const float uz = ok ? a.uz[j] : 0.0f, ur = ok ? a.ur[j] : 0.0f, uc = ok ? a.uc[j] : 0.0f;
+    const float hinit = (ok && a.h0 != nullptr) ? a.h0[b * H + j] : 0.0f;
+    int iters;
+    bool conv;
+    newton_on_tile<C, kFusedSubchunks, kCh, FULL>(xz, xr, xc, hv, val, ok, uz, ur, uc, hinit, a, iters, conv);
+#pragma unroll
+    for (int i = 0; i < C; ++i)
+        if (val[i]) a.h[base + i * H] = hv[i];
+    report_tile(a, iters, conv);
+}
+
 template <int C>
-static hipError_t launch_fused(const FusedGruArgs &fa, int64_t nblocks, hipStream_t s) {
+static hipError_t launch_fused(const FusedGruArgs &fa, int64_t ntiles, hipStream_t s) {
     const bool full = fa.L == (int64_t)kFusedSubchunks * C && fa.H % kCh == 0;
     if (full)
-        hipLaunchKernelGGL((gru_fused_kernel<C, true>), dim3((unsigned)nblocks), dim3(kNW * 64), 0, s, fa);
+        hipLaunchKernelGGL((gru_fused_kernel<C, true>), dim3((unsigned)ntiles), dim3(kNW * 64), 0, s, fa);
     else
-        hipLaunchKernelGGL((gru_fused_kernel<C, false>), dim3((unsigned)nblocks), dim3(kNW * 64), 0, s, fa);
+        hipLaunchKernelGGL((gru_fused_kernel<C, false>), dim3((unsigned)ntiles), dim3(kNW * 64), 0, s, fa);
     return hipGetLastError();
 }
 
@@ -213,19 +247,19 @@ hipError_t gru_forward_fused(const GruFwdArgs &a, hipStream_t s) {
     fa.info = a.info;
     fa.trace = reinterpret_cast<uint32_t *>(a.trace);
     FillRange fr[3] = {
-        {a.info, a.info ? 1ull : 0ull, 0, 4},                                // iterations = 0
-        {a.info ? a.info + 1 : nullptr, a.info ? 1ull : 0ull, 1, 4},         // converged = 1
+        {a.info, a.info ? 1ull : 0ull, 0, 4},                         // iterations = 0
+        {a.info ? a.info + 1 : nullptr, a.info ? 1ull : 0ull, 1, 4},  // converged = 1
         {a.trace, a.trace ? (uint64_t)a.cap : 0ull, 0, 4},
     };
     hipError_t e = fill(fr, 3, s);
     if (e != hipSuccess) return e;
-    const int64_t nblocks = a.B * fa.ncb;
+    const int64_t ntiles = a.B * fa.ncb;
     switch (C) {
-        case 1: return launch_fused<1>(fa, nblocks, s);
-        case 2: return launch_fused<2>(fa, nblocks, s);
-        case 4: return launch_fused<4>(fa, nblocks, s);
-        case 8: return launch_fused<8>(fa, nblocks, s);
-        case 16: return launch_fused<16>(fa, nblocks, s);
+        case 1: return launch_fused<1>(fa, ntiles, s);
+        case 2: return launch_fused<2>(fa, ntiles, s);
+        case 4: return launch_fused<4>(fa, ntiles, s);
+        case 8: return launch_fused<8>(fa, ntiles, s);
+        case 16: return launch_fused<16>(fa, ntiles, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -164,3 +164,17 @@ def test_trace_equals_oracle_newton_trace(orc, monkeypatch, path, B, L, H):
     say(path, "gpu trace", list(tr), "oracle", list(otr))
     for k in range(cap):
         assert abs(float(tr[k]) - otr[k]) <= 1e-4 * otr[k] + 1e-6, (k, tr, otr)
+
+
+def test_fused_full_tiles_with_h0_and_iterates(orc):
+    """Full 16-channel tiles of 512 positions (the unmasked kernel) with a
+    non-zero h0, and their first iterates against the oracle's Newton iterates."""
+    d = synth.gru_inputs(8, 512, 2048, seed=65, h0=True)
+    h, info = _run(d, 1e-5, 32)
+    assert info[1] == 1
+    assert max_abs(h, orc.gru_rollout(*gru_args(d), h0=d["h0"])) <= FWD_ATOL
+    for k in (1, 2, 3):
+        h, info = _run(d, 0.0, k)
+        s, it, conv, _ = orc.gru_newton(*gru_args(d), h0=d["h0"], tol=0.0, cap=k)
+        assert list(info) == [k, 0]
+        assert max_abs(h, s) <= ITER_ATOL, k
