@@ -45,6 +45,19 @@ DOMINANT = {
     "c3_lstm": "chunk_scan_kernel<LstmStepOp> (one launch per Newton iteration)",
     "c4_gru_long_fwd_adj": "chunk_scan_kernel<GruStepOp> (one launch per Newton iteration)",
 }
+# HBM bytes per launch of the dominant kernel from rocprofv3 counter runs
+# (FETCH_SIZE x 2.000 and WRITE_SIZE x 1.000, the factors a plain 1 GiB device
+# copy gives for these counters), valid only for the kernel sources they were
+# taken on: the sha256 prefix of those sources is checked at run time and the
+# figure is dropped (null) once any of them has changed.
+TRAFFIC = {
+    "c1_linscan": {"bytes": 566186598 + 276955136,
+                   "sources": ["common.hpp", "plan.hpp", "scan_core.hpp", "linscan.hip"],
+                   "sha256": "db8084d02383fb7c"},
+    "c2_gru_fused": {"bytes": 419278848 + 152395059,
+                     "sources": ["common.hpp", "cells.hpp", "plan.hpp", "gru_fused.hip"],
+                     "sha256": "acf48117198e404e"},
+}
 DESCRIBE = {
     "c1_linscan": "linear diagonal recurrence h_t = a_t h_{t-1} + b_t, B=16 L=4096 H=1024, "
                   "a~U(0.5,1), b~N(0,1), h0=0",
@@ -55,6 +68,20 @@ DESCRIBE = {
     "c4_gru_long_fwd_adj": "diagonal GRU Newton forward + reverse adjoint, B=16 L=1048576 H=1, "
                            "p~N(0,1), u~U(-0.5,0.5), g~N(0,1), h0=0, tol 1e-4, cap 32",
 }
+
+
+def measured_traffic(name):
+    """Counter-derived HBM bytes per launch, or None if not taken on the
+    current kernel sources."""
+    import hashlib
+    t = TRAFFIC.get(name)
+    if t is None:
+        return None
+    m = hashlib.sha256()
+    for f in t["sources"]:
+        with open(os.path.join(ROOT, "nonlinear_rnn_solve_pararnn_amd", "csrc", f), "rb") as fh:
+            m.update(fh.read())
+    return t["bytes"] if m.hexdigest()[:16] == t["sha256"] else None
 
 
 def log(*a):
@@ -256,7 +283,7 @@ def main():
     alg_bytes = ALG_BYTES[args.workload] * head["elements"]
     achieved = alg_bytes / (head["event_ms_per_step"] * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload),
                 "kernel": head["dominant_kernel"],
                 "alg_bytes_per_launch": alg_bytes,
                 "kernel_us": head["event_ms_per_step"] * 1e3}
