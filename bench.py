@@ -4,18 +4,20 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one call of the path on one batch of synthetic inputs that already
-reside in HBM.  The headline workload (default) is the diagonal GRU Newton
-forward at B=16, L=512, H=4096 (p = 0.5 N(0,1), u ~ U(-0.5,0.5), h0 = 0,
-tol 1e-4, cap 32): the sequence length the ParaRNN page highlights (Fig. 2
-caption) and the fully fused on-chip Newton kernel.  The other workloads
-(the exported diagonal scan, the LSTM Newton forward, and the long-sequence
-GRU forward plus adjoint) are measured in the same run and reported under
-"workloads".
+reside in HBM.  The headline workload (default) is the diagonal linear
+recurrence h_t = a_t h_{t-1} + b_t at B=16, L=4096, H=1024 (a ~ U(0.5,1),
+b ~ N(0,1), h0 = 0): the parallel reduction that every Newton iteration
+runs (ParaRNN page, Fig. 2 left), and for a linear recurrence the whole
+solve.  The other workloads are measured in the same run and reported under
+"workloads", each with its own roofline: the fully fused GRU Newton forward
+at B=16, L=512, H=4096 (ParaRNN page, Fig. 2 right and Fig. 5 at L = 2^9),
+the LSTM Newton forward at B=8, L=2048, H=2048 and the long-sequence GRU
+forward plus adjoint at B=16, L=2^20, H=1 (the DEER summary's V100 shape).
 
-Printed: one JSON line with the metric, the throughput (Newton-solved state
-elements per second = B*L*H / time), the roofline of the dominant kernel
-(timed with HIP events on the stream the kernel runs on) and the fp64 CPU
-oracle timed on this host as a baseline.
+Printed: one JSON line with the metric, the throughput (state elements per
+second = B*L*H / wall time per step), the roofline of the dominant kernel
+(its duration taken with HIP events on the stream it runs on) and the fp64
+CPU oracle timed on this host as a baseline.
 """
 from __future__ import annotations
 
@@ -84,6 +86,17 @@ def measured_traffic(name):
     return t["bytes"] if m.hexdigest()[:16] == t["sha256"] else None
 
 
+def roofline(name, elements, kernel_ms):
+    """HBM roofline of the workload's dominant kernel: algorithmic bytes (inputs
+    read once, outputs written once) over its event-timed duration."""
+    alg = ALG_BYTES[name] * elements
+    achieved = alg / (kernel_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(name),
+            "kernel": DOMINANT[name], "alg_bytes_per_launch": alg,
+            "kernel_us": kernel_ms * 1e3}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -107,14 +120,12 @@ class Workload:
         self.info = torch.zeros(2, dtype=torch.int32, device=dev)
         if name == "c1_linscan":
             self.out = torch.empty(B, L, H, device=dev)
-            self.ws = torch.empty(api.workspace_bytes(api.OP_LINSCAN_DIAG, B, L, H),
-                                  dtype=torch.uint8, device=dev)
+            self.ws = api.new_workspace(api.workspace_bytes(api.OP_LINSCAN_DIAG, B, L, H), dev)
             self._step = lambda: api.linscan_diag(t["a"], t["b"], None, out=self.out, ws=self.ws)
         elif name == "c2_gru_fused":
             self.out = torch.empty(B, L, H, device=dev)
             cap = self.w["cap"]
-            self.ws = torch.empty(api.workspace_bytes(api.OP_GRU_FORWARD, B, L, H, cap),
-                                  dtype=torch.uint8, device=dev)
+            self.ws = api.new_workspace(api.workspace_bytes(api.OP_GRU_FORWARD, B, L, H, cap), dev)
             args = [t[k] for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
             # no info/trace in the timed call: the step is exactly one kernel launch
             self._step = lambda: api.gru_forward(*args, None, tol=self.w["tol"], max_iter=cap,
@@ -125,8 +136,7 @@ class Workload:
             self.out = torch.empty(B, L, H, device=dev)
             self.out_c = torch.empty(B, L, H, device=dev)
             cap = self.w["cap"]
-            self.ws = torch.empty(api.workspace_bytes(api.OP_LSTM_FORWARD, B, L, H, cap),
-                                  dtype=torch.uint8, device=dev)
+            self.ws = api.new_workspace(api.workspace_bytes(api.OP_LSTM_FORWARD, B, L, H, cap), dev)
             args = [t[k] for k in ("pi", "pf", "po", "pg", "ui", "uf", "uo", "ug")]
             self._step = lambda: api.lstm_forward(*args, None, None, tol=self.w["tol"],
                                                   max_iter=cap, out_h=self.out, out_c=self.out_c,
@@ -134,9 +144,8 @@ class Workload:
         elif name == "c4_gru_long_fwd_adj":
             self.out = torch.empty(B, L, H, device=dev)
             cap = self.w["cap"]
-            self.ws = torch.empty(max(api.workspace_bytes(api.OP_GRU_FORWARD, B, L, H, cap),
-                                      api.workspace_bytes(api.OP_GRU_ADJOINT, B, L, H)),
-                                  dtype=torch.uint8, device=dev)
+            self.ws = api.new_workspace(max(api.workspace_bytes(api.OP_GRU_FORWARD, B, L, H, cap),
+                                            api.workspace_bytes(api.OP_GRU_ADJOINT, B, L, H)), dev)
             args = [t[k] for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
 
             def step():
@@ -222,7 +231,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2_gru_fused",
+    ap.add_argument("--workload", default="c1_linscan",
                     choices=["c1_linscan", "c2_gru_fused", "c3_lstm", "c4_gru_long_fwd_adj"])
     ap.add_argument("--only", action="store_true",
                     help="measure only the chosen workload (for profiling runs)")
@@ -260,18 +269,14 @@ def main():
         iters = wl.iterations() if name != "c1_linscan" else None
         wall_ms, per = time_workload(wl, args.steps, args.warmup)
         ev_ms = sum(per) / len(per)
-        gbs = ALG_BYTES[name] * wl.elements / (ev_ms * 1e-3) / 1e9
         results[name] = {
             "elements": wl.elements,
             "elements_per_s": wl.elements / (wall_ms * 1e-3),
             "ms_per_step": wall_ms,
             "event_ms_per_step": ev_ms,
             "newton_iterations": iters,
-            "alg_bytes_per_element": ALG_BYTES[name],
-            "effective_GBps": gbs,
-            "hbm_frac": gbs / PEAK_HBM_GBS,
-            "dominant_kernel": DOMINANT[name],
             "describe": DESCRIBE[name],
+            "roofline": roofline(name, wl.elements, ev_ms),
         }
         log(json.dumps({name: results[name]}))
         del wl
@@ -280,13 +285,6 @@ def main():
     head = results[args.workload]
     from nonlinear_rnn_solve_pararnn_amd import synth
     w = synth.WORKLOADS[args.workload]
-    alg_bytes = ALG_BYTES[args.workload] * head["elements"]
-    achieved = alg_bytes / (head["event_ms_per_step"] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.workload),
-                "kernel": head["dominant_kernel"],
-                "alg_bytes_per_launch": alg_bytes,
-                "kernel_us": head["event_ms_per_step"] * 1e3}
     out = {
         "metric": METRIC,
         "value": head["elements_per_s"],
@@ -303,8 +301,7 @@ def main():
         "config": {"workload": args.workload + ": " + DESCRIBE[args.workload],
                    "B": w["B"], "L": w["L"], "H": w["H"], "parallelism": "single GPU"},
         "newton_iterations": head["newton_iterations"],
-        "effective_GBps": head["effective_GBps"],
-        "roofline": roofline,
+        "roofline": head["roofline"],
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

@@ -21,10 +21,19 @@
  *  - Every pointer named as a tensor is a DEVICE pointer (hipMalloc'd or
  *    torch-allocated, at least 4-byte aligned).  The caller owns all memory,
  *    including the workspace; the library never allocates or frees and keeps
- *    no state between calls.  Outputs must not alias inputs.
+ *    no state of its own between calls (what persists lives in the caller's
+ *    workspace).  Outputs must not alias inputs.
  *  - `ws`/`ws_bytes`: a device scratch buffer of at least
- *    pararnn_workspace_bytes(...) bytes (256-byte aligned).  Concurrent calls
- *    on different streams need different workspaces.
+ *    pararnn_workspace_bytes(...) bytes (256-byte aligned).  It must be
+ *    zero-filled before its first use (hipMemset, torch.zeros); every call
+ *    leaves it ready for the next call of any entry point at any size that
+ *    fits, so it is never cleared again, and the caller must not write to it
+ *    between calls.  Its first 8 bytes count the workgroups of a launch and
+ *    number the launches; the look-back records of the scans carry the
+ *    number of the launch that wrote them, which is why no call has to clear
+ *    them.  Concurrent calls on different streams need different
+ *    workspaces.  A workspace that was not zero-filled gives wrong results
+ *    (the kernels still stay in bounds and finish).
  *  - `stream`: a hipStream_t passed as void* (NULL = the default stream).
  *    Every call only enqueues work on that stream and returns; it never
  *    synchronises.  Device-side outputs (including `info`) are valid once

@@ -99,6 +99,23 @@ def workspace_bytes(op: int, B: int, L: int, H: int, max_iter: int = 1) -> int:
     return int(load_library().pararnn_workspace_bytes(op, B, L, H, max_iter))
 
 
+# One zero-filled workspace per (device, stream), grown on demand.  The
+# library leaves a workspace ready for the next call of any entry point, so it
+# is cleared only when it is first allocated.
+_ws_cache = {}
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace of at least `nbytes` bytes (the library requires
+    a zero-filled workspace on first use; later calls keep it valid)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def release_workspaces():
+    """Drop the cached per-stream workspaces."""
+    _ws_cache.clear()
+
+
 def _workspace(op, B, L, H, device, max_iter=1, ws=None):
     n = workspace_bytes(op, B, L, H, max_iter)
     if n == 0:
@@ -106,8 +123,13 @@ def _workspace(op, B, L, H, device, max_iter=1, ws=None):
     if ws is not None:
         if ws.device != device or ws.numel() * ws.element_size() < n or ws.data_ptr() % 256:
             raise ValueError("workspace too small, misaligned or on the wrong device")
-        return ws, n
-    return torch.empty(n, dtype=torch.uint8, device=device), n
+        return ws, ws.numel() * ws.element_size()
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < n:
+        buf = new_workspace(n, device)
+        _ws_cache[key] = buf
+    return buf, buf.numel()
 
 
 # ---------------------------------------------------------------- scans

@@ -225,48 +225,38 @@ struct LstmAdjOp {
 
 size_t gru_adjoint_ws(int64_t B, int64_t L, int64_t H) {
     const ScanShape sh = scan_shape(kCfgGruAdj, B, L, H);
-    return scan_ws(kCfgGruAdj, Desc<1>::kAggWords, B, L, H, (sh.channel_lanes ? 64 : 1) * 3).total;
+    return scan_ws(kCfgGruAdj, 1, B, L, H, (sh.channel_lanes ? 64 : 1) * 3).total;
 }
 size_t lstm_adjoint_ws(int64_t B, int64_t L, int64_t H) {
     const ScanShape sh = scan_shape(kCfgLstmAdj, B, L, H);
-    return scan_ws(kCfgLstmAdj, Desc<2>::kAggWords, B, L, H, (sh.channel_lanes ? 64 : 1) * 4).total;
+    return scan_ws(kCfgLstmAdj, 2, B, L, H, (sh.channel_lanes ? 64 : 1) * 4).total;
 }
 
 template <class Op, int S, int NWC, int CC, int NWT, int CT>
 static hipError_t run_adjoint(const TileCfg &cfg, Op op, int ngates, const AdjArgs &a, char *ws,
                               hipStream_t s) {
     const ScanShape sh0 = scan_shape(cfg, a.B, a.L, a.H);
-    const ScanWs w = scan_ws(cfg, Desc<S>::kAggWords, a.B, a.L, a.H, (sh0.channel_lanes ? 64 : 1) * ngates);
+    const ScanWs w = scan_ws(cfg, S, a.B, a.L, a.H, (sh0.channel_lanes ? 64 : 1) * ngates);
     bool want_u = false;
     for (int q = 0; q < ngates; ++q) want_u = want_u || a.gu[q] != nullptr;
     op.partial = want_u ? reinterpret_cast<float *>(ws + w.partial) : nullptr;
-    FillRange fr[4] = {
-        {ws + w.counter, 1, 0, 4},
-        {ws + w.err, 1, 0, 4},
-        {ws + w.agg, (uint64_t)w.sh.ndesc * Desc<S>::kAggWords, kSentinel64, 8},
-        {ws + w.inc, (uint64_t)w.sh.ndesc, kSentinel64, 8},
-    };
-    hipError_t e = fill(fr, 4, s);
-    if (e != hipSuccess) return e;
     ScanGeo g;
     g.B = a.B;
     g.L = a.L;
     g.H = a.H;
     g.ncb = w.sh.ncb;
     g.nq = w.sh.nq;
-    g.counter = reinterpret_cast<uint32_t *>(ws + w.counter);
+    g.ntiles = w.sh.ntiles;
+    g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
     g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
     g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
-    g.agg_next = nullptr;
-    g.inc_next = nullptr;
-    g.err = reinterpret_cast<uint32_t *>(ws + w.err);
     if (w.sh.channel_lanes)
         hipLaunchKernelGGL((chunk_scan_kernel<Op, NWC, CC, true>), dim3((unsigned)w.sh.ntiles),
                            dim3(NWC * 64), 0, s, op, g);
     else
         hipLaunchKernelGGL((chunk_scan_kernel<Op, NWT, CT, false>), dim3((unsigned)w.sh.ntiles),
                            dim3(NWT * 64), 0, s, op, g);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess || !want_u) return e;
     UReduceArgs r;
     r.partial = op.partial;

@@ -28,10 +28,10 @@ int status_of(hipError_t e) { return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_
 bool grid_ok(int64_t ntiles) { return ntiles > 0 && ntiles < ((int64_t)1 << 31); }
 
 size_t gru_step_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
-    return newton_ws(kCfgGruStep, 1, 1, B, L, H, cap).total;
+    return newton_ws(kCfgGruStep, 1, B, L, H, cap).total;
 }
 size_t lstm_step_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
-    return newton_ws(kCfgLstmStep, 2, 3, B, L, H, cap).total;
+    return newton_ws(kCfgLstmStep, 2, B, L, H, cap).total;
 }
 
 // Path for the GRU forward: the fused on-chip kernel while the sequence fits
@@ -64,7 +64,7 @@ size_t pararnn_workspace_bytes(int32_t op, int64_t B, int64_t L, int64_t H, int3
     if (!dims_ok(B, L, H)) return 0;
     switch (op) {
         case PARARNN_OP_LINSCAN_DIAG: return scan_ws(kCfgLinDiag, 1, B, L, H).total;
-        case PARARNN_OP_LINSCAN_BLK2: return scan_ws(kCfgLinBlk2, 3, B, L, H).total;
+        case PARARNN_OP_LINSCAN_BLK2: return scan_ws(kCfgLinBlk2, 2, B, L, H).total;
         case PARARNN_OP_GRU_FORWARD:
             if (max_iter < 1) return 0;
             return gru_step_ws(B, L, H, max_iter);
@@ -92,7 +92,7 @@ int rnn_linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const floa
     if (!aligned(A, 16) || !aligned(b, 8) || !aligned(h, 8) || (h0 && !aligned(h0, 8)))
         return PARARNN_ERR_INVALID;
     if (!grid_ok(scan_shape(kCfgLinBlk2, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
-    if (ws_bytes < scan_ws(kCfgLinBlk2, 3, B, L, H).total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+    if (ws_bytes < scan_ws(kCfgLinBlk2, 2, B, L, H).total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
     return status_of(linscan_blk2(B, L, H, A, b, h0, h, static_cast<char *>(ws),
                                   static_cast<hipStream_t>(stream)));
 }

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "plan.hpp"
+
 namespace prn {
 
 // ---------------------------------------------------------------- math
@@ -91,27 +93,35 @@ template <> struct MonoidT<2> {
 };
 
 // ---------------------------------------------------------------- look-back
-// Decoupled look-back descriptors, one per (chunk, batch, channel).  Each
-// descriptor is a few 64-bit words that are written exactly once per launch
-// (from the sentinel to a value) with agent-scope atomic stores, and polled
-// with agent-scope atomic loads, which the compiler emits as device-coherent
-// (sc1) accesses, so they are seen across the XCDs' separate L2 caches.  A
-// word that is no longer the sentinel therefore already holds its final
-// value and no flag or fence is needed.  The sentinel is a signalling-NaN
-// pair that arithmetic never produces; published values are canonicalised so
-// that an input NaN cannot mimic it.
-//   agg : the chunk's aggregate map (S=1: 1 word; S=2: 3 words)
+// Decoupled look-back descriptors, one per (chunk, batch, channel).  Every
+// word is 64 bits: a float payload in the low half and the tag of the launch
+// that wrote it in the high half.  Words are written once per launch with
+// agent-scope atomic stores and polled with agent-scope atomic loads, which
+// the compiler emits as device-coherent (sc1) accesses, so they are seen
+// across the XCDs' separate L2 caches.  A word whose tag is this launch's
+// already holds its final value, so no flag, fence or clearing pass is
+// needed: words left over from earlier launches carry other tags.
+//   agg : the chunk's aggregate map (S=1: a, b; S=2: a00, a01, a10, a11, b0, b1)
 //   inc : the state after the chunk, i.e. the inclusive prefix applied to the
-//         initial state (S=1: low half of 1 word; S=2: 1 word)
-constexpr uint32_t kSentinel32 = 0x7f800001u;
-constexpr uint64_t kSentinel64 = 0x7f8000017f800001ull;
+//         initial state (S components)
+//
+// Launch tags are signalling-NaN bit patterns (exponent all ones, quiet bit
+// clear, non-zero mantissa; both signs), which arithmetic never produces, so
+// a float that another entry point left in the same workspace cannot look
+// like a tag.  Consecutive launches on one workspace get consecutive epochs;
+// tags repeat only after kTagPeriod launches.
+constexpr uint32_t kTagHalf = 0x3fffffu;
+constexpr uint32_t kTagPeriod = 2u * kTagHalf;
+__device__ __forceinline__ uint32_t launch_tag(uint32_t epoch) {
+    const uint32_t e = epoch % kTagPeriod;
+    return e < kTagHalf ? 0x7f800001u + e : 0xff800001u + (e - kTagHalf);
+}
 
-__device__ __forceinline__ float canon(float x) { return x != x ? __uint_as_float(0x7fc00000u) : x; }
-__device__ __forceinline__ uint64_t pack2(float lo, float hi) {
-    return (uint64_t)__float_as_uint(canon(lo)) | ((uint64_t)__float_as_uint(canon(hi)) << 32);
+__device__ __forceinline__ uint64_t tagged(float x, uint32_t tag) {
+    return (uint64_t)__float_as_uint(x) | ((uint64_t)tag << 32);
 }
 __device__ __forceinline__ float lo_f(uint64_t w) { return __uint_as_float((uint32_t)w); }
-__device__ __forceinline__ float hi_f(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
+__device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
 
 __device__ __forceinline__ uint64_t ld_coherent(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -129,52 +139,85 @@ template <> __device__ __forceinline__ float2s nan_state<2>() {
 template <int S> struct Desc;
 
 template <> struct Desc<1> {
-    static constexpr int kAggWords = 1;
-    static constexpr int kIncWords = 1;
-    __device__ static void put_agg(uint64_t *w, Aff1 m) { st_coherent(w, pack2(m.a, m.b)); }
-    __device__ static void put_inc(uint64_t *w, float x) { st_coherent(w, pack2(x, 0.0f)); }
-    __device__ static bool get_inc(const uint64_t *w, float &x) {
-        uint64_t v = ld_coherent(w);
-        if (v == kSentinel64) return false;
+    static constexpr int kAggWords = desc_agg_words(1);
+    static constexpr int kIncWords = desc_inc_words(1);
+    static_assert(kAggWords == 2 && kIncWords == 1, "one word per float");
+    __device__ static void put_agg(uint64_t *w, Aff1 m, uint32_t tag) {
+        st_coherent(w + 0, tagged(m.a, tag));
+        st_coherent(w + 1, tagged(m.b, tag));
+    }
+    __device__ static void put_inc(uint64_t *w, float x, uint32_t tag) { st_coherent(w, tagged(x, tag)); }
+    __device__ static bool get_inc(const uint64_t *w, float &x, uint32_t tag) {
+        const uint64_t v = ld_coherent(w);
+        if (!has_tag(v, tag)) return false;
         x = lo_f(v);
         return true;
     }
-    __device__ static bool get_agg(const uint64_t *w, Aff1 &m) {
-        uint64_t v = ld_coherent(w);
-        if (v == kSentinel64) return false;
-        m = {lo_f(v), hi_f(v)};
+    __device__ static bool get_agg(const uint64_t *w, Aff1 &m, uint32_t tag) {
+        const uint64_t v0 = ld_coherent(w + 0), v1 = ld_coherent(w + 1);
+        if (!has_tag(v0, tag) || !has_tag(v1, tag)) return false;
+        m = {lo_f(v0), lo_f(v1)};
         return true;
     }
 };
 
 template <> struct Desc<2> {
-    static constexpr int kAggWords = 3;
-    static constexpr int kIncWords = 1;
-    __device__ static void put_agg(uint64_t *w, Aff2 m) {
-        st_coherent(w + 0, pack2(m.a00, m.a01));
-        st_coherent(w + 1, pack2(m.a10, m.a11));
-        st_coherent(w + 2, pack2(m.b0, m.b1));
+    static constexpr int kAggWords = desc_agg_words(2);
+    static constexpr int kIncWords = desc_inc_words(2);
+    static_assert(kAggWords == 6 && kIncWords == 2, "one word per float");
+    __device__ static void put_agg(uint64_t *w, Aff2 m, uint32_t tag) {
+        st_coherent(w + 0, tagged(m.a00, tag));
+        st_coherent(w + 1, tagged(m.a01, tag));
+        st_coherent(w + 2, tagged(m.a10, tag));
+        st_coherent(w + 3, tagged(m.a11, tag));
+        st_coherent(w + 4, tagged(m.b0, tag));
+        st_coherent(w + 5, tagged(m.b1, tag));
     }
-    __device__ static void put_inc(uint64_t *w, float2s x) { st_coherent(w, pack2(x.x, x.y)); }
-    __device__ static bool get_inc(const uint64_t *w, float2s &x) {
-        uint64_t v = ld_coherent(w);
-        if (v == kSentinel64) return false;
-        x = {lo_f(v), hi_f(v)};
+    __device__ static void put_inc(uint64_t *w, float2s x, uint32_t tag) {
+        st_coherent(w + 0, tagged(x.x, tag));
+        st_coherent(w + 1, tagged(x.y, tag));
+    }
+    __device__ static bool get_inc(const uint64_t *w, float2s &x, uint32_t tag) {
+        const uint64_t v0 = ld_coherent(w + 0), v1 = ld_coherent(w + 1);
+        if (!has_tag(v0, tag) || !has_tag(v1, tag)) return false;
+        x = {lo_f(v0), lo_f(v1)};
         return true;
     }
-    __device__ static bool get_agg(const uint64_t *w, Aff2 &m) {
-        uint64_t v0 = ld_coherent(w + 0), v1 = ld_coherent(w + 1), v2 = ld_coherent(w + 2);
-        if (v0 == kSentinel64 || v1 == kSentinel64 || v2 == kSentinel64) return false;
-        m = {lo_f(v0), hi_f(v0), lo_f(v1), hi_f(v1), lo_f(v2), hi_f(v2)};
+    __device__ static bool get_agg(const uint64_t *w, Aff2 &m, uint32_t tag) {
+        uint64_t v[6];
+#pragma unroll
+        for (int k = 0; k < 6; ++k) v[k] = ld_coherent(w + k);
+        bool ok = true;
+#pragma unroll
+        for (int k = 0; k < 6; ++k) ok = ok && has_tag(v[k], tag);
+        if (!ok) return false;
+        m = {lo_f(v[0]), lo_f(v[1]), lo_f(v[2]), lo_f(v[3]), lo_f(v[4]), lo_f(v[5])};
         return true;
     }
 };
 
+// Ticket header of a workspace (its first 8 bytes): tickets drawn in the
+// current launch in the low half, the launch epoch in the high half.  The
+// workgroup that draws a launch's last ticket resets the count and advances
+// the epoch, so the next launch on the stream finds the header ready; a
+// zero-filled workspace is ready for its first launch.
+struct Ticket {
+    uint32_t index, tag;
+};
+__device__ __forceinline__ Ticket draw_ticket(uint64_t *hdr, uint32_t ntiles) {
+    const uint64_t old = __hip_atomic_fetch_add(hdr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t idx = (uint32_t)old, epoch = (uint32_t)(old >> 32);
+    if (idx == ntiles - 1)
+        __hip_atomic_store(hdr, (uint64_t)(epoch + 1u) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return {idx, launch_tag(epoch)};
+}
+
 // Bound on the polls of one unpublished descriptor.  Every predecessor of a
 // chunk holds a smaller dynamic ticket, so it is already resident and will
 // publish and the wait ends; the bound is only a guard against a broken
-// invariant: when it is hit the error word is set and NaN is returned, so
-// the failure shows in the output instead of hanging the device.
+// invariant (such as a workspace that was not zero-filled before its first
+// use): when it is hit NaN is returned, so the failure shows in the output
+// instead of hanging the device.
 constexpr uint32_t kMaxPolls = 1u << 20;
 
 // ---------------------------------------------------------------- indexing

@@ -55,6 +55,7 @@ __device__ __forceinline__ void lds_barrier() {
 // so give each XCD a contiguous run of tiles; neighbouring 16-channel tiles
 // share 128-byte lines and then share one L2.
 __device__ __forceinline__ int64_t xcd_tile(int64_t n, int64_t ntiles) {
+    if (!kFusedXcdOrder) return n;
     return (ntiles & 7) == 0 ? (n & 7) * (ntiles >> 3) + (n >> 3) : n;
 }
 

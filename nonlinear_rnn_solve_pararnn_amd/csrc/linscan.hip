@@ -150,27 +150,17 @@ static hipError_t launch_scan(const Op &op, const ScanGeo &g, int64_t ntiles, hi
 template <class Op, int S, int NWC, int CC, int NWT, int CT>
 static hipError_t run_scan(const TileCfg &cfg, const Op &op, int64_t B, int64_t L, int64_t H,
                            char *ws, hipStream_t s) {
-    const ScanWs w = scan_ws(cfg, Desc<S>::kAggWords, B, L, H);
-    FillRange fr[4] = {
-        {ws + w.counter, 1, 0, 4},
-        {ws + w.err, 1, 0, 4},
-        {ws + w.agg, (uint64_t)w.sh.ndesc * Desc<S>::kAggWords, kSentinel64, 8},
-        {ws + w.inc, (uint64_t)w.sh.ndesc, kSentinel64, 8},
-    };
-    hipError_t e = fill(fr, 4, s);
-    if (e != hipSuccess) return e;
+    const ScanWs w = scan_ws(cfg, S, B, L, H);
     ScanGeo g;
     g.B = B;
     g.L = L;
     g.H = H;
     g.ncb = w.sh.ncb;
     g.nq = w.sh.nq;
-    g.counter = reinterpret_cast<uint32_t *>(ws + w.counter);
+    g.ntiles = w.sh.ntiles;
+    g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
     g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
     g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
-    g.agg_next = nullptr;
-    g.inc_next = nullptr;
-    g.err = reinterpret_cast<uint32_t *>(ws + w.err);
     return w.sh.channel_lanes ? launch_scan<Op, NWC, CC, true>(op, g, w.sh.ntiles, s)
                               : launch_scan<Op, NWT, CT, false>(op, g, w.sh.ntiles, s);
 }

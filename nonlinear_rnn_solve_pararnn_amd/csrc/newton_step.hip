@@ -243,33 +243,23 @@ template <int S, int NWC, int CC, int NWT, int CT, class MakeOp>
 static hipError_t newton_loop(const TileCfg &cfg, int64_t B, int64_t L, int64_t H, int32_t cap,
                               float tol, int32_t *info, float *trace, char *ws, hipStream_t s,
                               MakeOp make_op) {
-    const NewtonWs w = newton_ws(cfg, S, Desc<S>::kAggWords, B, L, H, cap);
-    FillRange fr[7] = {
-        {ws + w.counters, (uint64_t)cap, 0, 4},
-        {ws + w.err, 1, 0, 4},
-        {ws + w.maxd, (uint64_t)cap, 0, 4},
-        {ws + w.agg[0], (uint64_t)w.sh.ndesc * Desc<S>::kAggWords, kSentinel64, 8},
-        {ws + w.inc[0], (uint64_t)w.sh.ndesc, kSentinel64, 8},
-        {ws + w.agg[1], (uint64_t)w.sh.ndesc * Desc<S>::kAggWords, kSentinel64, 8},
-        {ws + w.inc[1], (uint64_t)w.sh.ndesc, kSentinel64, 8},
-    };
-    hipError_t e = fill(fr, 7, s);
+    const NewtonWs w = newton_ws(cfg, S, B, L, H, cap);
+    FillRange fr[1] = {{ws + w.maxd, (uint64_t)cap, 0, 4}};
+    hipError_t e = fill(fr, 1, s);
     if (e != hipSuccess) return e;
     uint32_t *maxd = reinterpret_cast<uint32_t *>(ws + w.maxd);
+    ScanGeo g;
+    g.B = B;
+    g.L = L;
+    g.H = H;
+    g.ncb = w.sh.ncb;
+    g.nq = w.sh.nq;
+    g.ntiles = w.sh.ntiles;
+    g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
+    g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
+    g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
     for (int k = 1; k <= cap; ++k) {
         const int par = k & 1;
-        ScanGeo g;
-        g.B = B;
-        g.L = L;
-        g.H = H;
-        g.ncb = w.sh.ncb;
-        g.nq = w.sh.nq;
-        g.counter = reinterpret_cast<uint32_t *>(ws + w.counters) + (k - 1);
-        g.agg = reinterpret_cast<uint64_t *>(ws + w.agg[par]);
-        g.inc = reinterpret_cast<uint64_t *>(ws + w.inc[par]);
-        g.agg_next = reinterpret_cast<uint64_t *>(ws + w.agg[par ^ 1]);
-        g.inc_next = reinterpret_cast<uint64_t *>(ws + w.inc[par ^ 1]);
-        g.err = reinterpret_cast<uint32_t *>(ws + w.err);
         auto op = make_op(k, ws + w.bnd[par ^ 1], ws + w.bnd[par], maxd);
         e = w.sh.channel_lanes ? launch_iter<decltype(op), NWC, CC, true>(op, g, w.sh.ntiles, s)
                                : launch_iter<decltype(op), NWT, CT, false>(op, g, w.sh.ntiles, s);

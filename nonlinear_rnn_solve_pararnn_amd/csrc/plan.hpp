@@ -21,6 +21,9 @@ constexpr TileCfg kCfgLstmStep{16, 8, 4, 8};
 constexpr TileCfg kCfgGruAdj{4, 8, 16, 4};
 constexpr TileCfg kCfgLstmAdj{4, 4, 4, 4};
 constexpr int64_t kChannelLanesMinH = 32;
+// Look-back descriptors polled at once by one channel lane (diagonal, 2x2).
+constexpr int kLbBatchDiag = 4;
+constexpr int kLbBatchBlk2 = 1;
 
 struct ScanShape {
     bool channel_lanes;
@@ -55,55 +58,65 @@ struct Carve {
     }
 };
 
-// Workspace of one scan launch: ticket counter and one descriptor set.
+// Every workspace starts with the 8-byte ticket header (common.hpp), at the
+// same offset for every entry point, so one zero-filled buffer can serve any
+// sequence of calls.
+
+// 64-bit words of one look-back descriptor of a recurrence with S state
+// components: the aggregate map (S x S matrix and S offsets) and the
+// inclusive state.
+constexpr int desc_agg_words(int S) { return S * S + S; }
+constexpr int desc_inc_words(int S) { return S; }
+
+// Workspace of one scan launch: header and one descriptor set.
 struct ScanWs {
     ScanShape sh;
-    size_t counter, err, agg, inc, partial, total;
+    size_t hdr, agg, inc, partial, total;
 };
 
-inline ScanWs scan_ws(const TileCfg &cfg, int agg_words, int64_t B, int64_t L, int64_t H,
+inline ScanWs scan_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64_t H,
                       int64_t partial_floats_per_tile = 0) {
     ScanWs w;
     w.sh = scan_shape(cfg, B, L, H);
     Carve c;
-    w.counter = c.take(4);
-    w.err = c.take(4);
-    w.agg = c.take((size_t)w.sh.ndesc * agg_words * 8);
-    w.inc = c.take((size_t)w.sh.ndesc * 8);
+    w.hdr = c.take(8);
+    w.agg = c.take((size_t)w.sh.ndesc * desc_agg_words(S) * 8);
+    w.inc = c.take((size_t)w.sh.ndesc * desc_inc_words(S) * 8);
     w.partial = c.take((size_t)w.sh.ntiles * partial_floats_per_tile * 4);
     w.total = c.off;
     return w;
 }
 
-// Workspace of the per-iteration Newton path: a ticket counter and a
-// max|delta| slot per iteration, two descriptor sets used alternately, and
-// two sets of chunk-boundary states (state components `S`).
+// Workspace of the per-iteration Newton path: header, a max|delta| slot per
+// iteration, one descriptor set (launch tags tell the launches apart) and
+// two sets of chunk-boundary states (state components `S`), used
+// alternately by consecutive iterations.
 struct NewtonWs {
     ScanShape sh;
-    size_t counters, maxd, err, agg[2], inc[2], bnd[2], total;
+    size_t hdr, maxd, agg, inc, bnd[2], total;
 };
 
-inline NewtonWs newton_ws(const TileCfg &cfg, int S, int agg_words, int64_t B, int64_t L,
-                          int64_t H, int32_t cap) {
+inline NewtonWs newton_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64_t H,
+                          int32_t cap) {
     NewtonWs w;
     w.sh = scan_shape(cfg, B, L, H);
     Carve c;
-    w.counters = c.take((size_t)cap * 4);
+    w.hdr = c.take(8);
     w.maxd = c.take((size_t)cap * 4);
-    w.err = c.take(4);
-    for (int k = 0; k < 2; ++k) {
-        w.agg[k] = c.take((size_t)w.sh.ndesc * agg_words * 8);
-        w.inc[k] = c.take((size_t)w.sh.ndesc * 8);
-    }
+    w.agg = c.take((size_t)w.sh.ndesc * desc_agg_words(S) * 8);
+    w.inc = c.take((size_t)w.sh.ndesc * desc_inc_words(S) * 8);
     for (int k = 0; k < 2; ++k) w.bnd[k] = c.take((size_t)w.sh.ndesc * S * 4);
     w.total = c.off;
     return w;
 }
 
-// Fused on-chip GRU Newton: one workgroup owns all L positions of 16
-// channels of one batch row; 8 waves, each lane one (channel, sub-chunk),
-// 32 sub-chunks of C positions.  Usable while L <= 32 * 16.
+// Fused on-chip GRU Newton: one workgroup owns all L positions of
+// kFusedChannels channels of one batch row; each lane is one (channel,
+// sub-chunk), 32 sub-chunks of C positions (so 32 * kFusedChannels / 64
+// waves).  Usable while L <= 32 * 16.  kFusedXcdOrder gives each XCD a
+// contiguous run of tiles.
 constexpr int kFusedChannels = 16;
+constexpr bool kFusedXcdOrder = true;
 constexpr int kFusedSubchunks = 32;
 constexpr int kFusedMaxC = 16;
 constexpr int64_t kFusedMaxL = (int64_t)kFusedSubchunks * kFusedMaxC;

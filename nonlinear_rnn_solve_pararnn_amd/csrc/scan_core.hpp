@@ -32,10 +32,9 @@ struct ScanGeo {
     int64_t B, L, H;
     int64_t ncb;            // channel blocks per batch row (channel lanes: ceil(H/64); time lanes: H)
     int64_t nq;             // chunks along the sequence
-    uint32_t *counter;      // ticket counter, zero at launch
+    int64_t ntiles;         // workgroups of the launch (= tickets drawn)
+    uint64_t *hdr;          // ticket header of the workspace (common.hpp)
     uint64_t *agg, *inc;    // look-back descriptors [nq][B][H] (words per descriptor: Desc<S>)
-    uint64_t *agg_next, *inc_next;  // optional: descriptor set to reset for the next launch
-    uint32_t *err;          // optional: set to 1 if a look-back wait gave up
 };
 
 struct TilePos {
@@ -99,9 +98,11 @@ __device__ __forceinline__ Aff2 bcast0_m(Aff2 m) {
 __device__ __forceinline__ float bcast0_s(float x) { return bcast0_f(x); }
 __device__ __forceinline__ float2s bcast0_s(float2s x) { return {bcast0_f(x.x), bcast0_f(x.y)}; }
 
-// Descriptors polled per batch by one channel lane (channel lanes), and the
-// window of the holder wave (time lanes: lane i polls predecessor i).
-constexpr int kLbBatch = 4;
+// Descriptors polled per batch by one channel lane (channel lanes; fewer for
+// the 2x2 blocks, whose descriptors are four times larger, to bound the
+// registers held across the wait), and the window of the holder wave (time
+// lanes: lane i polls predecessor i).
+template <int S> constexpr int kLbBatch = S == 1 ? kLbBatchDiag : kLbBatchBlk2;
 
 // Poll up to R consecutive predecessors p0, p0-1, ... (those >= 0) of one
 // channel, issuing all loads before looking at any, and fold them nearest
@@ -110,8 +111,8 @@ constexpr int kLbBatch = 4;
 // predecessor that has published nothing yet stops the fold there, to be
 // polled again by the caller.
 template <int S, int R>
-__device__ __forceinline__ LbPart<S> lb_poll_batch(const ScanGeo &g, int64_t p0, int64_t stride,
-                                                   int64_t slot, int64_t *next) {
+__device__ __forceinline__ LbPart<S> lb_poll_batch(const ScanGeo &g, uint32_t tag, int64_t p0,
+                                                   int64_t stride, int64_t slot, int64_t *next) {
     using M = MonoidT<S>;
     using D = Desc<S>;
     typename M::State xs[R];
@@ -123,8 +124,8 @@ __device__ __forceinline__ LbPart<S> lb_poll_batch(const ScanGeo &g, int64_t p0,
         const int64_t p = p0 - k;
         if (p >= 0) {
             const int64_t d = p * stride + slot;
-            const bool hi = D::get_inc(g.inc + d * D::kIncWords, xs[k]);
-            const bool ha = D::get_agg(g.agg + d * D::kAggWords, ms[k]);
+            const bool hi = D::get_inc(g.inc + d * D::kIncWords, xs[k], tag);
+            const bool ha = D::get_agg(g.agg + d * D::kAggWords, ms[k], tag);
             st[k] = hi ? 2 : (ha ? 1 : 0);
         }
     }
@@ -148,25 +149,21 @@ __device__ __forceinline__ LbPart<S> lb_poll_batch(const ScanGeo &g, int64_t p0,
 // State entering chunk q > 0 of one channel: batched, decoupled look-back by
 // one lane.  Every predecessor holds a smaller ticket, so it is resident and
 // publishes; the wait is still bounded (kMaxPolls rounds without progress
-// set the error word and give NaN).
+// give NaN).
 template <int S>
-__device__ typename MonoidT<S>::State lane_lookback(const ScanGeo &g, int64_t q, int64_t stride,
-                                                    int64_t slot) {
+__device__ typename MonoidT<S>::State lane_lookback(const ScanGeo &g, uint32_t tag, int64_t q,
+                                                    int64_t stride, int64_t slot) {
     using M = MonoidT<S>;
     typename M::Map acc = M::id();  // state entering the farthest folded chunk -> entering q
     int64_t p = q - 1;
     uint32_t idle = 0;
     for (;;) {
         int64_t next;
-        const LbPart<S> part = lb_poll_batch<S, kLbBatch>(g, p, stride, slot, &next);
+        const LbPart<S> part = lb_poll_batch<S, kLbBatch<S>>(g, tag, p, stride, slot, &next);
         if (part.found) return M::apply(acc, part.x);
         acc = M::then(part.acc, acc);
         if (next == p) {
-            if (++idle >= kMaxPolls) {
-                if (g.err != nullptr)
-                    __hip_atomic_store(g.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                return nan_state<S>();
-            }
+            if (++idle >= kMaxPolls) return nan_state<S>();
             __builtin_amdgcn_s_sleep(1);
         } else {
             idle = 0;
@@ -180,8 +177,8 @@ __device__ typename MonoidT<S>::State lane_lookback(const ScanGeo &g, int64_t q,
 // q-1-i), folds it with shuffles, and repeats with the next window until an
 // inclusive state is met.  Called by every lane of one wave.
 template <int S>
-__device__ typename MonoidT<S>::State wave_lookback(const ScanGeo &g, int64_t q, int64_t stride,
-                                                    int64_t slot) {
+__device__ typename MonoidT<S>::State wave_lookback(const ScanGeo &g, uint32_t tag, int64_t q,
+                                                    int64_t stride, int64_t slot) {
     using M = MonoidT<S>;
     using D = Desc<S>;
     const int lane = threadIdx.x & 63;
@@ -194,11 +191,9 @@ __device__ typename MonoidT<S>::State wave_lookback(const ScanGeo &g, int64_t q,
             for (uint32_t polls = 0;; ++polls) {
                 typename M::State x;
                 typename M::Map m;
-                if (D::get_inc(g.inc + d * D::kIncWords, x)) { part = {M::id(), x, 1}; break; }
-                if (D::get_agg(g.agg + d * D::kAggWords, m)) { part = {m, M::zero(), 0}; break; }
+                if (D::get_inc(g.inc + d * D::kIncWords, x, tag)) { part = {M::id(), x, 1}; break; }
+                if (D::get_agg(g.agg + d * D::kAggWords, m, tag)) { part = {m, M::zero(), 0}; break; }
                 if (polls >= kMaxPolls) {
-                    if (g.err != nullptr)
-                        __hip_atomic_store(g.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     part = {M::id(), nan_state<S>(), 1};
                     break;
                 }
@@ -222,7 +217,8 @@ __device__ typename MonoidT<S>::State wave_lookback(const ScanGeo &g, int64_t q,
 // One tile (chunk q of a batch row and channel block, identified by its
 // ticket) of a scan.  Every thread of the workgroup calls this.
 template <class Op, int NW, int C, bool CHANNEL_LANES>
-__device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_t ticket) {
+__device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_t ticket,
+                                          uint32_t tag) {
     constexpr int S = Op::S;
     using M = MonoidT<S>;
     using D = Desc<S>;
@@ -293,30 +289,26 @@ __device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_
     if (tp.q == 0) {
         if (holder) {
             const State xin = op.init_state(tp);
-            if (tp.ok) D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin));
+            if (tp.ok) D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin), tag);
             s_carry[cslot] = xin;
         }
     } else if (CHANNEL_LANES) {
         if (holder) {
             State xin = M::zero();
             if (tp.ok) {
-                D::put_agg(g.agg + dsc * D::kAggWords, tot);
-                xin = lane_lookback<S>(g, tp.q, stride, slot);
-                D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin));
+                D::put_agg(g.agg + dsc * D::kAggWords, tot, tag);
+                xin = lane_lookback<S>(g, tag, tp.q, stride, slot);
+                D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin), tag);
             }
             s_carry[cslot] = xin;
         }
     } else if (w == NW - 1) {
-        if (holder) D::put_agg(g.agg + dsc * D::kAggWords, tot);
-        const State xin = wave_lookback<S>(g, tp.q, stride, slot);
+        if (holder) D::put_agg(g.agg + dsc * D::kAggWords, tot, tag);
+        const State xin = wave_lookback<S>(g, tag, tp.q, stride, slot);
         if (holder) {
-            D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin));
+            D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin), tag);
             s_carry[0] = xin;
         }
-    }
-    if (g.agg_next != nullptr && holder && tp.ok) {
-        for (int k = 0; k < D::kAggWords; ++k) g.agg_next[dsc * D::kAggWords + k] = kSentinel64;
-        for (int k = 0; k < D::kIncWords; ++k) g.inc_next[dsc * D::kIncWords + k] = kSentinel64;
     }
     __syncthreads();
     const State x = M::apply(ex, s_carry[CHANNEL_LANES ? lane : 0]);
@@ -324,15 +316,18 @@ __device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_
 }
 
 // One launch of a scan: each workgroup draws one ticket (tiles are handed
-// out in ticket order, which is what makes the look-back wait finite).
+// out in ticket order, which is what makes the look-back wait finite).  A
+// ticket beyond the grid can only come from a workspace that was not
+// zero-filled before its first use; such a workgroup does nothing.
 template <class Op, int NW, int C, bool CHANNEL_LANES>
 __global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
-    __shared__ uint32_t s_ticket;
+    __shared__ Ticket s_ticket;
     if (!op.active()) return;  // uniform over the grid (e.g. Newton already converged)
-    if (threadIdx.x == 0)
-        s_ticket = __hip_atomic_fetch_add(g.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) s_ticket = draw_ticket(g.hdr, (uint32_t)g.ntiles);
     __syncthreads();
-    scan_tile<Op, NW, C, CHANNEL_LANES>(op, g, s_ticket);
+    const Ticket t = s_ticket;
+    if (t.index >= g.ntiles) return;
+    scan_tile<Op, NW, C, CHANNEL_LANES>(op, g, t.index, t.tag);
 }
 
 // Reduce a per-thread value over the workgroup into one value per channel

@@ -98,3 +98,35 @@ def test_linscan_rejects_bad_arguments():
     ws = torch.empty(16, dtype=torch.uint8, device="cuda:0")
     with pytest.raises(ValueError):
         api.linscan_diag(a, a, ws=ws)
+
+
+def test_workspace_reused_across_entry_points_and_shapes(orc, monkeypatch):
+    """One zero-filled workspace serves a sequence of calls of different entry
+    points and shapes (every launch leaves its ticket header ready and its
+    look-back records tagged with its own launch number)."""
+    from tests.gpu_helpers import lstm_args
+    monkeypatch.setenv("PARARNN_GRU_PATH", "step")
+    big = max(api.workspace_bytes(op, 3, 5000, 70, 16) for op in range(6))
+    ws = api.new_workspace(big, "cuda:0")
+    d1 = synth.linscan_diag_inputs(3, 5000, 70, seed=21)
+    d2 = synth.linscan_blk2_inputs(2, 700, 33, seed=22)
+    d3 = synth.lstm_inputs(2, 300, 40, seed=23, h0=True)
+    d4 = synth.linscan_diag_inputs(1, 4000, 3, seed=24)
+    d5 = synth.gru_inputs(2, 2000, 5, seed=25)
+    for rnd in range(3):
+        say("round", rnd)
+        h = host(api.linscan_diag(dev(d1["a"]), dev(d1["b"]), ws=ws))
+        assert max_abs(h, orc.linscan_diag(d1["a"], d1["b"])) <= FWD_ATOL
+        h = host(api.linscan_blk2(dev(d2["A"]), dev(d2["b"]), ws=ws))
+        assert max_abs(h, orc.linscan_blk2(d2["A"], d2["b"])) <= FWD_ATOL
+        info = torch.zeros(2, dtype=torch.int32, device="cuda:0")
+        h, c = api.lstm_forward(*[dev(x) for x in lstm_args(d3)], dev(d3["h0"]), dev(d3["c0"]),
+                                tol=1e-5, max_iter=16, info=info, ws=ws)
+        hr, cr = orc.lstm_rollout(*lstm_args(d3), h0=d3["h0"], c0=d3["c0"])
+        assert int(info[1]) == 1 and max_abs(host(h), hr) <= FWD_ATOL and max_abs(host(c), cr) <= FWD_ATOL
+        h = host(api.linscan_diag(dev(d4["a"]), dev(d4["b"]), ws=ws))
+        assert max_abs(h, orc.linscan_diag(d4["a"], d4["b"])) <= FWD_ATOL
+        g = [dev(d5[k]) for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
+        h = host(api.gru_forward(*g, tol=1e-5, max_iter=16, info=info, ws=ws))
+        ref = orc.gru_rollout(*(d5[k] for k in ("pz", "pr", "pc", "uz", "ur", "uc")))
+        assert int(info[1]) == 1 and max_abs(h, ref) <= FWD_ATOL
