@@ -77,6 +77,7 @@ struct GruAdjOp {
     float *gpz, *gpr, *gpc, *gh0;
     float *partial;  // NULL when no dL/du is wanted
     int64_t L, H;
+    bool runs;  // H == 1 with 16-byte aligned rows: whole runs move as float4
 
     struct Elem {
         float J, g, dz, dr, dc, xz, xr, xc;  // xz.. = pre-activation derivative by u times dF/dp
@@ -84,11 +85,40 @@ struct GruAdjOp {
     __device__ bool active() const { return true; }
     __device__ float init_state(const TilePos &) const { return 0.0f; }
 
+    // The C positions of a thread are the times tlo + C-1 down to tlo; as a
+    // run in memory, position pos0 + i is element C-1-i.
+    __device__ bool whole_run(const TilePos &tp, int C) const {
+        return runs && tp.ok && tp.pos0 + C <= L;
+    }
+
     template <int C>
     __device__ Aff1 phase1(const TilePos &tp, Elem (&e)[C]) const {
         const float wz = tp.ok ? uz[tp.j] : 0.0f, wr = tp.ok ? ur[tp.j] : 0.0f,
                     wc = tp.ok ? uc[tp.j] : 0.0f;
         Aff1 acc = {1.0f, 0.0f};
+        if constexpr (C % 4 == 0) {
+            if (whole_run(tp, C)) {
+                const int64_t tlo = L - tp.pos0 - C;
+                const int64_t blo = idx3(tp.b, tlo, tp.j, L, H);
+                float vz[C], vr[C], vc[C], vg[C], vh[C];
+                load_run<C>(pz + blo, vz);
+                load_run<C>(pr + blo, vr);
+                load_run<C>(pc + blo, vc);
+                load_run<C>(gh + blo, vg);
+                load_run<C>(h + blo, vh);
+                const float hlo = tlo == 0 ? (h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f) : h[blo - 1];
+#pragma unroll
+                for (int i = 0; i < C; ++i) {
+                    const int m = C - 1 - i;
+                    const float hp = m == 0 ? hlo : vh[m - 1];
+                    float J, dz, dr, dc, r;
+                    gru_j_dp(hp, vz[m], vr[m], vc[m], wz, wr, wc, J, dz, dr, dc, r);
+                    e[i] = {J, vg[m], dz, dr, dc, dz * hp, dr * hp, dc * r * hp};
+                    acc = {acc.a * J, fmaf(J, acc.b, J * vg[m])};
+                }
+                return acc;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             const int64_t pos = tp.pos0 + i;
@@ -110,21 +140,48 @@ struct GruAdjOp {
     template <int C, int NW, bool CL>
     __device__ void phase2(const TilePos &tp, Elem (&e)[C], float nu) const {
         float su[3] = {0.0f, 0.0f, 0.0f};
+        bool done = false;  // store_u_partials below must be reached by every thread
+        if constexpr (C % 4 == 0) {
+            if (whole_run(tp, C)) {
+                const int64_t tlo = L - tp.pos0 - C;
+                const int64_t blo = idx3(tp.b, tlo, tp.j, L, H);
+                float oz[C], orr[C], oc[C];
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            const int64_t pos = tp.pos0 + i;
-            if (tp.ok && pos < L) {
-                const int64_t t = L - 1 - pos;
-                const int64_t kk = idx3(tp.b, t, tp.j, L, H);
-                const float lam = e[i].g + nu;
-                gpz[kk] = e[i].dz * lam;
-                gpr[kk] = e[i].dr * lam;
-                gpc[kk] = e[i].dc * lam;
-                su[0] = fmaf(e[i].xz, lam, su[0]);
-                su[1] = fmaf(e[i].xr, lam, su[1]);
-                su[2] = fmaf(e[i].xc, lam, su[2]);
-                nu = e[i].J * lam;
-                if (t == 0 && gh0 != nullptr) gh0[tp.b * H + tp.j] = nu;
+                for (int i = 0; i < C; ++i) {
+                    const int m = C - 1 - i;
+                    const float lam = e[i].g + nu;
+                    oz[m] = e[i].dz * lam;
+                    orr[m] = e[i].dr * lam;
+                    oc[m] = e[i].dc * lam;
+                    su[0] = fmaf(e[i].xz, lam, su[0]);
+                    su[1] = fmaf(e[i].xr, lam, su[1]);
+                    su[2] = fmaf(e[i].xc, lam, su[2]);
+                    nu = e[i].J * lam;
+                }
+                store_run<C>(gpz + blo, oz);
+                store_run<C>(gpr + blo, orr);
+                store_run<C>(gpc + blo, oc);
+                if (tlo == 0 && gh0 != nullptr) gh0[tp.b * H + tp.j] = nu;
+                done = true;
+            }
+        }
+        if (!done) {
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                const int64_t pos = tp.pos0 + i;
+                if (tp.ok && pos < L) {
+                    const int64_t t = L - 1 - pos;
+                    const int64_t kk = idx3(tp.b, t, tp.j, L, H);
+                    const float lam = e[i].g + nu;
+                    gpz[kk] = e[i].dz * lam;
+                    gpr[kk] = e[i].dr * lam;
+                    gpc[kk] = e[i].dc * lam;
+                    su[0] = fmaf(e[i].xz, lam, su[0]);
+                    su[1] = fmaf(e[i].xr, lam, su[1]);
+                    su[2] = fmaf(e[i].xc, lam, su[2]);
+                    nu = e[i].J * lam;
+                    if (t == 0 && gh0 != nullptr) gh0[tp.b * H + tp.j] = nu;
+                }
             }
         }
         if (partial != nullptr) store_u_partials<NW, CL, 3>(tp, su, partial);
@@ -289,6 +346,9 @@ hipError_t gru_adjoint(const AdjArgs &a, char *ws, hipStream_t s) {
     op.partial = nullptr;
     op.L = a.L;
     op.H = a.H;
+    op.runs = a.H == 1 && a.L % 4 == 0 && aligned16(a.p[0]) && aligned16(a.p[1]) && aligned16(a.p[2]) &&
+              aligned16(a.h) && aligned16(a.gh) && aligned16(a.gp[0]) && aligned16(a.gp[1]) &&
+              aligned16(a.gp[2]);
     constexpr TileCfg c = kCfgGruAdj;
     return run_adjoint<GruAdjOp, 1, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, op, 3, a, ws, s);
 }

@@ -220,6 +220,30 @@ __device__ __forceinline__ Ticket draw_ticket(uint64_t *hdr, uint32_t ntiles) {
 // instead of hanging the device.
 constexpr uint32_t kMaxPolls = 1u << 20;
 
+// ---------------------------------------------------------------- runs
+// C consecutive floats at a 16-byte aligned address, moved with one 16-byte
+// access per four floats: the sequence of a single channel (H = 1) walked by
+// one thread in the time-lane layout.
+template <int C>
+__device__ __forceinline__ void load_run(const float *p, float (&v)[C]) {
+    static_assert(C % 4 == 0, "runs are whole float4s");
+#pragma unroll
+    for (int k = 0; k < C / 4; ++k) {
+        const float4 q = reinterpret_cast<const float4 *>(p)[k];
+        v[4 * k + 0] = q.x;
+        v[4 * k + 1] = q.y;
+        v[4 * k + 2] = q.z;
+        v[4 * k + 3] = q.w;
+    }
+}
+template <int C>
+__device__ __forceinline__ void store_run(float *p, const float (&v)[C]) {
+    static_assert(C % 4 == 0, "runs are whole float4s");
+#pragma unroll
+    for (int k = 0; k < C / 4; ++k)
+        reinterpret_cast<float4 *>(p)[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+}
+
 // ---------------------------------------------------------------- indexing
 __device__ __forceinline__ int64_t idx3(int64_t b, int64_t t, int64_t j, int64_t L, int64_t H) {
     return (b * L + t) * H + j;

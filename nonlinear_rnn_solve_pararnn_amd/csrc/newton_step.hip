@@ -65,6 +65,8 @@ struct GruStepOp {
     __device__ bool active() const { return newton_active(maxd, k, tol); }
     __device__ float init_state(const TilePos &) const { return 0.0f; }
 
+    bool runs;  // H == 1 with 16-byte aligned rows: whole runs move as float4
+
     template <int C>
     __device__ Aff1 phase1(const TilePos &tp, Elem (&e)[C]) const {
         const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
@@ -84,6 +86,29 @@ struct GruStepOp {
                 hp = h[base - H];
         }
         Aff1 acc = {1.0f, 0.0f};
+        if constexpr (C % 4 == 0) {
+            if (runs && tp.ok && tp.pos0 + C <= L) {
+                float vz[C], vr[C], vc[C], vh[C];
+                load_run<C>(pz + base, vz);
+                load_run<C>(pr + base, vr);
+                load_run<C>(pc + base, vc);
+                if (k == 1) {
+#pragma unroll
+                    for (int i = 0; i < C; ++i) vh[i] = 0.0f;
+                } else {
+                    load_run<C>(h + base, vh);
+                }
+#pragma unroll
+                for (int i = 0; i < C; ++i) {
+                    float F, J;
+                    gru_f_j(hp, vz[i], vr[i], vc[i], wz, wr, wc, F, J);
+                    e[i] = {J, F - vh[i], vh[i]};
+                    hp = vh[i];
+                    acc = {acc.a * J, fmaf(J, acc.b, e[i].beta)};
+                }
+                return acc;
+            }
+        }
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             if (tp.ok && tp.pos0 + i < L) {
@@ -105,16 +130,34 @@ struct GruStepOp {
     __device__ void phase2(const TilePos &tp, Elem (&e)[C], float d) const {
         const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
         uint32_t mx = 0;
+        bool done = false;  // the workgroup reduction below must be reached by every thread
+        if constexpr (C % 4 == 0) {
+            if (runs && tp.ok && tp.pos0 + C <= L) {
+                float hn[C];
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            if (tp.ok && tp.pos0 + i < L) {
-                d = fmaf(e[i].J, d, e[i].beta);
-                const float hn = e[i].hc + d;
-                h[base + i * H] = hn;
-                const uint32_t ad = abs_bits(d);
-                mx = ad > mx ? ad : mx;
-                if (i == C - 1 && tp.sub == tp.nsub - 1)
-                    bnd_next[tp.q * B * H + tp.b * H + tp.j] = hn;
+                for (int i = 0; i < C; ++i) {
+                    d = fmaf(e[i].J, d, e[i].beta);
+                    hn[i] = e[i].hc + d;
+                    const uint32_t ad = abs_bits(d);
+                    mx = ad > mx ? ad : mx;
+                }
+                store_run<C>(h + base, hn);
+                if (tp.sub == tp.nsub - 1) bnd_next[tp.q * B * H + tp.b * H + tp.j] = hn[C - 1];
+                done = true;
+            }
+        }
+        if (!done) {
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                if (tp.ok && tp.pos0 + i < L) {
+                    d = fmaf(e[i].J, d, e[i].beta);
+                    const float hn = e[i].hc + d;
+                    h[base + i * H] = hn;
+                    const uint32_t ad = abs_bits(d);
+                    mx = ad > mx ? ad : mx;
+                    if (i == C - 1 && tp.sub == tp.nsub - 1)
+                        bnd_next[tp.q * B * H + tp.b * H + tp.j] = hn;
+                }
             }
         }
         wg_max_to<NW>(mx, maxd + (k - 1));
@@ -292,6 +335,8 @@ hipError_t gru_forward_step(const GruFwdArgs &a, char *ws, hipStream_t s) {
         op.B = a.B;
         op.L = a.L;
         op.H = a.H;
+        op.runs = a.H == 1 && a.L % 4 == 0 && aligned16(a.pz) && aligned16(a.pr) && aligned16(a.pc) &&
+                  aligned16(a.h);
         return op;
     };
     constexpr TileCfg c = kCfgGruStep;

@@ -26,7 +26,8 @@ def _gru_case(orc, d, with_h0=True, want_u=True, want_h0=True):
 
 
 @pytest.mark.parametrize("B,L,H", [(1, 1, 1), (1, 64, 4), (2, 100, 3), (3, 257, 70),
-                                   (2, 5000, 1), (2, 700, 33), (4, 128, 128)])
+                                   (2, 5000, 1), (2, 700, 33), (4, 128, 128),
+                                   (1, 12, 1), (2, 4098, 1), (3, 8192, 1)])
 def test_gru_adjoint_matches_bptt(orc, B, L, H):
     say("gru adjoint", B, L, H)
     d = synth.gru_inputs(B, L, H, seed=80 + H, h0=True, grad=True)
@@ -83,4 +84,32 @@ def test_lstm_adjoint_matches_bptt(orc, B, L, H, with_gc):
     d = synth.lstm_inputs(B, L, H, seed=90 + H, h0=True, grad=True)
     errs = _lstm_case(orc, d, with_gc)
     say(errs)
+    assert max(errs.values()) <= GRAD_RTOL, errs
+
+
+def _offset_view(x):
+    """A contiguous device copy of x whose data pointer is 4 bytes past a
+    16-byte boundary (the single-channel kernels then take their scalar path)."""
+    flat = torch.empty(x.size + 1, dtype=torch.float32, device="cuda:0")
+    v = flat[1:].view(*x.shape)
+    v.copy_(torch.from_numpy(x))
+    assert v.data_ptr() % 16 != 0
+    return v
+
+
+def test_gru_single_channel_unaligned_inputs(orc):
+    """H = 1 with inputs that are not 16-byte aligned: forward and adjoint
+    still match the oracle."""
+    d = synth.gru_inputs(2, 5000, 1, seed=82, h0=True, grad=True)
+    ins = [_offset_view(x) for x in gru_args(d)]
+    h0 = dev(d["h0"])
+    h = api.gru_forward(*ins, h0, tol=1e-5, max_iter=32)
+    href = orc.gru_rollout(*gru_args(d), h0=d["h0"])
+    from tests.gpu_helpers import FWD_ATOL, max_abs
+    assert max_abs(host(h), href) <= FWD_ATOL
+    g = api.adjoint_backward(api.CELL_GRU, ins[:3], ins[3:], h, _offset_view(d["g"]), h0)
+    dp, du, dh0 = orc.gru_bptt(*gru_args(d), href, d["g"], h0=d["h0"])
+    errs = {"dp%d" % q: rel_inf(host(g["p"][q]), dp[q]) for q in range(3)}
+    errs.update({"du%d" % q: rel_inf(host(g["u"][q]), du[q]) for q in range(3)})
+    errs["dh0"] = rel_inf(host(g["h0"]), dh0)
     assert max(errs.values()) <= GRAD_RTOL, errs

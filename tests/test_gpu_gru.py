@@ -70,8 +70,10 @@ def test_shapes_match_rollout(orc, monkeypatch, path, B, L, H):
     assert max_abs(h, orc.gru_rollout(*gru_args(d), h0=d["h0"])) <= FWD_ATOL
 
 
-@pytest.mark.parametrize("B,L,H", [(2, 513, 20), (1, 5000, 3), (2, 700, 100), (3, 20000, 1)])
-def test_long_sequences_step_path(orc, B, L, H):
+@pytest.mark.parametrize("B,L,H", [(2, 513, 20), (1, 5000, 3), (2, 700, 100), (3, 20000, 1),
+                                   (1, 12, 1), (2, 4098, 1), (2, 8192, 1)])
+def test_long_sequences_step_path(orc, monkeypatch, B, L, H):
+    monkeypatch.setenv("PARARNN_GRU_PATH", "step")
     say("gru long", B, L, H)
     d = synth.gru_inputs(B, L, H, seed=50 + H, h0=True)
     h, info = _run(d, 1e-5, 32)
