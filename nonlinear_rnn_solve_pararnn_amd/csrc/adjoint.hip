@@ -307,13 +307,8 @@ static hipError_t run_adjoint(const TileCfg &cfg, Op op, int ngates, const AdjAr
     g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
     g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
     g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
-    if (w.sh.channel_lanes)
-        hipLaunchKernelGGL((chunk_scan_kernel<Op, NWC, CC, true>), dim3((unsigned)w.sh.ntiles),
-                           dim3(NWC * 64), 0, s, op, g);
-    else
-        hipLaunchKernelGGL((chunk_scan_kernel<Op, NWT, CT, false>), dim3((unsigned)w.sh.ntiles),
-                           dim3(NWT * 64), 0, s, op, g);
-    hipError_t e = hipGetLastError();
+    hipError_t e = w.sh.channel_lanes ? launch_chunk_scan<Op, NWC, CC, true>(op, g, s)
+                                      : launch_chunk_scan<Op, NWT, CT, false>(op, g, s);
     if (e != hipSuccess || !want_u) return e;
     UReduceArgs r;
     r.partial = op.partial;

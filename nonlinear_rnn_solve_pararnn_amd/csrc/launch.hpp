@@ -22,6 +22,9 @@ struct FillRange {
 constexpr int kMaxFill = 8;
 
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+// Compute units of the current device (queried once per device).
+int device_cu_count();
 hipError_t fill(const FillRange *r, int n, hipStream_t s);
 
 hipError_t linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const float *b,

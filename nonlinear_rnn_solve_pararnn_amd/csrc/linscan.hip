@@ -140,11 +140,17 @@ struct LinBlk2Op {
     }
 };
 
-template <class Op, int NW, int C, bool CL>
-static hipError_t launch_scan(const Op &op, const ScanGeo &g, int64_t ntiles, hipStream_t s) {
-    hipLaunchKernelGGL((chunk_scan_kernel<Op, NW, C, CL>), dim3((unsigned)ntiles), dim3(NW * 64), 0, s,
-                       op, g);
-    return hipGetLastError();
+int device_cu_count() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 template <class Op, int S, int NWC, int CC, int NWT, int CT>
@@ -161,8 +167,8 @@ static hipError_t run_scan(const TileCfg &cfg, const Op &op, int64_t B, int64_t 
     g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
     g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
     g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
-    return w.sh.channel_lanes ? launch_scan<Op, NWC, CC, true>(op, g, w.sh.ntiles, s)
-                              : launch_scan<Op, NWT, CT, false>(op, g, w.sh.ntiles, s);
+    return w.sh.channel_lanes ? launch_chunk_scan<Op, NWC, CC, true>(op, g, s)
+                              : launch_chunk_scan<Op, NWT, CT, false>(op, g, s);
 }
 
 

@@ -273,13 +273,6 @@ __global__ void newton_finalize(const uint32_t *maxd, int cap, float tol, int32_
     }
 }
 
-template <class Op, int NW, int C, bool CL>
-static hipError_t launch_iter(const Op &op, const ScanGeo &g, int64_t ntiles, hipStream_t s) {
-    hipLaunchKernelGGL((chunk_scan_kernel<Op, NW, C, CL>), dim3((unsigned)ntiles), dim3(NW * 64), 0, s,
-                       op, g);
-    return hipGetLastError();
-}
-
 // Runs the launch sequence shared by both cells.  `make_op(k, parity)`
 // returns the op of iteration k.
 template <int S, int NWC, int CC, int NWT, int CT, class MakeOp>
@@ -304,8 +297,8 @@ static hipError_t newton_loop(const TileCfg &cfg, int64_t B, int64_t L, int64_t 
     for (int k = 1; k <= cap; ++k) {
         const int par = k & 1;
         auto op = make_op(k, ws + w.bnd[par ^ 1], ws + w.bnd[par], maxd);
-        e = w.sh.channel_lanes ? launch_iter<decltype(op), NWC, CC, true>(op, g, w.sh.ntiles, s)
-                               : launch_iter<decltype(op), NWT, CT, false>(op, g, w.sh.ntiles, s);
+        e = w.sh.channel_lanes ? launch_chunk_scan<decltype(op), NWC, CC, true>(op, g, s)
+                               : launch_chunk_scan<decltype(op), NWT, CT, false>(op, g, s);
         if (e != hipSuccess) return e;
     }
     if (info != nullptr || trace != nullptr) {

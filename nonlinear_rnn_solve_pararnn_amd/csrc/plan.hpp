@@ -22,7 +22,10 @@ constexpr TileCfg kCfgGruAdj{4, 8, 16, 4};
 constexpr TileCfg kCfgLstmAdj{4, 4, 4, 4};
 constexpr int64_t kChannelLanesMinH = 32;
 // Look-back descriptors polled at once by one channel lane (diagonal, 2x2).
-constexpr int kLbBatchDiag = 4;
+constexpr int kLbBatchDiag = 2;
+// Scan launches use a grid of as many workgroups as fit on the device at
+// once, each drawing tiles until none is left (instead of one per tile).
+constexpr bool kScanPersistent = true;
 constexpr int kLbBatchBlk2 = 1;
 
 struct ScanShape {

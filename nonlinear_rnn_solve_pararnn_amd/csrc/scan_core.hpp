@@ -25,6 +25,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace prn {
 
@@ -315,19 +316,55 @@ __device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_
     op.template phase2<C, NW, CHANNEL_LANES>(tp, e, x);
 }
 
-// One launch of a scan: each workgroup draws one ticket (tiles are handed
-// out in ticket order, which is what makes the look-back wait finite).  A
-// ticket beyond the grid can only come from a workspace that was not
-// zero-filled before its first use; such a workgroup does nothing.
+// One launch of a scan.  Tiles are handed out in the order of dynamically
+// drawn tickets, which is what makes the look-back wait finite: a tile only
+// waits for tiles with smaller tickets, whose workgroups are already running.
+// With a grid of one workgroup per tile each workgroup draws one ticket.
+// With a smaller (persistent) grid each workgroup keeps drawing until it
+// draws past the last tile, so a launch draws ntiles + gridDim.x tickets and
+// the last of them resets the header.  A tile ticket beyond the grid can only
+// come from a workspace that was not zero-filled before its first use; such a
+// workgroup does nothing.
 template <class Op, int NW, int C, bool CHANNEL_LANES>
 __global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
     __shared__ Ticket s_ticket;
     if (!op.active()) return;  // uniform over the grid (e.g. Newton already converged)
-    if (threadIdx.x == 0) s_ticket = draw_ticket(g.hdr, (uint32_t)g.ntiles);
-    __syncthreads();
-    const Ticket t = s_ticket;
-    if (t.index >= g.ntiles) return;
-    scan_tile<Op, NW, C, CHANNEL_LANES>(op, g, t.index, t.tag);
+    const bool persistent = (int64_t)gridDim.x < g.ntiles;
+    const uint32_t draws = (uint32_t)(persistent ? g.ntiles + gridDim.x : g.ntiles);
+    for (;;) {
+        if (threadIdx.x == 0) s_ticket = draw_ticket(g.hdr, draws);
+        __syncthreads();  // scan_tile's own barriers keep the next write after every read
+        const Ticket t = s_ticket;
+        if (t.index >= g.ntiles) return;
+        scan_tile<Op, NW, C, CHANNEL_LANES>(op, g, t.index, t.tag);
+        if (!persistent) return;
+    }
+}
+
+// Workgroups of a scan launch: one per tile, or with kScanPersistent as many
+// as fit on the device at once (fewer workgroups to dispatch, which matters
+// most for the Newton launches that find the iteration already converged
+// and exit at once).
+template <class Op, int NW, int C, bool CL>
+static int64_t scan_grid(int64_t ntiles) {
+    if (!kScanPersistent) return ntiles;
+    static int per_cu = 0;
+    if (per_cu == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_scan_kernel<Op, NW, C, CL>, NW * 64, 0) !=
+                hipSuccess || n <= 0)
+            n = 1;
+        per_cu = n;
+    }
+    const int64_t slots = (int64_t)per_cu * device_cu_count();
+    return ntiles < slots ? ntiles : slots;
+}
+
+template <class Op, int NW, int C, bool CL>
+static hipError_t launch_chunk_scan(const Op &op, const ScanGeo &g, hipStream_t s) {
+    const int64_t grid = scan_grid<Op, NW, C, CL>(g.ntiles);
+    hipLaunchKernelGGL((chunk_scan_kernel<Op, NW, C, CL>), dim3((unsigned)grid), dim3(NW * 64), 0, s, op, g);
+    return hipGetLastError();
 }
 
 // Reduce a per-thread value over the workgroup into one value per channel
