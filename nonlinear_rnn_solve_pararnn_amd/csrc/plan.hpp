@@ -16,9 +16,9 @@ struct TileCfg {
 };
 constexpr TileCfg kCfgLinDiag{8, 16, 4, 16};
 constexpr TileCfg kCfgLinBlk2{4, 8, 4, 8};
-constexpr TileCfg kCfgGruStep{4, 16, 16, 4};
+constexpr TileCfg kCfgGruStep{4, 16, 8, 16};
 constexpr TileCfg kCfgLstmStep{16, 8, 4, 8};
-constexpr TileCfg kCfgGruAdj{4, 8, 16, 4};
+constexpr TileCfg kCfgGruAdj{4, 8, 16, 8};
 constexpr TileCfg kCfgLstmAdj{4, 4, 4, 4};
 constexpr int64_t kChannelLanesMinH = 32;
 // Look-back descriptors polled at once by one channel lane (diagonal, 2x2).
