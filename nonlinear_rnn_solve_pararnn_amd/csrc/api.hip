@@ -27,23 +27,41 @@ int status_of(hipError_t e) { return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_
 
 bool grid_ok(int64_t ntiles) { return ntiles > 0 && ntiles < ((int64_t)1 << 31); }
 
-size_t gru_step_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
-    return newton_ws(kCfgGruStep, 1, B, L, H, cap).total;
+size_t max2(size_t a, size_t b) { return a > b ? a : b; }
+
+// Workspace of a Newton forward: enough for either long-sequence path.
+size_t gru_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
+    return max2(newton_ws(kCfgGruStep, 1, B, L, H, cap).total, chain_ws(kCfgGruChain, 1, B, L, H, cap).total);
 }
-size_t lstm_step_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
-    return newton_ws(kCfgLstmStep, 2, B, L, H, cap).total;
+size_t lstm_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
+    return max2(newton_ws(kCfgLstmStep, 2, B, L, H, cap).total, chain_ws(kCfgLstmChain, 2, B, L, H, cap).total);
 }
 
-// Path for the GRU forward: the fused on-chip kernel while the sequence fits
-// one workgroup's registers, else one launch per Newton iteration.
-// PARARNN_GRU_PATH=fused|step overrides the choice (for testing both).
-enum class GruPath { Fused, Step, Invalid };
-GruPath gru_path(int64_t L) {
-    const char *env = getenv("PARARNN_GRU_PATH");
+// Path of a Newton forward.  The GRU takes the fused on-chip kernel while
+// the sequence fits one workgroup's registers; longer sequences (and the
+// LSTM) take the chained kernel, which keeps each chunk on chip for all its
+// iterations.  The per-iteration launches remain selectable:
+// PARARNN_GRU_PATH=fused|chain|step and PARARNN_LSTM_PATH=chain|step
+// override the choice (for testing every path).
+enum class Path { Fused, Chain, Step, Invalid };
+Path env_path(const char *name) {
+    const char *env = getenv(name);
+    if (env == nullptr) return Path::Invalid;
+    if (strcmp(env, "fused") == 0) return Path::Fused;
+    if (strcmp(env, "chain") == 0) return Path::Chain;
+    if (strcmp(env, "step") == 0) return Path::Step;
+    return Path::Invalid;
+}
+Path gru_path(int64_t L) {
     const bool fits = fused_c_for(L) != 0;
-    if (env != nullptr && strcmp(env, "step") == 0) return GruPath::Step;
-    if (env != nullptr && strcmp(env, "fused") == 0) return fits ? GruPath::Fused : GruPath::Invalid;
-    return fits ? GruPath::Fused : GruPath::Step;
+    const Path p = env_path("PARARNN_GRU_PATH");
+    if (p == Path::Fused) return fits ? Path::Fused : Path::Invalid;
+    if (p == Path::Chain || p == Path::Step) return p;
+    return fits ? Path::Fused : Path::Chain;
+}
+Path lstm_path() {
+    const Path p = env_path("PARARNN_LSTM_PATH");
+    return p == Path::Step ? Path::Step : Path::Chain;
 }
 
 }  // namespace
@@ -67,10 +85,10 @@ size_t pararnn_workspace_bytes(int32_t op, int64_t B, int64_t L, int64_t H, int3
         case PARARNN_OP_LINSCAN_BLK2: return scan_ws(kCfgLinBlk2, 2, B, L, H).total;
         case PARARNN_OP_GRU_FORWARD:
             if (max_iter < 1) return 0;
-            return gru_step_ws(B, L, H, max_iter);
+            return gru_fwd_ws(B, L, H, max_iter);
         case PARARNN_OP_LSTM_FORWARD:
             if (max_iter < 1) return 0;
-            return lstm_step_ws(B, L, H, max_iter);
+            return lstm_fwd_ws(B, L, H, max_iter);
         case PARARNN_OP_GRU_ADJOINT: return gru_adjoint_ws(B, L, H);
         case PARARNN_OP_LSTM_ADJOINT: return lstm_adjoint_ws(B, L, H);
         default: return 0;
@@ -105,17 +123,19 @@ int pararnn_gru_forward(int64_t B, int64_t L, int64_t H, const float *pz, const 
     if (!(tol >= 0.0f) || max_iter < 1) return PARARNN_ERR_INVALID;  // rejects NaN too
     GruFwdArgs a{B, L, H, pz, pr, pc, uz, ur, uc, h0, h, tol, max_iter, info, trace};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    switch (gru_path(L)) {
-        case GruPath::Fused:
-            if (!grid_ok(B * ((H + kFusedChannels - 1) / kFusedChannels))) return PARARNN_ERR_INVALID;
-            return status_of(gru_forward_fused(a, s));
-        case GruPath::Step:
-            if (!ws || ws_bytes < gru_step_ws(B, L, H, max_iter) || !aligned(ws, 256))
-                return PARARNN_ERR_INVALID;
-            if (!grid_ok(scan_shape(kCfgGruStep, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
-            return status_of(gru_forward_step(a, static_cast<char *>(ws), s));
-        default: return PARARNN_ERR_UNSUPPORTED;
+    const Path path = gru_path(L);
+    if (path == Path::Fused) {
+        if (!grid_ok(B * ((H + kFusedChannels - 1) / kFusedChannels))) return PARARNN_ERR_INVALID;
+        return status_of(gru_forward_fused(a, s));
     }
+    if (path == Path::Invalid) return PARARNN_ERR_UNSUPPORTED;
+    if (!ws || ws_bytes < gru_fwd_ws(B, L, H, max_iter) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+    if (path == Path::Chain) {
+        if (!grid_ok(scan_shape(kCfgGruChain, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+        return status_of(gru_forward_chain(a, static_cast<char *>(ws), s));
+    }
+    if (!grid_ok(scan_shape(kCfgGruStep, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+    return status_of(gru_forward_step(a, static_cast<char *>(ws), s));
 }
 
 int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H, const float *pi, const float *pf,
@@ -126,10 +146,15 @@ int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H, const float *pi, const
     if (!dims_ok(B, L, H) || !pi || !pf || !po || !pg || !ui || !uf || !uo || !ug || !h || !c)
         return PARARNN_ERR_INVALID;
     if (!(tol >= 0.0f) || max_iter < 1) return PARARNN_ERR_INVALID;
-    if (!ws || ws_bytes < lstm_step_ws(B, L, H, max_iter) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
-    if (!grid_ok(scan_shape(kCfgLstmStep, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+    if (!ws || ws_bytes < lstm_fwd_ws(B, L, H, max_iter) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
     LstmFwdArgs a{B, L, H, pi, pf, po, pg, ui, uf, uo, ug, h0, c0, h, c, tol, max_iter, info, trace};
-    return status_of(lstm_forward_step(a, static_cast<char *>(ws), static_cast<hipStream_t>(stream)));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (lstm_path() == Path::Chain) {
+        if (!grid_ok(scan_shape(kCfgLstmChain, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+        return status_of(lstm_forward_chain(a, static_cast<char *>(ws), s));
+    }
+    if (!grid_ok(scan_shape(kCfgLstmStep, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+    return status_of(lstm_forward_step(a, static_cast<char *>(ws), s));
 }
 
 int pararnn_adjoint_backward(int32_t cell, int64_t B, int64_t L, int64_t H, const float *const *p,

@@ -43,6 +43,7 @@ struct GruFwdArgs {
 };
 hipError_t gru_forward_step(const GruFwdArgs &a, char *ws, hipStream_t s);
 hipError_t gru_forward_fused(const GruFwdArgs &a, hipStream_t s);
+hipError_t gru_forward_chain(const GruFwdArgs &a, char *ws, hipStream_t s);
 
 struct LstmFwdArgs {
     int64_t B, L, H;
@@ -54,6 +55,7 @@ struct LstmFwdArgs {
     float *trace;
 };
 hipError_t lstm_forward_step(const LstmFwdArgs &a, char *ws, hipStream_t s);
+hipError_t lstm_forward_chain(const LstmFwdArgs &a, char *ws, hipStream_t s);
 
 struct AdjArgs {
     int64_t B, L, H;

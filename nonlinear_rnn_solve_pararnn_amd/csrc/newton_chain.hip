@@ -1,0 +1,630 @@
+// newton_chain.hip -- Newton's method for sequences longer than one workgroup
+// holds, with every chunk kept on chip for all of its iterations (ParaRNN
+// page, Fig. 5: the fully fused modality, extended here past one
+// workgroup's reach).
+//
+// A tile is one chunk of T positions (of 64 channels, or of one channel for
+// small H).  Its workgroup loads the gate inputs once and then runs Newton
+// iterations k = 1, 2, ... on registers:
+//   - the state before the chunk at iterate k-1 is the last state the
+//     previous chunk published for iteration k-1 (h0 for the first chunk);
+//   - the cells give J_t and beta_t = F_t - s_t, composed per sub-chunk and
+//     scanned inside the workgroup;
+//   - the delta entering the chunk at iteration k comes from a decoupled
+//     look-back over the previous chunks' iteration-k records;
+//   - s += delta, and the chunk publishes its iteration-k records (aggregate,
+//     inclusive delta, last state).
+// A chunk stops after iteration k once max|delta| <= tol over it and every
+// chunk before it (a prefix AND of per-chunk flags, found by a second
+// look-back), so the last chunk stops exactly when global Newton over the
+// sequence would.  A stopped chunk's states are frozen: later iterations of
+// its successors take a zero delta and its last state from it.  With
+// tol = 0 no chunk stops before the cap and every iterate equals global
+// Newton's.
+//
+// Every wait is on a chunk with a smaller ticket, whose workgroup is already
+// running (tickets are drawn by running workgroups, in sequence order), so
+// the waits end; they are bounded anyway (kMaxPolls, then NaN).
+// The records of each iteration live in their own slice of the workspace,
+// written once per launch with launch tags (common.hpp); a chunk may run
+// several iterations ahead of its successor.
+#include "cells.hpp"
+#include "launch.hpp"
+#include "scan_core.hpp"
+
+namespace prn {
+
+struct ChainGeo {
+    int64_t B, L, H, ncb, nq, ntiles, ndesc;
+    int32_t cap;
+    float tol;
+    uint64_t *hdr;
+    uint64_t *agg, *inc, *bnd;  // [cap][ndesc][words]: iteration k at slice k-1
+    uint64_t *stop;             // [ntiles]: last iteration of the tile (tagged)
+    uint64_t *fagg, *finc;      // [cap][ntiles]: converged flag of the tile, and of it and all before it
+    int32_t *info;
+    uint32_t *trace;
+};
+
+// ---------------------------------------------------------------- cells
+namespace {
+constexpr float kE1 = -kLog2e, kE2 = -2.0f * kLog2e;
+}
+
+// GRU-style cell on pre-scaled gate inputs (pz, pr by -log2 e, pc by
+// -2 log2 e), the same arithmetic as the fused kernel.
+struct GruChain {
+    static constexpr int S = 1, NG = 3;
+    const float *pz, *pr, *pc, *uz, *ur, *uc, *h0;
+    float *h;
+    bool runs;  // H == 1 with 16-byte aligned rows: whole runs move as float4
+
+    struct W {
+        float uz, ur, uc, uzs, urs, ucs;
+    };
+    __device__ W weights(int64_t j, bool ok) const {
+        W w{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        if (ok) {
+            w.uz = uz[j];
+            w.ur = ur[j];
+            w.uc = uc[j];
+            w.uzs = kE1 * w.uz;
+            w.urs = kE1 * w.ur;
+            w.ucs = kE2 * w.uc;
+        }
+        return w;
+    }
+    __device__ float init(int64_t b, int64_t j, int64_t H) const {
+        return h0 != nullptr ? h0[b * H + j] : 0.0f;
+    }
+    template <int C>
+    __device__ void load(int64_t base, int64_t H, const bool (&val)[C], bool whole, float (&x)[NG][C]) const {
+        if constexpr (C % 4 == 0) {
+            if (runs && whole) {
+                load_run<C>(pz + base, x[0]);
+                load_run<C>(pr + base, x[1]);
+                load_run<C>(pc + base, x[2]);
+#pragma unroll
+                for (int i = 0; i < C; ++i) {
+                    x[0][i] *= kE1;
+                    x[1][i] *= kE1;
+                    x[2][i] *= kE2;
+                }
+                return;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            x[0][i] = val[i] ? kE1 * pz[base + i * H] : 0.0f;
+            x[1][i] = val[i] ? kE1 * pr[base + i * H] : 0.0f;
+            x[2][i] = val[i] ? kE2 * pc[base + i * H] : 0.0f;
+        }
+    }
+    // Newton map of one position: delta -> J delta + (F - s), F and J at hp.
+    __device__ Aff1 step(const W &w, float hp, float xz, float xr, float xc, float s) const {
+        const float z = fast_rcp(1.0f + fast_exp2(fmaf(w.uzs, hp, xz)));
+        const float r = fast_rcp(1.0f + fast_exp2(fmaf(w.urs, hp, xr)));
+        const float sc = fast_rcp(1.0f + fast_exp2(fmaf(w.ucs, r * hp, xc)));
+        const float c = fmaf(2.0f, sc, -1.0f);
+        const float cmh = c - hp;
+        const float F = fmaf(z, cmh, hp);
+        const float omz = 1.0f - z;
+        const float omc2 = fmaf(-c, c, 1.0f);
+        const float drh = fmaf(hp * fmaf(-r, r, r), w.ur, r);
+        const float inner = fmaf(omz * w.uz, cmh, (omc2 * w.uc) * drh);
+        return {fmaf(z, inner, omz), F - s};
+    }
+    template <int C>
+    __device__ void store(int64_t base, int64_t H, const bool (&val)[C], bool whole, const float (&s)[C]) const {
+        if constexpr (C % 4 == 0) {
+            if (runs && whole) {
+                store_run<C>(h + base, s);
+                return;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i)
+            if (val[i]) h[base + i * H] = s[i];
+    }
+};
+
+// LSTM-style cell; state (c, h) as (x, y).
+struct LstmChain {
+    static constexpr int S = 2, NG = 4;
+    const float *pi, *pf, *po, *pg, *ui, *uf, *uo, *ug, *h0, *c0;
+    float *h, *c;
+    bool runs;  // unused: the LSTM moves scalars
+
+    struct W {
+        float ui, uf, uo, ug;
+    };
+    __device__ W weights(int64_t j, bool ok) const {
+        if (!ok) return {0.0f, 0.0f, 0.0f, 0.0f};
+        return {ui[j], uf[j], uo[j], ug[j]};
+    }
+    __device__ float2s init(int64_t b, int64_t j, int64_t H) const {
+        return {c0 != nullptr ? c0[b * H + j] : 0.0f, h0 != nullptr ? h0[b * H + j] : 0.0f};
+    }
+    template <int C>
+    __device__ void load(int64_t base, int64_t H, const bool (&val)[C], bool, float (&x)[NG][C]) const {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            x[0][i] = val[i] ? pi[base + i * H] : 0.0f;
+            x[1][i] = val[i] ? pf[base + i * H] : 0.0f;
+            x[2][i] = val[i] ? po[base + i * H] : 0.0f;
+            x[3][i] = val[i] ? pg[base + i * H] : 0.0f;
+        }
+    }
+    __device__ Aff2 step(const W &w, float2s hp, float xi, float xf, float xo, float xg, float2s s) const {
+        const Lstm2 r = lstm_f_j(hp.x, hp.y, xi, xf, xo, xg, w.ui, w.uf, w.uo, w.ug);
+        return {r.j00, r.j01, r.j10, r.j11, r.Fc - s.x, r.Fh - s.y};
+    }
+    template <int C>
+    __device__ void store(int64_t base, int64_t H, const bool (&val)[C], bool, const float2s (&s)[C]) const {
+#pragma unroll
+        for (int i = 0; i < C; ++i)
+            if (val[i]) {
+                c[base + i * H] = s[i].x;
+                h[base + i * H] = s[i].y;
+            }
+    }
+};
+
+template <class Cell, int C>
+__device__ __forceinline__ typename MonoidT<Cell::S>::Map
+cell_step(const Cell &cell, const typename Cell::W &w, typename MonoidT<Cell::S>::State hp,
+          const float (&x)[Cell::NG][C], int i, typename MonoidT<Cell::S>::State s) {
+    if constexpr (Cell::NG == 3)
+        return cell.step(w, hp, x[0][i], x[1][i], x[2][i], s);
+    else
+        return cell.step(w, hp, x[0][i], x[1][i], x[2][i], x[3][i], s);
+}
+
+// ---------------------------------------------------------------- records
+__device__ __forceinline__ bool stopped_before(const ChainGeo &g, int64_t ptile, uint32_t tag, int k,
+                                               int *at = nullptr) {
+    const uint64_t w = ld_coherent(g.stop + ptile);
+    if (!has_tag(w, tag)) return false;
+    const int s = (int)lo_f(w);
+    if (at != nullptr) *at = s;
+    return s < k;
+}
+
+// Last state of chunk p at iterate kk (kk >= 1), or its final state if it
+// stopped before kk.
+template <int S>
+__device__ typename MonoidT<S>::State chain_boundary(const ChainGeo &g, uint32_t tag, int kk, int64_t d,
+                                                     int64_t ptile) {
+    using D = Desc<S>;
+    typename MonoidT<S>::State x;
+    int at = kk;
+    for (uint32_t polls = 0; polls < kMaxPolls; ++polls) {
+        if (D::get_inc(g.bnd + ((size_t)(at - 1) * g.ndesc + d) * D::kIncWords, x, tag)) return x;
+        if (at == kk) {
+            int s;
+            if (stopped_before(g, ptile, tag, kk, &s)) at = s;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return nan_state<S>();
+}
+
+// Delta entering chunk q at iteration k for one channel lane.
+template <int S>
+__device__ typename MonoidT<S>::State chain_lane_lookback(const ChainGeo &g, uint32_t tag, int k,
+                                                          int64_t q, int64_t b, int64_t cb,
+                                                          int64_t slot) {
+    using M = MonoidT<S>;
+    using D = Desc<S>;
+    const size_t kofs = (size_t)(k - 1) * g.ndesc;
+    const int64_t stride = g.B * g.H;
+    typename M::Map acc = M::id();
+    int64_t p = q - 1;
+    uint32_t idle = 0;
+    while (p >= 0) {
+        const int64_t d = p * stride + slot;
+        typename M::State x;
+        typename M::Map m;
+        if (D::get_inc(g.inc + (kofs + d) * D::kIncWords, x, tag)) return M::apply(acc, x);
+        if (D::get_agg(g.agg + (kofs + d) * D::kAggWords, m, tag)) {
+            acc = M::then(m, acc);
+            --p;
+            idle = 0;
+            continue;
+        }
+        if (stopped_before(g, (p * g.B + b) * g.ncb + cb, tag, k)) break;  // frozen prefix: zero delta
+        if (++idle >= kMaxPolls) return nan_state<S>();
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return M::apply(acc, M::zero());
+}
+
+// Time lanes: the holder wave polls 64 predecessors at once (lane i polls
+// chunk q-1-i) and folds them with shuffles.  Called by every lane of one wave.
+template <int S>
+__device__ typename MonoidT<S>::State chain_wave_lookback(const ChainGeo &g, uint32_t tag, int k,
+                                                          int64_t q, int64_t b, int64_t cb,
+                                                          int64_t slot) {
+    using M = MonoidT<S>;
+    using D = Desc<S>;
+    const int lane = threadIdx.x & 63;
+    const size_t kofs = (size_t)(k - 1) * g.ndesc;
+    const int64_t stride = g.B * g.H;
+    typename M::Map acc_total = M::id();
+    for (int64_t pbase = q - 1;; pbase -= 64) {
+        const int64_t p = pbase - lane;
+        LbPart<S> part = {M::id(), M::zero(), 1};  // before chunk 0: zero delta
+        if (p >= 0) {
+            const int64_t d = p * stride + slot;
+            for (uint32_t polls = 0;; ++polls) {
+                typename M::State x;
+                typename M::Map m;
+                if (D::get_inc(g.inc + (kofs + d) * D::kIncWords, x, tag)) { part = {M::id(), x, 1}; break; }
+                if (D::get_agg(g.agg + (kofs + d) * D::kAggWords, m, tag)) { part = {m, M::zero(), 0}; break; }
+                if (stopped_before(g, (p * g.B + b) * g.ncb + cb, tag, k)) { part = {M::id(), M::zero(), 1}; break; }
+                if (polls >= kMaxPolls) {
+                    part = {M::id(), nan_state<S>(), 1};
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+#pragma unroll
+        for (int dd = 1; dd < 64; dd <<= 1) {
+            LbPart<S> far;
+            far.acc = shfl_down_m(part.acc, dd);
+            far.x = shfl_down_s(part.x, dd);
+            far.found = __shfl_down(part.found, dd, 64);
+            if (lane + dd < 64) part = lb_combine<S>(part, far);
+        }
+        if (__shfl(part.found, 0, 64)) return M::apply(acc_total, bcast0_s(part.x));
+        acc_total = M::then(bcast0_m(part.acc), acc_total);
+    }
+}
+
+// Whether every chunk before q (same batch row and channel block) had
+// max|delta| <= tol at iteration k.  Called by every lane of one wave: lane i
+// polls chunk q-1-i for its prefix flag (inclusive), its own flag
+// (aggregate) or a stop before k (frozen, so converged); the nearest
+// inclusive answer and every own flag nearer than it decide, and a false
+// own flag decides at once.
+__device__ bool chain_flag_lookback(const ChainGeo &g, uint32_t tag, int k, int64_t q, int64_t b, int64_t cb) {
+    const int lane = threadIdx.x & 63;
+    const size_t kofs = (size_t)(k - 1) * g.ntiles;
+    for (int64_t pbase = q - 1;; pbase -= 64) {
+        const int64_t p = pbase - lane;
+        int st = 3;  // 0 own false, 1 own true, 2 prefix false, 3 prefix true (or before chunk 0)
+        if (p >= 0) {
+            const int64_t pt = (p * g.B + b) * g.ncb + cb;
+            for (uint32_t polls = 0;; ++polls) {
+                const uint64_t wi = ld_coherent(g.finc + kofs + pt);
+                if (has_tag(wi, tag)) {
+                    st = lo_f(wi) != 0.0f ? 3 : 2;
+                    break;
+                }
+                const uint64_t wa = ld_coherent(g.fagg + kofs + pt);
+                if (has_tag(wa, tag)) {
+                    st = lo_f(wa) != 0.0f ? 1 : 0;
+                    break;
+                }
+                if (stopped_before(g, pt, tag, k)) {
+                    st = 3;
+                    break;
+                }
+                if (polls >= kMaxPolls) {
+                    st = 2;  // gave up: report not converged
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        const uint64_t incl = __ballot(st >= 2);
+        const uint64_t bad = __ballot(st == 0 || st == 2);
+        if (incl != 0) {
+            const int first = __ffsll((unsigned long long)incl) - 1;
+            const uint64_t upto = first == 63 ? ~0ull : ((1ull << (first + 1)) - 1);
+            return (bad & upto) == 0;
+        }
+        if (bad != 0) return false;
+    }
+}
+
+__device__ __forceinline__ float2s shfl_up_s(float2s x, int d) {
+    return {__shfl_up(x.x, d, 64), __shfl_up(x.y, d, 64)};
+}
+__device__ __forceinline__ float shfl_up_s(float x, int d) { return __shfl_up(x, d, 64); }
+
+__device__ __forceinline__ uint32_t state_abs_max(float d) { return abs_bits(d); }
+__device__ __forceinline__ uint32_t state_abs_max(float2s d) {
+    const uint32_t a = abs_bits(d.x), b = abs_bits(d.y);
+    return a > b ? a : b;
+}
+__device__ __forceinline__ float state_add(float a, float b) { return a + b; }
+__device__ __forceinline__ float2s state_add(float2s a, float2s b) { return {a.x + b.x, a.y + b.y}; }
+
+// ---------------------------------------------------------------- tile
+template <class Cell, int NW, int C, bool CL>
+__device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, uint32_t tag) {
+    constexpr int S = Cell::S;
+    using M = MonoidT<S>;
+    using D = Desc<S>;
+    using Map = typename M::Map;
+    using State = typename M::State;
+    constexpr int NT = NW * 64;
+    constexpr int64_t T = CL ? (int64_t)NW * C : (int64_t)NT * C;
+
+    __shared__ Map s_part[CL ? NT : NW];
+    __shared__ State s_carry[CL ? 64 : 1];
+    __shared__ State s_last[CL ? NT : NW];
+    __shared__ uint32_t s_wmax[NW];
+    __shared__ int s_stop;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t per_q = g.B * g.ncb;
+    const int64_t q = ticket / per_q;
+    const int64_t rest = ticket - q * per_q;
+    const int64_t b = rest / g.ncb;
+    const int64_t cb = rest - b * g.ncb;
+    const int64_t j = CL ? cb * 64 + lane : cb;
+    const int sub = CL ? w : tid;
+    const bool ok = j < g.H;
+    const int64_t pos0 = q * T + (int64_t)sub * C;
+    const int64_t base = idx3(b, pos0, ok ? j : 0, g.L, g.H);
+    const int64_t stride = g.B * g.H, slot = b * g.H + j;
+    const int64_t dsc = q * stride + slot;
+    const int64_t ptile = ((q - 1) * g.B + b) * g.ncb + cb;
+    const bool holder = CL ? (w == NW - 1) : (tid == NT - 1);
+
+    bool val[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) val[i] = ok && pos0 + i < g.L;
+    const bool whole = ok && pos0 + C <= g.L;
+    float x[Cell::NG][C];
+    cell.template load<C>(base, g.H, val, whole, x);
+    const typename Cell::W wts = cell.weights(j, ok);
+    State s[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) s[i] = M::zero();
+    const State init = (ok && q == 0 && sub == 0) ? cell.init(b, j, g.H) : M::zero();
+
+    int k = 1;
+    bool conv = false;
+    for (;; ++k) {
+        // state before this thread's first position, at iterate k-1
+        State hp = M::zero();
+        State nb = M::zero();
+        if (!CL) nb = shfl_up_s(s[C - 1], 1);  // every lane active for the shuffle
+        if (sub == 0) {
+            if (q == 0)
+                hp = init;
+            else if (k > 1 && ok)
+                hp = chain_boundary<S>(g, tag, k - 1, dsc - stride, ptile);
+        } else if (k > 1) {
+            if (CL)
+                hp = s_last[(w - 1) * 64 + lane];
+            else
+                hp = lane == 0 ? s_last[w - 1] : nb;
+        }
+
+        Map e[C];
+        Map acc = M::id();
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            e[i] = val[i] ? cell_step<Cell, C>(cell, wts, hp, x, i, s[i]) : M::id();
+            hp = s[i];
+            acc = M::then(acc, e[i]);
+        }
+
+        // exclusive prefix of this sub-chunk inside the chunk, and the chunk aggregate
+        Map ex, tot;
+        if (CL) {
+            s_part[w * 64 + lane] = acc;
+            __syncthreads();
+            ex = M::id();
+            for (int kk = 0; kk < w; ++kk) ex = M::then(ex, s_part[kk * 64 + lane]);
+            tot = M::then(ex, acc);
+        } else {
+            Map incl = acc;
+#pragma unroll
+            for (int dd = 1; dd < 64; dd <<= 1) {
+                const Map o = M::shfl_up(incl, dd);
+                if (lane >= dd) incl = M::then(o, incl);
+            }
+            Map exw = M::shfl_up(incl, 1);
+            if (lane == 0) exw = M::id();
+            if (lane == 63) s_part[w] = incl;
+            __syncthreads();
+            Map pre = M::id();
+            for (int kk = 0; kk < w; ++kk) pre = M::then(pre, s_part[kk]);
+            ex = M::then(pre, exw);
+            tot = M::then(pre, incl);
+        }
+
+        // delta entering the chunk at iteration k
+        const size_t kofs = (size_t)(k - 1) * g.ndesc;
+        if (CL) {
+            if (holder) {
+                State din = M::zero();
+                if (ok) {
+                    if (q > 0) {
+                        D::put_agg(g.agg + (kofs + dsc) * D::kAggWords, tot, tag);
+                        din = chain_lane_lookback<S>(g, tag, k, q, b, cb, slot);
+                    }
+                    D::put_inc(g.inc + (kofs + dsc) * D::kIncWords, M::apply(tot, din), tag);
+                }
+                s_carry[lane] = din;
+            }
+        } else if (w == NW - 1) {
+            State din = M::zero();
+            if (q > 0) {
+                if (holder) D::put_agg(g.agg + (kofs + dsc) * D::kAggWords, tot, tag);
+                din = chain_wave_lookback<S>(g, tag, k, q, b, cb, slot);
+            }
+            if (holder) {
+                D::put_inc(g.inc + (kofs + dsc) * D::kIncWords, M::apply(tot, din), tag);
+                s_carry[0] = din;
+            }
+        }
+        __syncthreads();
+
+        // apply: delta through the sub-chunk, s += delta
+        State dlt = M::apply(ex, s_carry[CL ? lane : 0]);
+        uint32_t mx = 0;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            if (val[i]) {
+                dlt = M::apply(e[i], dlt);
+                s[i] = state_add(s[i], dlt);
+                const uint32_t a = state_abs_max(dlt);
+                mx = a > mx ? a : mx;
+            }
+        }
+        mx = clamp_nan_to_inf(mx);
+        if (holder && ok && q + 1 < g.nq) D::put_inc(g.bnd + (kofs + dsc) * D::kIncWords, s[C - 1], tag);
+        if (CL)
+            s_last[w * 64 + lane] = s[C - 1];
+        else if (lane == 63)
+            s_last[w] = s[C - 1];
+        mx = wave_max_u32(mx);
+        if (lane == 0) s_wmax[w] = mx;
+        __syncthreads();
+        uint32_t m = 0;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) m = s_wmax[ww] > m ? s_wmax[ww] : m;
+        // stop once this chunk and every chunk before it have converged
+        if (w == 0) {
+            const bool own = __uint_as_float(m) <= g.tol;
+            const size_t fofs = (size_t)(k - 1) * g.ntiles + ticket;
+            if (lane == 0) {
+                st_coherent(g.fagg + fofs, tagged(own ? 1.0f : 0.0f, tag));
+                if (g.trace != nullptr) {
+                    const uint32_t cur = __hip_atomic_load(g.trace + (k - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (m > cur)
+                        __hip_atomic_fetch_max(g.trace + (k - 1), m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+            bool prefix = own;
+            if (own && q > 0) prefix = chain_flag_lookback(g, tag, k, q, b, cb);
+            if (lane == 0) {
+                if (own) st_coherent(g.finc + fofs, tagged(prefix ? 1.0f : 0.0f, tag));
+                s_stop = prefix ? 1 : 0;
+            }
+        }
+        __syncthreads();
+        conv = s_stop != 0;
+        if (conv || k >= g.cap) break;
+    }
+    if (tid == 0) st_coherent(g.stop + ticket, tagged((float)k, tag));
+    cell.template store<C>(base, g.H, val, whole, s);
+    if (tid == 0 && g.info != nullptr) {
+        if (k > __hip_atomic_load(g.info, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+            __hip_atomic_fetch_max(g.info, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!conv && __hip_atomic_load(g.info + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+            __hip_atomic_store(g.info + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <class Cell, int NW, int C, bool CL>
+__global__ __launch_bounds__(NW * 64) void newton_chain_kernel(Cell cell, ChainGeo g) {
+    __shared__ Ticket s_ticket;
+    const bool persistent = (int64_t)gridDim.x < g.ntiles;
+    const uint32_t draws = (uint32_t)(persistent ? g.ntiles + gridDim.x : g.ntiles);
+    for (;;) {
+        if (threadIdx.x == 0) s_ticket = draw_ticket(g.hdr, draws);
+        __syncthreads();
+        const Ticket t = s_ticket;
+        if (t.index >= g.ntiles) return;
+        chain_tile<Cell, NW, C, CL>(cell, g, t.index, t.tag);
+        if (!persistent) return;
+        __syncthreads();  // the tile's last reads of shared memory before the next ticket
+    }
+}
+
+template <class Cell, int NW, int C, bool CL>
+static hipError_t launch_chain(const Cell &cell, const ChainGeo &g, hipStream_t s) {
+    static int per_cu = 0;
+    if (per_cu == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, newton_chain_kernel<Cell, NW, C, CL>, NW * 64, 0) !=
+                hipSuccess || n <= 0)
+            n = 1;
+        per_cu = n;
+    }
+    const int64_t slots = (int64_t)per_cu * device_cu_count();
+    const int64_t grid = g.ntiles < slots ? g.ntiles : slots;
+    hipLaunchKernelGGL((newton_chain_kernel<Cell, NW, C, CL>), dim3((unsigned)grid), dim3(NW * 64), 0, s, cell, g);
+    return hipGetLastError();
+}
+
+template <class Cell, int NWC, int CC, int NWT, int CT>
+static hipError_t chain_forward(const TileCfg &cfg, const Cell &cell, int64_t B, int64_t L, int64_t H,
+                                int32_t cap, float tol, int32_t *info, float *trace, char *ws, hipStream_t s) {
+    const ChainWs w = chain_ws(cfg, Cell::S, B, L, H, cap);
+    FillRange fr[3] = {
+        {info, info ? 1ull : 0ull, 0, 4},                         // iterations = 0
+        {info ? info + 1 : nullptr, info ? 1ull : 0ull, 1, 4},    // converged = 1
+        {trace, trace ? (uint64_t)cap : 0ull, 0, 4},
+    };
+    hipError_t e = fill(fr, 3, s);
+    if (e != hipSuccess) return e;
+    ChainGeo g;
+    g.B = B;
+    g.L = L;
+    g.H = H;
+    g.ncb = w.sh.ncb;
+    g.nq = w.sh.nq;
+    g.ntiles = w.sh.ntiles;
+    g.ndesc = w.sh.ndesc;
+    g.cap = cap;
+    g.tol = tol;
+    g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
+    g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
+    g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
+    g.bnd = reinterpret_cast<uint64_t *>(ws + w.bnd);
+    g.stop = reinterpret_cast<uint64_t *>(ws + w.stop);
+    g.fagg = reinterpret_cast<uint64_t *>(ws + w.fagg);
+    g.finc = reinterpret_cast<uint64_t *>(ws + w.finc);
+    g.info = info;
+    g.trace = reinterpret_cast<uint32_t *>(trace);
+    return w.sh.channel_lanes ? launch_chain<Cell, NWC, CC, true>(cell, g, s)
+                              : launch_chain<Cell, NWT, CT, false>(cell, g, s);
+}
+
+hipError_t gru_forward_chain(const GruFwdArgs &a, char *ws, hipStream_t s) {
+    GruChain cell;
+    cell.pz = a.pz;
+    cell.pr = a.pr;
+    cell.pc = a.pc;
+    cell.uz = a.uz;
+    cell.ur = a.ur;
+    cell.uc = a.uc;
+    cell.h0 = a.h0;
+    cell.h = a.h;
+    cell.runs = a.H == 1 && a.L % 4 == 0 && aligned16(a.pz) && aligned16(a.pr) && aligned16(a.pc) &&
+                aligned16(a.h);
+    constexpr TileCfg c = kCfgGruChain;
+    return chain_forward<GruChain, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, cell, a.B, a.L, a.H, a.cap, a.tol,
+                                                                    a.info, a.trace, ws, s);
+}
+
+hipError_t lstm_forward_chain(const LstmFwdArgs &a, char *ws, hipStream_t s) {
+    LstmChain cell;
+    cell.pi = a.pi;
+    cell.pf = a.pf;
+    cell.po = a.po;
+    cell.pg = a.pg;
+    cell.ui = a.ui;
+    cell.uf = a.uf;
+    cell.uo = a.uo;
+    cell.ug = a.ug;
+    cell.h0 = a.h0;
+    cell.c0 = a.c0;
+    cell.h = a.h;
+    cell.c = a.c;
+    cell.runs = false;
+    constexpr TileCfg c = kCfgLstmChain;
+    return chain_forward<LstmChain, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, cell, a.B, a.L, a.H, a.cap, a.tol,
+                                                                     a.info, a.trace, ws, s);
+}
+
+}  // namespace prn

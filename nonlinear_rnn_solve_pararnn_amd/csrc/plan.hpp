@@ -20,6 +20,8 @@ constexpr TileCfg kCfgGruStep{4, 16, 8, 16};
 constexpr TileCfg kCfgLstmStep{16, 8, 4, 8};
 constexpr TileCfg kCfgGruAdj{4, 8, 16, 8};
 constexpr TileCfg kCfgLstmAdj{4, 4, 4, 4};
+constexpr TileCfg kCfgGruChain{8, 16, 8, 16};
+constexpr TileCfg kCfgLstmChain{16, 8, 8, 8};
 constexpr int64_t kChannelLanesMinH = 32;
 // Look-back descriptors polled at once by one channel lane (diagonal, 2x2).
 constexpr int kLbBatchDiag = 2;
@@ -109,6 +111,29 @@ inline NewtonWs newton_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64
     w.agg = c.take((size_t)w.sh.ndesc * desc_agg_words(S) * 8);
     w.inc = c.take((size_t)w.sh.ndesc * desc_inc_words(S) * 8);
     for (int k = 0; k < 2; ++k) w.bnd[k] = c.take((size_t)w.sh.ndesc * S * 4);
+    w.total = c.off;
+    return w;
+}
+
+// Workspace of the chained Newton kernel: header, the records of every
+// iteration (aggregate, inclusive delta and last state of each chunk and
+// channel), a stop word per tile and per-iteration converged flags per tile.
+struct ChainWs {
+    ScanShape sh;
+    size_t hdr, agg, inc, bnd, stop, fagg, finc, total;
+};
+
+inline ChainWs chain_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64_t H, int32_t cap) {
+    ChainWs w;
+    w.sh = scan_shape(cfg, B, L, H);
+    Carve c;
+    w.hdr = c.take(8);
+    w.agg = c.take((size_t)cap * w.sh.ndesc * desc_agg_words(S) * 8);
+    w.inc = c.take((size_t)cap * w.sh.ndesc * desc_inc_words(S) * 8);
+    w.bnd = c.take((size_t)cap * w.sh.ndesc * desc_inc_words(S) * 8);
+    w.stop = c.take((size_t)w.sh.ntiles * 8);
+    w.fagg = c.take((size_t)cap * w.sh.ntiles * 8);
+    w.finc = c.take((size_t)cap * w.sh.ntiles * 8);
     w.total = c.off;
     return w;
 }

@@ -1,4 +1,5 @@
-"""GPU parity of the GRU Newton forward (both the fused on-chip path and the
+"""GPU parity of the GRU Newton forward (the fused on-chip path, the chained
+path that keeps every chunk on chip for all iterations, and the
 per-iteration path) against the fp64 oracle: the sequential rollout, and the
 oracle's own Newton iterates."""
 import numpy as np
@@ -9,7 +10,7 @@ from nonlinear_rnn_solve_pararnn_amd import api, synth
 from tests.gpu_helpers import (FWD_ATOL, ITER_ATOL, dev, gru_args, host, max_abs, say)
 
 pytestmark = pytest.mark.gpu
-PATHS = ["fused", "step"]
+PATHS = ["fused", "chain", "step"]
 
 
 def _run(d, tol, cap, with_h0=True, trace=False):
@@ -70,11 +71,12 @@ def test_shapes_match_rollout(orc, monkeypatch, path, B, L, H):
     assert max_abs(h, orc.gru_rollout(*gru_args(d), h0=d["h0"])) <= FWD_ATOL
 
 
+@pytest.mark.parametrize("path", ["chain", "step"])
 @pytest.mark.parametrize("B,L,H", [(2, 513, 20), (1, 5000, 3), (2, 700, 100), (3, 20000, 1),
-                                   (1, 12, 1), (2, 4098, 1), (2, 8192, 1)])
-def test_long_sequences_step_path(orc, monkeypatch, B, L, H):
-    monkeypatch.setenv("PARARNN_GRU_PATH", "step")
-    say("gru long", B, L, H)
+                                   (1, 12, 1), (2, 4098, 1), (2, 8192, 1), (2, 3000, 200)])
+def test_long_sequences(orc, monkeypatch, path, B, L, H):
+    monkeypatch.setenv("PARARNN_GRU_PATH", path)
+    say("gru long", path, B, L, H)
     d = synth.gru_inputs(B, L, H, seed=50 + H, h0=True)
     h, info = _run(d, 1e-5, 32)
     assert info[1] == 1
@@ -154,6 +156,7 @@ def test_invalid_arguments_raise():
 
 
 @pytest.mark.parametrize("path,B,L,H", [("step", 16, 20000, 1), ("step", 4, 3000, 256),
+                                        ("chain", 16, 20000, 1), ("chain", 4, 3000, 256),
                                         ("fused", 16, 512, 1024)])
 def test_trace_equals_oracle_newton_trace(orc, monkeypatch, path, B, L, H):
     """max|delta| of each iteration, reduced over thousands of workgroups on
@@ -178,5 +181,20 @@ def test_fused_full_tiles_with_h0_and_iterates(orc):
     for k in (1, 2, 3):
         h, info = _run(d, 0.0, k)
         s, it, conv, _ = orc.gru_newton(*gru_args(d), h0=d["h0"], tol=0.0, cap=k)
+        assert list(info) == [k, 0]
+        assert max_abs(h, s) <= ITER_ATOL, k
+
+
+@pytest.mark.parametrize("B,L,H", [(2, 1000, 40), (2, 20000, 1)])
+def test_chain_iterates_across_chunks(orc, monkeypatch, B, L, H):
+    """Chained path over several chunks (channel lanes: 128-position chunks;
+    time lanes: 8192): with tol = 0 no chunk stops early, so the k-th result
+    equals the oracle's k-th global Newton iterate."""
+    monkeypatch.setenv("PARARNN_GRU_PATH", "chain")
+    d = synth.gru_inputs(B, L, H, seed=66, h0=True)
+    for k in (1, 2, 3, 5):
+        h, info = _run(d, 0.0, k)
+        s, it, conv, _ = orc.gru_newton(*gru_args(d), h0=d["h0"], tol=0.0, cap=k)
+        say("chain", B, L, H, k, info, max_abs(h, s))
         assert list(info) == [k, 0]
         assert max_abs(h, s) <= ITER_ATOL, k

@@ -1,5 +1,6 @@
 """GPU parity of the LSTM Newton forward (2x2 block Jacobians) against the
-fp64 oracle."""
+fp64 oracle, on the chained path (each chunk on chip for all iterations) and
+on the per-iteration path."""
 import pytest
 import torch
 
@@ -7,6 +8,12 @@ from nonlinear_rnn_solve_pararnn_amd import api, synth
 from tests.gpu_helpers import FWD_ATOL, ITER_ATOL, dev, host, lstm_args, max_abs, say
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(params=["chain", "step"], autouse=True)
+def lstm_path(request, monkeypatch):
+    monkeypatch.setenv("PARARNN_LSTM_PATH", request.param)
+    return request.param
 
 
 def _run(d, tol, cap, with_init=True):
@@ -27,7 +34,8 @@ def test_iterates_match_oracle_newton(orc):
         assert max_abs(h, hr) <= ITER_ATOL and max_abs(c, cr) <= ITER_ATOL, k
 
 
-@pytest.mark.parametrize("B,L,H", [(1, 1, 1), (2, 100, 3), (3, 257, 70), (2, 3000, 1), (2, 700, 33)])
+@pytest.mark.parametrize("B,L,H", [(1, 1, 1), (2, 100, 3), (3, 257, 70), (2, 3000, 1), (2, 700, 33),
+                                   (2, 9000, 1)])
 def test_shapes_match_rollout(orc, B, L, H):
     say("lstm", B, L, H)
     d = synth.lstm_inputs(B, L, H, seed=71 + H, h0=True)
@@ -54,3 +62,15 @@ def test_workload_full(orc):
     eh, ec = max_abs(h, hr), max_abs(c, cr)
     say("iters", info, "err h", eh, "err c", ec)
     assert info[1] == 1 and eh <= FWD_ATOL and ec <= FWD_ATOL
+
+
+@pytest.mark.parametrize("B,L,H", [(2, 700, 40), (1, 9000, 2)])
+def test_iterates_across_chunks(orc, B, L, H):
+    """Several chunks per channel: with tol = 0 the k-th result equals the
+    oracle's k-th global Newton iterate on both paths."""
+    d = synth.lstm_inputs(B, L, H, seed=73, h0=True)
+    for k in (1, 2, 4):
+        h, c, info = _run(d, 0.0, k)
+        hr, cr, it, conv, _ = orc.lstm_newton(*lstm_args(d), h0=d["h0"], c0=d["c0"], tol=0.0, cap=k)
+        assert list(info) == [k, 0]
+        assert max_abs(h, hr) <= ITER_ATOL and max_abs(c, cr) <= ITER_ATOL, k
