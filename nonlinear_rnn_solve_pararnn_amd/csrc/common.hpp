@@ -220,6 +220,17 @@ __device__ __forceinline__ Ticket draw_ticket(uint64_t *hdr, uint32_t ntiles) {
 // instead of hanging the device.
 constexpr uint32_t kMaxPolls = 1u << 20;
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations but not for its outstanding global memory operations (loads
+// issued early stay in flight across it).  The empty asm statements keep the
+// compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left alone
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------- runs
 // C consecutive floats at a 16-byte aligned address, moved with one 16-byte
 // access per four floats: the sequence of a single channel (H = 1) walked by

@@ -40,17 +40,6 @@ struct FusedGruArgs {
     uint32_t *trace;
 };
 
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS
-// operations but not for its outstanding global memory operations.  The
-// empty asm statements keep the compiler from moving memory accesses across
-// the barrier.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt left alone
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // XCD-aware tile order: workgroups are dispatched round-robin over the 8 XCDs,
 // so give each XCD a contiguous run of tiles; neighbouring 16-channel tiles
 // share 128-byte lines and then share one L2.

@@ -181,6 +181,32 @@ cell_step(const Cell &cell, const typename Cell::W &w, typename MonoidT<Cell::S>
 }
 
 // ---------------------------------------------------------------- records
+// A state record read ahead of use: the loads are issued early (before the
+// cells of an iteration) and only looked at when the value is needed, so
+// their latency hides behind the arithmetic.  A record not yet published is
+// then polled as usual.
+template <int S>
+struct Ahead {
+    uint64_t w[S];
+    __device__ void issue(const uint64_t *p) {
+#pragma unroll
+        for (int k = 0; k < S; ++k) w[k] = ld_coherent(p + k);
+    }
+    __device__ bool get(typename MonoidT<S>::State &x, uint32_t tag) const;
+};
+template <>
+__device__ __forceinline__ bool Ahead<1>::get(float &x, uint32_t tag) const {
+    if (!has_tag(w[0], tag)) return false;
+    x = lo_f(w[0]);
+    return true;
+}
+template <>
+__device__ __forceinline__ bool Ahead<2>::get(float2s &x, uint32_t tag) const {
+    if (!has_tag(w[0], tag) || !has_tag(w[1], tag)) return false;
+    x = {lo_f(w[0]), lo_f(w[1])};
+    return true;
+}
+
 __device__ __forceinline__ bool stopped_before(const ChainGeo &g, int64_t ptile, uint32_t tag, int k,
                                                int *at = nullptr) {
     const uint64_t w = ld_coherent(g.stop + ptile);
@@ -194,9 +220,10 @@ __device__ __forceinline__ bool stopped_before(const ChainGeo &g, int64_t ptile,
 // stopped before kk.
 template <int S>
 __device__ typename MonoidT<S>::State chain_boundary(const ChainGeo &g, uint32_t tag, int kk, int64_t d,
-                                                     int64_t ptile) {
+                                                     int64_t ptile, const Ahead<S> &ahead) {
     using D = Desc<S>;
     typename MonoidT<S>::State x;
+    if (ahead.get(x, tag)) return x;
     int at = kk;
     for (uint32_t polls = 0; polls < kMaxPolls; ++polls) {
         if (D::get_inc(g.bnd + ((size_t)(at - 1) * g.ndesc + d) * D::kIncWords, x, tag)) return x;
@@ -213,9 +240,13 @@ __device__ typename MonoidT<S>::State chain_boundary(const ChainGeo &g, uint32_t
 template <int S>
 __device__ typename MonoidT<S>::State chain_lane_lookback(const ChainGeo &g, uint32_t tag, int k,
                                                           int64_t q, int64_t b, int64_t cb,
-                                                          int64_t slot) {
+                                                          int64_t slot, const Ahead<S> &ahead) {
     using M = MonoidT<S>;
     using D = Desc<S>;
+    {
+        typename M::State x;
+        if (ahead.get(x, tag)) return x;  // the previous chunk's inclusive delta, read ahead
+    }
     const size_t kofs = (size_t)(k - 1) * g.ndesc;
     const int64_t stride = g.B * g.H;
     typename M::Map acc = M::id();
@@ -244,7 +275,7 @@ __device__ typename MonoidT<S>::State chain_lane_lookback(const ChainGeo &g, uin
 template <int S>
 __device__ typename MonoidT<S>::State chain_wave_lookback(const ChainGeo &g, uint32_t tag, int k,
                                                           int64_t q, int64_t b, int64_t cb,
-                                                          int64_t slot) {
+                                                          int64_t slot, const Ahead<S> &ahead) {
     using M = MonoidT<S>;
     using D = Desc<S>;
     const int lane = threadIdx.x & 63;
@@ -254,7 +285,10 @@ __device__ typename MonoidT<S>::State chain_wave_lookback(const ChainGeo &g, uin
     for (int64_t pbase = q - 1;; pbase -= 64) {
         const int64_t p = pbase - lane;
         LbPart<S> part = {M::id(), M::zero(), 1};  // before chunk 0: zero delta
-        if (p >= 0) {
+        typename M::State xa;
+        if (p >= 0 && pbase == q - 1 && ahead.get(xa, tag)) {
+            part = {M::id(), xa, 1};  // read ahead
+        } else if (p >= 0) {
             const int64_t d = p * stride + slot;
             for (uint32_t polls = 0;; ++polls) {
                 typename M::State x;
@@ -288,13 +322,16 @@ __device__ typename MonoidT<S>::State chain_wave_lookback(const ChainGeo &g, uin
 // (aggregate) or a stop before k (frozen, so converged); the nearest
 // inclusive answer and every own flag nearer than it decide, and a false
 // own flag decides at once.
-__device__ bool chain_flag_lookback(const ChainGeo &g, uint32_t tag, int k, int64_t q, int64_t b, int64_t cb) {
+__device__ bool chain_flag_lookback(const ChainGeo &g, uint32_t tag, int k, int64_t q, int64_t b, int64_t cb,
+                                    uint64_t ahead) {
     const int lane = threadIdx.x & 63;
     const size_t kofs = (size_t)(k - 1) * g.ntiles;
     for (int64_t pbase = q - 1;; pbase -= 64) {
         const int64_t p = pbase - lane;
         int st = 3;  // 0 own false, 1 own true, 2 prefix false, 3 prefix true (or before chunk 0)
-        if (p >= 0) {
+        if (p >= 0 && pbase == q - 1 && has_tag(ahead, tag)) {
+            st = lo_f(ahead) != 0.0f ? 3 : 2;  // read ahead
+        } else if (p >= 0) {
             const int64_t pt = (p * g.B + b) * g.ncb + cb;
             for (uint32_t polls = 0;; ++polls) {
                 const uint64_t wi = ld_coherent(g.finc + kofs + pt);
@@ -390,7 +427,25 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
     int k = 1;
     bool conv = false;
     for (;; ++k) {
-        // state before this thread's first position, at iterate k-1
+        const size_t kofs = (size_t)(k - 1) * g.ndesc;
+        // Records of the previous chunk read ahead of the cells: its last
+        // state at iterate k-1, its inclusive delta and converged flag at k.
+        Ahead<S> a_bnd{}, a_inc{};  // zero words never carry a launch tag
+        uint64_t a_flag = 0;
+        if (q > 0) {
+            if (sub == 0 && k > 1 && ok) a_bnd.issue(g.bnd + ((size_t)(k - 2) * g.ndesc + dsc - stride) * D::kIncWords);
+            if (CL ? (holder && ok) : (w == NW - 1 && q - 1 - lane >= 0))
+                a_inc.issue(g.inc + (kofs + (CL ? dsc - stride : (q - 1 - lane) * stride + slot)) * D::kIncWords);
+            if (w == 0 && q - 1 - lane >= 0)
+                a_flag = ld_coherent(g.finc + (size_t)(k - 1) * g.ntiles + ((q - 1 - lane) * g.B + b) * g.ncb + cb);
+        }
+
+        // cells at iterate k-1: positions 1..C-1 first (their previous state
+        // is this thread's own), then position 0, whose previous state may
+        // come from the previous chunk
+        Map e[C];
+#pragma unroll
+        for (int i = 1; i < C; ++i) e[i] = val[i] ? cell_step<Cell, C>(cell, wts, s[i - 1], x, i, s[i]) : M::id();
         State hp = M::zero();
         State nb = M::zero();
         if (!CL) nb = shfl_up_s(s[C - 1], 1);  // every lane active for the shuffle
@@ -398,28 +453,23 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
             if (q == 0)
                 hp = init;
             else if (k > 1 && ok)
-                hp = chain_boundary<S>(g, tag, k - 1, dsc - stride, ptile);
+                hp = chain_boundary<S>(g, tag, k - 1, dsc - stride, ptile, a_bnd);
         } else if (k > 1) {
             if (CL)
                 hp = s_last[(w - 1) * 64 + lane];
             else
                 hp = lane == 0 ? s_last[w - 1] : nb;
         }
-
-        Map e[C];
+        e[0] = val[0] ? cell_step<Cell, C>(cell, wts, hp, x, 0, s[0]) : M::id();
         Map acc = M::id();
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            e[i] = val[i] ? cell_step<Cell, C>(cell, wts, hp, x, i, s[i]) : M::id();
-            hp = s[i];
-            acc = M::then(acc, e[i]);
-        }
+        for (int i = 0; i < C; ++i) acc = M::then(acc, e[i]);
 
         // exclusive prefix of this sub-chunk inside the chunk, and the chunk aggregate
         Map ex, tot;
         if (CL) {
             s_part[w * 64 + lane] = acc;
-            __syncthreads();
+            lds_barrier();
             ex = M::id();
             for (int kk = 0; kk < w; ++kk) ex = M::then(ex, s_part[kk * 64 + lane]);
             tot = M::then(ex, acc);
@@ -433,7 +483,7 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
             Map exw = M::shfl_up(incl, 1);
             if (lane == 0) exw = M::id();
             if (lane == 63) s_part[w] = incl;
-            __syncthreads();
+            lds_barrier();
             Map pre = M::id();
             for (int kk = 0; kk < w; ++kk) pre = M::then(pre, s_part[kk]);
             ex = M::then(pre, exw);
@@ -441,14 +491,13 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
         }
 
         // delta entering the chunk at iteration k
-        const size_t kofs = (size_t)(k - 1) * g.ndesc;
         if (CL) {
             if (holder) {
                 State din = M::zero();
                 if (ok) {
                     if (q > 0) {
                         D::put_agg(g.agg + (kofs + dsc) * D::kAggWords, tot, tag);
-                        din = chain_lane_lookback<S>(g, tag, k, q, b, cb, slot);
+                        din = chain_lane_lookback<S>(g, tag, k, q, b, cb, slot, a_inc);
                     }
                     D::put_inc(g.inc + (kofs + dsc) * D::kIncWords, M::apply(tot, din), tag);
                 }
@@ -458,14 +507,14 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
             State din = M::zero();
             if (q > 0) {
                 if (holder) D::put_agg(g.agg + (kofs + dsc) * D::kAggWords, tot, tag);
-                din = chain_wave_lookback<S>(g, tag, k, q, b, cb, slot);
+                din = chain_wave_lookback<S>(g, tag, k, q, b, cb, slot, a_inc);
             }
             if (holder) {
                 D::put_inc(g.inc + (kofs + dsc) * D::kIncWords, M::apply(tot, din), tag);
                 s_carry[0] = din;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // apply: delta through the sub-chunk, s += delta
         State dlt = M::apply(ex, s_carry[CL ? lane : 0]);
@@ -487,7 +536,7 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
             s_last[w] = s[C - 1];
         mx = wave_max_u32(mx);
         if (lane == 0) s_wmax[w] = mx;
-        __syncthreads();
+        lds_barrier();
         uint32_t m = 0;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) m = s_wmax[ww] > m ? s_wmax[ww] : m;
@@ -504,13 +553,13 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
                 }
             }
             bool prefix = own;
-            if (own && q > 0) prefix = chain_flag_lookback(g, tag, k, q, b, cb);
+            if (own && q > 0) prefix = chain_flag_lookback(g, tag, k, q, b, cb, a_flag);
             if (lane == 0) {
                 if (own) st_coherent(g.finc + fofs, tagged(prefix ? 1.0f : 0.0f, tag));
                 s_stop = prefix ? 1 : 0;
             }
         }
-        __syncthreads();
+        lds_barrier();
         conv = s_stop != 0;
         if (conv || k >= g.cap) break;
     }
@@ -525,7 +574,7 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
 }
 
 template <class Cell, int NW, int C, bool CL>
-__global__ __launch_bounds__(NW * 64) void newton_chain_kernel(Cell cell, ChainGeo g) {
+__global__ __launch_bounds__(NW * 64, kChainMinWaves) void newton_chain_kernel(Cell cell, ChainGeo g) {
     __shared__ Ticket s_ticket;
     const bool persistent = (int64_t)gridDim.x < g.ntiles;
     const uint32_t draws = (uint32_t)(persistent ? g.ntiles + gridDim.x : g.ntiles);

@@ -21,7 +21,9 @@ constexpr TileCfg kCfgLstmStep{16, 8, 4, 8};
 constexpr TileCfg kCfgGruAdj{4, 8, 16, 8};
 constexpr TileCfg kCfgLstmAdj{4, 4, 4, 4};
 constexpr TileCfg kCfgGruChain{8, 16, 8, 16};
-constexpr TileCfg kCfgLstmChain{16, 8, 8, 8};
+constexpr TileCfg kCfgLstmChain{8, 8, 8, 8};
+// Waves per SIMD the chained kernels are compiled for (bounds their registers).
+constexpr int kChainMinWaves = 1;
 constexpr int64_t kChannelLanesMinH = 32;
 // Look-back descriptors polled at once by one channel lane (diagonal, 2x2).
 constexpr int kLbBatchDiag = 2;
