@@ -153,7 +153,7 @@ int device_cu_count() {
     return cached[dev];
 }
 
-template <class Op, int S, int NWC, int CC, int NWT, int CT>
+template <class Op, int S, int NWC, int CC, int NWT, int CT, int NCW>
 static hipError_t run_scan(const TileCfg &cfg, const Op &op, int64_t B, int64_t L, int64_t H,
                            char *ws, hipStream_t s) {
     const ScanWs w = scan_ws(cfg, S, B, L, H);
@@ -167,7 +167,7 @@ static hipError_t run_scan(const TileCfg &cfg, const Op &op, int64_t B, int64_t 
     g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
     g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
     g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
-    return w.sh.channel_lanes ? launch_chunk_scan<Op, NWC, CC, true>(op, g, s)
+    return w.sh.channel_lanes ? launch_chunk_scan<Op, NWC, CC, true, NCW>(op, g, s)
                               : launch_chunk_scan<Op, NWT, CT, false>(op, g, s);
 }
 
@@ -176,14 +176,14 @@ hipError_t linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const f
                         const float *h0, float *h, char *ws, hipStream_t s) {
     LinDiagOp op{a, b, h0, h, L, H};
     constexpr TileCfg c = kCfgLinDiag;
-    return run_scan<LinDiagOp, 1, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, op, B, L, H, ws, s);
+    return run_scan<LinDiagOp, 1, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
 }
 
 hipError_t linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const float *b,
                         const float *h0, float *h, char *ws, hipStream_t s) {
     LinBlk2Op op{A, b, h0, h, L, H};
     constexpr TileCfg c = kCfgLinBlk2;
-    return run_scan<LinBlk2Op, 2, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, op, B, L, H, ws, s);
+    return run_scan<LinBlk2Op, 2, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
 }
 
 }  // namespace prn

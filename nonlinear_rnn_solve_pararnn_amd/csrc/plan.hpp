@@ -13,8 +13,9 @@ namespace prn {
 struct TileCfg {
     int nw_cl, c_cl;  // channel lanes (H >= 32)
     int nw_tl, c_tl;  // time lanes (H < 32)
+    int ncw_cl = 1;   // channel lanes: groups of 64 channels per workgroup
 };
-constexpr TileCfg kCfgLinDiag{8, 16, 4, 16};
+constexpr TileCfg kCfgLinDiag{16, 16, 4, 16, 2};
 constexpr TileCfg kCfgLinBlk2{4, 8, 4, 8};
 constexpr TileCfg kCfgGruStep{4, 16, 8, 16};
 constexpr TileCfg kCfgLstmStep{16, 8, 4, 8};
@@ -47,8 +48,9 @@ inline ScanShape scan_shape(const TileCfg &cfg, int64_t B, int64_t L, int64_t H)
     s.channel_lanes = H >= kChannelLanesMinH;
     s.nw = s.channel_lanes ? cfg.nw_cl : cfg.nw_tl;
     s.c = s.channel_lanes ? cfg.c_cl : cfg.c_tl;
-    s.T = s.channel_lanes ? (int64_t)s.nw * s.c : (int64_t)s.nw * 64 * s.c;
-    s.ncb = s.channel_lanes ? (H + 63) / 64 : H;
+    const int64_t width = s.channel_lanes ? (int64_t)64 * cfg.ncw_cl : 1;  // channels per tile
+    s.T = s.channel_lanes ? (int64_t)(s.nw / cfg.ncw_cl) * s.c : (int64_t)s.nw * 64 * s.c;
+    s.ncb = s.channel_lanes ? (H + width - 1) / width : H;
     s.nq = (L + s.T - 1) / s.T;
     s.ntiles = s.nq * B * s.ncb;
     s.ndesc = s.nq * B * H;

@@ -216,8 +216,11 @@ __device__ typename MonoidT<S>::State wave_lookback(const ScanGeo &g, uint32_t t
 }
 
 // One tile (chunk q of a batch row and channel block, identified by its
-// ticket) of a scan.  Every thread of the workgroup calls this.
-template <class Op, int NW, int C, bool CHANNEL_LANES>
+// ticket) of a scan.  Every thread of the workgroup calls this.  With
+// channel lanes the NW waves form NWC channel groups of 64 channels times
+// NW/NWC sub-chunks, so a tile is 64*NWC channels wide (wider row segments
+// per position) and (NW/NWC)*C positions long.
+template <class Op, int NW, int C, bool CHANNEL_LANES, int NWC = 1>
 __device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_t ticket,
                                           uint32_t tag) {
     constexpr int S = Op::S;
@@ -226,12 +229,15 @@ __device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_
     using Map = typename M::Map;
     using State = typename M::State;
     constexpr int NT = NW * 64;
-    constexpr int64_t T = CHANNEL_LANES ? (int64_t)NW * C : (int64_t)NT * C;
+    static_assert(NW % NWC == 0 && (CHANNEL_LANES || NWC == 1), "channel groups tile the waves");
+    constexpr int NWT = NW / NWC;  // sub-chunks per chunk (channel lanes)
+    constexpr int64_t T = CHANNEL_LANES ? (int64_t)NWT * C : (int64_t)NT * C;
 
     __shared__ Map s_part[CHANNEL_LANES ? NT : NW];
-    __shared__ State s_carry[CHANNEL_LANES ? 64 : 1];
+    __shared__ State s_carry[CHANNEL_LANES ? 64 * NWC : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int cw = w % NWC, tw = w / NWC;  // channel group, sub-chunk (channel lanes)
     const int64_t per_q = g.B * g.ncb;
 
     TilePos tp;
@@ -241,9 +247,9 @@ __device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_
     tp.b = rest / g.ncb;
     const int64_t cb = rest - tp.b * g.ncb;
     if (CHANNEL_LANES) {
-        tp.j = cb * 64 + lane;
-        tp.sub = w;
-        tp.nsub = NW;
+        tp.j = (cb * NWC + cw) * 64 + lane;
+        tp.sub = tw;
+        tp.nsub = NWT;
     } else {
         tp.j = cb;
         tp.sub = tid;
@@ -261,7 +267,7 @@ __device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_
         s_part[w * 64 + lane] = m;
         __syncthreads();
         ex = M::id();
-        for (int k = 0; k < w; ++k) ex = M::then(ex, s_part[k * 64 + lane]);
+        for (int k = 0; k < tw; ++k) ex = M::then(ex, s_part[(k * NWC + cw) * 64 + lane]);
         tot = M::then(ex, m);
     } else {
         Map incl = m;
@@ -283,8 +289,8 @@ __device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_
     // The holder of the chunk aggregate publishes it, finds the state
     // entering the chunk by look-back (per channel lane, or by the holder's
     // whole wave for time lanes) and publishes the state leaving the chunk.
-    const bool holder = CHANNEL_LANES ? (w == NW - 1) : (tid == NT - 1);
-    const int cslot = CHANNEL_LANES ? lane : 0;
+    const bool holder = CHANNEL_LANES ? (tw == NWT - 1) : (tid == NT - 1);
+    const int cslot = CHANNEL_LANES ? cw * 64 + lane : 0;
     const int64_t stride = g.B * g.H, slot = tp.b * g.H + tp.j;
     const int64_t dsc = tp.q * stride + slot;
     if (tp.q == 0) {
@@ -312,7 +318,7 @@ __device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_
         }
     }
     __syncthreads();
-    const State x = M::apply(ex, s_carry[CHANNEL_LANES ? lane : 0]);
+    const State x = M::apply(ex, s_carry[cslot]);
     op.template phase2<C, NW, CHANNEL_LANES>(tp, e, x);
 }
 
@@ -325,7 +331,7 @@ __device__ __forceinline__ void scan_tile(const Op &op, const ScanGeo &g, int64_
 // the last of them resets the header.  A tile ticket beyond the grid can only
 // come from a workspace that was not zero-filled before its first use; such a
 // workgroup does nothing.
-template <class Op, int NW, int C, bool CHANNEL_LANES>
+template <class Op, int NW, int C, bool CHANNEL_LANES, int NWC = 1>
 __global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
     __shared__ Ticket s_ticket;
     if (!op.active()) return;  // uniform over the grid (e.g. Newton already converged)
@@ -336,7 +342,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
         __syncthreads();  // scan_tile's own barriers keep the next write after every read
         const Ticket t = s_ticket;
         if (t.index >= g.ntiles) return;
-        scan_tile<Op, NW, C, CHANNEL_LANES>(op, g, t.index, t.tag);
+        scan_tile<Op, NW, C, CHANNEL_LANES, NWC>(op, g, t.index, t.tag);
         if (!persistent) return;
     }
 }
@@ -345,13 +351,13 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
 // as fit on the device at once (fewer workgroups to dispatch, which matters
 // most for the Newton launches that find the iteration already converged
 // and exit at once).
-template <class Op, int NW, int C, bool CL>
+template <class Op, int NW, int C, bool CL, int NWC>
 static int64_t scan_grid(int64_t ntiles) {
     if (!kScanPersistent) return ntiles;
     static int per_cu = 0;
     if (per_cu == 0) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_scan_kernel<Op, NW, C, CL>, NW * 64, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_scan_kernel<Op, NW, C, CL, NWC>, NW * 64, 0) !=
                 hipSuccess || n <= 0)
             n = 1;
         per_cu = n;
@@ -360,10 +366,10 @@ static int64_t scan_grid(int64_t ntiles) {
     return ntiles < slots ? ntiles : slots;
 }
 
-template <class Op, int NW, int C, bool CL>
+template <class Op, int NW, int C, bool CL, int NWC = 1>
 static hipError_t launch_chunk_scan(const Op &op, const ScanGeo &g, hipStream_t s) {
-    const int64_t grid = scan_grid<Op, NW, C, CL>(g.ntiles);
-    hipLaunchKernelGGL((chunk_scan_kernel<Op, NW, C, CL>), dim3((unsigned)grid), dim3(NW * 64), 0, s, op, g);
+    const int64_t grid = scan_grid<Op, NW, C, CL, NWC>(g.ntiles);
+    hipLaunchKernelGGL((chunk_scan_kernel<Op, NW, C, CL, NWC>), dim3((unsigned)grid), dim3(NW * 64), 0, s, op, g);
     return hipGetLastError();
 }
 
