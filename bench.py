@@ -44,8 +44,8 @@ ALG_BYTES = {
 DOMINANT = {
     "c1_linscan": "chunk_scan_kernel<LinDiagOp>",
     "c2_gru_fused": "gru_fused_kernel<16>",
-    "c3_lstm": "chunk_scan_kernel<LstmStepOp> (one launch per Newton iteration)",
-    "c4_gru_long_fwd_adj": "chunk_scan_kernel<GruStepOp> (one launch per Newton iteration)",
+    "c3_lstm": "newton_chain_kernel<LstmChain> (one launch for every iteration)",
+    "c4_gru_long_fwd_adj": "newton_chain_kernel<GruChain> + chunk_scan_kernel<GruAdjOp> (whole step)",
 }
 # HBM bytes per launch of the dominant kernel from rocprofv3 counter runs
 # (FETCH_SIZE x 2.000 and WRITE_SIZE x 1.000, the factors a plain 1 GiB device
@@ -53,12 +53,12 @@ DOMINANT = {
 # taken on: the sha256 prefix of those sources is checked at run time and the
 # figure is dropped (null) once any of them has changed.
 TRAFFIC = {
-    "c1_linscan": {"bytes": 566186598 + 276955136,
-                   "sources": ["common.hpp", "plan.hpp", "scan_core.hpp", "linscan.hip"],
-                   "sha256": "db8084d02383fb7c"},
-    "c2_gru_fused": {"bytes": 419278848 + 152395059,
-                     "sources": ["common.hpp", "cells.hpp", "plan.hpp", "gru_fused.hip"],
-                     "sha256": "acf48117198e404e"},
+    "c1_linscan": {"bytes": 560561562 + 289021952,
+                   "sources": ["common.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
+                   "sha256": "f3cf4f26b752c195"},
+    "c2_gru_fused": {"bytes": 419321037 + 152492646,
+                     "sources": ["common.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
+                     "sha256": "1bb02ff8daf9f5a2"},
 }
 DESCRIBE = {
     "c1_linscan": "linear diagonal recurrence h_t = a_t h_{t-1} + b_t, B=16 L=4096 H=1024, "
