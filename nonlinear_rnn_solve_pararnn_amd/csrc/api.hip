@@ -29,20 +29,27 @@ bool grid_ok(int64_t ntiles) { return ntiles > 0 && ntiles < ((int64_t)1 << 31);
 
 size_t max2(size_t a, size_t b) { return a > b ? a : b; }
 
-// Workspace of a Newton forward: enough for either long-sequence path.
+// The chained kernel keeps records of every iteration, so its workspace
+// grows with the cap; above kChainMaxCap the per-iteration path is used.
+bool chain_ok(int32_t cap) { return cap <= kChainMaxCap; }
+
+// Workspace of a Newton forward: enough for every path the call may take.
 size_t gru_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
-    return max2(newton_ws(kCfgGruStep, 1, B, L, H, cap).total, chain_ws(kCfgGruChain, 1, B, L, H, cap).total);
+    const size_t step = newton_ws(kCfgGruStep, 1, B, L, H, cap).total;
+    return chain_ok(cap) ? max2(step, chain_ws(kCfgGruChain, 1, B, L, H, cap).total) : step;
 }
 size_t lstm_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
-    return max2(newton_ws(kCfgLstmStep, 2, B, L, H, cap).total, chain_ws(kCfgLstmChain, 2, B, L, H, cap).total);
+    const size_t step = newton_ws(kCfgLstmStep, 2, B, L, H, cap).total;
+    return chain_ok(cap) ? max2(step, chain_ws(kCfgLstmChain, 2, B, L, H, cap).total) : step;
 }
 
 // Path of a Newton forward.  The GRU takes the fused on-chip kernel while
 // the sequence fits one workgroup's registers; longer sequences (and the
 // LSTM) take the chained kernel, which keeps each chunk on chip for all its
-// iterations.  The per-iteration launches remain selectable:
-// PARARNN_GRU_PATH=fused|chain|step and PARARNN_LSTM_PATH=chain|step
-// override the choice (for testing every path).
+// iterations, unless the cap is above kChainMaxCap.  The per-iteration
+// launches remain selectable: PARARNN_GRU_PATH=fused|chain|step and
+// PARARNN_LSTM_PATH=chain|step override the choice (for testing every path;
+// a chain request above kChainMaxCap still takes the per-iteration path).
 enum class Path { Fused, Chain, Step, Invalid };
 Path env_path(const char *name) {
     const char *env = getenv(name);
@@ -52,16 +59,17 @@ Path env_path(const char *name) {
     if (strcmp(env, "step") == 0) return Path::Step;
     return Path::Invalid;
 }
-Path gru_path(int64_t L) {
+Path gru_path(int64_t L, int32_t cap) {
     const bool fits = fused_c_for(L) != 0;
     const Path p = env_path("PARARNN_GRU_PATH");
     if (p == Path::Fused) return fits ? Path::Fused : Path::Invalid;
-    if (p == Path::Chain || p == Path::Step) return p;
-    return fits ? Path::Fused : Path::Chain;
+    if (p == Path::Step) return p;
+    if (p == Path::Chain) return chain_ok(cap) ? p : Path::Step;
+    return fits ? Path::Fused : (chain_ok(cap) ? Path::Chain : Path::Step);
 }
-Path lstm_path() {
+Path lstm_path(int32_t cap) {
     const Path p = env_path("PARARNN_LSTM_PATH");
-    return p == Path::Step ? Path::Step : Path::Chain;
+    return (p == Path::Step || !chain_ok(cap)) ? Path::Step : Path::Chain;
 }
 
 }  // namespace
@@ -123,7 +131,7 @@ int pararnn_gru_forward(int64_t B, int64_t L, int64_t H, const float *pz, const 
     if (!(tol >= 0.0f) || max_iter < 1) return PARARNN_ERR_INVALID;  // rejects NaN too
     GruFwdArgs a{B, L, H, pz, pr, pc, uz, ur, uc, h0, h, tol, max_iter, info, trace};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const Path path = gru_path(L);
+    const Path path = gru_path(L, max_iter);
     if (path == Path::Fused) {
         if (!grid_ok(B * ((H + kFusedChannels - 1) / kFusedChannels))) return PARARNN_ERR_INVALID;
         return status_of(gru_forward_fused(a, s));
@@ -149,7 +157,7 @@ int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H, const float *pi, const
     if (!ws || ws_bytes < lstm_fwd_ws(B, L, H, max_iter) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
     LstmFwdArgs a{B, L, H, pi, pf, po, pg, ui, uf, uo, ug, h0, c0, h, c, tol, max_iter, info, trace};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (lstm_path() == Path::Chain) {
+    if (lstm_path(max_iter) == Path::Chain) {
         if (!grid_ok(scan_shape(kCfgLstmChain, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
         return status_of(lstm_forward_chain(a, static_cast<char *>(ws), s));
     }

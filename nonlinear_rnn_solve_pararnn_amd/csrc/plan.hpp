@@ -25,6 +25,9 @@ constexpr TileCfg kCfgGruChain{8, 16, 8, 16};
 constexpr TileCfg kCfgLstmChain{8, 8, 8, 8};
 // Waves per SIMD the chained kernels are compiled for (bounds their registers).
 constexpr int kChainMinWaves = 1;
+// Largest Newton cap the chained kernels take (their workspace holds the
+// records of every iteration).
+constexpr int32_t kChainMaxCap = 64;
 constexpr int64_t kChannelLanesMinH = 32;
 // Look-back descriptors polled at once by one channel lane (diagonal, 2x2).
 constexpr int kLbBatchDiag = 2;

@@ -46,9 +46,11 @@ def test_workspace_query(lib):
         assert api.workspace_bytes(op, 2, -1, 70, 8) == 0
     assert api.workspace_bytes(api.OP_GRU_FORWARD, 2, 100, 70, 0) == 0
     assert api.workspace_bytes(99, 2, 100, 70, 8) == 0
-    # grows with the iteration cap (one counter and one max slot per iteration)
-    assert api.workspace_bytes(api.OP_GRU_FORWARD, 16, 4096, 64, 500) > \
-        api.workspace_bytes(api.OP_GRU_FORWARD, 16, 4096, 64, 2)
+    # grows with the iteration cap: records of every iteration on the chained
+    # path (caps up to 64), one max|delta| slot per iteration beyond
+    for op in (api.OP_GRU_FORWARD, api.OP_LSTM_FORWARD):
+        assert api.workspace_bytes(op, 16, 4096, 64, 60) > api.workspace_bytes(op, 16, 4096, 64, 2)
+        assert api.workspace_bytes(op, 16, 4096, 64, 500) > api.workspace_bytes(op, 16, 4096, 64, 100)
 
 
 def test_invalid_arguments_rejected_on_host(lib):

@@ -198,3 +198,13 @@ def test_chain_iterates_across_chunks(orc, monkeypatch, B, L, H):
         say("chain", B, L, H, k, info, max_abs(h, s))
         assert list(info) == [k, 0]
         assert max_abs(h, s) <= ITER_ATOL, k
+
+
+def test_large_cap_takes_per_iteration_path(orc, monkeypatch):
+    """A cap above the chained kernel's limit (its workspace holds every
+    iteration's records) runs the per-iteration launches, with the same result."""
+    monkeypatch.setenv("PARARNN_GRU_PATH", "chain")
+    d = synth.gru_inputs(2, 2000, 40, seed=67, h0=True)
+    h, info = _run(d, 1e-5, 200)
+    assert info[1] == 1
+    assert max_abs(h, orc.gru_rollout(*gru_args(d), h0=d["h0"])) <= FWD_ATOL

@@ -74,3 +74,10 @@ def test_iterates_across_chunks(orc, B, L, H):
         hr, cr, it, conv, _ = orc.lstm_newton(*lstm_args(d), h0=d["h0"], c0=d["c0"], tol=0.0, cap=k)
         assert list(info) == [k, 0]
         assert max_abs(h, hr) <= ITER_ATOL and max_abs(c, cr) <= ITER_ATOL, k
+
+
+def test_large_cap(orc):
+    d = synth.lstm_inputs(2, 700, 40, seed=74, h0=True)
+    h, c, info = _run(d, 1e-5, 200)
+    hr, cr = orc.lstm_rollout(*lstm_args(d), h0=d["h0"], c0=d["c0"])
+    assert info[1] == 1 and max_abs(h, hr) <= FWD_ATOL and max_abs(c, cr) <= FWD_ATOL
