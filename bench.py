@@ -40,12 +40,16 @@ ALG_BYTES = {
     "c2_gru_fused": 16,          # pz, pr, pc in; h out
     "c3_lstm": 24,               # pi, pf, po, pg in; h, c out
     "c4_gru_long_fwd_adj": 48,   # fwd: 3 p in, h out; adjoint: g, 3 p, h in, 3 dp out
+    "x_linscan_blk2": 32,        # A (2x2) and b (2) in; h (2) out, per (batch, position, channel)
+    "x_lstm_adjoint": 48,        # gh, gc, 4 p, h, c in; 4 dp out
 }
 DOMINANT = {
     "c1_linscan": "chunk_scan_kernel<LinDiagOp>",
     "c2_gru_fused": "gru_fused_kernel<16>",
     "c3_lstm": "newton_chain_kernel<LstmChain> (one launch for every iteration)",
     "c4_gru_long_fwd_adj": "newton_chain_kernel<GruChain> + chunk_scan_kernel<GruAdjOp> (whole step)",
+    "x_linscan_blk2": "chunk_scan_kernel<LinBlk2Op>",
+    "x_lstm_adjoint": "chunk_scan_kernel<LstmAdjOp> + reduce_u_kernel (whole step)",
 }
 # HBM bytes per launch of the dominant kernel from rocprofv3 counter runs
 # (FETCH_SIZE x 2.000 and WRITE_SIZE x 1.000, the factors a plain 1 GiB device
@@ -69,6 +73,10 @@ DESCRIBE = {
                "p~N(0,1), u~U(-0.5,0.5), h0=c0=0, tol 1e-4, cap 32",
     "c4_gru_long_fwd_adj": "diagonal GRU Newton forward + reverse adjoint, B=16 L=1048576 H=1, "
                            "p~N(0,1), u~U(-0.5,0.5), g~N(0,1), h0=0, tol 1e-4, cap 32",
+    "x_linscan_blk2": "2x2 block linear recurrence h_t = A_t h_{t-1} + b_t, B=16 L=4096 H=512, "
+                      "A~U(-0.6,0.6), b~N(0,1), h0=0",
+    "x_lstm_adjoint": "diagonal LSTM reverse adjoint at the converged forward, B=8 L=2048 H=2048, "
+                      "p~N(0,1), u~U(-0.5,0.5), gh, gc~N(0,1), h0=c0=0",
 }
 
 
@@ -122,6 +130,18 @@ class Workload:
             self.out = torch.empty(B, L, H, device=dev)
             self.ws = api.new_workspace(api.workspace_bytes(api.OP_LINSCAN_DIAG, B, L, H), dev)
             self._step = lambda: api.linscan_diag(t["a"], t["b"], None, out=self.out, ws=self.ws)
+        elif name == "x_linscan_blk2":
+            self.out = torch.empty(B, L, H, 2, device=dev)
+            self.ws = api.new_workspace(api.workspace_bytes(api.OP_LINSCAN_BLK2, B, L, H), dev)
+            self._step = lambda: api.linscan_blk2(t["A"], t["b"], None, out=self.out, ws=self.ws)
+        elif name == "x_lstm_adjoint":
+            p = [t[k] for k in ("pi", "pf", "po", "pg")]
+            u = [t[k] for k in ("ui", "uf", "uo", "ug")]
+            h, c = api.lstm_forward(*p, *u, None, None, tol=self.w["tol"], max_iter=self.w["cap"])
+            self.out = h
+            self.ws = api.new_workspace(api.workspace_bytes(api.OP_LSTM_ADJOINT, B, L, H), dev)
+            self._step = lambda: api.adjoint_backward(api.CELL_LSTM, p, u, h, t["gh"], None, c=c,
+                                                      grad_c=t["gc"], ws=self.ws)
         elif name == "c2_gru_fused":
             self.out = torch.empty(B, L, H, device=dev)
             cap = self.w["cap"]
@@ -210,6 +230,19 @@ def cpu_baseline(name, host):
         fn = lambda: oracle.lstm_rollout(*args)
         n = args[0].size
         what = "fp64 sequential LSTM rollout (oracle.lstm_rollout) over the full workload"
+    elif name == "x_lstm_adjoint":
+        keys = ("pi", "pf", "po", "pg", "ui", "uf", "uo", "ug")
+        args = [host[k].astype(np.float64) for k in keys]
+        h, c = oracle.lstm_rollout(*args)
+        gh, gc = host["gh"].astype(np.float64), host["gc"].astype(np.float64)
+        fn = lambda: oracle.lstm_bptt(*args, h, c, gh, gc)
+        n = args[0].size
+        what = "fp64 LSTM backpropagation through time (oracle.lstm_bptt) over the full workload"
+    elif name == "x_linscan_blk2":
+        args = [host["A"].astype(np.float64), host["b"].astype(np.float64)]
+        fn = lambda: oracle.linscan_blk2(*args)
+        n = args[1].size // 2
+        what = "fp64 serial 2x2 block recurrence (oracle.linscan_blk2) over the full workload"
     else:
         args = [host["a"].astype(np.float64), host["b"].astype(np.float64)]
         fn = lambda: oracle.linscan_diag(*args)
@@ -232,7 +265,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c1_linscan",
-                    choices=["c1_linscan", "c2_gru_fused", "c3_lstm", "c4_gru_long_fwd_adj"])
+                    choices=list(ALG_BYTES))
     ap.add_argument("--only", action="store_true",
                     help="measure only the chosen workload (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -266,7 +299,7 @@ def main():
     for name in names:
         log("workload", name)
         wl = Workload(name, dev)
-        iters = wl.iterations() if name != "c1_linscan" else None
+        iters = wl.iterations() if name in ("c2_gru_fused", "c3_lstm", "c4_gru_long_fwd_adj") else None
         wall_ms, per = time_workload(wl, args.steps, args.warmup)
         ev_ms = sum(per) / len(per)
         results[name] = {

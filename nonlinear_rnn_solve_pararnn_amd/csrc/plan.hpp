@@ -16,11 +16,11 @@ struct TileCfg {
     int ncw_cl = 1;   // channel lanes: groups of 64 channels per workgroup
 };
 constexpr TileCfg kCfgLinDiag{16, 16, 4, 16, 2};
-constexpr TileCfg kCfgLinBlk2{4, 8, 4, 8};
+constexpr TileCfg kCfgLinBlk2{16, 8, 4, 8, 2};
 constexpr TileCfg kCfgGruStep{4, 16, 8, 16};
 constexpr TileCfg kCfgLstmStep{16, 8, 4, 8};
 constexpr TileCfg kCfgGruAdj{4, 8, 16, 8};
-constexpr TileCfg kCfgLstmAdj{4, 4, 4, 4};
+constexpr TileCfg kCfgLstmAdj{16, 4, 4, 4};
 constexpr TileCfg kCfgGruChain{8, 16, 8, 16};
 constexpr TileCfg kCfgLstmChain{8, 8, 8, 8};
 // Waves per SIMD the chained kernels are compiled for (bounds their registers).
@@ -28,6 +28,11 @@ constexpr int kChainMinWaves = 1;
 // Largest Newton cap the chained kernels take (their workspace holds the
 // records of every iteration).
 constexpr int32_t kChainMaxCap = 64;
+// Only the exported scans use channel groups: the Newton and adjoint ops
+// reduce over all waves of a workgroup as if they were one channel group.
+static_assert(kCfgGruStep.ncw_cl == 1 && kCfgLstmStep.ncw_cl == 1 && kCfgGruAdj.ncw_cl == 1 &&
+                  kCfgLstmAdj.ncw_cl == 1 && kCfgGruChain.ncw_cl == 1 && kCfgLstmChain.ncw_cl == 1,
+              "channel groups are for the exported scans only");
 constexpr int64_t kChannelLanesMinH = 32;
 // Look-back descriptors polled at once by one channel lane (diagonal, 2x2).
 constexpr int kLbBatchDiag = 2;

@@ -29,6 +29,10 @@ WORKLOADS = {
     "c3_lstm": dict(kind="lstm", B=8, L=2048, H=2048, tol=1e-4, cap=32),
     "c4_gru_long_fwd_adj": dict(kind="gru_adjoint", B=16, L=1048576, H=1,
                                 tol=1e-4, cap=32),
+    # the exported 2x2 block scan at the diagonal scan's element count / 2
+    "x_linscan_blk2": dict(kind="linscan_blk2", B=16, L=4096, H=512),
+    # the LSTM adjoint at the LSTM forward's shape, with upstream gradients on h and c
+    "x_lstm_adjoint": dict(kind="lstm_adjoint", B=8, L=2048, H=2048, tol=1e-4, cap=32),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -127,4 +131,8 @@ def workload_inputs(name: str) -> dict:
         return lstm_inputs(B, L, H, seed)
     if name == "c4_gru_long_fwd_adj":
         return gru_inputs(B, L, H, seed, grad=True)
+    if name == "x_linscan_blk2":
+        return linscan_blk2_inputs(B, L, H, seed)
+    if name == "x_lstm_adjoint":
+        return lstm_inputs(B, L, H, seed, grad=True)
     raise KeyError(name)
