@@ -1,6 +1,7 @@
 // linscan.hip -- the exported linear-recurrence scans (diagonal and 2x2
-// block) on the chunked look-back scan of scan_core.hpp, plus the fill
-// kernel used to reset workspaces.
+// block) on the chunked look-back scan of scan_core.hpp, plus the small fill
+// kernel that initialises info words, traces and per-iteration slots, and
+// the device query shared by the launchers.
 #include "launch.hpp"
 #include "scan_core.hpp"
 

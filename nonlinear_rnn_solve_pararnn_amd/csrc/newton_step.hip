@@ -1,7 +1,9 @@
 // newton_step.hip -- Newton's method for the whole sequence with one launch
-// per iteration, for sequences too long to keep on chip (ParaRNN page,
-// Fig. 5 caption: the modality that assembles the system and runs the
-// parallel reduction as separate stages, here fused into one HBM pass).
+// per iteration (ParaRNN page, Fig. 5 caption: the modality that assembles
+// the system and runs the parallel reduction as separate stages, here fused
+// into one HBM pass).  The chained kernel (newton_chain.hip) is the default
+// for long sequences; this path is selectable and takes caps above the
+// chained kernel's limit.
 //
 // Iteration k (from s^0 = 0):
 //   F_t = f(s^{k-1}_{t-1}), J_t = df/ds there, beta_t = F_t - s^{k-1}_t,
@@ -273,8 +275,8 @@ __global__ void newton_finalize(const uint32_t *maxd, int cap, float tol, int32_
     }
 }
 
-// Runs the launch sequence shared by both cells.  `make_op(k, parity)`
-// returns the op of iteration k.
+// Runs the launch sequence shared by both cells.  `make_op(k, bnd_prev,
+// bnd_next, maxd)` returns the op of iteration k.
 template <int S, int NWC, int CC, int NWT, int CT, class MakeOp>
 static hipError_t newton_loop(const TileCfg &cfg, int64_t B, int64_t L, int64_t H, int32_t cap,
                               float tol, int32_t *info, float *trace, char *ws, hipStream_t s,

@@ -113,3 +113,24 @@ def test_gru_single_channel_unaligned_inputs(orc):
     errs.update({"du%d" % q: rel_inf(host(g["u"][q]), du[q]) for q in range(3)})
     errs["dh0"] = rel_inf(host(g["h0"]), dh0)
     assert max(errs.values()) <= GRAD_RTOL, errs
+
+
+def test_lstm_adjoint_full_workload(orc):
+    """B=8, L=2048, H=2048 (the LSTM forward's shape), gh, gc ~ N(0,1), h0 = c0 = 0:
+    Newton forward on the chained kernel, then the adjoint; every gradient checked."""
+    say("lstm adjoint full workload")
+    d = synth.workload_inputs("x_lstm_adjoint")
+    ins = [dev(x) for x in lstm_args(d)]
+    info = torch.zeros(2, dtype=torch.int32, device="cuda:0")
+    h, c = api.lstm_forward(*ins, None, None, tol=1e-4, max_iter=32, info=info)
+    g = api.adjoint_backward(api.CELL_LSTM, ins[:4], ins[4:], h, dev(d["gh"]), None, c=c,
+                             grad_c=dev(d["gc"]))
+    hr, cr = orc.lstm_rollout(*lstm_args(d))
+    dp, du, dh0, dc0 = orc.lstm_bptt(*lstm_args(d), hr, cr, d["gh"], d["gc"])
+    errs = {"dp%d" % q: rel_inf(host(g["p"][q]), dp[q]) for q in range(4)}
+    errs.update({"du%d" % q: rel_inf(host(g["u"][q]), du[q]) for q in range(4)})
+    errs["dh0"] = rel_inf(host(g["h0"]), dh0)
+    errs["dc0"] = rel_inf(host(g["c0"]), dc0)
+    say("info", host(info), errs)
+    assert host(info)[1] == 1
+    assert max(errs.values()) <= GRAD_RTOL, errs

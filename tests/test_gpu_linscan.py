@@ -67,6 +67,16 @@ def test_linscan_blk2_matches_oracle(orc, B, L, H, with_h0):
     assert max_abs(h, ref) <= FWD_ATOL
 
 
+def test_linscan_blk2_full_workload(orc):
+    """B=16, L=4096, H=512, A ~ U(-0.6,0.6), b ~ N(0,1), h0 = 0: every output checked."""
+    say("linscan_blk2 full workload")
+    d = synth.workload_inputs("x_linscan_blk2")
+    h = host(api.linscan_blk2(dev(d["A"]), dev(d["b"])))
+    err = max_abs(h, orc.linscan_blk2(d["A"], d["b"]))
+    say("max abs err", err)
+    assert err <= FWD_ATOL
+
+
 def test_linscan_blk2_large(orc):
     d = synth.linscan_blk2_inputs(4, 4096, 1024, seed=5)
     h = host(api.linscan_blk2(dev(d["A"]), dev(d["b"])))
