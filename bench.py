@@ -105,6 +105,25 @@ def roofline(name, elements, kernel_ms):
             "kernel_us": kernel_ms * 1e3}
 
 
+# Arithmetic roof of the fused GRU kernel.  Per position and Newton iteration
+# its loop issues 27.8 plain VALU instructions and 6 transcendental ones (exp2,
+# reciprocal; 541 VALU instructions per 16 positions in the gfx950 assembly).
+# The fp32 vector peak of 157.3 TFLOP/s is 78.6 T lane-operations per second
+# of FMA issue; transcendentals issue at a quarter of that rate, so each costs
+# four slots.
+FUSED_GRU_SLOTS_PER_ELEMENT_ITER = 27.8 + 6 * 4
+PEAK_VALU_TOPS = 78.6
+
+
+def alu_roofline(elements, iterations, kernel_ms):
+    slots = FUSED_GRU_SLOTS_PER_ELEMENT_ITER * elements * iterations
+    achieved = slots / (kernel_ms * 1e-3) / 1e12
+    return {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_TOPS,
+            "unit": "T VALU issue slots/s", "frac": achieved / PEAK_VALU_TOPS,
+            "model": "%.1f slots per element and Newton iteration (transcendentals count 4), "
+                     "%d iterations (the most any tile took)" % (FUSED_GRU_SLOTS_PER_ELEMENT_ITER, iterations)}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -311,6 +330,8 @@ def main():
             "describe": DESCRIBE[name],
             "roofline": roofline(name, wl.elements, ev_ms),
         }
+        if name == "c2_gru_fused" and iters:
+            results[name]["roofline_alu"] = alu_roofline(wl.elements, iters[0], ev_ms)
         log(json.dumps({name: results[name]}))
         del wl
         torch.cuda.empty_cache()
