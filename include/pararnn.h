@@ -112,7 +112,9 @@ int rnn_linscan_blk2(int64_t B, int64_t L, int64_t H,
  * pre-projections (input projections and biases already applied).
  * uz, ur, uc: [H].  h0: [B, H] or NULL.  h: [B, L, H] output.
  * tol >= 0: stop once max|delta| over the sequence tile is <= tol (the only
- * extra hyper-parameter; DEER summary, second paragraph).  max_iter >= 1.
+ * extra hyper-parameter; DEER summary, second paragraph).  max_iter >= 1;
+ * caps above L + 1 are taken as L + 1 (Newton from zero is exact after L
+ * iterations, and iteration L + 1 confirms it).
  * info: device int32[2] {iterations, converged} or NULL.  iterations is the
  * largest number of updates any tile applied; converged is 1 only if every
  * tile met the tolerance.

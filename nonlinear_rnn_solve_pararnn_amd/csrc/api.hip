@@ -27,7 +27,21 @@ int status_of(hipError_t e) { return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_
 
 bool grid_ok(int64_t ntiles) { return ntiles > 0 && ntiles < ((int64_t)1 << 31); }
 
+// Zeros for trace entries [from, to) that no iteration will write.
+int clear_trace_tail(float *trace, int32_t from, int32_t to, hipStream_t s) {
+    FillRange fr[1] = {{trace + from, (uint64_t)(to - from), 0, 4}};
+    return status_of(fill(fr, 1, s));
+}
+
 size_t max2(size_t a, size_t b) { return a > b ? a : b; }
+
+// Newton from zero reproduces the sequential result after L iterations (and
+// iteration L + 1 confirms it with a zero update), so caps above L + 1 change
+// nothing but the number of launches: they are taken as L + 1 (a trace still
+// receives zeros up to the caller's cap).
+int32_t eff_cap(int32_t max_iter, int64_t L) {
+    return (int64_t)max_iter > L + 1 ? (int32_t)(L + 1) : max_iter;
+}
 
 // The chained kernel keeps records of every iteration, so its workspace
 // grows with the cap; above kChainMaxCap the per-iteration path is used.
@@ -93,10 +107,10 @@ size_t pararnn_workspace_bytes(int32_t op, int64_t B, int64_t L, int64_t H, int3
         case PARARNN_OP_LINSCAN_BLK2: return scan_ws(kCfgLinBlk2, 2, B, L, H).total;
         case PARARNN_OP_GRU_FORWARD:
             if (max_iter < 1) return 0;
-            return gru_fwd_ws(B, L, H, max_iter);
+            return gru_fwd_ws(B, L, H, eff_cap(max_iter, L));
         case PARARNN_OP_LSTM_FORWARD:
             if (max_iter < 1) return 0;
-            return lstm_fwd_ws(B, L, H, max_iter);
+            return lstm_fwd_ws(B, L, H, eff_cap(max_iter, L));
         case PARARNN_OP_GRU_ADJOINT: return gru_adjoint_ws(B, L, H);
         case PARARNN_OP_LSTM_ADJOINT: return lstm_adjoint_ws(B, L, H);
         default: return 0;
@@ -129,20 +143,23 @@ int pararnn_gru_forward(int64_t B, int64_t L, int64_t H, const float *pz, const 
                         float *trace, void *ws, size_t ws_bytes, void *stream) {
     if (!dims_ok(B, L, H) || !pz || !pr || !pc || !uz || !ur || !uc || !h) return PARARNN_ERR_INVALID;
     if (!(tol >= 0.0f) || max_iter < 1) return PARARNN_ERR_INVALID;  // rejects NaN too
-    GruFwdArgs a{B, L, H, pz, pr, pc, uz, ur, uc, h0, h, tol, max_iter, info, trace};
+    const int32_t cap = eff_cap(max_iter, L);
+    GruFwdArgs a{B, L, H, pz, pr, pc, uz, ur, uc, h0, h, tol, cap, info, trace};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const Path path = gru_path(L, max_iter);
-    if (path == Path::Fused) {
-        if (!grid_ok(B * ((H + kFusedChannels - 1) / kFusedChannels))) return PARARNN_ERR_INVALID;
-        return status_of(gru_forward_fused(a, s));
-    }
+    const Path path = gru_path(L, cap);
     if (path == Path::Invalid) return PARARNN_ERR_UNSUPPORTED;
-    if (!ws || ws_bytes < gru_fwd_ws(B, L, H, max_iter) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
-    if (path == Path::Chain) {
-        if (!grid_ok(scan_shape(kCfgGruChain, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
-        return status_of(gru_forward_chain(a, static_cast<char *>(ws), s));
+    if (path != Path::Fused && (!ws || ws_bytes < gru_fwd_ws(B, L, H, cap) || !aligned(ws, 256)))
+        return PARARNN_ERR_INVALID;
+    const int64_t ntiles = path == Path::Fused ? B * ((H + kFusedChannels - 1) / kFusedChannels)
+                           : path == Path::Chain ? scan_shape(kCfgGruChain, B, L, H).ntiles
+                                                 : scan_shape(kCfgGruStep, B, L, H).ntiles;
+    if (!grid_ok(ntiles)) return PARARNN_ERR_INVALID;
+    if (trace != nullptr && max_iter > cap) {
+        const int st = clear_trace_tail(trace, cap, max_iter, s);
+        if (st != PARARNN_OK) return st;
     }
-    if (!grid_ok(scan_shape(kCfgGruStep, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+    if (path == Path::Fused) return status_of(gru_forward_fused(a, s));
+    if (path == Path::Chain) return status_of(gru_forward_chain(a, static_cast<char *>(ws), s));
     return status_of(gru_forward_step(a, static_cast<char *>(ws), s));
 }
 
@@ -154,14 +171,17 @@ int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H, const float *pi, const
     if (!dims_ok(B, L, H) || !pi || !pf || !po || !pg || !ui || !uf || !uo || !ug || !h || !c)
         return PARARNN_ERR_INVALID;
     if (!(tol >= 0.0f) || max_iter < 1) return PARARNN_ERR_INVALID;
-    if (!ws || ws_bytes < lstm_fwd_ws(B, L, H, max_iter) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
-    LstmFwdArgs a{B, L, H, pi, pf, po, pg, ui, uf, uo, ug, h0, c0, h, c, tol, max_iter, info, trace};
+    const int32_t cap = eff_cap(max_iter, L);
+    if (!ws || ws_bytes < lstm_fwd_ws(B, L, H, cap) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+    LstmFwdArgs a{B, L, H, pi, pf, po, pg, ui, uf, uo, ug, h0, c0, h, c, tol, cap, info, trace};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (lstm_path(max_iter) == Path::Chain) {
-        if (!grid_ok(scan_shape(kCfgLstmChain, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
-        return status_of(lstm_forward_chain(a, static_cast<char *>(ws), s));
+    const bool chain = lstm_path(cap) == Path::Chain;
+    if (!grid_ok(scan_shape(chain ? kCfgLstmChain : kCfgLstmStep, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+    if (trace != nullptr && max_iter > cap) {
+        const int st = clear_trace_tail(trace, cap, max_iter, s);
+        if (st != PARARNN_OK) return st;
     }
-    if (!grid_ok(scan_shape(kCfgLstmStep, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+    if (chain) return status_of(lstm_forward_chain(a, static_cast<char *>(ws), s));
     return status_of(lstm_forward_step(a, static_cast<char *>(ws), s));
 }
 

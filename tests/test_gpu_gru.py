@@ -208,3 +208,16 @@ def test_large_cap_takes_per_iteration_path(orc, monkeypatch):
     h, info = _run(d, 1e-5, 200)
     assert info[1] == 1
     assert max_abs(h, orc.gru_rollout(*gru_args(d), h0=d["h0"])) <= FWD_ATOL
+
+
+@pytest.mark.parametrize("path", ["fused", "chain", "step"])
+def test_cap_beyond_sequence_length(orc, monkeypatch, path):
+    """A cap far above L is taken as L + 1 (exact after L updates, confirmed by
+    the next): same result and count as the oracle, trace zero past the cap."""
+    monkeypatch.setenv("PARARNN_GRU_PATH", path)
+    d = synth.gru_inputs(2, 20, 5, seed=68, h0=True)
+    h, info, tr = _run(d, 0.0, 1000, trace=True)
+    s, it, conv, _ = orc.gru_newton(*gru_args(d), h0=d["h0"], tol=0.0, cap=21)
+    assert max_abs(h, orc.gru_rollout(*gru_args(d), h0=d["h0"])) <= FWD_ATOL
+    assert int(info[0]) <= 21
+    assert float(abs(tr[21:]).max()) == 0.0
