@@ -101,10 +101,10 @@ struct GruAdjOp {
                 const int64_t tlo = L - tp.pos0 - C;
                 const int64_t blo = idx3(tp.b, tlo, tp.j, L, H);
                 float vz[C], vr[C], vc[C], vg[C], vh[C];
-                load_run<C>(pz + blo, vz);
-                load_run<C>(pr + blo, vr);
-                load_run<C>(pc + blo, vc);
-                load_run<C>(gh + blo, vg);
+                load_run<C, true>(pz + blo, vz);
+                load_run<C, true>(pr + blo, vr);
+                load_run<C, true>(pc + blo, vc);
+                load_run<C, true>(gh + blo, vg);
                 load_run<C>(h + blo, vh);
                 const float hlo = tlo == 0 ? (h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f) : h[blo - 1];
 #pragma unroll
@@ -127,8 +127,8 @@ struct GruAdjOp {
                 const int64_t kk = idx3(tp.b, t, tp.j, L, H);
                 const float hp = t == 0 ? (h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f) : h[kk - H];
                 float J, dz, dr, dc, r;
-                gru_j_dp(hp, pz[kk], pr[kk], pc[kk], wz, wr, wc, J, dz, dr, dc, r);
-                e[i] = {J, gh[kk], dz, dr, dc, dz * hp, dr * hp, dc * r * hp};
+                gru_j_dp(hp, ld_once(pz + kk), ld_once(pr + kk), ld_once(pc + kk), wz, wr, wc, J, dz, dr, dc, r);
+                e[i] = {J, ld_once(gh + kk), dz, dr, dc, dz * hp, dr * hp, dc * r * hp};
             } else {
                 e[i] = {1.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
             }
@@ -229,8 +229,8 @@ struct LstmAdjOp {
                     hp = h[kk - H];
                     cp = c[kk - H];
                 }
-                const LstmAdj r = lstm_adj(cp, hp, pi[kk], pf[kk], po[kk], pg[kk], wi, wf, wo, wg);
-                e[i] = {r.j00, r.j01, r.j10, r.j11, gc != nullptr ? gc[kk] : 0.0f, gh[kk],
+                const LstmAdj r = lstm_adj(cp, hp, ld_once(pi + kk), ld_once(pf + kk), ld_once(po + kk), ld_once(pg + kk), wi, wf, wo, wg);
+                e[i] = {r.j00, r.j01, r.j10, r.j11, gc != nullptr ? ld_once(gc + kk) : 0.0f, ld_once(gh + kk),
                         r.dci, r.dcf, r.dcg, r.dhi, r.dhf, r.dho, r.dhg, hp};
                 // J^T and J^T g
                 m = {e[i].j00, e[i].j10, e[i].j01, e[i].j11,

@@ -63,15 +63,15 @@ struct LinDiagOp {
         if (tp.ok && tp.pos0 + C <= L) {
 #pragma unroll
             for (int i = 0; i < C; ++i) {
-                e[i].a = a[base + i * H];
-                e[i].b = b[base + i * H];
+                e[i].a = ld_once(a + base + i * H);
+                e[i].b = ld_once(b + base + i * H);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < C; ++i) {
                 const bool v = tp.ok && tp.pos0 + i < L;
-                e[i].a = v ? a[base + i * H] : 1.0f;
-                e[i].b = v ? b[base + i * H] : 0.0f;
+                e[i].a = v ? ld_once(a + base + i * H) : 1.0f;
+                e[i].b = v ? ld_once(b + base + i * H) : 0.0f;
             }
         }
         Aff1 acc = {1.0f, 0.0f};
@@ -117,8 +117,8 @@ struct LinBlk2Op {
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             if (tp.ok && tp.pos0 + i < L) {
-                const float4 m = A4[base + i * H];
-                const float2 v = b2[base + i * H];
+                const float4 m = ld_once(A4 + base + i * H);
+                const float2 v = ld_once(b2 + base + i * H);
                 e[i].m = {m.x, m.y, m.z, m.w, v.x, v.y};
             } else {
                 e[i].m = MonoidT<2>::id();

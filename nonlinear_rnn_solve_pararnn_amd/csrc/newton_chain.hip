@@ -81,8 +81,8 @@ struct GruChain {
     __device__ void load(int64_t base, int64_t H, const bool (&val)[C], bool whole, float (&x)[NG][C]) const {
         if constexpr (C % 4 == 0) {
             if (runs && whole) {
-                load_run<C>(pz + base, x[0]);
-                load_run<C>(pr + base, x[1]);
+                load_run<C>(pz + base, x[0]);  // ordinary loads: streamed 16-byte
+                load_run<C>(pr + base, x[1]);  // pieces of half-lines measured slower
                 load_run<C>(pc + base, x[2]);
 #pragma unroll
                 for (int i = 0; i < C; ++i) {
@@ -95,9 +95,9 @@ struct GruChain {
         }
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            x[0][i] = val[i] ? kE1 * pz[base + i * H] : 0.0f;
-            x[1][i] = val[i] ? kE1 * pr[base + i * H] : 0.0f;
-            x[2][i] = val[i] ? kE2 * pc[base + i * H] : 0.0f;
+            x[0][i] = val[i] ? kE1 * ld_once(pz + base + i * H) : 0.0f;
+            x[1][i] = val[i] ? kE1 * ld_once(pr + base + i * H) : 0.0f;
+            x[2][i] = val[i] ? kE2 * ld_once(pc + base + i * H) : 0.0f;
         }
     }
     // Newton map of one position: delta -> J delta + (F - s), F and J at hp.
@@ -149,10 +149,10 @@ struct LstmChain {
     __device__ void load(int64_t base, int64_t H, const bool (&val)[C], bool, float (&x)[NG][C]) const {
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            x[0][i] = val[i] ? pi[base + i * H] : 0.0f;
-            x[1][i] = val[i] ? pf[base + i * H] : 0.0f;
-            x[2][i] = val[i] ? po[base + i * H] : 0.0f;
-            x[3][i] = val[i] ? pg[base + i * H] : 0.0f;
+            x[0][i] = val[i] ? ld_once(pi + base + i * H) : 0.0f;
+            x[1][i] = val[i] ? ld_once(pf + base + i * H) : 0.0f;
+            x[2][i] = val[i] ? ld_once(po + base + i * H) : 0.0f;
+            x[3][i] = val[i] ? ld_once(pg + base + i * H) : 0.0f;
         }
     }
     __device__ Aff2 step(const W &w, float2s hp, float xi, float xf, float xo, float xg, float2s s) const {
@@ -443,9 +443,15 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
         // cells at iterate k-1: positions 1..C-1 first (their previous state
         // is this thread's own), then position 0, whose previous state may
         // come from the previous chunk
+        // Every position is evaluated, with no branch per position, so the
+        // compiler can interleave the independent cells.  A position past the
+        // end of the sequence or a channel past H runs on zero inputs; its map
+        // reaches only later positions of the same chunk (also past the end),
+        // the records of the last chunk (which no chunk reads) and states that
+        // are neither stored nor counted in max|delta|.
         Map e[C];
 #pragma unroll
-        for (int i = 1; i < C; ++i) e[i] = val[i] ? cell_step<Cell, C>(cell, wts, s[i - 1], x, i, s[i]) : M::id();
+        for (int i = 1; i < C; ++i) e[i] = cell_step<Cell, C>(cell, wts, s[i - 1], x, i, s[i]);
         State hp = M::zero();
         State nb = M::zero();
         if (!CL) nb = shfl_up_s(s[C - 1], 1);  // every lane active for the shuffle
@@ -460,7 +466,7 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
             else
                 hp = lane == 0 ? s_last[w - 1] : nb;
         }
-        e[0] = val[0] ? cell_step<Cell, C>(cell, wts, hp, x, 0, s[0]) : M::id();
+        e[0] = cell_step<Cell, C>(cell, wts, hp, x, 0, s[0]);
         Map acc = M::id();
 #pragma unroll
         for (int i = 0; i < C; ++i) acc = M::then(acc, e[i]);
@@ -470,8 +476,16 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
         if (CL) {
             s_part[w * 64 + lane] = acc;
             lds_barrier();
+            // the earlier sub-chunks' maps are all read before any is
+            // composed, so their LDS latencies overlap
+            Map pv[NW - 1];
+#pragma unroll
+            for (int kk = 0; kk < NW - 1; ++kk)
+                if (kk < w) pv[kk] = s_part[kk * 64 + lane];
             ex = M::id();
-            for (int kk = 0; kk < w; ++kk) ex = M::then(ex, s_part[kk * 64 + lane]);
+#pragma unroll
+            for (int kk = 0; kk < NW - 1; ++kk)
+                if (kk < w) ex = M::then(ex, pv[kk]);
             tot = M::then(ex, acc);
         } else {
             Map incl = acc;
@@ -521,12 +535,10 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
         uint32_t mx = 0;
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            if (val[i]) {
-                dlt = M::apply(e[i], dlt);
-                s[i] = state_add(s[i], dlt);
-                const uint32_t a = state_abs_max(dlt);
-                mx = a > mx ? a : mx;
-            }
+            dlt = M::apply(e[i], dlt);
+            s[i] = state_add(s[i], dlt);
+            const uint32_t a = val[i] ? state_abs_max(dlt) : 0u;
+            mx = a > mx ? a : mx;
         }
         mx = clamp_nan_to_inf(mx);
         if (holder && ok && q + 1 < g.nq) D::put_inc(g.bnd + (kofs + dsc) * D::kIncWords, s[C - 1], tag);

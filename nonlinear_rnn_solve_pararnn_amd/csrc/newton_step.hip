@@ -91,8 +91,8 @@ struct GruStepOp {
         if constexpr (C % 4 == 0) {
             if (runs && tp.ok && tp.pos0 + C <= L) {
                 float vz[C], vr[C], vc[C], vh[C];
-                load_run<C>(pz + base, vz);
-                load_run<C>(pr + base, vr);
+                load_run<C>(pz + base, vz);  // ordinary loads: streamed 16-byte
+                load_run<C>(pr + base, vr);  // pieces of half-lines measured slower
                 load_run<C>(pc + base, vc);
                 if (k == 1) {
 #pragma unroll
@@ -117,7 +117,7 @@ struct GruStepOp {
                 const int64_t kk = base + i * H;
                 const float hc = k == 1 ? 0.0f : h[kk];
                 float F, J;
-                gru_f_j(hp, pz[kk], pr[kk], pc[kk], wz, wr, wc, F, J);
+                gru_f_j(hp, ld_once(pz + kk), ld_once(pr + kk), ld_once(pc + kk), wz, wr, wc, F, J);
                 e[i] = {J, F - hc, hc};
                 hp = hc;
             } else {
@@ -216,7 +216,7 @@ struct LstmStepOp {
                 const int64_t kk = base + i * H;
                 const float cc = k == 1 ? 0.0f : c[kk];
                 const float hc = k == 1 ? 0.0f : h[kk];
-                const Lstm2 r = lstm_f_j(cp, hp, pi[kk], pf[kk], po[kk], pg[kk], wi, wf, wo, wg);
+                const Lstm2 r = lstm_f_j(cp, hp, ld_once(pi + kk), ld_once(pf + kk), ld_once(po + kk), ld_once(pg + kk), wi, wf, wo, wg);
                 e[i].m = {r.j00, r.j01, r.j10, r.j11, r.Fc - cc, r.Fh - hc};
                 e[i].cc = cc;
                 e[i].hc = hc;
