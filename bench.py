@@ -57,9 +57,9 @@ DOMINANT = {
 # taken on: the sha256 prefix of those sources is checked at run time and the
 # figure is dropped (null) once any of them has changed.
 TRAFFIC = {
-    "c1_linscan": {"bytes": 560561562 + 289021952,
+    "c1_linscan": {"bytes": 551673036 + 288956416,
                    "sources": ["common.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-                   "sha256": "f3cf4f26b752c195"},
+                   "sha256": "9624a28c20b3968f"},
     "c2_gru_fused": {"bytes": 419321037 + 152492646,
                      "sources": ["common.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
                      "sha256": "1bb02ff8daf9f5a2"},

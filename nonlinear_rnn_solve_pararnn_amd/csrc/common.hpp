@@ -237,10 +237,12 @@ __device__ __forceinline__ void lds_barrier() {
 // then do not push the look-back records and the lines still being written
 // out of L2 (the diagonal scan at B=16, L=4096, H=1024 gains about 12%).
 // Operands read twice (a state that is also the next position's previous
-// state) keep ordinary loads, and so do the 64-byte runs of the Newton
-// forward kernels, where one thread's four 16-byte loads share a line with
-// its neighbour's: streamed, such lines were fetched again (the GRU forward
-// at B=16, L=2^20, H=1 went from 0.30 to 0.40 ms per step).
+// state) keep ordinary loads, and so do two patterns where streaming was
+// measured to lose: the 64-byte runs of the Newton forward kernels (one
+// thread's four 16-byte loads share a line with its neighbour's; the GRU
+// forward at B=16, L=2^20, H=1 went from 0.30 to 0.40 ms per step) and the
+// 64-byte row pieces of the fused GRU tiles (11% more bytes fetched, no
+// gain).  The adjoint's 32-byte runs gain from it (0.166 -> 0.149 ms).
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float ld_once(const float *p) { return __builtin_nontemporal_load(p); }

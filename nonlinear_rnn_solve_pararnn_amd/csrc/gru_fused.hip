@@ -191,9 +191,9 @@ __global__ __launch_bounds__(kNW * 64, 4) void gru_fused_kernel(FusedGruArgs a) 
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         val[i] = FULL || (ok && (t0 + i < L));
-        xz[i] = val[i] ? kE1 * ld_once(a.pz + base + i * H) : 0.0f;
-        xr[i] = val[i] ? kE1 * ld_once(a.pr + base + i * H) : 0.0f;
-        xc[i] = val[i] ? kE2 * ld_once(a.pc + base + i * H) : 0.0f;
+        xz[i] = val[i] ? kE1 * a.pz[base + i * H] : 0.0f;
+        xr[i] = val[i] ? kE1 * a.pr[base + i * H] : 0.0f;
+        xc[i] = val[i] ? kE2 * a.pc[base + i * H] : 0.0f;
     }
     const float uz = ok ? a.uz[j] : 0.0f, ur = ok ? a.ur[j] : 0.0f, uc = ok ? a.uc[j] : 0.0f;
     const float hinit = (ok && a.h0 != nullptr) ? a.h0[b * H + j] : 0.0f;

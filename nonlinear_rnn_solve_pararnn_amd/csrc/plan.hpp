@@ -15,7 +15,7 @@ struct TileCfg {
     int nw_tl, c_tl;  // time lanes (H < 32)
     int ncw_cl = 1;   // channel lanes: groups of 64 channels per workgroup
 };
-constexpr TileCfg kCfgLinDiag{16, 16, 4, 16, 2};
+constexpr TileCfg kCfgLinDiag{16, 32, 4, 16, 4};
 constexpr TileCfg kCfgLinBlk2{16, 8, 4, 8, 2};
 constexpr TileCfg kCfgGruStep{4, 16, 8, 16};
 constexpr TileCfg kCfgLstmStep{16, 8, 4, 8};
@@ -35,7 +35,7 @@ static_assert(kCfgGruStep.ncw_cl == 1 && kCfgLstmStep.ncw_cl == 1 && kCfgGruAdj.
               "channel groups are for the exported scans only");
 constexpr int64_t kChannelLanesMinH = 32;
 // Look-back descriptors polled at once by one channel lane (diagonal, 2x2).
-constexpr int kLbBatchDiag = 2;
+constexpr int kLbBatchDiag = 1;
 // Scan launches use a grid of as many workgroups as fit on the device at
 // once, each drawing tiles until none is left (instead of one per tile).
 constexpr bool kScanPersistent = true;
