@@ -27,6 +27,35 @@ def test_linscan_diag_matches_oracle(orc, B, L, H, with_h0):
     assert max_abs(h, ref) <= FWD_ATOL
 
 
+def _offset(x, k):
+    """Copy of x whose data starts k floats past a 16-byte boundary."""
+    buf = torch.zeros(x.numel() + 4, dtype=x.dtype, device=x.device)
+    v = buf[k:k + x.numel()].view(x.shape)
+    v.copy_(x)
+    return v
+
+
+# Tensors whose data start 4 bytes past a 16-byte boundary, against aligned
+# ones, at tiles of 256 channels x 128 positions with ragged tails in L and in
+# the channel block.
+VIEW_SHAPES = [(1, 1, 32), (2, 129, 36), (2, 4100, 256), (1, 3000, 260), (3, 777, 1024), (1, 20000, 64)]
+
+
+@pytest.mark.parametrize("B,L,H", VIEW_SHAPES)
+@pytest.mark.parametrize("misalign", [0, 1])
+def test_linscan_diag_aligned_and_offset_views(orc, B, L, H, misalign):
+    say("linscan_diag paths", B, L, H, misalign)
+    d = synth.linscan_diag_inputs(B, L, H, seed=300 + L + H, h0=True)
+    a, b, h0 = dev(d["a"]), dev(d["b"]), dev(d["h0"])
+    if misalign:
+        a, b, h0 = _offset(a, misalign), _offset(b, misalign), _offset(h0, misalign)
+        out = _offset(torch.empty_like(a), misalign)
+    else:
+        out = torch.empty_like(a)
+    h = host(api.linscan_diag(a, b, h0, out=out))
+    assert max_abs(h, orc.linscan_diag(d["a"], d["b"], d["h0"])) <= FWD_ATOL
+
+
 def test_linscan_diag_signed_coefficients(orc):
     # a in (-1, 1): sign changes exercise the composition of negative factors
     d = synth.linscan_diag_inputs(2, 9000, 40, seed=7, alo=-1.0, ahi=1.0, h0=True)
