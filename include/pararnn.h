@@ -111,10 +111,19 @@ int rnn_linscan_blk2(int64_t B, int64_t L, int64_t H,
  * (ParaRNN TL;DR; DEER summary).  pz, pr, pc: [B, L, H] gate
  * pre-projections (input projections and biases already applied).
  * uz, ur, uc: [H].  h0: [B, H] or NULL.  h: [B, L, H] output.
- * tol >= 0: stop once max|delta| over the sequence tile is <= tol (the only
- * extra hyper-parameter; DEER summary, second paragraph).  max_iter >= 1;
- * caps above L + 1 are taken as L + 1 (Newton from zero is exact after L
- * iterations, and iteration L + 1 confirms it).
+ * tol >= 0: Newton stops once max|delta| <= tol (the only extra
+ * hyper-parameter; DEER summary, second paragraph), measured after the
+ * update and absolute.  Where the test is taken depends on the kernel:
+ *  - L <= 512: over the whole sequence of each 16 channels of a batch row;
+ *  - longer sequences with max_iter <= 64: each chunk of the sequence stops
+ *    once it and every earlier chunk of its channels meet the bound, so the
+ *    last chunk stops exactly when Newton over the whole sequence of those
+ *    channels would (earlier chunks may freeze a few iterations sooner, with
+ *    corrections of order tol^2 left);
+ *  - max_iter > 64: over the whole tensor (one launch per iteration).
+ * With tol = 0 nothing stops before the cap.  max_iter >= 1; caps above
+ * L + 1 are taken as L + 1 (Newton from zero is exact after L iterations,
+ * and iteration L + 1 confirms it).
  * info: device int32[2] {iterations, converged} or NULL.  iterations is the
  * largest number of updates any tile applied; converged is 1 only if every
  * tile met the tolerance.
@@ -135,7 +144,9 @@ int pararnn_gru_forward(int64_t B, int64_t L, int64_t H,
  *   g = tanh(pg + ug*h'),  c = f*c' + i*g,  h = o*tanh(c)
  * Newton from (c, h) = 0; max|delta| is taken over both components.
  * pi, pf, po, pg: [B, L, H]; ui, uf, uo, ug: [H]; h0, c0: [B, H] or NULL;
- * h, c: [B, L, H] outputs.  tol, max_iter, info, trace as for the GRU.
+ * h, c: [B, L, H] outputs.  tol, max_iter, info, trace as for the GRU,
+ * except that this cell has no single-tile kernel: the chunk rule applies at
+ * every L when max_iter <= 64.
  */
 int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H,
                          const float *pi, const float *pf, const float *po,
