@@ -42,6 +42,8 @@ ALG_BYTES = {
     "c4_gru_long_fwd_adj": 48,   # fwd: 3 p in, h out; adjoint: g, 3 p, h in, 3 dp out
     "x_linscan_blk2": 32,        # A (2x2) and b (2) in; h (2) out, per (batch, position, channel)
     "x_lstm_adjoint": 48,        # gh, gc, 4 p, h, c in; 4 dp out
+    "x_lstm_step": 24,           # as c3_lstm: the whole solve's inputs once, outputs once
+    "x_gru_long_step": 16,       # 3 p in; h out (the forward of c4 alone)
 }
 DOMINANT = {
     "c1_linscan": "chunk_scan_kernel<LinDiagOp>",
@@ -50,6 +52,10 @@ DOMINANT = {
     "c4_gru_long_fwd_adj": "newton_chain_kernel<GruChain> + chunk_scan_kernel<GruAdjOp> (whole step)",
     "x_linscan_blk2": "chunk_scan_kernel<LinBlk2Op>",
     "x_lstm_adjoint": "chunk_scan_kernel<LstmAdjOp> + reduce_u_kernel (whole step)",
+    "x_lstm_step": "chunk_scan_kernel<LstmStepOp> (one launch per iteration up to the cap; "
+                   "launches after convergence exit at once)",
+    "x_gru_long_step": "chunk_scan_kernel<GruStepOp> (one launch per iteration up to the cap; "
+                       "launches after convergence exit at once)",
 }
 # HBM bytes per launch of the dominant kernel from rocprofv3 counter runs
 # (FETCH_SIZE x 2.000 and WRITE_SIZE x 1.000, the factors a plain 1 GiB device
@@ -77,6 +83,10 @@ DESCRIBE = {
                       "A~U(-0.6,0.6), b~N(0,1), h0=0",
     "x_lstm_adjoint": "diagonal LSTM reverse adjoint at the converged forward, B=8 L=2048 H=2048, "
                       "p~N(0,1), u~U(-0.5,0.5), gh, gc~N(0,1), h0=c0=0",
+    "x_lstm_step": "the LSTM Newton forward of c3_lstm on the per-iteration path "
+                   "(PARARNN_LSTM_PATH=step)",
+    "x_gru_long_step": "the GRU Newton forward of c4_gru_long_fwd_adj on the per-iteration path "
+                       "(PARARNN_GRU_PATH=step)",
 }
 
 
@@ -180,6 +190,31 @@ class Workload:
             self._step = lambda: api.lstm_forward(*args, None, None, tol=self.w["tol"],
                                                   max_iter=cap, out_h=self.out, out_c=self.out_c,
                                                   info=self.info, ws=self.ws)
+        elif name in ("x_lstm_step", "x_gru_long_step"):
+            lstm = name == "x_lstm_step"
+            cap = self.w["cap"]
+            self.out = torch.empty(B, L, H, device=dev)
+            self.out_c = torch.empty(B, L, H, device=dev) if lstm else None
+            op = api.OP_LSTM_FORWARD if lstm else api.OP_GRU_FORWARD
+            self.ws = api.new_workspace(api.workspace_bytes(op, B, L, H, cap), dev)
+            keys = ("pi", "pf", "po", "pg", "ui", "uf", "uo", "ug") if lstm else \
+                ("pz", "pr", "pc", "uz", "ur", "uc")
+            args = [t[k] for k in keys]
+            var = "PARARNN_LSTM_PATH" if lstm else "PARARNN_GRU_PATH"
+
+            def step():
+                # the library reads the path override at each call
+                os.environ[var] = "step"
+                try:
+                    if lstm:
+                        return api.lstm_forward(*args, None, None, tol=self.w["tol"], max_iter=cap,
+                                                out_h=self.out, out_c=self.out_c, info=self.info,
+                                                ws=self.ws)
+                    return api.gru_forward(*args, None, tol=self.w["tol"], max_iter=cap,
+                                           out=self.out, info=self.info, ws=self.ws)
+                finally:
+                    del os.environ[var]
+            self._step = step
         elif name == "c4_gru_long_fwd_adj":
             self.out = torch.empty(B, L, H, device=dev)
             cap = self.w["cap"]
@@ -234,8 +269,10 @@ def cpu_baseline(name, host):
     import numpy as np
 
     import oracle
+    from nonlinear_rnn_solve_pararnn_amd import synth
     oracle.build(force=False)
     threads = oracle.num_threads()
+    name = synth.WORKLOADS[name].get("same_as", name)
     if name in ("c2_gru_fused", "c4_gru_long_fwd_adj", "c0_gru_tiny"):
         args = [host[k].astype(np.float64) for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
         fn = lambda: oracle.gru_rollout(*args)
@@ -267,7 +304,7 @@ def cpu_baseline(name, host):
     fn()  # page-in
     reps, t = 0, 0.0
     t0 = time.perf_counter()
-    while t < 2.0 and reps < 20:
+    while t < 10.0 and reps < 400:
         fn()
         reps += 1
         t = time.perf_counter() - t0
@@ -315,7 +352,8 @@ def main():
     for name in names:
         log("workload", name)
         wl = Workload(name, dev)
-        iters = wl.iterations() if name in ("c2_gru_fused", "c3_lstm", "c4_gru_long_fwd_adj") else None
+        iters = wl.iterations() if name in ("c2_gru_fused", "c3_lstm", "c4_gru_long_fwd_adj",
+                                            "x_lstm_step", "x_gru_long_step") else None
         wall_ms, ev_ms = time_workload(wl, args.steps, args.warmup)
         results[name] = {
             "elements": wl.elements,

@@ -33,6 +33,11 @@ WORKLOADS = {
     "x_linscan_blk2": dict(kind="linscan_blk2", B=16, L=4096, H=512),
     # the LSTM adjoint at the LSTM forward's shape, with upstream gradients on h and c
     "x_lstm_adjoint": dict(kind="lstm_adjoint", B=8, L=2048, H=2048, tol=1e-4, cap=32),
+    # the per-iteration Newton path (one launch per iteration) on the inputs of
+    # the LSTM forward and of the long GRU forward
+    "x_lstm_step": dict(kind="lstm", B=8, L=2048, H=2048, tol=1e-4, cap=32, same_as="c3_lstm"),
+    "x_gru_long_step": dict(kind="gru", B=16, L=1048576, H=1, tol=1e-4, cap=32,
+                            same_as="c4_gru_long_fwd_adj"),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -117,8 +122,11 @@ def linscan_blk2_inputs(B, L, H, seed, scale=0.6, h0=False):
 
 
 def workload_inputs(name: str) -> dict:
-    """Inputs of one named workload, seed 1000 + its index in WORKLOAD_ORDER."""
+    """Inputs of one named workload, seed 1000 + its index in WORKLOAD_ORDER
+    (a workload with `same_as` takes that workload's inputs)."""
     w = WORKLOADS[name]
+    if "same_as" in w:
+        return workload_inputs(w["same_as"])
     seed = 1000 + WORKLOAD_ORDER.index(name)
     B, L, H = w["B"], w["L"], w["H"]
     if name == "c0_gru_tiny":

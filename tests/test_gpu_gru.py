@@ -94,9 +94,12 @@ def test_fused_workload_full(orc):
     assert info[1] == 1 and err <= FWD_ATOL
 
 
-def test_long_workload_forward_full(orc):
-    """B=16, L=1,048,576, H=1, tol 1e-4, cap 32: every output checked."""
-    say("gru long workload")
+@pytest.mark.parametrize("path", ["chain", "step"])
+def test_long_workload_forward_full(orc, monkeypatch, path):
+    """B=16, L=1,048,576, H=1, tol 1e-4, cap 32: every output checked, on the
+    chained kernel and on the per-iteration launches."""
+    monkeypatch.setenv("PARARNN_GRU_PATH", path)
+    say("gru long workload", path)
     d = synth.workload_inputs("c4_gru_long_fwd_adj")
     h, info = _run(d, 1e-4, 32, with_h0=False)
     ref = orc.gru_rollout(*gru_args(d))
