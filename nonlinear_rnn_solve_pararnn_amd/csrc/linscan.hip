@@ -90,6 +90,164 @@ struct LinDiagOp {
     }
 };
 
+// ---------------------------------------------------------------- diag scan, prefetching
+// The diagonal scan with channel lanes, as a persistent kernel that keeps the
+// next tile's inputs in flight while the current tile finishes.  A tile is
+// the scan_core.hpp channel-lane tile (NWC groups of 64 channels x NW/NWC
+// sub-chunks of C positions).  Each workgroup draws its next ticket while it
+// composes the current tile; after the first barrier every wave issues the
+// loads of the next tile into a second register set, so they overlap the
+// look-back, the second barrier, the carry-in and the stores of the current
+// one.  The holder waves issue theirs after their look-back: loads complete in
+// issue order, so look-back loads queued behind them would wait for them.
+// The two register sets alternate by unrolling the tile loop twice.  Every
+// wait is still on a smaller ticket (a workgroup finishes its tiles in ticket
+// order), and each workgroup draws exactly one ticket past the last tile.
+struct DiagTilePos {
+    int64_t q, b, j, pos0, base;
+    bool ok;
+};
+
+template <int NW, int C, int NWC>
+__device__ __forceinline__ DiagTilePos diag_tile_pos(const ScanGeo &g, int64_t ticket) {
+    constexpr int NWT = NW / NWC;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int cw = w % NWC, tw = w / NWC;
+    DiagTilePos p;
+    const int64_t per_q = g.B * g.ncb;
+    p.q = ticket / per_q;
+    const int64_t rest = ticket - p.q * per_q;
+    p.b = rest / g.ncb;
+    const int64_t cb = rest - p.b * g.ncb;
+    p.j = (cb * NWC + cw) * 64 + lane;
+    p.ok = p.j < g.H;
+    p.pos0 = p.q * ((int64_t)NWT * C) + (int64_t)tw * C;
+    p.base = idx3(p.b, p.pos0, p.ok ? p.j : 0, g.L, g.H);
+    return p;
+}
+
+template <int C>
+__device__ __forceinline__ void diag_tile_load(const LinDiagOp &op, const DiagTilePos &p, float (&ea)[C],
+                                               float (&eb)[C]) {
+    if (p.ok && p.pos0 + C <= op.L) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            ea[i] = ld_once(op.a + p.base + i * op.H);
+            eb[i] = ld_once(op.b + p.base + i * op.H);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const bool v = p.ok && p.pos0 + i < op.L;
+            ea[i] = v ? ld_once(op.a + p.base + i * op.H) : 1.0f;
+            eb[i] = v ? ld_once(op.b + p.base + i * op.H) : 0.0f;
+        }
+    }
+}
+
+// One tile (inputs already in ea/eb); prefetches the next ticket's tile into
+// na/nb.  Returns whether there is a next tile.
+template <int NW, int C, int NWC>
+__device__ __forceinline__ bool diag_pf_tile(const LinDiagOp &op, const ScanGeo &g, uint32_t draws,
+                                             const DiagTilePos &p, uint32_t tag, float (&ea)[C],
+                                             float (&eb)[C], Ticket *s_next, Aff1 *s_part, float *s_carry,
+                                             DiagTilePos &pn, float (&na)[C], float (&nb)[C],
+                                             Ticket &tn) {
+    using M = MonoidT<1>;
+    using D = Desc<1>;
+    constexpr int NWT = NW / NWC;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int cw = w % NWC, tw = w / NWC;
+    const bool holder = tw == NWT - 1;
+    const int cslot = cw * 64 + lane;
+
+    Aff1 acc = M::id();
+#pragma unroll
+    for (int i = 0; i < C; ++i) acc = M::then(acc, Aff1{ea[i], eb[i]});
+    if (tid == 0) *s_next = draw_ticket(g.hdr, draws);
+    s_part[w * 64 + lane] = acc;
+    lds_barrier();
+    tn = *s_next;
+    const bool more = tn.index < g.ntiles;
+    if (more) pn = diag_tile_pos<NW, C, NWC>(g, tn.index);
+    if (more && !holder) diag_tile_load<C>(op, pn, na, nb);
+
+    Aff1 ex = M::id();
+    for (int k = 0; k < tw; ++k) ex = M::then(ex, s_part[(k * NWC + cw) * 64 + lane]);
+    if (holder) {
+        const Aff1 tot = M::then(ex, acc);
+        const int64_t stride = g.B * g.H, slot = p.b * g.H + p.j;
+        const int64_t dsc = p.q * stride + slot;
+        float xin = 0.0f;
+        if (p.ok) {
+            if (p.q == 0) {
+                xin = op.h0 != nullptr ? op.h0[p.b * g.H + p.j] : 0.0f;
+            } else {
+                D::put_agg(g.agg + dsc * D::kAggWords, tot, tag);
+                xin = lane_lookback<1>(g, tag, p.q, stride, slot);
+            }
+            D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin), tag);
+        }
+        s_carry[cslot] = xin;
+        if (more) diag_tile_load<C>(op, pn, na, nb);
+    }
+    lds_barrier();
+
+    float x = M::apply(ex, s_carry[cslot]);
+    if (p.ok && p.pos0 + C <= op.L) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            x = fmaf(ea[i], x, eb[i]);
+            op.h[p.base + i * op.H] = x;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            x = fmaf(ea[i], x, eb[i]);
+            if (p.ok && p.pos0 + i < op.L) op.h[p.base + i * op.H] = x;
+        }
+    }
+    return more;
+}
+
+template <int NW, int C, int NWC>
+__global__ __launch_bounds__(NW * 64) void diag_pf_kernel(LinDiagOp op, ScanGeo g) {
+    static_assert(NW % NWC == 0, "channel groups tile the waves");
+    __shared__ Aff1 s_part[NW * 64];
+    __shared__ float s_carry[64 * NWC];
+    __shared__ Ticket s_tk[2];
+    const uint32_t draws = (uint32_t)(g.ntiles + gridDim.x);  // one draw past the end per workgroup
+    if (threadIdx.x == 0) s_tk[0] = draw_ticket(g.hdr, draws);
+    __syncthreads();
+    Ticket tx = s_tk[0], ty;
+    if (tx.index >= g.ntiles) return;
+    DiagTilePos px = diag_tile_pos<NW, C, NWC>(g, tx.index), py;
+    float xa[C], xb[C], ya[C], yb[C];
+    diag_tile_load<C>(op, px, xa, xb);
+    for (;;) {
+        if (!diag_pf_tile<NW, C, NWC>(op, g, draws, px, tx.tag, xa, xb, &s_tk[1], s_part, s_carry, py, ya, yb, ty))
+            return;
+        if (!diag_pf_tile<NW, C, NWC>(op, g, draws, py, ty.tag, ya, yb, &s_tk[0], s_part, s_carry, px, xa, xb, tx))
+            return;
+    }
+}
+
+template <int NW, int C, int NWC>
+static hipError_t launch_diag_pf(const LinDiagOp &op, const ScanGeo &g, hipStream_t s) {
+    static int per_cu = 0;
+    if (per_cu == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, diag_pf_kernel<NW, C, NWC>, NW * 64, 0) != hipSuccess ||
+            n <= 0)
+            n = 1;
+        per_cu = n;
+    }
+    const int64_t slots = (int64_t)per_cu * device_cu_count();
+    const int64_t grid = g.ntiles < slots ? g.ntiles : slots;
+    hipLaunchKernelGGL((diag_pf_kernel<NW, C, NWC>), dim3((unsigned)grid), dim3(NW * 64), 0, s, op, g);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- 2x2 scan
 // h_t = A_t h_{t-1} + b_t with A_t a 2x2 block per (batch, channel).
 struct LinBlk2Op {
@@ -177,6 +335,20 @@ hipError_t linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const f
                         const float *h0, float *h, char *ws, hipStream_t s) {
     LinDiagOp op{a, b, h0, h, L, H};
     constexpr TileCfg c = kCfgLinDiag;
+    if (kDiagPrefetch && H >= kChannelLanesMinH) {
+        const ScanWs w = scan_ws(c, 1, B, L, H);
+        ScanGeo g;
+        g.B = B;
+        g.L = L;
+        g.H = H;
+        g.ncb = w.sh.ncb;
+        g.nq = w.sh.nq;
+        g.ntiles = w.sh.ntiles;
+        g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
+        g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
+        g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
+        return launch_diag_pf<c.nw_cl, c.c_cl, c.ncw_cl>(op, g, s);
+    }
     return run_scan<LinDiagOp, 1, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
 }
 

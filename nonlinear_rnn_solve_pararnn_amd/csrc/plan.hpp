@@ -15,7 +15,9 @@ struct TileCfg {
     int nw_tl, c_tl;  // time lanes (H < 32)
     int ncw_cl = 1;   // channel lanes: groups of 64 channels per workgroup
 };
-constexpr TileCfg kCfgLinDiag{16, 32, 4, 16, 4};
+constexpr TileCfg kCfgLinDiag{16, 16, 4, 16, 2};
+// The diagonal scan with channel lanes prefetches the next tile (linscan.hip).
+constexpr bool kDiagPrefetch = true;
 constexpr TileCfg kCfgLinBlk2{16, 8, 4, 8, 2};
 constexpr TileCfg kCfgGruStep{4, 16, 8, 16};
 constexpr TileCfg kCfgLstmStep{16, 8, 4, 8};
