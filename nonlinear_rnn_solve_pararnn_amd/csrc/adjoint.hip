@@ -190,6 +190,11 @@ struct GruAdjOp {
 
 // ---------------------------------------------------------------- LSTM
 // State order (c, h) as (x, y).  Map nu -> J^T (g + nu).
+//
+// Per position only ten values are kept between the two phases; the rest of
+// the Jacobian and of dh/dp follow from them (cells.hpp, LSTM partials):
+//   j10 = odtc j00, j11 = uo dho + odtc j01, dh/dp_{i,f,g} = odtc dc/dp_{i,f,g},
+// with odtc = o (1 - tanh^2 c) and dho = o (1 - o) tanh c.
 struct LstmAdjOp {
     static constexpr int S = 2;
     const float *pi, *pf, *po, *pg, *ui, *uf, *uo, *ug, *h0, *c0, *h, *c, *gh, *gc;
@@ -198,11 +203,30 @@ struct LstmAdjOp {
     int64_t L, H;
 
     struct Elem {
-        float j00, j01, j10, j11, gcv, ghv;
-        float dci, dcf, dcg, dhi, dhf, dho, dhg, hp;
+        float j00, j01, gcv, ghv, dci, dcf, dcg, odtc, dho, hp;
     };
     __device__ bool active() const { return true; }
     __device__ float2s init_state(const TilePos &) const { return {0.0f, 0.0f}; }
+
+    // Record and transposed map of position t (kk its element index).
+    __device__ __forceinline__ Aff2 elem_at(const TilePos &tp, int64_t t, int64_t kk, float wi, float wf,
+                                            float wo, float wg, Elem &e) const {
+        float hp, cp;
+        if (t == 0) {
+            hp = h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f;
+            cp = c0 != nullptr ? c0[tp.b * H + tp.j] : 0.0f;
+        } else {
+            hp = h[kk - H];
+            cp = c[kk - H];
+        }
+        const LstmAdj r = lstm_adj(cp, hp, ld_once(pi + kk), ld_once(pf + kk), ld_once(po + kk),
+                                   ld_once(pg + kk), wi, wf, wo, wg);
+        e = {r.j00, r.j01, gc != nullptr ? ld_once(gc + kk) : 0.0f, ld_once(gh + kk),
+             r.dci, r.dcf, r.dcg, r.odtc, r.dho, hp};
+        // J^T and J^T g, with the two derived entries formed as phase2 forms them
+        const float j10 = e.odtc * e.j00, j11 = fmaf(wo, e.dho, e.odtc * e.j01);
+        return {e.j00, j10, e.j01, j11, fmaf(e.j00, e.gcv, j10 * e.ghv), fmaf(e.j01, e.gcv, j11 * e.ghv)};
+    }
 
     template <int C>
     __device__ Aff2 phase1(const TilePos &tp, Elem (&e)[C]) const {
@@ -214,31 +238,22 @@ struct LstmAdjOp {
             wg = ug[tp.j];
         }
         Aff2 acc = MonoidT<2>::id();
+        if (tp.ok && tp.pos0 + C <= L) {  // every position inside: no test per position
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                const int64_t t = L - 1 - (tp.pos0 + i);
+                acc = MonoidT<2>::then(acc, elem_at(tp, t, idx3(tp.b, t, tp.j, L, H), wi, wf, wo, wg, e[i]));
+            }
+            return acc;
+        }
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             const int64_t pos = tp.pos0 + i;
-            Aff2 m;
+            Aff2 m = MonoidT<2>::id();
+            e[i] = {1.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
             if (tp.ok && pos < L) {
                 const int64_t t = L - 1 - pos;
-                const int64_t kk = idx3(tp.b, t, tp.j, L, H);
-                float hp, cp;
-                if (t == 0) {
-                    hp = h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f;
-                    cp = c0 != nullptr ? c0[tp.b * H + tp.j] : 0.0f;
-                } else {
-                    hp = h[kk - H];
-                    cp = c[kk - H];
-                }
-                const LstmAdj r = lstm_adj(cp, hp, ld_once(pi + kk), ld_once(pf + kk), ld_once(po + kk), ld_once(pg + kk), wi, wf, wo, wg);
-                e[i] = {r.j00, r.j01, r.j10, r.j11, gc != nullptr ? ld_once(gc + kk) : 0.0f, ld_once(gh + kk),
-                        r.dci, r.dcf, r.dcg, r.dhi, r.dhf, r.dho, r.dhg, hp};
-                // J^T and J^T g
-                m = {e[i].j00, e[i].j10, e[i].j01, e[i].j11,
-                     fmaf(e[i].j00, e[i].gcv, e[i].j10 * e[i].ghv),
-                     fmaf(e[i].j01, e[i].gcv, e[i].j11 * e[i].ghv)};
-            } else {
-                e[i] = {1.0f, 0.0f, 0.0f, 1.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-                m = MonoidT<2>::id();
+                m = elem_at(tp, t, idx3(tp.b, t, tp.j, L, H), wi, wf, wo, wg, e[i]);
             }
             acc = MonoidT<2>::then(acc, m);
         }
@@ -248,6 +263,7 @@ struct LstmAdjOp {
     template <int C, int NW, bool CL>
     __device__ void phase2(const TilePos &tp, Elem (&e)[C], float2s nu) const {
         float su[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        const float wo = tp.ok ? uo[tp.j] : 0.0f;
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             const int64_t pos = tp.pos0 + i;
@@ -255,10 +271,11 @@ struct LstmAdjOp {
                 const int64_t t = L - 1 - pos;
                 const int64_t kk = idx3(tp.b, t, tp.j, L, H);
                 const float lc = e[i].gcv + nu.x, lh = e[i].ghv + nu.y;
-                const float di = fmaf(e[i].dci, lc, e[i].dhi * lh);
-                const float df = fmaf(e[i].dcf, lc, e[i].dhf * lh);
+                const float olh = e[i].odtc * lh;
+                const float di = e[i].dci * (lc + olh);
+                const float df = e[i].dcf * (lc + olh);
                 const float dO = e[i].dho * lh;
-                const float dg = fmaf(e[i].dcg, lc, e[i].dhg * lh);
+                const float dg = e[i].dcg * (lc + olh);
                 gpi[kk] = di;
                 gpf[kk] = df;
                 gpo[kk] = dO;
@@ -267,7 +284,9 @@ struct LstmAdjOp {
                 su[1] = fmaf(df, e[i].hp, su[1]);
                 su[2] = fmaf(dO, e[i].hp, su[2]);
                 su[3] = fmaf(dg, e[i].hp, su[3]);
-                nu = {fmaf(e[i].j00, lc, e[i].j10 * lh), fmaf(e[i].j01, lc, e[i].j11 * lh)};
+                // nu = J^T lambda with j10 = odtc j00 and j11 = uo dho + odtc j01
+                const float j10 = e[i].odtc * e[i].j00, j11 = fmaf(wo, e[i].dho, e[i].odtc * e[i].j01);
+                nu = {fmaf(e[i].j00, lc, j10 * lh), fmaf(e[i].j01, lc, j11 * lh)};
                 if (t == 0) {
                     if (gh0 != nullptr) gh0[tp.b * H + tp.j] = nu.y;
                     if (gc0 != nullptr) gc0[tp.b * H + tp.j] = nu.x;

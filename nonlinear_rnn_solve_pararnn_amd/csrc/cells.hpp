@@ -84,6 +84,7 @@ struct LstmAdj {
     float j00, j01, j10, j11;
     float dci, dcf, dcg;
     float dhi, dhf, dho, dhg;
+    float odtc;  // o (1 - tanh^2 c): dh/dp_{i,f,g} = odtc dc/dp_{i,f,g}, j10 = odtc j00
 };
 
 __device__ __forceinline__ LstmAdj lstm_adj(float cp, float hp, float pi, float pf, float po,
@@ -109,6 +110,7 @@ __device__ __forceinline__ LstmAdj lstm_adj(float cp, float hp, float pi, float 
     a.dhf = odtc * a.dcf;
     a.dho = (o - o * o) * tc;
     a.dhg = odtc * a.dcg;
+    a.odtc = odtc;
     return a;
 }
 

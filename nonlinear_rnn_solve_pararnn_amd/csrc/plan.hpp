@@ -22,7 +22,7 @@ constexpr TileCfg kCfgLinBlk2{16, 8, 4, 8, 2};
 constexpr TileCfg kCfgGruStep{4, 16, 8, 16};
 constexpr TileCfg kCfgLstmStep{16, 8, 4, 8};
 constexpr TileCfg kCfgGruAdj{4, 8, 16, 8};
-constexpr TileCfg kCfgLstmAdj{16, 4, 4, 4};
+constexpr TileCfg kCfgLstmAdj{8, 16, 4, 4};
 constexpr TileCfg kCfgGruChain{8, 16, 8, 16};
 constexpr TileCfg kCfgLstmChain{8, 8, 8, 8};
 // Waves per SIMD the chained kernels are compiled for (bounds their registers).
