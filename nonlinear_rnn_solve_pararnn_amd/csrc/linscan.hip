@@ -272,14 +272,23 @@ struct LinBlk2Op {
         const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
         const float4 *A4 = reinterpret_cast<const float4 *>(A);
         const float2 *b2 = reinterpret_cast<const float2 *>(b);
+        if (tp.ok && tp.pos0 + C <= L) {  // every position inside: no test per position
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            if (tp.ok && tp.pos0 + i < L) {
+            for (int i = 0; i < C; ++i) {
                 const float4 m = ld_once(A4 + base + i * H);
                 const float2 v = ld_once(b2 + base + i * H);
                 e[i].m = {m.x, m.y, m.z, m.w, v.x, v.y};
-            } else {
-                e[i].m = MonoidT<2>::id();
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                if (tp.ok && tp.pos0 + i < L) {
+                    const float4 m = ld_once(A4 + base + i * H);
+                    const float2 v = ld_once(b2 + base + i * H);
+                    e[i].m = {m.x, m.y, m.z, m.w, v.x, v.y};
+                } else {
+                    e[i].m = MonoidT<2>::id();
+                }
             }
         }
         Aff2 acc = MonoidT<2>::id();
@@ -291,10 +300,18 @@ struct LinBlk2Op {
     __device__ void phase2(const TilePos &tp, Elem (&e)[C], float2s x) const {
         const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
         float2 *h2 = reinterpret_cast<float2 *>(h);
+        if (tp.ok && tp.pos0 + C <= L) {
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            x = MonoidT<2>::apply(e[i].m, x);
-            if (tp.ok && tp.pos0 + i < L) h2[base + i * H] = make_float2(x.x, x.y);
+            for (int i = 0; i < C; ++i) {
+                x = MonoidT<2>::apply(e[i].m, x);
+                h2[base + i * H] = make_float2(x.x, x.y);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                x = MonoidT<2>::apply(e[i].m, x);
+                if (tp.ok && tp.pos0 + i < L) h2[base + i * H] = make_float2(x.x, x.y);
+            }
         }
     }
 };
