@@ -119,19 +119,28 @@ struct GruAdjOp {
                 return acc;
             }
         }
+        const auto cell = [&](int i) {
+            const int64_t t = L - 1 - (tp.pos0 + i);
+            const int64_t kk = idx3(tp.b, t, tp.j, L, H);
+            const float hp = t == 0 ? (h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f) : h[kk - H];
+            float J, dz, dr, dc, r;
+            gru_j_dp(hp, ld_once(pz + kk), ld_once(pr + kk), ld_once(pc + kk), wz, wr, wc, J, dz, dr, dc, r);
+            e[i] = {J, ld_once(gh + kk), dz, dr, dc, dz * hp, dr * hp, dc * r * hp};
+        };
+        if (tp.ok && tp.pos0 + C <= L) {  // every position inside: no test per position
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                cell(i);
+                acc = {acc.a * e[i].J, fmaf(e[i].J, acc.b, e[i].J * e[i].g)};
+            }
+            return acc;
+        }
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            const int64_t pos = tp.pos0 + i;
-            if (tp.ok && pos < L) {
-                const int64_t t = L - 1 - pos;
-                const int64_t kk = idx3(tp.b, t, tp.j, L, H);
-                const float hp = t == 0 ? (h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f) : h[kk - H];
-                float J, dz, dr, dc, r;
-                gru_j_dp(hp, ld_once(pz + kk), ld_once(pr + kk), ld_once(pc + kk), wz, wr, wc, J, dz, dr, dc, r);
-                e[i] = {J, ld_once(gh + kk), dz, dr, dc, dz * hp, dr * hp, dc * r * hp};
-            } else {
+            if (tp.ok && tp.pos0 + i < L)
+                cell(i);
+            else
                 e[i] = {1.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-            }
             acc = {acc.a * e[i].J, fmaf(e[i].J, acc.b, e[i].J * e[i].g)};
         }
         return acc;
@@ -165,24 +174,26 @@ struct GruAdjOp {
                 done = true;
             }
         }
-        if (!done) {
+        const auto update = [&](int i) {
+            const int64_t t = L - 1 - (tp.pos0 + i);
+            const int64_t kk = idx3(tp.b, t, tp.j, L, H);
+            const float lam = e[i].g + nu;
+            gpz[kk] = e[i].dz * lam;
+            gpr[kk] = e[i].dr * lam;
+            gpc[kk] = e[i].dc * lam;
+            su[0] = fmaf(e[i].xz, lam, su[0]);
+            su[1] = fmaf(e[i].xr, lam, su[1]);
+            su[2] = fmaf(e[i].xc, lam, su[2]);
+            nu = e[i].J * lam;
+            if (t == 0 && gh0 != nullptr) gh0[tp.b * H + tp.j] = nu;
+        };
+        if (!done && tp.ok && tp.pos0 + C <= L) {
 #pragma unroll
-            for (int i = 0; i < C; ++i) {
-                const int64_t pos = tp.pos0 + i;
-                if (tp.ok && pos < L) {
-                    const int64_t t = L - 1 - pos;
-                    const int64_t kk = idx3(tp.b, t, tp.j, L, H);
-                    const float lam = e[i].g + nu;
-                    gpz[kk] = e[i].dz * lam;
-                    gpr[kk] = e[i].dr * lam;
-                    gpc[kk] = e[i].dc * lam;
-                    su[0] = fmaf(e[i].xz, lam, su[0]);
-                    su[1] = fmaf(e[i].xr, lam, su[1]);
-                    su[2] = fmaf(e[i].xc, lam, su[2]);
-                    nu = e[i].J * lam;
-                    if (t == 0 && gh0 != nullptr) gh0[tp.b * H + tp.j] = nu;
-                }
-            }
+            for (int i = 0; i < C; ++i) update(i);
+        } else if (!done) {
+#pragma unroll
+            for (int i = 0; i < C; ++i)
+                if (tp.ok && tp.pos0 + i < L) update(i);
         }
         if (partial != nullptr) store_u_partials<NW, CL, 3>(tp, su, partial);
     }
@@ -264,10 +275,11 @@ struct LstmAdjOp {
     __device__ void phase2(const TilePos &tp, Elem (&e)[C], float2s nu) const {
         float su[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         const float wo = tp.ok ? uo[tp.j] : 0.0f;
+        const bool whole = tp.ok && tp.pos0 + C <= L;
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             const int64_t pos = tp.pos0 + i;
-            if (tp.ok && pos < L) {
+            if (whole || (tp.ok && pos < L)) {
                 const int64_t t = L - 1 - pos;
                 const int64_t kk = idx3(tp.b, t, tp.j, L, H);
                 const float lc = e[i].gcv + nu.x, lh = e[i].ghv + nu.y;

@@ -111,18 +111,28 @@ struct GruStepOp {
                 return acc;
             }
         }
+        const auto cell = [&](int i) {
+            const int64_t kk = base + i * H;
+            const float hc = k == 1 ? 0.0f : h[kk];
+            float F, J;
+            gru_f_j(hp, ld_once(pz + kk), ld_once(pr + kk), ld_once(pc + kk), wz, wr, wc, F, J);
+            e[i] = {J, F - hc, hc};
+            hp = hc;
+        };
+        if (tp.ok && tp.pos0 + C <= L) {  // every position inside: no test per position
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                cell(i);
+                acc = {acc.a * e[i].J, fmaf(e[i].J, acc.b, e[i].beta)};
+            }
+            return acc;
+        }
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            if (tp.ok && tp.pos0 + i < L) {
-                const int64_t kk = base + i * H;
-                const float hc = k == 1 ? 0.0f : h[kk];
-                float F, J;
-                gru_f_j(hp, ld_once(pz + kk), ld_once(pr + kk), ld_once(pc + kk), wz, wr, wc, F, J);
-                e[i] = {J, F - hc, hc};
-                hp = hc;
-            } else {
+            if (tp.ok && tp.pos0 + i < L)
+                cell(i);
+            else
                 e[i] = {1.0f, 0.0f, 0.0f};
-            }
             acc = {acc.a * e[i].J, fmaf(e[i].J, acc.b, e[i].beta)};
         }
         return acc;
@@ -148,19 +158,21 @@ struct GruStepOp {
                 done = true;
             }
         }
-        if (!done) {
+        const auto update = [&](int i) {
+            d = fmaf(e[i].J, d, e[i].beta);
+            const float hn = e[i].hc + d;
+            h[base + i * H] = hn;
+            const uint32_t ad = abs_bits(d);
+            mx = ad > mx ? ad : mx;
+            if (i == C - 1 && tp.sub == tp.nsub - 1) bnd_next[tp.q * B * H + tp.b * H + tp.j] = hn;
+        };
+        if (!done && tp.ok && tp.pos0 + C <= L) {
 #pragma unroll
-            for (int i = 0; i < C; ++i) {
-                if (tp.ok && tp.pos0 + i < L) {
-                    d = fmaf(e[i].J, d, e[i].beta);
-                    const float hn = e[i].hc + d;
-                    h[base + i * H] = hn;
-                    const uint32_t ad = abs_bits(d);
-                    mx = ad > mx ? ad : mx;
-                    if (i == C - 1 && tp.sub == tp.nsub - 1)
-                        bnd_next[tp.q * B * H + tp.b * H + tp.j] = hn;
-                }
-            }
+            for (int i = 0; i < C; ++i) update(i);
+        } else if (!done) {
+#pragma unroll
+            for (int i = 0; i < C; ++i)
+                if (tp.ok && tp.pos0 + i < L) update(i);
         }
         wg_max_to<NW>(mx, maxd + (k - 1));
     }
@@ -210,18 +222,30 @@ struct LstmStepOp {
             }
         }
         Aff2 acc = MonoidT<2>::id();
+        const auto cell = [&](int i) {
+            const int64_t kk = base + i * H;
+            const float cc = k == 1 ? 0.0f : c[kk];
+            const float hc = k == 1 ? 0.0f : h[kk];
+            const Lstm2 r = lstm_f_j(cp, hp, ld_once(pi + kk), ld_once(pf + kk), ld_once(po + kk),
+                                     ld_once(pg + kk), wi, wf, wo, wg);
+            e[i].m = {r.j00, r.j01, r.j10, r.j11, r.Fc - cc, r.Fh - hc};
+            e[i].cc = cc;
+            e[i].hc = hc;
+            cp = cc;
+            hp = hc;
+        };
+        if (tp.ok && tp.pos0 + C <= L) {  // every position inside: no test per position
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                cell(i);
+                acc = MonoidT<2>::then(acc, e[i].m);
+            }
+            return acc;
+        }
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             if (tp.ok && tp.pos0 + i < L) {
-                const int64_t kk = base + i * H;
-                const float cc = k == 1 ? 0.0f : c[kk];
-                const float hc = k == 1 ? 0.0f : h[kk];
-                const Lstm2 r = lstm_f_j(cp, hp, ld_once(pi + kk), ld_once(pf + kk), ld_once(po + kk), ld_once(pg + kk), wi, wf, wo, wg);
-                e[i].m = {r.j00, r.j01, r.j10, r.j11, r.Fc - cc, r.Fh - hc};
-                e[i].cc = cc;
-                e[i].hc = hc;
-                cp = cc;
-                hp = hc;
+                cell(i);
             } else {
                 e[i].m = MonoidT<2>::id();
                 e[i].cc = 0.0f;
@@ -236,20 +260,25 @@ struct LstmStepOp {
     __device__ void phase2(const TilePos &tp, Elem (&e)[C], float2s d) const {
         const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
         uint32_t mx = 0;
+        const auto update = [&](int i) {
+            d = MonoidT<2>::apply(e[i].m, d);
+            const float cn = e[i].cc + d.x;
+            const float hn = e[i].hc + d.y;
+            c[base + i * H] = cn;
+            h[base + i * H] = hn;
+            const uint32_t a0 = abs_bits(d.x), a1 = abs_bits(d.y);
+            mx = a0 > mx ? a0 : mx;
+            mx = a1 > mx ? a1 : mx;
+            if (i == C - 1 && tp.sub == tp.nsub - 1)
+                bnd_next[tp.q * B * H + tp.b * H + tp.j] = make_float2(cn, hn);
+        };
+        if (tp.ok && tp.pos0 + C <= L) {
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            if (tp.ok && tp.pos0 + i < L) {
-                d = MonoidT<2>::apply(e[i].m, d);
-                const float cn = e[i].cc + d.x;
-                const float hn = e[i].hc + d.y;
-                c[base + i * H] = cn;
-                h[base + i * H] = hn;
-                const uint32_t a0 = abs_bits(d.x), a1 = abs_bits(d.y);
-                mx = a0 > mx ? a0 : mx;
-                mx = a1 > mx ? a1 : mx;
-                if (i == C - 1 && tp.sub == tp.nsub - 1)
-                    bnd_next[tp.q * B * H + tp.b * H + tp.j] = make_float2(cn, hn);
-            }
+            for (int i = 0; i < C; ++i) update(i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < C; ++i)
+                if (tp.ok && tp.pos0 + i < L) update(i);
         }
         wg_max_to<NW>(mx, maxd + (k - 1));
     }

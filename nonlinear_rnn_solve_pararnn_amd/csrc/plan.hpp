@@ -20,7 +20,7 @@ constexpr TileCfg kCfgLinDiag{16, 16, 4, 16, 2};
 constexpr bool kDiagPrefetch = true;
 constexpr TileCfg kCfgLinBlk2{16, 8, 4, 8, 1};
 constexpr TileCfg kCfgGruStep{4, 16, 8, 16};
-constexpr TileCfg kCfgLstmStep{16, 8, 4, 8};
+constexpr TileCfg kCfgLstmStep{8, 16, 4, 8};
 constexpr TileCfg kCfgGruAdj{4, 8, 16, 8};
 constexpr TileCfg kCfgLstmAdj{8, 16, 4, 4};
 constexpr TileCfg kCfgGruChain{8, 16, 8, 16};
