@@ -1,7 +1,9 @@
-// linscan.hip -- the exported linear-recurrence scans (diagonal and 2x2
-// block) on the chunked look-back scan of scan_core.hpp, plus the small fill
-// kernel that initialises info words, traces and per-iteration slots, and
-// the device query shared by the launchers.
+// linscan.hip -- the exported linear-recurrence scans: the diagonal scan
+// (channel lanes: its own persistent kernel that prefetches the next tile;
+// time lanes: the generic chunked look-back scan of scan_core.hpp) and the
+// 2x2 block scan (scan_core.hpp), plus the small fill kernel that
+// initialises info words, traces and per-iteration slots, and the device
+// query shared by the launchers.
 #include "launch.hpp"
 #include "scan_core.hpp"
 

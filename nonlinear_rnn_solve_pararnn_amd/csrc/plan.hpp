@@ -36,12 +36,13 @@ static_assert(kCfgGruStep.ncw_cl == 1 && kCfgLstmStep.ncw_cl == 1 && kCfgGruAdj.
                   kCfgLstmAdj.ncw_cl == 1 && kCfgGruChain.ncw_cl == 1 && kCfgLstmChain.ncw_cl == 1,
               "channel groups are for the exported scans only");
 constexpr int64_t kChannelLanesMinH = 32;
-// Look-back descriptors polled at once by one channel lane (diagonal, 2x2).
+// Look-back descriptors polled at once by one channel lane (diagonal, 2x2;
+// batches of 2 to 8 measured slower with the current tiles).
 constexpr int kLbBatchDiag = 1;
+constexpr int kLbBatchBlk2 = 1;
 // Scan launches use a grid of as many workgroups as fit on the device at
 // once, each drawing tiles until none is left (instead of one per tile).
 constexpr bool kScanPersistent = true;
-constexpr int kLbBatchBlk2 = 1;
 
 struct ScanShape {
     bool channel_lanes;
