@@ -27,7 +27,7 @@ def _gru_case(orc, d, with_h0=True, want_u=True, want_h0=True):
 
 @pytest.mark.parametrize("B,L,H", [(1, 1, 1), (1, 64, 4), (2, 100, 3), (3, 257, 70),
                                    (2, 5000, 1), (2, 700, 33), (4, 128, 128),
-                                   (1, 12, 1), (2, 4098, 1), (3, 8192, 1)])
+                                   (1, 12, 1), (2, 4098, 1), (3, 8192, 1), (2, 300, 31), (2, 300, 32)])
 def test_gru_adjoint_matches_bptt(orc, B, L, H):
     say("gru adjoint", B, L, H)
     d = synth.gru_inputs(B, L, H, seed=80 + H, h0=True, grad=True)
@@ -77,7 +77,8 @@ def _lstm_case(orc, d, with_gc=True):
     return errs
 
 
-@pytest.mark.parametrize("B,L,H", [(1, 1, 1), (2, 100, 3), (3, 257, 70), (2, 3000, 1), (2, 500, 33)])
+@pytest.mark.parametrize("B,L,H", [(1, 1, 1), (2, 100, 3), (3, 257, 70), (2, 3000, 1), (2, 500, 33),
+                                   (2, 300, 31), (2, 300, 32)])
 @pytest.mark.parametrize("with_gc", [True, False])
 def test_lstm_adjoint_matches_bptt(orc, B, L, H, with_gc):
     say("lstm adjoint", B, L, H, with_gc)

@@ -57,7 +57,9 @@ def test_L_iterations_reproduce_rollout(orc, monkeypatch, path):
     assert max_abs(h, orc.gru_rollout(*gru_args(d), h0=d["h0"])) <= FWD_ATOL
 
 
-SHAPES = [(1, 1, 1), (2, 100, 70), (3, 37, 5), (2, 512, 20), (1, 33, 16), (4, 300, 130)]
+# H = 31 is the widest time-lane layout, H = 32 the narrowest channel-lane one.
+SHAPES = [(1, 1, 1), (2, 100, 70), (3, 37, 5), (2, 512, 20), (1, 33, 16), (4, 300, 130), (2, 300, 31),
+          (2, 300, 32)]
 
 
 @pytest.mark.parametrize("path", PATHS)

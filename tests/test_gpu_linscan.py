@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 # 4096 / 64 positions, ragged tails in L and in the channel blocks.
 DIAG_SHAPES = [
     (1, 1, 1), (2, 100, 3), (3, 257, 70), (2, 5000, 1), (1, 70000, 2),
-    (4, 1000, 64), (2, 3001, 33), (1, 64, 4), (3, 130, 200),
+    (4, 1000, 64), (2, 3001, 33), (1, 64, 4), (3, 130, 200), (2, 300, 31), (2, 300, 32),
 ]
 
 
@@ -169,3 +169,25 @@ def test_workspace_reused_across_entry_points_and_shapes(orc, monkeypatch):
         h = host(api.gru_forward(*g, tol=1e-5, max_iter=16, info=info, ws=ws))
         ref = orc.gru_rollout(*(d5[k] for k in ("pz", "pr", "pc", "uz", "ur", "uc")))
         assert int(info[1]) == 1 and max_abs(h, ref) <= FWD_ATOL
+
+
+def test_two_streams_with_their_own_workspaces(orc):
+    """Calls enqueued on two streams at once, each stream with the workspace
+    the binding keeps for it, overlap on the device and stay independent."""
+    d1 = synth.linscan_diag_inputs(4, 6000, 96, seed=31)
+    d2 = synth.linscan_diag_inputs(3, 5000, 2, seed=32)
+    a1, b1, a2, b2 = dev(d1["a"]), dev(d1["b"]), dev(d2["a"]), dev(d2["b"])
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    out1, out2 = [], []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            out1.append(api.linscan_diag(a1, b1))
+        with torch.cuda.stream(s2):
+            out2.append(api.linscan_diag(a2, b2))
+    torch.cuda.synchronize()
+    ref1, ref2 = orc.linscan_diag(d1["a"], d1["b"]), orc.linscan_diag(d2["a"], d2["b"])
+    for h in out1:
+        assert max_abs(host(h), ref1) <= FWD_ATOL
+    for h in out2:
+        assert max_abs(host(h), ref2) <= FWD_ATOL
