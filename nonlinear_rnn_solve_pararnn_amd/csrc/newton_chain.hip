@@ -6,21 +6,25 @@
 // A tile is one chunk of T positions (of 64 channels, or of one channel for
 // small H).  Its workgroup loads the gate inputs once and then runs Newton
 // iterations k = 1, 2, ... on registers:
-//   - the state before the chunk at iterate k-1 is the last state the
-//     previous chunk published for iteration k-1 (h0 for the first chunk);
+//   - the state before the chunk at iterate k-1 (h0 for the first chunk)
+//     is kept on chip: zero at iterate 0, then advanced at every iteration
+//     by the delta that enters the chunk, which is the previous chunk's
+//     inclusive delta and so its last position's update;
 //   - the cells give J_t and beta_t = F_t - s_t, composed per sub-chunk and
 //     scanned inside the workgroup;
 //   - the delta entering the chunk at iteration k comes from a decoupled
 //     look-back over the previous chunks' iteration-k records;
-//   - s += delta, and the chunk publishes its iteration-k records (aggregate,
-//     inclusive delta, last state).
+//   - s += delta, and the chunk publishes its iteration-k records (aggregate
+//     and inclusive delta).
 // A chunk stops after iteration k once max|delta| <= tol over it and every
 // chunk before it (a prefix AND of per-chunk flags, found by a second
 // look-back), so the last chunk stops exactly when global Newton over the
 // sequence would.  A stopped chunk's states are frozen: later iterations of
-// its successors take a zero delta and its last state from it.  With
-// tol = 0 no chunk stops before the cap and every iterate equals global
-// Newton's.
+// its successors take a zero delta from it, so their copy of its last state
+// stays put.  With tol = 0 no chunk stops before the cap and every iterate
+// equals global Newton's (up to rounding: the state before a chunk is the sum
+// of the deltas that entered it, which equals the previous chunk's stored
+// last state in exact arithmetic).
 //
 // Every wait is on a chunk with a smaller ticket, whose workgroup is already
 // running (tickets are drawn by running workgroups, in sequence order), so
@@ -39,7 +43,7 @@ struct ChainGeo {
     int32_t cap;
     float tol;
     uint64_t *hdr;
-    uint64_t *agg, *inc, *bnd;  // [cap][ndesc][words]: iteration k at slice k-1
+    uint64_t *agg, *inc;        // [cap][ndesc][words]: iteration k at slice k-1
     uint64_t *stop;             // [ntiles]: last iteration of the tile (tagged)
     uint64_t *fagg, *finc;      // [cap][ntiles]: converged flag of the tile, and of it and all before it
     int32_t *info;
@@ -216,26 +220,6 @@ __device__ __forceinline__ bool stopped_before(const ChainGeo &g, int64_t ptile,
     return s < k;
 }
 
-// Last state of chunk p at iterate kk (kk >= 1), or its final state if it
-// stopped before kk.
-template <int S>
-__device__ typename MonoidT<S>::State chain_boundary(const ChainGeo &g, uint32_t tag, int kk, int64_t d,
-                                                     int64_t ptile, const Ahead<S> &ahead) {
-    using D = Desc<S>;
-    typename MonoidT<S>::State x;
-    if (ahead.get(x, tag)) return x;
-    int at = kk;
-    for (uint32_t polls = 0; polls < kMaxPolls; ++polls) {
-        if (D::get_inc(g.bnd + ((size_t)(at - 1) * g.ndesc + d) * D::kIncWords, x, tag)) return x;
-        if (at == kk) {
-            int s;
-            if (stopped_before(g, ptile, tag, kk, &s)) at = s;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    return nan_state<S>();
-}
-
 // Delta entering chunk q at iteration k for one channel lane.
 template <int S>
 __device__ typename MonoidT<S>::State chain_lane_lookback(const ChainGeo &g, uint32_t tag, int k,
@@ -409,7 +393,6 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
     const int64_t base = idx3(b, pos0, ok ? j : 0, g.L, g.H);
     const int64_t stride = g.B * g.H, slot = b * g.H + j;
     const int64_t dsc = q * stride + slot;
-    const int64_t ptile = ((q - 1) * g.B + b) * g.ncb + cb;
     const bool holder = CL ? (w == NW - 1) : (tid == NT - 1);
 
     bool val[C];
@@ -423,17 +406,22 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
 #pragma unroll
     for (int i = 0; i < C; ++i) s[i] = M::zero();
     const State init = (ok && q == 0 && sub == 0) ? cell.init(b, j, g.H) : M::zero();
+    // The state before this chunk (the previous chunk's last state) at the
+    // current iterate, kept by the sub-chunk-0 threads: zero at iterate 0
+    // (the initial guess), then advanced by the delta entering the chunk at
+    // each iteration, which is the previous chunk's inclusive delta (zero
+    // once that chunk has stopped).
+    State hb = M::zero();
 
     int k = 1;
     bool conv = false;
     for (;; ++k) {
         const size_t kofs = (size_t)(k - 1) * g.ndesc;
-        // Records of the previous chunk read ahead of the cells: its last
-        // state at iterate k-1, its inclusive delta and converged flag at k.
-        Ahead<S> a_bnd{}, a_inc{};  // zero words never carry a launch tag
+        // Records of the previous chunk read ahead of the cells: its
+        // inclusive delta and converged flag at k.
+        Ahead<S> a_inc{};  // zero words never carry a launch tag
         uint64_t a_flag = 0;
         if (q > 0) {
-            if (sub == 0 && k > 1 && ok) a_bnd.issue(g.bnd + ((size_t)(k - 2) * g.ndesc + dsc - stride) * D::kIncWords);
             if (CL ? (holder && ok) : (w == NW - 1 && q - 1 - lane >= 0))
                 a_inc.issue(g.inc + (kofs + (CL ? dsc - stride : (q - 1 - lane) * stride + slot)) * D::kIncWords);
             if (w == 0 && q - 1 - lane >= 0)
@@ -456,10 +444,7 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
         State nb = M::zero();
         if (!CL) nb = shfl_up_s(s[C - 1], 1);  // every lane active for the shuffle
         if (sub == 0) {
-            if (q == 0)
-                hp = init;
-            else if (k > 1 && ok)
-                hp = chain_boundary<S>(g, tag, k - 1, dsc - stride, ptile, a_bnd);
+            hp = q == 0 ? init : hb;
         } else if (k > 1) {
             if (CL)
                 hp = s_last[(w - 1) * 64 + lane];
@@ -531,7 +516,9 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
         lds_barrier();
 
         // apply: delta through the sub-chunk, s += delta
-        State dlt = M::apply(ex, s_carry[CL ? lane : 0]);
+        const State cin = s_carry[CL ? lane : 0];
+        if (sub == 0) hb = state_add(hb, cin);  // the previous chunk's last state at iterate k
+        State dlt = M::apply(ex, cin);
         uint32_t mx = 0;
 #pragma unroll
         for (int i = 0; i < C; ++i) {
@@ -541,7 +528,6 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
             mx = a > mx ? a : mx;
         }
         mx = clamp_nan_to_inf(mx);
-        if (holder && ok && q + 1 < g.nq) D::put_inc(g.bnd + (kofs + dsc) * D::kIncWords, s[C - 1], tag);
         if (CL)
             s_last[w * 64 + lane] = s[C - 1];
         else if (lane == 63)
@@ -641,7 +627,6 @@ static hipError_t chain_forward(const TileCfg &cfg, const Cell &cell, int64_t B,
     g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
     g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
     g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
-    g.bnd = reinterpret_cast<uint64_t *>(ws + w.bnd);
     g.stop = reinterpret_cast<uint64_t *>(ws + w.stop);
     g.fagg = reinterpret_cast<uint64_t *>(ws + w.fagg);
     g.finc = reinterpret_cast<uint64_t *>(ws + w.finc);

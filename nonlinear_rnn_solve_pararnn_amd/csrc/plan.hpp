@@ -131,11 +131,11 @@ inline NewtonWs newton_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64
 }
 
 // Workspace of the chained Newton kernel: header, the records of every
-// iteration (aggregate, inclusive delta and last state of each chunk and
-// channel), a stop word per tile and per-iteration converged flags per tile.
+// iteration (aggregate and inclusive delta of each chunk and channel), a stop
+// word per tile and per-iteration converged flags per tile.
 struct ChainWs {
     ScanShape sh;
-    size_t hdr, agg, inc, bnd, stop, fagg, finc, total;
+    size_t hdr, agg, inc, stop, fagg, finc, total;
 };
 
 inline ChainWs chain_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64_t H, int32_t cap) {
@@ -145,7 +145,6 @@ inline ChainWs chain_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64_t
     w.hdr = c.take(8);
     w.agg = c.take((size_t)cap * w.sh.ndesc * desc_agg_words(S) * 8);
     w.inc = c.take((size_t)cap * w.sh.ndesc * desc_inc_words(S) * 8);
-    w.bnd = c.take((size_t)cap * w.sh.ndesc * desc_inc_words(S) * 8);
     w.stop = c.take((size_t)w.sh.ntiles * 8);
     w.fagg = c.take((size_t)cap * w.sh.ntiles * 8);
     w.finc = c.take((size_t)cap * w.sh.ntiles * 8);
