@@ -23,7 +23,7 @@ constexpr TileCfg kCfgGruStep{4, 16, 8, 16};
 constexpr TileCfg kCfgLstmStep{8, 16, 4, 8};
 constexpr TileCfg kCfgGruAdj{4, 8, 16, 8};
 constexpr TileCfg kCfgLstmAdj{8, 16, 4, 4};
-constexpr TileCfg kCfgGruChain{8, 16, 8, 16};
+constexpr TileCfg kCfgGruChain{4, 16, 8, 16};
 constexpr TileCfg kCfgLstmChain{8, 8, 8, 8};
 // Waves per SIMD the chained kernels are compiled for (bounds their registers).
 constexpr int kChainMinWaves = 1;
