@@ -63,12 +63,12 @@ DOMINANT = {
 # taken on: the sha256 prefix of those sources is checked at run time and the
 # figure is dropped (null) once any of them has changed.
 TRAFFIC = {
-    "c1_linscan": {"bytes": 551266508 + 289021952,
+    "c1_linscan": {"bytes": 551445504 + 289021952,
                    "sources": ["common.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-                   "sha256": "4d571ccbaf2d751c"},
-    "c2_gru_fused": {"bytes": 419291955 + 152472166,
+                   "sha256": "baee66652d9f525a"},
+    "c2_gru_fused": {"bytes": 419260416 + 152481587,
                      "sources": ["common.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
-                     "sha256": "5511d49dc4a38939"},
+                     "sha256": "1994d8fbb6dff556"},
 }
 DESCRIBE = {
     "c1_linscan": "linear diagonal recurrence h_t = a_t h_{t-1} + b_t, B=16 L=4096 H=1024, "
