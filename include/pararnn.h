@@ -21,8 +21,9 @@
  *  - Every pointer named as a tensor is a DEVICE pointer (hipMalloc'd or
  *    torch-allocated, at least 4-byte aligned).  The caller owns all memory,
  *    including the workspace; the library never allocates or frees and keeps
- *    no state of its own between calls (what persists lives in the caller's
- *    workspace).  Outputs must not alias inputs.
+ *    no state of its own between calls beyond cached device properties (what
+ *    persists lives in the caller's workspace).  Outputs must not alias
+ *    inputs.
  *  - `ws`/`ws_bytes`: a device scratch buffer of at least
  *    pararnn_workspace_bytes(...) bytes (256-byte aligned).  It must be
  *    zero-filled before its first use (hipMemset, torch.zeros); every call
