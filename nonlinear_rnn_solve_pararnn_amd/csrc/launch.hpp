@@ -25,6 +25,10 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
 // Compute units of the current device (queried once per device).
 int device_cu_count();
+// Workgroups of `threads` threads of `kernel` that fit on one CU at once (at
+// least 1).  Launchers keep the result in a function-local static, which C++
+// initialises once and thread-safely.
+int blocks_per_cu(const void *kernel, int threads);
 hipError_t fill(const FillRange *r, int n, hipStream_t s);
 
 hipError_t linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const float *b,

@@ -4,6 +4,8 @@
 // 2x2 block scan (scan_core.hpp), plus the small fill kernel that
 // initialises info words, traces and per-iteration slots, and the device
 // query shared by the launchers.
+#include <atomic>
+
 #include "launch.hpp"
 #include "scan_core.hpp"
 
@@ -236,14 +238,7 @@ __global__ __launch_bounds__(NW * 64) void diag_pf_kernel(LinDiagOp op, ScanGeo 
 
 template <int NW, int C, int NWC>
 static hipError_t launch_diag_pf(const LinDiagOp &op, const ScanGeo &g, hipStream_t s) {
-    static int per_cu = 0;
-    if (per_cu == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, diag_pf_kernel<NW, C, NWC>, NW * 64, 0) != hipSuccess ||
-            n <= 0)
-            n = 1;
-        per_cu = n;
-    }
+    static const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(diag_pf_kernel<NW, C, NWC>), NW * 64);
     const int64_t slots = (int64_t)per_cu * device_cu_count();
     const int64_t grid = g.ntiles < slots ? g.ntiles : slots;
     hipLaunchKernelGGL((diag_pf_kernel<NW, C, NWC>), dim3((unsigned)grid), dim3(NW * 64), 0, s, op, g);
@@ -319,16 +314,22 @@ struct LinBlk2Op {
 };
 
 int device_cu_count() {
-    static int cached[64];
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
+}
+
+int blocks_per_cu(const void *kernel, int threads) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0) n = 1;
+    return n;
 }
 
 template <class Op, int S, int NWC, int CC, int NWT, int CT, int NCW>

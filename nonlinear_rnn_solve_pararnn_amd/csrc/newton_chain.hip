@@ -589,14 +589,8 @@ __global__ __launch_bounds__(NW * 64, kChainMinWaves) void newton_chain_kernel(C
 
 template <class Cell, int NW, int C, bool CL>
 static hipError_t launch_chain(const Cell &cell, const ChainGeo &g, hipStream_t s) {
-    static int per_cu = 0;
-    if (per_cu == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, newton_chain_kernel<Cell, NW, C, CL>, NW * 64, 0) !=
-                hipSuccess || n <= 0)
-            n = 1;
-        per_cu = n;
-    }
+    static const int per_cu =
+        blocks_per_cu(reinterpret_cast<const void *>(newton_chain_kernel<Cell, NW, C, CL>), NW * 64);
     const int64_t slots = (int64_t)per_cu * device_cu_count();
     const int64_t grid = g.ntiles < slots ? g.ntiles : slots;
     hipLaunchKernelGGL((newton_chain_kernel<Cell, NW, C, CL>), dim3((unsigned)grid), dim3(NW * 64), 0, s, cell, g);

@@ -354,14 +354,8 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
 template <class Op, int NW, int C, bool CL, int NWC>
 static int64_t scan_grid(int64_t ntiles) {
     if (!kScanPersistent) return ntiles;
-    static int per_cu = 0;
-    if (per_cu == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, chunk_scan_kernel<Op, NW, C, CL, NWC>, NW * 64, 0) !=
-                hipSuccess || n <= 0)
-            n = 1;
-        per_cu = n;
-    }
+    static const int per_cu =
+        blocks_per_cu(reinterpret_cast<const void *>(chunk_scan_kernel<Op, NW, C, CL, NWC>), NW * 64);
     const int64_t slots = (int64_t)per_cu * device_cu_count();
     return ntiles < slots ? ntiles : slots;
 }
