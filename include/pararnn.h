@@ -169,7 +169,8 @@ int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H,
  * h (and c for the LSTM): the forward outputs [B, L, H].  grad_h: [B, L, H];
  * grad_c: [B, L, H] or NULL (LSTM only; NULL means zero).  grad_p[k]:
  * [B, L, H] outputs (overwritten).  grad_u: NULL, or an array whose entries
- * are [H] outputs or NULL.  grad_h0, grad_c0: [B, H] outputs or NULL.
+ * are [H] outputs or NULL (any of them requires H < 2^31).  grad_h0,
+ * grad_c0: [B, H] outputs or NULL.
  */
 int pararnn_adjoint_backward(int32_t cell, int64_t B, int64_t L, int64_t H,
                              const float *const *p, const float *const *u,

@@ -210,6 +210,9 @@ int pararnn_adjoint_backward(int32_t cell, int64_t B, int64_t L, int64_t H, cons
     a.h = h;
     a.gh = grad_h;
     a.gh0 = grad_h0;
+    bool want_u = false;
+    for (int q = 0; q < ng; ++q) want_u = want_u || a.gu[q] != nullptr;
+    if (want_u && H > 0x7fffffff) return PARARNN_ERR_INVALID;  // the dL/du reduction has one workgroup per channel
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (cell == PARARNN_CELL_GRU) {
         if (grad_c || grad_c0) return PARARNN_ERR_INVALID;
