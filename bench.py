@@ -48,7 +48,7 @@ ALG_BYTES = {
 DOMINANT = {
     "c1_linscan": "diag_pf_kernel<16,16,2> (chunked scan, next tile prefetched)",
     "c2_gru_fused": "gru_fused_kernel<16>",
-    "c3_lstm": "newton_chain_kernel<LstmChain> (one launch for every iteration)",
+    "c3_lstm": "newton_local_kernel<LstmChain> (one launch for every iteration; each workgroup owns whole chains)",
     "c4_gru_long_fwd_adj": "newton_chain_kernel<GruChain> + chunk_scan_kernel<GruAdjOp> (whole step)",
     "x_linscan_blk2": "chunk_scan_kernel<LinBlk2Op>",
     "x_lstm_adjoint": "chunk_scan_kernel<LstmAdjOp> + reduce_u_kernel (whole step)",

@@ -60,18 +60,30 @@ size_t lstm_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
 // Path of a Newton forward.  The GRU takes the fused on-chip kernel while
 // the sequence fits one workgroup's registers; longer sequences (and the
 // LSTM) take the chained kernel, which keeps each chunk on chip for all its
-// iterations, unless the cap is above kChainMaxCap.  The per-iteration
-// launches remain selectable: PARARNN_GRU_PATH=fused|chain|step and
-// PARARNN_LSTM_PATH=chain|step override the choice (for testing every path;
-// a chain request above kChainMaxCap still takes the per-iteration path).
+// iterations, unless the cap is above kChainMaxCap.  The chained kernel lets
+// each workgroup own whole chains of chunks when there are at least as many
+// chains as workgroup slots, and chains chunks across workgroups otherwise.
+// PARARNN_GRU_PATH=fused|chain|local|step and PARARNN_LSTM_PATH=chain|local|step
+// override the choice (for testing every path; "chain" and "local" force the
+// two forms of the chained kernel, "local" only with channel lanes; a chain
+// request above kChainMaxCap still takes the per-iteration path).
 enum class Path { Fused, Chain, Step, Invalid };
 Path env_path(const char *name) {
     const char *env = getenv(name);
     if (env == nullptr) return Path::Invalid;
     if (strcmp(env, "fused") == 0) return Path::Fused;
-    if (strcmp(env, "chain") == 0) return Path::Chain;
+    if (strcmp(env, "chain") == 0 || strcmp(env, "local") == 0) return Path::Chain;
     if (strcmp(env, "step") == 0) return Path::Step;
     return Path::Invalid;
+}
+// Form of the chained kernel: 1 workgroups own whole chains, 0 chunks are
+// chained across workgroups, -1 chosen from the shape.
+int env_chain_local(const char *name) {
+    const char *env = getenv(name);
+    if (env == nullptr) return -1;
+    if (strcmp(env, "local") == 0) return 1;
+    if (strcmp(env, "chain") == 0) return 0;
+    return -1;
 }
 Path gru_path(int64_t L, int32_t cap) {
     const bool fits = fused_c_for(L) != 0;
@@ -144,7 +156,7 @@ int pararnn_gru_forward(int64_t B, int64_t L, int64_t H, const float *pz, const 
     if (!dims_ok(B, L, H) || !pz || !pr || !pc || !uz || !ur || !uc || !h) return PARARNN_ERR_INVALID;
     if (!(tol >= 0.0f) || max_iter < 1) return PARARNN_ERR_INVALID;  // rejects NaN too
     const int32_t cap = eff_cap(max_iter, L);
-    GruFwdArgs a{B, L, H, pz, pr, pc, uz, ur, uc, h0, h, tol, cap, info, trace};
+    GruFwdArgs a{B, L, H, pz, pr, pc, uz, ur, uc, h0, h, tol, cap, info, trace, env_chain_local("PARARNN_GRU_PATH")};
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Path path = gru_path(L, cap);
     if (path == Path::Invalid) return PARARNN_ERR_UNSUPPORTED;
@@ -173,7 +185,8 @@ int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H, const float *pi, const
     if (!(tol >= 0.0f) || max_iter < 1) return PARARNN_ERR_INVALID;
     const int32_t cap = eff_cap(max_iter, L);
     if (!ws || ws_bytes < lstm_fwd_ws(B, L, H, cap) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
-    LstmFwdArgs a{B, L, H, pi, pf, po, pg, ui, uf, uo, ug, h0, c0, h, c, tol, cap, info, trace};
+    LstmFwdArgs a{B, L, H, pi, pf, po, pg, ui, uf, uo, ug, h0, c0, h, c, tol, cap, info, trace,
+                  env_chain_local("PARARNN_LSTM_PATH")};
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool chain = lstm_path(cap) == Path::Chain;
     if (!grid_ok(scan_shape(chain ? kCfgLstmChain : kCfgLstmStep, B, L, H).ntiles)) return PARARNN_ERR_INVALID;

@@ -44,6 +44,7 @@ struct GruFwdArgs {
     int32_t cap;
     int32_t *info;
     float *trace;
+    int local;  // chained kernel: 1 workgroups own whole chains, 0 never, -1 choose
 };
 hipError_t gru_forward_step(const GruFwdArgs &a, char *ws, hipStream_t s);
 hipError_t gru_forward_fused(const GruFwdArgs &a, hipStream_t s);
@@ -57,6 +58,7 @@ struct LstmFwdArgs {
     int32_t cap;
     int32_t *info;
     float *trace;
+    int local;  // as for the GRU
 };
 hipError_t lstm_forward_step(const LstmFwdArgs &a, char *ws, hipStream_t s);
 hipError_t lstm_forward_chain(const LstmFwdArgs &a, char *ws, hipStream_t s);

@@ -364,8 +364,14 @@ __device__ __forceinline__ float state_add(float a, float b) { return a + b; }
 __device__ __forceinline__ float2s state_add(float2s a, float2s b) { return {a.x + b.x, a.y + b.y}; }
 
 // ---------------------------------------------------------------- tile
-template <class Cell, int NW, int C, bool CL>
-__device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, uint32_t tag) {
+// LOCAL: the workgroup also ran the previous chunk of this chain (see
+// newton_local_kernel), so the previous chunk's inclusive deltas are in LDS
+// (s_rec, iteration k at row k-1), and kprev/cprev hold its last iteration and
+// whether it stopped converged; nothing goes through global memory.
+template <class Cell, int NW, int C, bool CL, bool LOCAL = false>
+__device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, uint32_t tag,
+                                           int &kprev, bool &cprev) {
+    static_assert(!LOCAL || CL, "workgroups own whole chains only with channel lanes");
     constexpr int S = Cell::S;
     using M = MonoidT<S>;
     using D = Desc<S>;
@@ -379,6 +385,7 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
     __shared__ State s_last[CL ? NT : NW];
     __shared__ uint32_t s_wmax[NW];
     __shared__ int s_stop;
+    __shared__ State s_rec[LOCAL ? kChainMaxCap * 64 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t per_q = g.B * g.ncb;
@@ -421,7 +428,7 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
         // inclusive delta and converged flag at k.
         Ahead<S> a_inc{};  // zero words never carry a launch tag
         uint64_t a_flag = 0;
-        if (q > 0) {
+        if (!LOCAL && q > 0) {
             if (CL ? (holder && ok) : (w == NW - 1 && q - 1 - lane >= 0))
                 a_inc.issue(g.inc + (kofs + (CL ? dsc - stride : (q - 1 - lane) * stride + slot)) * D::kIncWords);
             if (w == 0 && q - 1 - lane >= 0)
@@ -490,7 +497,15 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
         }
 
         // delta entering the chunk at iteration k
-        if (CL) {
+        if (LOCAL) {
+            if (holder) {
+                // the previous chunk's inclusive delta at k (zero once it has
+                // stopped), replaced by this chunk's for the next chunk
+                const State din = (q > 0 && k <= kprev) ? s_rec[(k - 1) * 64 + lane] : M::zero();
+                s_rec[(k - 1) * 64 + lane] = M::apply(tot, din);
+                s_carry[lane] = din;
+            }
+        } else if (CL) {
             if (holder) {
                 State din = M::zero();
                 if (ok) {
@@ -539,6 +554,18 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) m = s_wmax[ww] > m ? s_wmax[ww] : m;
         // stop once this chunk and every chunk before it have converged
+        if (LOCAL) {
+            // every thread decides alike: the previous chunk counts as
+            // converged from the iteration it stopped at, if it converged
+            conv = __uint_as_float(m) <= g.tol && (q == 0 || (cprev && k >= kprev));
+            if (tid == 0 && g.trace != nullptr) {
+                const uint32_t cur = __hip_atomic_load(g.trace + (k - 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (m > cur)
+                    __hip_atomic_fetch_max(g.trace + (k - 1), m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (conv || k >= g.cap) break;
+            continue;
+        }
         if (w == 0) {
             const bool own = __uint_as_float(m) <= g.tol;
             const size_t fofs = (size_t)(k - 1) * g.ntiles + ticket;
@@ -561,7 +588,9 @@ __device__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, 
         conv = s_stop != 0;
         if (conv || k >= g.cap) break;
     }
-    if (tid == 0) st_coherent(g.stop + ticket, tagged((float)k, tag));
+    if (!LOCAL && tid == 0) st_coherent(g.stop + ticket, tagged((float)k, tag));
+    kprev = k;
+    cprev = conv;
     cell.template store<C>(base, g.H, val, whole, s);
     if (tid == 0 && g.info != nullptr) {
         if (k > __hip_atomic_load(g.info, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
@@ -581,10 +610,47 @@ __global__ __launch_bounds__(NW * 64, kChainMinWaves) void newton_chain_kernel(C
         __syncthreads();
         const Ticket t = s_ticket;
         if (t.index >= g.ntiles) return;
-        chain_tile<Cell, NW, C, CL>(cell, g, t.index, t.tag);
+        int kprev = 0;
+        bool cprev = false;
+        chain_tile<Cell, NW, C, CL>(cell, g, t.index, t.tag, kprev, cprev);
         if (!persistent) return;
         __syncthreads();  // the tile's last reads of shared memory before the next ticket
     }
+}
+
+// Workgroups that own whole chains (a chain: the chunks of one batch row and
+// channel block): workgroup i runs chains i, i + grid, ... and each chain's
+// chunks in order, so a chunk finds everything it needs from its predecessor
+// in LDS and no workgroup waits on another.  The iterates equal those of the
+// chained kernel above.  Worth it once there are at least as many chains as
+// workgroup slots on the device.
+template <class Cell, int NW, int C>
+__global__ __launch_bounds__(NW * 64, kChainMinWaves) void newton_local_kernel(Cell cell, ChainGeo g) {
+    const int64_t nchains = g.B * g.ncb;
+    for (int64_t ch = blockIdx.x; ch < nchains; ch += gridDim.x) {
+        int kprev = 0;
+        bool cprev = false;
+        for (int64_t q = 0; q < g.nq; ++q) {
+            chain_tile<Cell, NW, C, true, true>(cell, g, q * nchains + ch, 0u, kprev, cprev);
+            __syncthreads();  // the chunk's last reads of shared memory before the next chunk
+        }
+    }
+}
+
+template <class Cell, int NW, int C, bool CL>
+static int64_t chain_slots() {
+    static const int per_cu =
+        blocks_per_cu(reinterpret_cast<const void *>(newton_chain_kernel<Cell, NW, C, CL>), NW * 64);
+    return (int64_t)per_cu * device_cu_count();
+}
+
+template <class Cell, int NW, int C>
+static hipError_t launch_local(const Cell &cell, const ChainGeo &g, hipStream_t s) {
+    static const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(newton_local_kernel<Cell, NW, C>), NW * 64);
+    const int64_t slots = (int64_t)per_cu * device_cu_count(), nchains = g.B * g.ncb;
+    const int64_t grid = nchains < slots ? nchains : slots;
+    hipLaunchKernelGGL((newton_local_kernel<Cell, NW, C>), dim3((unsigned)grid), dim3(NW * 64), 0, s, cell, g);
+    return hipGetLastError();
 }
 
 template <class Cell, int NW, int C, bool CL>
@@ -597,9 +663,12 @@ static hipError_t launch_chain(const Cell &cell, const ChainGeo &g, hipStream_t 
     return hipGetLastError();
 }
 
+// local: 1 workgroups own whole chains, 0 chunks chained across workgroups,
+// -1 choose (own whole chains when there are as many chains as slots).
 template <class Cell, int NWC, int CC, int NWT, int CT>
 static hipError_t chain_forward(const TileCfg &cfg, const Cell &cell, int64_t B, int64_t L, int64_t H,
-                                int32_t cap, float tol, int32_t *info, float *trace, char *ws, hipStream_t s) {
+                                int32_t cap, float tol, int32_t *info, float *trace, int local, char *ws,
+                                hipStream_t s) {
     const ChainWs w = chain_ws(cfg, Cell::S, B, L, H, cap);
     FillRange fr[3] = {
         {info, info ? 1ull : 0ull, 0, 4},                         // iterations = 0
@@ -626,8 +695,9 @@ static hipError_t chain_forward(const TileCfg &cfg, const Cell &cell, int64_t B,
     g.finc = reinterpret_cast<uint64_t *>(ws + w.finc);
     g.info = info;
     g.trace = reinterpret_cast<uint32_t *>(trace);
-    return w.sh.channel_lanes ? launch_chain<Cell, NWC, CC, true>(cell, g, s)
-                              : launch_chain<Cell, NWT, CT, false>(cell, g, s);
+    if (!w.sh.channel_lanes) return launch_chain<Cell, NWT, CT, false>(cell, g, s);
+    const bool own = local > 0 || (local < 0 && B * w.sh.ncb >= chain_slots<Cell, NWC, CC, true>());
+    return own ? launch_local<Cell, NWC, CC>(cell, g, s) : launch_chain<Cell, NWC, CC, true>(cell, g, s);
 }
 
 hipError_t gru_forward_chain(const GruFwdArgs &a, char *ws, hipStream_t s) {
@@ -644,7 +714,7 @@ hipError_t gru_forward_chain(const GruFwdArgs &a, char *ws, hipStream_t s) {
                 aligned16(a.h);
     constexpr TileCfg c = kCfgGruChain;
     return chain_forward<GruChain, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, cell, a.B, a.L, a.H, a.cap, a.tol,
-                                                                    a.info, a.trace, ws, s);
+                                                                    a.info, a.trace, a.local, ws, s);
 }
 
 hipError_t lstm_forward_chain(const LstmFwdArgs &a, char *ws, hipStream_t s) {
@@ -664,7 +734,7 @@ hipError_t lstm_forward_chain(const LstmFwdArgs &a, char *ws, hipStream_t s) {
     cell.runs = false;
     constexpr TileCfg c = kCfgLstmChain;
     return chain_forward<LstmChain, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, cell, a.B, a.L, a.H, a.cap, a.tol,
-                                                                     a.info, a.trace, ws, s);
+                                                                     a.info, a.trace, a.local, ws, s);
 }
 
 }  // namespace prn

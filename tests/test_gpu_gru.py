@@ -10,7 +10,9 @@ from nonlinear_rnn_solve_pararnn_amd import api, synth
 from tests.gpu_helpers import (FWD_ATOL, ITER_ATOL, dev, gru_args, host, max_abs, say)
 
 pytestmark = pytest.mark.gpu
-PATHS = ["fused", "chain", "step"]
+# "chain" and "local" force the two forms of the chained kernel (chunks chained
+# across workgroups; workgroups owning whole chains, channel lanes only).
+PATHS = ["fused", "chain", "local", "step"]
 
 
 def _run(d, tol, cap, with_h0=True, trace=False):
@@ -73,7 +75,7 @@ def test_shapes_match_rollout(orc, monkeypatch, path, B, L, H):
     assert max_abs(h, orc.gru_rollout(*gru_args(d), h0=d["h0"])) <= FWD_ATOL
 
 
-@pytest.mark.parametrize("path", ["chain", "step"])
+@pytest.mark.parametrize("path", ["chain", "local", "step"])
 @pytest.mark.parametrize("B,L,H", [(2, 513, 20), (1, 5000, 3), (2, 700, 100), (3, 20000, 1),
                                    (1, 12, 1), (2, 4098, 1), (2, 8192, 1), (2, 3000, 200)])
 def test_long_sequences(orc, monkeypatch, path, B, L, H):
@@ -190,12 +192,13 @@ def test_fused_full_tiles_with_h0_and_iterates(orc):
         assert max_abs(h, s) <= ITER_ATOL, k
 
 
+@pytest.mark.parametrize("path", ["chain", "local"])
 @pytest.mark.parametrize("B,L,H", [(2, 1000, 40), (2, 20000, 1)])
-def test_chain_iterates_across_chunks(orc, monkeypatch, B, L, H):
+def test_chain_iterates_across_chunks(orc, monkeypatch, path, B, L, H):
     """Chained path over several chunks (channel lanes: 64-position chunks;
     time lanes: 8192): with tol = 0 no chunk stops early, so the k-th result
     equals the oracle's k-th global Newton iterate."""
-    monkeypatch.setenv("PARARNN_GRU_PATH", "chain")
+    monkeypatch.setenv("PARARNN_GRU_PATH", path)
     d = synth.gru_inputs(B, L, H, seed=66, h0=True)
     for k in (1, 2, 3, 5):
         h, info = _run(d, 0.0, k)
@@ -215,7 +218,7 @@ def test_large_cap_takes_per_iteration_path(orc, monkeypatch):
     assert max_abs(h, orc.gru_rollout(*gru_args(d), h0=d["h0"])) <= FWD_ATOL
 
 
-@pytest.mark.parametrize("path", ["fused", "chain", "step"])
+@pytest.mark.parametrize("path", ["fused", "chain", "local", "step"])
 def test_cap_beyond_sequence_length(orc, monkeypatch, path):
     """A cap far above L is taken as L + 1 (exact after L updates, confirmed by
     the next): same result and count as the oracle, trace zero past the cap."""

@@ -10,7 +10,9 @@ from tests.gpu_helpers import FWD_ATOL, ITER_ATOL, dev, host, lstm_args, max_abs
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["chain", "step"], autouse=True)
+# "chain" and "local" force the two forms of the chained kernel (chunks chained
+# across workgroups; workgroups owning whole chains, channel lanes only).
+@pytest.fixture(params=["chain", "local", "step"], autouse=True)
 def lstm_path(request, monkeypatch):
     monkeypatch.setenv("PARARNN_LSTM_PATH", request.param)
     return request.param
