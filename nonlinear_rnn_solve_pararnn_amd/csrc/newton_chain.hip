@@ -637,17 +637,15 @@ __global__ __launch_bounds__(NW * 64, kChainMinWaves) void newton_local_kernel(C
     }
 }
 
-template <class Cell, int NW, int C, bool CL>
-static int64_t chain_slots() {
-    static const int per_cu =
-        blocks_per_cu(reinterpret_cast<const void *>(newton_chain_kernel<Cell, NW, C, CL>), NW * 64);
+template <class Cell, int NW, int C>
+static int64_t local_slots() {
+    static const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(newton_local_kernel<Cell, NW, C>), NW * 64);
     return (int64_t)per_cu * device_cu_count();
 }
 
 template <class Cell, int NW, int C>
 static hipError_t launch_local(const Cell &cell, const ChainGeo &g, hipStream_t s) {
-    static const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(newton_local_kernel<Cell, NW, C>), NW * 64);
-    const int64_t slots = (int64_t)per_cu * device_cu_count(), nchains = g.B * g.ncb;
+    const int64_t slots = local_slots<Cell, NW, C>(), nchains = g.B * g.ncb;
     const int64_t grid = nchains < slots ? nchains : slots;
     hipLaunchKernelGGL((newton_local_kernel<Cell, NW, C>), dim3((unsigned)grid), dim3(NW * 64), 0, s, cell, g);
     return hipGetLastError();
@@ -664,11 +662,12 @@ static hipError_t launch_chain(const Cell &cell, const ChainGeo &g, hipStream_t 
 }
 
 // local: 1 workgroups own whole chains, 0 chunks chained across workgroups,
-// -1 choose (own whole chains when there are as many chains as slots).
-template <class Cell, int NWC, int CC, int NWT, int CT>
-static hipError_t chain_forward(const TileCfg &cfg, const Cell &cell, int64_t B, int64_t L, int64_t H,
-                                int32_t cap, float tol, int32_t *info, float *trace, int local, char *ws,
-                                hipStream_t s) {
+// -1 choose (own whole chains when there are as many chains as slots for the
+// kernel that owns them).  lcfg is the tile of that kernel (channel lanes).
+template <class Cell, int NWC, int CC, int NWT, int CT, int NWL, int CLC>
+static hipError_t chain_forward(const TileCfg &cfg, const TileCfg &lcfg, const Cell &cell, int64_t B, int64_t L,
+                                int64_t H, int32_t cap, float tol, int32_t *info, float *trace, int local,
+                                char *ws, hipStream_t s) {
     const ChainWs w = chain_ws(cfg, Cell::S, B, L, H, cap);
     FillRange fr[3] = {
         {info, info ? 1ull : 0ull, 0, 4},                         // iterations = 0
@@ -696,8 +695,12 @@ static hipError_t chain_forward(const TileCfg &cfg, const Cell &cell, int64_t B,
     g.info = info;
     g.trace = reinterpret_cast<uint32_t *>(trace);
     if (!w.sh.channel_lanes) return launch_chain<Cell, NWT, CT, false>(cell, g, s);
-    const bool own = local > 0 || (local < 0 && B * w.sh.ncb >= chain_slots<Cell, NWC, CC, true>());
-    return own ? launch_local<Cell, NWC, CC>(cell, g, s) : launch_chain<Cell, NWC, CC, true>(cell, g, s);
+    const ScanShape ls = scan_shape(lcfg, B, L, H);  // 64 channels per tile, like the chained form
+    const bool own = local > 0 || (local < 0 && B * ls.ncb >= local_slots<Cell, NWL, CLC>());
+    if (!own) return launch_chain<Cell, NWC, CC, true>(cell, g, s);
+    g.nq = ls.nq;  // the workgroups owning whole chains use no workspace records
+    g.ntiles = ls.ntiles;
+    return launch_local<Cell, NWL, CLC>(cell, g, s);
 }
 
 hipError_t gru_forward_chain(const GruFwdArgs &a, char *ws, hipStream_t s) {
@@ -712,9 +715,9 @@ hipError_t gru_forward_chain(const GruFwdArgs &a, char *ws, hipStream_t s) {
     cell.h = a.h;
     cell.runs = a.H == 1 && a.L % 4 == 0 && aligned16(a.pz) && aligned16(a.pr) && aligned16(a.pc) &&
                 aligned16(a.h);
-    constexpr TileCfg c = kCfgGruChain;
-    return chain_forward<GruChain, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, cell, a.B, a.L, a.H, a.cap, a.tol,
-                                                                    a.info, a.trace, a.local, ws, s);
+    constexpr TileCfg c = kCfgGruChain, lc = kCfgGruLocal;
+    return chain_forward<GruChain, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, lc.nw_cl, lc.c_cl>(
+        c, lc, cell, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, a.local, ws, s);
 }
 
 hipError_t lstm_forward_chain(const LstmFwdArgs &a, char *ws, hipStream_t s) {
@@ -732,9 +735,9 @@ hipError_t lstm_forward_chain(const LstmFwdArgs &a, char *ws, hipStream_t s) {
     cell.h = a.h;
     cell.c = a.c;
     cell.runs = false;
-    constexpr TileCfg c = kCfgLstmChain;
-    return chain_forward<LstmChain, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, cell, a.B, a.L, a.H, a.cap, a.tol,
-                                                                     a.info, a.trace, a.local, ws, s);
+    constexpr TileCfg c = kCfgLstmChain, lc = kCfgLstmLocal;
+    return chain_forward<LstmChain, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, lc.nw_cl, lc.c_cl>(
+        c, lc, cell, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, a.local, ws, s);
 }
 
 }  // namespace prn

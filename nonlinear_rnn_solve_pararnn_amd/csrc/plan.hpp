@@ -25,6 +25,10 @@ constexpr TileCfg kCfgGruAdj{4, 8, 16, 8};
 constexpr TileCfg kCfgLstmAdj{8, 16, 4, 4};
 constexpr TileCfg kCfgGruChain{4, 16, 8, 16};
 constexpr TileCfg kCfgLstmChain{8, 8, 8, 8};
+// Channel-lane tiles of the chained kernel's form in which workgroups own
+// whole chains (its time-lane fields are unused).
+constexpr TileCfg kCfgGruLocal{16, 8, 8, 16};
+constexpr TileCfg kCfgLstmLocal{8, 8, 8, 8};
 // Waves per SIMD the chained kernels are compiled for (bounds their registers).
 constexpr int kChainMinWaves = 1;
 // Largest Newton cap the chained kernels take (their workspace holds the
@@ -33,7 +37,8 @@ constexpr int32_t kChainMaxCap = 64;
 // Only the exported scans use channel groups: the Newton and adjoint ops
 // reduce over all waves of a workgroup as if they were one channel group.
 static_assert(kCfgGruStep.ncw_cl == 1 && kCfgLstmStep.ncw_cl == 1 && kCfgGruAdj.ncw_cl == 1 &&
-                  kCfgLstmAdj.ncw_cl == 1 && kCfgGruChain.ncw_cl == 1 && kCfgLstmChain.ncw_cl == 1,
+                  kCfgLstmAdj.ncw_cl == 1 && kCfgGruChain.ncw_cl == 1 && kCfgLstmChain.ncw_cl == 1 &&
+                  kCfgGruLocal.ncw_cl == 1 && kCfgLstmLocal.ncw_cl == 1,
               "channel groups are for the exported scans only");
 constexpr int64_t kChannelLanesMinH = 32;
 // Look-back descriptors polled at once by one channel lane (diagonal, 2x2;
