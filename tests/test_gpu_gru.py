@@ -196,7 +196,7 @@ def test_fused_full_tiles_with_h0_and_iterates(orc):
 @pytest.mark.parametrize("B,L,H", [(2, 1000, 40), (2, 20000, 1)])
 def test_chain_iterates_across_chunks(orc, monkeypatch, path, B, L, H):
     """Chained path over several chunks (channel lanes: 64-position chunks;
-    time lanes: 8192): with tol = 0 no chunk stops early, so the k-th result
+    time lanes: 12288): with tol = 0 no chunk stops early, so the k-th result
     equals the oracle's k-th global Newton iterate."""
     monkeypatch.setenv("PARARNN_GRU_PATH", path)
     d = synth.gru_inputs(B, L, H, seed=66, h0=True)
