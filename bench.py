@@ -115,23 +115,31 @@ def roofline(name, elements, kernel_ms):
             "kernel_us": kernel_ms * 1e3}
 
 
-# Arithmetic roof of the fused GRU kernel.  Per position and Newton iteration
-# its loop issues 27.8 plain VALU instructions and 6 transcendental ones (exp2,
-# reciprocal; 541 VALU instructions per 16 positions in the gfx950 assembly).
-# The fp32 vector peak of 157.3 TFLOP/s is 78.6 T lane-operations per second
-# of FMA issue; transcendentals issue at a quarter of that rate, so each costs
-# four slots.
-FUSED_GRU_SLOTS_PER_ELEMENT_ITER = 27.8 + 6 * 4
+# Arithmetic roofs of the Newton kernels that iterate on chip, from their
+# gfx950 assembly (VALU instructions of the Newton loop per position and
+# iteration; transcendentals are exp2 and reciprocal).  The fp32 vector peak of
+# 157.3 TFLOP/s is 78.6 T lane-operations per second of FMA issue;
+# transcendentals issue at a quarter of that rate, so each costs four slots.
+#  - fused GRU: 541 VALU instructions per 16 positions, 27.8 plain and 6
+#    transcendental per position;
+#  - LSTM, workgroups owning whole chains (8 waves x 8 positions): 600 VALU
+#    instructions per 8 positions, 65 plain and 10 transcendental per position
+#    (the cross-wave composition of the sub-chunk maps not counted).
+ALU_SLOTS_PER_ELEMENT_ITER = {
+    "c2_gru_fused": 27.8 + 6 * 4,
+    "c3_lstm": 65.0 + 10 * 4,
+}
 PEAK_VALU_TOPS = 78.6
 
 
-def alu_roofline(elements, iterations, kernel_ms):
-    slots = FUSED_GRU_SLOTS_PER_ELEMENT_ITER * elements * iterations
+def alu_roofline(name, elements, iterations, kernel_ms):
+    per = ALU_SLOTS_PER_ELEMENT_ITER[name]
+    slots = per * elements * iterations
     achieved = slots / (kernel_ms * 1e-3) / 1e12
     return {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_TOPS,
             "unit": "T VALU issue slots/s", "frac": achieved / PEAK_VALU_TOPS,
             "model": "%.1f slots per element and Newton iteration (transcendentals count 4), "
-                     "%d iterations (the most any tile took)" % (FUSED_GRU_SLOTS_PER_ELEMENT_ITER, iterations)}
+                     "%d iterations (the most any tile took)" % (per, iterations)}
 
 
 def log(*a):
@@ -364,8 +372,8 @@ def main():
             "describe": DESCRIBE[name],
             "roofline": roofline(name, wl.elements, ev_ms),
         }
-        if name == "c2_gru_fused" and iters:
-            results[name]["roofline_alu"] = alu_roofline(wl.elements, iters[0], ev_ms)
+        if name in ALU_SLOTS_PER_ELEMENT_ITER and iters:
+            results[name]["roofline_alu"] = alu_roofline(name, wl.elements, iters[0], ev_ms)
         log(json.dumps({name: results[name]}))
         del wl
         torch.cuda.empty_cache()
