@@ -99,6 +99,23 @@ def lstm_inputs(B, L, H, seed, pscale=1.0, ulo=-0.5, uhi=0.5, h0=False,
     return out
 
 
+def layer_inputs(B, L, D, H, ngates, seed):
+    """Trainable-layer draws: x ~ N(0,1) [B,L,D]; weight ~ U(-1/sqrt(D), 1/sqrt(D))
+    [ngates,H,D]; bias ~ U(-0.5,0.5) [ngates,H]; u ~ U(-0.5,0.5) [ngates,H];
+    h0, c0 ~ U(-0.9,0.9) [B,H]; upstream gradients gh, gc ~ N(0,1) [B,L,H]."""
+    rng = _rng(seed)
+    k = 1.0 / np.sqrt(D)
+    out = {"x": _normal(rng, (B, L, D)),
+           "weight": _uniform(rng, (ngates, H, D), -k, k),
+           "bias": _uniform(rng, (ngates, H), -0.5, 0.5),
+           "u": _uniform(rng, (ngates, H), -0.5, 0.5),
+           "h0": _uniform(rng, (B, H), -0.9, 0.9),
+           "c0": _uniform(rng, (B, H), -0.9, 0.9),
+           "gh": _normal(rng, (B, L, H)),
+           "gc": _normal(rng, (B, L, H))}
+    return out
+
+
 def linscan_diag_inputs(B, L, H, seed, alo=0.5, ahi=1.0, h0=False):
     """Diagonal linear recurrence draws: a ~ U(alo,ahi), b ~ N(0,1) [B,L,H];
     optionally h0 ~ N(0,1) [B,H]."""
