@@ -44,6 +44,9 @@ ALG_BYTES = {
     "x_lstm_adjoint": 48,        # gh, gc, 4 p, h, c in; 4 dp out
     "x_lstm_step": 24,           # as c3_lstm: the whole solve's inputs once, outputs once
     "x_gru_long_step": 16,       # 3 p in; h out (the forward of c4 alone)
+    "x_gru_seq": 16,             # 3 p in; h out
+    "x_lstm_seq": 24,            # 4 p in; h, c out
+    "x_gru_long_seq": 16,        # 3 p in; h out
 }
 DOMINANT = {
     "c1_linscan": "diag_pf_kernel<16,16,2> (chunked scan, next tile prefetched)",
@@ -56,6 +59,9 @@ DOMINANT = {
                    "launches after convergence exit at once)",
     "x_gru_long_step": "chunk_scan_kernel<GruStepOp> (one launch per iteration up to the cap; "
                        "launches after convergence exit at once)",
+    "x_gru_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
+    "x_lstm_seq": "lstm_rollout_kernel (sequential application, one thread per channel)",
+    "x_gru_long_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
 }
 # HBM bytes per launch of the dominant kernel from rocprofv3 counter runs
 # (FETCH_SIZE x 2.000 and WRITE_SIZE x 1.000, the factors a plain 1 GiB device
@@ -87,7 +93,18 @@ DESCRIBE = {
                    "(PARARNN_LSTM_PATH=step)",
     "x_gru_long_step": "the GRU Newton forward of c4_gru_long_fwd_adj on the per-iteration path "
                        "(PARARNN_GRU_PATH=step)",
+    "x_gru_seq": "sequential application of the GRU cell on the inputs of c2_gru_fused "
+                 "(B*H = 65536 threads, 512 positions each)",
+    "x_lstm_seq": "sequential application of the LSTM cell on the inputs of c3_lstm "
+                  "(B*H = 16384 threads, 2048 positions each)",
+    "x_gru_long_seq": "sequential application of the GRU cell on the inputs of c4_gru_long_fwd_adj "
+                      "(B*H = 16 threads, 2^20 positions each)",
 }
+
+
+# Sequential-application workload on the same inputs as a Newton forward.
+SEQUENTIAL_OF = {"c2_gru_fused": "x_gru_seq", "c3_lstm": "x_lstm_seq",
+                 "x_lstm_step": "x_lstm_seq", "x_gru_long_step": "x_gru_long_seq"}
 
 
 def measured_traffic(name):
@@ -223,6 +240,16 @@ class Workload:
                 finally:
                     del os.environ[var]
             self._step = step
+        elif name in ("x_gru_seq", "x_gru_long_seq"):
+            self.out = torch.empty(B, L, H, device=dev)
+            args = [t[k] for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
+            self._step = lambda: api.gru_sequential(*args, None, out=self.out)
+        elif name == "x_lstm_seq":
+            self.out = torch.empty(B, L, H, device=dev)
+            self.out_c = torch.empty(B, L, H, device=dev)
+            args = [t[k] for k in ("pi", "pf", "po", "pg", "ui", "uf", "uo", "ug")]
+            self._step = lambda: api.lstm_sequential(*args, None, None, out_h=self.out,
+                                                     out_c=self.out_c)
         elif name == "c4_gru_long_fwd_adj":
             self.out = torch.empty(B, L, H, device=dev)
             cap = self.w["cap"]
@@ -377,6 +404,13 @@ def main():
         log(json.dumps({name: results[name]}))
         del wl
         torch.cuda.empty_cache()
+
+    # Newton forwards against sequential application of the same cell on the
+    # same inputs (the comparison the pages quote their speedups for)
+    for newton, seq in SEQUENTIAL_OF.items():
+        if newton in results and seq in results:
+            results[newton]["speedup_vs_sequential"] = (results[seq]["event_ms_per_step"] /
+                                                        results[newton]["event_ms_per_step"])
 
     head = results[args.workload]
     from nonlinear_rnn_solve_pararnn_amd import synth

@@ -181,6 +181,31 @@ int pararnn_adjoint_backward(int32_t cell, int64_t B, int64_t L, int64_t H,
                              float *grad_h0, float *grad_c0,
                              void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Sequential application of the GRU-style cell: one thread per channel
+ * walks t = 0..L-1 in order, one cell evaluation per position, no Newton
+ * iteration.  This is the evaluation the pages quote their speedups against
+ * (ParaRNN page, abstract and Fig. 2 caption: speedup over sequential
+ * application; DEER summary page, results: sequential GRU at L = 2^20), and
+ * the exact answer Newton converges to.  It exposes only B*H-fold
+ * parallelism.  Arguments, layouts and the cell as for pararnn_gru_forward
+ * (no tolerance, cap, info, trace or workspace).
+ */
+int pararnn_gru_sequential(int64_t B, int64_t L, int64_t H,
+                           const float *pz, const float *pr, const float *pc,
+                           const float *uz, const float *ur, const float *uc,
+                           const float *h0, float *h, void *stream);
+
+/*
+ * Sequential application of the LSTM-style cell (as above; arguments as for
+ * pararnn_lstm_forward without tolerance, cap, info, trace or workspace).
+ */
+int pararnn_lstm_sequential(int64_t B, int64_t L, int64_t H,
+                            const float *pi, const float *pf, const float *po,
+                            const float *pg, const float *ui, const float *uf,
+                            const float *uo, const float *ug, const float *h0,
+                            const float *c0, float *h, float *c, void *stream);
+
 /* Short text for a status code (static storage). */
 const char *pararnn_status_string(int status);
 

@@ -24,7 +24,7 @@ CELL_GRU, CELL_LSTM = 0, 1
 
 EXPORTS = ("pararnn_workspace_bytes", "rnn_linscan_diag", "rnn_linscan_blk2",
            "pararnn_gru_forward", "pararnn_lstm_forward", "pararnn_adjoint_backward",
-           "pararnn_status_string")
+           "pararnn_gru_sequential", "pararnn_lstm_sequential", "pararnn_status_string")
 
 _lib = None
 
@@ -60,6 +60,10 @@ def load_library():
     lib.pararnn_adjoint_backward.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                              vp, vp, vp, vp, vp, sz, vp]
     lib.pararnn_adjoint_backward.restype = ctypes.c_int
+    lib.pararnn_gru_sequential.argtypes = [i64, i64, i64] + [vp] * 8 + [vp]
+    lib.pararnn_gru_sequential.restype = ctypes.c_int
+    lib.pararnn_lstm_sequential.argtypes = [i64, i64, i64] + [vp] * 12 + [vp]
+    lib.pararnn_lstm_sequential.restype = ctypes.c_int
     lib.pararnn_status_string.argtypes = [ctypes.c_int]
     lib.pararnn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -227,6 +231,50 @@ def lstm_forward(pi, pf, po, pg, ui, uf, uo, ug, h0=None, c0=None, *, tol=1e-4, 
                                     _ptr(uf), _ptr(uo), _ptr(ug), _ptr(h0), _ptr(c0), _ptr(h),
                                     _ptr(c), float(tol), int(max_iter), _ptr(info), _ptr(trace),
                                     _ptr(ws), n, _stream(dev)), "pararnn_lstm_forward")
+    return h, c
+
+
+# ---------------------------------------------------------------- sequential
+def gru_sequential(pz, pr, pc, uz, ur, uc, h0=None, *, out=None):
+    """Sequential application of the GRU cell (one thread per channel, one
+    cell per position); returns h [B, L, H]."""
+    lib = load_library()
+    B, L, H = pz.shape
+    dev = pz.device
+    for t, n in ((pz, "pz"), (pr, "pr"), (pc, "pc")):
+        _need(t, (B, L, H), n, dev)
+    for t, n in ((uz, "uz"), (ur, "ur"), (uc, "uc")):
+        _need(t, (H,), n, dev)
+    if h0 is not None:
+        _need(h0, (B, H), "h0", dev)
+    h = torch.empty_like(pz) if out is None else out
+    _need(h, (B, L, H), "out", dev)
+    _check(lib.pararnn_gru_sequential(B, L, H, _ptr(pz), _ptr(pr), _ptr(pc), _ptr(uz), _ptr(ur),
+                                      _ptr(uc), _ptr(h0), _ptr(h), _stream(dev)),
+           "pararnn_gru_sequential")
+    return h
+
+
+def lstm_sequential(pi, pf, po, pg, ui, uf, uo, ug, h0=None, c0=None, *, out_h=None, out_c=None):
+    """Sequential application of the LSTM cell; returns (h, c), each [B, L, H]."""
+    lib = load_library()
+    B, L, H = pi.shape
+    dev = pi.device
+    for t, n in ((pi, "pi"), (pf, "pf"), (po, "po"), (pg, "pg")):
+        _need(t, (B, L, H), n, dev)
+    for t, n in ((ui, "ui"), (uf, "uf"), (uo, "uo"), (ug, "ug")):
+        _need(t, (H,), n, dev)
+    if h0 is not None:
+        _need(h0, (B, H), "h0", dev)
+    if c0 is not None:
+        _need(c0, (B, H), "c0", dev)
+    h = torch.empty_like(pi) if out_h is None else out_h
+    c = torch.empty_like(pi) if out_c is None else out_c
+    _need(h, (B, L, H), "out_h", dev)
+    _need(c, (B, L, H), "out_c", dev)
+    _check(lib.pararnn_lstm_sequential(B, L, H, _ptr(pi), _ptr(pf), _ptr(po), _ptr(pg), _ptr(ui),
+                                       _ptr(uf), _ptr(uo), _ptr(ug), _ptr(h0), _ptr(c0), _ptr(h),
+                                       _ptr(c), _stream(dev)), "pararnn_lstm_sequential")
     return h, c
 
 

@@ -198,6 +198,26 @@ int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H, const float *pi, const
     return status_of(lstm_forward_step(a, static_cast<char *>(ws), s));
 }
 
+int pararnn_gru_sequential(int64_t B, int64_t L, int64_t H, const float *pz, const float *pr,
+                           const float *pc, const float *uz, const float *ur, const float *uc,
+                           const float *h0, float *h, void *stream) {
+    if (!dims_ok(B, L, H) || !pz || !pr || !pc || !uz || !ur || !uc || !h) return PARARNN_ERR_INVALID;
+    if (!grid_ok((B * H + 63) / 64)) return PARARNN_ERR_INVALID;
+    GruFwdArgs a{B, L, H, pz, pr, pc, uz, ur, uc, h0, h, 0.0f, 1, nullptr, nullptr, -1};
+    return status_of(gru_rollout(a, static_cast<hipStream_t>(stream)));
+}
+
+int pararnn_lstm_sequential(int64_t B, int64_t L, int64_t H, const float *pi, const float *pf,
+                            const float *po, const float *pg, const float *ui, const float *uf,
+                            const float *uo, const float *ug, const float *h0, const float *c0,
+                            float *h, float *c, void *stream) {
+    if (!dims_ok(B, L, H) || !pi || !pf || !po || !pg || !ui || !uf || !uo || !ug || !h || !c)
+        return PARARNN_ERR_INVALID;
+    if (!grid_ok((B * H + 63) / 64)) return PARARNN_ERR_INVALID;
+    LstmFwdArgs a{B, L, H, pi, pf, po, pg, ui, uf, uo, ug, h0, c0, h, c, 0.0f, 1, nullptr, nullptr, -1};
+    return status_of(lstm_rollout(a, static_cast<hipStream_t>(stream)));
+}
+
 int pararnn_adjoint_backward(int32_t cell, int64_t B, int64_t L, int64_t H, const float *const *p,
                              const float *const *u, const float *h0, const float *c0,
                              const float *h, const float *c, const float *grad_h,

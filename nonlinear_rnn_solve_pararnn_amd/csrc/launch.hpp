@@ -63,6 +63,11 @@ struct LstmFwdArgs {
 hipError_t lstm_forward_step(const LstmFwdArgs &a, char *ws, hipStream_t s);
 hipError_t lstm_forward_chain(const LstmFwdArgs &a, char *ws, hipStream_t s);
 
+// Sequential application (one thread per channel; tol, cap, info, trace and
+// local unused).
+hipError_t gru_rollout(const GruFwdArgs &a, hipStream_t s);
+hipError_t lstm_rollout(const LstmFwdArgs &a, hipStream_t s);
+
 struct AdjArgs {
     int64_t B, L, H;
     const float *p[4], *u[4];

@@ -59,6 +59,8 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.rnn_linscan_diag(0, 10, 10, n, n, n, n, n, 0, n) == -1
     assert lib.pararnn_gru_forward(1, 10, 10, *([n] * 8), ctypes.c_float(1e-4), 5, n, n, n, 0, n) == -1
     assert lib.pararnn_adjoint_backward(7, 1, 10, 10, *([n] * 13), 0, n) == -1
+    assert lib.pararnn_gru_sequential(1, 0, 10, *([n] * 8), n) == -1
+    assert lib.pararnn_lstm_sequential(1, 10, 10, *([n] * 12), n) == -1
     assert lib.pararnn_status_string(-1) == b"invalid argument"
 
 
