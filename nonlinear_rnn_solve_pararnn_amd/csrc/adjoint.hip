@@ -52,16 +52,32 @@ __global__ __launch_bounds__(256) void reduce_u_kernel(UReduceArgs r) {
     if (threadIdx.x == 0) out[j] = red[0];
 }
 
-// Store per-workgroup dL/du partials of `ngates` gates.
+// Store per-workgroup dL/du partials of NG gates: every gate's per-thread sum
+// is reduced over the workgroup to one value per channel lane (channel lanes:
+// over the waves of each lane; time lanes: over every thread) in one pass,
+// with a single barrier.  `red` is written again only by the next tile, whose
+// workgroup has passed the ticket barrier (after wave 0's reads) by then.
 template <int NW, bool CL, int NG>
 __device__ __forceinline__ void store_u_partials(const TilePos &tp, const float (&su)[NG],
                                                  float *partial) {
-    __shared__ float red[NW * 64];
+    constexpr int W = CL ? NW * 64 : NW;  // slots per gate
+    __shared__ float red[NG * W];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
-        const float s = wg_channel_sum<NW, CL>(su[q], red);
-        if (w == 0) {
+        if (CL) {
+            red[q * W + w * 64 + lane] = su[q];
+        } else {
+            const float v = wave_sum(su[q]);
+            if (lane == 0) red[q * W + w] = v;
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            float s = 0.0f;
+            for (int k = 0; k < NW; ++k) s += red[q * W + (CL ? k * 64 + lane : k)];
             if (CL)
                 partial[(tp.tile * NG + q) * 64 + lane] = s;
             else if (lane == 0)

@@ -367,25 +367,4 @@ static hipError_t launch_chunk_scan(const Op &op, const ScanGeo &g, hipStream_t 
     return hipGetLastError();
 }
 
-// Reduce a per-thread value over the workgroup into one value per channel
-// lane (channel lanes: sum over the waves of each lane; time lanes: sum over
-// every thread).  Returns the total in wave 0 (lane = channel, or lane 0).
-template <int NW, bool CHANNEL_LANES>
-__device__ __forceinline__ float wg_channel_sum(float v, float *red /* shared, NW*64 */) {
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    if (!CHANNEL_LANES) v = wave_sum(v);
-    red[w * 64 + lane] = v;
-    __syncthreads();
-    float s = 0.0f;
-    if (w == 0) {
-        if (CHANNEL_LANES) {
-            for (int k = 0; k < NW; ++k) s += red[k * 64 + lane];
-        } else {
-            for (int k = 0; k < NW; ++k) s += red[k * 64];
-        }
-    }
-    __syncthreads();
-    return s;
-}
-
 }  // namespace prn
