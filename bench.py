@@ -69,12 +69,12 @@ DOMINANT = {
 # taken on: the sha256 prefix of those sources is checked at run time and the
 # figure is dropped (null) once any of them has changed.
 TRAFFIC = {
-    "c1_linscan": {"bytes": 551430553 + 289021952,
+    "c1_linscan": {"bytes": 551291699 + 289021952,
                    "sources": ["common.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-                   "sha256": "ba6bfeac1f98fb63"},
-    "c2_gru_fused": {"bytes": 419274137 + 152557465,
+                   "sha256": "ca1412e4e73cc72c"},
+    "c2_gru_fused": {"bytes": 419274547 + 152450969,
                      "sources": ["common.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
-                     "sha256": "358fa2674944adba"},
+                     "sha256": "3dbbce9e340c6e2d"},
 }
 DESCRIBE = {
     "c1_linscan": "linear diagonal recurrence h_t = a_t h_{t-1} + b_t, B=16 L=4096 H=1024, "
