@@ -143,6 +143,19 @@ def linscan_blk2_inputs(B, L, H, seed, scale=0.6, h0=False):
     return {"A": A, "b": b, "h0": hz}
 
 
+def linscan_blk_inputs(B, L, H, k, seed, h0=False):
+    """k x k block linear recurrence draws: A ~ U(-s,s) [B,L,H,k,k] with
+    s = 0.6*sqrt(2/k) (row-major), b ~ N(0,1) [B,L,H,k]; optionally h0 ~ N(0,1)
+    [B,H,k].  With that s a random block shrinks a vector by about half per
+    step on average, as the 2x2 draws do, so long products stay bounded."""
+    rng = _rng(seed)
+    s = 0.6 * np.sqrt(2.0 / k)
+    A = _uniform(rng, (B, L, H, k, k), -s, s)
+    b = _normal(rng, (B, L, H, k))
+    hz = _normal(rng, (B, H, k)) if h0 else np.zeros((B, H, k), np.float32)
+    return {"A": A, "b": b, "h0": hz}
+
+
 def workload_inputs(name: str) -> dict:
     """Inputs of one named workload, seed 1000 + its index in WORKLOAD_ORDER
     (a workload with `same_as` takes that workload's inputs)."""

@@ -50,6 +50,7 @@ def _load():
     vp = ctypes.c_void_p
     lib.orc_linscan_diag.argtypes = [_I64, _I64, _I64, vp, vp, vp, vp]
     lib.orc_linscan_blk2.argtypes = [_I64, _I64, _I64, vp, vp, vp, vp]
+    lib.orc_linscan_blk.argtypes = [_I64, _I64, _I64, _I64, vp, vp, vp, vp]
     lib.orc_gru_cell.argtypes = [ctypes.c_double] * 7 + [vp, vp, vp, vp]
     lib.orc_lstm_cell.argtypes = [ctypes.c_double] * 10 + [vp, vp, vp, vp, vp]
     lib.orc_gru_rollout.argtypes = [_I64, _I64, _I64] + [vp] * 8
@@ -128,6 +129,18 @@ def linscan_blk2(A, b, h0=None):
     assert A.shape == (B, L, H, 2, 2) and b.shape == (B, L, H, 2)
     h = np.empty_like(b)
     _load().orc_linscan_blk2(B, L, H, _p(A), _p(b), _p(h0), _p(h))
+    return h
+
+
+def linscan_blk(A, b, h0=None):
+    """k x k block recurrence h_t = A_t h_{t-1} + b_t; A [B,L,H,k,k], b [B,L,H,k]."""
+    A, b, h0 = _f64(A), _f64(b), _f64(h0)
+    B, L, H, k = b.shape
+    assert A.shape == (B, L, H, k, k) and 1 <= k <= 64
+    if h0 is not None:
+        assert h0.shape == (B, H, k)
+    h = np.empty_like(b)
+    _load().orc_linscan_blk(k, B, L, H, _p(A), _p(b), _p(h0), _p(h))
     return h
 
 

@@ -23,7 +23,8 @@
  *    backpropagation through time (DEER summary: forward plus gradients).
  *  - The linear recurrence h_t = a_t*h_{t-1} + b_t by a serial loop
  *    (minimal-RNN article: gates without h-dependence give a recurrence that
- *    a parallel scan solves; DEER summary: associative scan).
+ *    a parallel scan solves; DEER summary: associative scan), and its 2x2 and
+ *    k x k block forms (at most 8x8 here).
  *
  * All arithmetic is fp64 and in the natural sequential order.  Channels
  * (b, j) are independent and are spread over threads with OpenMP; that does
@@ -163,6 +164,39 @@ void orc_linscan_blk2(int64_t B, int64_t L, int64_t H, const double *A,
                 x1 = y1;
                 h[2 * k + 0] = x0;
                 h[2 * k + 1] = x1;
+            }
+        }
+}
+
+/* -------------------------------------------------------------------------
+ * k x k block linear recurrence, serial loop (ParaRNN Fig. 2 caption: block
+ * bi-diagonal systems whose blocks are the per-channel Jacobians, 2x2 for
+ * ParaLSTM; DEER summary, limitations paragraph: dense Jacobians as the
+ * hidden size grows).  Per (batch, channel) block:
+ *     h_t = A_t h_{t-1} + b_t,   h_{-1} = h0 (NULL means 0)
+ * A [B, L, H, k, k] row-major (A[i][l] multiplies component l into i),
+ * b, h [B, L, H, k], h0 [B, H, k].
+ * ------------------------------------------------------------------------- */
+void orc_linscan_blk(int64_t k, int64_t B, int64_t L, int64_t H, const double *A,
+                     const double *b, const double *h0, double *h)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t bb = 0; bb < B; ++bb)
+        for (int64_t j = 0; j < H; ++j) {
+            double x[64], y[64];
+            for (int64_t i = 0; i < k; ++i) x[i] = h0 ? h0[(bb * H + j) * k + i] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                size_t e = IDX(bb, t, j);
+                const double *M = A + (size_t)k * k * e;
+                for (int64_t i = 0; i < k; ++i) {
+                    double acc = 0.0;
+                    for (int64_t l = 0; l < k; ++l) acc += M[i * k + l] * x[l];
+                    y[i] = acc + b[(size_t)k * e + i];
+                }
+                for (int64_t i = 0; i < k; ++i) {
+                    x[i] = y[i];
+                    h[(size_t)k * e + i] = x[i];
+                }
             }
         }
 }

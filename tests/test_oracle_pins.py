@@ -192,6 +192,57 @@ def test_linscan_blk2_diagonal_blocks_are_two_diag_scans(orc):
     np.testing.assert_allclose(h[..., 1], orc.linscan_diag(a1, b[..., 1]), rtol=1e-13, atol=1e-13)
 
 
+@pytest.mark.parametrize("k", [3, 4, 8])
+def test_linscan_blk_dense_solve_and_powers(orc, k):
+    """k x k blocks: the recurrence is the block bi-diagonal system
+    [I; -A_1 I; ...] h = b (+ A_0 h0 in the first row), solved densely; with a
+    constant non-symmetric A it is sum_s A^(t-s) b_s (a transposed A fails)."""
+    L = 20
+    d = synth.linscan_blk_inputs(1, L, 2, k, 9, h0=True)
+    h = orc.linscan_blk(d["A"], d["b"], d["h0"])
+    for j in range(2):
+        M = np.eye(k * L)
+        rhs = d["b"][0, :, j].astype(np.float64).reshape(-1).copy()
+        for t in range(L):
+            At = d["A"][0, t, j].astype(np.float64)
+            if t == 0:
+                rhs[0:k] += At @ d["h0"][0, j].astype(np.float64)
+            else:
+                M[k * t:k * t + k, k * t - k:k * t] = -At
+        ref = np.linalg.solve(M, rhs).reshape(L, k)
+        np.testing.assert_allclose(h[0, :, j], ref, rtol=1e-11, atol=1e-12)
+    A = RNG.uniform(-0.4, 0.4, size=(k, k))
+    assert not np.allclose(A, A.T)
+    bb = RNG.normal(size=(1, 10, 1, k))
+    hh = orc.linscan_blk(np.broadcast_to(A, (1, 10, 1, k, k)), bb)
+    for t in range(10):
+        ref = sum(np.linalg.matrix_power(A, t - s) @ bb[0, s, 0] for s in range(t + 1))
+        np.testing.assert_allclose(hh[0, t, 0], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_linscan_blk_reduces_to_diag_and_2x2(orc):
+    """Diagonal blocks give k independent diagonal scans; k = 2 equals the 2x2
+    scan and k = 1 the diagonal scan (separately written oracle loops)."""
+    B, L, H, k = 2, 40, 3, 4
+    a = RNG.uniform(-1.0, 1.0, size=(B, L, H, k))
+    A = np.zeros((B, L, H, k, k))
+    for i in range(k):
+        A[..., i, i] = a[..., i]
+    b = RNG.normal(size=(B, L, H, k))
+    h0 = RNG.normal(size=(B, H, k))
+    h = orc.linscan_blk(A, b, h0)
+    for i in range(k):
+        np.testing.assert_allclose(h[..., i], orc.linscan_diag(a[..., i], b[..., i], h0[..., i]),
+                                   rtol=1e-13, atol=1e-13)
+    d = synth.linscan_blk2_inputs(2, 30, 3, 10, h0=True)
+    np.testing.assert_allclose(orc.linscan_blk(d["A"], d["b"], d["h0"]),
+                               orc.linscan_blk2(d["A"], d["b"], d["h0"]), rtol=1e-13, atol=1e-13)
+    a1 = RNG.uniform(-1, 1, size=(B, L, H))
+    b1 = RNG.normal(size=(B, L, H))
+    np.testing.assert_allclose(orc.linscan_blk(a1[..., None, None], b1[..., None])[..., 0],
+                               orc.linscan_diag(a1, b1), rtol=1e-13, atol=1e-13)
+
+
 # ---------------------------------------------------------------- Newton
 def _gru_args(d):
     return [d[k] for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
