@@ -47,6 +47,7 @@ ALG_BYTES = {
     "x_gru_seq": 16,             # 3 p in; h out
     "x_lstm_seq": 24,            # 4 p in; h, c out
     "x_gru_long_seq": 16,        # 3 p in; h out
+    "x_linscan_blk4": 96,        # A (4x4) and b (4) in; h (4) out, per (batch, position, channel)
 }
 DOMINANT = {
     "c1_linscan": "diag_pf_kernel<16,16,2> (chunked scan, next tile prefetched)",
@@ -62,6 +63,7 @@ DOMINANT = {
     "x_gru_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
     "x_lstm_seq": "lstm_rollout_kernel (sequential application, one thread per channel)",
     "x_gru_long_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
+    "x_linscan_blk4": "chunk_scan_kernel<LinBlkOp<4>>",
 }
 # HBM bytes per launch of the dominant kernel from rocprofv3 counter runs
 # (FETCH_SIZE x 2.000 and WRITE_SIZE x 1.000, the factors a plain 1 GiB device
@@ -99,6 +101,8 @@ DESCRIBE = {
                   "(B*H = 16384 threads, 2048 positions each)",
     "x_gru_long_seq": "sequential application of the GRU cell on the inputs of c4_gru_long_fwd_adj "
                       "(B*H = 16 threads, 2^20 positions each)",
+    "x_linscan_blk4": "4x4 block linear recurrence h_t = A_t h_{t-1} + b_t, B=16 L=2048 H=256, "
+                      "A~U(-0.42,0.42), b~N(0,1), h0=0",
 }
 
 
@@ -188,6 +192,10 @@ class Workload:
             self.out = torch.empty(B, L, H, 2, device=dev)
             self.ws = api.new_workspace(api.workspace_bytes(api.OP_LINSCAN_BLK2, B, L, H), dev)
             self._step = lambda: api.linscan_blk2(t["A"], t["b"], None, out=self.out, ws=self.ws)
+        elif name == "x_linscan_blk4":
+            self.out = torch.empty(B, L, H, 4, device=dev)
+            self.ws = api.new_workspace(api.workspace_bytes(api.OP_LINSCAN_BLK4, B, L, H), dev)
+            self._step = lambda: api.linscan_blk(t["A"], t["b"], None, out=self.out, ws=self.ws)
         elif name == "x_lstm_adjoint":
             p = [t[k] for k in ("pi", "pf", "po", "pg")]
             u = [t[k] for k in ("ui", "uf", "uo", "ug")]

@@ -70,7 +70,8 @@ enum {
     PARARNN_OP_GRU_FORWARD = 2,
     PARARNN_OP_LSTM_FORWARD = 3,
     PARARNN_OP_GRU_ADJOINT = 4,
-    PARARNN_OP_LSTM_ADJOINT = 5
+    PARARNN_OP_LSTM_ADJOINT = 5,
+    PARARNN_OP_LINSCAN_BLK4 = 6   /* rnn_linscan_blk with k = 4 */
 };
 
 /*
@@ -103,6 +104,24 @@ int rnn_linscan_diag(int64_t B, int64_t L, int64_t H,
 int rnn_linscan_blk2(int64_t B, int64_t L, int64_t H,
                      const float *A, const float *b, const float *h0,
                      float *h, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * k x k block linear recurrence: the 2x2 solver widened to small dense
+ * blocks, such as the per-head Jacobians of a cell with dense recurrence
+ * inside heads of k channels (ParaRNN page, Fig. 2 caption: block
+ * bi-diagonal systems; DEER summary page, limitations paragraph: dense
+ * Jacobians as the hidden size grows):
+ *     h[b,t,j,:] = A[b,t,j] @ h[b,t-1,j,:] + b[b,t,j,:]
+ * A: [B, L, H, k, k] row-major blocks (A[i][l] takes component l into i).
+ * b, h: [B, L, H, k].  h0: [B, H, k] or NULL.
+ * k = 2 is rnn_linscan_blk2 (its workspace query, PARARNN_OP_LINSCAN_BLK2);
+ * k = 4 needs A, b, h and h0 16-byte aligned and PARARNN_OP_LINSCAN_BLK4
+ * workspace.  Other k return PARARNN_ERR_UNSUPPORTED (k < 1:
+ * PARARNN_ERR_INVALID).
+ */
+int rnn_linscan_blk(int32_t k, int64_t B, int64_t L, int64_t H,
+                    const float *A, const float *b, const float *h0,
+                    float *h, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * GRU-style cell with diagonal recurrence (ParaGRU, ParaRNN page Fig. 2):

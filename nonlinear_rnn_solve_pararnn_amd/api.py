@@ -19,10 +19,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpararnn.so")
 
 OP_LINSCAN_DIAG, OP_LINSCAN_BLK2, OP_GRU_FORWARD, OP_LSTM_FORWARD, OP_GRU_ADJOINT, \
-    OP_LSTM_ADJOINT = range(6)
+    OP_LSTM_ADJOINT, OP_LINSCAN_BLK4 = range(7)
 CELL_GRU, CELL_LSTM = 0, 1
 
-EXPORTS = ("pararnn_workspace_bytes", "rnn_linscan_diag", "rnn_linscan_blk2",
+EXPORTS = ("pararnn_workspace_bytes", "rnn_linscan_diag", "rnn_linscan_blk2", "rnn_linscan_blk",
            "pararnn_gru_forward", "pararnn_lstm_forward", "pararnn_adjoint_backward",
            "pararnn_gru_sequential", "pararnn_lstm_sequential", "pararnn_status_string")
 
@@ -51,6 +51,8 @@ def load_library():
     lib.rnn_linscan_diag.restype = ctypes.c_int
     lib.rnn_linscan_blk2.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.rnn_linscan_blk2.restype = ctypes.c_int
+    lib.rnn_linscan_blk.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]
+    lib.rnn_linscan_blk.restype = ctypes.c_int
     lib.pararnn_gru_forward.argtypes = [i64, i64, i64] + [vp] * 8 + [
         ctypes.c_float, i32, vp, vp, vp, sz, vp]
     lib.pararnn_gru_forward.restype = ctypes.c_int
@@ -172,6 +174,27 @@ def linscan_blk2(A, b, h0=None, *, out=None, ws=None):
 
 
 # ---------------------------------------------------------------- Newton forward
+def linscan_blk(A, b, h0=None, *, out=None, ws=None):
+    """k x k block scan h_t = A_t h_{t-1} + b_t (k = 2 or 4); A [B, L, H, k, k],
+    b [B, L, H, k]; returns h [B, L, H, k]."""
+    lib = load_library()
+    B, L, H, k = b.shape
+    dev = b.device
+    _need(A, (B, L, H, k, k), "A", dev)
+    _need(b, (B, L, H, k), "b", dev)
+    if h0 is not None:
+        _need(h0, (B, H, k), "h0", dev)
+    h = torch.empty_like(b) if out is None else out
+    _need(h, (B, L, H, k), "out", dev)
+    op = {2: OP_LINSCAN_BLK2, 4: OP_LINSCAN_BLK4}.get(k)
+    if op is None:
+        raise PararnnError("rnn_linscan_blk supports k = 2 and 4, got %d" % k)
+    ws, n = _workspace(op, B, L, H, dev, ws=ws)
+    _check(lib.rnn_linscan_blk(k, B, L, H, _ptr(A), _ptr(b), _ptr(h0), _ptr(h), _ptr(ws), n,
+                               _stream(dev)), "rnn_linscan_blk")
+    return h
+
+
 def gru_forward(pz, pr, pc, uz, ur, uc, h0=None, *, tol=1e-4, max_iter=32, out=None,
                 info=None, trace=None, ws=None):
     """Newton solve of the diagonal GRU over [B, L, H] gate pre-projections.

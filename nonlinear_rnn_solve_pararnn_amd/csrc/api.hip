@@ -123,6 +123,7 @@ size_t pararnn_workspace_bytes(int32_t op, int64_t B, int64_t L, int64_t H, int3
         case PARARNN_OP_LSTM_FORWARD:
             if (max_iter < 1) return 0;
             return lstm_fwd_ws(B, L, H, eff_cap(max_iter, L));
+        case PARARNN_OP_LINSCAN_BLK4: return scan_ws(kCfgLinBlk4, 4, B, L, H).total;
         case PARARNN_OP_GRU_ADJOINT: return gru_adjoint_ws(B, L, H);
         case PARARNN_OP_LSTM_ADJOINT: return lstm_adjoint_ws(B, L, H);
         default: return 0;
@@ -147,6 +148,20 @@ int rnn_linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const floa
     if (ws_bytes < scan_ws(kCfgLinBlk2, 2, B, L, H).total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
     return status_of(linscan_blk2(B, L, H, A, b, h0, h, static_cast<char *>(ws),
                                   static_cast<hipStream_t>(stream)));
+}
+
+int rnn_linscan_blk(int32_t k, int64_t B, int64_t L, int64_t H, const float *A, const float *b,
+                    const float *h0, float *h, void *ws, size_t ws_bytes, void *stream) {
+    if (k == 2) return rnn_linscan_blk2(B, L, H, A, b, h0, h, ws, ws_bytes, stream);
+    if (k < 1) return PARARNN_ERR_INVALID;
+    if (k != 4) return PARARNN_ERR_UNSUPPORTED;
+    if (!dims_ok(B, L, H) || !A || !b || !h || !ws) return PARARNN_ERR_INVALID;
+    if (!aligned(A, 16) || !aligned(b, 16) || !aligned(h, 16) || (h0 && !aligned(h0, 16)))
+        return PARARNN_ERR_INVALID;
+    if (!grid_ok(scan_shape(kCfgLinBlk4, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+    if (ws_bytes < scan_ws(kCfgLinBlk4, 4, B, L, H).total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+    return status_of(linscan_blk(4, B, L, H, A, b, h0, h, static_cast<char *>(ws),
+                                 static_cast<hipStream_t>(stream)));
 }
 
 int pararnn_gru_forward(int64_t B, int64_t L, int64_t H, const float *pz, const float *pr,

@@ -48,7 +48,78 @@ struct Aff2 {
     float a00, a01, a10, a11, b0, b1;
 };
 
-template <int S> struct MonoidT;
+// k x k blocks (k >= 3): A row-major, a[i * k + l] takes component l into i.
+template <int K>
+struct AffK {
+    float a[K * K];
+    float b[K];
+};
+template <int K>
+struct VecK {
+    float v[K];
+};
+
+// The primary template serves k x k blocks; k = 1 and k = 2 are specialised
+// below with named fields.
+template <int S>
+struct MonoidT {
+    static_assert(S >= 3 && S <= 8, "k x k blocks for 3 <= k <= 8");
+    using Map = AffK<S>;
+    using State = VecK<S>;
+    __device__ __forceinline__ static Map id() {
+        Map m;
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+#pragma unroll
+            for (int l = 0; l < S; ++l) m.a[i * S + l] = i == l ? 1.0f : 0.0f;
+            m.b[i] = 0.0f;
+        }
+        return m;
+    }
+    __device__ __forceinline__ static Map then(const Map &e, const Map &l) {
+        Map r;
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+#pragma unroll
+            for (int c = 0; c < S; ++c) {
+                float acc = l.a[i * S] * e.a[c];
+#pragma unroll
+                for (int m = 1; m < S; ++m) acc = fmaf(l.a[i * S + m], e.a[m * S + c], acc);
+                r.a[i * S + c] = acc;
+            }
+            float acc = l.b[i];
+#pragma unroll
+            for (int m = 0; m < S; ++m) acc = fmaf(l.a[i * S + m], e.b[m], acc);
+            r.b[i] = acc;
+        }
+        return r;
+    }
+    __device__ __forceinline__ static State apply(const Map &m, const State &x) {
+        State y;
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+            float acc = m.b[i];
+#pragma unroll
+            for (int l = 0; l < S; ++l) acc = fmaf(m.a[i * S + l], x.v[l], acc);
+            y.v[i] = acc;
+        }
+        return y;
+    }
+    __device__ __forceinline__ static State zero() {
+        State x;
+#pragma unroll
+        for (int i = 0; i < S; ++i) x.v[i] = 0.0f;
+        return x;
+    }
+    __device__ __forceinline__ static Map shfl_up(const Map &m, int d) {
+        Map r;
+#pragma unroll
+        for (int i = 0; i < S * S; ++i) r.a[i] = __shfl_up(m.a[i], d, 64);
+#pragma unroll
+        for (int i = 0; i < S; ++i) r.b[i] = __shfl_up(m.b[i], d, 64);
+        return r;
+    }
+};
 
 template <> struct MonoidT<1> {
     using Map = Aff1;
@@ -130,13 +201,60 @@ __device__ __forceinline__ void st_coherent(uint64_t *p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int S> __device__ __forceinline__ typename MonoidT<S>::State nan_state();
+template <int S> __device__ __forceinline__ typename MonoidT<S>::State nan_state() {
+    typename MonoidT<S>::State x;
+#pragma unroll
+    for (int i = 0; i < S; ++i) x.v[i] = __uint_as_float(0x7fc00000u);
+    return x;
+}
 template <> __device__ __forceinline__ float nan_state<1>() { return __uint_as_float(0x7fc00000u); }
 template <> __device__ __forceinline__ float2s nan_state<2>() {
     return {__uint_as_float(0x7fc00000u), __uint_as_float(0x7fc00000u)};
 }
 
-template <int S> struct Desc;
+// k x k blocks: the k*k entries of A then the k offsets; the state's k components.
+template <int S>
+struct Desc {
+    static constexpr int kAggWords = desc_agg_words(S);
+    static constexpr int kIncWords = desc_inc_words(S);
+    static_assert(kAggWords == S * S + S && kIncWords == S, "one word per float");
+    __device__ static void put_agg(uint64_t *w, const AffK<S> &m, uint32_t tag) {
+#pragma unroll
+        for (int i = 0; i < S * S; ++i) st_coherent(w + i, tagged(m.a[i], tag));
+#pragma unroll
+        for (int i = 0; i < S; ++i) st_coherent(w + S * S + i, tagged(m.b[i], tag));
+    }
+    __device__ static void put_inc(uint64_t *w, const VecK<S> &x, uint32_t tag) {
+#pragma unroll
+        for (int i = 0; i < S; ++i) st_coherent(w + i, tagged(x.v[i], tag));
+    }
+    __device__ static bool get_inc(const uint64_t *w, VecK<S> &x, uint32_t tag) {
+        uint64_t v[S];
+#pragma unroll
+        for (int i = 0; i < S; ++i) v[i] = ld_coherent(w + i);
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < S; ++i) ok = ok && has_tag(v[i], tag);
+        if (!ok) return false;
+#pragma unroll
+        for (int i = 0; i < S; ++i) x.v[i] = lo_f(v[i]);
+        return true;
+    }
+    __device__ static bool get_agg(const uint64_t *w, AffK<S> &m, uint32_t tag) {
+        uint64_t v[S * S + S];
+#pragma unroll
+        for (int i = 0; i < S * S + S; ++i) v[i] = ld_coherent(w + i);
+        bool ok = true;
+#pragma unroll
+        for (int i = 0; i < S * S + S; ++i) ok = ok && has_tag(v[i], tag);
+        if (!ok) return false;
+#pragma unroll
+        for (int i = 0; i < S * S; ++i) m.a[i] = lo_f(v[i]);
+#pragma unroll
+        for (int i = 0; i < S; ++i) m.b[i] = lo_f(v[S * S + i]);
+        return true;
+    }
+};
 
 template <> struct Desc<1> {
     static constexpr int kAggWords = desc_agg_words(1);

@@ -35,6 +35,9 @@ hipError_t linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const f
                         const float *h0, float *h, char *ws, hipStream_t s);
 hipError_t linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const float *b,
                         const float *h0, float *h, char *ws, hipStream_t s);
+// k x k blocks, k = 4 (hipErrorInvalidValue otherwise)
+hipError_t linscan_blk(int k, int64_t B, int64_t L, int64_t H, const float *A, const float *b,
+                       const float *h0, float *h, char *ws, hipStream_t s);
 
 struct GruFwdArgs {
     int64_t B, L, H;

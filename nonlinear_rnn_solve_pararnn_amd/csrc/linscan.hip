@@ -313,6 +313,102 @@ struct LinBlk2Op {
     }
 };
 
+// ---------------------------------------------------------------- k x k scan
+// h_t = A_t h_{t-1} + b_t with A_t a dense k x k block per (batch, channel):
+// the 2x2 case widened to the small dense blocks that dense Jacobians per
+// head give (ParaRNN page, Fig. 2 caption: block bi-diagonal systems; DEER
+// summary page, limitations: dense Jacobians).  Every block row and state
+// moves as whole 16-byte pieces.  Instantiated for k = 4: one thread holds
+// k*k + k floats per position, so at k = 8 this layout spills.
+template <int K>
+struct LinBlkOp {
+    static_assert(K % 4 == 0, "blocks move as float4s");
+    static constexpr int S = K;
+    using M = MonoidT<K>;
+    const float *A, *b, *h0;
+    float *h;
+    int64_t L, H;
+
+    struct Elem {
+        AffK<K> m;
+    };
+    __device__ bool active() const { return true; }
+    __device__ static void load_vec(const float *p, float *v) {
+#pragma unroll
+        for (int q = 0; q < K / 4; ++q) {
+            const float4 x = reinterpret_cast<const float4 *>(p)[q];
+            v[4 * q] = x.x;
+            v[4 * q + 1] = x.y;
+            v[4 * q + 2] = x.z;
+            v[4 * q + 3] = x.w;
+        }
+    }
+    __device__ VecK<K> init_state(const TilePos &tp) const {
+        VecK<K> x = M::zero();
+        if (h0 != nullptr && tp.ok) load_vec(h0 + (tp.b * H + tp.j) * K, x.v);
+        return x;
+    }
+    // map of element e = (b, t, j): its block and offsets.  A lane's block is
+    // 64 consecutive bytes, half a line, read as four 16-byte pieces: ordinary
+    // loads there (the streamed hint took 322 us against 264 us at B=16,
+    // L=2048, H=256); the offsets are streamed.
+    __device__ void load_elem(int64_t e, AffK<K> &m) const {
+        const float4 *a4 = reinterpret_cast<const float4 *>(A) + e * (K * K / 4);
+#pragma unroll
+        for (int q = 0; q < K * K / 4; ++q) {
+            const float4 x = a4[q];
+            m.a[4 * q] = x.x;
+            m.a[4 * q + 1] = x.y;
+            m.a[4 * q + 2] = x.z;
+            m.a[4 * q + 3] = x.w;
+        }
+        const float4 *b4 = reinterpret_cast<const float4 *>(b) + e * (K / 4);
+#pragma unroll
+        for (int q = 0; q < K / 4; ++q) {
+            const float4 x = ld_once(b4 + q);
+            m.b[4 * q] = x.x;
+            m.b[4 * q + 1] = x.y;
+            m.b[4 * q + 2] = x.z;
+            m.b[4 * q + 3] = x.w;
+        }
+    }
+    template <int C>
+    __device__ AffK<K> phase1(const TilePos &tp, Elem (&e)[C]) const {
+        const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
+        if (tp.ok && tp.pos0 + C <= L) {  // every position inside: no test per position
+#pragma unroll
+            for (int i = 0; i < C; ++i) load_elem(base + i * H, e[i].m);
+        } else {
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                if (tp.ok && tp.pos0 + i < L)
+                    load_elem(base + i * H, e[i].m);
+                else
+                    e[i].m = M::id();
+            }
+        }
+        AffK<K> acc = M::id();
+#pragma unroll
+        for (int i = 0; i < C; ++i) acc = M::then(acc, e[i].m);
+        return acc;
+    }
+    __device__ void store_state(int64_t e, const VecK<K> &x) const {
+        float4 *h4 = reinterpret_cast<float4 *>(h) + e * (K / 4);
+#pragma unroll
+        for (int q = 0; q < K / 4; ++q)
+            h4[q] = make_float4(x.v[4 * q], x.v[4 * q + 1], x.v[4 * q + 2], x.v[4 * q + 3]);
+    }
+    template <int C, int NW, bool CL>
+    __device__ void phase2(const TilePos &tp, Elem (&e)[C], VecK<K> x) const {
+        const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            x = M::apply(e[i].m, x);
+            if (tp.ok && tp.pos0 + i < L) store_state(base + i * H, x);
+        }
+    }
+};
+
 int device_cu_count() {
     static std::atomic<int> cached[64];
     int dev = 0;
@@ -377,6 +473,16 @@ hipError_t linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const f
     LinBlk2Op op{A, b, h0, h, L, H};
     constexpr TileCfg c = kCfgLinBlk2;
     return run_scan<LinBlk2Op, 2, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
+}
+
+hipError_t linscan_blk(int k, int64_t B, int64_t L, int64_t H, const float *A, const float *b,
+                       const float *h0, float *h, char *ws, hipStream_t s) {
+    if (k == 4) {
+        LinBlkOp<4> op{A, b, h0, h, L, H};
+        constexpr TileCfg c = kCfgLinBlk4;
+        return run_scan<LinBlkOp<4>, 4, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace prn

@@ -19,6 +19,8 @@ constexpr TileCfg kCfgLinDiag{16, 16, 4, 16, 2};
 // The diagonal scan with channel lanes prefetches the next tile (linscan.hip).
 constexpr bool kDiagPrefetch = true;
 constexpr TileCfg kCfgLinBlk2{16, 8, 4, 8, 1};
+// 4x4 blocks (the maps hold 20 floats per position)
+constexpr TileCfg kCfgLinBlk4{8, 4, 4, 2, 1};
 constexpr TileCfg kCfgGruStep{4, 16, 8, 16};
 constexpr TileCfg kCfgLstmStep{8, 16, 4, 8};
 constexpr TileCfg kCfgGruAdj{4, 8, 16, 8};

@@ -91,10 +91,43 @@ __device__ __forceinline__ float2s shfl_down_s(float2s x, int d) {
     return {shfl_down_f(x.x, d), shfl_down_f(x.y, d)};
 }
 
+template <int K>
+__device__ __forceinline__ AffK<K> shfl_down_m(const AffK<K> &m, int d) {
+    AffK<K> r;
+#pragma unroll
+    for (int i = 0; i < K * K; ++i) r.a[i] = shfl_down_f(m.a[i], d);
+#pragma unroll
+    for (int i = 0; i < K; ++i) r.b[i] = shfl_down_f(m.b[i], d);
+    return r;
+}
+template <int K>
+__device__ __forceinline__ VecK<K> shfl_down_s(const VecK<K> &x, int d) {
+    VecK<K> r;
+#pragma unroll
+    for (int i = 0; i < K; ++i) r.v[i] = shfl_down_f(x.v[i], d);
+    return r;
+}
+
 __device__ __forceinline__ float bcast0_f(float v) { return __shfl(v, 0, 64); }
 __device__ __forceinline__ Aff1 bcast0_m(Aff1 m) { return {bcast0_f(m.a), bcast0_f(m.b)}; }
 __device__ __forceinline__ Aff2 bcast0_m(Aff2 m) {
     return {bcast0_f(m.a00), bcast0_f(m.a01), bcast0_f(m.a10), bcast0_f(m.a11), bcast0_f(m.b0), bcast0_f(m.b1)};
+}
+template <int K>
+__device__ __forceinline__ AffK<K> bcast0_m(const AffK<K> &m) {
+    AffK<K> r;
+#pragma unroll
+    for (int i = 0; i < K * K; ++i) r.a[i] = bcast0_f(m.a[i]);
+#pragma unroll
+    for (int i = 0; i < K; ++i) r.b[i] = bcast0_f(m.b[i]);
+    return r;
+}
+template <int K>
+__device__ __forceinline__ VecK<K> bcast0_s(const VecK<K> &x) {
+    VecK<K> r;
+#pragma unroll
+    for (int i = 0; i < K; ++i) r.v[i] = bcast0_f(x.v[i]);
+    return r;
 }
 __device__ __forceinline__ float bcast0_s(float x) { return bcast0_f(x); }
 __device__ __forceinline__ float2s bcast0_s(float2s x) { return {bcast0_f(x.x), bcast0_f(x.y)}; }

@@ -43,6 +43,8 @@ WORKLOADS = {
     "x_gru_seq": dict(kind="gru", B=16, L=512, H=4096, same_as="c2_gru_fused"),
     "x_lstm_seq": dict(kind="lstm", B=8, L=2048, H=2048, same_as="c3_lstm"),
     "x_gru_long_seq": dict(kind="gru", B=16, L=1048576, H=1, same_as="c4_gru_long_fwd_adj"),
+    # the 4x4 block scan at the diagonal scan's byte count (96 B per block position)
+    "x_linscan_blk4": dict(kind="linscan_blk", B=16, L=2048, H=256, k=4),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -178,4 +180,6 @@ def workload_inputs(name: str) -> dict:
         return linscan_blk2_inputs(B, L, H, seed)
     if name == "x_lstm_adjoint":
         return lstm_inputs(B, L, H, seed, grad=True)
+    if name == "x_linscan_blk4":
+        return linscan_blk_inputs(B, L, H, w["k"], seed)
     raise KeyError(name)

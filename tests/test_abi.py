@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_workspace_query(lib):
-    for op in range(6):
+    for op in range(7):
         assert api.workspace_bytes(op, 2, 100, 70, 8) > 0
         assert api.workspace_bytes(op, 0, 100, 70, 8) == 0
         assert api.workspace_bytes(op, 2, -1, 70, 8) == 0
@@ -60,6 +60,9 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.pararnn_gru_forward(1, 10, 10, *([n] * 8), ctypes.c_float(1e-4), 5, n, n, n, 0, n) == -1
     assert lib.pararnn_adjoint_backward(7, 1, 10, 10, *([n] * 13), 0, n) == -1
     assert lib.pararnn_gru_sequential(1, 0, 10, *([n] * 8), n) == -1
+    assert lib.rnn_linscan_blk(4, 1, 10, 10, n, n, n, n, n, 0, n) == -1
+    assert lib.rnn_linscan_blk(0, 1, 10, 10, n, n, n, n, n, 0, n) == -1
+    assert lib.rnn_linscan_blk(3, 1, 10, 10, n, n, n, n, n, 0, n) == -3  # unsupported k
     assert lib.pararnn_lstm_sequential(1, 10, 10, *([n] * 12), n) == -1
     assert lib.pararnn_status_string(-1) == b"invalid argument"
 

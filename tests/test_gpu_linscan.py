@@ -191,3 +191,58 @@ def test_two_streams_with_their_own_workspaces(orc):
         assert max_abs(host(h), ref1) <= FWD_ATOL
     for h in out2:
         assert max_abs(host(h), ref2) <= FWD_ATOL
+
+
+# 4x4 blocks: time lanes (H < 32: chunks of 4 waves x 64 threads x 2
+# positions) and channel lanes (chunks of 64 channels x 32 positions), ragged
+# tails in L and in the channel blocks.
+BLK4_SHAPES = [(1, 1, 1), (2, 100, 3), (2, 1500, 2), (3, 257, 70), (2, 300, 31), (2, 300, 32),
+               (4, 1000, 64), (1, 64, 4), (2, 97, 130)]
+
+
+@pytest.mark.parametrize("B,L,H", BLK4_SHAPES)
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_linscan_blk4_matches_oracle(orc, B, L, H, with_h0):
+    say("linscan_blk4", B, L, H, with_h0)
+    d = synth.linscan_blk_inputs(B, L, H, 4, seed=300 + B * 7 + H, h0=with_h0)
+    h0 = dev(d["h0"]) if with_h0 else None
+    h = host(api.linscan_blk(dev(d["A"]), dev(d["b"]), h0))
+    ref = orc.linscan_blk(d["A"], d["b"], d["h0"] if with_h0 else None)
+    err = max_abs(h, ref)
+    say(err)
+    assert err <= FWD_ATOL
+
+
+def test_linscan_blk4_full_workload(orc):
+    """The 4x4 scan at the measured size, B=16, L=2048, H=256, every element."""
+    say("linscan_blk4 full workload")
+    d = synth.workload_inputs("x_linscan_blk4")
+    h = host(api.linscan_blk(dev(d["A"]), dev(d["b"])))
+    err = max_abs(h, orc.linscan_blk(d["A"], d["b"]))
+    say(err)
+    assert err <= FWD_ATOL
+
+
+def test_linscan_blk_k2_is_the_2x2_scan(orc):
+    d = synth.linscan_blk2_inputs(2, 700, 40, seed=310, h0=True)
+    h = host(api.linscan_blk(dev(d["A"]), dev(d["b"]), dev(d["h0"])))
+    assert max_abs(h, orc.linscan_blk2(d["A"], d["b"], d["h0"])) <= FWD_ATOL
+
+
+def test_linscan_blk4_repeated_calls_share_a_workspace(orc):
+    """Back-to-back calls on one workspace (launch tags keep the records of the
+    calls apart) give the same result as fresh ones."""
+    d = synth.linscan_blk_inputs(2, 2000, 96, 4, seed=311)
+    A, b = dev(d["A"]), dev(d["b"])
+    ws = api.new_workspace(api.workspace_bytes(api.OP_LINSCAN_BLK4, 2, 2000, 96), A.device)
+    outs = [host(api.linscan_blk(A, b, ws=ws)) for _ in range(3)]
+    ref = orc.linscan_blk(d["A"], d["b"])
+    for h in outs:
+        assert max_abs(h, ref) <= FWD_ATOL
+
+
+def test_linscan_blk_rejects_unsupported_k():
+    A = torch.zeros(1, 4, 2, 3, 3, device="cuda")
+    b = torch.zeros(1, 4, 2, 3, device="cuda")
+    with pytest.raises(api.PararnnError):
+        api.linscan_blk(A, b)
