@@ -1,7 +1,7 @@
 // linscan.hip -- the exported linear-recurrence scans: the diagonal scan
 // (channel lanes: its own persistent kernel that prefetches the next tile;
-// time lanes: the generic chunked look-back scan of scan_core.hpp) and the
-// 2x2 block scan (scan_core.hpp), plus the small fill kernel that
+// time lanes: the generic chunked look-back scan of scan_core.hpp), the
+// 2x2 and 4x4 block scans (scan_core.hpp), plus the small fill kernel that
 // initialises info words, traces and per-iteration slots, and the device
 // query shared by the launchers.
 #include <atomic>
