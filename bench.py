@@ -12,7 +12,11 @@ solve.  The other workloads are measured in the same run and reported under
 "workloads", each with its own roofline: the fully fused GRU Newton forward
 at B=16, L=512, H=4096 (ParaRNN page, Fig. 2 right and Fig. 5 at L = 2^9),
 the LSTM Newton forward at B=8, L=2048, H=2048 and the long-sequence GRU
-forward plus adjoint at B=16, L=2^20, H=1 (the DEER summary's V100 shape).
+forward plus adjoint at B=16, L=2^20, H=1 (the DEER summary's V100 shape),
+then the 2x2 and 4x4 block scans, the LSTM adjoint, the per-iteration
+Newton path, and sequential application (one thread per channel) of the
+same cells on the same inputs, whose ratio to each Newton forward is
+reported as speedup_vs_sequential.
 
 Printed: one JSON line with the metric, the throughput (state elements per
 second = B*L*H / wall time per step), the roofline of the dominant kernel
