@@ -75,12 +75,12 @@ DOMINANT = {
 # taken on: the sha256 prefix of those sources is checked at run time and the
 # figure is dropped (null) once any of them has changed.
 TRAFFIC = {
-    "c1_linscan": {"bytes": 551291699 + 289021952,
+    "c1_linscan": {"bytes": 551421952 + 289021952,
                    "sources": ["common.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-                   "sha256": "ca1412e4e73cc72c"},
-    "c2_gru_fused": {"bytes": 419274547 + 152450969,
+                   "sha256": "3c1d79cf3f80249c"},
+    "c2_gru_fused": {"bytes": 419277619 + 152519270,
                      "sources": ["common.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
-                     "sha256": "3dbbce9e340c6e2d"},
+                     "sha256": "17fe61c95e651689"},
 }
 DESCRIBE = {
     "c1_linscan": "linear diagonal recurrence h_t = a_t h_{t-1} + b_t, B=16 L=4096 H=1024, "
