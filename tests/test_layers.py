@@ -94,3 +94,12 @@ def test_layer_has_no_cpu_path():
     m = layers.ParaGRU(3, 4)
     with pytest.raises((ValueError, api.PararnnError)):
         m(torch.zeros(1, 5, 3))
+
+
+def test_generic_solve_has_no_cpu_path():
+    """The generic Newton solve assembles with torch but solves with the HIP
+    scan, which rejects host tensors."""
+    from nonlinear_rnn_solve_pararnn_amd import generic
+    x = torch.zeros(1, 5, 3)
+    with pytest.raises((ValueError, api.PararnnError)):
+        generic.newton_solve(lambda h, p: torch.tanh(p + h), [x])
