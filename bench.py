@@ -233,11 +233,16 @@ class Workload:
             self.out = torch.empty(B, L, H, device=dev)
             self.out_c = torch.empty(B, L, H, device=dev) if lstm else None
             op = api.OP_LSTM_FORWARD if lstm else api.OP_GRU_FORWARD
-            self.ws = api.new_workspace(api.workspace_bytes(op, B, L, H, cap), dev)
             keys = ("pi", "pf", "po", "pg", "ui", "uf", "uo", "ug") if lstm else \
                 ("pz", "pr", "pc", "uz", "ur", "uc")
             args = [t[k] for k in keys]
             var = "PARARNN_LSTM_PATH" if lstm else "PARARNN_GRU_PATH"
+            # the workspace of the path the calls take (the query reads the override too)
+            os.environ[var] = "step"
+            try:
+                self.ws = api.new_workspace(api.workspace_bytes(op, B, L, H, cap), dev)
+            finally:
+                del os.environ[var]
 
             def step():
                 # the library reads the path override at each call

@@ -76,8 +76,13 @@ enum {
 
 /*
  * Bytes of workspace that operation `op` needs at (B, L, H) with Newton
- * iteration cap `max_iter` (ignored by the scans and the adjoints).
- * Returns 0 for invalid arguments.
+ * iteration cap `max_iter` (ignored by the scans and the adjoints).  For the
+ * Newton forwards it is the need of the kernel the call will take, which
+ * depends on L, the cap and the PARARNN_GRU_PATH / PARARNN_LSTM_PATH
+ * environment overrides as read at the time of the query (the GRU's fused
+ * kernel needs none: 256 bytes are returned); a call whose workspace is too
+ * small for its kernel returns PARARNN_ERR_INVALID.  Returns 0 for invalid
+ * arguments.
  */
 size_t pararnn_workspace_bytes(int32_t op, int64_t B, int64_t L, int64_t H,
                                int32_t max_iter);

@@ -33,8 +33,6 @@ int clear_trace_tail(float *trace, int32_t from, int32_t to, hipStream_t s) {
     return status_of(fill(fr, 1, s));
 }
 
-size_t max2(size_t a, size_t b) { return a > b ? a : b; }
-
 // Newton from zero reproduces the sequential result after L iterations (and
 // iteration L + 1 confirms it with a zero update), so caps above L + 1 change
 // nothing but the number of launches: they are taken as L + 1 (a trace still
@@ -47,15 +45,6 @@ int32_t eff_cap(int32_t max_iter, int64_t L) {
 // grows with the cap; above kChainMaxCap the per-iteration path is used.
 bool chain_ok(int32_t cap) { return cap <= kChainMaxCap; }
 
-// Workspace of a Newton forward: enough for every path the call may take.
-size_t gru_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
-    const size_t step = newton_ws(kCfgGruStep, 1, B, L, H, cap).total;
-    return chain_ok(cap) ? max2(step, chain_ws(kCfgGruChain, 1, B, L, H, cap).total) : step;
-}
-size_t lstm_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
-    const size_t step = newton_ws(kCfgLstmStep, 2, B, L, H, cap).total;
-    return chain_ok(cap) ? max2(step, chain_ws(kCfgLstmChain, 2, B, L, H, cap).total) : step;
-}
 
 // Path of a Newton forward.  The GRU takes the fused on-chip kernel while
 // the sequence fits one workgroup's registers; longer sequences (and the
@@ -96,6 +85,21 @@ Path gru_path(int64_t L, int32_t cap) {
 Path lstm_path(int32_t cap) {
     const Path p = env_path("PARARNN_LSTM_PATH");
     return (p == Path::Step || !chain_ok(cap)) ? Path::Step : Path::Chain;
+}
+
+// Workspace of a Newton forward: that of the path the call takes (the fused
+// kernel uses none; the query returns the 256-byte minimum for it).
+constexpr size_t kMinWs = 256;
+size_t gru_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
+    switch (gru_path(L, cap)) {
+        case Path::Chain: return chain_ws(kCfgGruChain, 1, B, L, H, cap).total;
+        case Path::Step: return newton_ws(kCfgGruStep, 1, B, L, H, cap).total;
+        default: return kMinWs;
+    }
+}
+size_t lstm_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
+    return lstm_path(cap) == Path::Chain ? chain_ws(kCfgLstmChain, 2, B, L, H, cap).total
+                                         : newton_ws(kCfgLstmStep, 2, B, L, H, cap).total;
 }
 
 }  // namespace

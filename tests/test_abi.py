@@ -39,18 +39,26 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(api.EXPORTS) <= set(_declared())
 
 
-def test_workspace_query(lib):
+def test_workspace_query(lib, monkeypatch):
     for op in range(7):
         assert api.workspace_bytes(op, 2, 100, 70, 8) > 0
         assert api.workspace_bytes(op, 0, 100, 70, 8) == 0
         assert api.workspace_bytes(op, 2, -1, 70, 8) == 0
     assert api.workspace_bytes(api.OP_GRU_FORWARD, 2, 100, 70, 0) == 0
     assert api.workspace_bytes(99, 2, 100, 70, 8) == 0
+    # the fused GRU kernel (L <= 512) needs none beyond the minimum; a forced
+    # override is sized for the kernel it forces
+    assert api.workspace_bytes(api.OP_GRU_FORWARD, 16, 512, 4096, 32) == 256
+    assert api.workspace_bytes(api.OP_GRU_FORWARD, 16, 513, 4096, 32) > 256
     # grows with the iteration cap: records of every iteration on the chained
     # path (caps up to 64), one max|delta| slot per iteration beyond
     for op in (api.OP_GRU_FORWARD, api.OP_LSTM_FORWARD):
         assert api.workspace_bytes(op, 16, 4096, 64, 60) > api.workspace_bytes(op, 16, 4096, 64, 2)
         assert api.workspace_bytes(op, 16, 4096, 64, 500) > api.workspace_bytes(op, 16, 4096, 64, 100)
+    monkeypatch.setenv("PARARNN_GRU_PATH", "step")
+    assert api.workspace_bytes(api.OP_GRU_FORWARD, 16, 512, 4096, 32) > 256
+    monkeypatch.setenv("PARARNN_GRU_PATH", "chain")
+    assert api.workspace_bytes(api.OP_GRU_FORWARD, 16, 512, 4096, 32) > 256
 
 
 def test_invalid_arguments_rejected_on_host(lib):
