@@ -48,6 +48,7 @@ ALG_BYTES = {
     "x_lstm_adjoint": 48,        # gh, gc, 4 p, h, c in; 4 dp out
     "x_lstm_step": 24,           # as c3_lstm: the whole solve's inputs once, outputs once
     "x_gru_long_step": 16,       # 3 p in; h out (the forward of c4 alone)
+    "x_gru_long_fwd": 16,        # 3 p in; h out (the forward of c4 alone)
     "x_gru_seq": 16,             # 3 p in; h out
     "x_lstm_seq": 24,            # 4 p in; h, c out
     "x_gru_long_seq": 16,        # 3 p in; h out
@@ -64,6 +65,7 @@ DOMINANT = {
                    "launches after convergence exit at once)",
     "x_gru_long_step": "chunk_scan_kernel<GruStepOp> (one launch per iteration up to the cap; "
                        "launches after convergence exit at once)",
+    "x_gru_long_fwd": "newton_chain_kernel<GruChain> (time lanes, one launch for every iteration)",
     "x_gru_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
     "x_lstm_seq": "lstm_rollout_kernel (sequential application, one thread per channel)",
     "x_gru_long_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
@@ -99,6 +101,7 @@ DESCRIBE = {
                    "(PARARNN_LSTM_PATH=step)",
     "x_gru_long_step": "the GRU Newton forward of c4_gru_long_fwd_adj on the per-iteration path "
                        "(PARARNN_GRU_PATH=step)",
+    "x_gru_long_fwd": "the GRU Newton forward of c4_gru_long_fwd_adj alone (chained kernel)",
     "x_gru_seq": "sequential application of the GRU cell on the inputs of c2_gru_fused "
                  "(B*H = 65536 threads, 512 positions each)",
     "x_lstm_seq": "sequential application of the LSTM cell on the inputs of c3_lstm "
@@ -112,7 +115,8 @@ DESCRIBE = {
 
 # Sequential-application workload on the same inputs as a Newton forward.
 SEQUENTIAL_OF = {"c2_gru_fused": "x_gru_seq", "c3_lstm": "x_lstm_seq",
-                 "x_lstm_step": "x_lstm_seq", "x_gru_long_step": "x_gru_long_seq"}
+                 "x_lstm_step": "x_lstm_seq", "x_gru_long_step": "x_gru_long_seq",
+                 "x_gru_long_fwd": "x_gru_long_seq"}
 
 
 def measured_traffic(name):
@@ -257,6 +261,13 @@ class Workload:
                 finally:
                     del os.environ[var]
             self._step = step
+        elif name == "x_gru_long_fwd":
+            self.out = torch.empty(B, L, H, device=dev)
+            cap = self.w["cap"]
+            self.ws = api.new_workspace(api.workspace_bytes(api.OP_GRU_FORWARD, B, L, H, cap), dev)
+            args = [t[k] for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
+            self._step = lambda: api.gru_forward(*args, None, tol=self.w["tol"], max_iter=cap,
+                                                 out=self.out, info=self.info, ws=self.ws)
         elif name in ("x_gru_seq", "x_gru_long_seq"):
             self.out = torch.empty(B, L, H, device=dev)
             args = [t[k] for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
@@ -405,7 +416,8 @@ def main():
         log("workload", name)
         wl = Workload(name, dev)
         iters = wl.iterations() if name in ("c2_gru_fused", "c3_lstm", "c4_gru_long_fwd_adj",
-                                            "x_lstm_step", "x_gru_long_step") else None
+                                            "x_lstm_step", "x_gru_long_step",
+                                            "x_gru_long_fwd") else None
         wall_ms, ev_ms = time_workload(wl, args.steps, args.warmup)
         results[name] = {
             "elements": wl.elements,

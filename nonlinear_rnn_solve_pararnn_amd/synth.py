@@ -40,6 +40,9 @@ WORKLOADS = {
                             same_as="c4_gru_long_fwd_adj"),
     # sequential application (one thread per channel) on the inputs of the
     # fused GRU forward, the LSTM forward and the long GRU forward
+    # the long GRU forward alone (chained kernel), for its ratio to sequential application
+    "x_gru_long_fwd": dict(kind="gru", B=16, L=1048576, H=1, tol=1e-4, cap=32,
+                           same_as="c4_gru_long_fwd_adj"),
     "x_gru_seq": dict(kind="gru", B=16, L=512, H=4096, same_as="c2_gru_fused"),
     "x_lstm_seq": dict(kind="lstm", B=8, L=2048, H=2048, same_as="c3_lstm"),
     "x_gru_long_seq": dict(kind="gru", B=16, L=1048576, H=1, same_as="c4_gru_long_fwd_adj"),
