@@ -366,8 +366,11 @@ __device__ __forceinline__ float2s state_add(float2s a, float2s b) { return {a.x
 // ---------------------------------------------------------------- tile
 // LOCAL: the workgroup also ran the previous chunk of this chain (see
 // newton_local_kernel), so the previous chunk's inclusive deltas are in LDS
-// (s_rec, iteration k at row k-1), and kprev/cprev hold its last iteration and
-// whether it stopped converged; nothing goes through global memory.
+// (s_rec, two halves used by alternate chunks, iteration k at row k-1), and
+// kprev/cprev hold its last iteration and whether it stopped converged;
+// nothing goes through global memory.  Every thread reads the delta entering
+// the chunk from the previous chunk's half itself, while the holder writes
+// this chunk's into the other half, so no barrier is needed between them.
 template <class Cell, int NW, int C, bool CL, bool LOCAL = false>
 __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, uint32_t tag,
                                            int &kprev, bool &cprev) {
@@ -385,7 +388,8 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
     __shared__ State s_last[CL ? NT : NW];
     __shared__ uint32_t s_wmax[NW];
     __shared__ int s_stop;
-    __shared__ State s_rec[LOCAL ? kChainMaxCap * 64 : 1];
+    constexpr int kRecHalf = kChainMaxCap * 64;
+    __shared__ State s_rec[LOCAL ? 2 * kRecHalf : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t per_q = g.B * g.ncb;
@@ -497,14 +501,12 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
         }
 
         // delta entering the chunk at iteration k
+        State cin;
         if (LOCAL) {
-            if (holder) {
-                // the previous chunk's inclusive delta at k (zero once it has
-                // stopped), replaced by this chunk's for the next chunk
-                const State din = (q > 0 && k <= kprev) ? s_rec[(k - 1) * 64 + lane] : M::zero();
-                s_rec[(k - 1) * 64 + lane] = M::apply(tot, din);
-                s_carry[lane] = din;
-            }
+            // the previous chunk's inclusive delta at k (zero once it has
+            // stopped); the holder records this chunk's for the next chunk
+            cin = (q > 0 && k <= kprev) ? s_rec[((q - 1) & 1) * kRecHalf + (k - 1) * 64 + lane] : M::zero();
+            if (holder) s_rec[(q & 1) * kRecHalf + (k - 1) * 64 + lane] = M::apply(tot, cin);
         } else if (CL) {
             if (holder) {
                 State din = M::zero();
@@ -528,10 +530,12 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
                 s_carry[0] = din;
             }
         }
-        lds_barrier();
+        if (!LOCAL) {
+            lds_barrier();
+            cin = s_carry[CL ? lane : 0];
+        }
 
         // apply: delta through the sub-chunk, s += delta
-        const State cin = s_carry[CL ? lane : 0];
         if (sub == 0) hb = state_add(hb, cin);  // the previous chunk's last state at iterate k
         State dlt = M::apply(ex, cin);
         uint32_t mx = 0;
