@@ -39,12 +39,12 @@ def _seq(kind, p, u, h0, c0):
     return torch.stack(hs, 1), (torch.stack(cs, 1) if cs else None)
 
 
-def reference(kind, d, with_h0=True, loss_on=("h", "c")):
+def reference(kind, d, with_h0=True, loss_on=("h", "c"), bias=True):
     """Outputs and gradients of loss = sum(gh*h) (+ sum(gc*c)) in fp64."""
     t = {k: torch.tensor(np.asarray(v, dtype=np.float64), requires_grad=True) for k, v in d.items()}
     B, L, D = d["x"].shape
     H = d["u"].shape[1]
-    p = [t["x"] @ t["weight"][g].T + t["bias"][g] for g in range(NG[kind])]
+    p = [t["x"] @ t["weight"][g].T + (t["bias"][g] if bias else 0.0) for g in range(NG[kind])]
     h0 = t["h0"] if with_h0 else torch.zeros(B, H, dtype=torch.float64)
     c0 = t["c0"] if with_h0 else torch.zeros(B, H, dtype=torch.float64)
     h, c = _seq(kind, p, [t["u"][g] for g in range(NG[kind])], h0, c0)
@@ -57,7 +57,7 @@ def reference(kind, d, with_h0=True, loss_on=("h", "c")):
     out = {"h": h.detach().numpy()}
     if c is not None:
         out["c"] = c.detach().numpy()
-    for k in ("x", "weight", "bias", "u"):
+    for k in ("x", "weight", "bias", "u") if bias else ("x", "weight", "u"):
         out["d" + k] = t[k].grad.numpy()
     if with_h0:
         out["dh0"] = t["h0"].grad.numpy()
@@ -66,14 +66,15 @@ def reference(kind, d, with_h0=True, loss_on=("h", "c")):
     return out
 
 
-def run_layer(kind, d, device, with_h0=True, loss_on=("h", "c"), tol=1e-5, max_iter=32):
+def run_layer(kind, d, device, with_h0=True, loss_on=("h", "c"), tol=1e-5, max_iter=32, bias=True):
     """The same through layers.ParaGRU / ParaLSTM on `device` (fp32)."""
     B, L, D = d["x"].shape
     H = d["u"].shape[1]
     cls = layers.ParaGRU if kind == "gru" else layers.ParaLSTM
-    m = cls(D, H, tol=tol, max_iter=max_iter, device=device)
+    m = cls(D, H, bias=bias, tol=tol, max_iter=max_iter, device=device)
+    keys = ("weight", "bias", "u") if bias else ("weight", "u")
     with torch.no_grad():
-        for k in ("weight", "bias", "u"):
+        for k in keys:
             getattr(m, k).copy_(torch.from_numpy(d[k]))
     x = torch.from_numpy(d["x"]).to(device).requires_grad_(True)
     h0 = torch.from_numpy(d["h0"]).to(device).requires_grad_(True) if with_h0 else None
@@ -95,7 +96,7 @@ def run_layer(kind, d, device, with_h0=True, loss_on=("h", "c"), tol=1e-5, max_i
     if c is not None:
         out["c"] = c.detach().cpu().numpy()
     out["dx"] = x.grad.cpu().numpy()
-    for k in ("weight", "bias", "u"):
+    for k in keys:
         out["d" + k] = getattr(m, k).grad.cpu().numpy()
     if with_h0:
         out["dh0"] = h0.grad.cpu().numpy()

@@ -41,3 +41,23 @@ def test_layer_without_initial_state(kind):
 def test_lstm_layer_loss_on_one_output(loss_on):
     d = synth.layer_inputs(2, 150, 4, 40, 4, seed=161)
     _check("lstm", run_layer("lstm", d, DEV, loss_on=loss_on), reference("lstm", d, loss_on=loss_on))
+
+
+def test_layer_without_bias_on_the_per_iteration_path():
+    """bias=False, and a cap above the chained kernel's limit (per-iteration
+    launches) with L > 512."""
+    d = synth.layer_inputs(2, 700, 5, 40, 3, seed=162)
+    got = run_layer("gru", d, DEV, max_iter=100, bias=False)
+    assert "dbias" not in got
+    _check("gru", got, reference("gru", d, bias=False))
+
+
+def test_layer_inference_without_grad():
+    import torch
+    from nonlinear_rnn_solve_pararnn_amd import layers
+    m = layers.ParaLSTM(4, 33, device=DEV)
+    x = torch.randn(2, 50, 4, device=DEV)
+    with torch.no_grad():
+        h, c = m(x)
+    assert not h.requires_grad and h.shape == (2, 50, 33) and c.shape == (2, 50, 33)
+    assert m.last_info.cpu().tolist()[1] == 1

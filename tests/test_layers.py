@@ -69,6 +69,11 @@ def test_layer_gradients_match_autograd_rollout(oracle_solve, kind, with_h0):
     _compare(run_layer(kind, d, "cpu", with_h0=with_h0), reference(kind, d, with_h0=with_h0))
 
 
+def test_layer_without_bias(oracle_solve):
+    d = synth.layer_inputs(2, 25, 3, 4, 4, seed=142)
+    _compare(run_layer("lstm", d, "cpu", bias=False), reference("lstm", d, bias=False))
+
+
 @pytest.mark.parametrize("loss_on", [("h",), ("c",)])
 def test_lstm_loss_on_one_output(oracle_solve, loss_on):
     d = synth.layer_inputs(2, 20, 4, 3, 4, seed=141)
