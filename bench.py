@@ -144,19 +144,22 @@ def roofline(name, elements, kernel_ms):
             "kernel_us": kernel_ms * 1e3}
 
 
-# Arithmetic roofs of the Newton kernels that iterate on chip, from their
-# gfx950 assembly (VALU instructions of the Newton loop per position and
-# iteration; transcendentals are exp2 and reciprocal).  The fp32 vector peak of
-# 157.3 TFLOP/s is 78.6 T lane-operations per second of FMA issue;
-# transcendentals issue at a quarter of that rate, so each costs four slots.
-#  - fused GRU: 541 VALU instructions per 16 positions, 27.8 plain and 6
-#    transcendental per position;
-#  - LSTM, workgroups owning whole chains (8 waves x 8 positions): 600 VALU
-#    instructions per 8 positions, 65 plain and 10 transcendental per position
-#    (the cross-wave composition of the sub-chunk maps not counted).
+# Arithmetic roofs of the Newton kernels that iterate on chip.  VALU issue
+# slots per element and Newton iteration, from rocprofv3 counters of one
+# dispatch (SQ_INSTS_VALU and SQ_INSTS_VALU_TRANS_F32 count wave instructions;
+# times 64 lanes, over elements x iterations): plain instructions count one
+# slot, transcendentals (exp2, reciprocal) four, since they issue at a
+# quarter of the rate.  The fp32 vector peak of 157.3 TFLOP/s is 78.6 T
+# lane-operations per second of FMA issue.
+#  - fused GRU, B=16 L=512 H=4096, 4 iterations: 80,297,984 VALU and
+#    12,615,680 transcendental wave instructions = 38.29 and 6.02 per element
+#    and iteration (the gfx950 assembly of the loop gives 33.8 and 6; the rest
+#    is per-iteration work outside the cell loop);
+#  - LSTM whole chains, B=8 L=2048 H=2048, 4 iterations: 180,076,284 and
+#    20,975,616 = 85.87 and 10.00.
 ALU_SLOTS_PER_ELEMENT_ITER = {
-    "c2_gru_fused": 27.8 + 6 * 4,
-    "c3_lstm": 65.0 + 10 * 4,
+    "c2_gru_fused": (38.29 - 6.02) + 6.02 * 4,
+    "c3_lstm": (85.87 - 10.00) + 10.00 * 4,
 }
 PEAK_VALU_TOPS = 78.6
 

@@ -26,7 +26,8 @@ def test_roofline_object():
     assert r["achieved"] == pytest.approx(805306368 / 0.128e-3 / 1e9)
     assert r["frac"] == pytest.approx(r["achieved"] / 8000.0)
     a = bench.alu_roofline("c3_lstm", 1000, 4, 1.0)
-    assert a["bound"] == "alu" and a["achieved"] == pytest.approx(105.0 * 4000 / 1e-3 / 1e12)
+    per = bench.ALU_SLOTS_PER_ELEMENT_ITER["c3_lstm"]
+    assert a["bound"] == "alu" and a["achieved"] == pytest.approx(per * 4000 / 1e-3 / 1e12)
 
 
 def test_every_workload_has_bytes_kernel_and_description():
