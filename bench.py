@@ -174,6 +174,29 @@ def alu_roofline(name, elements, iterations, kernel_ms):
                      "%d iterations (the most any tile took)" % (per, iterations)}
 
 
+def copy_ceiling(dev, reps=10):
+    """Achievable HBM bandwidth on this device: a plain 1 GiB device-to-device
+    copy (torch copy_, read + write), timed with HIP events."""
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * 4 * n / (ms * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return {"value": gbs, "unit": "GB/s", "frac_of_peak": gbs / PEAK_HBM_GBS,
+            "what": "torch copy_ of 1 GiB fp32 (1 GiB read + 1 GiB written), %d copies, HIP events" % reps}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -367,15 +390,29 @@ def cpu_baseline(name, host):
         fn = lambda: oracle.linscan_diag(*args)
         n = args[0].size
         what = "fp64 serial linear recurrence (oracle.linscan_diag) over the full workload"
+    def timed(limit_s, max_reps):
+        reps, t = 0, 0.0
+        t0 = time.perf_counter()
+        while t < limit_s and reps < max_reps:
+            fn()
+            reps += 1
+            t = time.perf_counter() - t0
+        return reps, t
+
     fn()  # page-in
-    reps, t = 0, 0.0
-    t0 = time.perf_counter()
-    while t < 10.0 and reps < 400:
-        fn()
-        reps += 1
-        t = time.perf_counter() - t0
-    return {"value": n * reps / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": "%s, %d repetition(s), %.2f s" % (what, reps, t)}
+    reps, t = timed(10.0, 400)
+    out = {"value": n * reps / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
+           "sample": "%s, %d repetition(s), %.2f s" % (what, reps, t)}
+    # the same on one core (channels are independent, so the threaded figure
+    # is this one times the parallel efficiency)
+    oracle.set_num_threads(1)
+    try:
+        reps1, t1 = timed(4.0, 400)
+    finally:
+        oracle.set_num_threads(threads)
+    out["single_thread"] = {"value": n * reps1 / t1, "cores": 1,
+                            "sample": "%d repetition(s), %.2f s" % (reps1, t1)}
+    return out
 
 
 def main():
@@ -470,6 +507,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline(args.workload, synth.workload_inputs(args.workload))
     else:
         out["cpu_baseline"] = None
+    if not args.only:
+        out["copy_ceiling"] = copy_ceiling(dev)
     if len(results) > 1:
         out["workloads"] = {k: v for k, v in results.items() if k != args.workload}
     print(json.dumps(out), flush=True)
