@@ -174,9 +174,10 @@ def alu_roofline(name, elements, iterations, kernel_ms):
                      "%d iterations (the most any tile took)" % (per, iterations)}
 
 
-def copy_ceiling(dev, reps=10):
-    """Achievable HBM bandwidth on this device: a plain 1 GiB device-to-device
-    copy (torch copy_, read + write), timed with HIP events."""
+def device_copy(dev, reps=10):
+    """Bandwidth of a plain 1 GiB device-to-device copy (torch copy_, read +
+    write), timed with HIP events: a reference point for the HBM figures
+    (kernels with streamed loads go past it)."""
     import torch
     n = 1 << 28
     a = torch.ones(n, device=dev)
@@ -508,7 +509,7 @@ def main():
     else:
         out["cpu_baseline"] = None
     if not args.only:
-        out["copy_ceiling"] = copy_ceiling(dev)
+        out["device_copy"] = device_copy(dev)
     if len(results) > 1:
         out["workloads"] = {k: v for k, v in results.items() if k != args.workload}
     print(json.dumps(out), flush=True)
