@@ -174,6 +174,71 @@ def alu_roofline(name, elements, iterations, kernel_ms):
                      "%d iterations (the most any tile took)" % (per, iterations)}
 
 
+def _torch_gru_cell(h, pz, pr, pc, uz, ur, uc):
+    import torch
+    z = torch.sigmoid(pz + uz * h)
+    r = torch.sigmoid(pr + ur * h)
+    c = torch.tanh(pc + uc * (r * h))
+    return (1 - z) * h + z * c
+
+
+def modalities(dev, steps, warmup):
+    """The GRU at B=16, L=512, H=4096 (the fused workload's inputs) through
+    every way this library can evaluate it (ParaRNN page, Fig. 2 and Fig. 5:
+    sequential application, tensor-op assembly with a dedicated reduction
+    kernel, one fused pass per iteration, the fully fused solver), and the
+    residual max|delta| per Newton iteration from a zero start at several
+    sequence lengths (Fig. 4, on synthetic inputs)."""
+    import torch
+
+    from nonlinear_rnn_solve_pararnn_amd import api, generic, synth
+    w = synth.WORKLOADS["c2_gru_fused"]
+    host = synth.workload_inputs("c2_gru_fused")
+    t = {k: torch.from_numpy(v).to(dev) for k, v in host.items()}
+    p = [t["pz"], t["pr"], t["pc"]]
+    u = [t["uz"], t["ur"], t["uc"]]
+    tol, cap = w["tol"], w["cap"]
+
+    def per_iteration():
+        os.environ["PARARNN_GRU_PATH"] = "step"
+        try:
+            return api.gru_forward(*p, *u, tol=tol, max_iter=cap)
+        finally:
+            del os.environ["PARARNN_GRU_PATH"]
+
+    ways = {
+        "sequential application (one thread per channel)": lambda: api.gru_sequential(*p, *u),
+        "torch assembly + HIP diagonal scan (generic.newton_solve)":
+            lambda: generic.newton_solve(_torch_gru_cell, p, None, u, tol=tol, max_iter=cap),
+        "one fused pass per Newton iteration (chunk_scan_kernel<GruStepOp>)": per_iteration,
+        "fully fused Newton (gru_fused_kernel)": lambda: api.gru_forward(*p, *u, tol=tol, max_iter=cap),
+    }
+    ref = api.gru_sequential(*p, *u)
+    out = {"workload": "GRU B=16 L=512 H=4096, pz, pr, pc = 0.5 N(0,1), u ~ U(-0.5,0.5), "
+                       "h0 = 0, tol 1e-4, cap 32", "ms_per_call": {}, "max_abs_vs_sequential": {}}
+    for name, fn in ways.items():
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            h = fn()
+        torch.cuda.synchronize()
+        out["ms_per_call"][name] = (time.perf_counter() - t0) / steps * 1e3
+        out["max_abs_vs_sequential"][name] = float((h - ref).abs().max())
+    # residual per iteration from h = 0 at fixed B*H, tol = 0 (no early stop)
+    traces = {}
+    for L in (64, 512, 4096, 32768):
+        d = synth.gru_inputs(8, L, 256, seed=700 + L)
+        a = [torch.from_numpy(d[k]).to(dev) for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
+        tr = torch.zeros(12, device=dev)
+        api.gru_forward(*a, tol=0.0, max_iter=12, trace=tr)
+        traces["L=%d" % L] = [float(x) for x in tr.cpu()]
+    out["residual_per_iteration"] = {"shape": "B=8 H=256, p ~ N(0,1), u ~ U(-0.5,0.5), h = 0 start, "
+                                              "max|delta| of iterations 1..12", "traces": traces}
+    return out
+
+
 def device_copy(dev, reps=10):
     """Bandwidth of a plain 1 GiB device-to-device copy (torch copy_, read +
     write), timed with HIP events: a reference point for the HBM figures
@@ -426,6 +491,8 @@ def main():
     ap.add_argument("--only", action="store_true",
                     help="measure only the chosen workload (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--modalities", action="store_true",
+                    help="only the modality comparison and residual traces (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -439,6 +506,10 @@ def main():
 
     import torch
     dev = torch.device("cuda:0")
+
+    if args.modalities:
+        print(json.dumps(modalities(dev, args.steps, args.warmup)), flush=True)
+        return
 
     if args.copy_calibration:
         n = 1 << 28  # 1 GiB of fp32
