@@ -182,60 +182,147 @@ def _torch_gru_cell(h, pz, pr, pc, uz, ur, uc):
     return (1 - z) * h + z * c
 
 
-def modalities(dev, steps, warmup):
-    """The GRU at B=16, L=512, H=4096 (the fused workload's inputs) through
-    every way this library can evaluate it (ParaRNN page, Fig. 2 and Fig. 5:
-    sequential application, tensor-op assembly with a dedicated reduction
-    kernel, one fused pass per iteration, the fully fused solver), and the
-    residual max|delta| per Newton iteration from a zero start at several
-    sequence lengths (Fig. 4, on synthetic inputs)."""
+def _torch_lstm_cell(s, pi, pf, po, pg, ui, uf, uo, ug):
+    import torch
+    cp, hp = s[..., 0], s[..., 1]
+    i = torch.sigmoid(pi + ui * hp)
+    f = torch.sigmoid(pf + uf * hp)
+    o = torch.sigmoid(po + uo * hp)
+    g = torch.tanh(pg + ug * hp)
+    c = f * cp + i * g
+    return torch.stack([c, o * torch.tanh(c)], dim=-1)
+
+
+class _env:
+    """Set (or, with None, remove) an environment variable for a block and
+    restore what was there before."""
+
+    def __init__(self, name, value):
+        self.name, self.value = name, value
+
+    def __enter__(self):
+        self.old = os.environ.get(self.name)
+        if self.value is None:
+            os.environ.pop(self.name, None)
+        else:
+            os.environ[self.name] = self.value
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            os.environ.pop(self.name, None)
+        else:
+            os.environ[self.name] = self.old
+
+
+def _event_median_ms(fn, reps, warmup=1):
+    """Median over `reps` calls of fn, each between its own HIP event pair on
+    the current stream (the stream the library launches on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    pairs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in pairs)
+    return t[len(t) // 2]
+
+
+# Sequence lengths and shape of the modality sweep (ParaRNN page, Fig. 5:
+# time against L for ParaGRU and ParaLSTM, each way of evaluating them).
+SWEEP_L = (512, 2048, 8192, 32768)
+SWEEP_B, SWEEP_H = 16, 256
+
+
+def modalities(dev, reps=3):
+    """The ParaRNN page's Fig. 5 and Fig. 4 on synthetic inputs.
+
+    Fig. 5: the GRU and the LSTM at B=16, H=256 and L = 2^9 ... 2^15 through
+    every way this library evaluates them: sequential application (one
+    thread per channel), tensor-op assembly with the library's scan as the
+    reduction kernel (generic.newton_solve), one fused pass per Newton
+    iteration, and the fully fused solver (one launch for the whole solve:
+    the fused GRU kernel up to L = 512, the chained kernel beyond, and the
+    chained kernel for every LSTM).  Inputs: torch's seeded generator on the
+    device, p ~ N(0,1), u ~ U(-0.5, 0.5), zero initial state, tol 1e-4, cap
+    32.  Times are medians of HIP-event pairs around each call.
+
+    Fig. 4: max|delta| per Newton iteration from a zero start (tol = 0, no
+    early stop) for both cells at B=8, H=256 and several L."""
     import torch
 
-    from nonlinear_rnn_solve_pararnn_amd import api, generic, synth
-    w = synth.WORKLOADS["c2_gru_fused"]
-    host = synth.workload_inputs("c2_gru_fused")
-    t = {k: torch.from_numpy(v).to(dev) for k, v in host.items()}
-    p = [t["pz"], t["pr"], t["pc"]]
-    u = [t["uz"], t["ur"], t["uc"]]
-    tol, cap = w["tol"], w["cap"]
-
-    def per_iteration():
-        os.environ["PARARNN_GRU_PATH"] = "step"
-        try:
-            return api.gru_forward(*p, *u, tol=tol, max_iter=cap)
-        finally:
-            del os.environ["PARARNN_GRU_PATH"]
-
-    ways = {
-        "sequential application (one thread per channel)": lambda: api.gru_sequential(*p, *u),
-        "torch assembly + HIP diagonal scan (generic.newton_solve)":
-            lambda: generic.newton_solve(_torch_gru_cell, p, None, u, tol=tol, max_iter=cap),
-        "one fused pass per Newton iteration (chunk_scan_kernel<GruStepOp>)": per_iteration,
-        "fully fused Newton (gru_fused_kernel)": lambda: api.gru_forward(*p, *u, tol=tol, max_iter=cap),
-    }
-    ref = api.gru_sequential(*p, *u)
-    out = {"workload": "GRU B=16 L=512 H=4096, pz, pr, pc = 0.5 N(0,1), u ~ U(-0.5,0.5), "
-                       "h0 = 0, tol 1e-4, cap 32", "ms_per_call": {}, "max_abs_vs_sequential": {}}
-    for name, fn in ways.items():
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            h = fn()
-        torch.cuda.synchronize()
-        out["ms_per_call"][name] = (time.perf_counter() - t0) / steps * 1e3
-        out["max_abs_vs_sequential"][name] = float((h - ref).abs().max())
-    # residual per iteration from h = 0 at fixed B*H, tol = 0 (no early stop)
-    traces = {}
+    from nonlinear_rnn_solve_pararnn_amd import api, generic
+    tol, cap = 1e-4, 32
+    out = {"shape": "B=%d H=%d, p ~ N(0,1), u ~ U(-0.5,0.5), zero initial state, tol %g, cap %d"
+                    % (SWEEP_B, SWEEP_H, tol, cap),
+           "timing": "median of %d HIP-event pairs per call (after one warm-up call)" % reps,
+           "ms_per_call": {"gru": {}, "lstm": {}}, "speedup_fused_vs_sequential": {"gru": {}, "lstm": {}},
+           "max_abs_vs_sequential": {"gru": {}, "lstm": {}}}
+    for cell in ("gru", "lstm"):
+        ng = 3 if cell == "gru" else 4
+        var = "PARARNN_GRU_PATH" if cell == "gru" else "PARARNN_LSTM_PATH"
+        for L in SWEEP_L:
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(7000 + L + (0 if cell == "gru" else 1))
+            p = [torch.randn(SWEEP_B, L, SWEEP_H, device=dev, generator=gen) for _ in range(ng)]
+            u = [torch.rand(SWEEP_H, device=dev, generator=gen) - 0.5 for _ in range(ng)]
+            if cell == "gru":
+                h_out = torch.empty_like(p[0])
+                seq = lambda: api.gru_sequential(*p, *u, out=h_out)  # noqa: E731
+                torch_asm = lambda: generic.newton_solve(_torch_gru_cell, p, None, u, tol=tol,  # noqa: E731
+                                                         max_iter=cap)
+                newton = lambda: api.gru_forward(*p, *u, tol=tol, max_iter=cap, out=h_out)  # noqa: E731
+                fused_path = "fused" if L <= 512 else None
+                pick = lambda r: r  # noqa: E731
+            else:
+                h_out, c_out = torch.empty_like(p[0]), torch.empty_like(p[0])
+                seq = lambda: api.lstm_sequential(*p, *u, out_h=h_out, out_c=c_out)  # noqa: E731
+                torch_asm = lambda: generic.newton_solve(_torch_lstm_cell, p, None, u, tol=tol,  # noqa: E731
+                                                         max_iter=cap, state_size=2)
+                newton = lambda: api.lstm_forward(*p, *u, tol=tol, max_iter=cap,  # noqa: E731
+                                                  out_h=h_out, out_c=c_out)
+                fused_path = None
+                pick = lambda r: r[0] if isinstance(r, tuple) else r[..., 1]  # noqa: E731
+            ways = {"sequential": (seq, None),
+                    "torch_assembly_hip_scan": (torch_asm, None),
+                    "per_iteration_pass": (newton, "step"),
+                    "fully_fused": (newton, fused_path)}
+            ref = pick(seq()).clone()
+            row, err = {}, {}
+            for name, (fn, path) in ways.items():
+                with _env(var, path):
+                    row[name] = _event_median_ms(fn, reps)
+                    err[name] = float((pick(fn()) - ref).abs().max())
+            key = "L=%d" % L
+            out["ms_per_call"][cell][key] = row
+            out["max_abs_vs_sequential"][cell][key] = err
+            out["speedup_fused_vs_sequential"][cell][key] = row["sequential"] / row["fully_fused"]
+            log("modalities", cell, key, json.dumps(row))
+            del p, u
+            torch.cuda.empty_cache()
+    # residual per iteration from a zero start, tol = 0 (no early stop)
+    traces = {"gru": {}, "lstm": {}}
     for L in (64, 512, 4096, 32768):
-        d = synth.gru_inputs(8, L, 256, seed=700 + L)
-        a = [torch.from_numpy(d[k]).to(dev) for k in ("pz", "pr", "pc", "uz", "ur", "uc")]
-        tr = torch.zeros(12, device=dev)
-        api.gru_forward(*a, tol=0.0, max_iter=12, trace=tr)
-        traces["L=%d" % L] = [float(x) for x in tr.cpu()]
-    out["residual_per_iteration"] = {"shape": "B=8 H=256, p ~ N(0,1), u ~ U(-0.5,0.5), h = 0 start, "
-                                              "max|delta| of iterations 1..12", "traces": traces}
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(700 + L)
+        for cell, ng in (("gru", 3), ("lstm", 4)):
+            p = [torch.randn(8, L, 256, device=dev, generator=gen) for _ in range(ng)]
+            u = [torch.rand(256, device=dev, generator=gen) - 0.5 for _ in range(ng)]
+            tr = torch.zeros(12, device=dev)
+            if cell == "gru":
+                api.gru_forward(*p, *u, tol=0.0, max_iter=12, trace=tr)
+            else:
+                api.lstm_forward(*p, *u, tol=0.0, max_iter=12, trace=tr)
+            traces[cell]["L=%d" % L] = [float(x) for x in tr.cpu()]
+    out["residual_per_iteration"] = {"shape": "B=8 H=256, p ~ N(0,1), u ~ U(-0.5,0.5), zero start, "
+                                              "max|delta| of iterations 1..12 (tol = 0)",
+                                     "traces": traces}
     return out
 
 
@@ -399,9 +486,20 @@ class Workload:
         return [int(x) for x in self.info.cpu().tolist()]
 
 
-def time_workload(wl, steps, warmup):
-    """Returns (ms per step from the wall clock around K steps, ms per step
-    from a HIP event pair around the same K steps on the launch stream)."""
+# Bytes written between timed reps to evict the MI355X's 256 MB last-level
+# cache (MALL), so that no rep reads inputs the previous one left in it.
+EVICT_BYTES = 512 << 20
+
+
+def time_workload(wl, steps, warmup, scratch):
+    """Times K steps twice.
+
+    back to back: K steps bracketed by a device synchronisation on both
+      sides, timed by the wall clock and by one HIP event pair on the launch
+      stream (the contract's ms per step and value come from the wall clock);
+    cold: before each of K steps a 512 MB scratch write, then the step between
+      its own HIP event pair on the launch stream; the median is the kernel
+      duration the roofline uses."""
     import torch
     for _ in range(warmup):
         wl.step()
@@ -415,12 +513,25 @@ def time_workload(wl, steps, warmup):
     e1.record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    return wall, e0.elapsed_time(e1) / steps
+    warm = e0.elapsed_time(e1) / steps
+    pairs = []
+    for _ in range(steps):
+        scratch.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        wl.step()
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    cold = sorted(a.elapsed_time(b) for a, b in pairs)
+    return {"wall_ms": wall, "warm_event_ms": warm, "cold_median_ms": cold[len(cold) // 2],
+            "cold_min_ms": cold[0], "cold_max_ms": cold[-1]}
 
 
-def cpu_baseline(name, host):
+def cpu_baseline(name, host, budget_s=10.0, single_s=4.0):
     """The fp64 oracle's sequential rollout (the definition of the result) on
-    this host, timed over the full workload or a bounded sample of it."""
+    this host, timed over repetitions of the full workload for about
+    `budget_s` seconds on every core the oracle uses and `single_s` on one."""
     import numpy as np
 
     import oracle
@@ -466,14 +577,14 @@ def cpu_baseline(name, host):
         return reps, t
 
     fn()  # page-in
-    reps, t = timed(10.0, 400)
+    reps, t = timed(budget_s, 400)
     out = {"value": n * reps / t, "unit": "elements/s", "cores": threads, "kind": "oracle",
            "sample": "%s, %d repetition(s), %.2f s" % (what, reps, t)}
     # the same on one core (channels are independent, so the threaded figure
     # is this one times the parallel efficiency)
     oracle.set_num_threads(1)
     try:
-        reps1, t1 = timed(4.0, 400)
+        reps1, t1 = timed(single_s, 400)
     finally:
         oracle.set_num_threads(threads)
     out["single_thread"] = {"value": n * reps1 / t1, "cores": 1,

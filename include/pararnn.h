@@ -25,16 +25,21 @@
  *    persists lives in the caller's workspace).  Outputs must not alias
  *    inputs.
  *  - `ws`/`ws_bytes`: a device scratch buffer of at least
- *    pararnn_workspace_bytes(...) bytes (256-byte aligned).  It must be
- *    zero-filled before its first use (hipMemset, torch.zeros); every call
- *    leaves it ready for the next call of any entry point at any size that
- *    fits, so it is never cleared again, and the caller must not write to it
- *    between calls.  Its first 8 bytes count the workgroups of a launch and
- *    number the launches; the look-back records of the scans carry the
- *    number of the launch that wrote them, which is why no call has to clear
- *    them.  Concurrent calls on different streams need different
- *    workspaces.  A workspace that was not zero-filled gives wrong results
- *    (the kernels still stay in bounds and finish).
+ *    pararnn_workspace_bytes(...) bytes (256-byte aligned); `ws_bytes` is
+ *    its whole size.  It must be zero-filled before its first use
+ *    (hipMemset, torch.zeros); every call leaves it ready for the next call
+ *    of any entry point at any size that fits, so the caller never clears it
+ *    again and must not write to it between calls.  Its first 16 bytes
+ *    count the workgroups of a launch and number the launches; the
+ *    look-back records of the scans carry the number of the launch that
+ *    wrote them, which is why no call has to clear them.  Launch numbers
+ *    repeat after 8,388,606 launches on one workspace: the launch that uses
+ *    the last number clears all `ws_bytes` past the 16-byte header when its
+ *    last workgroup finishes (about a millisecond per few hundred MB, once
+ *    per period), so no record of an earlier period is ever read.
+ *    Concurrent calls on different streams need different workspaces.  A
+ *    workspace that was not zero-filled gives wrong results (the kernels
+ *    still stay in bounds and finish).
  *  - `stream`: a hipStream_t passed as void* (NULL = the default stream).
  *    Every call only enqueues work on that stream and returns; it never
  *    synchronises.  Device-side outputs (including `info`) are valid once
@@ -78,11 +83,12 @@ enum {
  * Bytes of workspace that operation `op` needs at (B, L, H) with Newton
  * iteration cap `max_iter` (ignored by the scans and the adjoints).  For the
  * Newton forwards it is the need of the kernel the call will take, which
- * depends on L, the cap and the PARARNN_GRU_PATH / PARARNN_LSTM_PATH
- * environment overrides as read at the time of the query (the GRU's fused
- * kernel needs none: 256 bytes are returned); a call whose workspace is too
- * small for its kernel returns PARARNN_ERR_INVALID.  Returns 0 for invalid
- * arguments.
+ * depends on the shape, the cap, the device (how many workgroups fit on it)
+ * and the PARARNN_GRU_PATH / PARARNN_LSTM_PATH environment overrides as read
+ * at the time of the query.  The GRU's fused kernel and the chained kernel's
+ * form in which workgroups own whole chains need none: 256 bytes are
+ * returned.  A call whose workspace is too small for its kernel returns
+ * PARARNN_ERR_INVALID.  Returns 0 for invalid arguments.
  */
 size_t pararnn_workspace_bytes(int32_t op, int64_t B, int64_t L, int64_t H,
                                int32_t max_iter);
@@ -104,7 +110,9 @@ int rnn_linscan_diag(int64_t B, int64_t L, int64_t H,
  * solver used by ParaLSTM):
  *     h[b,t,j,:] = A[b,t,j] @ h[b,t-1,j,:] + b[b,t,j,:]
  * A: [B, L, H, 2, 2] row-major blocks (a00, a01, a10, a11).
- * b, h: [B, L, H, 2].  h0: [B, H, 2] or NULL.
+ * b, h: [B, L, H, 2].  h0: [B, H, 2] or NULL.  Any 4-byte alignment; with
+ * A 16-byte aligned and b, h, h0 8-byte aligned, blocks and pairs move as
+ * single vector accesses (faster).
  */
 int rnn_linscan_blk2(int64_t B, int64_t L, int64_t H,
                      const float *A, const float *b, const float *h0,
@@ -120,9 +128,10 @@ int rnn_linscan_blk2(int64_t B, int64_t L, int64_t H,
  * A: [B, L, H, k, k] row-major blocks (A[i][l] takes component l into i).
  * b, h: [B, L, H, k].  h0: [B, H, k] or NULL.
  * k = 2 is rnn_linscan_blk2 (its workspace query, PARARNN_OP_LINSCAN_BLK2);
- * k = 4 needs A, b, h and h0 16-byte aligned and PARARNN_OP_LINSCAN_BLK4
- * workspace.  Other k return PARARNN_ERR_UNSUPPORTED (k < 1:
- * PARARNN_ERR_INVALID).
+ * k = 4 takes PARARNN_OP_LINSCAN_BLK4 workspace and any 4-byte alignment
+ * (with A, b, h and h0 16-byte aligned, block rows and states move as
+ * 16-byte accesses, faster).  Other k return PARARNN_ERR_UNSUPPORTED
+ * (k < 1: PARARNN_ERR_INVALID).
  */
 int rnn_linscan_blk(int32_t k, int64_t B, int64_t L, int64_t H,
                     const float *A, const float *b, const float *h0,

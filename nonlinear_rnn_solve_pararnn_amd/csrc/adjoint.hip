@@ -337,13 +337,13 @@ size_t lstm_adjoint_ws(int64_t B, int64_t L, int64_t H) {
 }
 
 template <class Op, int S, int NWC, int CC, int NWT, int CT>
-static hipError_t run_adjoint(const TileCfg &cfg, Op op, int ngates, const AdjArgs &a, char *ws,
+static hipError_t run_adjoint(const TileCfg &cfg, Op op, int ngates, const AdjArgs &a, const Ws &ws,
                               hipStream_t s) {
     const ScanShape sh0 = scan_shape(cfg, a.B, a.L, a.H);
     const ScanWs w = scan_ws(cfg, S, a.B, a.L, a.H, (sh0.channel_lanes ? 64 : 1) * ngates);
     bool want_u = false;
     for (int q = 0; q < ngates; ++q) want_u = want_u || a.gu[q] != nullptr;
-    op.partial = want_u ? reinterpret_cast<float *>(ws + w.partial) : nullptr;
+    op.partial = want_u ? reinterpret_cast<float *>(ws.p + w.partial) : nullptr;
     ScanGeo g;
     g.B = a.B;
     g.L = a.L;
@@ -351,9 +351,9 @@ static hipError_t run_adjoint(const TileCfg &cfg, Op op, int ngates, const AdjAr
     g.ncb = w.sh.ncb;
     g.nq = w.sh.nq;
     g.ntiles = w.sh.ntiles;
-    g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
-    g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
-    g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
+    g.ws = ws_span(ws, w.partial, w.keep_end);  // the dL/du partials are reduced by the next launch
+    g.agg = reinterpret_cast<uint64_t *>(ws.p + w.agg);
+    g.inc = reinterpret_cast<uint64_t *>(ws.p + w.inc);
     hipError_t e = w.sh.channel_lanes ? launch_chunk_scan<Op, NWC, CC, true>(op, g, s)
                                       : launch_chunk_scan<Op, NWT, CT, false>(op, g, s);
     if (e != hipSuccess || !want_u) return e;
@@ -370,7 +370,7 @@ static hipError_t run_adjoint(const TileCfg &cfg, Op op, int ngates, const AdjAr
     return hipGetLastError();
 }
 
-hipError_t gru_adjoint(const AdjArgs &a, char *ws, hipStream_t s) {
+hipError_t gru_adjoint(const AdjArgs &a, const Ws &ws, hipStream_t s) {
     GruAdjOp op;
     op.pz = a.p[0];
     op.pr = a.p[1];
@@ -395,7 +395,7 @@ hipError_t gru_adjoint(const AdjArgs &a, char *ws, hipStream_t s) {
     return run_adjoint<GruAdjOp, 1, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, op, 3, a, ws, s);
 }
 
-hipError_t lstm_adjoint(const AdjArgs &a, char *ws, hipStream_t s) {
+hipError_t lstm_adjoint(const AdjArgs &a, const Ws &ws, hipStream_t s) {
     LstmAdjOp op;
     op.pi = a.p[0];
     op.pf = a.p[1];

@@ -87,19 +87,23 @@ Path lstm_path(int32_t cap) {
     return (p == Path::Step || !chain_ok(cap)) ? Path::Step : Path::Chain;
 }
 
-// Workspace of a Newton forward: that of the path the call takes (the fused
-// kernel uses none; the query returns the 256-byte minimum for it).
+// Workspace of a Newton forward: that of the kernel the call takes (the
+// fused kernel and the chained kernel's whole-chain form use none; the query
+// returns the 256-byte minimum for them).
 constexpr size_t kMinWs = 256;
 size_t gru_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
     switch (gru_path(L, cap)) {
-        case Path::Chain: return chain_ws(kCfgGruChain, 1, B, L, H, cap).total;
+        case Path::Chain:
+            if (gru_chain_owns_chains(B, L, H, env_chain_local("PARARNN_GRU_PATH"))) return kMinWs;
+            return chain_ws(kCfgGruChain, 1, B, L, H, cap).total;
         case Path::Step: return newton_ws(kCfgGruStep, 1, B, L, H, cap).total;
         default: return kMinWs;
     }
 }
 size_t lstm_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
-    return lstm_path(cap) == Path::Chain ? chain_ws(kCfgLstmChain, 2, B, L, H, cap).total
-                                         : newton_ws(kCfgLstmStep, 2, B, L, H, cap).total;
+    if (lstm_path(cap) == Path::Step) return newton_ws(kCfgLstmStep, 2, B, L, H, cap).total;
+    if (lstm_chain_owns_chains(B, L, H, env_chain_local("PARARNN_LSTM_PATH"))) return kMinWs;
+    return chain_ws(kCfgLstmChain, 2, B, L, H, cap).total;
 }
 
 }  // namespace
@@ -139,18 +143,18 @@ int rnn_linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const floa
     if (!dims_ok(B, L, H) || !a || !b || !h || !ws) return PARARNN_ERR_INVALID;
     if (!grid_ok(scan_shape(kCfgLinDiag, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
     if (ws_bytes < scan_ws(kCfgLinDiag, 1, B, L, H).total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
-    return status_of(linscan_diag(B, L, H, a, b, h0, h, static_cast<char *>(ws),
+    return status_of(linscan_diag(B, L, H, a, b, h0, h, Ws{static_cast<char *>(ws), ws_bytes},
                                   static_cast<hipStream_t>(stream)));
 }
 
 int rnn_linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const float *b,
                      const float *h0, float *h, void *ws, size_t ws_bytes, void *stream) {
     if (!dims_ok(B, L, H) || !A || !b || !h || !ws) return PARARNN_ERR_INVALID;
-    if (!aligned(A, 16) || !aligned(b, 8) || !aligned(h, 8) || (h0 && !aligned(h0, 8)))
+    if (!aligned(A, 4) || !aligned(b, 4) || !aligned(h, 4) || (h0 && !aligned(h0, 4)))
         return PARARNN_ERR_INVALID;
     if (!grid_ok(scan_shape(kCfgLinBlk2, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
     if (ws_bytes < scan_ws(kCfgLinBlk2, 2, B, L, H).total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
-    return status_of(linscan_blk2(B, L, H, A, b, h0, h, static_cast<char *>(ws),
+    return status_of(linscan_blk2(B, L, H, A, b, h0, h, Ws{static_cast<char *>(ws), ws_bytes},
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -160,11 +164,11 @@ int rnn_linscan_blk(int32_t k, int64_t B, int64_t L, int64_t H, const float *A, 
     if (k < 1) return PARARNN_ERR_INVALID;
     if (k != 4) return PARARNN_ERR_UNSUPPORTED;
     if (!dims_ok(B, L, H) || !A || !b || !h || !ws) return PARARNN_ERR_INVALID;
-    if (!aligned(A, 16) || !aligned(b, 16) || !aligned(h, 16) || (h0 && !aligned(h0, 16)))
+    if (!aligned(A, 4) || !aligned(b, 4) || !aligned(h, 4) || (h0 && !aligned(h0, 4)))
         return PARARNN_ERR_INVALID;
     if (!grid_ok(scan_shape(kCfgLinBlk4, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
     if (ws_bytes < scan_ws(kCfgLinBlk4, 4, B, L, H).total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
-    return status_of(linscan_blk(4, B, L, H, A, b, h0, h, static_cast<char *>(ws),
+    return status_of(linscan_blk(4, B, L, H, A, b, h0, h, Ws{static_cast<char *>(ws), ws_bytes},
                                  static_cast<hipStream_t>(stream)));
 }
 
@@ -189,9 +193,10 @@ int pararnn_gru_forward(int64_t B, int64_t L, int64_t H, const float *pz, const 
         const int st = clear_trace_tail(trace, cap, max_iter, s);
         if (st != PARARNN_OK) return st;
     }
+    const Ws w{static_cast<char *>(ws), ws_bytes};
     if (path == Path::Fused) return status_of(gru_forward_fused(a, s));
-    if (path == Path::Chain) return status_of(gru_forward_chain(a, static_cast<char *>(ws), s));
-    return status_of(gru_forward_step(a, static_cast<char *>(ws), s));
+    if (path == Path::Chain) return status_of(gru_forward_chain(a, w, s));
+    return status_of(gru_forward_step(a, w, s));
 }
 
 int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H, const float *pi, const float *pf,
@@ -213,8 +218,9 @@ int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H, const float *pi, const
         const int st = clear_trace_tail(trace, cap, max_iter, s);
         if (st != PARARNN_OK) return st;
     }
-    if (chain) return status_of(lstm_forward_chain(a, static_cast<char *>(ws), s));
-    return status_of(lstm_forward_step(a, static_cast<char *>(ws), s));
+    const Ws w{static_cast<char *>(ws), ws_bytes};
+    if (chain) return status_of(lstm_forward_chain(a, w, s));
+    return status_of(lstm_forward_step(a, w, s));
 }
 
 int pararnn_gru_sequential(int64_t B, int64_t L, int64_t H, const float *pz, const float *pr,
@@ -270,7 +276,7 @@ int pararnn_adjoint_backward(int32_t cell, int64_t B, int64_t L, int64_t H, cons
         if (grad_c || grad_c0) return PARARNN_ERR_INVALID;
         if (!grid_ok(scan_shape(kCfgGruAdj, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
         if (ws_bytes < gru_adjoint_ws(B, L, H) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
-        return status_of(gru_adjoint(a, static_cast<char *>(ws), s));
+        return status_of(gru_adjoint(a, Ws{static_cast<char *>(ws), ws_bytes}, s));
     }
     if (!c) return PARARNN_ERR_INVALID;
     a.c0 = c0;
@@ -279,7 +285,7 @@ int pararnn_adjoint_backward(int32_t cell, int64_t B, int64_t L, int64_t H, cons
     a.gc0 = grad_c0;
     if (!grid_ok(scan_shape(kCfgLstmAdj, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
     if (ws_bytes < lstm_adjoint_ws(B, L, H) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
-    return status_of(lstm_adjoint(a, static_cast<char *>(ws), s));
+    return status_of(lstm_adjoint(a, Ws{static_cast<char *>(ws), ws_bytes}, s));
 }
 
 }  // extern "C"

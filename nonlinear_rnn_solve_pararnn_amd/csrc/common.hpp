@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "plan.hpp"
+#include "tags.hpp"
 
 namespace prn {
 
@@ -176,18 +177,9 @@ template <> struct MonoidT<2> {
 //   inc : the state after the chunk, i.e. the inclusive prefix applied to the
 //         initial state (S components)
 //
-// Launch tags are signalling-NaN bit patterns (exponent all ones, quiet bit
-// clear, non-zero mantissa; both signs), which arithmetic never produces, so
-// a float that another entry point left in the same workspace cannot look
-// like a tag.  Consecutive launches on one workspace get consecutive epochs;
-// tags repeat only after kTagPeriod launches.
-constexpr uint32_t kTagHalf = 0x3fffffu;
-constexpr uint32_t kTagPeriod = 2u * kTagHalf;
-__device__ __forceinline__ uint32_t launch_tag(uint32_t epoch) {
-    const uint32_t e = epoch % kTagPeriod;
-    return e < kTagHalf ? 0x7f800001u + e : 0xff800001u + (e - kTagHalf);
-}
-
+// Launch tags and the epochs that number the launches on one workspace are
+// defined in tags.hpp: no two launches of one period share a tag, and the
+// last launch of a period clears the workspace (finish_launch below).
 __device__ __forceinline__ uint64_t tagged(float x, uint32_t tag) {
     return (uint64_t)__float_as_uint(x) | ((uint64_t)tag << 32);
 }
@@ -314,20 +306,83 @@ template <> struct Desc<2> {
     }
 };
 
-// Ticket header of a workspace (its first 8 bytes): tickets drawn in the
-// current launch in the low half, the launch epoch in the high half.  The
-// workgroup that draws a launch's last ticket resets the count and advances
-// the epoch, so the next launch on the stream finds the header ready; a
-// zero-filled workspace is ready for its first launch.
+// Ticket header of a workspace (its first two words, tags.hpp): tickets
+// drawn in the current launch and the launch epoch, then the count of
+// finished workgroups of the last launch of a period.  The workgroup that
+// draws a launch's last ticket resets the count and advances the epoch, so
+// the next launch on the stream finds the header ready; a zero-filled
+// workspace is ready for its first launch.  Every draw of one launch sees
+// the same epoch.
 struct Ticket {
     uint32_t index, tag;
+    bool wrap;  // this launch uses the last tag of the period
 };
-__device__ __forceinline__ Ticket draw_ticket(uint64_t *hdr, uint32_t ntiles) {
+__device__ __forceinline__ Ticket draw_ticket(uint64_t *hdr, uint32_t draws) {
     const uint64_t old = __hip_atomic_fetch_add(hdr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t idx = (uint32_t)old, epoch = (uint32_t)(old >> 32);
-    if (idx == ntiles - 1)
-        __hip_atomic_store(hdr, (uint64_t)(epoch + 1u) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return {idx, launch_tag(epoch)};
+    uint32_t idx = (uint32_t)old, epoch = (uint32_t)(old >> 32);
+    if (epoch >= kTagPeriod) epoch = kTagPeriod - 1u;  // only a header the library did not write
+    if (idx + 1u == draws)
+        __hip_atomic_store(hdr, header_after_draw(idx, epoch, draws), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return {idx, launch_tag(epoch), is_wrap_launch(epoch)};
+}
+
+// Where a launch's caller workspace is and what it must keep.  At the end of
+// the last launch of a period (Ticket::wrap) the workgroup that finishes last
+// zeroes every word past the header except [keep_lo, keep_hi): state that a
+// later launch of the same call reads (the per-iteration path's max|delta|
+// slots and boundary states, the adjoint's dL/du partials), which holds no
+// tagged words.
+struct WsSpan {
+    uint64_t *hdr;
+    uint64_t words;            // 64-bit words of the caller's whole buffer
+    uint64_t keep_lo, keep_hi;
+};
+
+// Zero words [lo, hi) of w (w 16-byte aligned) with every thread of the
+// workgroup: an odd word at either end alone, 16-byte stores in between.
+__device__ __forceinline__ void clear_words(uint64_t *w, uint64_t lo, uint64_t hi) {
+    if (lo >= hi) return;
+    if (lo & 1) {
+        if (threadIdx.x == 0) w[lo] = 0;
+        ++lo;
+    }
+    if (hi > lo && (hi & 1)) {
+        if (threadIdx.x == 0) w[hi - 1] = 0;
+        --hi;
+    }
+    uint4 *v = reinterpret_cast<uint4 *>(w + lo);
+    for (uint64_t i = threadIdx.x; i < (hi - lo) / 2; i += blockDim.x) v[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Called by every thread of every workgroup of a launch that draws tickets,
+// after the workgroup's last draw and last access to records; `t` is any of
+// its tickets.  Outside the last launch of a period it does nothing.  In that
+// launch every workgroup counts itself out (its record stores released
+// first), and the one that finishes last clears the workspace; the next
+// launch on the stream starts after it.  No workgroup waits for another.
+// The wrap step is a call, not inlined: its loops would otherwise raise the
+// register count of every kernel that ends with it.
+__device__ __noinline__ void finish_wrap_launch(const WsSpan ws) {
+    __shared__ int s_last;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this thread's record stores first
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint64_t before =
+            __hip_atomic_fetch_add(ws.hdr + 1, 1ull, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = before + 1 == (uint64_t)gridDim.x ? 1 : 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const ClearRanges r = clear_ranges(ws.words, ws.keep_lo, ws.keep_hi);
+    clear_words(ws.hdr, r.lo0, r.hi0);
+    clear_words(ws.hdr, r.lo1, r.hi1);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(ws.hdr + 1, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void finish_launch(const Ticket &t, const WsSpan &ws) {
+    if (t.wrap) finish_wrap_launch(ws);  // the same for every workgroup of the launch
 }
 
 // Bound on the polls of one unpublished descriptor.  Every predecessor of a

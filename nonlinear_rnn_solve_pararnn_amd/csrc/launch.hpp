@@ -21,7 +21,15 @@ struct FillRange {
 };
 constexpr int kMaxFill = 8;
 
-inline bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+inline bool aligned_to(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+inline bool aligned16(const void *p) { return aligned_to(p, 16); }
+
+// The caller's workspace: its base (256-byte aligned) and its whole size in
+// bytes (at the end of a tag period all of it but the header is cleared).
+struct Ws {
+    char *p;
+    size_t bytes;
+};
 
 // Compute units of the current device (queried once per device).
 int device_cu_count();
@@ -32,12 +40,12 @@ int blocks_per_cu(const void *kernel, int threads);
 hipError_t fill(const FillRange *r, int n, hipStream_t s);
 
 hipError_t linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const float *b,
-                        const float *h0, float *h, char *ws, hipStream_t s);
+                        const float *h0, float *h, const Ws &ws, hipStream_t s);
 hipError_t linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const float *b,
-                        const float *h0, float *h, char *ws, hipStream_t s);
+                        const float *h0, float *h, const Ws &ws, hipStream_t s);
 // k x k blocks, k = 4 (hipErrorInvalidValue otherwise)
 hipError_t linscan_blk(int k, int64_t B, int64_t L, int64_t H, const float *A, const float *b,
-                       const float *h0, float *h, char *ws, hipStream_t s);
+                       const float *h0, float *h, const Ws &ws, hipStream_t s);
 
 struct GruFwdArgs {
     int64_t B, L, H;
@@ -49,9 +57,9 @@ struct GruFwdArgs {
     float *trace;
     int local;  // chained kernel: 1 workgroups own whole chains, 0 never, -1 choose
 };
-hipError_t gru_forward_step(const GruFwdArgs &a, char *ws, hipStream_t s);
+hipError_t gru_forward_step(const GruFwdArgs &a, const Ws &ws, hipStream_t s);
 hipError_t gru_forward_fused(const GruFwdArgs &a, hipStream_t s);
-hipError_t gru_forward_chain(const GruFwdArgs &a, char *ws, hipStream_t s);
+hipError_t gru_forward_chain(const GruFwdArgs &a, const Ws &ws, hipStream_t s);
 
 struct LstmFwdArgs {
     int64_t B, L, H;
@@ -63,8 +71,14 @@ struct LstmFwdArgs {
     float *trace;
     int local;  // as for the GRU
 };
-hipError_t lstm_forward_step(const LstmFwdArgs &a, char *ws, hipStream_t s);
-hipError_t lstm_forward_chain(const LstmFwdArgs &a, char *ws, hipStream_t s);
+hipError_t lstm_forward_step(const LstmFwdArgs &a, const Ws &ws, hipStream_t s);
+hipError_t lstm_forward_chain(const LstmFwdArgs &a, const Ws &ws, hipStream_t s);
+
+// Whether the chained Newton forward at this shape lets each workgroup own
+// whole chains of chunks (no workspace beyond the header) rather than
+// chaining chunks across workgroups; local as in GruFwdArgs.
+bool gru_chain_owns_chains(int64_t B, int64_t L, int64_t H, int local);
+bool lstm_chain_owns_chains(int64_t B, int64_t L, int64_t H, int local);
 
 // Sequential application (one thread per channel; tol, cap, info, trace and
 // local unused).
@@ -78,8 +92,8 @@ struct AdjArgs {
     float *gp[4], *gu[4];
     float *gh0, *gc0;
 };
-hipError_t gru_adjoint(const AdjArgs &a, char *ws, hipStream_t s);
-hipError_t lstm_adjoint(const AdjArgs &a, char *ws, hipStream_t s);
+hipError_t gru_adjoint(const AdjArgs &a, const Ws &ws, hipStream_t s);
+hipError_t lstm_adjoint(const AdjArgs &a, const Ws &ws, hipStream_t s);
 
 size_t gru_adjoint_ws(int64_t B, int64_t L, int64_t H);
 size_t lstm_adjoint_ws(int64_t B, int64_t L, int64_t H);

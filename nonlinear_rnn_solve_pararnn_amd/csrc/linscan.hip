@@ -168,7 +168,7 @@ __device__ __forceinline__ bool diag_pf_tile(const LinDiagOp &op, const ScanGeo 
     Aff1 acc = M::id();
 #pragma unroll
     for (int i = 0; i < C; ++i) acc = M::then(acc, Aff1{ea[i], eb[i]});
-    if (tid == 0) *s_next = draw_ticket(g.hdr, draws);
+    if (tid == 0) *s_next = draw_ticket(g.ws.hdr, draws);
     s_part[w * 64 + lane] = acc;
     lds_barrier();
     tn = *s_next;
@@ -221,19 +221,23 @@ __global__ __launch_bounds__(NW * 64) void diag_pf_kernel(LinDiagOp op, ScanGeo 
     __shared__ float s_carry[64 * NWC];
     __shared__ Ticket s_tk[2];
     const uint32_t draws = (uint32_t)(g.ntiles + gridDim.x);  // one draw past the end per workgroup
-    if (threadIdx.x == 0) s_tk[0] = draw_ticket(g.hdr, draws);
+    if (threadIdx.x == 0) s_tk[0] = draw_ticket(g.ws.hdr, draws);
     __syncthreads();
     Ticket tx = s_tk[0], ty;
-    if (tx.index >= g.ntiles) return;
+    if (tx.index >= g.ntiles) {
+        finish_launch(tx, g.ws);
+        return;
+    }
     DiagTilePos px = diag_tile_pos<NW, C, NWC>(g, tx.index), py;
     float xa[C], xb[C], ya[C], yb[C];
     diag_tile_load<C>(op, px, xa, xb);
     for (;;) {
         if (!diag_pf_tile<NW, C, NWC>(op, g, draws, px, tx.tag, xa, xb, &s_tk[1], s_part, s_carry, py, ya, yb, ty))
-            return;
+            break;
         if (!diag_pf_tile<NW, C, NWC>(op, g, draws, py, ty.tag, ya, yb, &s_tk[0], s_part, s_carry, px, xa, xb, tx))
-            return;
+            break;
     }
+    finish_launch(tx, g.ws);  // every draw of a launch carries the same epoch
 }
 
 template <int NW, int C, int NWC>
@@ -246,7 +250,11 @@ static hipError_t launch_diag_pf(const LinDiagOp &op, const ScanGeo &g, hipStrea
 }
 
 // ---------------------------------------------------------------- 2x2 scan
-// h_t = A_t h_{t-1} + b_t with A_t a 2x2 block per (batch, channel).
+// h_t = A_t h_{t-1} + b_t with A_t a 2x2 block per (batch, channel).  VEC:
+// A 16-byte aligned, b, h and h0 8-byte aligned, so a block moves as one
+// 16-byte access and a pair as one 8-byte access; otherwise every float is
+// moved alone (any 4-byte aligned tensors).
+template <bool VEC>
 struct LinBlk2Op {
     static constexpr int S = 2;
     const float *A, *b, *h0;
@@ -259,33 +267,46 @@ struct LinBlk2Op {
     __device__ bool active() const { return true; }
     __device__ float2s init_state(const TilePos &tp) const {
         if (h0 != nullptr && tp.ok) {
-            const float2 v = reinterpret_cast<const float2 *>(h0)[tp.b * H + tp.j];
-            return {v.x, v.y};
+            const int64_t e = tp.b * H + tp.j;
+            if (VEC) {
+                const float2 v = reinterpret_cast<const float2 *>(h0)[e];
+                return {v.x, v.y};
+            }
+            return {h0[2 * e], h0[2 * e + 1]};
         }
         return {0.0f, 0.0f};
+    }
+    __device__ void load_elem(int64_t e, Aff2 &m) const {
+        if (VEC) {
+            const float4 a = ld_once(reinterpret_cast<const float4 *>(A) + e);
+            const float2 v = ld_once(reinterpret_cast<const float2 *>(b) + e);
+            m = {a.x, a.y, a.z, a.w, v.x, v.y};
+        } else {
+            m = {ld_once(A + 4 * e), ld_once(A + 4 * e + 1), ld_once(A + 4 * e + 2), ld_once(A + 4 * e + 3),
+                 ld_once(b + 2 * e), ld_once(b + 2 * e + 1)};
+        }
+    }
+    __device__ void store_state(int64_t e, float2s x) const {
+        if (VEC) {
+            reinterpret_cast<float2 *>(h)[e] = make_float2(x.x, x.y);
+        } else {
+            h[2 * e] = x.x;
+            h[2 * e + 1] = x.y;
+        }
     }
     template <int C>
     __device__ Aff2 phase1(const TilePos &tp, Elem (&e)[C]) const {
         const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
-        const float4 *A4 = reinterpret_cast<const float4 *>(A);
-        const float2 *b2 = reinterpret_cast<const float2 *>(b);
         if (tp.ok && tp.pos0 + C <= L) {  // every position inside: no test per position
 #pragma unroll
-            for (int i = 0; i < C; ++i) {
-                const float4 m = ld_once(A4 + base + i * H);
-                const float2 v = ld_once(b2 + base + i * H);
-                e[i].m = {m.x, m.y, m.z, m.w, v.x, v.y};
-            }
+            for (int i = 0; i < C; ++i) load_elem(base + i * H, e[i].m);
         } else {
 #pragma unroll
             for (int i = 0; i < C; ++i) {
-                if (tp.ok && tp.pos0 + i < L) {
-                    const float4 m = ld_once(A4 + base + i * H);
-                    const float2 v = ld_once(b2 + base + i * H);
-                    e[i].m = {m.x, m.y, m.z, m.w, v.x, v.y};
-                } else {
+                if (tp.ok && tp.pos0 + i < L)
+                    load_elem(base + i * H, e[i].m);
+                else
                     e[i].m = MonoidT<2>::id();
-                }
             }
         }
         Aff2 acc = MonoidT<2>::id();
@@ -296,18 +317,17 @@ struct LinBlk2Op {
     template <int C, int NW, bool CL>
     __device__ void phase2(const TilePos &tp, Elem (&e)[C], float2s x) const {
         const int64_t base = idx3(tp.b, tp.pos0, tp.j, L, H);
-        float2 *h2 = reinterpret_cast<float2 *>(h);
         if (tp.ok && tp.pos0 + C <= L) {
 #pragma unroll
             for (int i = 0; i < C; ++i) {
                 x = MonoidT<2>::apply(e[i].m, x);
-                h2[base + i * H] = make_float2(x.x, x.y);
+                store_state(base + i * H, x);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < C; ++i) {
                 x = MonoidT<2>::apply(e[i].m, x);
-                if (tp.ok && tp.pos0 + i < L) h2[base + i * H] = make_float2(x.x, x.y);
+                if (tp.ok && tp.pos0 + i < L) store_state(base + i * H, x);
             }
         }
     }
@@ -317,10 +337,11 @@ struct LinBlk2Op {
 // h_t = A_t h_{t-1} + b_t with A_t a dense k x k block per (batch, channel):
 // the 2x2 case widened to the small dense blocks that dense Jacobians per
 // head give (ParaRNN page, Fig. 2 caption: block bi-diagonal systems; DEER
-// summary page, limitations: dense Jacobians).  Every block row and state
-// moves as whole 16-byte pieces.  Instantiated for k = 4: one thread holds
-// k*k + k floats per position, so at k = 8 this layout spills.
-template <int K>
+// summary page, limitations: dense Jacobians).  VEC: every tensor 16-byte
+// aligned, so block rows and states move as whole 16-byte pieces; otherwise
+// every float is moved alone.  Instantiated for k = 4: one thread holds
+// k*k + k floats per position.
+template <int K, bool VEC>
 struct LinBlkOp {
     static_assert(K % 4 == 0, "blocks move as float4s");
     static constexpr int S = K;
@@ -334,13 +355,18 @@ struct LinBlkOp {
     };
     __device__ bool active() const { return true; }
     __device__ static void load_vec(const float *p, float *v) {
+        if (VEC) {
 #pragma unroll
-        for (int q = 0; q < K / 4; ++q) {
-            const float4 x = reinterpret_cast<const float4 *>(p)[q];
-            v[4 * q] = x.x;
-            v[4 * q + 1] = x.y;
-            v[4 * q + 2] = x.z;
-            v[4 * q + 3] = x.w;
+            for (int q = 0; q < K / 4; ++q) {
+                const float4 x = reinterpret_cast<const float4 *>(p)[q];
+                v[4 * q] = x.x;
+                v[4 * q + 1] = x.y;
+                v[4 * q + 2] = x.z;
+                v[4 * q + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < K; ++q) v[q] = p[q];
         }
     }
     __device__ VecK<K> init_state(const TilePos &tp) const {
@@ -353,23 +379,30 @@ struct LinBlkOp {
     // loads there (the streamed hint took 322 us against 264 us at B=16,
     // L=2048, H=256); the offsets are streamed.
     __device__ void load_elem(int64_t e, AffK<K> &m) const {
-        const float4 *a4 = reinterpret_cast<const float4 *>(A) + e * (K * K / 4);
+        if (VEC) {
+            const float4 *a4 = reinterpret_cast<const float4 *>(A) + e * (K * K / 4);
 #pragma unroll
-        for (int q = 0; q < K * K / 4; ++q) {
-            const float4 x = a4[q];
-            m.a[4 * q] = x.x;
-            m.a[4 * q + 1] = x.y;
-            m.a[4 * q + 2] = x.z;
-            m.a[4 * q + 3] = x.w;
-        }
-        const float4 *b4 = reinterpret_cast<const float4 *>(b) + e * (K / 4);
+            for (int q = 0; q < K * K / 4; ++q) {
+                const float4 x = a4[q];
+                m.a[4 * q] = x.x;
+                m.a[4 * q + 1] = x.y;
+                m.a[4 * q + 2] = x.z;
+                m.a[4 * q + 3] = x.w;
+            }
+            const float4 *b4 = reinterpret_cast<const float4 *>(b) + e * (K / 4);
 #pragma unroll
-        for (int q = 0; q < K / 4; ++q) {
-            const float4 x = ld_once(b4 + q);
-            m.b[4 * q] = x.x;
-            m.b[4 * q + 1] = x.y;
-            m.b[4 * q + 2] = x.z;
-            m.b[4 * q + 3] = x.w;
+            for (int q = 0; q < K / 4; ++q) {
+                const float4 x = ld_once(b4 + q);
+                m.b[4 * q] = x.x;
+                m.b[4 * q + 1] = x.y;
+                m.b[4 * q + 2] = x.z;
+                m.b[4 * q + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < K * K; ++q) m.a[q] = A[e * (K * K) + q];
+#pragma unroll
+            for (int q = 0; q < K; ++q) m.b[q] = ld_once(b + e * K + q);
         }
     }
     template <int C>
@@ -393,10 +426,15 @@ struct LinBlkOp {
         return acc;
     }
     __device__ void store_state(int64_t e, const VecK<K> &x) const {
-        float4 *h4 = reinterpret_cast<float4 *>(h) + e * (K / 4);
+        if (VEC) {
+            float4 *h4 = reinterpret_cast<float4 *>(h) + e * (K / 4);
 #pragma unroll
-        for (int q = 0; q < K / 4; ++q)
-            h4[q] = make_float4(x.v[4 * q], x.v[4 * q + 1], x.v[4 * q + 2], x.v[4 * q + 3]);
+            for (int q = 0; q < K / 4; ++q)
+                h4[q] = make_float4(x.v[4 * q], x.v[4 * q + 1], x.v[4 * q + 2], x.v[4 * q + 3]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < K; ++q) h[e * K + q] = x.v[q];
+        }
     }
     template <int C, int NW, bool CL>
     __device__ void phase2(const TilePos &tp, Elem (&e)[C], VecK<K> x) const {
@@ -430,7 +468,7 @@ int blocks_per_cu(const void *kernel, int threads) {
 
 template <class Op, int S, int NWC, int CC, int NWT, int CT, int NCW>
 static hipError_t run_scan(const TileCfg &cfg, const Op &op, int64_t B, int64_t L, int64_t H,
-                           char *ws, hipStream_t s) {
+                           const Ws &ws, hipStream_t s) {
     const ScanWs w = scan_ws(cfg, S, B, L, H);
     ScanGeo g;
     g.B = B;
@@ -439,16 +477,16 @@ static hipError_t run_scan(const TileCfg &cfg, const Op &op, int64_t B, int64_t 
     g.ncb = w.sh.ncb;
     g.nq = w.sh.nq;
     g.ntiles = w.sh.ntiles;
-    g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
-    g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
-    g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
+    g.ws = ws_span(ws);
+    g.agg = reinterpret_cast<uint64_t *>(ws.p + w.agg);
+    g.inc = reinterpret_cast<uint64_t *>(ws.p + w.inc);
     return w.sh.channel_lanes ? launch_chunk_scan<Op, NWC, CC, true, NCW>(op, g, s)
                               : launch_chunk_scan<Op, NWT, CT, false>(op, g, s);
 }
 
 
 hipError_t linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const float *b,
-                        const float *h0, float *h, char *ws, hipStream_t s) {
+                        const float *h0, float *h, const Ws &ws, hipStream_t s) {
     LinDiagOp op{a, b, h0, h, L, H};
     constexpr TileCfg c = kCfgLinDiag;
     if (kDiagPrefetch && H >= kChannelLanesMinH) {
@@ -460,27 +498,37 @@ hipError_t linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const f
         g.ncb = w.sh.ncb;
         g.nq = w.sh.nq;
         g.ntiles = w.sh.ntiles;
-        g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
-        g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
-        g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
+        g.ws = ws_span(ws);
+        g.agg = reinterpret_cast<uint64_t *>(ws.p + w.agg);
+        g.inc = reinterpret_cast<uint64_t *>(ws.p + w.inc);
         return launch_diag_pf<c.nw_cl, c.c_cl, c.ncw_cl>(op, g, s);
     }
     return run_scan<LinDiagOp, 1, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
 }
 
 hipError_t linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const float *b,
-                        const float *h0, float *h, char *ws, hipStream_t s) {
-    LinBlk2Op op{A, b, h0, h, L, H};
+                        const float *h0, float *h, const Ws &ws, hipStream_t s) {
     constexpr TileCfg c = kCfgLinBlk2;
-    return run_scan<LinBlk2Op, 2, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
+    const bool vec = aligned16(A) && aligned_to(b, 8) && aligned_to(h, 8) && (h0 == nullptr || aligned_to(h0, 8));
+    if (vec) {
+        LinBlk2Op<true> op{A, b, h0, h, L, H};
+        return run_scan<LinBlk2Op<true>, 2, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
+    }
+    LinBlk2Op<false> op{A, b, h0, h, L, H};
+    return run_scan<LinBlk2Op<false>, 2, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
 }
 
 hipError_t linscan_blk(int k, int64_t B, int64_t L, int64_t H, const float *A, const float *b,
-                       const float *h0, float *h, char *ws, hipStream_t s) {
+                       const float *h0, float *h, const Ws &ws, hipStream_t s) {
     if (k == 4) {
-        LinBlkOp<4> op{A, b, h0, h, L, H};
         constexpr TileCfg c = kCfgLinBlk4;
-        return run_scan<LinBlkOp<4>, 4, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
+        const bool vec = aligned16(A) && aligned16(b) && aligned16(h) && (h0 == nullptr || aligned16(h0));
+        if (vec) {
+            LinBlkOp<4, true> op{A, b, h0, h, L, H};
+            return run_scan<LinBlkOp<4, true>, 4, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
+        }
+        LinBlkOp<4, false> op{A, b, h0, h, L, H};
+        return run_scan<LinBlkOp<4, false>, 4, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
     }
     return hipErrorInvalidValue;
 }

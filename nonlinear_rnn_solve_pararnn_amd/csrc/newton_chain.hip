@@ -42,7 +42,7 @@ struct ChainGeo {
     int64_t B, L, H, ncb, nq, ntiles, ndesc;
     int32_t cap;
     float tol;
-    uint64_t *hdr;
+    WsSpan ws;                  // the caller's workspace (ticket header first)
     uint64_t *agg, *inc;        // [cap][ndesc][words]: iteration k at slice k-1
     uint64_t *stop;             // [ntiles]: last iteration of the tile (tagged)
     uint64_t *fagg, *finc;      // [cap][ntiles]: converged flag of the tile, and of it and all before it
@@ -610,14 +610,20 @@ __global__ __launch_bounds__(NW * 64, kChainMinWaves) void newton_chain_kernel(C
     const bool persistent = (int64_t)gridDim.x < g.ntiles;
     const uint32_t draws = (uint32_t)(persistent ? g.ntiles + gridDim.x : g.ntiles);
     for (;;) {
-        if (threadIdx.x == 0) s_ticket = draw_ticket(g.hdr, draws);
+        if (threadIdx.x == 0) s_ticket = draw_ticket(g.ws.hdr, draws);
         __syncthreads();
         const Ticket t = s_ticket;
-        if (t.index >= g.ntiles) return;
+        if (t.index >= g.ntiles) {
+            finish_launch(t, g.ws);
+            return;
+        }
         int kprev = 0;
         bool cprev = false;
         chain_tile<Cell, NW, C, CL>(cell, g, t.index, t.tag, kprev, cprev);
-        if (!persistent) return;
+        if (!persistent) {
+            finish_launch(t, g.ws);
+            return;
+        }
         __syncthreads();  // the tile's last reads of shared memory before the next ticket
     }
 }
@@ -665,14 +671,23 @@ static hipError_t launch_chain(const Cell &cell, const ChainGeo &g, hipStream_t 
     return hipGetLastError();
 }
 
-// local: 1 workgroups own whole chains, 0 chunks chained across workgroups,
-// -1 choose (own whole chains when there are as many chains as slots for the
-// kernel that owns them).  lcfg is the tile of that kernel (channel lanes).
+// Whether the chained forward lets workgroups own whole chains: always with
+// local = 1 (and channel lanes), never with local = 0, and with local = -1
+// when there are at least as many chains as workgroup slots for the kernel
+// that owns them.  lcfg is the tile of that kernel (channel lanes).  The
+// workspace query and the dispatch both decide with this function: the
+// whole-chain form uses no workspace beyond the header.
+template <class Cell, int NWL, int CLC>
+static bool owns_chains(const TileCfg &lcfg, int64_t B, int64_t L, int64_t H, int local) {
+    if (H < kChannelLanesMinH || local == 0) return false;
+    if (local > 0) return true;
+    return B * scan_shape(lcfg, B, L, H).ncb >= local_slots<Cell, NWL, CLC>();
+}
+
 template <class Cell, int NWC, int CC, int NWT, int CT, int NWL, int CLC>
 static hipError_t chain_forward(const TileCfg &cfg, const TileCfg &lcfg, const Cell &cell, int64_t B, int64_t L,
                                 int64_t H, int32_t cap, float tol, int32_t *info, float *trace, int local,
-                                char *ws, hipStream_t s) {
-    const ChainWs w = chain_ws(cfg, Cell::S, B, L, H, cap);
+                                const Ws &ws, hipStream_t s) {
     FillRange fr[3] = {
         {info, info ? 1ull : 0ull, 0, 4},                         // iterations = 0
         {info ? info + 1 : nullptr, info ? 1ull : 0ull, 1, 4},    // converged = 1
@@ -684,30 +699,46 @@ static hipError_t chain_forward(const TileCfg &cfg, const TileCfg &lcfg, const C
     g.B = B;
     g.L = L;
     g.H = H;
+    g.cap = cap;
+    g.tol = tol;
+    g.info = info;
+    g.trace = reinterpret_cast<uint32_t *>(trace);
+    g.ws = ws_span(ws);
+    if (owns_chains<Cell, NWL, CLC>(lcfg, B, L, H, local)) {
+        // no records, no tickets: the workspace is not touched
+        const ScanShape ls = scan_shape(lcfg, B, L, H);
+        g.ncb = ls.ncb;
+        g.nq = ls.nq;
+        g.ntiles = ls.ntiles;
+        g.ndesc = ls.ndesc;
+        g.agg = g.inc = g.stop = g.fagg = g.finc = nullptr;
+        return launch_local<Cell, NWL, CLC>(cell, g, s);
+    }
+    const ChainWs w = chain_ws(cfg, Cell::S, B, L, H, cap);
     g.ncb = w.sh.ncb;
     g.nq = w.sh.nq;
     g.ntiles = w.sh.ntiles;
     g.ndesc = w.sh.ndesc;
-    g.cap = cap;
-    g.tol = tol;
-    g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
-    g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
-    g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
-    g.stop = reinterpret_cast<uint64_t *>(ws + w.stop);
-    g.fagg = reinterpret_cast<uint64_t *>(ws + w.fagg);
-    g.finc = reinterpret_cast<uint64_t *>(ws + w.finc);
-    g.info = info;
-    g.trace = reinterpret_cast<uint32_t *>(trace);
+    g.agg = reinterpret_cast<uint64_t *>(ws.p + w.agg);
+    g.inc = reinterpret_cast<uint64_t *>(ws.p + w.inc);
+    g.stop = reinterpret_cast<uint64_t *>(ws.p + w.stop);
+    g.fagg = reinterpret_cast<uint64_t *>(ws.p + w.fagg);
+    g.finc = reinterpret_cast<uint64_t *>(ws.p + w.finc);
     if (!w.sh.channel_lanes) return launch_chain<Cell, NWT, CT, false>(cell, g, s);
-    const ScanShape ls = scan_shape(lcfg, B, L, H);  // 64 channels per tile, like the chained form
-    const bool own = local > 0 || (local < 0 && B * ls.ncb >= local_slots<Cell, NWL, CLC>());
-    if (!own) return launch_chain<Cell, NWC, CC, true>(cell, g, s);
-    g.nq = ls.nq;  // the workgroups owning whole chains use no workspace records
-    g.ntiles = ls.ntiles;
-    return launch_local<Cell, NWL, CLC>(cell, g, s);
+    return launch_chain<Cell, NWC, CC, true>(cell, g, s);
 }
 
-hipError_t gru_forward_chain(const GruFwdArgs &a, char *ws, hipStream_t s) {
+bool gru_chain_owns_chains(int64_t B, int64_t L, int64_t H, int local) {
+    constexpr TileCfg lc = kCfgGruLocal;
+    return owns_chains<GruChain, lc.nw_cl, lc.c_cl>(lc, B, L, H, local);
+}
+
+bool lstm_chain_owns_chains(int64_t B, int64_t L, int64_t H, int local) {
+    constexpr TileCfg lc = kCfgLstmLocal;
+    return owns_chains<LstmChain, lc.nw_cl, lc.c_cl>(lc, B, L, H, local);
+}
+
+hipError_t gru_forward_chain(const GruFwdArgs &a, const Ws &ws, hipStream_t s) {
     GruChain cell;
     cell.pz = a.pz;
     cell.pr = a.pr;
@@ -724,7 +755,7 @@ hipError_t gru_forward_chain(const GruFwdArgs &a, char *ws, hipStream_t s) {
         c, lc, cell, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, a.local, ws, s);
 }
 
-hipError_t lstm_forward_chain(const LstmFwdArgs &a, char *ws, hipStream_t s) {
+hipError_t lstm_forward_chain(const LstmFwdArgs &a, const Ws &ws, hipStream_t s) {
     LstmChain cell;
     cell.pi = a.pi;
     cell.pf = a.pf;

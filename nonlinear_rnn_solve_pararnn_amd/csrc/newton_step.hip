@@ -308,13 +308,13 @@ __global__ void newton_finalize(const uint32_t *maxd, int cap, float tol, int32_
 // bnd_next, maxd)` returns the op of iteration k.
 template <int S, int NWC, int CC, int NWT, int CT, class MakeOp>
 static hipError_t newton_loop(const TileCfg &cfg, int64_t B, int64_t L, int64_t H, int32_t cap,
-                              float tol, int32_t *info, float *trace, char *ws, hipStream_t s,
+                              float tol, int32_t *info, float *trace, const Ws &ws, hipStream_t s,
                               MakeOp make_op) {
     const NewtonWs w = newton_ws(cfg, S, B, L, H, cap);
-    FillRange fr[1] = {{ws + w.maxd, (uint64_t)cap, 0, 4}};
+    FillRange fr[1] = {{ws.p + w.maxd, (uint64_t)cap, 0, 4}};
     hipError_t e = fill(fr, 1, s);
     if (e != hipSuccess) return e;
-    uint32_t *maxd = reinterpret_cast<uint32_t *>(ws + w.maxd);
+    uint32_t *maxd = reinterpret_cast<uint32_t *>(ws.p + w.maxd);
     ScanGeo g;
     g.B = B;
     g.L = L;
@@ -322,12 +322,12 @@ static hipError_t newton_loop(const TileCfg &cfg, int64_t B, int64_t L, int64_t 
     g.ncb = w.sh.ncb;
     g.nq = w.sh.nq;
     g.ntiles = w.sh.ntiles;
-    g.hdr = reinterpret_cast<uint64_t *>(ws + w.hdr);
-    g.agg = reinterpret_cast<uint64_t *>(ws + w.agg);
-    g.inc = reinterpret_cast<uint64_t *>(ws + w.inc);
+    g.ws = ws_span(ws, w.maxd, w.keep_end);  // max|delta| slots and boundary states outlive a launch
+    g.agg = reinterpret_cast<uint64_t *>(ws.p + w.agg);
+    g.inc = reinterpret_cast<uint64_t *>(ws.p + w.inc);
     for (int k = 1; k <= cap; ++k) {
         const int par = k & 1;
-        auto op = make_op(k, ws + w.bnd[par ^ 1], ws + w.bnd[par], maxd);
+        auto op = make_op(k, ws.p + w.bnd[par ^ 1], ws.p + w.bnd[par], maxd);
         e = w.sh.channel_lanes ? launch_chunk_scan<decltype(op), NWC, CC, true>(op, g, s)
                                : launch_chunk_scan<decltype(op), NWT, CT, false>(op, g, s);
         if (e != hipSuccess) return e;
@@ -340,7 +340,7 @@ static hipError_t newton_loop(const TileCfg &cfg, int64_t B, int64_t L, int64_t 
 }
 
 
-hipError_t gru_forward_step(const GruFwdArgs &a, char *ws, hipStream_t s) {
+hipError_t gru_forward_step(const GruFwdArgs &a, const Ws &ws, hipStream_t s) {
     auto make = [&](int k, char *bprev, char *bnext, uint32_t *maxd) {
         GruStepOp op;
         op.pz = a.pz;
@@ -368,7 +368,7 @@ hipError_t gru_forward_step(const GruFwdArgs &a, char *ws, hipStream_t s) {
                                  make);
 }
 
-hipError_t lstm_forward_step(const LstmFwdArgs &a, char *ws, hipStream_t s) {
+hipError_t lstm_forward_step(const LstmFwdArgs &a, const Ws &ws, hipStream_t s) {
     auto make = [&](int k, char *bprev, char *bnext, uint32_t *maxd) {
         LstmStepOp op;
         op.pi = a.pi;

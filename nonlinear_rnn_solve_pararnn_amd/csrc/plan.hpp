@@ -85,7 +85,7 @@ struct Carve {
     }
 };
 
-// Every workspace starts with the 8-byte ticket header (common.hpp), at the
+// Every workspace starts with the 16-byte ticket header (tags.hpp), at the
 // same offset for every entry point, so one zero-filled buffer can serve any
 // sequence of calls.
 
@@ -95,10 +95,13 @@ struct Carve {
 constexpr int desc_agg_words(int S) { return S * S + S; }
 constexpr int desc_inc_words(int S) { return S; }
 
-// Workspace of one scan launch: header and one descriptor set.
+// Workspace of one scan launch: header, the per-tile partial sums of the
+// adjoint's dL/du (read by a later launch of the same call, so the clear at
+// the end of a tag period keeps them: [partial, keep_end)) and one
+// descriptor set.
 struct ScanWs {
     ScanShape sh;
-    size_t hdr, agg, inc, partial, total;
+    size_t hdr, partial, keep_end, agg, inc, total;
 };
 
 inline ScanWs scan_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64_t H,
@@ -106,21 +109,23 @@ inline ScanWs scan_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64_t H
     ScanWs w;
     w.sh = scan_shape(cfg, B, L, H);
     Carve c;
-    w.hdr = c.take(8);
+    w.hdr = c.take(16);
+    w.partial = c.take((size_t)w.sh.ntiles * partial_floats_per_tile * 4);
+    w.keep_end = c.off;
     w.agg = c.take((size_t)w.sh.ndesc * desc_agg_words(S) * 8);
     w.inc = c.take((size_t)w.sh.ndesc * desc_inc_words(S) * 8);
-    w.partial = c.take((size_t)w.sh.ntiles * partial_floats_per_tile * 4);
     w.total = c.off;
     return w;
 }
 
 // Workspace of the per-iteration Newton path: header, a max|delta| slot per
-// iteration, one descriptor set (launch tags tell the launches apart) and
-// two sets of chunk-boundary states (state components `S`), used
-// alternately by consecutive iterations.
+// iteration and two sets of chunk-boundary states (state components `S`),
+// used alternately by consecutive iterations (state that later launches of
+// the call read: [maxd, keep_end)), then one descriptor set (launch tags
+// tell the launches apart).
 struct NewtonWs {
     ScanShape sh;
-    size_t hdr, maxd, agg, inc, bnd[2], total;
+    size_t hdr, maxd, bnd[2], keep_end, agg, inc, total;
 };
 
 inline NewtonWs newton_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64_t H,
@@ -128,11 +133,12 @@ inline NewtonWs newton_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64
     NewtonWs w;
     w.sh = scan_shape(cfg, B, L, H);
     Carve c;
-    w.hdr = c.take(8);
+    w.hdr = c.take(16);
     w.maxd = c.take((size_t)cap * 4);
+    for (int k = 0; k < 2; ++k) w.bnd[k] = c.take((size_t)w.sh.ndesc * S * 4);
+    w.keep_end = c.off;
     w.agg = c.take((size_t)w.sh.ndesc * desc_agg_words(S) * 8);
     w.inc = c.take((size_t)w.sh.ndesc * desc_inc_words(S) * 8);
-    for (int k = 0; k < 2; ++k) w.bnd[k] = c.take((size_t)w.sh.ndesc * S * 4);
     w.total = c.off;
     return w;
 }
@@ -149,7 +155,7 @@ inline ChainWs chain_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64_t
     ChainWs w;
     w.sh = scan_shape(cfg, B, L, H);
     Carve c;
-    w.hdr = c.take(8);
+    w.hdr = c.take(16);
     w.agg = c.take((size_t)cap * w.sh.ndesc * desc_agg_words(S) * 8);
     w.inc = c.take((size_t)cap * w.sh.ndesc * desc_inc_words(S) * 8);
     w.stop = c.take((size_t)w.sh.ntiles * 8);

@@ -34,9 +34,16 @@ struct ScanGeo {
     int64_t ncb;            // channel blocks per batch row (channel lanes: ceil(H/64); time lanes: H)
     int64_t nq;             // chunks along the sequence
     int64_t ntiles;         // workgroups of the launch (= tickets drawn)
-    uint64_t *hdr;          // ticket header of the workspace (common.hpp)
+    WsSpan ws;              // the caller's workspace: ticket header, size, what a wrap clear keeps
     uint64_t *agg, *inc;    // look-back descriptors [nq][B][H] (words per descriptor: Desc<S>)
 };
+
+// The span of a caller's workspace, keeping bytes [keep_lo, keep_hi) at the
+// clear that ends a tag period (common.hpp, finish_launch).
+inline WsSpan ws_span(const Ws &w, size_t keep_lo = 0, size_t keep_hi = 0) {
+    return {reinterpret_cast<uint64_t *>(w.p), (uint64_t)(w.bytes / 8), (uint64_t)(keep_lo / 8),
+            (uint64_t)(keep_hi / 8)};
+}
 
 struct TilePos {
     int64_t tile;           // workgroup ticket: (q * B + b) * ncb + channel block
@@ -371,12 +378,18 @@ __global__ __launch_bounds__(NW * 64) void chunk_scan_kernel(Op op, ScanGeo g) {
     const bool persistent = (int64_t)gridDim.x < g.ntiles;
     const uint32_t draws = (uint32_t)(persistent ? g.ntiles + gridDim.x : g.ntiles);
     for (;;) {
-        if (threadIdx.x == 0) s_ticket = draw_ticket(g.hdr, draws);
+        if (threadIdx.x == 0) s_ticket = draw_ticket(g.ws.hdr, draws);
         __syncthreads();  // scan_tile's own barriers keep the next write after every read
         const Ticket t = s_ticket;
-        if (t.index >= g.ntiles) return;
+        if (t.index >= g.ntiles) {
+            finish_launch(t, g.ws);
+            return;
+        }
         scan_tile<Op, NW, C, CHANNEL_LANES, NWC>(op, g, t.index, t.tag);
-        if (!persistent) return;
+        if (!persistent) {
+            finish_launch(t, g.ws);
+            return;
+        }
     }
 }
 

@@ -1,5 +1,5 @@
 """Writes c0_gru_rollout.txt: the fp64 oracle's sequential GRU rollout of the
-tiny workload (B=1, L=64, H=4, seeded synthetic inputs with a non-zero h0).
+tiny workload (B=1, L=64, H=4, seeded synthetic inputs, h0 = 0).
 
     python tests/golden/make_golden.py
 

@@ -49,16 +49,29 @@ def test_workspace_query(lib, monkeypatch):
     # the fused GRU kernel (L <= 512) needs none beyond the minimum; a forced
     # override is sized for the kernel it forces
     assert api.workspace_bytes(api.OP_GRU_FORWARD, 16, 512, 4096, 32) == 256
-    assert api.workspace_bytes(api.OP_GRU_FORWARD, 16, 513, 4096, 32) > 256
+    # past 512 positions: the chained kernel, here with workgroups owning
+    # whole chains (1024 chains), which keeps no records
+    assert api.workspace_bytes(api.OP_GRU_FORWARD, 16, 513, 4096, 32) == 256
     # grows with the iteration cap: records of every iteration on the chained
     # path (caps up to 64), one max|delta| slot per iteration beyond
     for op in (api.OP_GRU_FORWARD, api.OP_LSTM_FORWARD):
         assert api.workspace_bytes(op, 16, 4096, 64, 60) > api.workspace_bytes(op, 16, 4096, 64, 2)
         assert api.workspace_bytes(op, 16, 4096, 64, 500) > api.workspace_bytes(op, 16, 4096, 64, 100)
+    # the chained kernel's whole-chain form (as many chains as workgroup
+    # slots: the LSTM at B=8, L=2048, H=2048) keeps no records either
+    assert api.workspace_bytes(api.OP_LSTM_FORWARD, 8, 2048, 2048, 32) == 256
+    monkeypatch.setenv("PARARNN_LSTM_PATH", "chain")
+    assert api.workspace_bytes(api.OP_LSTM_FORWARD, 8, 2048, 2048, 32) > 10 ** 8
+    monkeypatch.setenv("PARARNN_LSTM_PATH", "local")
+    assert api.workspace_bytes(api.OP_LSTM_FORWARD, 2, 700, 64, 32) == 256
+    monkeypatch.setenv("PARARNN_GRU_PATH", "local")
+    assert api.workspace_bytes(api.OP_GRU_FORWARD, 2, 700, 64, 32) == 256
+    assert api.workspace_bytes(api.OP_GRU_FORWARD, 2, 70000, 1, 32) > 256  # time lanes: always chained
     monkeypatch.setenv("PARARNN_GRU_PATH", "step")
     assert api.workspace_bytes(api.OP_GRU_FORWARD, 16, 512, 4096, 32) > 256
     monkeypatch.setenv("PARARNN_GRU_PATH", "chain")
     assert api.workspace_bytes(api.OP_GRU_FORWARD, 16, 512, 4096, 32) > 256
+    assert api.workspace_bytes(api.OP_GRU_FORWARD, 16, 513, 4096, 32) > 256
 
 
 def test_invalid_arguments_rejected_on_host(lib):

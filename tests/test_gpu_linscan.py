@@ -246,3 +246,35 @@ def test_linscan_blk_rejects_unsupported_k():
     b = torch.zeros(1, 4, 2, 3, device="cuda")
     with pytest.raises(api.PararnnError):
         api.linscan_blk(A, b)
+
+
+# Block scans on tensors whose data start 4, 8 or 12 bytes past a 16-byte
+# boundary (the per-float load path) against aligned ones (16-byte blocks),
+# channel lanes and time lanes, ragged tails in L and in the channel block.
+BLK_VIEW_SHAPES = [(1, 1, 1), (2, 129, 36), (2, 1030, 3), (1, 3000, 70)]
+
+
+@pytest.mark.parametrize("B,L,H", BLK_VIEW_SHAPES)
+@pytest.mark.parametrize("misalign", [0, 1, 2])
+def test_linscan_blk2_aligned_and_offset_views(orc, B, L, H, misalign):
+    say("linscan_blk2 paths", B, L, H, misalign)
+    d = synth.linscan_blk2_inputs(B, L, H, seed=320 + L + H, h0=True)
+    A, b, h0 = dev(d["A"]), dev(d["b"]), dev(d["h0"])
+    out = torch.empty_like(b)
+    if misalign:
+        A, b, h0, out = (_offset(x, misalign) for x in (A, b, h0, out))
+    h = host(api.linscan_blk2(A, b, h0, out=out))
+    assert max_abs(h, orc.linscan_blk2(d["A"], d["b"], d["h0"])) <= FWD_ATOL
+
+
+@pytest.mark.parametrize("B,L,H", BLK_VIEW_SHAPES)
+@pytest.mark.parametrize("misalign", [0, 1, 3])
+def test_linscan_blk4_aligned_and_offset_views(orc, B, L, H, misalign):
+    say("linscan_blk4 paths", B, L, H, misalign)
+    d = synth.linscan_blk_inputs(B, L, H, 4, seed=330 + L + H, h0=True)
+    A, b, h0 = dev(d["A"]), dev(d["b"]), dev(d["h0"])
+    out = torch.empty_like(b)
+    if misalign:
+        A, b, h0, out = (_offset(x, misalign) for x in (A, b, h0, out))
+    h = host(api.linscan_blk(A, b, h0, out=out))
+    assert max_abs(h, orc.linscan_blk(d["A"], d["b"], d["h0"])) <= FWD_ATOL
