@@ -486,8 +486,11 @@ class Workload:
         return [int(x) for x in self.info.cpu().tolist()]
 
 
-# Bytes written between timed reps to evict the MI355X's 256 MB last-level
-# cache (MALL), so that no rep reads inputs the previous one left in it.
+# Bytes read between timed reps to evict the MI355X's 256 MB last-level
+# cache (MALL), so that no rep reads inputs the previous one left in it.  A
+# read, not a write: a 512 MB write leaves the cache full of dirty lines
+# whose write-back then competes with the timed step (the diagonal scan
+# measured 153 us after a write against 130 us back to back).
 EVICT_BYTES = 512 << 20
 
 
@@ -497,9 +500,10 @@ def time_workload(wl, steps, warmup, scratch):
     back to back: K steps bracketed by a device synchronisation on both
       sides, timed by the wall clock and by one HIP event pair on the launch
       stream (the contract's ms per step and value come from the wall clock);
-    cold: before each of K steps a 512 MB scratch write, then the step between
-      its own HIP event pair on the launch stream; the median is the kernel
-      duration the roofline uses."""
+    cold: before each of K steps a 512 MB scratch read (the reduction of a
+      buffer written once beforehand), then the step between its own HIP
+      event pair on the launch stream; the median is the kernel duration the
+      roofline uses."""
     import torch
     for _ in range(warmup):
         wl.step()
@@ -516,7 +520,7 @@ def time_workload(wl, steps, warmup, scratch):
     warm = e0.elapsed_time(e1) / steps
     pairs = []
     for _ in range(steps):
-        scratch.zero_()
+        scratch.sum()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         wl.step()
@@ -592,6 +596,11 @@ def cpu_baseline(name, host, budget_s=10.0, single_s=4.0):
     return out
 
 
+# Newton workloads whose entry also carries the oracle timed on this host
+# (a bounded sample: repetitions of the full workload for a few seconds).
+CPU_BASELINE_OF = ("c2_gru_fused", "c3_lstm", "c4_gru_long_fwd_adj")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -602,8 +611,10 @@ def main():
     ap.add_argument("--only", action="store_true",
                     help="measure only the chosen workload (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-modalities", action="store_true",
+                    help="leave out the modality sweep and residual traces")
     ap.add_argument("--modalities", action="store_true",
-                    help="only the modality comparison and residual traces (one JSON line)")
+                    help="only the modality sweep and residual traces (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -619,7 +630,7 @@ def main():
     dev = torch.device("cuda:0")
 
     if args.modalities:
-        print(json.dumps(modalities(dev, args.steps, args.warmup)), flush=True)
+        print(json.dumps(modalities(dev)), flush=True)
         return
 
     if args.copy_calibration:
@@ -632,6 +643,7 @@ def main():
         log("copy calibration: %d launches of a %d-byte device copy" % (args.warmup + args.steps, 4 * n))
         return
 
+    scratch = torch.zeros(EVICT_BYTES // 4, dtype=torch.float32, device=dev)
     names = [args.workload] if args.only else \
         [args.workload] + [n for n in ALG_BYTES if n != args.workload]
     results = {}
@@ -641,18 +653,23 @@ def main():
         iters = wl.iterations() if name in ("c2_gru_fused", "c3_lstm", "c4_gru_long_fwd_adj",
                                             "x_lstm_step", "x_gru_long_step",
                                             "x_gru_long_fwd") else None
-        wall_ms, ev_ms = time_workload(wl, args.steps, args.warmup)
+        t = time_workload(wl, args.steps, args.warmup, scratch)
+        kernel_ms = t["cold_median_ms"]
         results[name] = {
             "elements": wl.elements,
-            "elements_per_s": wl.elements / (wall_ms * 1e-3),
-            "ms_per_step": wall_ms,
-            "event_ms_per_step": ev_ms,
+            "elements_per_s": wl.elements / (t["wall_ms"] * 1e-3),
+            "ms_per_step": t["wall_ms"],
+            "event_ms_per_step": kernel_ms,
+            "timing": t,
             "newton_iterations": iters,
             "describe": DESCRIBE[name],
-            "roofline": roofline(name, wl.elements, ev_ms),
+            "roofline": roofline(name, wl.elements, kernel_ms),
         }
         if name in ALU_SLOTS_PER_ELEMENT_ITER and iters:
-            results[name]["roofline_alu"] = alu_roofline(name, wl.elements, iters[0], ev_ms)
+            results[name]["roofline_alu"] = alu_roofline(name, wl.elements, iters[0], kernel_ms)
+        if name != args.workload and name in CPU_BASELINE_OF and not args.no_cpu_baseline:
+            log("cpu baseline (oracle) for", name)
+            results[name]["cpu_baseline"] = cpu_baseline(name, wl.host, budget_s=5.0, single_s=2.0)
         log(json.dumps({name: results[name]}))
         del wl
         torch.cuda.empty_cache()
@@ -684,7 +701,12 @@ def main():
                    "B": w["B"], "L": w["L"], "H": w["H"], "parallelism": "single GPU"},
         "newton_iterations": head["newton_iterations"],
         "roofline": head["roofline"],
+        "timing": head["timing"],
     }
+    if args.workload == "c1_linscan":
+        out["config"]["note"] = ("a linear recurrence is its own Newton linearisation: one Newton step "
+                                 "(this bi-diagonal solve) is exact; the nonlinear Newton forwards are "
+                                 "under workloads (c2_gru_fused, c3_lstm, c4_gru_long_fwd_adj)")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(args.workload, synth.workload_inputs(args.workload))
@@ -694,6 +716,11 @@ def main():
         out["device_copy"] = device_copy(dev)
     if len(results) > 1:
         out["workloads"] = {k: v for k, v in results.items() if k != args.workload}
+    del scratch
+    torch.cuda.empty_cache()
+    if not args.only and not args.no_modalities:
+        log("modalities and residual traces ...")
+        out["modalities"] = modalities(dev)
     print(json.dumps(out), flush=True)
 
 

@@ -154,6 +154,8 @@ def newton_solve(cell: Callable[..., torch.Tensor], inputs: Sequence[torch.Tenso
     if state_size not in (1, 2):
         raise ValueError("state_size must be 1 or 2")
     x0 = inputs[0]
+    if x0.device.type != "cuda":
+        raise ValueError("newton_solve runs on a HIP device only; inputs are on %s" % x0.device)
     if x0.dim() != 3:
         raise ValueError("inputs must be [B, L, H]")
     if not tol >= 0.0 or max_iter < 1:

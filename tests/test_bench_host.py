@@ -45,3 +45,19 @@ def test_traffic_is_dropped_once_a_source_changes(monkeypatch):
         monkeypatch.setitem(bench.TRAFFIC, name, dict(t, sha256="0" * 16))
         assert bench.measured_traffic(name) is None
     assert bench.measured_traffic("x_lstm_step") is None
+
+
+def test_path_override_is_restored(monkeypatch):
+    """The modality sweep sets PARARNN_*_PATH around each call and puts back
+    whatever the user had set (or nothing)."""
+    monkeypatch.setenv("PARARNN_GRU_PATH", "chain")
+    with bench._env("PARARNN_GRU_PATH", "step"):
+        assert os.environ["PARARNN_GRU_PATH"] == "step"
+    assert os.environ["PARARNN_GRU_PATH"] == "chain"
+    with bench._env("PARARNN_GRU_PATH", None):
+        assert "PARARNN_GRU_PATH" not in os.environ
+    assert os.environ["PARARNN_GRU_PATH"] == "chain"
+    monkeypatch.delenv("PARARNN_LSTM_PATH", raising=False)
+    with bench._env("PARARNN_LSTM_PATH", "step"):
+        assert os.environ["PARARNN_LSTM_PATH"] == "step"
+    assert "PARARNN_LSTM_PATH" not in os.environ
