@@ -63,7 +63,8 @@ enum {
     PARARNN_OK = 0,
     PARARNN_ERR_INVALID = -1,     /* bad pointer, size, tolerance, cap or workspace */
     PARARNN_ERR_HIP = -2,         /* a HIP launch or runtime call failed */
-    PARARNN_ERR_UNSUPPORTED = -3  /* combination not implemented */
+    PARARNN_ERR_UNSUPPORTED = -3, /* combination not implemented */
+    PARARNN_ERR_TOO_LARGE = -4    /* needs more than the library's static scratch buffer */
 };
 
 enum { PARARNN_CELL_GRU = 0, PARARNN_CELL_LSTM = 1 };
@@ -238,6 +239,29 @@ int pararnn_lstm_sequential(int64_t B, int64_t L, int64_t H,
                             const float *pg, const float *ui, const float *uf,
                             const float *uo, const float *ug, const float *h0,
                             const float *c0, float *h, float *c, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the GRU
+ * Newton forward of pararnn_gru_forward, with the same arguments, results
+ * and errors, but no workspace argument.  Its workspace is a static device
+ * array of the library, PARARNN_NOALLOC_SCRATCH_BYTES bytes on each device
+ * it runs on, held until the process ends.  The first call on a device looks
+ * up the array's address (with that device current) and zero-fills it with
+ * one kernel on `stream`; no call allocates or frees anything.  A shape
+ * whose workspace (pararnn_workspace_bytes(PARARNN_OP_GRU_FORWARD, ...))
+ * exceeds the array returns PARARNN_ERR_TOO_LARGE before anything is
+ * enqueued.  Every call on a device shares the one array: calls that overlap
+ * in time on one device (other streams, other threads) race on it and must
+ * not be issued; consecutive calls, in any order of shapes, are fine.
+ * The device is the current one, which must be the device of `stream`.
+ */
+#define PARARNN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int pararnn_gru_forward_noalloc(int64_t B, int64_t L, int64_t H,
+                                const float *pz, const float *pr, const float *pc,
+                                const float *uz, const float *ur, const float *uc,
+                                const float *h0, float *h, float tol, int32_t max_iter,
+                                int32_t *info, float *trace, void *stream);
 
 /* Short text for a status code (static storage). */
 const char *pararnn_status_string(int status);

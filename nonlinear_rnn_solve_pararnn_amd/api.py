@@ -24,7 +24,9 @@ CELL_GRU, CELL_LSTM = 0, 1
 
 EXPORTS = ("pararnn_workspace_bytes", "rnn_linscan_diag", "rnn_linscan_blk2", "rnn_linscan_blk",
            "pararnn_gru_forward", "pararnn_lstm_forward", "pararnn_adjoint_backward",
-           "pararnn_gru_sequential", "pararnn_lstm_sequential", "pararnn_status_string")
+           "pararnn_gru_sequential", "pararnn_lstm_sequential", "pararnn_status_string",
+           "pararnn_gru_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # PARARNN_NOALLOC_SCRATCH_BYTES
 
 _lib = None
 
@@ -66,6 +68,9 @@ def load_library():
     lib.pararnn_gru_sequential.restype = ctypes.c_int
     lib.pararnn_lstm_sequential.argtypes = [i64, i64, i64] + [vp] * 12 + [vp]
     lib.pararnn_lstm_sequential.restype = ctypes.c_int
+    lib.pararnn_gru_forward_noalloc.argtypes = [i64, i64, i64] + [vp] * 8 + [
+        ctypes.c_float, i32, vp, vp, vp]
+    lib.pararnn_gru_forward_noalloc.restype = ctypes.c_int
     lib.pararnn_status_string.argtypes = [ctypes.c_int]
     lib.pararnn_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -255,6 +260,34 @@ def lstm_forward(pi, pf, po, pg, ui, uf, uo, ug, h0=None, c0=None, *, tol=1e-4, 
                                     _ptr(c), float(tol), int(max_iter), _ptr(info), _ptr(trace),
                                     _ptr(ws), n, _stream(dev)), "pararnn_lstm_forward")
     return h, c
+
+
+def gru_forward_noalloc(pz, pr, pc, uz, ur, uc, h0=None, *, tol=1e-4, max_iter=32, out=None,
+                        info=None, trace=None):
+    """gru_forward with the library's static scratch buffer as workspace
+    (pararnn_gru_forward_noalloc): the call allocates nothing on the device
+    when `out` is given."""
+    lib = load_library()
+    B, L, H = pz.shape
+    dev = pz.device
+    for t, n in ((pz, "pz"), (pr, "pr"), (pc, "pc")):
+        _need(t, (B, L, H), n, dev)
+    for t, n in ((uz, "uz"), (ur, "ur"), (uc, "uc")):
+        _need(t, (H,), n, dev)
+    if h0 is not None:
+        _need(h0, (B, H), "h0", dev)
+    h = torch.empty_like(pz) if out is None else out
+    _need(h, (B, L, H), "out", dev)
+    if info is not None and (info.dtype != torch.int32 or info.numel() < 2 or info.device != dev):
+        raise ValueError("info must be an int32 device tensor with 2 elements")
+    if trace is not None and (trace.dtype != torch.float32 or trace.numel() < max_iter or
+                              trace.device != dev):
+        raise ValueError("trace must be a float32 device tensor with max_iter elements")
+    _check(lib.pararnn_gru_forward_noalloc(B, L, H, _ptr(pz), _ptr(pr), _ptr(pc), _ptr(uz), _ptr(ur),
+                                           _ptr(uc), _ptr(h0), _ptr(h), float(tol), int(max_iter),
+                                           _ptr(info), _ptr(trace), _stream(dev)),
+           "pararnn_gru_forward_noalloc")
+    return h
 
 
 # ---------------------------------------------------------------- sequential

@@ -116,6 +116,7 @@ const char *pararnn_status_string(int status) {
         case PARARNN_ERR_INVALID: return "invalid argument";
         case PARARNN_ERR_HIP: return "HIP error";
         case PARARNN_ERR_UNSUPPORTED: return "unsupported";
+        case PARARNN_ERR_TOO_LARGE: return "needs more scratch than the library's static buffer holds";
         default: return "unknown status";
     }
 }
