@@ -371,24 +371,31 @@ __device__ __forceinline__ float2s state_add(float2s a, float2s b) { return {a.x
 // nothing goes through global memory.  Every thread reads the delta entering
 // the chunk from the previous chunk's half itself, while the holder writes
 // this chunk's into the other half, so no barrier is needed between them.
-template <class Cell, int NW, int C, bool CL, bool LOCAL = false>
+// CW (channel lanes): channels per wave row.  With CW = 32 a wave holds two
+// sub-chunks of 32 channels (lanes 0-31 and 32-63), so a chain is 32
+// channels wide (128-byte rows) and a small workgroup still covers a
+// useful chunk; only the whole-chain form takes it.
+template <class Cell, int NW, int C, bool CL, bool LOCAL = false, int CW = 64>
 __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, int64_t ticket, uint32_t tag,
                                            int &kprev, bool &cprev) {
     static_assert(!LOCAL || CL, "workgroups own whole chains only with channel lanes");
+    static_assert(CW == 64 || (CW == 32 && LOCAL), "half-wave channel rows only for the whole-chain form");
+    constexpr int SPW = CL ? 64 / CW : 1;  // sub-chunks per wave (channel lanes)
+    constexpr int NS = NW * SPW;           // sub-chunks per chunk (channel lanes)
     constexpr int S = Cell::S;
     using M = MonoidT<S>;
     using D = Desc<S>;
     using Map = typename M::Map;
     using State = typename M::State;
     constexpr int NT = NW * 64;
-    constexpr int64_t T = CL ? (int64_t)NW * C : (int64_t)NT * C;
+    constexpr int64_t T = CL ? (int64_t)NS * C : (int64_t)NT * C;
 
     __shared__ Map s_part[CL ? NT : NW];
     __shared__ State s_carry[CL ? 64 : 1];
     __shared__ State s_last[CL ? NT : NW];
     __shared__ uint32_t s_wmax[NW];
     __shared__ int s_stop;
-    constexpr int kRecHalf = kChainMaxCap * 64;
+    constexpr int kRecHalf = kChainMaxCap * CW;
     __shared__ State s_rec[LOCAL ? 2 * kRecHalf : 1];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -397,14 +404,15 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
     const int64_t rest = ticket - q * per_q;
     const int64_t b = rest / g.ncb;
     const int64_t cb = rest - b * g.ncb;
-    const int64_t j = CL ? cb * 64 + lane : cb;
-    const int sub = CL ? w : tid;
+    const int ch = lane % CW;  // channel within the chain's block (channel lanes)
+    const int64_t j = CL ? cb * CW + ch : cb;
+    const int sub = CL ? w * SPW + lane / CW : tid;
     const bool ok = j < g.H;
     const int64_t pos0 = q * T + (int64_t)sub * C;
     const int64_t base = idx3(b, pos0, ok ? j : 0, g.L, g.H);
     const int64_t stride = g.B * g.H, slot = b * g.H + j;
     const int64_t dsc = q * stride + slot;
-    const bool holder = CL ? (w == NW - 1) : (tid == NT - 1);
+    const bool holder = CL ? (sub == NS - 1) : (tid == NT - 1);
 
     bool val[C];
 #pragma unroll
@@ -458,7 +466,7 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
             hp = q == 0 ? init : hb;
         } else if (k > 1) {
             if (CL)
-                hp = s_last[(w - 1) * 64 + lane];
+                hp = s_last[(sub - 1) * CW + ch];
             else
                 hp = lane == 0 ? s_last[w - 1] : nb;
         }
@@ -470,18 +478,18 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
         // exclusive prefix of this sub-chunk inside the chunk, and the chunk aggregate
         Map ex, tot;
         if (CL) {
-            s_part[w * 64 + lane] = acc;
+            s_part[sub * CW + ch] = acc;
             lds_barrier();
             // the earlier sub-chunks' maps are all read before any is
             // composed, so their LDS latencies overlap
-            Map pv[NW - 1];
+            Map pv[NS - 1];
 #pragma unroll
-            for (int kk = 0; kk < NW - 1; ++kk)
-                if (kk < w) pv[kk] = s_part[kk * 64 + lane];
+            for (int kk = 0; kk < NS - 1; ++kk)
+                if (kk < sub) pv[kk] = s_part[kk * CW + ch];
             ex = M::id();
 #pragma unroll
-            for (int kk = 0; kk < NW - 1; ++kk)
-                if (kk < w) ex = M::then(ex, pv[kk]);
+            for (int kk = 0; kk < NS - 1; ++kk)
+                if (kk < sub) ex = M::then(ex, pv[kk]);
             tot = M::then(ex, acc);
         } else {
             Map incl = acc;
@@ -505,8 +513,8 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
         if (LOCAL) {
             // the previous chunk's inclusive delta at k (zero once it has
             // stopped); the holder records this chunk's for the next chunk
-            cin = (q > 0 && k <= kprev) ? s_rec[((q - 1) & 1) * kRecHalf + (k - 1) * 64 + lane] : M::zero();
-            if (holder) s_rec[(q & 1) * kRecHalf + (k - 1) * 64 + lane] = M::apply(tot, cin);
+            cin = (q > 0 && k <= kprev) ? s_rec[((q - 1) & 1) * kRecHalf + (k - 1) * CW + ch] : M::zero();
+            if (holder) s_rec[(q & 1) * kRecHalf + (k - 1) * CW + ch] = M::apply(tot, cin);
         } else if (CL) {
             if (holder) {
                 State din = M::zero();
@@ -548,7 +556,7 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
         }
         mx = clamp_nan_to_inf(mx);
         if (CL)
-            s_last[w * 64 + lane] = s[C - 1];
+            s_last[sub * CW + ch] = s[C - 1];
         else if (lane == 63)
             s_last[w] = s[C - 1];
         mx = wave_max_u32(mx);
@@ -634,30 +642,31 @@ __global__ __launch_bounds__(NW * 64, kChainMinWaves) void newton_chain_kernel(C
 // in LDS and no workgroup waits on another.  The iterates equal those of the
 // chained kernel above.  Worth it once there are at least as many chains as
 // workgroup slots on the device.
-template <class Cell, int NW, int C>
+template <class Cell, int NW, int C, int CW>
 __global__ __launch_bounds__(NW * 64, kChainMinWaves) void newton_local_kernel(Cell cell, ChainGeo g) {
     const int64_t nchains = g.B * g.ncb;
     for (int64_t ch = blockIdx.x; ch < nchains; ch += gridDim.x) {
         int kprev = 0;
         bool cprev = false;
         for (int64_t q = 0; q < g.nq; ++q) {
-            chain_tile<Cell, NW, C, true, true>(cell, g, q * nchains + ch, 0u, kprev, cprev);
+            chain_tile<Cell, NW, C, true, true, CW>(cell, g, q * nchains + ch, 0u, kprev, cprev);
             __syncthreads();  // the chunk's last reads of shared memory before the next chunk
         }
     }
 }
 
-template <class Cell, int NW, int C>
+template <class Cell, int NW, int C, int CW>
 static int64_t local_slots() {
-    static const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(newton_local_kernel<Cell, NW, C>), NW * 64);
+    static const int per_cu =
+        blocks_per_cu(reinterpret_cast<const void *>(newton_local_kernel<Cell, NW, C, CW>), NW * 64);
     return (int64_t)per_cu * device_cu_count();
 }
 
-template <class Cell, int NW, int C>
+template <class Cell, int NW, int C, int CW>
 static hipError_t launch_local(const Cell &cell, const ChainGeo &g, hipStream_t s) {
-    const int64_t slots = local_slots<Cell, NW, C>(), nchains = g.B * g.ncb;
+    const int64_t slots = local_slots<Cell, NW, C, CW>(), nchains = g.B * g.ncb;
     const int64_t grid = nchains < slots ? nchains : slots;
-    hipLaunchKernelGGL((newton_local_kernel<Cell, NW, C>), dim3((unsigned)grid), dim3(NW * 64), 0, s, cell, g);
+    hipLaunchKernelGGL((newton_local_kernel<Cell, NW, C, CW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, cell, g);
     return hipGetLastError();
 }
 
@@ -677,14 +686,14 @@ static hipError_t launch_chain(const Cell &cell, const ChainGeo &g, hipStream_t 
 // that owns them.  lcfg is the tile of that kernel (channel lanes).  The
 // workspace query and the dispatch both decide with this function: the
 // whole-chain form uses no workspace beyond the header.
-template <class Cell, int NWL, int CLC>
+template <class Cell, int NWL, int CLC, int CWL>
 static bool owns_chains(const TileCfg &lcfg, int64_t B, int64_t L, int64_t H, int local) {
     if (H < kChannelLanesMinH || local == 0) return false;
     if (local > 0) return true;
-    return B * scan_shape(lcfg, B, L, H).ncb >= local_slots<Cell, NWL, CLC>();
+    return B * scan_shape(lcfg, B, L, H).ncb >= local_slots<Cell, NWL, CLC, CWL>();
 }
 
-template <class Cell, int NWC, int CC, int NWT, int CT, int NWL, int CLC>
+template <class Cell, int NWC, int CC, int NWT, int CT, int NWL, int CLC, int CWL>
 static hipError_t chain_forward(const TileCfg &cfg, const TileCfg &lcfg, const Cell &cell, int64_t B, int64_t L,
                                 int64_t H, int32_t cap, float tol, int32_t *info, float *trace, int local,
                                 const Ws &ws, hipStream_t s) {
@@ -704,7 +713,7 @@ static hipError_t chain_forward(const TileCfg &cfg, const TileCfg &lcfg, const C
     g.info = info;
     g.trace = reinterpret_cast<uint32_t *>(trace);
     g.ws = ws_span(ws);
-    if (owns_chains<Cell, NWL, CLC>(lcfg, B, L, H, local)) {
+    if (owns_chains<Cell, NWL, CLC, CWL>(lcfg, B, L, H, local)) {
         // no records, no tickets: the workspace is not touched
         const ScanShape ls = scan_shape(lcfg, B, L, H);
         g.ncb = ls.ncb;
@@ -712,7 +721,7 @@ static hipError_t chain_forward(const TileCfg &cfg, const TileCfg &lcfg, const C
         g.ntiles = ls.ntiles;
         g.ndesc = ls.ndesc;
         g.agg = g.inc = g.stop = g.fagg = g.finc = nullptr;
-        return launch_local<Cell, NWL, CLC>(cell, g, s);
+        return launch_local<Cell, NWL, CLC, CWL>(cell, g, s);
     }
     const ChainWs w = chain_ws(cfg, Cell::S, B, L, H, cap);
     g.ncb = w.sh.ncb;
@@ -730,12 +739,12 @@ static hipError_t chain_forward(const TileCfg &cfg, const TileCfg &lcfg, const C
 
 bool gru_chain_owns_chains(int64_t B, int64_t L, int64_t H, int local) {
     constexpr TileCfg lc = kCfgGruLocal;
-    return owns_chains<GruChain, lc.nw_cl, lc.c_cl>(lc, B, L, H, local);
+    return owns_chains<GruChain, lc.nw_cl, lc.c_cl, lc.cw_cl>(lc, B, L, H, local);
 }
 
 bool lstm_chain_owns_chains(int64_t B, int64_t L, int64_t H, int local) {
     constexpr TileCfg lc = kCfgLstmLocal;
-    return owns_chains<LstmChain, lc.nw_cl, lc.c_cl>(lc, B, L, H, local);
+    return owns_chains<LstmChain, lc.nw_cl, lc.c_cl, lc.cw_cl>(lc, B, L, H, local);
 }
 
 hipError_t gru_forward_chain(const GruFwdArgs &a, const Ws &ws, hipStream_t s) {
@@ -751,7 +760,7 @@ hipError_t gru_forward_chain(const GruFwdArgs &a, const Ws &ws, hipStream_t s) {
     cell.runs = a.H == 1 && a.L % 4 == 0 && aligned16(a.pz) && aligned16(a.pr) && aligned16(a.pc) &&
                 aligned16(a.h);
     constexpr TileCfg c = kCfgGruChain, lc = kCfgGruLocal;
-    return chain_forward<GruChain, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, lc.nw_cl, lc.c_cl>(
+    return chain_forward<GruChain, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, lc.nw_cl, lc.c_cl, lc.cw_cl>(
         c, lc, cell, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, a.local, ws, s);
 }
 
@@ -771,7 +780,7 @@ hipError_t lstm_forward_chain(const LstmFwdArgs &a, const Ws &ws, hipStream_t s)
     cell.c = a.c;
     cell.runs = false;
     constexpr TileCfg c = kCfgLstmChain, lc = kCfgLstmLocal;
-    return chain_forward<LstmChain, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, lc.nw_cl, lc.c_cl>(
+    return chain_forward<LstmChain, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, lc.nw_cl, lc.c_cl, lc.cw_cl>(
         c, lc, cell, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, a.local, ws, s);
 }
 

@@ -14,6 +14,7 @@ struct TileCfg {
     int nw_cl, c_cl;  // channel lanes (H >= 32)
     int nw_tl, c_tl;  // time lanes (H < 32)
     int ncw_cl = 1;   // channel lanes: groups of 64 channels per workgroup
+    int cw_cl = 64;   // channel lanes: channels per wave row (32: a wave holds two sub-chunks)
 };
 constexpr TileCfg kCfgLinDiag{16, 16, 4, 16, 2};
 // The diagonal scan with channel lanes prefetches the next tile (linscan.hip).
@@ -28,9 +29,11 @@ constexpr TileCfg kCfgLstmAdj{8, 16, 4, 4};
 constexpr TileCfg kCfgGruChain{4, 16, 8, 24};
 constexpr TileCfg kCfgLstmChain{8, 8, 8, 8};
 // Channel-lane tiles of the chained kernel's form in which workgroups own
-// whole chains (its time-lane fields are unused).
+// whole chains (its time-lane fields are unused).  The LSTM's chains are 32
+// channels wide, so that two 4-wave workgroups share a CU and each one's
+// serial phases overlap the other's cells.
 constexpr TileCfg kCfgGruLocal{16, 8, 8, 16};
-constexpr TileCfg kCfgLstmLocal{8, 8, 8, 8};
+constexpr TileCfg kCfgLstmLocal{4, 8, 8, 8, 1, 32};
 // Waves per SIMD the chained kernels are compiled for (bounds their registers).
 constexpr int kChainMinWaves = 1;
 // Largest Newton cap the chained kernels take (their workspace holds the
@@ -42,6 +45,10 @@ static_assert(kCfgGruStep.ncw_cl == 1 && kCfgLstmStep.ncw_cl == 1 && kCfgGruAdj.
                   kCfgLstmAdj.ncw_cl == 1 && kCfgGruChain.ncw_cl == 1 && kCfgLstmChain.ncw_cl == 1 &&
                   kCfgGruLocal.ncw_cl == 1 && kCfgLstmLocal.ncw_cl == 1,
               "channel groups are for the exported scans only");
+static_assert(kCfgGruStep.cw_cl == 64 && kCfgLstmStep.cw_cl == 64 && kCfgGruAdj.cw_cl == 64 &&
+                  kCfgLstmAdj.cw_cl == 64 && kCfgGruChain.cw_cl == 64 && kCfgLstmChain.cw_cl == 64 &&
+                  kCfgLinDiag.cw_cl == 64 && kCfgLinBlk2.cw_cl == 64 && kCfgLinBlk4.cw_cl == 64,
+              "half-wave channel rows are for the whole-chain form only");
 constexpr int64_t kChannelLanesMinH = 32;
 // Look-back descriptors polled at once by one channel lane (diagonal, 2x2;
 // batches of 2 to 8 measured slower with the current tiles).
@@ -66,8 +73,8 @@ inline ScanShape scan_shape(const TileCfg &cfg, int64_t B, int64_t L, int64_t H)
     s.channel_lanes = H >= kChannelLanesMinH;
     s.nw = s.channel_lanes ? cfg.nw_cl : cfg.nw_tl;
     s.c = s.channel_lanes ? cfg.c_cl : cfg.c_tl;
-    const int64_t width = s.channel_lanes ? (int64_t)64 * cfg.ncw_cl : 1;  // channels per tile
-    s.T = s.channel_lanes ? (int64_t)(s.nw / cfg.ncw_cl) * s.c : (int64_t)s.nw * 64 * s.c;
+    const int64_t width = s.channel_lanes ? (int64_t)cfg.cw_cl * cfg.ncw_cl : 1;  // channels per tile
+    s.T = s.channel_lanes ? (int64_t)(s.nw / cfg.ncw_cl) * (64 / cfg.cw_cl) * s.c : (int64_t)s.nw * 64 * s.c;
     s.ncb = s.channel_lanes ? (H + width - 1) / width : H;
     s.nq = (L + s.T - 1) / s.T;
     s.ntiles = s.nq * B * s.ncb;
