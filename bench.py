@@ -52,7 +52,8 @@ ALG_BYTES = {
     "x_gru_seq": 16,             # 3 p in; h out
     "x_lstm_seq": 24,            # 4 p in; h, c out
     "x_gru_long_seq": 16,        # 3 p in; h out
-    "x_linscan_blk4": 96,        # A (4x4) and b (4) in; h (4) out, per (batch, position, channel)
+    "x_linscan_blk4": 96,        # A (4x4) and b (4) in; h (4) out, per (batch, position, block)
+    "x_linscan_blk8": 320,       # A (8x8) and b (8) in; h (8) out, per (batch, position, block)
 }
 DOMINANT = {
     "c1_linscan": "diag_pf_kernel<16,16,2> (chunked scan, next tile prefetched)",
@@ -69,7 +70,8 @@ DOMINANT = {
     "x_gru_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
     "x_lstm_seq": "lstm_rollout_kernel (sequential application, one thread per channel)",
     "x_gru_long_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
-    "x_linscan_blk4": "chunk_scan_kernel<LinBlkOp<4>>",
+    "x_linscan_blk4": "blkrow_scan_kernel<4,8,8,1> (each block's rows on a group of 4 lanes)",
+    "x_linscan_blk8": "blkrow_scan_kernel<8,4,8,3> (each block's rows on a group of 8 lanes)",
 }
 # HBM bytes per launch of the dominant kernel from rocprofv3 counter runs
 # (FETCH_SIZE x 2.000 and WRITE_SIZE x 1.000, the factors a plain 1 GiB device
@@ -110,6 +112,8 @@ DESCRIBE = {
                       "(B*H = 16 threads, 2^20 positions each)",
     "x_linscan_blk4": "4x4 block linear recurrence h_t = A_t h_{t-1} + b_t, B=16 L=2048 H=256, "
                       "A~U(-0.42,0.42), b~N(0,1), h0=0",
+    "x_linscan_blk8": "8x8 block linear recurrence h_t = A_t h_{t-1} + b_t (heads of 8 channels), "
+                      "B=16 L=2048 H=64 heads, A~U(-0.3,0.3), b~N(0,1), h0=0",
 }
 
 
@@ -379,9 +383,11 @@ class Workload:
             self.out = torch.empty(B, L, H, 2, device=dev)
             self.ws = api.new_workspace(api.workspace_bytes(api.OP_LINSCAN_BLK2, B, L, H), dev)
             self._step = lambda: api.linscan_blk2(t["A"], t["b"], None, out=self.out, ws=self.ws)
-        elif name == "x_linscan_blk4":
-            self.out = torch.empty(B, L, H, 4, device=dev)
-            self.ws = api.new_workspace(api.workspace_bytes(api.OP_LINSCAN_BLK4, B, L, H), dev)
+        elif name in ("x_linscan_blk4", "x_linscan_blk8"):
+            k = self.w["k"]
+            self.out = torch.empty(B, L, H, k, device=dev)
+            op = api.OP_LINSCAN_BLK4 if k == 4 else api.OP_LINSCAN_BLK8
+            self.ws = api.new_workspace(api.workspace_bytes(op, B, L, H), dev)
             self._step = lambda: api.linscan_blk(t["A"], t["b"], None, out=self.out, ws=self.ws)
         elif name == "x_lstm_adjoint":
             p = [t[k] for k in ("pi", "pf", "po", "pg")]

@@ -77,7 +77,8 @@ enum {
     PARARNN_OP_LSTM_FORWARD = 3,
     PARARNN_OP_GRU_ADJOINT = 4,
     PARARNN_OP_LSTM_ADJOINT = 5,
-    PARARNN_OP_LINSCAN_BLK4 = 6   /* rnn_linscan_blk with k = 4 */
+    PARARNN_OP_LINSCAN_BLK4 = 6,  /* rnn_linscan_blk with k = 4 */
+    PARARNN_OP_LINSCAN_BLK8 = 7   /* rnn_linscan_blk with k = 8 */
 };
 
 /*
@@ -128,11 +129,13 @@ int rnn_linscan_blk2(int64_t B, int64_t L, int64_t H,
  *     h[b,t,j,:] = A[b,t,j] @ h[b,t-1,j,:] + b[b,t,j,:]
  * A: [B, L, H, k, k] row-major blocks (A[i][l] takes component l into i).
  * b, h: [B, L, H, k].  h0: [B, H, k] or NULL.
- * k = 2 is rnn_linscan_blk2 (its workspace query, PARARNN_OP_LINSCAN_BLK2);
- * k = 4 takes PARARNN_OP_LINSCAN_BLK4 workspace and any 4-byte alignment
- * (with A, b, h and h0 16-byte aligned, block rows and states move as
- * 16-byte accesses, faster).  Other k return PARARNN_ERR_UNSUPPORTED
- * (k < 1: PARARNN_ERR_INVALID).
+ * k = 2 is rnn_linscan_blk2 (its workspace query, PARARNN_OP_LINSCAN_BLK2).
+ * k = 4 and k = 8 take the workspace of PARARNN_OP_LINSCAN_BLK4 and
+ * PARARNN_OP_LINSCAN_BLK8 and any 4-byte alignment (with A 16-byte aligned,
+ * block rows move as 16-byte accesses, faster).  The rows of each block are
+ * spread over k lanes; PARARNN_BLK4_PATH=thread (read at the query and at
+ * the call) makes k = 4 take the kernel with one thread per block instead.
+ * Other k return PARARNN_ERR_UNSUPPORTED (k < 1: PARARNN_ERR_INVALID).
  */
 int rnn_linscan_blk(int32_t k, int64_t B, int64_t L, int64_t H,
                     const float *A, const float *b, const float *h0,

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpararnn.so")
 
 OP_LINSCAN_DIAG, OP_LINSCAN_BLK2, OP_GRU_FORWARD, OP_LSTM_FORWARD, OP_GRU_ADJOINT, \
-    OP_LSTM_ADJOINT, OP_LINSCAN_BLK4 = range(7)
+    OP_LSTM_ADJOINT, OP_LINSCAN_BLK4, OP_LINSCAN_BLK8 = range(8)
 CELL_GRU, CELL_LSTM = 0, 1
 
 EXPORTS = ("pararnn_workspace_bytes", "rnn_linscan_diag", "rnn_linscan_blk2", "rnn_linscan_blk",
@@ -180,7 +180,7 @@ def linscan_blk2(A, b, h0=None, *, out=None, ws=None):
 
 # ---------------------------------------------------------------- Newton forward
 def linscan_blk(A, b, h0=None, *, out=None, ws=None):
-    """k x k block scan h_t = A_t h_{t-1} + b_t (k = 2 or 4); A [B, L, H, k, k],
+    """k x k block scan h_t = A_t h_{t-1} + b_t (k = 2, 4 or 8); A [B, L, H, k, k],
     b [B, L, H, k]; returns h [B, L, H, k]."""
     lib = load_library()
     B, L, H, k = b.shape
@@ -191,9 +191,9 @@ def linscan_blk(A, b, h0=None, *, out=None, ws=None):
         _need(h0, (B, H, k), "h0", dev)
     h = torch.empty_like(b) if out is None else out
     _need(h, (B, L, H, k), "out", dev)
-    op = {2: OP_LINSCAN_BLK2, 4: OP_LINSCAN_BLK4}.get(k)
+    op = {2: OP_LINSCAN_BLK2, 4: OP_LINSCAN_BLK4, 8: OP_LINSCAN_BLK8}.get(k)
     if op is None:
-        raise PararnnError("rnn_linscan_blk supports k = 2 and 4, got %d" % k)
+        raise PararnnError("rnn_linscan_blk supports k = 2, 4 and 8, got %d" % k)
     ws, n = _workspace(op, B, L, H, dev, ws=ws)
     _check(lib.rnn_linscan_blk(k, B, L, H, _ptr(A), _ptr(b), _ptr(h0), _ptr(h), _ptr(ws), n,
                                _stream(dev)), "rnn_linscan_blk")

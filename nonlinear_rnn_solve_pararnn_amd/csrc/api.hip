@@ -100,6 +100,16 @@ size_t gru_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
         default: return kMinWs;
     }
 }
+// The 4x4 blocks take the lane-group kernel (blkrow.hip) unless
+// PARARNN_BLK4_PATH=thread asks for the one-thread-per-block scan.
+bool blk4_rows() {
+    const char *env = getenv("PARARNN_BLK4_PATH");
+    return !(env != nullptr && strcmp(env, "thread") == 0);
+}
+size_t blk4_ws(int64_t B, int64_t L, int64_t H) {
+    return blk4_rows() ? blkrow_ws(4, B, L, H).total : scan_ws(kCfgLinBlk4, 4, B, L, H).total;
+}
+
 size_t lstm_fwd_ws(int64_t B, int64_t L, int64_t H, int32_t cap) {
     if (lstm_path(cap) == Path::Step) return newton_ws(kCfgLstmStep, 2, B, L, H, cap).total;
     if (lstm_chain_owns_chains(B, L, H, env_chain_local("PARARNN_LSTM_PATH"))) return kMinWs;
@@ -132,7 +142,8 @@ size_t pararnn_workspace_bytes(int32_t op, int64_t B, int64_t L, int64_t H, int3
         case PARARNN_OP_LSTM_FORWARD:
             if (max_iter < 1) return 0;
             return lstm_fwd_ws(B, L, H, eff_cap(max_iter, L));
-        case PARARNN_OP_LINSCAN_BLK4: return scan_ws(kCfgLinBlk4, 4, B, L, H).total;
+        case PARARNN_OP_LINSCAN_BLK4: return blk4_ws(B, L, H);
+        case PARARNN_OP_LINSCAN_BLK8: return blkrow_ws(8, B, L, H).total;
         case PARARNN_OP_GRU_ADJOINT: return gru_adjoint_ws(B, L, H);
         case PARARNN_OP_LSTM_ADJOINT: return lstm_adjoint_ws(B, L, H);
         default: return 0;
@@ -163,14 +174,21 @@ int rnn_linscan_blk(int32_t k, int64_t B, int64_t L, int64_t H, const float *A, 
                     const float *h0, float *h, void *ws, size_t ws_bytes, void *stream) {
     if (k == 2) return rnn_linscan_blk2(B, L, H, A, b, h0, h, ws, ws_bytes, stream);
     if (k < 1) return PARARNN_ERR_INVALID;
-    if (k != 4) return PARARNN_ERR_UNSUPPORTED;
+    if (k != 4 && k != 8) return PARARNN_ERR_UNSUPPORTED;
     if (!dims_ok(B, L, H) || !A || !b || !h || !ws) return PARARNN_ERR_INVALID;
     if (!aligned(A, 4) || !aligned(b, 4) || !aligned(h, 4) || (h0 && !aligned(h0, 4)))
         return PARARNN_ERR_INVALID;
-    if (!grid_ok(scan_shape(kCfgLinBlk4, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
-    if (ws_bytes < scan_ws(kCfgLinBlk4, 4, B, L, H).total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
-    return status_of(linscan_blk(4, B, L, H, A, b, h0, h, Ws{static_cast<char *>(ws), ws_bytes},
-                                 static_cast<hipStream_t>(stream)));
+    const Ws w{static_cast<char *>(ws), ws_bytes};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (k == 4 && !blk4_rows()) {
+        if (!grid_ok(scan_shape(kCfgLinBlk4, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
+        if (ws_bytes < scan_ws(kCfgLinBlk4, 4, B, L, H).total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+        return status_of(linscan_blk(4, B, L, H, A, b, h0, h, w, s));
+    }
+    const BlkRowWs need = blkrow_ws(k, B, L, H);
+    if (!grid_ok(need.ntiles)) return PARARNN_ERR_INVALID;
+    if (ws_bytes < need.total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+    return status_of(linscan_blkrow(k, B, L, H, A, b, h0, h, w, s));
 }
 
 int pararnn_gru_forward(int64_t B, int64_t L, int64_t H, const float *pz, const float *pr,

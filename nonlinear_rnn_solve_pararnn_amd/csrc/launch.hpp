@@ -47,6 +47,10 @@ hipError_t linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const f
 hipError_t linscan_blk(int k, int64_t B, int64_t L, int64_t H, const float *A, const float *b,
                        const float *h0, float *h, const Ws &ws, hipStream_t s);
 
+// k x k blocks with each block's rows on a lane group, k = 4 or 8
+// (hipErrorInvalidValue otherwise); workspace blkrow_ws
+hipError_t linscan_blkrow(int k, int64_t B, int64_t L, int64_t H, const float *A, const float *b,
+                          const float *h0, float *h, const Ws &ws, hipStream_t s);
 struct GruFwdArgs {
     int64_t B, L, H;
     const float *pz, *pr, *pc, *uz, *ur, *uc, *h0;

@@ -172,6 +172,48 @@ inline ChainWs chain_ws(const TileCfg &cfg, int S, int64_t B, int64_t L, int64_t
     return w;
 }
 
+// k x k blocks (k = 4, 8) with each block's rows on a group of k lanes
+// (blkrow.hip): a wave holds 64/k heads, a workgroup nw waves that are
+// consecutive sub-chunks of c positions of the same heads.
+struct BlkRowCfg {
+    int nw, c;
+    int minw;  // waves per SIMD the kernel's registers must allow
+};
+// Measured at B=16, L=2048 (8x8: H=64 heads, 4x4: H=256): 8x8 with 4 waves
+// x 8 positions bounded to 168 registers (three workgroups per CU, a few
+// spills) 166 us, unbounded (180 registers, two per CU) 188 us, 8 x 4 or
+// 4 x 16 250-315 us; 4x4 with 8 waves x 8 positions 180 us, 8 x 4 229-239
+// us, 4 x 8 238 us.
+constexpr BlkRowCfg kBlkRow8{4, 8, 3};
+constexpr BlkRowCfg kBlkRow4{8, 8, 1};
+// The lane exchanges of the lane-group scan ride on the multiply-adds
+// (v_fmac_f32 with a DPP operand) instead of separate DPP moves.
+constexpr bool kBlkRowDppFma = true;
+
+// Workspace: header, then per chunk the aggregate rows (k + 1 words per
+// row) and the inclusive state rows (one word), both [chunk][word][row].
+struct BlkRowWs {
+    int64_t T, ncb, nq, ntiles, nrow;
+    size_t hdr, agg, inc, total;
+};
+
+inline BlkRowWs blkrow_ws(int k, int64_t B, int64_t L, int64_t H) {
+    const BlkRowCfg cfg = k == 8 ? kBlkRow8 : kBlkRow4;
+    BlkRowWs w;
+    w.T = (int64_t)cfg.nw * cfg.c;
+    const int64_t heads = 64 / k;
+    w.ncb = (H + heads - 1) / heads;
+    w.nq = (L + w.T - 1) / w.T;
+    w.ntiles = w.nq * B * w.ncb;
+    w.nrow = B * H * k;
+    Carve c;
+    w.hdr = c.take(16);
+    w.agg = c.take((size_t)w.nq * (k + 1) * w.nrow * 8);
+    w.inc = c.take((size_t)w.nq * w.nrow * 8);
+    w.total = c.off;
+    return w;
+}
+
 // Fused on-chip GRU Newton: one workgroup owns all L positions of
 // kFusedChannels channels of one batch row; each lane is one (channel,
 // sub-chunk), 32 sub-chunks of C positions (so 32 * kFusedChannels / 64

@@ -48,6 +48,9 @@ WORKLOADS = {
     "x_gru_long_seq": dict(kind="gru", B=16, L=1048576, H=1, same_as="c4_gru_long_fwd_adj"),
     # the 4x4 block scan at the diagonal scan's byte count (96 B per block position)
     "x_linscan_blk4": dict(kind="linscan_blk", B=16, L=2048, H=256, k=4),
+    # 8x8 blocks: heads of 8 channels with dense recurrence inside a head,
+    # 64 heads (512 channels), 320 B per block position
+    "x_linscan_blk8": dict(kind="linscan_blk", B=16, L=2048, H=64, k=8),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -183,6 +186,6 @@ def workload_inputs(name: str) -> dict:
         return linscan_blk2_inputs(B, L, H, seed)
     if name == "x_lstm_adjoint":
         return lstm_inputs(B, L, H, seed, grad=True)
-    if name == "x_linscan_blk4":
+    if name in ("x_linscan_blk4", "x_linscan_blk8"):
         return linscan_blk_inputs(B, L, H, w["k"], seed)
     raise KeyError(name)

@@ -193,9 +193,10 @@ def test_two_streams_with_their_own_workspaces(orc):
         assert max_abs(host(h), ref2) <= FWD_ATOL
 
 
-# 4x4 blocks: time lanes (H < 32: chunks of 4 waves x 64 threads x 2
-# positions) and channel lanes (chunks of 64 channels x 32 positions), ragged
-# tails in L and in the channel blocks.
+# 4x4 blocks: 16 blocks per wave (each block's rows on 4 lanes), chunks of 8
+# waves x 8 positions; ragged tails in L and in the blocks of a wave.  The
+# thread-per-block kernel (time and channel lanes) is covered by
+# test_linscan_blk4_thread_path.
 BLK4_SHAPES = [(1, 1, 1), (2, 100, 3), (2, 1500, 2), (3, 257, 70), (2, 300, 31), (2, 300, 32),
                (4, 1000, 64), (1, 64, 4), (2, 97, 130)]
 
@@ -241,6 +242,55 @@ def test_linscan_blk4_repeated_calls_share_a_workspace(orc):
         assert max_abs(h, ref) <= FWD_ATOL
 
 
+def test_linscan_blk4_thread_path(orc, monkeypatch):
+    """The one-thread-per-block 4x4 kernel, still selectable, on both lane
+    layouts with ragged tails."""
+    monkeypatch.setenv("PARARNN_BLK4_PATH", "thread")
+    for B, L, H in [(2, 1500, 2), (3, 257, 70)]:
+        say("linscan_blk4 thread path", B, L, H)
+        d = synth.linscan_blk_inputs(B, L, H, 4, seed=340 + H, h0=True)
+        h = host(api.linscan_blk(dev(d["A"]), dev(d["b"]), dev(d["h0"])))
+        assert max_abs(h, orc.linscan_blk(d["A"], d["b"], d["h0"])) <= FWD_ATOL
+
+
+# 8x8 blocks: 8 heads per wave, chunks of 4 waves x 8 positions; ragged head
+# blocks (H not a multiple of 8), ragged chunks, a single head over a long L.
+BLK8_SHAPES = [(1, 1, 1), (2, 100, 3), (3, 257, 9), (2, 1500, 2), (2, 300, 16), (1, 64, 8),
+               (2, 97, 13), (1, 3000, 1)]
+
+
+@pytest.mark.parametrize("B,L,H", BLK8_SHAPES)
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_linscan_blk8_matches_oracle(orc, B, L, H, with_h0):
+    say("linscan_blk8", B, L, H, with_h0)
+    d = synth.linscan_blk_inputs(B, L, H, 8, seed=400 + B * 7 + H, h0=with_h0)
+    h0 = dev(d["h0"]) if with_h0 else None
+    h = host(api.linscan_blk(dev(d["A"]), dev(d["b"]), h0))
+    err = max_abs(h, orc.linscan_blk(d["A"], d["b"], d["h0"] if with_h0 else None))
+    say(err)
+    assert err <= FWD_ATOL
+
+
+def test_linscan_blk8_full_workload(orc):
+    """The 8x8 scan at the measured size, B=16, L=2048, H=64 heads, every element."""
+    say("linscan_blk8 full workload")
+    d = synth.workload_inputs("x_linscan_blk8")
+    h = host(api.linscan_blk(dev(d["A"]), dev(d["b"])))
+    err = max_abs(h, orc.linscan_blk(d["A"], d["b"]))
+    say(err)
+    assert err <= FWD_ATOL
+
+
+def test_linscan_blk8_repeated_calls_share_a_workspace(orc):
+    d = synth.linscan_blk_inputs(2, 2000, 24, 8, seed=411)
+    A, b = dev(d["A"]), dev(d["b"])
+    ws = api.new_workspace(api.workspace_bytes(api.OP_LINSCAN_BLK8, 2, 2000, 24), A.device)
+    outs = [host(api.linscan_blk(A, b, ws=ws)) for _ in range(3)]
+    ref = orc.linscan_blk(d["A"], d["b"])
+    for h in outs:
+        assert max_abs(h, ref) <= FWD_ATOL
+
+
 def test_linscan_blk_rejects_unsupported_k():
     A = torch.zeros(1, 4, 2, 3, 3, device="cuda")
     b = torch.zeros(1, 4, 2, 3, device="cuda")
@@ -272,6 +322,19 @@ def test_linscan_blk2_aligned_and_offset_views(orc, B, L, H, misalign):
 def test_linscan_blk4_aligned_and_offset_views(orc, B, L, H, misalign):
     say("linscan_blk4 paths", B, L, H, misalign)
     d = synth.linscan_blk_inputs(B, L, H, 4, seed=330 + L + H, h0=True)
+    A, b, h0 = dev(d["A"]), dev(d["b"]), dev(d["h0"])
+    out = torch.empty_like(b)
+    if misalign:
+        A, b, h0, out = (_offset(x, misalign) for x in (A, b, h0, out))
+    h = host(api.linscan_blk(A, b, h0, out=out))
+    assert max_abs(h, orc.linscan_blk(d["A"], d["b"], d["h0"])) <= FWD_ATOL
+
+
+@pytest.mark.parametrize("B,L,H", BLK_VIEW_SHAPES)
+@pytest.mark.parametrize("misalign", [0, 1, 3])
+def test_linscan_blk8_aligned_and_offset_views(orc, B, L, H, misalign):
+    say("linscan_blk8 paths", B, L, H, misalign)
+    d = synth.linscan_blk_inputs(B, L, H, 8, seed=430 + L + H, h0=True)
     A, b, h0 = dev(d["A"]), dev(d["b"]), dev(d["h0"])
     out = torch.empty_like(b)
     if misalign:
