@@ -63,6 +63,12 @@ def _load():
     lib.orc_lstm_newton.restype = ctypes.c_int
     lib.orc_gru_bptt.argtypes = [_I64, _I64, _I64] + [vp] * 16
     lib.orc_lstm_bptt.argtypes = [_I64, _I64, _I64] + [vp] * 24
+    lib.orc_hgru_cell.argtypes = [ctypes.c_int] + [vp] * 10
+    lib.orc_hgru_rollout.argtypes = [_I64, _I64, _I64, ctypes.c_int] + [vp] * 8
+    lib.orc_hgru_newton.argtypes = [_I64, _I64, _I64, ctypes.c_int] + [vp] * 7 + [
+        ctypes.c_double, ctypes.c_int, vp, vp, vp]
+    lib.orc_hgru_newton.restype = ctypes.c_int
+    lib.orc_hgru_bptt.argtypes = [_I64, _I64, _I64, ctypes.c_int] + [vp] * 16
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
@@ -230,3 +236,62 @@ def lstm_bptt(pi, pf, po, pg, ui, uf, uo, ug, h, c, gh, gc=None, h0=None, c0=Non
                           _p(h0), _p(c0), _p(h), _p(c), _p(gh), _p(gc),
                           *[_p(x) for x in dp], *[_p(x) for x in du], _p(dh0), _p(dc0))
     return dp, du, dh0, dc0
+
+
+# ----------------------------------------------------------------- head GRU
+def hgru_cell(h, pz, pr, pc, Uz, Ur, Uc):
+    """One step of the GRU with dense recurrence inside a head of k channels:
+    vectors [k], matrices [k, k].  Returns (f [k], J [k, k], gates [4, k] =
+    z, r, c, r*h)."""
+    h, pz, pr, pc = _f64(h), _f64(pz), _f64(pr), _f64(pc)
+    Uz, Ur, Uc = _f64(Uz), _f64(Ur), _f64(Uc)
+    k = h.shape[0]
+    f = np.zeros(k)
+    J = np.zeros((k, k))
+    gt = np.zeros((4, k))
+    _load().orc_hgru_cell(k, _p(h), _p(pz), _p(pr), _p(pc), _p(Uz), _p(Ur), _p(Uc),
+                          _p(f), _p(J), _p(gt))
+    return f, J, gt
+
+
+def hgru_rollout(pz, pr, pc, Uz, Ur, Uc, h0=None):
+    """Sequential head GRU: p [B, L, NH, k], U [NH, k, k], h0 [B, NH, k]."""
+    pz, pr, pc = _f64(pz), _f64(pr), _f64(pc)
+    Uz, Ur, Uc, h0 = _f64(Uz), _f64(Ur), _f64(Uc), _f64(h0)
+    B, L, NH, k = pz.shape
+    assert k <= 8 and Uz.shape == (NH, k, k)
+    h = np.empty_like(pz)
+    _load().orc_hgru_rollout(B, L, NH, k, _p(pz), _p(pr), _p(pc), _p(Uz), _p(Ur), _p(Uc),
+                             _p(h0), _p(h))
+    return h
+
+
+def hgru_newton(pz, pr, pc, Uz, Ur, Uc, h0=None, tol=1e-6, cap=64):
+    """CPU Newton for the head GRU from s = 0 (k x k block Jacobians).
+    Returns (s, iterations, converged, trace[iters])."""
+    pz, pr, pc = _f64(pz), _f64(pr), _f64(pc)
+    Uz, Ur, Uc, h0 = _f64(Uz), _f64(Ur), _f64(Uc), _f64(h0)
+    B, L, NH, k = pz.shape
+    s = np.empty_like(pz)
+    conv = np.zeros(1, np.int32)
+    trace = np.zeros(max(cap, 1))
+    it = _load().orc_hgru_newton(B, L, NH, k, _p(pz), _p(pr), _p(pc), _p(Uz), _p(Ur), _p(Uc),
+                                 _p(h0), float(tol), int(cap), _p(s),
+                                 conv.ctypes.data_as(ctypes.c_void_p), _p(trace))
+    return s, int(it), int(conv[0]), trace[:it].copy()
+
+
+def hgru_bptt(pz, pr, pc, Uz, Ur, Uc, h, g, h0=None):
+    """Gradients of sum(g * h) through the head GRU rollout h.  Returns
+    (dpz, dpr, dpc, dUz, dUr, dUc, dh0)."""
+    pz, pr, pc = _f64(pz), _f64(pr), _f64(pc)
+    Uz, Ur, Uc, h0 = _f64(Uz), _f64(Ur), _f64(Uc), _f64(h0)
+    h, g = _f64(h), _f64(g)
+    B, L, NH, k = pz.shape
+    dp = [np.empty_like(pz) for _ in range(3)]
+    dU = [np.empty_like(Uz) for _ in range(3)]
+    dh0 = np.empty((B, NH, k))
+    _load().orc_hgru_bptt(B, L, NH, k, _p(pz), _p(pr), _p(pc), _p(Uz), _p(Ur), _p(Uc),
+                          _p(h0), _p(h), _p(g), *[_p(x) for x in dp], *[_p(x) for x in dU],
+                          _p(dh0))
+    return (*dp, *dU, dh0)

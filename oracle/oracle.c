@@ -21,6 +21,9 @@
  *    forms of the classical cells that those captions name.
  *  - Gradients of L = sum g*h through the rollout, by plain reverse-mode
  *    backpropagation through time (DEER summary: forward plus gradients).
+ *  - A GRU with dense recurrence inside heads of k channels (DEER summary,
+ *    limitations paragraph): its rollout, Newton with k x k block Jacobians
+ *    and backpropagation through time.
  *  - The linear recurrence h_t = a_t*h_{t-1} + b_t by a serial loop
  *    (minimal-RNN article: gates without h-dependence give a recurrence that
  *    a parallel scan solves; DEER summary: associative scan), and its 2x2 and
@@ -486,6 +489,227 @@ void orc_lstm_bptt(int64_t B, int64_t L, int64_t H,
             outs[q][j] = a;
         }
     }
+    free(acc);
+}
+
+/* -------------------------------------------------------------------------
+ * GRU cell with dense recurrence inside heads of k channels (k <= 8): the
+ * diagonal GRU cell above with its weight vectors u replaced by one k x k
+ * matrix per head (DEER summary page, limitations paragraph: dense
+ * Jacobians; its GRU with heads of 8 channels).  Reading: each U acts on the
+ * state vector where the diagonal cell multiplies elementwise by u, so a
+ * diagonal U is exactly the diagonal cell:
+ *   z = sig(pz + Uz h), r = sig(pr + Ur h), c = tanh(pc + Uc (r*h)),
+ *   f = (1 - z)*h + z*c         (vectors of k, '*' elementwise)
+ * U is row-major: U[i*k + l] takes component l of its operand into i.
+ * Outputs f[k]; optionally J[k*k] = df/dh (row i, column l: d f_i / d h_l)
+ * and the gates z, r, c, s = r*h (4 x k) for the backward pass.
+ * ------------------------------------------------------------------------- */
+void orc_hgru_cell(int k, const double *h, const double *pz, const double *pr,
+                   const double *pc, const double *Uz, const double *Ur,
+                   const double *Uc, double *f, double *J, double *gates)
+{
+    double z[8], r[8], s[8], c[8];
+    for (int i = 0; i < k; ++i) {
+        double az = pz[i], ar = pr[i];
+        for (int l = 0; l < k; ++l) {
+            az += Uz[i * k + l] * h[l];
+            ar += Ur[i * k + l] * h[l];
+        }
+        z[i] = sigm(az);
+        r[i] = sigm(ar);
+        s[i] = r[i] * h[i];
+    }
+    for (int i = 0; i < k; ++i) {
+        double ac = pc[i];
+        for (int m = 0; m < k; ++m) ac += Uc[i * k + m] * s[m];
+        c[i] = tanh(ac);
+        f[i] = (1.0 - z[i]) * h[i] + z[i] * c[i];
+    }
+    if (J) {
+        /* ds_m/dh_l = [m == l] r_m + h_m r_m (1 - r_m) Ur[m][l]
+           dc_i/dh_l = (1 - c_i^2) sum_m Uc[i][m] ds_m/dh_l
+           df_i/dh_l = [i == l](1 - z_i) + (c_i - h_i) z_i (1 - z_i) Uz[i][l]
+                       + z_i dc_i/dh_l */
+        for (int i = 0; i < k; ++i)
+            for (int l = 0; l < k; ++l) {
+                double dc = 0.0;
+                for (int m = 0; m < k; ++m) {
+                    double ds = (m == l ? r[m] : 0.0) + h[m] * r[m] * (1.0 - r[m]) * Ur[m * k + l];
+                    dc += Uc[i * k + m] * ds;
+                }
+                dc *= 1.0 - c[i] * c[i];
+                J[i * k + l] = (i == l ? 1.0 - z[i] : 0.0)
+                               + (c[i] - h[i]) * z[i] * (1.0 - z[i]) * Uz[i * k + l]
+                               + z[i] * dc;
+            }
+    }
+    if (gates)
+        for (int i = 0; i < k; ++i) {
+            gates[i] = z[i];
+            gates[k + i] = r[i];
+            gates[2 * k + i] = c[i];
+            gates[3 * k + i] = s[i];
+        }
+}
+
+/* Index of component i of head n at (b, t) in a [B, L, NH, k] tensor. */
+#define HIDX(b, t, n, i) ((((size_t)(b) * (size_t)L + (size_t)(t)) * (size_t)NH + (size_t)(n)) * (size_t)k + (size_t)(i))
+
+/* Sequential rollout of the head GRU: tensors [B, L, NH, k], U [NH, k, k],
+   h0 [B, NH, k] or NULL. */
+void orc_hgru_rollout(int64_t B, int64_t L, int64_t NH, int k,
+                      const double *pz, const double *pr, const double *pc,
+                      const double *Uz, const double *Ur, const double *Uc,
+                      const double *h0, double *h)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t bb = 0; bb < B; ++bb)
+        for (int64_t n = 0; n < NH; ++n) {
+            double x[8], f[8];
+            for (int i = 0; i < k; ++i) x[i] = h0 ? h0[((size_t)bb * NH + n) * k + i] : 0.0;
+            const size_t u = (size_t)n * k * k;
+            for (int64_t t = 0; t < L; ++t) {
+                size_t e = HIDX(bb, t, n, 0);
+                orc_hgru_cell(k, x, pz + e, pr + e, pc + e, Uz + u, Ur + u, Uc + u, f, NULL, NULL);
+                for (int i = 0; i < k; ++i) {
+                    x[i] = f[i];
+                    h[e + i] = f[i];
+                }
+            }
+        }
+}
+
+/* Newton's method for the head GRU from s = 0, as orc_gru_newton: the
+   linearised system is block bi-diagonal with the k x k Jacobians of the
+   cell, solved by forward substitution delta_t = J_t delta_{t-1} - r_t. */
+int orc_hgru_newton(int64_t B, int64_t L, int64_t NH, int k,
+                    const double *pz, const double *pr, const double *pc,
+                    const double *Uz, const double *Ur, const double *Uc,
+                    const double *h0, double tol, int cap, double *s,
+                    int *converged, double *trace)
+{
+    size_t N = (size_t)B * (size_t)L * (size_t)NH * (size_t)k;
+    double *F = (double *)malloc(N * sizeof(double));
+    double *Jm = (double *)malloc(N * (size_t)k * sizeof(double));
+    memset(s, 0, N * sizeof(double));
+    *converged = 0;
+    int it;
+    for (it = 1; it <= cap; ++it) {
+        double e = 0.0;
+#pragma omp parallel for collapse(2) schedule(static) reduction(max : e)
+        for (int64_t bb = 0; bb < B; ++bb)
+            for (int64_t n = 0; n < NH; ++n) {
+                const size_t u = (size_t)n * k * k;
+                double prev[8];
+                for (int64_t t = 0; t < L; ++t) {
+                    size_t ee = HIDX(bb, t, n, 0);
+                    for (int i = 0; i < k; ++i)
+                        prev[i] = t > 0 ? s[HIDX(bb, t - 1, n, i)]
+                                        : (h0 ? h0[((size_t)bb * NH + n) * k + i] : 0.0);
+                    orc_hgru_cell(k, prev, pz + ee, pr + ee, pc + ee, Uz + u, Ur + u, Uc + u,
+                                  F + ee, Jm + ee * k, NULL);
+                }
+                double d[8] = {0}, dn[8], em = 0.0;
+                for (int64_t t = 0; t < L; ++t) {
+                    size_t ee = HIDX(bb, t, n, 0);
+                    for (int i = 0; i < k; ++i) {
+                        double v = F[ee + i] - s[ee + i];
+                        for (int l = 0; l < k; ++l) v += Jm[(ee + i) * k + l] * d[l];
+                        dn[i] = v;
+                    }
+                    for (int i = 0; i < k; ++i) {
+                        d[i] = dn[i];
+                        em = absmax_update(em, d[i]);
+                        s[ee + i] += d[i];
+                    }
+                }
+                if (em > e) e = em;
+            }
+        if (trace) trace[it - 1] = e;
+        if (e <= tol) {
+            *converged = 1;
+            break;
+        }
+    }
+    free(F);
+    free(Jm);
+    return it > cap ? cap : it;
+}
+
+/* Backpropagation through time for L = sum_t g_t . h_t through the head GRU,
+   given the forward states h:
+     lambda_t = g_t + J_{t+1}^T lambda_{t+1}
+     dL/dpz_i = lambda_i (c_i - h_i) z_i (1 - z_i)
+     dL/dpc_i = lambda_i z_i (1 - c_i^2)
+     dL/dpr_m = h_m r_m (1 - r_m) sum_i Uc[i][m] dL/dpc_i
+     dL/dUz[i][l] += dL/dpz_i h_l,  dL/dUr[m][l] += dL/dpr_m h_l,
+     dL/dUc[i][m] += dL/dpc_i s_m   (h the state entering the step)
+     dL/dh0 = J_0^T lambda_0.
+   dU [NH, k, k] is summed over b and t and written; dh0 may be NULL. */
+void orc_hgru_bptt(int64_t B, int64_t L, int64_t NH, int k,
+                   const double *pz, const double *pr, const double *pc,
+                   const double *Uz, const double *Ur, const double *Uc,
+                   const double *h0, const double *h, const double *g,
+                   double *dpz, double *dpr, double *dpc,
+                   double *dUz, double *dUr, double *dUc, double *dh0)
+{
+    const size_t kk = (size_t)k * k;
+    double *acc = (double *)calloc((size_t)B * NH * 3 * kk, sizeof(double));
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t bb = 0; bb < B; ++bb)
+        for (int64_t n = 0; n < NH; ++n) {
+            const size_t u = (size_t)n * kk;
+            double *az = acc + ((size_t)bb * NH + n) * 3 * kk, *ar = az + kk, *ac = ar + kk;
+            double lam[8] = {0}, prev[8], f[8], J[64], gt[32];
+            for (int64_t t = L - 1; t >= 0; --t) {
+                size_t ee = HIDX(bb, t, n, 0);
+                for (int i = 0; i < k; ++i) {
+                    lam[i] += g[ee + i];
+                    prev[i] = t > 0 ? h[HIDX(bb, t - 1, n, i)]
+                                    : (h0 ? h0[((size_t)bb * NH + n) * k + i] : 0.0);
+                }
+                orc_hgru_cell(k, prev, pz + ee, pr + ee, pc + ee, Uz + u, Ur + u, Uc + u, f, J, gt);
+                const double *z = gt, *r = gt + k, *c = gt + 2 * k, *sv = gt + 3 * k;
+                for (int i = 0; i < k; ++i) {
+                    dpz[ee + i] = lam[i] * (c[i] - prev[i]) * z[i] * (1.0 - z[i]);
+                    dpc[ee + i] = lam[i] * z[i] * (1.0 - c[i] * c[i]);
+                }
+                for (int m = 0; m < k; ++m) {
+                    double v = 0.0;
+                    for (int i = 0; i < k; ++i) v += Uc[u + i * k + m] * dpc[ee + i];
+                    dpr[ee + m] = prev[m] * r[m] * (1.0 - r[m]) * v;
+                }
+                for (int i = 0; i < k; ++i)
+                    for (int l = 0; l < k; ++l) {
+                        az[i * k + l] += dpz[ee + i] * prev[l];
+                        ar[i * k + l] += dpr[ee + i] * prev[l];
+                        ac[i * k + l] += dpc[ee + i] * sv[l];
+                    }
+                double nl[8];
+                for (int l = 0; l < k; ++l) {
+                    double v = 0.0;
+                    for (int i = 0; i < k; ++i) v += J[i * k + l] * lam[i];
+                    nl[l] = v;
+                }
+                for (int l = 0; l < k; ++l) lam[l] = nl[l];
+            }
+            if (dh0)
+                for (int i = 0; i < k; ++i) dh0[((size_t)bb * NH + n) * k + i] = lam[i];
+        }
+    for (int64_t n = 0; n < NH; ++n)
+        for (size_t q = 0; q < kk; ++q) {
+            double a0 = 0, a1 = 0, a2 = 0;
+            for (int64_t bb = 0; bb < B; ++bb) {
+                const double *a = acc + ((size_t)bb * NH + n) * 3 * kk;
+                a0 += a[q];
+                a1 += a[kk + q];
+                a2 += a[2 * kk + q];
+            }
+            dUz[n * kk + q] = a0;
+            dUr[n * kk + q] = a1;
+            dUc[n * kk + q] = a2;
+        }
     free(acc);
 }
 

@@ -476,3 +476,152 @@ def test_gru_bptt_u0_is_reverse_linear_scan(orc):
     hp = np.concatenate([np.zeros((2, 1, 3)), h[:, :-1]], axis=1)
     np.testing.assert_allclose(dp[0], (c - hp) * z * (1 - z) * lam, atol=1e-12)
     np.testing.assert_allclose(dp[2], z * (1 - c * c) * lam, atol=1e-12)
+
+
+# ---------------------------------------------------------------- head GRU
+def _hgru_draw(seed, B, L, NH, k, dense=True, tri=False):
+    """Inputs of the GRU with dense recurrence inside heads of k channels:
+    p ~ N(0,1), U = diag(U(-0.5,0.5)) plus, if dense, off-diagonal entries
+    U(-0.3,0.3)/sqrt(k) (only below the diagonal if tri), h0 ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    p = [rng.standard_normal((B, L, NH, k)) for _ in range(3)]
+    Us = []
+    for _ in range(3):
+        U = np.zeros((NH, k, k))
+        for n in range(NH):
+            U[n] = np.diag(rng.uniform(-0.5, 0.5, k))
+            if dense:
+                off = rng.uniform(-0.3, 0.3, (k, k)) / np.sqrt(k)
+                np.fill_diagonal(off, 0.0)
+                if tri:
+                    off = np.tril(off, -1)
+                U[n] += off
+        Us.append(U)
+    h0 = rng.standard_normal((B, NH, k))
+    return p, Us, h0
+
+
+def test_hgru_diagonal_weights_are_the_diagonal_gru(orc):
+    """Diagonal U: the head GRU is the diagonal GRU on NH*k channels, rollout
+    and gradients (dU's diagonal is du)."""
+    B, L, NH, k = 2, 30, 3, 4
+    p, Us, h0 = _hgru_draw(11, B, L, NH, k, dense=False)
+    h = orc.hgru_rollout(*p, *Us, h0=h0)
+    flat = [x.reshape(B, L, NH * k) for x in p]
+    us = [np.concatenate([np.diag(U[n]) for n in range(NH)]) for U in Us]
+    ref = orc.gru_rollout(*flat, *us, h0=h0.reshape(B, NH * k))
+    np.testing.assert_allclose(h.reshape(B, L, NH * k), ref, rtol=0, atol=1e-14)
+    g = np.random.default_rng(12).standard_normal((B, L, NH, k))
+    got = orc.hgru_bptt(*p, *Us, h, g, h0=h0)
+    dp, du, dh0 = orc.gru_bptt(*flat, *us, ref, g.reshape(B, L, NH * k), h0=h0.reshape(B, NH * k))
+    for a, e in zip(got[:3], dp):
+        np.testing.assert_allclose(a.reshape(B, L, NH * k), e, rtol=1e-12, atol=1e-12)
+    for a, e in zip(got[3:6], du):
+        diag = np.concatenate([np.diag(a[n]) for n in range(NH)])
+        np.testing.assert_allclose(diag, e, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got[6].reshape(B, NH * k), dh0, rtol=1e-12, atol=1e-12)
+
+
+def test_hgru_equals_torch_gru_with_block_diagonal_weights(orc):
+    """Dense Uz, Ur (diagonal Uc, where torch's r*(W h) equals Uc (r*h)):
+    rollout and every gradient against torch.nn.GRU with block-diagonal
+    recurrent weights and autograd.  A transposed Uz or Ur fails it."""
+    B, L, NH, k = 2, 12, 2, 8
+    p, Us, h0 = _hgru_draw(13, B, L, NH, k)
+    Us[2] = np.stack([np.diag(np.diag(U)) for U in Us[2]])  # Uc diagonal
+    h = orc.hgru_rollout(*p, *Us, h0=h0)
+    m = tr.make_hgru(NH, k, *Us)
+    H = NH * k
+    pz, pr, pc = (torch.tensor(x.reshape(B, L, H), requires_grad=True) for x in p)
+    hx = torch.tensor(h0.reshape(1, B, H), requires_grad=True)
+    y, _ = m(torch.cat([pr, -pz, pc], dim=-1), hx)
+    np.testing.assert_allclose(h.reshape(B, L, H), y.detach().numpy(), rtol=0, atol=1e-13)
+    g = np.random.default_rng(14).standard_normal((B, L, NH, k))
+    (y * torch.tensor(g.reshape(B, L, H))).sum().backward()
+    got = orc.hgru_bptt(*p, *Us, h, g, h0=h0)
+    for a, t in zip(got[:3], (pz, pr, pc)):
+        np.testing.assert_allclose(a.reshape(B, L, H), t.grad.numpy(), rtol=1e-10, atol=1e-11)
+    w = m.weight_hh_l0.grad.numpy()
+    for n in range(NH):
+        sl = slice(n * k, (n + 1) * k)
+        np.testing.assert_allclose(got[4][n], w[0:H][sl, sl], rtol=1e-10, atol=1e-11)        # Ur
+        np.testing.assert_allclose(got[3][n], -w[H:2 * H][sl, sl], rtol=1e-10, atol=1e-11)   # Uz
+    np.testing.assert_allclose(got[6].reshape(B, H), hx.grad.numpy()[0], rtol=1e-10, atol=1e-11)
+
+
+def test_hgru_coupling_direction(orc):
+    """Couplings only below the diagonal (component i reads components l < i):
+    component 0 then evolves as a scalar GRU of its own; a transposed U (or
+    one applied to the wrong operand) would feed the others into it."""
+    B, L, NH, k = 2, 40, 2, 5
+    p, Us, h0 = _hgru_draw(15, B, L, NH, k, tri=True)
+    h = orc.hgru_rollout(*p, *Us, h0=h0)
+    for n in range(NH):
+        own = orc.gru_rollout(*[x[:, :, n, :1] for x in p], *[U[n, 0, :1] for U in Us],
+                              h0=h0[:, n, :1])
+        np.testing.assert_allclose(h[:, :, n, :1], own, rtol=0, atol=1e-14)
+        last = orc.gru_rollout(*[x[:, :, n, k - 1:] for x in p], *[U[n, k - 1, k - 1:] for U in Us],
+                               h0=h0[:, n, k - 1:])
+        assert np.abs(h[:, :, n, k - 1:] - last).max() > 1e-3  # the coupling is live
+
+
+def test_hgru_cell_jacobian_central_differences(orc):
+    rng = np.random.default_rng(16)
+    k = 5
+    p, Us, _ = _hgru_draw(17, 1, 1, 1, k)
+    args = [x[0, 0, 0] for x in p] + [U[0] for U in Us]
+    h = rng.standard_normal(k)
+    _, J, _ = orc.hgru_cell(h, *args)
+    eps = 1e-6
+    for l in range(k):
+        e = np.zeros(k)
+        e[l] = eps
+        fp, _, _ = orc.hgru_cell(h + e, *args)
+        fm, _, _ = orc.hgru_cell(h - e, *args)
+        np.testing.assert_allclose(J[:, l], (fp - fm) / (2 * eps), rtol=0, atol=1e-8)
+
+
+def test_hgru_bptt_central_differences(orc):
+    """Every gradient, dense Uc included, against central differences of
+    sum(g * h) through the rollout."""
+    B, L, NH, k = 1, 6, 2, 3
+    p, Us, h0 = _hgru_draw(18, B, L, NH, k)
+    g = np.random.default_rng(19).standard_normal((B, L, NH, k))
+    h = orc.hgru_rollout(*p, *Us, h0=h0)
+    got = orc.hgru_bptt(*p, *Us, h, g, h0=h0)
+    base = [*p, *Us, h0]
+    eps = 1e-6
+
+    def loss(vals):
+        return float((orc.hgru_rollout(*vals[:6], h0=vals[6]) * g).sum())
+
+    picks = [(0, (0, 2, 1, 0)), (1, (0, 4, 0, 2)), (2, (0, 5, 1, 1)), (3, (1, 0, 2)),
+             (4, (0, 2, 1)), (5, (1, 1, 0)), (5, (0, 0, 2)), (6, (0, 1, 2))]
+    for which, idx in picks:
+        vp = [x.copy() for x in base]
+        vm = [x.copy() for x in base]
+        vp[which][idx] += eps
+        vm[which][idx] -= eps
+        fd = (loss(vp) - loss(vm)) / (2 * eps)
+        assert abs(got[which][idx] - fd) <= 1e-7 * max(1.0, abs(fd)), (which, idx, got[which][idx], fd)
+
+
+def test_hgru_newton_prefix_exactness_and_convergence(orc):
+    """Newton with k x k block Jacobians from s = 0: after n iterations the
+    first n positions are the rollout's; after L iterations all are; with a
+    tolerance it converges to the rollout in far fewer."""
+    B, L, NH, k = 2, 9, 2, 8
+    p, Us, h0 = _hgru_draw(20, B, L, NH, k)
+    ref = orc.hgru_rollout(*p, *Us, h0=h0)
+    for n in (1, 3, 5):
+        s, it, _, _ = orc.hgru_newton(*p, *Us, h0=h0, tol=0.0, cap=n)
+        assert it == n
+        np.testing.assert_allclose(s[:, :n], ref[:, :n], rtol=0, atol=1e-13)
+        if n == 1:  # the first iterate is not yet the rollout beyond position 0
+            assert np.abs(s[:, n:] - ref[:, n:]).max() > 1e-3
+    s, it, conv, _ = orc.hgru_newton(*p, *Us, h0=h0, tol=0.0, cap=L)
+    np.testing.assert_allclose(s, ref, rtol=0, atol=1e-13)
+    p2, Us2, h02 = _hgru_draw(21, 2, 300, 2, 8)
+    s, it, conv, trace = orc.hgru_newton(*p2, *Us2, h0=h02, tol=1e-10, cap=64)
+    assert conv == 1 and it < 20
+    np.testing.assert_allclose(s, orc.hgru_rollout(*p2, *Us2, h0=h02), rtol=0, atol=1e-9)

@@ -94,3 +94,26 @@ def lstm_rollout(pi, pf, po, pg, ui, uf, uo, ug, h0=None, c0=None):
             hs.append(h)
             cs.append(c)
     return torch.stack(hs, 1).numpy(), torch.stack(cs, 1).numpy()
+
+
+def _blockdiag(U):
+    """[NH, k, k] -> the [NH*k, NH*k] block-diagonal matrix."""
+    return torch.block_diag(*[_t(u) for u in np.asarray(U)])
+
+
+def make_hgru(NH, k, Uz, Ur, Uc):
+    """torch.nn.GRU computing the GRU with dense recurrence inside heads of k
+    channels, for a diagonal Uc: torch applies r after its recurrent matrix,
+    r*(W_hn h), which equals Uc (r*h) only when Uc is diagonal.  Uz and Ur
+    may be dense: W_hz = blockdiag(-Uz), W_hr = blockdiag(Ur)."""
+    H = NH * k
+    m = torch.nn.GRU(input_size=3 * H, hidden_size=H, batch_first=True,
+                     bias=False, dtype=torch.float64)
+    with torch.no_grad():
+        m.weight_ih_l0.copy_(torch.eye(3 * H, dtype=torch.float64))
+        whh = torch.zeros(3 * H, H, dtype=torch.float64)
+        whh[0:H] = _blockdiag(Ur)
+        whh[H:2 * H] = -_blockdiag(Uz)
+        whh[2 * H:3 * H] = _blockdiag(Uc)
+        m.weight_hh_l0.copy_(whh)
+    return m
