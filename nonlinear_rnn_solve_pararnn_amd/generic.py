@@ -1,24 +1,27 @@
-"""Newton solve for user-defined cells whose Jacobian is diagonal over the
-channels: one state value per channel (diagonal Jacobian) or two (2x2 blocks).
+"""Newton solve for user-defined cells whose Jacobian is block-diagonal over
+the channels: one state value per channel (diagonal Jacobian), or k per
+channel or head (k x k blocks, k = 2, 4 or 8).
 
 A cell is any function ``cell(s_prev, *inputs, *params) -> s`` written with
-torch operations that acts channel by channel: the state of channel j depends
-on the state of channel j only (and on anything in the inputs and
-parameters).  With ``state_size=1`` states are [B, L, H]; with
-``state_size=2`` they are [B, L, H, 2] (an LSTM-like cell with (c, h) per
-channel).  The whole sequence s_t = cell(s_{t-1}, x_t) is then solved by
-Newton's method (ParaRNN page, TL;DR and abstract: Newton iterations on the
-whole-sequence system, diagonal and 2x2 block-diagonal Jacobians; a framework
-for parallelising new nonlinear RNNs; DEER summary page, method paragraph:
-the same for any differentiable recurrence, tolerance the only extra
+torch operations whose state of channel (or head) j depends on the state of
+j only (and on anything in the inputs and parameters).  With
+``state_size=1`` states are [B, L, H]; with ``state_size=k`` they are
+[B, L, H, k]: an LSTM-like cell with (c, h) per channel (k = 2), or a cell
+with dense recurrence inside heads of k channels (head_gru_cell below, the
+GRU with 8-channel heads of the DEER summary page's limitations paragraph).
+The whole sequence s_t = cell(s_{t-1}, x_t) is then solved by Newton's
+method (ParaRNN page, TL;DR and abstract: Newton iterations on the
+whole-sequence system, diagonal and block-diagonal Jacobians; a framework for
+parallelising new nonlinear RNNs; DEER summary page, method paragraph: the
+same for any differentiable recurrence, tolerance the only extra
 hyper-parameter).  This is the modality in which the system is assembled by
 the framework's tensor operations and only the parallel reduction runs in a
 dedicated kernel (ParaRNN page, Fig. 5 caption): each iteration evaluates the
 cell and its Jacobian blocks with torch (forward-mode differentiation, one
 tangent per state component), and solves the block bi-diagonal linear system
-with the library's diagonal or 2x2 scan (rnn_linscan_diag, rnn_linscan_blk2).
-Cells with a built-in kernel (GRU, LSTM) are much faster through
-pararnn_gru_forward / pararnn_lstm_forward.
+with the library's diagonal, 2x2 or k x k scan (rnn_linscan_diag,
+rnn_linscan_blk2, rnn_linscan_blk).  Cells with a built-in kernel (GRU, LSTM)
+are much faster through pararnn_gru_forward / pararnn_lstm_forward.
 
 Stopping: the convergence decision is taken on the device.  Each iteration
 computes max|delta| there and clears a device flag once it is <= tol; every
@@ -68,11 +71,34 @@ def _cell_and_jacobian(cell, sp, inputs, params, k):
 def _scan(J, b, k):
     if k == 1:
         return api.linscan_diag(J.contiguous(), b.contiguous())
-    return api.linscan_blk2(J.contiguous(), b.contiguous())
+    if k == 2:
+        return api.linscan_blk2(J.contiguous(), b.contiguous())
+    return api.linscan_blk(J.contiguous(), b.contiguous())
+
+
+STATE_SIZES = (1, 2, 4, 8)
+
+
+def head_gru_cell(s, pz, pr, pc, Uz, Ur, Uc):
+    """GRU with dense recurrence inside heads of k channels: the diagonal GRU
+    cell with each weight vector replaced by one k x k matrix per head, acting
+    on the state where the diagonal cell multiplies by u (a diagonal U gives
+    the diagonal cell):
+        z = sig(pz + Uz s), r = sig(pr + Ur s), c = tanh(pc + Uc (r*s)),
+        s' = (1 - z)*s + z*c.
+    s, p: [B, L, NH, k]; U: [NH, k, k] (U[n, i, l] takes component l into i).
+    Its Jacobian blocks are dense k x k (DEER summary page, limitations
+    paragraph); solve it with newton_solve(..., state_size=k)."""
+    def mv(U, v):
+        return torch.matmul(U, v.unsqueeze(-1)).squeeze(-1)
+    z = torch.sigmoid(pz + mv(Uz, s))
+    r = torch.sigmoid(pr + mv(Ur, s))
+    c = torch.tanh(pc + mv(Uc, r * s))
+    return (1 - z) * s + z * c
 
 
 def _solve(cell, inputs, params, h0, tol, max_iter, info, k):
-    B, L, H = inputs[0].shape
+    B, L, H = inputs[0].shape[:3]
     shape = (B, L, H) if k == 1 else (B, L, H, k)
     s = torch.zeros(shape, dtype=inputs[0].dtype, device=inputs[0].device)
     dev = s.device
@@ -141,29 +167,31 @@ def newton_solve(cell: Callable[..., torch.Tensor], inputs: Sequence[torch.Tenso
                  state_size: int = 1) -> torch.Tensor:
     """Solve s_t = cell(s_{t-1}, *inputs_t, *params) over the whole sequence.
 
-    inputs: tensors [B, L, H] (fp32, on a HIP device) passed to the cell
-    position-wise; params: tensors the cell uses as they are (weights,
-    broadcast against the state); state_size: 1 (states [B, L, H]) or 2
-    (states [B, L, H, 2]); h0: [B, H] or [B, H, 2], or None (zeros).  Newton
-    starts from s = 0 and stops once max|delta| <= tol or after max_iter
-    updates; `info`, if a list of two, receives [iterations, converged].
-    Returns the states, differentiable with respect to inputs, params and h0
-    through the adjoint of the solve."""
+    inputs: tensors [B, L, H] or [B, L, H, state_size] (fp32, on a HIP
+    device) passed to the cell position-wise; params: tensors the cell uses as
+    they are (weights, broadcast against the state); state_size: 1 (states
+    [B, L, H]) or k = 2, 4, 8 (states [B, L, H, k], k x k Jacobian blocks);
+    h0: [B, H] or [B, H, k], or None (zeros).  Newton starts from s = 0 and
+    stops once max|delta| <= tol or after max_iter updates; `info`, if a list
+    of two, receives [iterations, converged].  Returns the states,
+    differentiable with respect to inputs, params and h0 through the adjoint
+    of the solve."""
     if not inputs:
         raise ValueError("at least one input sequence is needed")
-    if state_size not in (1, 2):
-        raise ValueError("state_size must be 1 or 2")
+    if state_size not in STATE_SIZES:
+        raise ValueError("state_size must be one of %s" % (STATE_SIZES,))
     x0 = inputs[0]
     if x0.device.type != "cuda":
         raise ValueError("newton_solve runs on a HIP device only; inputs are on %s" % x0.device)
-    if x0.dim() != 3:
-        raise ValueError("inputs must be [B, L, H]")
+    if x0.dim() not in (3, 4):
+        raise ValueError("inputs must be [B, L, H] or [B, L, H, state_size]")
     if not tol >= 0.0 or max_iter < 1:
         raise ValueError("tol must be >= 0 and max_iter >= 1")
-    B, L, H = x0.shape
+    B, L, H = x0.shape[:3]
+    shapes = ((B, L, H), (B, L, H, state_size))
     for x in inputs:
-        if tuple(x.shape) != (B, L, H):
-            raise ValueError("every input must be [B, L, H]")
+        if tuple(x.shape) not in shapes:
+            raise ValueError("every input must be [B, L, H] or [B, L, H, %d]" % state_size)
     hshape = (B, H) if state_size == 1 else (B, H, state_size)
     if h0 is None:
         h0 = torch.zeros(hshape, dtype=x0.dtype, device=x0.device)

@@ -88,6 +88,27 @@ def gru_inputs(B, L, H, seed, pscale=1.0, ulo=-0.5, uhi=0.5, h0=False,
     return out
 
 
+def head_gru_inputs(B, L, NH, k, seed, h0=False, grad=False):
+    """Draws for the GRU with dense recurrence inside heads of k channels:
+    pz, pr, pc ~ N(0,1) [B,L,NH,k]; Uz, Ur, Uc [NH,k,k] with diagonal
+    U(-0.5,0.5) (the diagonal cell's u) and off-diagonal U(-0.3,0.3)/sqrt(k);
+    then optionally h0 ~ U(-0.9,0.9) [B,NH,k] and g ~ N(0,1) [B,L,NH,k]."""
+    rng = _rng(seed)
+    out = {}
+    for key in ("pz", "pr", "pc"):
+        out[key] = _normal(rng, (B, L, NH, k))
+    for key in ("Uz", "Ur", "Uc"):
+        off = _uniform(rng, (NH, k, k), -0.3, 0.3) / np.float32(np.sqrt(k))
+        diag = _uniform(rng, (NH, k), -0.5, 0.5)
+        idx = np.arange(k)
+        off[:, idx, idx] = diag
+        out[key] = off.astype(np.float32)
+    out["h0"] = _uniform(rng, (B, NH, k), -0.9, 0.9) if h0 else np.zeros((B, NH, k), np.float32)
+    if grad:
+        out["g"] = _normal(rng, (B, L, NH, k))
+    return out
+
+
 def lstm_inputs(B, L, H, seed, pscale=1.0, ulo=-0.5, uhi=0.5, h0=False,
                 grad=False, zero_u=False):
     """LSTM draws: pi, pf, po, pg ~ pscale*N(0,1) [B,L,H]; ui, uf, uo, ug ~ U(ulo,uhi);

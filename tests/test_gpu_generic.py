@@ -170,3 +170,49 @@ def test_generic_stops_on_the_device_one_iteration_late(orc):
         say(tol, cap, info, (it, conv))
         assert abs(info[0] - it) <= (1 if tol > 0 else 0) and info[1] == conv
         assert max_abs(host(h), s) <= (FWD_ATOL if tol > 0 else 1e-5)
+
+
+# ---------------------------------------------------------------- k x k blocks
+def _hgru(d):
+    return [d[x] for x in ("pz", "pr", "pc", "Uz", "Ur", "Uc")]
+
+
+@pytest.mark.parametrize("B,L,NH,k", [(2, 300, 3, 8), (2, 700, 5, 4), (1, 64, 1, 8), (2, 2000, 16, 8),
+                                      (1, 3000, 2, 8)])
+def test_generic_head_gru_matches_oracle(orc, B, L, NH, k):
+    """The GRU with dense recurrence inside heads of k channels: k x k Jacobian
+    blocks from torch, solved by the k x k scan; forward and every gradient
+    (p, U, h0) against the oracle's rollout and backpropagation."""
+    say("generic head gru", B, L, NH, k)
+    d = synth.head_gru_inputs(B, L, NH, k, seed=550 + NH * k, h0=True, grad=True)
+    p = [dev(d[x]).requires_grad_(True) for x in ("pz", "pr", "pc")]
+    U = [dev(d[x]).requires_grad_(True) for x in ("Uz", "Ur", "Uc")]
+    h0 = dev(d["h0"]).requires_grad_(True)
+    info = [0, 0]
+    h = generic.newton_solve(generic.head_gru_cell, p, h0, U, tol=1e-6, max_iter=64, info=info,
+                             state_size=k)
+    href = orc.hgru_rollout(*_hgru(d), h0=d["h0"])
+    err = max_abs(host(h), href)
+    (h * dev(d["g"])).sum().backward()
+    ref = orc.hgru_bptt(*_hgru(d), href, d["g"], h0=d["h0"])
+    got = [x.grad for x in p + U] + [h0.grad]
+    names = ["dpz", "dpr", "dpc", "dUz", "dUr", "dUc", "dh0"]
+    errs = {n: rel_inf(host(g), r) for n, g, r in zip(names, got, ref)}
+    say(info, err, errs)
+    assert info[1] == 1 and err <= FWD_ATOL
+    assert max(errs.values()) <= GRAD_RTOL, errs
+
+
+def test_generic_head_gru_iterates_equal_oracle_newton(orc):
+    """tol = 0 and a cap of n: the n-th Newton iterate (k x k blocks) equals
+    the oracle's."""
+    d = synth.head_gru_inputs(2, 300, 3, 8, seed=560, h0=True)
+    t = [dev(x) for x in _hgru(d)]
+    for n in (1, 2, 3):
+        info = [0, 0]
+        s = generic.newton_solve(generic.head_gru_cell, t[:3], dev(d["h0"]), t[3:], tol=0.0,
+                                 max_iter=n, info=info, state_size=8)
+        ref, it, _, _ = orc.hgru_newton(*_hgru(d), h0=d["h0"], tol=0.0, cap=n)
+        err = max_abs(host(s), ref)
+        say(n, info, it, err)
+        assert info[0] == n == it and err <= 1e-5
