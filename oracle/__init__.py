@@ -55,17 +55,17 @@ def _load():
     lib.orc_lstm_cell.argtypes = [ctypes.c_double] * 10 + [vp, vp, vp, vp, vp]
     lib.orc_gru_rollout.argtypes = [_I64, _I64, _I64] + [vp] * 8
     lib.orc_lstm_rollout.argtypes = [_I64, _I64, _I64] + [vp] * 12
-    lib.orc_gru_newton.argtypes = [_I64, _I64, _I64] + [vp] * 7 + [
+    lib.orc_gru_newton.argtypes = [_I64, _I64, _I64] + [vp] * 8 + [
         ctypes.c_double, ctypes.c_int, vp, vp, vp]
     lib.orc_gru_newton.restype = ctypes.c_int
-    lib.orc_lstm_newton.argtypes = [_I64, _I64, _I64] + [vp] * 10 + [
+    lib.orc_lstm_newton.argtypes = [_I64, _I64, _I64] + [vp] * 12 + [
         ctypes.c_double, ctypes.c_int, vp, vp, vp, vp]
     lib.orc_lstm_newton.restype = ctypes.c_int
     lib.orc_gru_bptt.argtypes = [_I64, _I64, _I64] + [vp] * 16
     lib.orc_lstm_bptt.argtypes = [_I64, _I64, _I64] + [vp] * 24
     lib.orc_hgru_cell.argtypes = [ctypes.c_int] + [vp] * 10
     lib.orc_hgru_rollout.argtypes = [_I64, _I64, _I64, ctypes.c_int] + [vp] * 8
-    lib.orc_hgru_newton.argtypes = [_I64, _I64, _I64, ctypes.c_int] + [vp] * 7 + [
+    lib.orc_hgru_newton.argtypes = [_I64, _I64, _I64, ctypes.c_int] + [vp] * 8 + [
         ctypes.c_double, ctypes.c_int, vp, vp, vp]
     lib.orc_hgru_newton.restype = ctypes.c_int
     lib.orc_hgru_bptt.argtypes = [_I64, _I64, _I64, ctypes.c_int] + [vp] * 16
@@ -174,33 +174,40 @@ def lstm_rollout(pi, pf, po, pg, ui, uf, uo, ug, h0=None, c0=None):
 
 
 # ----------------------------------------------------------------- Newton
-def gru_newton(pz, pr, pc, uz, ur, uc, h0=None, tol=1e-6, cap=64):
-    """CPU Newton from s = 0.  Returns (s, iterations, converged, trace[iters])."""
+def gru_newton(pz, pr, pc, uz, ur, uc, h0=None, tol=1e-6, cap=64, init=None):
+    """CPU Newton from s = 0, or from the iterate `init` [B, L, H].  Returns
+    (s, iterations, converged, trace[iters])."""
     pz, pr, pc = _f64(pz), _f64(pr), _f64(pc)
     uz, ur, uc, h0 = _f64(uz), _f64(ur), _f64(uc), _f64(h0)
+    init = _f64(init)
     B, L, H = pz.shape
+    assert init is None or init.shape == (B, L, H)
     s = np.empty_like(pz)
     conv = np.zeros(1, np.int32)
     trace = np.zeros(max(cap, 1))
     it = _load().orc_gru_newton(B, L, H, _p(pz), _p(pr), _p(pc), _p(uz),
-                                _p(ur), _p(uc), _p(h0), float(tol), int(cap),
+                                _p(ur), _p(uc), _p(h0), _p(init), float(tol), int(cap),
                                 _p(s), conv.ctypes.data_as(ctypes.c_void_p),
                                 _p(trace))
     return s, int(it), int(conv[0]), trace[:it].copy()
 
 
-def lstm_newton(pi, pf, po, pg, ui, uf, uo, ug, h0=None, c0=None, tol=1e-4, cap=32):
-    """CPU Newton on (c, h) from 0.  Returns (h, c, iterations, converged, trace)."""
+def lstm_newton(pi, pf, po, pg, ui, uf, uo, ug, h0=None, c0=None, tol=1e-4, cap=32,
+                h_init=None, c_init=None):
+    """CPU Newton on (c, h) from 0, or from the iterates h_init, c_init
+    [B, L, H] (zero where None).  Returns (h, c, iterations, converged, trace)."""
     ps = [_f64(x) for x in (pi, pf, po, pg)]
     us = [_f64(x) for x in (ui, uf, uo, ug)]
     h0, c0 = _f64(h0), _f64(c0)
+    h_init, c_init = _f64(h_init), _f64(c_init)
     B, L, H = ps[0].shape
     h = np.empty_like(ps[0])
     c = np.empty_like(ps[0])
     conv = np.zeros(1, np.int32)
     trace = np.zeros(max(cap, 1))
     it = _load().orc_lstm_newton(B, L, H, *[_p(x) for x in ps], *[_p(x) for x in us],
-                                 _p(h0), _p(c0), float(tol), int(cap), _p(h), _p(c),
+                                 _p(h0), _p(c0), _p(h_init), _p(c_init), float(tol), int(cap),
+                                 _p(h), _p(c),
                                  conv.ctypes.data_as(ctypes.c_void_p), _p(trace))
     return h, c, int(it), int(conv[0]), trace[:it].copy()
 
@@ -266,17 +273,18 @@ def hgru_rollout(pz, pr, pc, Uz, Ur, Uc, h0=None):
     return h
 
 
-def hgru_newton(pz, pr, pc, Uz, Ur, Uc, h0=None, tol=1e-6, cap=64):
-    """CPU Newton for the head GRU from s = 0 (k x k block Jacobians).
-    Returns (s, iterations, converged, trace[iters])."""
+def hgru_newton(pz, pr, pc, Uz, Ur, Uc, h0=None, tol=1e-6, cap=64, init=None):
+    """CPU Newton for the head GRU from s = 0 or from `init` (k x k block
+    Jacobians).  Returns (s, iterations, converged, trace[iters])."""
     pz, pr, pc = _f64(pz), _f64(pr), _f64(pc)
     Uz, Ur, Uc, h0 = _f64(Uz), _f64(Ur), _f64(Uc), _f64(h0)
+    init = _f64(init)
     B, L, NH, k = pz.shape
     s = np.empty_like(pz)
     conv = np.zeros(1, np.int32)
     trace = np.zeros(max(cap, 1))
     it = _load().orc_hgru_newton(B, L, NH, k, _p(pz), _p(pr), _p(pc), _p(Uz), _p(Ur), _p(Uc),
-                                 _p(h0), float(tol), int(cap), _p(s),
+                                 _p(h0), _p(init), float(tol), int(cap), _p(s),
                                  conv.ctypes.data_as(ctypes.c_void_p), _p(trace))
     return s, int(it), int(conv[0]), trace[:it].copy()
 

@@ -265,6 +265,9 @@ void orc_lstm_rollout(int64_t B, int64_t L, int64_t H,
  *   as +inf); stop when e_k <= tol or k = cap.
  * Returns the number of iterations applied; *converged is 1 when the last
  * e_k <= tol.  trace (length cap, may be NULL) receives e_1..e_iters.
+ * s_init (may be NULL) replaces the zero start: the same iteration from a
+ * given whole-sequence iterate s^0 (a warm start); iterate n from s^0 = the
+ * k-th iterate from zero is the (k+n)-th iterate from zero.
  * ------------------------------------------------------------------------- */
 static double absmax_update(double m, double d)
 {
@@ -276,13 +279,16 @@ static double absmax_update(double m, double d)
 int orc_gru_newton(int64_t B, int64_t L, int64_t H,
                    const double *pz, const double *pr, const double *pc,
                    const double *uz, const double *ur, const double *uc,
-                   const double *h0, double tol, int cap, double *s,
-                   int *converged, double *trace)
+                   const double *h0, const double *s_init, double tol, int cap,
+                   double *s, int *converged, double *trace)
 {
     size_t N = (size_t)B * (size_t)L * (size_t)H;
     double *F = (double *)malloc(N * sizeof(double));
     double *Jm = (double *)malloc(N * sizeof(double));
-    memset(s, 0, N * sizeof(double));
+    if (s_init)
+        memcpy(s, s_init, N * sizeof(double));
+    else
+        memset(s, 0, N * sizeof(double));
     *converged = 0;
     int k;
     for (k = 1; k <= cap; ++k) {
@@ -326,15 +332,23 @@ int orc_lstm_newton(int64_t B, int64_t L, int64_t H,
                     const double *pi, const double *pf, const double *po,
                     const double *pg, const double *ui, const double *uf,
                     const double *uo, const double *ug, const double *h0,
-                    const double *c0, double tol, int cap, double *h, double *c,
+                    const double *c0, const double *h_init, const double *c_init,
+                    double tol, int cap, double *h, double *c,
                     int *converged, double *trace)
 {
     size_t N = (size_t)B * (size_t)L * (size_t)H;
     double *Fc = (double *)malloc(N * sizeof(double));
     double *Fh = (double *)malloc(N * sizeof(double));
     double *Jm = (double *)malloc(4 * N * sizeof(double));
-    memset(h, 0, N * sizeof(double));
-    memset(c, 0, N * sizeof(double));
+    /* initial iterate: the given (h, c) trajectories, zero where NULL */
+    if (h_init)
+        memcpy(h, h_init, N * sizeof(double));
+    else
+        memset(h, 0, N * sizeof(double));
+    if (c_init)
+        memcpy(c, c_init, N * sizeof(double));
+    else
+        memset(c, 0, N * sizeof(double));
     *converged = 0;
     int k;
     for (k = 1; k <= cap; ++k) {
@@ -580,19 +594,22 @@ void orc_hgru_rollout(int64_t B, int64_t L, int64_t NH, int k,
         }
 }
 
-/* Newton's method for the head GRU from s = 0, as orc_gru_newton: the
+/* Newton's method for the head GRU from s = 0 (or s_init), as orc_gru_newton: the
    linearised system is block bi-diagonal with the k x k Jacobians of the
    cell, solved by forward substitution delta_t = J_t delta_{t-1} - r_t. */
 int orc_hgru_newton(int64_t B, int64_t L, int64_t NH, int k,
                     const double *pz, const double *pr, const double *pc,
                     const double *Uz, const double *Ur, const double *Uc,
-                    const double *h0, double tol, int cap, double *s,
-                    int *converged, double *trace)
+                    const double *h0, const double *s_init, double tol, int cap,
+                    double *s, int *converged, double *trace)
 {
     size_t N = (size_t)B * (size_t)L * (size_t)NH * (size_t)k;
     double *F = (double *)malloc(N * sizeof(double));
     double *Jm = (double *)malloc(N * (size_t)k * sizeof(double));
-    memset(s, 0, N * sizeof(double));
+    if (s_init)
+        memcpy(s, s_init, N * sizeof(double));
+    else
+        memset(s, 0, N * sizeof(double));
     *converged = 0;
     int it;
     for (it = 1; it <= cap; ++it) {

@@ -625,3 +625,44 @@ def test_hgru_newton_prefix_exactness_and_convergence(orc):
     s, it, conv, trace = orc.hgru_newton(*p2, *Us2, h0=h02, tol=1e-10, cap=64)
     assert conv == 1 and it < 20
     np.testing.assert_allclose(s, orc.hgru_rollout(*p2, *Us2, h0=h02), rtol=0, atol=1e-9)
+
+
+
+# ---------------------------------------------------------------- warm start
+def test_newton_warm_start_continues_the_cold_iteration(orc):
+    """Newton from a given iterate is the same map: n iterations from the
+    k-th iterate from zero equal k + n iterations from zero (GRU, LSTM, head
+    GRU); a warm start at the rollout stops after one zero update."""
+    d = synth.gru_inputs(2, 60, 5, seed=70, h0=True)
+    a = [d[x] for x in ("pz", "pr", "pc", "uz", "ur", "uc")]
+    for kk, n in ((1, 2), (2, 1), (3, 3)):
+        sk, _, _, _ = orc.gru_newton(*a, h0=d["h0"], tol=0.0, cap=kk)
+        warm, it, _, _ = orc.gru_newton(*a, h0=d["h0"], tol=0.0, cap=n, init=sk)
+        cold, _, _, _ = orc.gru_newton(*a, h0=d["h0"], tol=0.0, cap=kk + n)
+        assert it == n
+        np.testing.assert_allclose(warm, cold, rtol=0, atol=1e-14)
+    ref = orc.gru_rollout(*a, h0=d["h0"])
+    s, it, conv, trace = orc.gru_newton(*a, h0=d["h0"], tol=1e-12, cap=10, init=ref)
+    assert (it, conv) == (1, 1) and trace[0] <= 1e-14
+    np.testing.assert_allclose(s, ref, rtol=0, atol=1e-14)
+
+    dl = synth.lstm_inputs(2, 50, 4, seed=71, h0=True)
+    al = [dl[x] for x in ("pi", "pf", "po", "pg", "ui", "uf", "uo", "ug")]
+    hk, ck, _, _, _ = orc.lstm_newton(*al, h0=dl["h0"], c0=dl["c0"], tol=0.0, cap=2)
+    hw, cw, it, _, _ = orc.lstm_newton(*al, h0=dl["h0"], c0=dl["c0"], tol=0.0, cap=2,
+                                       h_init=hk, c_init=ck)
+    hc, cc, _, _, _ = orc.lstm_newton(*al, h0=dl["h0"], c0=dl["c0"], tol=0.0, cap=4)
+    np.testing.assert_allclose(hw, hc, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(cw, cc, rtol=0, atol=1e-14)
+    # only one component given: the other starts at zero (as a cold start has it)
+    h1, c1, _, _, _ = orc.lstm_newton(*al, h0=dl["h0"], c0=dl["c0"], tol=0.0, cap=1)
+    hz, cz, _, _, _ = orc.lstm_newton(*al, h0=dl["h0"], c0=dl["c0"], tol=0.0, cap=1,
+                                      h_init=np.zeros_like(h1))
+    np.testing.assert_allclose(hz, h1, rtol=0, atol=0)
+    np.testing.assert_allclose(cz, c1, rtol=0, atol=0)
+
+    p, Us, h0 = _hgru_draw(72, 2, 30, 2, 8)
+    sk, _, _, _ = orc.hgru_newton(*p, *Us, h0=h0, tol=0.0, cap=2)
+    warm, _, _, _ = orc.hgru_newton(*p, *Us, h0=h0, tol=0.0, cap=2, init=sk)
+    cold, _, _, _ = orc.hgru_newton(*p, *Us, h0=h0, tol=0.0, cap=4)
+    np.testing.assert_allclose(warm, cold, rtol=0, atol=1e-14)
