@@ -145,10 +145,16 @@ int rnn_linscan_blk(int32_t k, int64_t B, int64_t L, int64_t H,
  * GRU-style cell with diagonal recurrence (ParaGRU, ParaRNN page Fig. 2):
  *   z = sigmoid(pz + uz*h), r = sigmoid(pr + ur*h),
  *   c = tanh(pc + uc*(r*h)),  h' = (1 - z)*h + z*c
- * evaluated over the whole sequence by Newton's method from h = 0
- * (ParaRNN TL;DR; DEER summary).  pz, pr, pc: [B, L, H] gate
- * pre-projections (input projections and biases already applied).
- * uz, ur, uc: [H].  h0: [B, H] or NULL.  h: [B, L, H] output.
+ * evaluated over the whole sequence by Newton's method (ParaRNN TL;DR;
+ * DEER summary), from h = 0 or from a given initial iterate.
+ * pz, pr, pc: [B, L, H] gate pre-projections (input projections and biases
+ * already applied).  uz, ur, uc: [H].  h0: [B, H] or NULL.
+ * h_init: [B, L, H] initial iterate (a warm start, such as the solution of a
+ * nearby input), or NULL for zeros; read only, and it must not overlap h
+ * (PARARNN_ERR_INVALID).  Newton from any iterate is exact after L
+ * iterations, so the cap rule below holds for warm starts too; a start that
+ * already solves the system returns after one iteration with a zero update.
+ * h: [B, L, H] output.
  * tol >= 0: Newton stops once max|delta| <= tol (the only extra
  * hyper-parameter; DEER summary, second paragraph), measured after the
  * update and absolute.  Where the test is taken depends on the kernel:
@@ -171,8 +177,8 @@ int rnn_linscan_blk(int32_t k, int64_t B, int64_t L, int64_t H,
 int pararnn_gru_forward(int64_t B, int64_t L, int64_t H,
                         const float *pz, const float *pr, const float *pc,
                         const float *uz, const float *ur, const float *uc,
-                        const float *h0, float *h, float tol, int32_t max_iter,
-                        int32_t *info, float *trace,
+                        const float *h0, const float *h_init, float *h, float tol,
+                        int32_t max_iter, int32_t *info, float *trace,
                         void *ws, size_t ws_bytes, void *stream);
 
 /*
@@ -180,7 +186,9 @@ int pararnn_gru_forward(int64_t B, int64_t L, int64_t H,
  * per channel the state is (c, h) and the Jacobian a 2x2 block.
  *   i = sigmoid(pi + ui*h'), f = sigmoid(pf + uf*h'), o = sigmoid(po + uo*h'),
  *   g = tanh(pg + ug*h'),  c = f*c' + i*g,  h = o*tanh(c)
- * Newton from (c, h) = 0; max|delta| is taken over both components.
+ * Newton from (c, h) = 0, or from the initial iterates h_init, c_init
+ * ([B, L, H] each, a NULL one taken as zeros; read only, neither may overlap
+ * h or c); max|delta| is taken over both components.
  * pi, pf, po, pg: [B, L, H]; ui, uf, uo, ug: [H]; h0, c0: [B, H] or NULL;
  * h, c: [B, L, H] outputs.  tol, max_iter, info, trace as for the GRU,
  * except that this cell has no single-tile kernel: the chunk rule applies at
@@ -190,8 +198,9 @@ int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H,
                          const float *pi, const float *pf, const float *po,
                          const float *pg, const float *ui, const float *uf,
                          const float *uo, const float *ug, const float *h0,
-                         const float *c0, float *h, float *c, float tol,
-                         int32_t max_iter, int32_t *info, float *trace,
+                         const float *c0, const float *h_init, const float *c_init,
+                         float *h, float *c, float tol, int32_t max_iter,
+                         int32_t *info, float *trace,
                          void *ws, size_t ws_bytes, void *stream);
 
 /*
@@ -246,8 +255,8 @@ int pararnn_lstm_sequential(int64_t B, int64_t L, int64_t H,
 /*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the GRU
- * Newton forward of pararnn_gru_forward, with the same arguments, results
- * and errors, but no workspace argument.  Its workspace is a static device
+ * Newton forward of pararnn_gru_forward from h = 0 (no initial iterate),
+ * with its other arguments, results and errors, but no workspace argument.  Its workspace is a static device
  * array of the library, PARARNN_NOALLOC_SCRATCH_BYTES bytes on each device
  * it runs on, held until the process ends.  The first call on a device looks
  * up the array's address (with that device current) and zero-fills it with

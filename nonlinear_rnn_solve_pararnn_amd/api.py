@@ -55,10 +55,10 @@ def load_library():
     lib.rnn_linscan_blk2.restype = ctypes.c_int
     lib.rnn_linscan_blk.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, sz, vp]
     lib.rnn_linscan_blk.restype = ctypes.c_int
-    lib.pararnn_gru_forward.argtypes = [i64, i64, i64] + [vp] * 8 + [
+    lib.pararnn_gru_forward.argtypes = [i64, i64, i64] + [vp] * 9 + [
         ctypes.c_float, i32, vp, vp, vp, sz, vp]
     lib.pararnn_gru_forward.restype = ctypes.c_int
-    lib.pararnn_lstm_forward.argtypes = [i64, i64, i64] + [vp] * 12 + [
+    lib.pararnn_lstm_forward.argtypes = [i64, i64, i64] + [vp] * 14 + [
         ctypes.c_float, i32, vp, vp, vp, sz, vp]
     lib.pararnn_lstm_forward.restype = ctypes.c_int
     lib.pararnn_adjoint_backward.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -201,12 +201,13 @@ def linscan_blk(A, b, h0=None, *, out=None, ws=None):
 
 
 def gru_forward(pz, pr, pc, uz, ur, uc, h0=None, *, tol=1e-4, max_iter=32, out=None,
-                info=None, trace=None, ws=None):
+                info=None, trace=None, ws=None, init=None):
     """Newton solve of the diagonal GRU over [B, L, H] gate pre-projections.
 
-    Returns h [B, L, H].  `info` (int32[2] device tensor) receives
-    {iterations, converged}; `trace` (float32[max_iter]) receives max|delta|
-    per iteration."""
+    Returns h [B, L, H].  `init` [B, L, H] is Newton's initial iterate (a warm
+    start; None starts from zero; it must not share memory with the output).
+    `info` (int32[2] device tensor) receives {iterations, converged}; `trace`
+    (float32[max_iter]) receives max|delta| per iteration."""
     lib = load_library()
     B, L, H = pz.shape
     dev = pz.device
@@ -216,6 +217,8 @@ def gru_forward(pz, pr, pc, uz, ur, uc, h0=None, *, tol=1e-4, max_iter=32, out=N
         _need(t, (H,), n, dev)
     if h0 is not None:
         _need(h0, (B, H), "h0", dev)
+    if init is not None:
+        _need(init, (B, L, H), "init", dev)
     h = torch.empty_like(pz) if out is None else out
     _need(h, (B, L, H), "out", dev)
     if info is not None and (info.dtype != torch.int32 or info.numel() < 2 or info.device != dev):
@@ -225,15 +228,19 @@ def gru_forward(pz, pr, pc, uz, ur, uc, h0=None, *, tol=1e-4, max_iter=32, out=N
         raise ValueError("trace must be a float32 device tensor with max_iter elements")
     ws, n = _workspace(OP_GRU_FORWARD, B, L, H, dev, max_iter, ws)
     _check(lib.pararnn_gru_forward(B, L, H, _ptr(pz), _ptr(pr), _ptr(pc), _ptr(uz), _ptr(ur),
-                                   _ptr(uc), _ptr(h0), _ptr(h), float(tol), int(max_iter),
-                                   _ptr(info), _ptr(trace), _ptr(ws), n, _stream(dev)),
+                                   _ptr(uc), _ptr(h0), _ptr(init), _ptr(h), float(tol),
+                                   int(max_iter), _ptr(info), _ptr(trace), _ptr(ws), n,
+                                   _stream(dev)),
            "pararnn_gru_forward")
     return h
 
 
 def lstm_forward(pi, pf, po, pg, ui, uf, uo, ug, h0=None, c0=None, *, tol=1e-4, max_iter=32,
-                 out_h=None, out_c=None, info=None, trace=None, ws=None):
-    """Newton solve of the diagonal LSTM; returns (h, c), each [B, L, H]."""
+                 out_h=None, out_c=None, info=None, trace=None, ws=None, init_h=None,
+                 init_c=None):
+    """Newton solve of the diagonal LSTM; returns (h, c), each [B, L, H].
+    `init_h`, `init_c` [B, L, H]: Newton's initial iterates (a warm start; a
+    missing one is zero; neither may share memory with the outputs)."""
     lib = load_library()
     B, L, H = pi.shape
     dev = pi.device
@@ -245,6 +252,10 @@ def lstm_forward(pi, pf, po, pg, ui, uf, uo, ug, h0=None, c0=None, *, tol=1e-4, 
         _need(h0, (B, H), "h0", dev)
     if c0 is not None:
         _need(c0, (B, H), "c0", dev)
+    if init_h is not None:
+        _need(init_h, (B, L, H), "init_h", dev)
+    if init_c is not None:
+        _need(init_c, (B, L, H), "init_c", dev)
     h = torch.empty_like(pi) if out_h is None else out_h
     c = torch.empty_like(pi) if out_c is None else out_c
     _need(h, (B, L, H), "out_h", dev)
@@ -256,9 +267,10 @@ def lstm_forward(pi, pf, po, pg, ui, uf, uo, ug, h0=None, c0=None, *, tol=1e-4, 
         raise ValueError("trace must be a float32 device tensor with max_iter elements")
     ws, n = _workspace(OP_LSTM_FORWARD, B, L, H, dev, max_iter, ws)
     _check(lib.pararnn_lstm_forward(B, L, H, _ptr(pi), _ptr(pf), _ptr(po), _ptr(pg), _ptr(ui),
-                                    _ptr(uf), _ptr(uo), _ptr(ug), _ptr(h0), _ptr(c0), _ptr(h),
-                                    _ptr(c), float(tol), int(max_iter), _ptr(info), _ptr(trace),
-                                    _ptr(ws), n, _stream(dev)), "pararnn_lstm_forward")
+                                    _ptr(uf), _ptr(uo), _ptr(ug), _ptr(h0), _ptr(c0),
+                                    _ptr(init_h), _ptr(init_c), _ptr(h), _ptr(c), float(tol),
+                                    int(max_iter), _ptr(info), _ptr(trace), _ptr(ws), n,
+                                    _stream(dev)), "pararnn_lstm_forward")
     return h, c
 
 

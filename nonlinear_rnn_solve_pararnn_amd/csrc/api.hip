@@ -27,6 +27,13 @@ int status_of(hipError_t e) { return e == hipSuccess ? PARARNN_OK : PARARNN_ERR_
 
 bool grid_ok(int64_t ntiles) { return ntiles > 0 && ntiles < ((int64_t)1 << 31); }
 
+// Whether the n-float arrays at p and q share any byte (a null one shares none).
+bool overlaps(const float *p, const float *q, int64_t n) {
+    if (p == nullptr || q == nullptr) return false;
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q, len = (uintptr_t)n * sizeof(float);
+    return a < b + len && b < a + len;
+}
+
 // Zeros for trace entries [from, to) that no iteration will write.
 int clear_trace_tail(float *trace, int32_t from, int32_t to, hipStream_t s) {
     FillRange fr[1] = {{trace + from, (uint64_t)(to - from), 0, 4}};
@@ -193,12 +200,15 @@ int rnn_linscan_blk(int32_t k, int64_t B, int64_t L, int64_t H, const float *A, 
 
 int pararnn_gru_forward(int64_t B, int64_t L, int64_t H, const float *pz, const float *pr,
                         const float *pc, const float *uz, const float *ur, const float *uc,
-                        const float *h0, float *h, float tol, int32_t max_iter, int32_t *info,
-                        float *trace, void *ws, size_t ws_bytes, void *stream) {
+                        const float *h0, const float *h_init, float *h, float tol, int32_t max_iter,
+                        int32_t *info, float *trace, void *ws, size_t ws_bytes, void *stream) {
     if (!dims_ok(B, L, H) || !pz || !pr || !pc || !uz || !ur || !uc || !h) return PARARNN_ERR_INVALID;
     if (!(tol >= 0.0f) || max_iter < 1) return PARARNN_ERR_INVALID;  // rejects NaN too
+    if (overlaps(h_init, h, B * L * H)) return PARARNN_ERR_INVALID;
     const int32_t cap = eff_cap(max_iter, L);
-    GruFwdArgs a{B, L, H, pz, pr, pc, uz, ur, uc, h0, h, tol, cap, info, trace, env_chain_local("PARARNN_GRU_PATH")};
+    GruFwdArgs a{B,  L,   H,   pz,    pr,   pc,    uz,   ur,
+                 uc, h0,  h_init, h,  tol,  cap,   info, trace,
+                 env_chain_local("PARARNN_GRU_PATH")};
     hipStream_t s = static_cast<hipStream_t>(stream);
     const Path path = gru_path(L, cap);
     if (path == Path::Invalid) return PARARNN_ERR_UNSUPPORTED;
@@ -221,15 +231,19 @@ int pararnn_gru_forward(int64_t B, int64_t L, int64_t H, const float *pz, const 
 int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H, const float *pi, const float *pf,
                          const float *po, const float *pg, const float *ui, const float *uf,
                          const float *uo, const float *ug, const float *h0, const float *c0,
-                         float *h, float *c, float tol, int32_t max_iter, int32_t *info,
-                         float *trace, void *ws, size_t ws_bytes, void *stream) {
+                         const float *h_init, const float *c_init, float *h, float *c, float tol,
+                         int32_t max_iter, int32_t *info, float *trace, void *ws, size_t ws_bytes,
+                         void *stream) {
     if (!dims_ok(B, L, H) || !pi || !pf || !po || !pg || !ui || !uf || !uo || !ug || !h || !c)
         return PARARNN_ERR_INVALID;
     if (!(tol >= 0.0f) || max_iter < 1) return PARARNN_ERR_INVALID;
+    const int64_t n = B * L * H;
+    if (overlaps(h_init, h, n) || overlaps(h_init, c, n) || overlaps(c_init, h, n) || overlaps(c_init, c, n))
+        return PARARNN_ERR_INVALID;
     const int32_t cap = eff_cap(max_iter, L);
     if (!ws || ws_bytes < lstm_fwd_ws(B, L, H, cap) || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
-    LstmFwdArgs a{B, L, H, pi, pf, po, pg, ui, uf, uo, ug, h0, c0, h, c, tol, cap, info, trace,
-                  env_chain_local("PARARNN_LSTM_PATH")};
+    LstmFwdArgs a{B,  L,  H,      pi,     pf, po, pg,  ui,  uf,   uo,    ug,
+                  h0, c0, h_init, c_init, h,  c,  tol, cap, info, trace, env_chain_local("PARARNN_LSTM_PATH")};
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool chain = lstm_path(cap) == Path::Chain;
     if (!grid_ok(scan_shape(chain ? kCfgLstmChain : kCfgLstmStep, B, L, H).ntiles)) return PARARNN_ERR_INVALID;
@@ -247,7 +261,7 @@ int pararnn_gru_sequential(int64_t B, int64_t L, int64_t H, const float *pz, con
                            const float *h0, float *h, void *stream) {
     if (!dims_ok(B, L, H) || !pz || !pr || !pc || !uz || !ur || !uc || !h) return PARARNN_ERR_INVALID;
     if (!grid_ok((B * H + 63) / 64)) return PARARNN_ERR_INVALID;
-    GruFwdArgs a{B, L, H, pz, pr, pc, uz, ur, uc, h0, h, 0.0f, 1, nullptr, nullptr, -1};
+    GruFwdArgs a{B, L, H, pz, pr, pc, uz, ur, uc, h0, nullptr, h, 0.0f, 1, nullptr, nullptr, -1};
     return status_of(gru_rollout(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -258,7 +272,7 @@ int pararnn_lstm_sequential(int64_t B, int64_t L, int64_t H, const float *pi, co
     if (!dims_ok(B, L, H) || !pi || !pf || !po || !pg || !ui || !uf || !uo || !ug || !h || !c)
         return PARARNN_ERR_INVALID;
     if (!grid_ok((B * H + 63) / 64)) return PARARNN_ERR_INVALID;
-    LstmFwdArgs a{B, L, H, pi, pf, po, pg, ui, uf, uo, ug, h0, c0, h, c, 0.0f, 1, nullptr, nullptr, -1};
+    LstmFwdArgs a{B, L, H, pi, pf, po, pg, ui, uf, uo, ug, h0, c0, nullptr, nullptr, h, c, 0.0f, 1, nullptr, nullptr, -1};
     return status_of(lstm_rollout(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -33,6 +33,7 @@ constexpr float kE1 = -kLog2e, kE2 = -2.0f * kLog2e;
 struct FusedGruArgs {
     int64_t B, L, H, ncb;
     const float *pz, *pr, *pc, *uz, *ur, *uc, *h0;
+    const float *h_init;  // initial iterate [B, L, H], or null for zeros
     float *h;
     float tol;
     int32_t cap;
@@ -49,7 +50,8 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t n, int64_t ntiles) {
 }
 
 // Newton iterations on one tile held in registers.  x* are the pre-scaled
-// gate inputs (pz, pr by -log2 e; pc by -2 log2 e), hv receives the solution.
+// gate inputs (pz, pr by -log2 e; pc by -2 log2 e); hv holds the initial
+// iterate when `warm` (zero otherwise) and receives the solution.
 //
 // Arithmetic per position and iteration (h the previous state, hc the current
 // one): each gate is one fma, one exp2, one add and one reciprocal; then
@@ -62,7 +64,7 @@ template <int C, int NSUB, int CH, bool FULL>
 __device__ __forceinline__ void newton_on_tile(const float (&xz)[C], const float (&xr)[C],
                                                const float (&xc)[C], float (&hv)[C],
                                                const bool (&val)[C], bool ok, float uz, float ur,
-                                               float uc, float hinit, const FusedGruArgs &a,
+                                               float uc, float hinit, bool warm, const FusedGruArgs &a,
                                                int &iters, bool &conv) {
     constexpr int SUBW = 64 / CH;     // sub-chunks per wave
     constexpr int NW = NSUB / SUBW;   // waves of the workgroup
@@ -74,15 +76,21 @@ __device__ __forceinline__ void newton_on_tile(const float (&xz)[C], const float
     const int sub = w * SUBW + sl;
     const float uzs = kE1 * uz, urs = kE1 * ur, ucs = kE2 * uc;
     float Jv[C], bv[C];
+    if (warm) {
+        // the initial iterate's last state of every sub-chunk, for its successor
+        s_last[sub][ch] = hv[C - 1];
+        lds_barrier();
+    } else {
 #pragma unroll
-    for (int i = 0; i < C; ++i) hv[i] = 0.0f;
+        for (int i = 0; i < C; ++i) hv[i] = 0.0f;
+    }
     iters = 0;
     conv = false;
     for (int k = 1; k <= a.cap; ++k) {
         float hp = 0.0f;
         if (sub == 0)
             hp = hinit;
-        else if (k > 1)
+        else if (k > 1 || warm)
             hp = s_last[sub - 1][ch];
 
         Aff1 acc = {1.0f, 0.0f};
@@ -197,9 +205,15 @@ __global__ __launch_bounds__(kNW * 64, 4) void gru_fused_kernel(FusedGruArgs a) 
     }
     const float uz = ok ? a.uz[j] : 0.0f, ur = ok ? a.ur[j] : 0.0f, uc = ok ? a.uc[j] : 0.0f;
     const float hinit = (ok && a.h0 != nullptr) ? a.h0[b * H + j] : 0.0f;
+    const bool warm = a.h_init != nullptr;
+    if (warm) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) hv[i] = val[i] ? a.h_init[base + i * H] : 0.0f;
+    }
     int iters;
     bool conv;
-    newton_on_tile<C, kFusedSubchunks, kCh, FULL>(xz, xr, xc, hv, val, ok, uz, ur, uc, hinit, a, iters, conv);
+    newton_on_tile<C, kFusedSubchunks, kCh, FULL>(xz, xr, xc, hv, val, ok, uz, ur, uc, hinit, warm, a, iters,
+                                                  conv);
 #pragma unroll
     for (int i = 0; i < C; ++i)
         if (val[i]) a.h[base + i * H] = hv[i];
@@ -231,6 +245,7 @@ hipError_t gru_forward_fused(const GruFwdArgs &a, hipStream_t s) {
     fa.ur = a.ur;
     fa.uc = a.uc;
     fa.h0 = a.h0;
+    fa.h_init = a.h_init;
     fa.h = a.h;
     fa.tol = a.tol;
     fa.cap = a.cap;

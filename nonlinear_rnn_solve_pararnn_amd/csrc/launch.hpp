@@ -54,6 +54,7 @@ hipError_t linscan_blkrow(int k, int64_t B, int64_t L, int64_t H, const float *A
 struct GruFwdArgs {
     int64_t B, L, H;
     const float *pz, *pr, *pc, *uz, *ur, *uc, *h0;
+    const float *h_init;  // Newton's initial iterate [B, L, H], or null for zeros
     float *h;
     float tol;
     int32_t cap;
@@ -68,6 +69,7 @@ hipError_t gru_forward_chain(const GruFwdArgs &a, const Ws &ws, hipStream_t s);
 struct LstmFwdArgs {
     int64_t B, L, H;
     const float *pi, *pf, *po, *pg, *ui, *uf, *uo, *ug, *h0, *c0;
+    const float *h_init, *c_init;  // initial iterates [B, L, H]; a null one is zero
     float *h, *c;
     float tol;
     int32_t cap;

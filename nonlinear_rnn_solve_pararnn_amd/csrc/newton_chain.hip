@@ -60,6 +60,7 @@ constexpr float kE1 = -kLog2e, kE2 = -2.0f * kLog2e;
 struct GruChain {
     static constexpr int S = 1, NG = 3;
     const float *pz, *pr, *pc, *uz, *ur, *uc, *h0;
+    const float *h_init;  // initial iterate [B, L, H], or null for zeros
     float *h;
     bool runs;  // H == 1 with 16-byte aligned rows: whole runs move as float4
 
@@ -81,6 +82,9 @@ struct GruChain {
     __device__ float init(int64_t b, int64_t j, int64_t H) const {
         return h0 != nullptr ? h0[b * H + j] : 0.0f;
     }
+    __device__ bool warm() const { return h_init != nullptr; }
+    // element e of the initial iterate (warm starts only)
+    __device__ float guess(int64_t e) const { return h_init[e]; }
     template <int C>
     __device__ void load(int64_t base, int64_t H, const bool (&val)[C], bool whole, float (&x)[NG][C]) const {
         if constexpr (C % 4 == 0) {
@@ -136,6 +140,7 @@ struct GruChain {
 struct LstmChain {
     static constexpr int S = 2, NG = 4;
     const float *pi, *pf, *po, *pg, *ui, *uf, *uo, *ug, *h0, *c0;
+    const float *h_init, *c_init;  // initial iterates [B, L, H]; a null one is zero
     float *h, *c;
     bool runs;  // unused: the LSTM moves scalars
 
@@ -148,6 +153,10 @@ struct LstmChain {
     }
     __device__ float2s init(int64_t b, int64_t j, int64_t H) const {
         return {c0 != nullptr ? c0[b * H + j] : 0.0f, h0 != nullptr ? h0[b * H + j] : 0.0f};
+    }
+    __device__ bool warm() const { return h_init != nullptr || c_init != nullptr; }
+    __device__ float2s guess(int64_t e) const {
+        return {c_init != nullptr ? c_init[e] : 0.0f, h_init != nullptr ? h_init[e] : 0.0f};
     }
     template <int C>
     __device__ void load(int64_t base, int64_t H, const bool (&val)[C], bool, float (&x)[NG][C]) const {
@@ -421,16 +430,18 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
     float x[Cell::NG][C];
     cell.template load<C>(base, g.H, val, whole, x);
     const typename Cell::W wts = cell.weights(j, ok);
+    // iterate 0: zero, or the caller's initial iterate (a warm start)
+    const bool warm = cell.warm();
     State s[C];
 #pragma unroll
-    for (int i = 0; i < C; ++i) s[i] = M::zero();
+    for (int i = 0; i < C; ++i) s[i] = (warm && val[i]) ? cell.guess(base + i * g.H) : M::zero();
     const State init = (ok && q == 0 && sub == 0) ? cell.init(b, j, g.H) : M::zero();
     // The state before this chunk (the previous chunk's last state) at the
-    // current iterate, kept by the sub-chunk-0 threads: zero at iterate 0
-    // (the initial guess), then advanced by the delta entering the chunk at
-    // each iteration, which is the previous chunk's inclusive delta (zero
-    // once that chunk has stopped).
-    State hb = M::zero();
+    // current iterate, kept by the sub-chunk-0 threads: its value at iterate
+    // 0 (zero, or the initial iterate's), then advanced by the delta entering
+    // the chunk at each iteration, which is the previous chunk's inclusive
+    // delta (zero once that chunk has stopped).
+    State hb = (warm && ok && q > 0 && sub == 0) ? cell.guess(base - g.H) : M::zero();
 
     int k = 1;
     bool conv = false;
@@ -469,6 +480,8 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
                 hp = s_last[(sub - 1) * CW + ch];
             else
                 hp = lane == 0 ? s_last[w - 1] : nb;
+        } else if (warm && ok && pos0 <= g.L) {
+            hp = cell.guess(base - g.H);  // iterate 0 before this sub-chunk
         }
         e[0] = cell_step<Cell, C>(cell, wts, hp, x, 0, s[0]);
         Map acc = M::id();
@@ -756,6 +769,7 @@ hipError_t gru_forward_chain(const GruFwdArgs &a, const Ws &ws, hipStream_t s) {
     cell.ur = a.ur;
     cell.uc = a.uc;
     cell.h0 = a.h0;
+    cell.h_init = a.h_init;
     cell.h = a.h;
     cell.runs = a.H == 1 && a.L % 4 == 0 && aligned16(a.pz) && aligned16(a.pr) && aligned16(a.pc) &&
                 aligned16(a.h);
@@ -776,6 +790,8 @@ hipError_t lstm_forward_chain(const LstmFwdArgs &a, const Ws &ws, hipStream_t s)
     cell.ug = a.ug;
     cell.h0 = a.h0;
     cell.c0 = a.c0;
+    cell.h_init = a.h_init;
+    cell.c_init = a.c_init;
     cell.h = a.h;
     cell.c = a.c;
     cell.runs = false;

@@ -5,7 +5,7 @@
 // for long sequences; this path is selectable and takes caps above the
 // chained kernel's limit.
 //
-// Iteration k (from s^0 = 0):
+// Iteration k (from s^0 = 0, or from the caller's initial iterate):
 //   F_t = f(s^{k-1}_{t-1}), J_t = df/ds there, beta_t = F_t - s^{k-1}_t,
 //   delta_t = J_t delta_{t-1} + beta_t (delta_{-1} = 0)  -- the bi-diagonal
 //   solve, done by the chunked look-back scan,
@@ -17,6 +17,11 @@
 // (alternating between two copies).  Every launch first reads e_{k-1}; once
 // an iteration has met the tolerance every later launch exits at once, so
 // the host can enqueue max_iter launches without waiting for the device.
+// A warm start first copies the initial iterate into the outputs and its
+// chunk-end states into the boundary array that iteration 1 reads; iteration
+// 1 then runs as every later one.
+#include <algorithm>
+
 #include "cells.hpp"
 #include "launch.hpp"
 #include "scan_core.hpp"
@@ -59,6 +64,7 @@ struct GruStepOp {
     uint32_t *maxd;
     float tol;
     int k;
+    bool cold1;  // iteration 1 from s^0 = 0 (no initial iterate)
     int64_t B, L, H;
 
     struct Elem {
@@ -80,7 +86,7 @@ struct GruStepOp {
             wc = uc[tp.j];
             if (tp.pos0 == 0)
                 hp = h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f;
-            else if (k == 1)
+            else if (cold1)
                 hp = 0.0f;
             else if (tp.sub == 0)
                 hp = bnd_prev[(tp.q - 1) * B * H + tp.b * H + tp.j];
@@ -94,7 +100,7 @@ struct GruStepOp {
                 load_run<C>(pz + base, vz);  // ordinary loads: streamed 16-byte
                 load_run<C>(pr + base, vr);  // pieces of half-lines measured slower
                 load_run<C>(pc + base, vc);
-                if (k == 1) {
+                if (cold1) {
 #pragma unroll
                     for (int i = 0; i < C; ++i) vh[i] = 0.0f;
                 } else {
@@ -113,7 +119,7 @@ struct GruStepOp {
         }
         const auto cell = [&](int i) {
             const int64_t kk = base + i * H;
-            const float hc = k == 1 ? 0.0f : h[kk];
+            const float hc = cold1 ? 0.0f : h[kk];
             float F, J;
             gru_f_j(hp, ld_once(pz + kk), ld_once(pr + kk), ld_once(pc + kk), wz, wr, wc, F, J);
             e[i] = {J, F - hc, hc};
@@ -189,6 +195,7 @@ struct LstmStepOp {
     uint32_t *maxd;
     float tol;
     int k;
+    bool cold1;  // iteration 1 from s^0 = 0 (no initial iterate)
     int64_t B, L, H;
 
     struct Elem {
@@ -211,7 +218,7 @@ struct LstmStepOp {
             if (tp.pos0 == 0) {
                 hp = h0 != nullptr ? h0[tp.b * H + tp.j] : 0.0f;
                 cp = c0 != nullptr ? c0[tp.b * H + tp.j] : 0.0f;
-            } else if (k == 1) {
+            } else if (cold1) {
             } else if (tp.sub == 0) {
                 const float2 v = bnd_prev[(tp.q - 1) * B * H + tp.b * H + tp.j];
                 cp = v.x;
@@ -224,8 +231,8 @@ struct LstmStepOp {
         Aff2 acc = MonoidT<2>::id();
         const auto cell = [&](int i) {
             const int64_t kk = base + i * H;
-            const float cc = k == 1 ? 0.0f : c[kk];
-            const float hc = k == 1 ? 0.0f : h[kk];
+            const float cc = cold1 ? 0.0f : c[kk];
+            const float hc = cold1 ? 0.0f : h[kk];
             const Lstm2 r = lstm_f_j(cp, hp, ld_once(pi + kk), ld_once(pf + kk), ld_once(po + kk),
                                      ld_once(pg + kk), wi, wf, wo, wg);
             e[i].m = {r.j00, r.j01, r.j10, r.j11, r.Fc - cc, r.Fh - hc};
@@ -304,16 +311,58 @@ __global__ void newton_finalize(const uint32_t *maxd, int cap, float tol, int32_
     }
 }
 
+// Warm start of the per-iteration path: the initial iterate (h, and c for
+// S = 2; a null one is zero) copied into the outputs, and its state at the
+// last position of every chunk into the boundary array iteration 1 reads.
+struct SeedArgs {
+    const float *h_init, *c_init;
+    float *h, *c;
+    void *bnd;
+    int64_t B, L, H, T;
+};
+
+template <int S>
+__global__ __launch_bounds__(256) void newton_seed_kernel(SeedArgs a) {
+    const int64_t n = a.B * a.L * a.H;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t j = e % a.H, bt = e / a.H, t = bt % a.L, b = bt / a.L;
+        const float hv = a.h_init != nullptr ? a.h_init[e] : 0.0f;
+        a.h[e] = hv;
+        float cv = 0.0f;
+        if constexpr (S == 2) {
+            cv = a.c_init != nullptr ? a.c_init[e] : 0.0f;
+            a.c[e] = cv;
+        }
+        if ((t + 1) % a.T == 0 || t == a.L - 1) {
+            const int64_t slot = (t / a.T) * a.B * a.H + b * a.H + j;
+            if constexpr (S == 1)
+                static_cast<float *>(a.bnd)[slot] = hv;
+            else
+                static_cast<float2 *>(a.bnd)[slot] = make_float2(cv, hv);
+        }
+    }
+}
+
 // Runs the launch sequence shared by both cells.  `make_op(k, bnd_prev,
-// bnd_next, maxd)` returns the op of iteration k.
+// bnd_next, maxd)` returns the op of iteration k.  `seed`, when not null,
+// holds a warm start's initial iterate (its bnd and T are set here).
 template <int S, int NWC, int CC, int NWT, int CT, class MakeOp>
 static hipError_t newton_loop(const TileCfg &cfg, int64_t B, int64_t L, int64_t H, int32_t cap,
                               float tol, int32_t *info, float *trace, const Ws &ws, hipStream_t s,
-                              MakeOp make_op) {
+                              SeedArgs *seed, MakeOp make_op) {
     const NewtonWs w = newton_ws(cfg, S, B, L, H, cap);
     FillRange fr[1] = {{ws.p + w.maxd, (uint64_t)cap, 0, 4}};
     hipError_t e = fill(fr, 1, s);
     if (e != hipSuccess) return e;
+    if (seed != nullptr) {
+        seed->bnd = ws.p + w.bnd[0];  // iteration 1 reads bnd[0] as its previous iterate's
+        seed->T = w.sh.T;
+        const int64_t n = B * L * H;
+        const int64_t blocks = std::min<int64_t>((n + 255) / 256, (int64_t)device_cu_count() * 8);
+        hipLaunchKernelGGL(newton_seed_kernel<S>, dim3((unsigned)blocks), dim3(256), 0, s, *seed);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     uint32_t *maxd = reinterpret_cast<uint32_t *>(ws.p + w.maxd);
     ScanGeo g;
     g.B = B;
@@ -356,6 +405,7 @@ hipError_t gru_forward_step(const GruFwdArgs &a, const Ws &ws, hipStream_t s) {
         op.maxd = maxd;
         op.tol = a.tol;
         op.k = k;
+        op.cold1 = k == 1 && a.h_init == nullptr;
         op.B = a.B;
         op.L = a.L;
         op.H = a.H;
@@ -364,8 +414,9 @@ hipError_t gru_forward_step(const GruFwdArgs &a, const Ws &ws, hipStream_t s) {
         return op;
     };
     constexpr TileCfg c = kCfgGruStep;
+    SeedArgs seed{a.h_init, nullptr, a.h, nullptr, nullptr, a.B, a.L, a.H, 0};
     return newton_loop<1, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, ws, s,
-                                 make);
+                                                            a.h_init != nullptr ? &seed : nullptr, make);
 }
 
 hipError_t lstm_forward_step(const LstmFwdArgs &a, const Ws &ws, hipStream_t s) {
@@ -388,14 +439,17 @@ hipError_t lstm_forward_step(const LstmFwdArgs &a, const Ws &ws, hipStream_t s) 
         op.maxd = maxd;
         op.tol = a.tol;
         op.k = k;
+        op.cold1 = k == 1 && a.h_init == nullptr && a.c_init == nullptr;
         op.B = a.B;
         op.L = a.L;
         op.H = a.H;
         return op;
     };
     constexpr TileCfg c = kCfgLstmStep;
+    const bool warm = a.h_init != nullptr || a.c_init != nullptr;
+    SeedArgs seed{a.h_init, a.c_init, a.h, a.c, nullptr, a.B, a.L, a.H, 0};
     return newton_loop<2, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl>(c, a.B, a.L, a.H, a.cap, a.tol, a.info, a.trace, ws, s,
-                                make);
+                                                            warm ? &seed : nullptr, make);
 }
 
 }  // namespace prn

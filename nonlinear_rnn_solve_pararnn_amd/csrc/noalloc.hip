@@ -54,6 +54,6 @@ extern "C" int pararnn_gru_forward_noalloc(int64_t B, int64_t L, int64_t H, cons
     void *ws = nullptr;
     const int st = scratch_address(&ws, static_cast<hipStream_t>(stream));
     if (st != PARARNN_OK) return st;
-    return pararnn_gru_forward(B, L, H, pz, pr, pc, uz, ur, uc, h0, h, tol, max_iter, info, trace, ws,
+    return pararnn_gru_forward(B, L, H, pz, pr, pc, uz, ur, uc, h0, nullptr, h, tol, max_iter, info, trace, ws,
                                kScratchBytes, stream);
 }

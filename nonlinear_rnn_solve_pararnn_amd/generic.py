@@ -97,10 +97,13 @@ def head_gru_cell(s, pz, pr, pc, Uz, Ur, Uc):
     return (1 - z) * s + z * c
 
 
-def _solve(cell, inputs, params, h0, tol, max_iter, info, k):
+def _solve(cell, inputs, params, h0, tol, max_iter, info, k, init=None):
     B, L, H = inputs[0].shape[:3]
     shape = (B, L, H) if k == 1 else (B, L, H, k)
-    s = torch.zeros(shape, dtype=inputs[0].dtype, device=inputs[0].device)
+    if init is None:
+        s = torch.zeros(shape, dtype=inputs[0].dtype, device=inputs[0].device)
+    else:
+        s = init.detach().clone()
     dev = s.device
     active = torch.ones((), dtype=torch.float32, device=dev)   # 1 until converged
     its = torch.zeros((), dtype=torch.int32, device=dev)       # updates applied
@@ -129,9 +132,9 @@ def _solve(cell, inputs, params, h0, tol, max_iter, info, k):
 
 class _BlockDiagonalSolve(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, cell, tol, max_iter, info, k, n_inputs, h0, *tensors):
+    def forward(ctx, cell, tol, max_iter, info, k, n_inputs, init, h0, *tensors):
         inputs, params = tensors[:n_inputs], tensors[n_inputs:]
-        s = _solve(cell, inputs, params, h0, tol, max_iter, info, k)
+        s = _solve(cell, inputs, params, h0, tol, max_iter, info, k, init)
         ctx.cell, ctx.n_inputs, ctx.k = cell, n_inputs, k
         ctx.save_for_backward(h0, s, *tensors)
         return s
@@ -150,7 +153,7 @@ class _BlockDiagonalSolve(torch.autograd.Function):
             lam = _scan(a.flip(1), g.flip(1), k).flip(1)
         # one vector-Jacobian product of the cell at the converged states
         with torch.enable_grad():
-            h0_ = h0.detach().requires_grad_(ctx.needs_input_grad[6])
+            h0_ = h0.detach().requires_grad_(ctx.needs_input_grad[7])
             ins = [x.detach().requires_grad_(True) for x in tensors]
             F = ctx.cell(_shift(s, h0_), *ins)
             wrt = [x for x in [h0_] + ins if x.requires_grad]
@@ -158,22 +161,23 @@ class _BlockDiagonalSolve(torch.autograd.Function):
         gh0 = next(grads) if h0_.requires_grad else None
         gt = [next(grads) for _ in ins]
         gt = [torch.zeros_like(x) if gx is None else gx for x, gx in zip(tensors, gt)]
-        return (None, None, None, None, None, None, gh0, *gt)
+        return (None, None, None, None, None, None, None, gh0, *gt)
 
 
 def newton_solve(cell: Callable[..., torch.Tensor], inputs: Sequence[torch.Tensor],
                  h0: Optional[torch.Tensor] = None, params: Sequence[torch.Tensor] = (), *,
                  tol: float = 1e-4, max_iter: int = 32, info: Optional[list] = None,
-                 state_size: int = 1) -> torch.Tensor:
+                 state_size: int = 1, init: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Solve s_t = cell(s_{t-1}, *inputs_t, *params) over the whole sequence.
 
     inputs: tensors [B, L, H] or [B, L, H, state_size] (fp32, on a HIP
     device) passed to the cell position-wise; params: tensors the cell uses as
     they are (weights, broadcast against the state); state_size: 1 (states
     [B, L, H]) or k = 2, 4, 8 (states [B, L, H, k], k x k Jacobian blocks);
-    h0: [B, H] or [B, H, k], or None (zeros).  Newton starts from s = 0 and
-    stops once max|delta| <= tol or after max_iter updates; `info`, if a list
-    of two, receives [iterations, converged].  Returns the states,
+    h0: [B, H] or [B, H, k], or None (zeros).  Newton starts from s = 0, or
+    from `init` (a warm start, shaped as the states; no gradient flows to
+    it), and stops once max|delta| <= tol or after max_iter updates; `info`,
+    if a list of two, receives [iterations, converged].  Returns the states,
     differentiable with respect to inputs, params and h0 through the adjoint
     of the solve."""
     if not inputs:
@@ -197,5 +201,8 @@ def newton_solve(cell: Callable[..., torch.Tensor], inputs: Sequence[torch.Tenso
         h0 = torch.zeros(hshape, dtype=x0.dtype, device=x0.device)
     elif tuple(h0.shape) != hshape:
         raise ValueError("h0 must be %s" % (hshape,))
+    sshape = (B, L, H) if state_size == 1 else (B, L, H, state_size)
+    if init is not None and (tuple(init.shape) != sshape or init.device != x0.device):
+        raise ValueError("init must be %s on %s" % (sshape, x0.device))
     return _BlockDiagonalSolve.apply(cell, float(tol), int(max_iter), info, state_size,
-                                     len(inputs), h0, *inputs, *params)
+                                     len(inputs), init, h0, *inputs, *params)

@@ -78,7 +78,8 @@ def test_invalid_arguments_rejected_on_host(lib):
     # validation happens before any HIP call: NULL pointers / bad sizes
     n = None
     assert lib.rnn_linscan_diag(0, 10, 10, n, n, n, n, n, 0, n) == -1
-    assert lib.pararnn_gru_forward(1, 10, 10, *([n] * 8), ctypes.c_float(1e-4), 5, n, n, n, 0, n) == -1
+    assert lib.pararnn_gru_forward(1, 10, 10, *([n] * 9), ctypes.c_float(1e-4), 5, n, n, n, 0, n) == -1
+    assert lib.pararnn_lstm_forward(1, 10, 10, *([n] * 14), ctypes.c_float(1e-4), 5, n, n, n, 0, n) == -1
     assert lib.pararnn_adjoint_backward(7, 1, 10, 10, *([n] * 13), 0, n) == -1
     assert lib.pararnn_gru_sequential(1, 0, 10, *([n] * 8), n) == -1
     assert lib.rnn_linscan_blk(4, 1, 10, 10, n, n, n, n, n, 0, n) == -1
@@ -86,6 +87,33 @@ def test_invalid_arguments_rejected_on_host(lib):
     assert lib.rnn_linscan_blk(3, 1, 10, 10, n, n, n, n, n, 0, n) == -3  # unsupported k
     assert lib.pararnn_lstm_sequential(1, 10, 10, *([n] * 12), n) == -1
     assert lib.pararnn_status_string(-1) == b"invalid argument"
+
+
+def test_initial_iterate_must_not_overlap_outputs(lib):
+    """A warm start's initial iterate is read while the outputs are written:
+    any overlap is rejected before anything is enqueued (the pointers below
+    are never dereferenced)."""
+    B, L, H = 1, 10, 10
+    nbytes = B * L * H * 4
+    fake = [ctypes.c_void_p(0x10000 * (i + 1)) for i in range(8)]
+    h = ctypes.c_void_p(0x100000)
+    for off in (0, 4, nbytes - 4, -(nbytes - 4)):
+        init = ctypes.c_void_p(0x100000 + off)
+        assert lib.pararnn_gru_forward(B, L, H, *fake[:6], None, init, h, ctypes.c_float(1e-4), 5,
+                                       None, None, None, 0, None) == -1
+    c = ctypes.c_void_p(0x200000)
+    for hi, ci in ((ctypes.c_void_p(0x200000), None), (None, ctypes.c_void_p(0x100000 + 8)),
+                   (ctypes.c_void_p(0x200000 + nbytes - 4), None)):
+        assert lib.pararnn_lstm_forward(B, L, H, *fake[:8], None, None, hi, ci, h, c,
+                                        ctypes.c_float(1e-4), 5, None, None, None, 0, None) == -1
+
+
+def test_blk8_workspace_query():
+    # header 256 B, then per chunk of 32 positions 9 aggregate words and 1
+    # inclusive word per (batch row, head, row)
+    nq, nrow = 2048 // 32, 16 * 64 * 8
+    assert api.workspace_bytes(api.OP_LINSCAN_BLK8, 16, 2048, 64) == 256 + nq * 9 * nrow * 8 + nq * nrow * 8
+    assert api.workspace_bytes(api.OP_LINSCAN_BLK8, 0, 2048, 64) == 0
 
 
 def test_product_path_does_not_use_the_oracle():
