@@ -79,12 +79,39 @@ DOMINANT = {
 # taken on: the sha256 prefix of those sources is checked at run time and the
 # figure is dropped (null) once any of them has changed.
 TRAFFIC = {
-    "c1_linscan": {"bytes": 551421952 + 289021952,
-                   "sources": ["common.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-                   "sha256": "3c1d79cf3f80249c"},
-    "c2_gru_fused": {"bytes": 419277619 + 152519270,
-                     "sources": ["common.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
-                     "sha256": "17fe61c95e651689"},
+    "c1_linscan": {"bytes": 551357001 + 289021984,
+        "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
+        "sha256": "84bc0eda9b11303a"},
+    "c2_gru_fused": {"bytes": 419047168 + 151348484,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
+        "sha256": "97c1fdd40c04be32"},
+    "c3_lstm": {"bytes": 537181344 + 268440036,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "newton_chain.hip"],
+        "sha256": "3ce3acf6e2e31460"},
+    "c4_gru_long_fwd_adj": {"bytes": 543064320 + 269437508,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "newton_chain.hip", "adjoint.hip"],
+        "sha256": "6f0322f5f9b73c44"},
+    "x_linscan_blk2": {"bytes": 823123200 + 325722144,
+        "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
+        "sha256": "84bc0eda9b11303a"},
+    "x_linscan_blk4": {"bytes": 695712293 + 159006752,
+        "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "blkrow.hip"],
+        "sha256": "283c0ae062777af0"},
+    "x_linscan_blk8": {"bytes": 694930560 + 118677390,
+        "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "blkrow.hip"],
+        "sha256": "283c0ae062777af0"},
+    "x_lstm_adjoint": {"bytes": 1127502958 + 597172256,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "adjoint.hip"],
+        "sha256": "d63848690d598bff"},
+    "x_gru_long_fwd": {"bytes": 203717840 + 67796908,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "newton_chain.hip"],
+        "sha256": "3ce3acf6e2e31460"},
+    "x_gru_seq": {"bytes": 402868407 + 134217728,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
+        "sha256": "e7a50c4b18aee253"},
+    "x_lstm_seq": {"bytes": 537127058 + 268435456,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
+        "sha256": "e7a50c4b18aee253"},
 }
 DESCRIBE = {
     "c1_linscan": "linear diagonal recurrence h_t = a_t h_{t-1} + b_t, B=16 L=4096 H=1024, "
@@ -153,29 +180,43 @@ def roofline(name, elements, kernel_ms):
 # dispatch (SQ_INSTS_VALU and SQ_INSTS_VALU_TRANS_F32 count wave instructions;
 # times 64 lanes, over elements x iterations): plain instructions count one
 # slot, transcendentals (exp2, reciprocal) four, since they issue at a
-# quarter of the rate.  The fp32 vector peak of 157.3 TFLOP/s is 78.6 T
-# lane-operations per second of FMA issue.
-#  - fused GRU, B=16 L=512 H=4096, 4 iterations: 80,297,984 VALU and
+# quarter of the rate (measured: 4.3 multiply-add slots each).  The fp32
+# vector peak of 157.3 TFLOP/s is 78.6 T lane-operations per second of FMA
+# issue, counting packed fp32; the measured plain rate of this build is
+# reported beside it (alu_calibration).
+#  - fused GRU, B=16 L=512 H=4096, 4 iterations: 80,299,017 VALU and
 #    12,615,680 transcendental wave instructions = 38.29 and 6.02 per element
 #    and iteration (the gfx950 assembly of the loop gives 33.8 and 6; the rest
 #    is per-iteration work outside the cell loop);
-#  - LSTM whole chains, B=8 L=2048 H=2048, 4 iterations: 180,076,284 and
-#    20,975,616 = 85.87 and 10.00.
+#  - LSTM whole chains, B=8 L=2048 H=2048, 4 iterations: 184,651,902 and
+#    20,975,616 = 88.05 and 10.00;
+#  - long GRU forward (chained, time lanes), B=16 L=2^20 H=1, 3 iterations:
+#    38,601,066 and 4,759,552 = 49.08 and 6.05.
 ALU_SLOTS_PER_ELEMENT_ITER = {
     "c2_gru_fused": (38.29 - 6.02) + 6.02 * 4,
-    "c3_lstm": (85.87 - 10.00) + 10.00 * 4,
+    "c3_lstm": (88.05 - 10.00) + 10.00 * 4,
+    "x_gru_long_fwd": (49.08 - 6.05) + 6.05 * 4,
 }
 PEAK_VALU_TOPS = 78.6
 
 
-def alu_roofline(name, elements, iterations, kernel_ms):
+def alu_roofline(name, elements, iterations, kernel_ms, calib=None):
+    """Arithmetic roof: issue slots over the kernel time, against the
+    published fp32 vector peak (the primary basis, which counts packed fp32
+    issue) and, when `calib` is given, against the measured plain
+    multiply-add rate of this device with packed fp32 off (the build's)."""
     per = ALU_SLOTS_PER_ELEMENT_ITER[name]
     slots = per * elements * iterations
     achieved = slots / (kernel_ms * 1e-3) / 1e12
-    return {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_TOPS,
-            "unit": "T VALU issue slots/s", "frac": achieved / PEAK_VALU_TOPS,
-            "model": "%.1f slots per element and Newton iteration (transcendentals count 4), "
-                     "%d iterations (the most any tile took)" % (per, iterations)}
+    out = {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_TOPS,
+           "unit": "T VALU issue slots/s", "frac": achieved / PEAK_VALU_TOPS,
+           "model": "%.1f slots per element and Newton iteration (transcendentals count 4), "
+                    "%d iterations (the most any tile took)" % (per, iterations)}
+    if calib is not None:
+        fma = calib["fma"]["lane_ops_per_s"] / 1e12
+        out["peak_measured_fma"] = fma
+        out["frac_measured_fma"] = achieved / fma
+    return out
 
 
 def _torch_gru_cell(h, pz, pr, pc, uz, ur, uc):
@@ -352,6 +393,41 @@ def device_copy(dev, reps=10):
     torch.cuda.empty_cache()
     return {"value": gbs, "unit": "GB/s", "frac_of_peak": gbs / PEAK_HBM_GBS,
             "what": "torch copy_ of 1 GiB fp32 (1 GiB read + 1 GiB written), %d copies, HIP events" % reps}
+
+
+def alu_calibration(dev):
+    """Measured issue rates of plain fp32 multiply-adds and of exp2/reciprocal
+    pairs (nonlinear_rnn_solve_pararnn_amd/probe/alu_probe.hip, compiled with
+    the library's flags, packed fp32 off): lane operations per second over one
+    launch of 8 independent register chains per thread, HIP events on the
+    launch stream.  The basis next to the published fp32 vector peak for the
+    arithmetic rooflines."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "nonlinear_rnn_solve_pararnn_amd", "libpararnn_probe.so"))
+    for f in (lib.alu_probe_fma, lib.alu_probe_trans):
+        f.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        f.restype = ctypes.c_int
+    tpb, steps = lib.alu_probe_threads_per_block(), lib.alu_probe_steps_per_iter()
+    blocks = 256 * 32  # 32 workgroups of 4 waves per CU: every SIMD busy
+    out = torch.empty(blocks * tpb, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for name, fn, iters in (("fma", lib.alu_probe_fma, 2048), ("exp2_rcp", lib.alu_probe_trans, 256)):
+        ops = blocks * tpb * iters * steps * (1 if name == "fma" else 2)
+        for _ in range(2):
+            assert fn(blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream)) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        assert fn(blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream)) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        res[name] = {"lane_ops_per_s": ops / (ms * 1e-3), "ms": ms, "lane_ops": ops}
+    res["what"] = ("alu_probe.hip: v_fma (fmamk) chains, and exp2 + add + reciprocal chains "
+                   "(2 transcendental lane-ops per step), %d workgroups of %d threads" % (blocks, tpb))
+    return res
 
 
 def log(*a):
@@ -621,6 +697,8 @@ def main():
                     help="leave out the modality sweep and residual traces")
     ap.add_argument("--modalities", action="store_true",
                     help="only the modality sweep and residual traces (one JSON line)")
+    ap.add_argument("--alu-calibration", action="store_true",
+                    help="print the measured fp32 multiply-add and exp2/reciprocal issue rates")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -639,6 +717,10 @@ def main():
         print(json.dumps(modalities(dev)), flush=True)
         return
 
+    if args.alu_calibration:
+        print(json.dumps(alu_calibration(dev)), flush=True)
+        return
+
     if args.copy_calibration:
         n = 1 << 28  # 1 GiB of fp32
         a = torch.ones(n, device=dev)
@@ -649,6 +731,8 @@ def main():
         log("copy calibration: %d launches of a %d-byte device copy" % (args.warmup + args.steps, 4 * n))
         return
 
+    calib = alu_calibration(dev)
+    log("alu calibration", json.dumps(calib))
     scratch = torch.zeros(EVICT_BYTES // 4, dtype=torch.float32, device=dev)
     names = [args.workload] if args.only else \
         [args.workload] + [n for n in ALG_BYTES if n != args.workload]
@@ -672,7 +756,7 @@ def main():
             "roofline": roofline(name, wl.elements, kernel_ms),
         }
         if name in ALU_SLOTS_PER_ELEMENT_ITER and iters:
-            results[name]["roofline_alu"] = alu_roofline(name, wl.elements, iters[0], kernel_ms)
+            results[name]["roofline_alu"] = alu_roofline(name, wl.elements, iters[0], kernel_ms, calib)
         if name != args.workload and name in CPU_BASELINE_OF and not args.no_cpu_baseline:
             log("cpu baseline (oracle) for", name)
             results[name]["cpu_baseline"] = cpu_baseline(name, wl.host, budget_s=5.0, single_s=2.0)
@@ -718,6 +802,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(args.workload, synth.workload_inputs(args.workload))
     else:
         out["cpu_baseline"] = None
+    out["alu_calibration"] = calib
     if not args.only:
         out["device_copy"] = device_copy(dev)
     if len(results) > 1:

@@ -20,6 +20,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpararnn.so")
+# measurement-only probe (arithmetic issue rates), a library of its own
+PROBE_SRC = os.path.join(HERE, "probe", "alu_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libpararnn_probe.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")  # the C ABI header
 ARCH = os.environ.get("PARARNN_ARCH", "gfx950")
 
@@ -63,7 +66,21 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    build_probe(verbose)
     return LIB
+
+
+def build_probe(verbose: bool = False) -> str:
+    obj = _compile(PROBE_SRC)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    r = subprocess.run([_hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", obj, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("probe link failed:\n" + r.stderr)
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print("built", PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
