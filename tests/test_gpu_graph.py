@@ -62,3 +62,62 @@ def test_captured_scan_newton_and_adjoint_replay(orc):
         errs.append(rel_inf(host(grads["h0"]), dh0))
         say(max(errs))
         assert max(errs) <= GRAD_RTOL
+
+
+def test_captured_block_scans_and_warm_start_replay(orc):
+    """The 8x8 and 4x4 lane-group scans and a warm-started chained LSTM forward
+    under capture: three replays with the inputs changed in place, eager work
+    in between, every replay against the oracle."""
+    from tests.gpu_helpers import lstm_args
+    import numpy as np
+    B, L, H = 2, 700, 24
+    d8 = [synth.linscan_blk_inputs(B, L, H, 8, seed=660 + r) for r in range(3)]
+    d4 = [synth.linscan_blk_inputs(B, L, H, 4, seed=670 + r) for r in range(3)]
+    dl = [synth.lstm_inputs(B, 1500, 40, seed=680 + r, h0=True) for r in range(3)]
+    A8, b8 = dev(d8[0]["A"]), dev(d8[0]["b"])
+    A4, b4 = dev(d4[0]["A"]), dev(d4[0]["b"])
+    lk = ("pi", "pf", "po", "pg", "ui", "uf", "uo", "ug", "h0", "c0")
+    tl = {k: dev(dl[0][k]) for k in lk}
+    init_h = torch.zeros(B, 1500, 40, device="cuda")
+    init_c = torch.zeros(B, 1500, 40, device="cuda")
+    h8, h4 = torch.empty_like(b8), torch.empty_like(b4)
+    hl, cl = torch.empty(B, 1500, 40, device="cuda"), torch.empty(B, 1500, 40, device="cuda")
+    info = torch.zeros(2, dtype=torch.int32, device="cuda")
+    ws8 = api.new_workspace(api.workspace_bytes(api.OP_LINSCAN_BLK8, B, L, H), A8.device)
+    ws4 = api.new_workspace(api.workspace_bytes(api.OP_LINSCAN_BLK4, B, L, H), A8.device)
+    wsl = api.new_workspace(api.workspace_bytes(api.OP_LSTM_FORWARD, B, 1500, 40, 32), A8.device)
+
+    def calls():
+        api.linscan_blk(A8, b8, out=h8, ws=ws8)
+        api.linscan_blk(A4, b4, out=h4, ws=ws4)
+        api.lstm_forward(*[tl[k] for k in lk[:8]], tl["h0"], tl["c0"], tol=1e-5, max_iter=32,
+                         out_h=hl, out_c=cl, info=info, ws=wsl, init_h=init_h, init_c=init_c)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for r in range(3):
+        say("replay", r)
+        A8.copy_(dev(d8[r]["A"]))
+        b8.copy_(dev(d8[r]["b"]))
+        A4.copy_(dev(d4[r]["A"]))
+        b4.copy_(dev(d4[r]["b"]))
+        for k in lk:
+            tl[k].copy_(dev(dl[r][k]))
+        # warm start from a perturbed rollout of this replay's inputs
+        rh, rc = orc.lstm_rollout(*lstm_args(dl[r]), h0=dl[r]["h0"], c0=dl[r]["c0"])
+        init_h.copy_(dev((rh + 0.01).astype(np.float32)))
+        init_c.copy_(dev((rc - 0.01).astype(np.float32)))
+        api.linscan_blk(A8 * 0.5, b8)  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert max_abs(host(h8), orc.linscan_blk(d8[r]["A"], d8[r]["b"])) <= FWD_ATOL
+        assert max_abs(host(h4), orc.linscan_blk(d4[r]["A"], d4[r]["b"])) <= FWD_ATOL
+        assert info.cpu().tolist()[1] == 1
+        assert max(max_abs(host(hl), rh), max_abs(host(cl), rc)) <= FWD_ATOL

@@ -83,3 +83,23 @@ def test_gru_chained_beyond_2_31_elements(orc):
         assert err <= FWD_ATOL
     del p, u, h
     _free()
+
+
+def test_linscan_blk8_beyond_2_31_floats(orc):
+    """8x8 blocks: A holds more than 2^31 floats (and the records more than
+    2^31 words' worth of index range); sampled heads against the oracle."""
+    B, L, H = 2, (1 << 17) + 5, 130  # A: 2 x 131077 x 130 x 64 = 2,181,121,280 floats
+    assert B * L * H * 64 > 2 ** 31
+    say("linscan_blk8", B, L, H)
+    g = _gen(430)
+    A = (torch.rand((B, L, H, 8, 8), generator=g, device="cuda") - 0.5) * 0.6
+    b = torch.randn((B, L, H, 8), generator=g, device="cuda")
+    h = api.linscan_blk(A, b)
+    for bb, j in [(0, 0), (1, H - 1), (1, 64), (0, 127)]:
+        Aj = A[bb, :, j].contiguous().cpu().numpy()[None, :, None]
+        bj = b[bb, :, j].contiguous().cpu().numpy()[None, :, None]
+        err = max_abs(h[bb, :, j].contiguous().cpu().numpy()[None, :, None], orc.linscan_blk(Aj, bj))
+        say(bb, j, err)
+        assert err <= FWD_ATOL
+    del A, b, h
+    _free()
