@@ -26,7 +26,7 @@ constexpr TileCfg kCfgGruStep{4, 16, 8, 16};
 constexpr TileCfg kCfgLstmStep{8, 16, 4, 8};
 constexpr TileCfg kCfgGruAdj{4, 8, 16, 8};
 constexpr TileCfg kCfgLstmAdj{8, 16, 4, 4};
-constexpr TileCfg kCfgGruChain{4, 16, 8, 24};
+constexpr TileCfg kCfgGruChain{4, 16, 8, 28};
 constexpr TileCfg kCfgLstmChain{8, 8, 8, 8};
 // Channel-lane tiles of the chained kernel's form in which workgroups own
 // whole chains (its time-lane fields are unused).  The LSTM's chains are 32
