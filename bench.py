@@ -54,6 +54,7 @@ ALG_BYTES = {
     "x_gru_long_seq": 16,        # 3 p in; h out
     "x_linscan_blk4": 96,        # A (4x4) and b (4) in; h (4) out, per (batch, position, block)
     "x_linscan_blk8": 320,       # A (8x8) and b (8) in; h (8) out, per (batch, position, block)
+    "x_hgru8_fwd": 128,          # pz, pr, pc (8 each) in; h (8) out, per (batch, position, head): the whole solve
 }
 DOMINANT = {
     "c1_linscan": "diag_pf_kernel<16,16,2> (chunked scan, next tile prefetched)",
@@ -70,8 +71,10 @@ DOMINANT = {
     "x_gru_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
     "x_lstm_seq": "lstm_rollout_kernel (sequential application, one thread per channel)",
     "x_gru_long_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
-    "x_linscan_blk4": "blkrow_scan_kernel<4,8,8,1> (each block's rows on a group of 4 lanes)",
-    "x_linscan_blk8": "blkrow_scan_kernel<8,4,8,3> (each block's rows on a group of 8 lanes)",
+    "x_linscan_blk4": "lg::scan_kernel<LinRowOp<4>,8,8,1> (each block's rows on a group of 4 lanes)",
+    "x_linscan_blk8": "lg::scan_kernel<LinRowOp<8>,4,8,3> (each block's rows on a group of 8 lanes)",
+    "x_hgru8_fwd": "lg::scan_kernel<HgruStepOp<8>,4,8,1> (one launch per Newton iteration up to the cap; "
+                   "launches after convergence exit at once)",
 }
 # HBM bytes per launch of the dominant kernel from rocprofv3 counter runs
 # (FETCH_SIZE x 2.000 and WRITE_SIZE x 1.000, the factors a plain 1 GiB device
@@ -141,6 +144,9 @@ DESCRIBE = {
                       "A~U(-0.42,0.42), b~N(0,1), h0=0",
     "x_linscan_blk8": "8x8 block linear recurrence h_t = A_t h_{t-1} + b_t (heads of 8 channels), "
                       "B=16 L=2048 H=64 heads, A~U(-0.3,0.3), b~N(0,1), h0=0",
+    "x_hgru8_fwd": "Newton forward of the GRU with dense recurrence inside heads of 8 channels (8x8 "
+                   "Jacobian blocks), B=16 L=2048 H=64 heads, p~N(0,1), U: diagonal U(-0.5,0.5), "
+                   "off-diagonal U(-0.3,0.3)/sqrt(8), h0=0, tol 1e-4, cap 32",
 }
 
 
@@ -522,6 +528,13 @@ class Workload:
                 finally:
                     del os.environ[var]
             self._step = step
+        elif name == "x_hgru8_fwd":
+            cap = self.w["cap"]
+            self.out = torch.empty(B, L, H, self.w["k"], device=dev)
+            self.ws = api.new_workspace(api.workspace_bytes(api.OP_HGRU8_FORWARD, B, L, H, cap), dev)
+            args = [t[k] for k in ("pz", "pr", "pc", "Uz", "Ur", "Uc")]
+            self._step = lambda: api.hgru_forward(*args, None, tol=self.w["tol"], max_iter=cap,
+                                                  out=self.out, info=self.info, ws=self.ws)
         elif name == "x_gru_long_fwd":
             self.out = torch.empty(B, L, H, device=dev)
             cap = self.w["cap"]
@@ -742,7 +755,7 @@ def main():
         wl = Workload(name, dev)
         iters = wl.iterations() if name in ("c2_gru_fused", "c3_lstm", "c4_gru_long_fwd_adj",
                                             "x_lstm_step", "x_gru_long_step",
-                                            "x_gru_long_fwd") else None
+                                            "x_gru_long_fwd", "x_hgru8_fwd") else None
         t = time_workload(wl, args.steps, args.warmup, scratch)
         kernel_ms = t["cold_median_ms"]
         results[name] = {

@@ -78,7 +78,9 @@ enum {
     PARARNN_OP_GRU_ADJOINT = 4,
     PARARNN_OP_LSTM_ADJOINT = 5,
     PARARNN_OP_LINSCAN_BLK4 = 6,  /* rnn_linscan_blk with k = 4 */
-    PARARNN_OP_LINSCAN_BLK8 = 7   /* rnn_linscan_blk with k = 8 */
+    PARARNN_OP_LINSCAN_BLK8 = 7,  /* rnn_linscan_blk with k = 8 */
+    PARARNN_OP_HGRU4_FORWARD = 8, /* pararnn_hgru_forward with k = 4 (H = heads) */
+    PARARNN_OP_HGRU8_FORWARD = 9  /* pararnn_hgru_forward with k = 8 (H = heads) */
 };
 
 /*
@@ -201,6 +203,35 @@ int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H,
                          const float *c0, const float *h_init, const float *c_init,
                          float *h, float *c, float tol, int32_t max_iter,
                          int32_t *info, float *trace,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * GRU with dense recurrence inside heads of k channels (k = 4 or 8): the
+ * GRU-style cell above with each weight vector replaced by one k x k matrix
+ * per head, acting on the state vector of the head where the diagonal cell
+ * multiplies by u (a diagonal U is exactly the diagonal cell), so the
+ * Jacobian is block-diagonal with dense k x k blocks (DEER summary page,
+ * limitations paragraph: dense Jacobians, the GRU with 8-channel heads;
+ * ParaRNN page, Fig. 2 caption: block bi-diagonal systems):
+ *   z = sigmoid(pz + Uz h), r = sigmoid(pr + Ur h),
+ *   c = tanh(pc + Uc (r*h)),  h' = (1 - z)*h + z*c
+ * evaluated over the whole sequence by Newton's method, one launch per
+ * iteration (launches after convergence exit at once; the host never waits),
+ * each solving the block bi-diagonal system with the k x k scan.
+ * pz, pr, pc: [B, L, NH, k] gate pre-projections; Uz, Ur, Uc: [NH, k, k]
+ * row-major (U[n][i][l] takes component l into i); h0: [B, NH, k] or NULL;
+ * h_init: [B, L, NH, k] initial iterate or NULL for zeros (must not overlap
+ * h); h: [B, L, NH, k] output.  tol, max_iter, info, trace as for
+ * pararnn_gru_forward, with max|delta| over the whole tensor (every cap
+ * takes this path).  Workspace: PARARNN_OP_HGRU4_FORWARD /
+ * PARARNN_OP_HGRU8_FORWARD with H = NH.  Other k return
+ * PARARNN_ERR_UNSUPPORTED (k < 1: PARARNN_ERR_INVALID).
+ */
+int pararnn_hgru_forward(int32_t k, int64_t B, int64_t L, int64_t NH,
+                         const float *pz, const float *pr, const float *pc,
+                         const float *Uz, const float *Ur, const float *Uc,
+                         const float *h0, const float *h_init, float *h, float tol,
+                         int32_t max_iter, int32_t *info, float *trace,
                          void *ws, size_t ws_bytes, void *stream);
 
 /*

@@ -19,13 +19,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpararnn.so")
 
 OP_LINSCAN_DIAG, OP_LINSCAN_BLK2, OP_GRU_FORWARD, OP_LSTM_FORWARD, OP_GRU_ADJOINT, \
-    OP_LSTM_ADJOINT, OP_LINSCAN_BLK4, OP_LINSCAN_BLK8 = range(8)
+    OP_LSTM_ADJOINT, OP_LINSCAN_BLK4, OP_LINSCAN_BLK8, OP_HGRU4_FORWARD, OP_HGRU8_FORWARD = range(10)
 CELL_GRU, CELL_LSTM = 0, 1
 
 EXPORTS = ("pararnn_workspace_bytes", "rnn_linscan_diag", "rnn_linscan_blk2", "rnn_linscan_blk",
            "pararnn_gru_forward", "pararnn_lstm_forward", "pararnn_adjoint_backward",
            "pararnn_gru_sequential", "pararnn_lstm_sequential", "pararnn_status_string",
-           "pararnn_gru_forward_noalloc")
+           "pararnn_gru_forward_noalloc", "pararnn_hgru_forward")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # PARARNN_NOALLOC_SCRATCH_BYTES
 
 _lib = None
@@ -61,6 +61,9 @@ def load_library():
     lib.pararnn_lstm_forward.argtypes = [i64, i64, i64] + [vp] * 14 + [
         ctypes.c_float, i32, vp, vp, vp, sz, vp]
     lib.pararnn_lstm_forward.restype = ctypes.c_int
+    lib.pararnn_hgru_forward.argtypes = [i32, i64, i64, i64] + [vp] * 9 + [
+        ctypes.c_float, i32, vp, vp, vp, sz, vp]
+    lib.pararnn_hgru_forward.restype = ctypes.c_int
     lib.pararnn_adjoint_backward.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                              vp, vp, vp, vp, vp, sz, vp]
     lib.pararnn_adjoint_backward.restype = ctypes.c_int
@@ -274,6 +277,42 @@ def lstm_forward(pi, pf, po, pg, ui, uf, uo, ug, h0=None, c0=None, *, tol=1e-4, 
     return h, c
 
 
+def hgru_forward(pz, pr, pc, Uz, Ur, Uc, h0=None, *, tol=1e-4, max_iter=32, out=None, info=None,
+                 trace=None, ws=None, init=None):
+    """Newton solve of the GRU with dense recurrence inside heads of k
+    channels (k = 4 or 8): p [B, L, NH, k], U [NH, k, k], h0 [B, NH, k];
+    returns h [B, L, NH, k].  `init` is Newton's initial iterate (a warm
+    start; it must not share memory with the output); `info`, `trace` as for
+    gru_forward."""
+    lib = load_library()
+    B, L, NH, k = pz.shape
+    dev = pz.device
+    for t, n in ((pz, "pz"), (pr, "pr"), (pc, "pc")):
+        _need(t, (B, L, NH, k), n, dev)
+    for t, n in ((Uz, "Uz"), (Ur, "Ur"), (Uc, "Uc")):
+        _need(t, (NH, k, k), n, dev)
+    if h0 is not None:
+        _need(h0, (B, NH, k), "h0", dev)
+    if init is not None:
+        _need(init, (B, L, NH, k), "init", dev)
+    op = {4: OP_HGRU4_FORWARD, 8: OP_HGRU8_FORWARD}.get(k)
+    if op is None:
+        raise PararnnError("pararnn_hgru_forward supports k = 4 and 8, got %d" % k)
+    h = torch.empty_like(pz) if out is None else out
+    _need(h, (B, L, NH, k), "out", dev)
+    if info is not None and (info.dtype != torch.int32 or info.numel() < 2 or info.device != dev):
+        raise ValueError("info must be an int32 device tensor with 2 elements")
+    if trace is not None and (trace.dtype != torch.float32 or trace.numel() < max_iter or
+                              trace.device != dev):
+        raise ValueError("trace must be a float32 device tensor with max_iter elements")
+    ws, n = _workspace(op, B, L, NH, dev, max_iter, ws)
+    _check(lib.pararnn_hgru_forward(k, B, L, NH, _ptr(pz), _ptr(pr), _ptr(pc), _ptr(Uz), _ptr(Ur),
+                                    _ptr(Uc), _ptr(h0), _ptr(init), _ptr(h), float(tol), int(max_iter),
+                                    _ptr(info), _ptr(trace), _ptr(ws), n, _stream(dev)),
+           "pararnn_hgru_forward")
+    return h
+
+
 def gru_forward_noalloc(pz, pr, pc, uz, ur, uc, h0=None, *, tol=1e-4, max_iter=32, out=None,
                         info=None, trace=None):
     """gru_forward with the library's static scratch buffer as workspace
@@ -298,7 +337,7 @@ def gru_forward_noalloc(pz, pr, pc, uz, ur, uc, h0=None, *, tol=1e-4, max_iter=3
     _check(lib.pararnn_gru_forward_noalloc(B, L, H, _ptr(pz), _ptr(pr), _ptr(pc), _ptr(uz), _ptr(ur),
                                            _ptr(uc), _ptr(h0), _ptr(h), float(tol), int(max_iter),
                                            _ptr(info), _ptr(trace), _stream(dev)),
-           "pararnn_gru_forward_noalloc")
+           "pararnn_gru_forward_noalloc", "pararnn_hgru_forward")
     return h
 
 

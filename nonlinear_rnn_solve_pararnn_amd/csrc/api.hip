@@ -151,6 +151,12 @@ size_t pararnn_workspace_bytes(int32_t op, int64_t B, int64_t L, int64_t H, int3
             return lstm_fwd_ws(B, L, H, eff_cap(max_iter, L));
         case PARARNN_OP_LINSCAN_BLK4: return blk4_ws(B, L, H);
         case PARARNN_OP_LINSCAN_BLK8: return blkrow_ws(8, B, L, H).total;
+        case PARARNN_OP_HGRU4_FORWARD:
+        case PARARNN_OP_HGRU8_FORWARD: {
+            const int k = op == PARARNN_OP_HGRU8_FORWARD ? 8 : 4;
+            if (max_iter < 1 || !dims_ok(B, L, H * k)) return 0;
+            return hgru_ws(k, B, L, H, eff_cap(max_iter, L)).total;
+        }
         case PARARNN_OP_GRU_ADJOINT: return gru_adjoint_ws(B, L, H);
         case PARARNN_OP_LSTM_ADJOINT: return lstm_adjoint_ws(B, L, H);
         default: return 0;
@@ -254,6 +260,29 @@ int pararnn_lstm_forward(int64_t B, int64_t L, int64_t H, const float *pi, const
     const Ws w{static_cast<char *>(ws), ws_bytes};
     if (chain) return status_of(lstm_forward_chain(a, w, s));
     return status_of(lstm_forward_step(a, w, s));
+}
+
+int pararnn_hgru_forward(int32_t k, int64_t B, int64_t L, int64_t NH, const float *pz, const float *pr,
+                         const float *pc, const float *Uz, const float *Ur, const float *Uc, const float *h0,
+                         const float *h_init, float *h, float tol, int32_t max_iter, int32_t *info, float *trace,
+                         void *ws, size_t ws_bytes, void *stream) {
+    if (k < 1) return PARARNN_ERR_INVALID;
+    if (k != 4 && k != 8) return PARARNN_ERR_UNSUPPORTED;
+    if (!dims_ok(B, L, NH) || !dims_ok(B, L, NH * k)) return PARARNN_ERR_INVALID;
+    if (!pz || !pr || !pc || !Uz || !Ur || !Uc || !h) return PARARNN_ERR_INVALID;
+    if (!(tol >= 0.0f) || max_iter < 1) return PARARNN_ERR_INVALID;
+    if (overlaps(h_init, h, B * L * NH * k)) return PARARNN_ERR_INVALID;
+    const int32_t cap = eff_cap(max_iter, L);
+    const HgruWs need = hgru_ws(k, B, L, NH, cap);
+    if (!grid_ok(need.sh.ntiles)) return PARARNN_ERR_INVALID;
+    if (!ws || ws_bytes < need.total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (trace != nullptr && max_iter > cap) {
+        const int st = clear_trace_tail(trace, cap, max_iter, s);
+        if (st != PARARNN_OK) return st;
+    }
+    const HgruFwdArgs a{k, B, L, NH, pz, pr, pc, Uz, Ur, Uc, h0, h_init, h, tol, cap, info, trace};
+    return status_of(hgru_forward(a, Ws{static_cast<char *>(ws), ws_bytes}, s));
 }
 
 int pararnn_gru_sequential(int64_t B, int64_t L, int64_t H, const float *pz, const float *pr,

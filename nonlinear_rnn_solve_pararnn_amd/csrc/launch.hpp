@@ -51,6 +51,19 @@ hipError_t linscan_blk(int k, int64_t B, int64_t L, int64_t H, const float *A, c
 // (hipErrorInvalidValue otherwise); workspace blkrow_ws
 hipError_t linscan_blkrow(int k, int64_t B, int64_t L, int64_t H, const float *A, const float *b,
                           const float *h0, float *h, const Ws &ws, hipStream_t s);
+// Newton forward of the GRU with dense recurrence inside heads of k
+// channels (k = 4, 8): tensors [B, L, NH, k], U [NH, k, k].
+struct HgruFwdArgs {
+    int k;
+    int64_t B, L, NH;
+    const float *pz, *pr, *pc, *Uz, *Ur, *Uc, *h0, *h_init;
+    float *h;
+    float tol;
+    int32_t cap;
+    int32_t *info;
+    float *trace;
+};
+hipError_t hgru_forward(const HgruFwdArgs &a, const Ws &ws, hipStream_t s);
 struct GruFwdArgs {
     int64_t B, L, H;
     const float *pz, *pr, *pc, *uz, *ur, *uc, *h0;
@@ -91,6 +104,16 @@ bool lstm_chain_owns_chains(int64_t B, int64_t L, int64_t H, int local);
 hipError_t gru_rollout(const GruFwdArgs &a, hipStream_t s);
 hipError_t lstm_rollout(const LstmFwdArgs &a, hipStream_t s);
 
+// info = {first k with max|delta| <= tol, 1} or {cap, 0}, trace[k-1] =
+// max|delta| of iteration k, from the per-iteration slots of a workspace
+// (either output may be null).
+hipError_t newton_finalize_launch(const uint32_t *maxd, int cap, float tol, int32_t *info, float *trace,
+                                  hipStream_t s);
+// Warm start of a per-iteration path on a one-component state of H
+// channels per batch row and chunks of T positions: init copied into h, and
+// its state at the last position of every chunk into bnd [chunk][B][H].
+hipError_t newton_seed1(const float *init, float *h, float *bnd, int64_t B, int64_t L, int64_t H, int64_t T,
+                        hipStream_t s);
 struct AdjArgs {
     int64_t B, L, H;
     const float *p[4], *u[4];

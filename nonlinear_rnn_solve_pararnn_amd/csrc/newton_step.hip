@@ -24,35 +24,10 @@
 
 #include "cells.hpp"
 #include "launch.hpp"
+#include "newton_iter.hpp"
 #include "scan_core.hpp"
 
 namespace prn {
-
-__device__ __forceinline__ bool newton_active(const uint32_t *maxd, int k, float tol) {
-    // maxd holds |delta| bits; iterations not run hold 0.
-    return k == 1 || !(__uint_as_float(maxd[k - 2]) <= tol);
-}
-
-// Fold the per-thread max|delta| (bits of non-negative floats; NaN above
-// +inf) over the workgroup and merge it into *dst.  All workgroups of an
-// iteration share *dst, so same-address atomics would serialise: only the
-// workgroup's first thread updates it, and only when its value exceeds the
-// value it reads there (maxima only grow, so a stale read can only cause an
-// unnecessary update, never a lost one).
-template <int NW>
-__device__ __forceinline__ void wg_max_to(uint32_t mx, uint32_t *dst) {
-    __shared__ uint32_t s_wmax[NW];
-    mx = wave_max_u32(clamp_nan_to_inf(mx));
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) s_wmax[w] = mx;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t m = 0;
-        for (int k = 0; k < NW; ++k) m = s_wmax[k] > m ? s_wmax[k] : m;
-        const uint32_t cur = __hip_atomic_load(dst, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (m > cur) __hip_atomic_fetch_max(dst, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-}
 
 // ---------------------------------------------------------------- GRU
 struct GruStepOp {
@@ -311,6 +286,12 @@ __global__ void newton_finalize(const uint32_t *maxd, int cap, float tol, int32_
     }
 }
 
+hipError_t newton_finalize_launch(const uint32_t *maxd, int cap, float tol, int32_t *info, float *trace,
+                                  hipStream_t s) {
+    hipLaunchKernelGGL(newton_finalize, dim3(1), dim3(64), 0, s, maxd, cap, tol, info, trace);
+    return hipGetLastError();
+}
+
 // Warm start of the per-iteration path: the initial iterate (h, and c for
 // S = 2; a null one is zero) copied into the outputs, and its state at the
 // last position of every chunk into the boundary array iteration 1 reads.
@@ -341,6 +322,15 @@ __global__ __launch_bounds__(256) void newton_seed_kernel(SeedArgs a) {
                 static_cast<float2 *>(a.bnd)[slot] = make_float2(cv, hv);
         }
     }
+}
+
+hipError_t newton_seed1(const float *init, float *h, float *bnd, int64_t B, int64_t L, int64_t H, int64_t T,
+                        hipStream_t s) {
+    SeedArgs a{init, nullptr, h, nullptr, bnd, B, L, H, T};
+    const int64_t n = B * L * H;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, (int64_t)device_cu_count() * 8);
+    hipLaunchKernelGGL(newton_seed_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 // Runs the launch sequence shared by both cells.  `make_op(k, bnd_prev,

@@ -214,6 +214,41 @@ inline BlkRowWs blkrow_ws(int k, int64_t B, int64_t L, int64_t H) {
     return w;
 }
 
+// Newton steps of the GRU with dense recurrence inside heads of k channels
+// (hgru.hip): one launch per iteration on the lane-group scan.  Measured for
+// k = 8 at B=16 L=2048 NH=64, 4 iterations: 4 waves x 8 positions (181
+// VGPRs) 1.09 ms, 4 x 4 1.13, 2 x 8 1.14, 8 x 8 1.20, 8 x 4 1.63, 4 x 2 1.71.
+constexpr BlkRowCfg kHgru8{4, 8, 1};
+constexpr BlkRowCfg kHgru4{8, 4, 1};
+
+// Workspace: header, a max|delta| slot per iteration and two sets of
+// chunk-boundary states (kept across the launches of a call: [maxd,
+// keep_end)), then the look-back records of one launch.
+struct HgruWs {
+    BlkRowWs sh;  // chunking and record layout (the sh.hdr/agg/inc/total offsets unused)
+    size_t hdr, maxd, bnd[2], keep_end, agg, inc, total;
+};
+
+inline HgruWs hgru_ws(int k, int64_t B, int64_t L, int64_t NH, int32_t cap) {
+    const BlkRowCfg cfg = k == 8 ? kHgru8 : kHgru4;
+    HgruWs w;
+    w.sh.T = (int64_t)cfg.nw * cfg.c;
+    const int64_t heads = 64 / k;
+    w.sh.ncb = (NH + heads - 1) / heads;
+    w.sh.nq = (L + w.sh.T - 1) / w.sh.T;
+    w.sh.ntiles = w.sh.nq * B * w.sh.ncb;
+    w.sh.nrow = B * NH * k;
+    Carve c;
+    w.hdr = c.take(16);
+    w.maxd = c.take((size_t)cap * 4);
+    for (int i = 0; i < 2; ++i) w.bnd[i] = c.take((size_t)w.sh.nq * w.sh.nrow * 4);
+    w.keep_end = c.off;
+    w.agg = c.take((size_t)w.sh.nq * (k + 1) * w.sh.nrow * 8);
+    w.inc = c.take((size_t)w.sh.nq * w.sh.nrow * 8);
+    w.total = c.off;
+    return w;
+}
+
 // Fused on-chip GRU Newton: one workgroup owns all L positions of
 // kFusedChannels channels of one batch row; each lane is one (channel,
 // sub-chunk), 32 sub-chunks of C positions (so 32 * kFusedChannels / 64

@@ -142,26 +142,71 @@ class _BlockDiagonalSolve(torch.autograd.Function):
     @staticmethod
     def backward(ctx, g):
         h0, s, *tensors = ctx.saved_tensors
-        inputs, params = tensors[:ctx.n_inputs], tensors[ctx.n_inputs:]
-        k = ctx.k
-        with torch.no_grad():
-            _, J = _cell_and_jacobian(ctx.cell, _shift(s, h0), inputs, params, k)
-            if k > 1:
-                J = J.transpose(-1, -2)
-            # lambda_t = g_t + J_{t+1}^T lambda_{t+1}: a scan in reversed time
-            a = torch.cat([J[:, 1:], torch.zeros_like(J[:, :1])], dim=1)
-            lam = _scan(a.flip(1), g.flip(1), k).flip(1)
-        # one vector-Jacobian product of the cell at the converged states
-        with torch.enable_grad():
-            h0_ = h0.detach().requires_grad_(ctx.needs_input_grad[7])
-            ins = [x.detach().requires_grad_(True) for x in tensors]
-            F = ctx.cell(_shift(s, h0_), *ins)
-            wrt = [x for x in [h0_] + ins if x.requires_grad]
-            grads = iter(torch.autograd.grad(F, wrt, grad_outputs=lam, allow_unused=True))
-        gh0 = next(grads) if h0_.requires_grad else None
-        gt = [next(grads) for _ in ins]
-        gt = [torch.zeros_like(x) if gx is None else gx for x, gx in zip(tensors, gt)]
+        gh0, gt = _adjoint(ctx.cell, ctx.k, ctx.n_inputs, h0, s, tensors, g, ctx.needs_input_grad[7])
         return (None, None, None, None, None, None, None, gh0, *gt)
+
+
+def _adjoint(cell, k, n_inputs, h0, s, tensors, g, want_h0):
+    """Gradients of <g, s> through the converged solve s: the adjoint
+    lambda_t = g_t + J_{t+1}^T lambda_{t+1} (a scan in reversed time on the
+    same kernels, transposed blocks), then one vector-Jacobian product of
+    the cell for h0, the inputs and the parameters."""
+    inputs, params = tensors[:n_inputs], tensors[n_inputs:]
+    with torch.no_grad():
+        _, J = _cell_and_jacobian(cell, _shift(s, h0), inputs, params, k)
+        if k > 1:
+            J = J.transpose(-1, -2)
+        a = torch.cat([J[:, 1:], torch.zeros_like(J[:, :1])], dim=1)
+        lam = _scan(a.flip(1), g.flip(1), k).flip(1)
+    with torch.enable_grad():
+        h0_ = h0.detach().requires_grad_(want_h0)
+        ins = [x.detach().requires_grad_(True) for x in tensors]
+        F = cell(_shift(s, h0_), *ins)
+        wrt = [x for x in [h0_] + ins if x.requires_grad]
+        grads = iter(torch.autograd.grad(F, wrt, grad_outputs=lam, allow_unused=True))
+    gh0 = next(grads) if h0_.requires_grad else None
+    gt = [next(grads) for _ in ins]
+    gt = [torch.zeros_like(x) if gx is None else gx for x, gx in zip(tensors, gt)]
+    return gh0, gt
+
+
+class _HeadGruSolve(torch.autograd.Function):
+    """Forward by the library's head-GRU Newton kernel (pararnn_hgru_forward),
+    backward by the adjoint above with head_gru_cell."""
+
+    @staticmethod
+    def forward(ctx, tol, max_iter, info, init, h0, pz, pr, pc, Uz, Ur, Uc):
+        dev_info = torch.zeros(2, dtype=torch.int32, device=pz.device) if info is not None else None
+        s = api.hgru_forward(pz.detach(), pr.detach(), pc.detach(), Uz.detach(), Ur.detach(), Uc.detach(),
+                             h0.detach(), tol=tol, max_iter=max_iter, info=dev_info,
+                             init=None if init is None else init.detach())
+        if info is not None:
+            info[0], info[1] = [int(v) for v in dev_info.tolist()]
+        ctx.save_for_backward(h0, s, pz, pr, pc, Uz, Ur, Uc)
+        ctx.k = pz.shape[-1]
+        return s
+
+    @staticmethod
+    def backward(ctx, g):
+        h0, s, *tensors = ctx.saved_tensors
+        gh0, gt = _adjoint(head_gru_cell, ctx.k, 3, h0, s, tensors, g.contiguous(), ctx.needs_input_grad[4])
+        return (None, None, None, None, gh0, *gt)
+
+
+def head_gru_solve(pz: torch.Tensor, pr: torch.Tensor, pc: torch.Tensor, Uz: torch.Tensor,
+                   Ur: torch.Tensor, Uc: torch.Tensor, h0: Optional[torch.Tensor] = None, *,
+                   tol: float = 1e-4, max_iter: int = 32, info: Optional[list] = None,
+                   init: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The GRU with dense recurrence inside heads of k channels (head_gru_cell,
+    k = 4 or 8) solved by the library's Newton kernel (pararnn_hgru_forward:
+    cell, k x k Jacobian rows and the block scan in one launch per
+    iteration), differentiable with respect to p, U and h0 through the
+    adjoint of the solve.  p [B, L, NH, k], U [NH, k, k], h0 [B, NH, k] or
+    None; `init` a warm start; `info` receives [iterations, converged]."""
+    B, L, NH, k = pz.shape
+    if h0 is None:
+        h0 = torch.zeros((B, NH, k), dtype=pz.dtype, device=pz.device)
+    return _HeadGruSolve.apply(float(tol), int(max_iter), info, init, h0, pz, pr, pc, Uz, Ur, Uc)
 
 
 def newton_solve(cell: Callable[..., torch.Tensor], inputs: Sequence[torch.Tensor],

@@ -51,6 +51,9 @@ WORKLOADS = {
     # 8x8 blocks: heads of 8 channels with dense recurrence inside a head,
     # 64 heads (512 channels), 320 B per block position
     "x_linscan_blk8": dict(kind="linscan_blk", B=16, L=2048, H=64, k=8),
+    # Newton forward of the GRU with dense recurrence inside heads of 8
+    # channels (8x8 Jacobian blocks), 64 heads (512 channels)
+    "x_hgru8_fwd": dict(kind="hgru", B=16, L=2048, H=64, k=8, tol=1e-4, cap=32),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -209,4 +212,6 @@ def workload_inputs(name: str) -> dict:
         return lstm_inputs(B, L, H, seed, grad=True)
     if name in ("x_linscan_blk4", "x_linscan_blk8"):
         return linscan_blk_inputs(B, L, H, w["k"], seed)
+    if name == "x_hgru8_fwd":
+        return head_gru_inputs(B, L, H, w["k"], seed)
     raise KeyError(name)
