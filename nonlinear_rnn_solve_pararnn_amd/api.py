@@ -337,7 +337,7 @@ def gru_forward_noalloc(pz, pr, pc, uz, ur, uc, h0=None, *, tol=1e-4, max_iter=3
     _check(lib.pararnn_gru_forward_noalloc(B, L, H, _ptr(pz), _ptr(pr), _ptr(pc), _ptr(uz), _ptr(ur),
                                            _ptr(uc), _ptr(h0), _ptr(h), float(tol), int(max_iter),
                                            _ptr(info), _ptr(trace), _stream(dev)),
-           "pararnn_gru_forward_noalloc", "pararnn_hgru_forward")
+           "pararnn_gru_forward_noalloc")
     return h
 
 
