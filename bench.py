@@ -72,7 +72,7 @@ DOMINANT = {
     "x_lstm_seq": "lstm_rollout_kernel (sequential application, one thread per channel)",
     "x_gru_long_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
     "x_linscan_blk4": "lg::scan_kernel<LinRowOp<4>,8,8,1> (each block's rows on a group of 4 lanes)",
-    "x_linscan_blk8": "lg::scan_kernel<LinRowOp<8>,4,8,3> (each block's rows on a group of 8 lanes)",
+    "x_linscan_blk8": "lg::scan_kernel<LinRowOp<8>,4,7,3> (each block's rows on a group of 8 lanes)",
     "x_hgru8_fwd": "lg::scan_kernel<HgruStepOp<8>,4,8,1> (one launch per Newton iteration up to the cap; "
                    "launches after convergence exit at once)",
 }
@@ -97,12 +97,18 @@ TRAFFIC = {
     "x_linscan_blk2": {"bytes": 823099538 + 325722144,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
         "sha256": "4b0a47bfb091a9cf"},
-    "x_linscan_blk4": {"bytes": 695714121 + 159006752,
-        "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "blkrow.hip"],
-        "sha256": "1fe76d99e5192a76"},
-    "x_linscan_blk8": {"bytes": 695395877 + 118677426,
-        "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "blkrow.hip"],
-        "sha256": "1fe76d99e5192a76"},
+    "x_linscan_blk4": {"bytes": 695790317 + 159006720,
+        "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "blkrow.hip"],
+        "sha256": "6c07d7fa57928125"},
+    "x_linscan_blk8": {"bytes": 678004122 + 115343360,
+        "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "blkrow.hip"],
+        "sha256": "6c07d7fa57928125"},
+    # per step: the launches of the iterations that ran (the launches after
+    # convergence read and write almost nothing)
+    "x_hgru8_fwd": {"bytes": 1221210608 + 443353828,
+        "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "newton_iter.hpp",
+                    "hgru.hip"],
+        "sha256": "6be214b813f1d95a"},
     "x_lstm_adjoint": {"bytes": 1127497893 + 597172256,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "adjoint.hip"],
         "sha256": "9691b2ad60873d2b"},
@@ -181,36 +187,54 @@ def roofline(name, elements, kernel_ms):
             "kernel_us": kernel_ms * 1e3}
 
 
-# Arithmetic roofs of the Newton kernels that iterate on chip.  VALU issue
-# slots per element and Newton iteration, from rocprofv3 counters of one
-# dispatch (SQ_INSTS_VALU and SQ_INSTS_VALU_TRANS_F32 count wave instructions;
-# times 64 lanes, over elements x iterations): plain instructions count one
-# slot, transcendentals (exp2, reciprocal) four, since they issue at a
-# quarter of the rate (measured: 4.3 multiply-add slots each).  The fp32
-# vector peak of 157.3 TFLOP/s is 78.6 T lane-operations per second of FMA
-# issue, counting packed fp32; the measured plain rate of this build is
-# reported beside it (alu_calibration).
-#  - fused GRU, B=16 L=512 H=4096, 4 iterations: 80,299,017 VALU and
-#    12,615,680 transcendental wave instructions = 38.29 and 6.02 per element
-#    and iteration (the gfx950 assembly of the loop gives 33.8 and 6; the rest
-#    is per-iteration work outside the cell loop);
-#  - LSTM whole chains, B=8 L=2048 H=2048, 4 iterations: 184,651,902 and
-#    20,975,616 = 88.05 and 10.00;
+# Arithmetic roofs of the Newton kernels that iterate on chip, from rocprofv3
+# counters of one dispatch, times 64 lanes, over elements x iterations.
+#
+# Primary basis (published peak): SQ_INSTS_VALU and SQ_INSTS_VALU_TRANS_F32
+# count wave instructions; plain instructions count one slot and
+# transcendentals (exp2, reciprocal) four, against the fp32 vector peak of
+# 157.3 TFLOP/s = 78.6 T lane-operations per second.  The measured
+# multiply-add rate of this build is reported beside it (alu_calibration).
+#  - fused GRU, B=16 L=512 H=4096, 4 iterations: 38.29 VALU and 6.02
+#    transcendental wave instructions per element and iteration (the gfx950
+#    assembly of the loop gives 33.8 and 6; the rest is per-iteration work
+#    outside the cell loop);
+#  - LSTM whole chains, B=8 L=2048 H=2048, 4 iterations: 88.05 and 10.00;
 #  - long GRU forward (chained, time lanes), B=16 L=2^20 H=1, 3 iterations:
-#    37,723,419 and 4,777,984 = 47.97 and 6.08.
+#    47.97 and 6.08;
+#  - GRU with 8x8 heads, B=16 L=2048 NH=64, per launch of one iteration:
+#    347.87 and 6.02.
 ALU_SLOTS_PER_ELEMENT_ITER = {
     "c2_gru_fused": (38.29 - 6.02) + 6.02 * 4,
     "c3_lstm": (88.05 - 10.00) + 10.00 * 4,
     "x_gru_long_fwd": (47.97 - 6.08) + 6.08 * 4,
+    "x_hgru8_fwd": (347.87 - 6.02) + 6.02 * 4,
 }
 PEAK_VALU_TOPS = 78.6
+# Issue basis: SQ_ACTIVE_INST_VALU counts the quad-cycles a SIMD spends
+# issuing a wave's VALU instructions (one per plain instruction, two per
+# transcendental, as the probes' own counters show).  A SIMD issues one such
+# quad-cycle at a time unless two waves' plain instructions pair up, which
+# the probes show happens for pure multiply-add streams (2 per quad-cycle: the
+# 66.9 T rate) but hardly at all once transcendentals are mixed in (under 4%
+# of quad-cycles in a probe of 8 transcendentals and 4-36 multiply-adds per
+# step; 17% in the fused GRU, 7% in the LSTM).  The roof is then the
+# single-issue rate, measured live with one wave per SIMD (alu_calibration,
+# "fma_1wave"), against the issue quad-cycles per element and iteration:
+ALU_ISSUE_PER_ELEMENT_ITER = {
+    "c2_gru_fused": 44.31,
+    "c3_lstm": 98.05,
+    "x_gru_long_fwd": 54.05,
+    "x_hgru8_fwd": 353.88,
+}
 
 
 def alu_roofline(name, elements, iterations, kernel_ms, calib=None):
     """Arithmetic roof: issue slots over the kernel time, against the
-    published fp32 vector peak (the primary basis, which counts packed fp32
-    issue) and, when `calib` is given, against the measured plain
-    multiply-add rate of this device with packed fp32 off (the build's)."""
+    published fp32 vector peak (the primary basis) and, when `calib` is given,
+    against the measured multiply-add rate of this build (two waves per SIMD
+    pairing their instructions) and the issue quad-cycles against the
+    measured single-issue rate (one wave per SIMD)."""
     per = ALU_SLOTS_PER_ELEMENT_ITER[name]
     slots = per * elements * iterations
     achieved = slots / (kernel_ms * 1e-3) / 1e12
@@ -222,6 +246,12 @@ def alu_roofline(name, elements, iterations, kernel_ms, calib=None):
         fma = calib["fma"]["lane_ops_per_s"] / 1e12
         out["peak_measured_fma"] = fma
         out["frac_measured_fma"] = achieved / fma
+        if "fma_1wave" in calib:
+            one = calib["fma_1wave"]["lane_ops_per_s"] / 1e12
+            issue = ALU_ISSUE_PER_ELEMENT_ITER[name] * elements * iterations / (kernel_ms * 1e-3) / 1e12
+            out["issue"] = {"achieved": issue, "peak_single_issue": one, "frac": issue / one,
+                            "model": "%.2f VALU issue quad-cycles x 64 lanes per element and Newton "
+                                     "iteration (SQ_ACTIVE_INST_VALU)" % ALU_ISSUE_PER_ELEMENT_ITER[name]}
     return out
 
 
@@ -420,20 +450,70 @@ def alu_calibration(dev):
     out = torch.empty(blocks * tpb, device=dev)
     stream = torch.cuda.current_stream(dev)
     res = {}
-    for name, fn, iters in (("fma", lib.alu_probe_fma, 2048), ("exp2_rcp", lib.alu_probe_trans, 256)):
-        ops = blocks * tpb * iters * steps * (1 if name == "fma" else 2)
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    # one workgroup of 4 waves per CU: one wave per SIMD, no pairing
+    for name, fn, iters, nb in (("fma", lib.alu_probe_fma, 2048, blocks),
+                                ("exp2_rcp", lib.alu_probe_trans, 256, blocks),
+                                ("fma_1wave", lib.alu_probe_fma, 8192, ncu)):
+        ops = nb * tpb * iters * steps * (2 if name == "exp2_rcp" else 1)
         for _ in range(2):
-            assert fn(blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream)) == 0
+            assert fn(nb, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream)) == 0
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        assert fn(blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream)) == 0
+        assert fn(nb, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream)) == 0
         e1.record(stream)
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
         res[name] = {"lane_ops_per_s": ops / (ms * 1e-3), "ms": ms, "lane_ops": ops}
     res["what"] = ("alu_probe.hip: v_fma (fmamk) chains, and exp2 + add + reciprocal chains "
-                   "(2 transcendental lane-ops per step), %d workgroups of %d threads" % (blocks, tpb))
+                   "(2 transcendental lane-ops per step), %d workgroups of %d threads; fma_1wave: the "
+                   "fma chains with one workgroup per CU (one wave per SIMD)" % (blocks, tpb))
     return res
+
+
+def issue_probe(dev):
+    """How a SIMD shares its issue between waves (alu_probe.hip): the
+    multiply-add chains at 1, 2, 4 and 8 waves per SIMD (1, 2, 4, 8
+    workgroups of 4 waves per CU), and the mix probe (4 exp2/add/reciprocal
+    chains plus m multiply-adds per step) at 8 waves per SIMD.  Rates in lane
+    operations per second; HIP events on the launch stream."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "nonlinear_rnn_solve_pararnn_amd", "libpararnn_probe.so"))
+    lib.alu_probe_fma.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.alu_probe_mix.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    tpb, steps = lib.alu_probe_threads_per_block(), lib.alu_probe_steps_per_iter()
+    msteps = lib.alu_probe_mix_steps_per_iter()
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(ncu * 8 * tpb, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(launch):
+        for _ in range(2):
+            assert launch() == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        assert launch() == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
+
+    rows = []
+    for wps in (1, 2, 4, 8):
+        nb, iters = ncu * wps, 2048
+        sec = timed(lambda: lib.alu_probe_fma(nb, iters, ctypes.c_void_p(out.data_ptr()), sp))
+        rows.append({"probe": "fma", "waves_per_simd": wps, "ms": sec * 1e3,
+                     "fma_lane_ops_per_s": nb * tpb * iters * steps / sec})
+    for m in (0, 4, 8, 16, 32):
+        nb, iters = ncu * 8, 512
+        sec = timed(lambda: lib.alu_probe_mix(nb, iters, m, ctypes.c_void_p(out.data_ptr()), sp))
+        n = nb * tpb * iters * msteps  # lane-steps
+        rows.append({"probe": "mix", "fma_per_step": m, "waves_per_simd": 8, "ms": sec * 1e3,
+                     "trans_lane_ops_per_s": n * 8 / sec, "plain_lane_ops_per_s": n * (m + 4) / sec,
+                     "ns_per_step_per_simd_lane": sec / n * 1e9 * ncu * 4 * 64})
+    return rows
 
 
 def log(*a):
@@ -710,6 +790,8 @@ def main():
                     help="leave out the modality sweep and residual traces")
     ap.add_argument("--modalities", action="store_true",
                     help="only the modality sweep and residual traces (one JSON line)")
+    ap.add_argument("--issue-probe", action="store_true",
+                    help="print the issue-sharing probe table (alu_probe.hip) and exit")
     ap.add_argument("--alu-calibration", action="store_true",
                     help="print the measured fp32 multiply-add and exp2/reciprocal issue rates")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -730,6 +812,10 @@ def main():
         print(json.dumps(modalities(dev)), flush=True)
         return
 
+    if args.issue_probe:
+        for row in issue_probe(dev):
+            print(json.dumps(row), flush=True)
+        return
     if args.alu_calibration:
         print(json.dumps(alu_calibration(dev)), flush=True)
         return

@@ -59,12 +59,16 @@ struct LinRowOp {
 
     template <int C>
     __device__ RowK<K> phase1(const Pos &p, Elem (&e)[C]) const {
+        // Branch-free: a position past the end (or a missing head) reads
+        // block 0 and takes the identity map in its place.
+        const int64_t base = (p.b * L + p.pos0) * H + p.j;
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            if (p.ok && p.pos0 + i < L)
-                load_row((p.b * L + p.pos0 + i) * H + p.j, p.c, e[i].m);
-            else
-                e[i].m = row_id<K>();
+            const bool v = p.ok && p.pos0 + i < L;
+            load_row(v ? base + i * H : 0, p.c, e[i].m);
+#pragma unroll
+            for (int k = 0; k < K; ++k) e[i].m.a[k] = v ? e[i].m.a[k] : (k == 0 ? 1.0f : 0.0f);
+            e[i].m.b = v ? e[i].m.b : 0.0f;
         }
         RowK<K> m = e[0].m;
 #pragma unroll

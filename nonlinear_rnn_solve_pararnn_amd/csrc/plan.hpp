@@ -179,12 +179,13 @@ struct BlkRowCfg {
     int nw, c;
     int minw;  // waves per SIMD the kernel's registers must allow
 };
-// Measured at B=16, L=2048 (8x8: H=64 heads, 4x4: H=256): 8x8 with 4 waves
-// x 8 positions bounded to 168 registers (three workgroups per CU, a few
-// spills) 166 us, unbounded (180 registers, two per CU) 188 us, 8 x 4 or
-// 4 x 16 250-315 us; 4x4 with 8 waves x 8 positions 180 us, 8 x 4 229-239
-// us, 4 x 8 238 us.
-constexpr BlkRowCfg kBlkRow8{4, 8, 3};
+// Measured at B=16, L=2048 (8x8: H=64 heads, 4x4: H=256) with branch-free
+// loads: 8x8 with 4 waves x 7 positions bounded to 168 registers (three
+// workgroups per CU, no spills in the 16-byte path) 159-161 us, 4 x 8 at
+// 168 registers (spilling) 166 us, 4 x 6 175 us, 8 x 7 190 us; 4x4 with 8
+// waves x 8 positions 157 us, 8 x 6 or 4 x 12 174-176 us, 8 x 10 184 us,
+// 4 x 8 or 16 x 4 236-240 us.
+constexpr BlkRowCfg kBlkRow8{4, 7, 3};
 constexpr BlkRowCfg kBlkRow4{8, 8, 1};
 // The lane exchanges of the lane-group scan ride on the multiply-adds
 // (v_fmac_f32 with a DPP operand) instead of separate DPP moves.

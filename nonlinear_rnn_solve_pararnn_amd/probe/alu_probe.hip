@@ -51,6 +51,34 @@ __global__ __launch_bounds__(kThreads) void trans_probe_kernel(int iters, float 
     out[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
+// Per step: four chains of (exp2, add, reciprocal) and M multiply-adds on
+// eight other chains, the mix of the Newton cells (transcendentals among
+// plain instructions), to see how the two share the issue of a SIMD.
+template <int M>
+__global__ __launch_bounds__(kThreads) void mix_probe_kernel(int iters, float *out) {
+    float t[4], a[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = 1e-3f * (threadIdx.x + k);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = 1e-3f * (threadIdx.x + k);
+    const float m = 0.9999f, c = 1e-4f;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) t[k] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(t[k]));
+#pragma unroll
+            for (int r = 0; r < M; ++r) a[r & 7] = fmaf(a[r & 7], m, c);
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s += t[k];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += a[k];
+    out[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -70,6 +98,24 @@ int alu_probe_fma(int64_t blocks, int32_t iters, float *out, void *stream) {
 int alu_probe_trans(int64_t blocks, int32_t iters, float *out, void *stream) {
     hipLaunchKernelGGL(trans_probe_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), iters, out);
+    return (int)hipGetLastError();
+}
+
+// Steps per iteration of the mix probe (each: 4 x (exp2, add, reciprocal)
+// and m multiply-adds, m in {0, 4, 8, 16, 32}); returns -1 for another m.
+int alu_probe_mix_steps_per_iter(void) { return 8; }
+
+int alu_probe_mix(int64_t blocks, int32_t iters, int32_t m, float *out, void *stream) {
+    const dim3 g((unsigned)blocks), b(kThreads);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (m) {
+        case 0: hipLaunchKernelGGL(mix_probe_kernel<0>, g, b, 0, s, iters, out); break;
+        case 4: hipLaunchKernelGGL(mix_probe_kernel<4>, g, b, 0, s, iters, out); break;
+        case 8: hipLaunchKernelGGL(mix_probe_kernel<8>, g, b, 0, s, iters, out); break;
+        case 16: hipLaunchKernelGGL(mix_probe_kernel<16>, g, b, 0, s, iters, out); break;
+        case 32: hipLaunchKernelGGL(mix_probe_kernel<32>, g, b, 0, s, iters, out); break;
+        default: return -1;
+    }
     return (int)hipGetLastError();
 }
 

@@ -109,9 +109,9 @@ def test_initial_iterate_must_not_overlap_outputs(lib):
 
 
 def test_blk8_workspace_query():
-    # header 256 B, then per chunk of 32 positions 9 aggregate words and 1
-    # inclusive word per (batch row, head, row)
-    nq, nrow = 2048 // 32, 16 * 64 * 8
+    # header 256 B, then per chunk of 28 positions (4 waves x 7) 9 aggregate
+    # words and 1 inclusive word per (batch row, head, row)
+    nq, nrow = -(-2048 // 28), 16 * 64 * 8
     assert api.workspace_bytes(api.OP_LINSCAN_BLK8, 16, 2048, 64) == 256 + nq * 9 * nrow * 8 + nq * nrow * 8
     assert api.workspace_bytes(api.OP_LINSCAN_BLK8, 0, 2048, 64) == 0
 
@@ -125,3 +125,24 @@ def test_product_path_does_not_use_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "liboracle" not in text and "oracle.c" not in text, f
+
+
+def test_binding_calls_match_the_declared_signatures(lib):
+    """Every library call in the binding passes as many arguments as its
+    ctypes signature declares, and every status check names what failed."""
+    import ast
+    tree = ast.parse(open(api.__file__).read())
+    calls = checks = 0
+    for node in ast.walk(tree):
+        if not isinstance(node, ast.Call):
+            continue
+        f = node.func
+        if isinstance(f, ast.Name) and f.id == "_check":
+            checks += 1
+            assert len(node.args) == 2 and not node.keywords, ast.unparse(node)[:120]
+        if (isinstance(f, ast.Attribute) and isinstance(f.value, ast.Name) and f.value.id == "lib"
+                and f.attr.startswith(("pararnn_", "rnn_"))):
+            calls += 1
+            assert not any(isinstance(a, ast.Starred) for a in node.args), f.attr
+            assert len(node.args) == len(getattr(lib, f.attr).argtypes), f.attr
+    assert calls >= 10 and checks >= 10

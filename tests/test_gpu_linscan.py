@@ -253,7 +253,7 @@ def test_linscan_blk4_thread_path(orc, monkeypatch):
         assert max_abs(h, orc.linscan_blk(d["A"], d["b"], d["h0"])) <= FWD_ATOL
 
 
-# 8x8 blocks: 8 heads per wave, chunks of 4 waves x 8 positions; ragged head
+# 8x8 blocks: 8 heads per wave, chunks of 4 waves x 7 positions; ragged head
 # blocks (H not a multiple of 8), ragged chunks, a single head over a long L.
 BLK8_SHAPES = [(1, 1, 1), (2, 100, 3), (3, 257, 9), (2, 1500, 2), (2, 300, 16), (1, 64, 8),
                (2, 97, 13), (1, 3000, 1)]
