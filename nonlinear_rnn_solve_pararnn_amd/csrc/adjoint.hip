@@ -264,15 +264,17 @@ struct LstmAdjOp {
             wo = uo[tp.j];
             wg = ug[tp.j];
         }
-        Aff2 acc = MonoidT<2>::id();
+        Aff2 acc;
         if (tp.ok && tp.pos0 + C <= L) {  // every position inside: no test per position
 #pragma unroll
             for (int i = 0; i < C; ++i) {
                 const int64_t t = L - 1 - (tp.pos0 + i);
-                acc = MonoidT<2>::then(acc, elem_at(tp, t, idx3(tp.b, t, tp.j, L, H), wi, wf, wo, wg, e[i]));
+                const Aff2 m = elem_at(tp, t, idx3(tp.b, t, tp.j, L, H), wi, wf, wo, wg, e[i]);
+                acc = i == 0 ? m : MonoidT<2>::then(acc, m);
             }
             return acc;
         }
+        acc = MonoidT<2>::id();
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             const int64_t pos = tp.pos0 + i;

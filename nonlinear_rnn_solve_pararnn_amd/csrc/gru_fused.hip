@@ -198,10 +198,19 @@ __global__ __launch_bounds__(kNW * 64, 4) void gru_fused_kernel(FusedGruArgs a) 
     bool val[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) {
+        // every load issued, none behind a branch (a position outside reads
+        // element 0), so they are all in flight together; scaled afterwards
         val[i] = FULL || (ok && (t0 + i < L));
-        xz[i] = val[i] ? kE1 * a.pz[base + i * H] : 0.0f;
-        xr[i] = val[i] ? kE1 * a.pr[base + i * H] : 0.0f;
-        xc[i] = val[i] ? kE2 * a.pc[base + i * H] : 0.0f;
+        const int64_t e = val[i] ? base + i * H : 0;
+        xz[i] = a.pz[e];
+        xr[i] = a.pr[e];
+        xc[i] = a.pc[e];
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        xz[i] = val[i] ? kE1 * xz[i] : 0.0f;
+        xr[i] = val[i] ? kE1 * xr[i] : 0.0f;
+        xc[i] = val[i] ? kE2 * xc[i] : 0.0f;
     }
     const float uz = ok ? a.uz[j] : 0.0f, ur = ok ? a.ur[j] : 0.0f, uc = ok ? a.uc[j] : 0.0f;
     const float hinit = (ok && a.h0 != nullptr) ? a.h0[b * H + j] : 0.0f;

@@ -309,9 +309,9 @@ struct LinBlk2Op {
                     e[i].m = MonoidT<2>::id();
             }
         }
-        Aff2 acc = MonoidT<2>::id();
+        Aff2 acc = e[0].m;
 #pragma unroll
-        for (int i = 0; i < C; ++i) acc = MonoidT<2>::then(acc, e[i].m);
+        for (int i = 1; i < C; ++i) acc = MonoidT<2>::then(acc, e[i].m);
         return acc;
     }
     template <int C, int NW, bool CL>
@@ -420,9 +420,9 @@ struct LinBlkOp {
                     e[i].m = M::id();
             }
         }
-        AffK<K> acc = M::id();
+        AffK<K> acc = e[0].m;
 #pragma unroll
-        for (int i = 0; i < C; ++i) acc = M::then(acc, e[i].m);
+        for (int i = 1; i < C; ++i) acc = M::then(acc, e[i].m);
         return acc;
     }
     __device__ void store_state(int64_t e, const VecK<K> &x) const {

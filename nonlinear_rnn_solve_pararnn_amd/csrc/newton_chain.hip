@@ -103,9 +103,18 @@ struct GruChain {
         }
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            x[0][i] = val[i] ? kE1 * ld_once(pz + base + i * H) : 0.0f;
-            x[1][i] = val[i] ? kE1 * ld_once(pr + base + i * H) : 0.0f;
-            x[2][i] = val[i] ? kE2 * ld_once(pc + base + i * H) : 0.0f;
+            // every load issued, none behind a branch (a position outside
+            // reads element 0), so they are all in flight together
+            const int64_t e = val[i] ? base + i * H : 0;
+            x[0][i] = ld_once(pz + e);
+            x[1][i] = ld_once(pr + e);
+            x[2][i] = ld_once(pc + e);
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            x[0][i] = val[i] ? kE1 * x[0][i] : 0.0f;
+            x[1][i] = val[i] ? kE1 * x[1][i] : 0.0f;
+            x[2][i] = val[i] ? kE2 * x[2][i] : 0.0f;
         }
     }
     // Newton map of one position: delta -> J delta + (F - s), F and J at hp.
@@ -145,11 +154,22 @@ struct LstmChain {
     bool runs;  // unused: the LSTM moves scalars
 
     struct W {
-        float ui, uf, uo, ug;
+        float ui, uf, uo, ug;      // as given (the Jacobian)
+        float uis, ufs, uos, ugs;  // pre-scaled as the gate inputs (the gates)
     };
     __device__ W weights(int64_t j, bool ok) const {
-        if (!ok) return {0.0f, 0.0f, 0.0f, 0.0f};
-        return {ui[j], uf[j], uo[j], ug[j]};
+        W w{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+        if (ok) {
+            w.ui = ui[j];
+            w.uf = uf[j];
+            w.uo = uo[j];
+            w.ug = ug[j];
+            w.uis = kE1 * w.ui;
+            w.ufs = kE1 * w.uf;
+            w.uos = kE1 * w.uo;
+            w.ugs = kE2 * w.ug;
+        }
+        return w;
     }
     __device__ float2s init(int64_t b, int64_t j, int64_t H) const {
         return {c0 != nullptr ? c0[b * H + j] : 0.0f, h0 != nullptr ? h0[b * H + j] : 0.0f};
@@ -162,15 +182,36 @@ struct LstmChain {
     __device__ void load(int64_t base, int64_t H, const bool (&val)[C], bool, float (&x)[NG][C]) const {
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            x[0][i] = val[i] ? ld_once(pi + base + i * H) : 0.0f;
-            x[1][i] = val[i] ? ld_once(pf + base + i * H) : 0.0f;
-            x[2][i] = val[i] ? ld_once(po + base + i * H) : 0.0f;
-            x[3][i] = val[i] ? ld_once(pg + base + i * H) : 0.0f;
+            // every load issued, none behind a branch (a position outside
+            // reads element 0), so they are all in flight together
+            const int64_t e = val[i] ? base + i * H : 0;
+            x[0][i] = ld_once(pi + e);
+            x[1][i] = ld_once(pf + e);
+            x[2][i] = ld_once(po + e);
+            x[3][i] = ld_once(pg + e);
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            x[0][i] = val[i] ? kE1 * x[0][i] : 0.0f;
+            x[1][i] = val[i] ? kE1 * x[1][i] : 0.0f;
+            x[2][i] = val[i] ? kE1 * x[2][i] : 0.0f;
+            x[3][i] = val[i] ? kE2 * x[3][i] : 0.0f;
         }
     }
+    // Newton map of one position on the pre-scaled gate inputs (pi, pf, po by
+    // -log2 e, pg by -2 log2 e): the arithmetic of lstm_f_j in cells.hpp with
+    // each gate's pre-activation one fma in the exp2 domain.
     __device__ Aff2 step(const W &w, float2s hp, float xi, float xf, float xo, float xg, float2s s) const {
-        const Lstm2 r = lstm_f_j(hp.x, hp.y, xi, xf, xo, xg, w.ui, w.uf, w.uo, w.ug);
-        return {r.j00, r.j01, r.j10, r.j11, r.Fc - s.x, r.Fh - s.y};
+        const float h = hp.y, cp = hp.x;
+        const float i = fast_rcp(1.0f + fast_exp2(fmaf(w.uis, h, xi)));
+        const float f = fast_rcp(1.0f + fast_exp2(fmaf(w.ufs, h, xf)));
+        const float o = fast_rcp(1.0f + fast_exp2(fmaf(w.uos, h, xo)));
+        const float g = fmaf(2.0f, fast_rcp(1.0f + fast_exp2(fmaf(w.ugs, h, xg))), -1.0f);
+        const float c = fmaf(f, cp, i * g);
+        const float tc = fmaf(2.0f, fast_rcp(1.0f + fast_exp2(kE2 * c)), -1.0f);
+        const float odtc = o * fmaf(-tc, tc, 1.0f);
+        const float kappa = fmaf(cp * fmaf(-f, f, f), w.uf, fmaf(g * fmaf(-i, i, i), w.ui, i * fmaf(-g, g, 1.0f) * w.ug));
+        return {f, kappa, odtc * f, fmaf(fmaf(-o, o, o) * w.uo, tc, odtc * kappa), c - s.x, o * tc - s.y};
     }
     template <int C>
     __device__ void store(int64_t base, int64_t H, const bool (&val)[C], bool, const float2s (&s)[C]) const {
@@ -484,9 +525,9 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
             hp = cell.guess(base - g.H);  // iterate 0 before this sub-chunk
         }
         e[0] = cell_step<Cell, C>(cell, wts, hp, x, 0, s[0]);
-        Map acc = M::id();
+        Map acc = e[0];
 #pragma unroll
-        for (int i = 0; i < C; ++i) acc = M::then(acc, e[i]);
+        for (int i = 1; i < C; ++i) acc = M::then(acc, e[i]);
 
         // exclusive prefix of this sub-chunk inside the chunk, and the chunk aggregate
         Map ex, tot;
@@ -499,11 +540,11 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
 #pragma unroll
             for (int kk = 0; kk < NS - 1; ++kk)
                 if (kk < sub) pv[kk] = s_part[kk * CW + ch];
-            ex = M::id();
+            ex = sub > 0 ? pv[0] : M::id();
 #pragma unroll
-            for (int kk = 0; kk < NS - 1; ++kk)
+            for (int kk = 1; kk < NS - 1; ++kk)
                 if (kk < sub) ex = M::then(ex, pv[kk]);
-            tot = M::then(ex, acc);
+            tot = sub > 0 ? M::then(ex, acc) : acc;
         } else {
             Map incl = acc;
 #pragma unroll

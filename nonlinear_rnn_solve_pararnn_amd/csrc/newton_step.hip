@@ -203,7 +203,7 @@ struct LstmStepOp {
                 hp = h[base - H];
             }
         }
-        Aff2 acc = MonoidT<2>::id();
+        Aff2 acc;
         const auto cell = [&](int i) {
             const int64_t kk = base + i * H;
             const float cc = cold1 ? 0.0f : c[kk];
@@ -220,7 +220,7 @@ struct LstmStepOp {
 #pragma unroll
             for (int i = 0; i < C; ++i) {
                 cell(i);
-                acc = MonoidT<2>::then(acc, e[i].m);
+                acc = i == 0 ? e[0].m : MonoidT<2>::then(acc, e[i].m);
             }
             return acc;
         }
@@ -233,7 +233,7 @@ struct LstmStepOp {
                 e[i].cc = 0.0f;
                 e[i].hc = 0.0f;
             }
-            acc = MonoidT<2>::then(acc, e[i].m);
+            acc = i == 0 ? e[0].m : MonoidT<2>::then(acc, e[i].m);
         }
         return acc;
     }
