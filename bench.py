@@ -82,45 +82,49 @@ DOMINANT = {
 # taken on: the sha256 prefix of those sources is checked at run time and the
 # figure is dropped (null) once any of them has changed.
 TRAFFIC = {
-    "c1_linscan": {"bytes": 551347858 + 289021984,
+    "c1_linscan": {"bytes": 551301358 + 289021984,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-        "sha256": "4b0a47bfb091a9cf"},
-    "c2_gru_fused": {"bytes": 418834928 + 152145828,
+        "sha256": "70f3305fa6c96cd4"},
+    "c2_gru_fused": {"bytes": 418850000 + 151935796,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
-        "sha256": "b556fecc9dd4ee85"},
-    "c3_lstm": {"bytes": 537180976 + 268440012,
-        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "97d21beaa40395d3"},
-    "c4_gru_long_fwd_adj": {"bytes": 543722480 + 269388476,
-        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "newton_chain.hip", "adjoint.hip"],
-        "sha256": "2b26ccb117de1248"},
-    "x_linscan_blk2": {"bytes": 823099538 + 325722144,
+        "sha256": "2cf2b08fafae5079"},
+    "c3_lstm": {"bytes": 537186752 + 268440696,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
+                    "scan_core.hpp", "newton_chain.hip"],
+        "sha256": "bb06c9ca75067026"},
+    "c4_gru_long_fwd_adj": {"bytes": 546381664 + 269407176,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp",
+                    "newton_chain.hip", "adjoint.hip"],
+        "sha256": "170a061ec829a393"},
+    "x_linscan_blk2": {"bytes": 823221138 + 325722144,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-        "sha256": "4b0a47bfb091a9cf"},
-    "x_linscan_blk4": {"bytes": 695790317 + 159006720,
+        "sha256": "70f3305fa6c96cd4"},
+    "x_linscan_blk4": {"bytes": 695774939 + 159006752,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "blkrow.hip"],
         "sha256": "6c07d7fa57928125"},
-    "x_linscan_blk8": {"bytes": 678004122 + 115343360,
+    "x_linscan_blk8": {"bytes": 677625033 + 115343392,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "blkrow.hip"],
         "sha256": "6c07d7fa57928125"},
+    "x_lstm_adjoint": {"bytes": 1127552658 + 597172256,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
+                    "scan_core.hpp", "adjoint.hip"],
+        "sha256": "4817b8e8a7d4ed39"},
+    "x_gru_long_fwd": {"bytes": 206417104 + 67810172,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
+                    "scan_core.hpp", "newton_chain.hip"],
+        "sha256": "bb06c9ca75067026"},
+    "x_gru_seq": {"bytes": 402870181 + 134217728,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
+        "sha256": "91a3de061c0d874e"},
+    "x_lstm_seq": {"bytes": 537126747 + 268435456,
+        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
+        "sha256": "91a3de061c0d874e"},
     # per step: the launches of the iterations that ran (the launches after
     # convergence read and write almost nothing)
-    "x_hgru8_fwd": {"bytes": 1221210608 + 443353828,
-        "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "newton_iter.hpp",
-                    "hgru.hip"],
+    "x_hgru8_fwd": {"bytes": 1218613536 + 443353740,
+        "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp",
+                    "newton_iter.hpp", "hgru.hip"],
         "sha256": "6be214b813f1d95a"},
-    "x_lstm_adjoint": {"bytes": 1127497893 + 597172256,
-        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "adjoint.hip"],
-        "sha256": "9691b2ad60873d2b"},
-    "x_gru_long_fwd": {"bytes": 204295056 + 67766220,
-        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "97d21beaa40395d3"},
-    "x_gru_seq": {"bytes": 402868535 + 134217728,
-        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
-        "sha256": "41f86b710348291f"},
-    "x_lstm_seq": {"bytes": 537126766 + 268435456,
-        "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
-        "sha256": "41f86b710348291f"},
 }
 DESCRIBE = {
     "c1_linscan": "linear diagonal recurrence h_t = a_t h_{t-1} + b_t, B=16 L=4096 H=1024, "
@@ -195,20 +199,20 @@ def roofline(name, elements, kernel_ms):
 # transcendentals (exp2, reciprocal) four, against the fp32 vector peak of
 # 157.3 TFLOP/s = 78.6 T lane-operations per second.  The measured
 # multiply-add rate of this build is reported beside it (alu_calibration).
-#  - fused GRU, B=16 L=512 H=4096, 4 iterations: 38.29 VALU and 6.02
+#  - fused GRU, B=16 L=512 H=4096, 4 iterations: 38.32 VALU and 6.02
 #    transcendental wave instructions per element and iteration (the gfx950
 #    assembly of the loop gives 33.8 and 6; the rest is per-iteration work
 #    outside the cell loop);
-#  - LSTM whole chains, B=8 L=2048 H=2048, 4 iterations: 88.05 and 10.00;
+#  - LSTM whole chains, B=8 L=2048 H=2048, 4 iterations: 82.98 and 10.00;
 #  - long GRU forward (chained, time lanes), B=16 L=2^20 H=1, 3 iterations:
-#    47.97 and 6.08;
+#    47.43 and 6.08;
 #  - GRU with 8x8 heads, B=16 L=2048 NH=64, per launch of one iteration:
-#    347.87 and 6.02.
+#    347.81 and 6.02.
 ALU_SLOTS_PER_ELEMENT_ITER = {
-    "c2_gru_fused": (38.29 - 6.02) + 6.02 * 4,
-    "c3_lstm": (88.05 - 10.00) + 10.00 * 4,
-    "x_gru_long_fwd": (47.97 - 6.08) + 6.08 * 4,
-    "x_hgru8_fwd": (347.87 - 6.02) + 6.02 * 4,
+    "c2_gru_fused": (38.32 - 6.02) + 6.02 * 4,
+    "c3_lstm": (82.98 - 10.00) + 10.00 * 4,
+    "x_gru_long_fwd": (47.43 - 6.08) + 6.08 * 4,
+    "x_hgru8_fwd": (347.81 - 6.02) + 6.02 * 4,
 }
 PEAK_VALU_TOPS = 78.6
 # Issue basis: SQ_ACTIVE_INST_VALU counts the quad-cycles a SIMD spends
@@ -218,14 +222,14 @@ PEAK_VALU_TOPS = 78.6
 # the probes show happens for pure multiply-add streams (2 per quad-cycle: the
 # 66.9 T rate) but hardly at all once transcendentals are mixed in (under 4%
 # of quad-cycles in a probe of 8 transcendentals and 4-36 multiply-adds per
-# step; 17% in the fused GRU, 7% in the LSTM).  The roof is then the
+# step; 17% in the fused GRU, 9% in the LSTM).  The roof is then the
 # single-issue rate, measured live with one wave per SIMD (alu_calibration,
 # "fma_1wave"), against the issue quad-cycles per element and iteration:
 ALU_ISSUE_PER_ELEMENT_ITER = {
-    "c2_gru_fused": 44.31,
-    "c3_lstm": 98.05,
-    "x_gru_long_fwd": 54.05,
-    "x_hgru8_fwd": 353.88,
+    "c2_gru_fused": 44.34,
+    "c3_lstm": 92.98,
+    "x_gru_long_fwd": 53.51,
+    "x_hgru8_fwd": 353.82,
 }
 
 
@@ -502,7 +506,7 @@ def issue_probe(dev):
 
     rows = []
     for wps in (1, 2, 4, 8):
-        nb, iters = ncu * wps, 2048
+        nb, iters = ncu * wps, 16384 // wps  # about 2 ms a launch
         sec = timed(lambda: lib.alu_probe_fma(nb, iters, ctypes.c_void_p(out.data_ptr()), sp))
         rows.append({"probe": "fma", "waves_per_simd": wps, "ms": sec * 1e3,
                      "fma_lane_ops_per_s": nb * tpb * iters * steps / sec})
