@@ -73,7 +73,7 @@ DOMINANT = {
     "x_gru_long_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
     "x_linscan_blk4": "lg::scan_kernel<LinRowOp<4>,8,8,1> (each block's rows on a group of 4 lanes)",
     "x_linscan_blk8": "lg::scan_kernel<LinRowOp<8>,4,7,3> (each block's rows on a group of 8 lanes)",
-    "x_hgru8_fwd": "lg::scan_kernel<HgruStepOp<8>,4,8,1> (one launch per Newton iteration up to the cap; "
+    "x_hgru8_fwd": "lg::scan_kernel<HgruStepOp<8>,4,6,3> (one launch per Newton iteration up to the cap; "
                    "launches after convergence exit at once)",
 }
 # HBM bytes per launch of the dominant kernel from rocprofv3 counter runs
@@ -84,47 +84,47 @@ DOMINANT = {
 TRAFFIC = {
     "c1_linscan": {"bytes": 551301358 + 289021984,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-        "sha256": "70f3305fa6c96cd4"},
+        "sha256": "12cb7a3dab2680ec"},
     "c2_gru_fused": {"bytes": 418850000 + 151935796,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
-        "sha256": "2cf2b08fafae5079"},
+        "sha256": "65f471058d8eebd5"},
     "c3_lstm": {"bytes": 537186752 + 268440696,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "bb06c9ca75067026"},
+        "sha256": "4ad4c71274c15da5"},
     "c4_gru_long_fwd_adj": {"bytes": 546381664 + 269407176,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp",
                     "newton_chain.hip", "adjoint.hip"],
-        "sha256": "170a061ec829a393"},
+        "sha256": "840099f56890b6d2"},
     "x_linscan_blk2": {"bytes": 823221138 + 325722144,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-        "sha256": "70f3305fa6c96cd4"},
+        "sha256": "12cb7a3dab2680ec"},
     "x_linscan_blk4": {"bytes": 695774939 + 159006752,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "blkrow.hip"],
-        "sha256": "6c07d7fa57928125"},
+        "sha256": "de5c8dc768390615"},
     "x_linscan_blk8": {"bytes": 677625033 + 115343392,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "blkrow.hip"],
-        "sha256": "6c07d7fa57928125"},
+        "sha256": "de5c8dc768390615"},
     "x_lstm_adjoint": {"bytes": 1127552658 + 597172256,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "adjoint.hip"],
-        "sha256": "4817b8e8a7d4ed39"},
+        "sha256": "b2bf2dde0c14689b"},
     "x_gru_long_fwd": {"bytes": 206417104 + 67810172,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "bb06c9ca75067026"},
+        "sha256": "4ad4c71274c15da5"},
     "x_gru_seq": {"bytes": 402870181 + 134217728,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
-        "sha256": "91a3de061c0d874e"},
+        "sha256": "fcc8f2aecb1c39d2"},
     "x_lstm_seq": {"bytes": 537126747 + 268435456,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
-        "sha256": "91a3de061c0d874e"},
+        "sha256": "fcc8f2aecb1c39d2"},
     # per step: the launches of the iterations that ran (the launches after
     # convergence read and write almost nothing)
-    "x_hgru8_fwd": {"bytes": 1218613536 + 443353740,
+    "x_hgru8_fwd": {"bytes": 1426876272 + 504170704,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp",
                     "newton_iter.hpp", "hgru.hip"],
-        "sha256": "6be214b813f1d95a"},
+        "sha256": "df05e4a9075d6d7c"},
 }
 DESCRIBE = {
     "c1_linscan": "linear diagonal recurrence h_t = a_t h_{t-1} + b_t, B=16 L=4096 H=1024, "
@@ -207,12 +207,12 @@ def roofline(name, elements, kernel_ms):
 #  - long GRU forward (chained, time lanes), B=16 L=2^20 H=1, 3 iterations:
 #    47.43 and 6.08;
 #  - GRU with 8x8 heads, B=16 L=2048 NH=64, per launch of one iteration:
-#    347.81 and 6.02.
+#    366.37 and 6.04.
 ALU_SLOTS_PER_ELEMENT_ITER = {
     "c2_gru_fused": (38.32 - 6.02) + 6.02 * 4,
     "c3_lstm": (82.98 - 10.00) + 10.00 * 4,
     "x_gru_long_fwd": (47.43 - 6.08) + 6.08 * 4,
-    "x_hgru8_fwd": (347.81 - 6.02) + 6.02 * 4,
+    "x_hgru8_fwd": (366.37 - 6.04) + 6.04 * 4,
 }
 PEAK_VALU_TOPS = 78.6
 # Issue basis: SQ_ACTIVE_INST_VALU counts the quad-cycles a SIMD spends
@@ -229,7 +229,7 @@ ALU_ISSUE_PER_ELEMENT_ITER = {
     "c2_gru_fused": 44.34,
     "c3_lstm": 92.98,
     "x_gru_long_fwd": 53.51,
-    "x_hgru8_fwd": 353.82,
+    "x_hgru8_fwd": 372.41,
 }
 
 

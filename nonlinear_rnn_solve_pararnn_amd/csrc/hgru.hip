@@ -117,24 +117,32 @@ struct HgruStepOp {
                 hp = 0.0f;
             else if (p.w == 0)
                 hp = bnd_prev[(p.q - 1) * nrow + slot];  // the previous chunk may be overwritten already
-            else
+            else if (p.pos0 <= L)  // a sub-chunk wholly past the end reads nothing
                 hp = h[((p.b * L + p.pos0 - 1) * NH + p.j) * K + p.c];
         }
         // Every position is evaluated, with no branch per position (the DPP
         // exchanges run on whole lane groups either way): a position past the
         // end of the sequence or a head past NH runs on zeros and its map is
-        // replaced by the identity.
+        // replaced by the identity.  All of the sub-chunk's loads are issued
+        // before the first cell (an index outside reads element 0, replaced
+        // by a select), so their latencies overlap.
+        float xs[C], xz[C], xr[C], xc[C];
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             const int64_t t = p.pos0 + i;
             const bool val = p.ok && t < L;  // uniform over the lane group
             const int64_t idx = ((p.b * L + (val ? t : 0)) * NH + (p.ok ? p.j : 0)) * K + p.c;
-            const float s = (val && !cold1) ? h[idx] : 0.0f;
-            const float xz = val ? ld_once(pz + idx) : 0.0f;
-            const float xr = val ? ld_once(pr + idx) : 0.0f;
-            const float xc = val ? ld_once(pc + idx) : 0.0f;
+            xs[i] = cold1 ? 0.0f : h[idx];
+            xz[i] = ld_once(pz + idx);
+            xr[i] = ld_once(pr + idx);
+            xc[i] = ld_once(pc + idx);
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const bool val = p.ok && p.pos0 + i < L;
+            const float s = val ? xs[i] : 0.0f;
             RowK<K> m;
-            cell(hp, xz, xr, xc, uz, ur, uc, s, m);
+            cell(hp, val ? xz[i] : 0.0f, val ? xr[i] : 0.0f, val ? xc[i] : 0.0f, uz, ur, uc, s, m);
 #pragma unroll
             for (int q = 0; q < K; ++q) e[i].m.a[q] = val ? m.a[q] : (q == 0 ? 1.0f : 0.0f);
             e[i].m.b = val ? m.b : 0.0f;

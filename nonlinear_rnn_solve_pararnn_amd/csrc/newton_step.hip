@@ -65,7 +65,7 @@ struct GruStepOp {
                 hp = 0.0f;
             else if (tp.sub == 0)
                 hp = bnd_prev[(tp.q - 1) * B * H + tp.b * H + tp.j];
-            else
+            else if (tp.pos0 <= L)  // a sub-chunk wholly past the end reads nothing
                 hp = h[base - H];
         }
         Aff1 acc = {1.0f, 0.0f};
@@ -198,7 +198,7 @@ struct LstmStepOp {
                 const float2 v = bnd_prev[(tp.q - 1) * B * H + tp.b * H + tp.j];
                 cp = v.x;
                 hp = v.y;
-            } else {
+            } else if (tp.pos0 <= L) {  // a sub-chunk wholly past the end reads nothing
                 cp = c[base - H];
                 hp = h[base - H];
             }

@@ -217,9 +217,11 @@ inline BlkRowWs blkrow_ws(int k, int64_t B, int64_t L, int64_t H) {
 
 // Newton steps of the GRU with dense recurrence inside heads of k channels
 // (hgru.hip): one launch per iteration on the lane-group scan.  Measured for
-// k = 8 at B=16 L=2048 NH=64, 4 iterations: 4 waves x 8 positions (181
-// VGPRs) 1.09 ms, 4 x 4 1.13, 2 x 8 1.14, 8 x 8 1.20, 8 x 4 1.63, 4 x 2 1.71.
-constexpr BlkRowCfg kHgru8{4, 8, 1};
+// k = 8 at B=16 L=2048 NH=64, 4 iterations, with a sub-chunk's loads issued
+// before its cells: 4 waves x 6 positions (162 VGPRs, three waves per SIMD)
+// 0.93 ms, 4 x 8 bounded to 168 registers (spilling) 0.92-0.93, 4 x 8 at 181
+// registers 0.96, 2 x 8 1.01-1.03, 4 x 4 1.08, 8 x 8 1.10, 8 x 4 1.53.
+constexpr BlkRowCfg kHgru8{4, 6, 3};
 constexpr BlkRowCfg kHgru4{8, 4, 1};
 
 // Workspace: header, a max|delta| slot per iteration and two sets of
