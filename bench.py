@@ -55,6 +55,7 @@ ALG_BYTES = {
     "x_linscan_blk4": 96,        # A (4x4) and b (4) in; h (4) out, per (batch, position, block)
     "x_linscan_blk8": 320,       # A (8x8) and b (8) in; h (8) out, per (batch, position, block)
     "x_hgru8_fwd": 128,          # pz, pr, pc (8 each) in; h (8) out, per (batch, position, head): the whole solve
+    "x_hgru8_bwd": 256,          # pz, pr, pc, h, g (8 each) in; dpz, dpr, dpc (8 each) out, per (batch, position, head)
 }
 DOMINANT = {
     "c1_linscan": "diag_pf_kernel<16,16,2> (chunked scan, next tile prefetched)",
@@ -73,6 +74,8 @@ DOMINANT = {
     "x_gru_long_seq": "gru_rollout_kernel (sequential application, one thread per channel)",
     "x_linscan_blk4": "lg::scan_kernel<LinRowOp<4>,8,8,1> (each block's rows on a group of 4 lanes)",
     "x_linscan_blk8": "lg::scan_kernel<LinRowOp<8>,4,7,3> (each block's rows on a group of 8 lanes)",
+    "x_hgru8_bwd": "lg::scan_kernel<HgruAdjOp<8>,4,8,1> + hgru_u_reduce_kernel (whole step: the reverse-time "
+                   "scan of the transposed blocks with dL/dp, and the dL/dU reduction)",
     "x_hgru8_fwd": "lg::scan_kernel<HgruStepOp<8>,4,6,3> (one launch per Newton iteration up to the cap; "
                    "launches after convergence exit at once)",
 }
@@ -84,47 +87,51 @@ DOMINANT = {
 TRAFFIC = {
     "c1_linscan": {"bytes": 551301358 + 289021984,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-        "sha256": "12cb7a3dab2680ec"},
+        "sha256": "824e51b5f0f2217b"},
     "c2_gru_fused": {"bytes": 418850000 + 151935796,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
-        "sha256": "65f471058d8eebd5"},
+        "sha256": "aa41ca07633cc0e0"},
     "c3_lstm": {"bytes": 537186752 + 268440696,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "4ad4c71274c15da5"},
+        "sha256": "87c47b671ed40842"},
     "c4_gru_long_fwd_adj": {"bytes": 546381664 + 269407176,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp",
                     "newton_chain.hip", "adjoint.hip"],
-        "sha256": "840099f56890b6d2"},
+        "sha256": "a76f05dadec592f6"},
     "x_linscan_blk2": {"bytes": 823221138 + 325722144,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-        "sha256": "12cb7a3dab2680ec"},
+        "sha256": "824e51b5f0f2217b"},
     "x_linscan_blk4": {"bytes": 695774939 + 159006752,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "blkrow.hip"],
-        "sha256": "de5c8dc768390615"},
+        "sha256": "94389dbd5e94023c"},
     "x_linscan_blk8": {"bytes": 677625033 + 115343392,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "blkrow.hip"],
-        "sha256": "de5c8dc768390615"},
+        "sha256": "94389dbd5e94023c"},
     "x_lstm_adjoint": {"bytes": 1127552658 + 597172256,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "adjoint.hip"],
-        "sha256": "b2bf2dde0c14689b"},
+        "sha256": "682ed3f7b33aef74"},
     "x_gru_long_fwd": {"bytes": 206417104 + 67810172,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "4ad4c71274c15da5"},
+        "sha256": "87c47b671ed40842"},
+    "x_hgru8_bwd": {"bytes": 445603493 + 296485243,
+        "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp",
+                    "newton_iter.hpp", "hgru.hip"],
+        "sha256": "2a02d50e4da835a7"},
     "x_gru_seq": {"bytes": 402870181 + 134217728,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
-        "sha256": "fcc8f2aecb1c39d2"},
+        "sha256": "7cc376916e3c84a1"},
     "x_lstm_seq": {"bytes": 537126747 + 268435456,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
-        "sha256": "fcc8f2aecb1c39d2"},
+        "sha256": "7cc376916e3c84a1"},
     # per step: the launches of the iterations that ran (the launches after
     # convergence read and write almost nothing)
     "x_hgru8_fwd": {"bytes": 1426876272 + 504170704,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp",
                     "newton_iter.hpp", "hgru.hip"],
-        "sha256": "df05e4a9075d6d7c"},
+        "sha256": "2a02d50e4da835a7"},
 }
 DESCRIBE = {
     "c1_linscan": "linear diagonal recurrence h_t = a_t h_{t-1} + b_t, B=16 L=4096 H=1024, "
@@ -154,6 +161,9 @@ DESCRIBE = {
                       "A~U(-0.42,0.42), b~N(0,1), h0=0",
     "x_linscan_blk8": "8x8 block linear recurrence h_t = A_t h_{t-1} + b_t (heads of 8 channels), "
                       "B=16 L=2048 H=64 heads, A~U(-0.3,0.3), b~N(0,1), h0=0",
+    "x_hgru8_bwd": "gradients of the GRU with dense recurrence inside heads of 8 channels (the adjoint: "
+                   "reverse-time scan of the transposed 8x8 blocks, dL/dp, dL/dU, dL/dh0) at the converged "
+                   "forward of x_hgru8_fwd's inputs, B=16 L=2048 H=64 heads, upstream g~N(0,1)",
     "x_hgru8_fwd": "Newton forward of the GRU with dense recurrence inside heads of 8 channels (8x8 "
                    "Jacobian blocks), B=16 L=2048 H=64 heads, p~N(0,1), U: diagonal U(-0.5,0.5), "
                    "off-diagonal U(-0.3,0.3)/sqrt(8), h0=0, tol 1e-4, cap 32",
@@ -612,6 +622,16 @@ class Workload:
                 finally:
                     del os.environ[var]
             self._step = step
+        elif name == "x_hgru8_bwd":
+            k = self.w["k"]
+            args = [t[x] for x in ("pz", "pr", "pc", "Uz", "Ur", "Uc")]
+            h = api.hgru_forward(*args, None, tol=self.w["tol"], max_iter=self.w["cap"])
+            self.out = (torch.empty(B, L, H, k, device=dev), torch.empty(B, L, H, k, device=dev),
+                        torch.empty(B, L, H, k, device=dev), torch.empty(H, k, k, device=dev),
+                        torch.empty(H, k, k, device=dev), torch.empty(H, k, k, device=dev), None)
+            self.ws = api.new_workspace(api.workspace_bytes(api.OP_HGRU8_BACKWARD, B, L, H), dev)
+            self._step = lambda: api.hgru_backward(*args, None, h, t["g"], want_h0=False, ws=self.ws,
+                                                   out=self.out)
         elif name == "x_hgru8_fwd":
             cap = self.w["cap"]
             self.out = torch.empty(B, L, H, self.w["k"], device=dev)

@@ -79,8 +79,10 @@ enum {
     PARARNN_OP_LSTM_ADJOINT = 5,
     PARARNN_OP_LINSCAN_BLK4 = 6,  /* rnn_linscan_blk with k = 4 */
     PARARNN_OP_LINSCAN_BLK8 = 7,  /* rnn_linscan_blk with k = 8 */
-    PARARNN_OP_HGRU4_FORWARD = 8, /* pararnn_hgru_forward with k = 4 (H = heads) */
-    PARARNN_OP_HGRU8_FORWARD = 9  /* pararnn_hgru_forward with k = 8 (H = heads) */
+    PARARNN_OP_HGRU4_FORWARD = 8,  /* pararnn_hgru_forward with k = 4 (H = heads) */
+    PARARNN_OP_HGRU8_FORWARD = 9,  /* pararnn_hgru_forward with k = 8 (H = heads) */
+    PARARNN_OP_HGRU4_BACKWARD = 10, /* pararnn_hgru_backward with k = 4 (H = heads) */
+    PARARNN_OP_HGRU8_BACKWARD = 11  /* pararnn_hgru_backward with k = 8 (H = heads) */
 };
 
 /*
@@ -233,6 +235,34 @@ int pararnn_hgru_forward(int32_t k, int64_t B, int64_t L, int64_t NH,
                          const float *h0, const float *h_init, float *h, float tol,
                          int32_t max_iter, int32_t *info, float *trace,
                          void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Gradients through the converged solve of pararnn_hgru_forward (DEER
+ * summary page: forward plus gradients; the adjoint is the transposed block
+ * bi-diagonal system, ParaRNN page, Fig. 2 caption), by a reverse-time scan
+ * of k x k blocks:
+ *   nu_t = J_t^T (nu_{t+1} + g_t) with nu_L = 0,  lambda_t = g_t + nu_{t+1},
+ *   dL/dpz = lambda dF/daz,  dL/dpc = lambda dF/dac,  dL/dpr = dL/dar,
+ *   dL/dU = sum over batch rows and positions of the outer products of the
+ *   pre-activation gradients with the vectors U multiplies (h for Uz and Ur,
+ *   r*h for Uc),  dL/dh0 = nu_0,
+ * for L = sum g*h, with the cell and J_t evaluated at the given states.
+ * pz, pr, pc, Uz, Ur, Uc, h0 as for pararnn_hgru_forward; h: [B, L, NH, k]
+ * the forward's solution; grad_h: [B, L, NH, k].  grad_pz, grad_pr,
+ * grad_pc: [B, L, NH, k] outputs (overwritten; each may be its own p, none
+ * may overlap h).  grad_Uz, grad_Ur, grad_Uc: [NH, k, k] outputs or NULL
+ * (any of them requires NH < 2^31).  grad_h0: [B, NH, k] output or NULL.
+ * Workspace: PARARNN_OP_HGRU4_BACKWARD / PARARNN_OP_HGRU8_BACKWARD with
+ * H = NH (max_iter ignored).  Other k return PARARNN_ERR_UNSUPPORTED (k < 1:
+ * PARARNN_ERR_INVALID).
+ */
+int pararnn_hgru_backward(int32_t k, int64_t B, int64_t L, int64_t NH,
+                          const float *pz, const float *pr, const float *pc,
+                          const float *Uz, const float *Ur, const float *Uc,
+                          const float *h0, const float *h, const float *grad_h,
+                          float *grad_pz, float *grad_pr, float *grad_pc,
+                          float *grad_Uz, float *grad_Ur, float *grad_Uc, float *grad_h0,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Gradients through the converged solve (DEER summary: forward plus

@@ -19,13 +19,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpararnn.so")
 
 OP_LINSCAN_DIAG, OP_LINSCAN_BLK2, OP_GRU_FORWARD, OP_LSTM_FORWARD, OP_GRU_ADJOINT, \
-    OP_LSTM_ADJOINT, OP_LINSCAN_BLK4, OP_LINSCAN_BLK8, OP_HGRU4_FORWARD, OP_HGRU8_FORWARD = range(10)
+    OP_LSTM_ADJOINT, OP_LINSCAN_BLK4, OP_LINSCAN_BLK8, OP_HGRU4_FORWARD, OP_HGRU8_FORWARD, \
+    OP_HGRU4_BACKWARD, OP_HGRU8_BACKWARD = range(12)
 CELL_GRU, CELL_LSTM = 0, 1
 
 EXPORTS = ("pararnn_workspace_bytes", "rnn_linscan_diag", "rnn_linscan_blk2", "rnn_linscan_blk",
            "pararnn_gru_forward", "pararnn_lstm_forward", "pararnn_adjoint_backward",
            "pararnn_gru_sequential", "pararnn_lstm_sequential", "pararnn_status_string",
-           "pararnn_gru_forward_noalloc", "pararnn_hgru_forward")
+           "pararnn_gru_forward_noalloc", "pararnn_hgru_forward", "pararnn_hgru_backward")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # PARARNN_NOALLOC_SCRATCH_BYTES
 
 _lib = None
@@ -64,6 +65,8 @@ def load_library():
     lib.pararnn_hgru_forward.argtypes = [i32, i64, i64, i64] + [vp] * 9 + [
         ctypes.c_float, i32, vp, vp, vp, sz, vp]
     lib.pararnn_hgru_forward.restype = ctypes.c_int
+    lib.pararnn_hgru_backward.argtypes = [i32, i64, i64, i64] + [vp] * 17 + [sz, vp]
+    lib.pararnn_hgru_backward.restype = ctypes.c_int
     lib.pararnn_adjoint_backward.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                              vp, vp, vp, vp, vp, sz, vp]
     lib.pararnn_adjoint_backward.restype = ctypes.c_int
@@ -311,6 +314,45 @@ def hgru_forward(pz, pr, pc, Uz, Ur, Uc, h0=None, *, tol=1e-4, max_iter=32, out=
                                     _ptr(info), _ptr(trace), _ptr(ws), n, _stream(dev)),
            "pararnn_hgru_forward")
     return h
+
+
+def hgru_backward(pz, pr, pc, Uz, Ur, Uc, h0, h, grad_h, *, want_u=True, want_h0=True, ws=None, out=None):
+    """Gradients of sum(grad_h * h) through the head-GRU solve h (the
+    converged output of hgru_forward): returns (dpz, dpr, dpc, dUz, dUr, dUc,
+    dh0), the U gradients None unless want_u, dh0 None unless want_h0.
+    `out`: the seven output tensors to write instead (None entries for the
+    gradients not wanted)."""
+    lib = load_library()
+    B, L, NH, k = pz.shape
+    dev = pz.device
+    for t, n in ((pz, "pz"), (pr, "pr"), (pc, "pc"), (h, "h"), (grad_h, "grad_h")):
+        _need(t, (B, L, NH, k), n, dev)
+    for t, n in ((Uz, "Uz"), (Ur, "Ur"), (Uc, "Uc")):
+        _need(t, (NH, k, k), n, dev)
+    if h0 is not None:
+        _need(h0, (B, NH, k), "h0", dev)
+    op = {4: OP_HGRU4_BACKWARD, 8: OP_HGRU8_BACKWARD}.get(k)
+    if op is None:
+        raise PararnnError("pararnn_hgru_backward supports k = 4 and 8, got %d" % k)
+    if out is not None:
+        gp, gU, gh0 = list(out[:3]), list(out[3:6]), out[6]
+        for t, n in zip(gp, ("dpz", "dpr", "dpc")):
+            _need(t, (B, L, NH, k), n, dev)
+        for t, n in zip(gU, ("dUz", "dUr", "dUc")):
+            if t is not None:
+                _need(t, (NH, k, k), n, dev)
+        if gh0 is not None:
+            _need(gh0, (B, NH, k), "dh0", dev)
+    else:
+        gp = [torch.empty_like(pz) for _ in range(3)]
+        gU = [torch.empty_like(Uz) for _ in range(3)] if want_u else [None] * 3
+        gh0 = torch.empty(B, NH, k, device=dev) if want_h0 else None
+    ws, n = _workspace(op, B, L, NH, dev, 1, ws)
+    _check(lib.pararnn_hgru_backward(k, B, L, NH, _ptr(pz), _ptr(pr), _ptr(pc), _ptr(Uz), _ptr(Ur), _ptr(Uc),
+                                     _ptr(h0), _ptr(h), _ptr(grad_h), _ptr(gp[0]), _ptr(gp[1]), _ptr(gp[2]),
+                                     _ptr(gU[0]), _ptr(gU[1]), _ptr(gU[2]), _ptr(gh0), _ptr(ws), n, _stream(dev)),
+           "pararnn_hgru_backward")
+    return (*gp, *gU, gh0)
 
 
 def gru_forward_noalloc(pz, pr, pc, uz, ur, uc, h0=None, *, tol=1e-4, max_iter=32, out=None,

@@ -157,6 +157,12 @@ size_t pararnn_workspace_bytes(int32_t op, int64_t B, int64_t L, int64_t H, int3
             if (max_iter < 1 || !dims_ok(B, L, H * k)) return 0;
             return hgru_ws(k, B, L, H, eff_cap(max_iter, L)).total;
         }
+        case PARARNN_OP_HGRU4_BACKWARD:
+        case PARARNN_OP_HGRU8_BACKWARD: {
+            const int k = op == PARARNN_OP_HGRU8_BACKWARD ? 8 : 4;
+            if (!dims_ok(B, L, H * k)) return 0;
+            return hgru_adj_ws(k, B, L, H).total;
+        }
         case PARARNN_OP_GRU_ADJOINT: return gru_adjoint_ws(B, L, H);
         case PARARNN_OP_LSTM_ADJOINT: return lstm_adjoint_ws(B, L, H);
         default: return 0;
@@ -283,6 +289,28 @@ int pararnn_hgru_forward(int32_t k, int64_t B, int64_t L, int64_t NH, const floa
     }
     const HgruFwdArgs a{k, B, L, NH, pz, pr, pc, Uz, Ur, Uc, h0, h_init, h, tol, cap, info, trace};
     return status_of(hgru_forward(a, Ws{static_cast<char *>(ws), ws_bytes}, s));
+}
+
+int pararnn_hgru_backward(int32_t k, int64_t B, int64_t L, int64_t NH, const float *pz, const float *pr,
+                          const float *pc, const float *Uz, const float *Ur, const float *Uc, const float *h0,
+                          const float *h, const float *grad_h, float *grad_pz, float *grad_pr, float *grad_pc,
+                          float *grad_Uz, float *grad_Ur, float *grad_Uc, float *grad_h0, void *ws,
+                          size_t ws_bytes, void *stream) {
+    if (k < 1) return PARARNN_ERR_INVALID;
+    if (k != 4 && k != 8) return PARARNN_ERR_UNSUPPORTED;
+    if (!dims_ok(B, L, NH) || !dims_ok(B, L, NH * k)) return PARARNN_ERR_INVALID;
+    if (!pz || !pr || !pc || !Uz || !Ur || !Uc || !h || !grad_h || !grad_pz || !grad_pr || !grad_pc)
+        return PARARNN_ERR_INVALID;
+    const int64_t n = B * L * NH * k;
+    // h is read at other positions than the thread's own: no output may alias it
+    if (overlaps(grad_pz, h, n) || overlaps(grad_pr, h, n) || overlaps(grad_pc, h, n)) return PARARNN_ERR_INVALID;
+    if ((grad_Uz || grad_Ur || grad_Uc) && NH > 0x7fffffff) return PARARNN_ERR_INVALID;
+    const HgruAdjWs need = hgru_adj_ws(k, B, L, NH);
+    if (!grid_ok(need.sh.ntiles)) return PARARNN_ERR_INVALID;
+    if (!ws || ws_bytes < need.total || !aligned(ws, 256)) return PARARNN_ERR_INVALID;
+    HgruBwdArgs a{k, B, L, NH, pz, pr, pc, Uz, Ur, Uc, h0, h, grad_h, grad_pz, grad_pr, grad_pc,
+                  {grad_Uz, grad_Ur, grad_Uc}, grad_h0};
+    return status_of(hgru_backward(a, Ws{static_cast<char *>(ws), ws_bytes}, static_cast<hipStream_t>(stream)));
 }
 
 int pararnn_gru_sequential(int64_t B, int64_t L, int64_t H, const float *pz, const float *pr,

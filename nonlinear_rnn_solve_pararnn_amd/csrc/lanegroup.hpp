@@ -68,6 +68,23 @@ __device__ __forceinline__ void xor_lanes(float v, float (&o)[K]) {
     }
 }
 
+// o[p] = a[p] of lane (lane ^ p): with a[p] = A[c][c ^ p] (row c in xor
+// order), o is row c of A^T in xor order, since A^T[c][c ^ p] = A[c ^ p][c]
+// is entry p of lane c ^ p.
+template <int K>
+__device__ __forceinline__ void xor_each(const float (&a)[K], float (&o)[K]) {
+    o[0] = a[0];
+    o[1] = dpp_f<kQpXor1>(a[1]);
+    o[2] = dpp_f<kQpXor2>(a[2]);
+    o[3] = dpp_f<kQpXor3>(a[3]);
+    if constexpr (K == 8) {
+        o[7] = dpp_f<kHalfRowMirror>(a[7]);                   // lane ^ 7
+        o[6] = dpp_f<kQpXor1>(dpp_f<kHalfRowMirror>(a[6]));  // lane ^ 7 ^ 1
+        o[5] = dpp_f<kQpXor2>(dpp_f<kHalfRowMirror>(a[5]));  // lane ^ 7 ^ 2
+        o[4] = dpp_f<kQpXor3>(dpp_f<kHalfRowMirror>(a[4]));  // lane ^ 7 ^ 3
+    }
+}
+
 // 1 when every lane of the group has f = 1
 template <int K>
 __device__ __forceinline__ int group_all(int f) {

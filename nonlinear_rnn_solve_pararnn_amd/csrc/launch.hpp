@@ -64,6 +64,15 @@ struct HgruFwdArgs {
     float *trace;
 };
 hipError_t hgru_forward(const HgruFwdArgs &a, const Ws &ws, hipStream_t s);
+struct HgruBwdArgs {
+    int k;
+    int64_t B, L, NH;
+    const float *pz, *pr, *pc, *Uz, *Ur, *Uc, *h0, *h, *gh;
+    float *gpz, *gpr, *gpc;
+    float *gU[3];  // dL/dUz, dL/dUr, dL/dUc [NH, k, k], each or null
+    float *gh0;
+};
+hipError_t hgru_backward(const HgruBwdArgs &a, const Ws &ws, hipStream_t s);
 struct GruFwdArgs {
     int64_t B, L, H;
     const float *pz, *pr, *pc, *uz, *ur, *uc, *h0;

@@ -252,6 +252,45 @@ inline HgruWs hgru_ws(int k, int64_t B, int64_t L, int64_t NH, int32_t cap) {
     return w;
 }
 
+// Gradients of the head GRU (hgru.hip, the adjoint on the lane-group scan,
+// positions in reverse time): each lane keeps its rows of dL/dUz, dL/dUr,
+// dL/dUc over its positions; a workgroup sums them over its waves into one
+// partial per (tile, head), and a second launch sums the partials of each
+// head over chunks and batch rows.  Measured for k = 8 at B=16 L=2048
+// NH=64: 4 waves x 8 positions (247 VGPRs) 372-376 us, 8 x 6 434, 4 x 6
+// 435, 2 x 8 469-493, 8 x 4 525, 4 x 4 540, 4 x 6 bounded to 168 registers
+// 567.
+constexpr BlkRowCfg kHgruAdj8{4, 8, 1};
+constexpr BlkRowCfg kHgruAdj4{8, 4, 1};
+
+constexpr int kHgruUSlices = 64;  // slices of the first dL/dU reduction pass
+
+struct HgruAdjWs {
+    BlkRowWs sh;     // chunking and look-back records
+    size_t partial;  // [tile][64/k heads][3 gates][k][k] floats (kept at a wrap clear)
+    size_t stage;    // [NH][3][kHgruUSlices][k][k] floats, the first pass's sums
+    size_t total;
+};
+
+inline HgruAdjWs hgru_adj_ws(int k, int64_t B, int64_t L, int64_t NH) {
+    const BlkRowCfg cfg = k == 8 ? kHgruAdj8 : kHgruAdj4;
+    HgruAdjWs w;
+    w.sh.T = (int64_t)cfg.nw * cfg.c;
+    const int64_t heads = 64 / k;
+    w.sh.ncb = (NH + heads - 1) / heads;
+    w.sh.nq = (L + w.sh.T - 1) / w.sh.T;
+    w.sh.ntiles = w.sh.nq * B * w.sh.ncb;
+    w.sh.nrow = B * NH * k;
+    Carve c;
+    w.sh.hdr = c.take(16);
+    w.sh.agg = c.take((size_t)w.sh.nq * (k + 1) * w.sh.nrow * 8);
+    w.sh.inc = c.take((size_t)w.sh.nq * w.sh.nrow * 8);
+    w.partial = c.take((size_t)w.sh.ntiles * heads * 3 * k * k * 4);
+    w.stage = c.take((size_t)NH * 3 * kHgruUSlices * k * k * 4);
+    w.sh.total = w.total = c.off;
+    return w;
+}
+
 // Fused on-chip GRU Newton: one workgroup owns all L positions of
 // kFusedChannels channels of one batch row; each lane is one (channel,
 // sub-chunk), 32 sub-chunks of C positions (so 32 * kFusedChannels / 64

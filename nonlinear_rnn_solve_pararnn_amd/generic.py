@@ -172,7 +172,7 @@ def _adjoint(cell, k, n_inputs, h0, s, tensors, g, want_h0):
 
 class _HeadGruSolve(torch.autograd.Function):
     """Forward by the library's head-GRU Newton kernel (pararnn_hgru_forward),
-    backward by the adjoint above with head_gru_cell."""
+    backward by its adjoint kernel (pararnn_hgru_backward)."""
 
     @staticmethod
     def forward(ctx, tol, max_iter, info, init, h0, pz, pr, pc, Uz, Ur, Uc):
@@ -188,9 +188,12 @@ class _HeadGruSolve(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, g):
-        h0, s, *tensors = ctx.saved_tensors
-        gh0, gt = _adjoint(head_gru_cell, ctx.k, 3, h0, s, tensors, g.contiguous(), ctx.needs_input_grad[4])
-        return (None, None, None, None, gh0, *gt)
+        h0, s, pz, pr, pc, Uz, Ur, Uc = ctx.saved_tensors
+        need = ctx.needs_input_grad
+        dpz, dpr, dpc, dUz, dUr, dUc, dh0 = api.hgru_backward(
+            pz.detach(), pr.detach(), pc.detach(), Uz.detach(), Ur.detach(), Uc.detach(), h0.detach(), s,
+            g.contiguous(), want_u=any(need[8:11]), want_h0=need[4])
+        return (None, None, None, None, dh0, dpz, dpr, dpc, dUz, dUr, dUc)
 
 
 def head_gru_solve(pz: torch.Tensor, pr: torch.Tensor, pc: torch.Tensor, Uz: torch.Tensor,

@@ -54,6 +54,9 @@ WORKLOADS = {
     # Newton forward of the GRU with dense recurrence inside heads of 8
     # channels (8x8 Jacobian blocks), 64 heads (512 channels)
     "x_hgru8_fwd": dict(kind="hgru", B=16, L=2048, H=64, k=8, tol=1e-4, cap=32),
+    # its gradients: the adjoint at the converged forward's states, with
+    # upstream gradients ~ N(0,1)
+    "x_hgru8_bwd": dict(kind="hgru", B=16, L=2048, H=64, k=8, tol=1e-4, cap=32),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -214,4 +217,6 @@ def workload_inputs(name: str) -> dict:
         return linscan_blk_inputs(B, L, H, w["k"], seed)
     if name == "x_hgru8_fwd":
         return head_gru_inputs(B, L, H, w["k"], seed)
+    if name == "x_hgru8_bwd":
+        return head_gru_inputs(B, L, H, w["k"], seed, grad=True)
     raise KeyError(name)

@@ -2,8 +2,9 @@
 heads of k channels (pararnn_hgru_forward: k x k Jacobian blocks, one launch
 per iteration on the lane-group scan) against the oracle: single iterates
 (tol 0, cap n), the converged solve against the rollout, warm starts,
-non-convergence and NaN, the measured workload, and gradients through
-generic.head_gru_solve (the library's forward, the adjoint of the solve)."""
+non-convergence and NaN, the measured workload; the adjoint kernel
+(pararnn_hgru_backward) against the oracle's backpropagation through time,
+and gradients through generic.head_gru_solve (both kernels under autograd)."""
 import numpy as np
 import pytest
 import torch
@@ -137,3 +138,95 @@ def test_head_gru_solve_gradients_match_oracle(orc, B, L, NH, k):
     say(info, err, errs)
     assert info[1] == 1 and err <= FWD_ATOL
     assert max(errs.values()) <= GRAD_RTOL, errs
+
+
+@pytest.mark.parametrize("B,L,NH,k", SHAPES + [(1, 1, 1, 8), (2, 5, 3, 4)])
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_hgru_backward_matches_oracle_bptt(orc, B, L, NH, k, with_h0):
+    """The adjoint kernel against the oracle's backpropagation through time,
+    both at the oracle's rollout: dp, dU and dh0 at GRAD_RTOL each."""
+    say("hgru_backward", B, L, NH, k, with_h0)
+    d = synth.head_gru_inputs(B, L, NH, k, seed=800 + 7 * NH + L % 97, h0=with_h0, grad=True)
+    h = orc.hgru_rollout(*_args(d), h0=d["h0"]).astype(np.float32)
+    ref = orc.hgru_bptt(*_args(d), h, d["g"], h0=d["h0"])
+    got = api.hgru_backward(*[dev(x) for x in _args(d)], dev(d["h0"]) if with_h0 else None, dev(h),
+                            dev(d["g"]))
+    names = ["dpz", "dpr", "dpc", "dUz", "dUr", "dUc", "dh0"]
+    errs = {n: rel_inf(host(gv), rv) for n, gv, rv in zip(names, got, ref)}
+    say(errs)
+    assert max(errs.values()) <= GRAD_RTOL, errs
+
+
+def test_hgru_backward_full_workload(orc):
+    """B=16, L=2048, 64 heads of 8 channels (the forward's measured
+    workload) at the converged forward's states, every gradient against the
+    oracle's backpropagation through time at those states."""
+    say("hgru_backward full workload")
+    d = synth.head_gru_inputs(16, 2048, 64, 8, seed=830, grad=True)
+    t = [dev(x) for x in _args(d)]
+    h = api.hgru_forward(*t, None, tol=1e-4, max_iter=32)
+    hh = host(h)
+    ref = orc.hgru_bptt(*_args(d), hh, d["g"])
+    got = api.hgru_backward(*t, None, h, dev(d["g"]))
+    names = ["dpz", "dpr", "dpc", "dUz", "dUr", "dUc", "dh0"]
+    errs = {n: rel_inf(host(gv), rv) for n, gv, rv in zip(names, got, ref)}
+    say(errs)
+    assert max(errs.values()) <= GRAD_RTOL, errs
+
+
+def test_hgru_backward_options_and_reuse(orc):
+    """Without dL/dU and dL/dh0 the other gradients are unchanged; the
+    gradients may overwrite the inputs p; one workspace serves two shapes and
+    both k in a row (the partials of the first call are not read by the
+    second)."""
+    d = synth.head_gru_inputs(2, 300, 5, 8, seed=840, h0=True, grad=True)
+    h = orc.hgru_rollout(*_args(d), h0=d["h0"]).astype(np.float32)
+    ref = orc.hgru_bptt(*_args(d), h, d["g"], h0=d["h0"])
+    ws = api.new_workspace(max(api.workspace_bytes(api.OP_HGRU8_BACKWARD, 2, 300, 5),
+                               api.workspace_bytes(api.OP_HGRU4_BACKWARD, 3, 200, 7)), torch.device("cuda:0"))
+    full = api.hgru_backward(*[dev(x) for x in _args(d)], dev(d["h0"]), dev(h), dev(d["g"]), ws=ws)
+    part = api.hgru_backward(*[dev(x) for x in _args(d)], dev(d["h0"]), dev(h), dev(d["g"]),
+                             want_u=False, want_h0=False, ws=ws)
+    assert part[3] is None and part[6] is None
+    for a, b in zip(full[:3], part[:3]):
+        assert torch.equal(a, b)
+    d4 = synth.head_gru_inputs(3, 200, 7, 4, seed=841, grad=True)
+    h4 = orc.hgru_rollout(*_args(d4)).astype(np.float32)
+    ref4 = orc.hgru_bptt(*_args(d4), h4, d4["g"])
+    got4 = api.hgru_backward(*[dev(x) for x in _args(d4)], None, dev(h4), dev(d4["g"]), ws=ws)
+    assert max(rel_inf(host(a), b) for a, b in zip(got4, ref4)) <= GRAD_RTOL
+    # the gradients written over the inputs p (each element is read before it is written)
+    t = [dev(x) for x in _args(d)]
+    h0_d, h_d, g_d = dev(d["h0"]), dev(h), dev(d["g"])  # held: the call takes raw pointers
+    lib = api.load_library()
+    gU = [torch.empty_like(t[3]) for _ in range(3)]
+    gh0 = torch.empty(2, 5, 8, device="cuda:0")
+    n = api.workspace_bytes(api.OP_HGRU8_BACKWARD, 2, 300, 5)
+    st = lib.pararnn_hgru_backward(8, 2, 300, 5, *[api._ptr(x) for x in t], api._ptr(h0_d),
+                                   api._ptr(h_d), api._ptr(g_d), *[api._ptr(x) for x in t[:3]],
+                                   *[api._ptr(x) for x in gU], api._ptr(gh0), api._ptr(ws), n,
+                                   api._stream(torch.device("cuda:0")))
+    assert st == 0
+    errs = [rel_inf(host(a), b) for a, b in zip(t[:3] + gU + [gh0], ref)]
+    assert max(errs) <= GRAD_RTOL, errs
+
+
+def test_hgru_backward_rejects_bad_arguments():
+    d = synth.head_gru_inputs(1, 64, 2, 8, seed=850, grad=True)
+    t = [dev(x) for x in _args(d)]
+    h = torch.zeros(1, 64, 2, 8, device="cuda:0")
+    g = dev(d["g"])
+    lib = api.load_library()
+    ws = api.new_workspace(api.workspace_bytes(api.OP_HGRU8_BACKWARD, 1, 64, 2), torch.device("cuda:0"))
+    n = ws.numel()
+    s = api._stream(torch.device("cuda:0"))
+
+    def call(k=8, gp=None, wsb=n):
+        gp = gp or [torch.empty_like(t[0]) for _ in range(3)]
+        return lib.pararnn_hgru_backward(k, 1, 64, 2, *[api._ptr(x) for x in t], None, api._ptr(h), api._ptr(g),
+                                         *[api._ptr(x) for x in gp], None, None, None, None, api._ptr(ws), wsb, s)
+    assert call() == 0
+    assert call(gp=[h, torch.empty_like(h), torch.empty_like(h)]) != 0  # a gradient over h
+    assert call(k=3) != 0
+    assert call(k=0) != 0
+    assert call(wsb=n - 256) != 0  # workspace too small
