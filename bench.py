@@ -879,7 +879,9 @@ def main():
             "roofline": roofline(name, wl.elements, kernel_ms),
         }
         if name in ALU_SLOTS_PER_ELEMENT_ITER and iters:
-            results[name]["roofline_alu"] = alu_roofline(name, wl.elements, iters[0], kernel_ms, calib)
+            # the slot counts are per state element: k of them per head position for the head GRU
+            n_state = wl.elements * (wl.w["k"] if wl.w.get("kind") == "hgru" else 1)
+            results[name]["roofline_alu"] = alu_roofline(name, n_state, iters[0], kernel_ms, calib)
         if name != args.workload and name in CPU_BASELINE_OF and not args.no_cpu_baseline:
             log("cpu baseline (oracle) for", name)
             results[name]["cpu_baseline"] = cpu_baseline(name, wl.host, budget_s=5.0, single_s=2.0)
