@@ -650,6 +650,12 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
                 s_stop = prefix ? 1 : 0;
             }
         }
+        if (__uint_as_float(m) > g.tol) {
+            // every thread already knows this chunk has not converged: there
+            // is no prefix decision to wait for (wave 0 published the flag)
+            if (k >= g.cap) break;
+            continue;
+        }
         lds_barrier();
         conv = s_stop != 0;
         if (conv || k >= g.cap) break;
