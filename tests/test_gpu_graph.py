@@ -121,3 +121,53 @@ def test_captured_block_scans_and_warm_start_replay(orc):
         assert max_abs(host(h4), orc.linscan_blk(d4[r]["A"], d4[r]["b"])) <= FWD_ATOL
         assert info.cpu().tolist()[1] == 1
         assert max(max_abs(host(hl), rh), max_abs(host(cl), rc)) <= FWD_ATOL
+
+
+def test_captured_head_gru_forward_and_backward_replay(orc):
+    """The head GRU's Newton forward (launches up to the cap, the later ones
+    exiting at once) and its adjoint (scan plus the two dL/dU passes) under
+    capture, each replay against the oracle's rollout and backpropagation
+    through time, with the inputs changed in place and eager calls between
+    replays."""
+    B, L, NH, k = 2, 700, 9, 8
+    ds = [synth.head_gru_inputs(B, L, NH, k, seed=870 + r, h0=True, grad=True) for r in range(3)]
+    keys = ("pz", "pr", "pc", "Uz", "Ur", "Uc", "h0", "g")
+    t = {x: dev(ds[0][x]) for x in keys}
+    args = [t[x] for x in ("pz", "pr", "pc", "Uz", "Ur", "Uc")]
+    h = torch.empty(B, L, NH, k, device="cuda")
+    info = torch.zeros(2, dtype=torch.int32, device="cuda")
+    out = tuple(torch.empty(B, L, NH, k, device="cuda") for _ in range(3)) + \
+        tuple(torch.empty(NH, k, k, device="cuda") for _ in range(3)) + (torch.empty(B, NH, k, device="cuda"),)
+    ws_f = api.new_workspace(api.workspace_bytes(api.OP_HGRU8_FORWARD, B, L, NH, 16), h.device)
+    ws_b = api.new_workspace(api.workspace_bytes(api.OP_HGRU8_BACKWARD, B, L, NH), h.device)
+
+    def calls():
+        api.hgru_forward(*args, t["h0"], tol=1e-6, max_iter=16, out=h, info=info, ws=ws_f)
+        api.hgru_backward(*args, t["h0"], h, t["g"], ws=ws_b, out=out)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for r in range(3):
+        say("head GRU replay", r)
+        for x in keys:
+            t[x].copy_(dev(ds[r][x]))
+        api.hgru_forward(*[dev(ds[(r + 1) % 3][x]) for x in ("pz", "pr", "pc", "Uz", "Ur", "Uc")], None,
+                         tol=1e-4, max_iter=8)  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        d = ds[r]
+        p = [d[x] for x in ("pz", "pr", "pc", "Uz", "Ur", "Uc")]
+        href = orc.hgru_rollout(*p, h0=d["h0"])
+        assert info.cpu().tolist()[1] == 1
+        assert max_abs(host(h), href) <= FWD_ATOL
+        ref = orc.hgru_bptt(*p, host(h), d["g"], h0=d["h0"])
+        errs = [rel_inf(host(gv), rv) for gv, rv in zip(out, ref)]
+        say(errs)
+        assert max(errs) <= GRAD_RTOL, errs
