@@ -468,6 +468,8 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
 #pragma unroll
     for (int i = 0; i < C; ++i) val[i] = ok && pos0 + i < g.L;
     const bool whole = ok && pos0 + C <= g.L;
+    // time lanes: positions of this thread inside the sequence, the first nv
+    int nv = ok ? (int)(g.L - pos0 < 0 ? 0 : g.L - pos0 < C ? g.L - pos0 : C) : 0;
     float x[Cell::NG][C];
     cell.template load<C>(base, g.H, val, whole, x);
     const typename Cell::W wts = cell.weights(j, ok);
@@ -601,13 +603,30 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
         if (sub == 0) hb = state_add(hb, cin);  // the previous chunk's last state at iterate k
         State dlt = M::apply(ex, cin);
         uint32_t mx = 0;
+        // With time lanes, a thread whose positions all lie inside the
+        // sequence (every thread but those of a chain's last chunk) takes
+        // max|delta| with no per-position mask: the masks are lane masks in
+        // scalar registers, which that kernel keeps spilled, so each masked
+        // position would cost two reloads.  (With channel lanes the split
+        // measured slower.)
+        // With time lanes the per-position tests are taken here from nv,
+        // which the empty asm makes opaque, so that their lane masks are not
+        // hoisted out of the loop and kept live in scalar registers across it.
+        if constexpr (!CL) asm volatile("" : "+v"(nv));
+        const auto apply_all = [&](auto masked) {
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            dlt = M::apply(e[i], dlt);
-            s[i] = state_add(s[i], dlt);
-            const uint32_t a = val[i] ? state_abs_max(dlt) : 0u;
-            mx = a > mx ? a : mx;
-        }
+            for (int i = 0; i < C; ++i) {
+                dlt = M::apply(e[i], dlt);
+                s[i] = state_add(s[i], dlt);
+                const bool in = CL ? val[i] : i < nv;
+                const uint32_t a = (!decltype(masked)::value || in) ? state_abs_max(dlt) : 0u;
+                mx = a > mx ? a : mx;
+            }
+        };
+        if (!CL && whole)
+            apply_all(std::false_type{});
+        else
+            apply_all(std::true_type{});
         mx = clamp_nan_to_inf(mx);
         if (CL)
             s_last[sub * CW + ch] = s[C - 1];
@@ -663,6 +682,11 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
     if (!LOCAL && tid == 0) st_coherent(g.stop + ticket, tagged((float)k, tag));
     kprev = k;
     cprev = conv;
+    if constexpr (!CL) {
+        asm volatile("" : "+v"(nv));
+#pragma unroll
+        for (int i = 0; i < C; ++i) val[i] = i < nv;
+    }
     cell.template store<C>(base, g.H, val, whole, s);
     if (tid == 0 && g.info != nullptr) {
         if (k > __hip_atomic_load(g.info, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
