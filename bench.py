@@ -88,17 +88,17 @@ TRAFFIC = {
     "c1_linscan": {"bytes": 551301358 + 289021984,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
         "sha256": "824e51b5f0f2217b"},
-    "c2_gru_fused": {"bytes": 418850000 + 151935796,
+    "c2_gru_fused": {"bytes": 418748032 + 152030544,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
-        "sha256": "aa41ca07633cc0e0"},
-    "c3_lstm": {"bytes": 537187088 + 268440092,
+        "sha256": "f70485a8bc4a5ca2"},
+    "c3_lstm": {"bytes": 537187344 + 268440064,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "c733f2f8f4ab0243"},
-    "c4_gru_long_fwd_adj": {"bytes": 544906928 + 269379424,
+        "sha256": "31cb93a4bc8aa18b"},
+    "c4_gru_long_fwd_adj": {"bytes": 544462192 + 269380452,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp",
                     "newton_chain.hip", "adjoint.hip"],
-        "sha256": "68f796982c1b3c57"},
+        "sha256": "933ddc3afe62b5fb"},
     "x_linscan_blk2": {"bytes": 823221138 + 325722144,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
         "sha256": "824e51b5f0f2217b"},
@@ -108,24 +108,24 @@ TRAFFIC = {
     "x_linscan_blk8": {"bytes": 677625033 + 115343392,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "blkrow.hip"],
         "sha256": "94389dbd5e94023c"},
-    "x_lstm_adjoint": {"bytes": 1127552658 + 597172256,
+    "x_lstm_adjoint": {"bytes": 1127667803 + 597172256,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "adjoint.hip"],
-        "sha256": "682ed3f7b33aef74"},
-    "x_gru_long_fwd": {"bytes": 205630848 + 67764148,
+        "sha256": "bfc84b6bd7a7c19f"},
+    "x_gru_long_fwd": {"bytes": 205119456 + 67770908,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "c733f2f8f4ab0243"},
+        "sha256": "31cb93a4bc8aa18b"},
     "x_hgru8_bwd": {"bytes": 445603493 + 296485243,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp",
                     "newton_iter.hpp", "hgru.hip"],
         "sha256": "2a02d50e4da835a7"},
-    "x_gru_seq": {"bytes": 402870181 + 134217728,
+    "x_gru_seq": {"bytes": 402868535 + 134217728,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
-        "sha256": "7cc376916e3c84a1"},
-    "x_lstm_seq": {"bytes": 537126747 + 268435456,
+        "sha256": "4a1c026d3ab8d36c"},
+    "x_lstm_seq": {"bytes": 537126802 + 268435456,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
-        "sha256": "7cc376916e3c84a1"},
+        "sha256": "4a1c026d3ab8d36c"},
     # per step: the launches of the iterations that ran (the launches after
     # convergence read and write almost nothing)
     "x_hgru8_fwd": {"bytes": 1426876272 + 504170704,
@@ -209,19 +209,19 @@ def roofline(name, elements, kernel_ms):
 # transcendentals (exp2, reciprocal) four, against the fp32 vector peak of
 # 157.3 TFLOP/s = 78.6 T lane-operations per second.  The measured
 # multiply-add rate of this build is reported beside it (alu_calibration).
-#  - fused GRU, B=16 L=512 H=4096, 4 iterations: 38.32 VALU and 6.02
+#  - fused GRU, B=16 L=512 H=4096, 4 iterations: 36.34 VALU and 6.02
 #    transcendental wave instructions per element and iteration (the gfx950
-#    assembly of the loop gives 33.8 and 6; the rest is per-iteration work
+#    assembly of the loop gives 31.8 and 6; the rest is per-iteration work
 #    outside the cell loop);
-#  - LSTM whole chains, B=8 L=2048 H=2048, 4 iterations: 82.98 and 10.00;
+#  - LSTM whole chains, B=8 L=2048 H=2048, 4 iterations: 79.98 and 10.00;
 #  - long GRU forward (chained, time lanes), B=16 L=2^20 H=1, 3 iterations:
-#    43.40 and 6.08;
+#    41.42 and 6.08;
 #  - GRU with 8x8 heads, B=16 L=2048 NH=64, per launch of one iteration:
 #    366.37 and 6.04.
 ALU_SLOTS_PER_ELEMENT_ITER = {
-    "c2_gru_fused": (38.32 - 6.02) + 6.02 * 4,
-    "c3_lstm": (82.98 - 10.00) + 10.00 * 4,
-    "x_gru_long_fwd": (43.40 - 6.08) + 6.08 * 4,
+    "c2_gru_fused": (36.34 - 6.02) + 6.02 * 4,
+    "c3_lstm": (79.98 - 10.00) + 10.00 * 4,
+    "x_gru_long_fwd": (41.42 - 6.08) + 6.08 * 4,
     "x_hgru8_fwd": (366.37 - 6.04) + 6.04 * 4,
 }
 PEAK_VALU_TOPS = 78.6
@@ -232,13 +232,13 @@ PEAK_VALU_TOPS = 78.6
 # the probes show happens for pure multiply-add streams (2 per quad-cycle: the
 # 66.9 T rate) but hardly at all once transcendentals are mixed in (under 4%
 # of quad-cycles in a probe of 8 transcendentals and 4-36 multiply-adds per
-# step; 17% in the fused GRU, 9% in the LSTM).  The roof is then the
+# step; 16% in the fused GRU, 9% in the LSTM).  The roof is then the
 # single-issue rate, measured live with one wave per SIMD (alu_calibration,
 # "fma_1wave"), against the issue quad-cycles per element and iteration:
 ALU_ISSUE_PER_ELEMENT_ITER = {
-    "c2_gru_fused": 44.34,
-    "c3_lstm": 92.98,
-    "x_gru_long_fwd": 49.48,
+    "c2_gru_fused": 42.35,
+    "c3_lstm": 89.98,
+    "x_gru_long_fwd": 47.50,
     "x_hgru8_fwd": 372.41,
 }
 

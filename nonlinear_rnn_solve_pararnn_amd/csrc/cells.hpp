@@ -52,6 +52,36 @@ __device__ __forceinline__ void gru_j_dp(float h, float pz, float pr, float pc, 
     r_out = r;
 }
 
+// The GRU's Newton map at one position, on gate inputs and weights
+// pre-scaled into the exp2 domain (xz, xr and wz, wr by -log2 e; xc and wc by
+// -2 log2 e), so that each gate is one fma, exp2, add and reciprocal.  Gives
+// J = dF/dh and beta = F - s at previous state hp.  Rewritten to save
+// instructions, exactly equal in real arithmetic to gru_f_j above:
+//   - with sc the sigmoid behind c = 2 sc - 1, 1 - c^2 = 4 sc (1 - sc), so
+//     uc enters as uc4 = 4 uc;
+//   - h r (1 - r) = rh - rh r with rh = r h, which the c gate needs anyway;
+//   - (1 - z) + z inner = 1 + z (inner - 1), (1 - z) uz = uz - z uz, and
+//     the -1 folds into the multiply-add of the c term.
+struct GruScaledW {
+    float wz, wr, wc;   // the gates' weights, scaled as their inputs
+    float uz, ur, uc4;  // the Jacobian's: uz, ur as given, 4 uc
+};
+__device__ __forceinline__ GruScaledW gru_scaled_weights(float uz, float ur, float uc) {
+    return {-kLog2e * uz, -kLog2e * ur, -2.0f * kLog2e * uc, uz, ur, 4.0f * uc};
+}
+__device__ __forceinline__ void gru_map_scaled(const GruScaledW &w, float hp, float xz, float xr, float xc,
+                                               float s, float &J, float &beta) {
+    const float z = fast_rcp(1.0f + fast_exp2(fmaf(w.wz, hp, xz)));
+    const float r = fast_rcp(1.0f + fast_exp2(fmaf(w.wr, hp, xr)));
+    const float rh = r * hp;
+    const float sc = fast_rcp(1.0f + fast_exp2(fmaf(w.wc, rh, xc)));
+    const float cmh = fmaf(2.0f, sc, -1.0f) - hp;  // c - h
+    beta = fmaf(z, cmh, hp) - s;
+    const float drh = fmaf(fmaf(-rh, r, rh), w.ur, r);            // d(r h)/dh
+    const float v = fmaf(fmaf(-sc, sc, sc) * w.uc4, drh, -1.0f);  // (1 - c^2) uc d(r h)/dh - 1
+    J = fmaf(z, fmaf(fmaf(-z, w.uz, w.uz), cmh, v), 1.0f);
+}
+
 struct Lstm2 {
     float Fc, Fh;
     float j00, j01, j10, j11;

@@ -74,7 +74,7 @@ __device__ __forceinline__ void newton_on_tile(const float (&xz)[C], const float
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int ch = lane % CH, sl = lane / CH;
     const int sub = w * SUBW + sl;
-    const float uzs = kE1 * uz, urs = kE1 * ur, ucs = kE2 * uc;
+    const GruScaledW gw = gru_scaled_weights(uz, ur, uc);
     float Jv[C], bv[C];
     if (warm) {
         // the initial iterate's last state of every sub-chunk, for its successor
@@ -96,20 +96,8 @@ __device__ __forceinline__ void newton_on_tile(const float (&xz)[C], const float
         Aff1 acc = {1.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            const float z = fast_rcp(1.0f + fast_exp2(fmaf(uzs, hp, xz[i])));
-            const float r = fast_rcp(1.0f + fast_exp2(fmaf(urs, hp, xr[i])));
-            const float rh = r * hp;
-            const float sc = fast_rcp(1.0f + fast_exp2(fmaf(ucs, rh, xc[i])));
-            const float c = fmaf(2.0f, sc, -1.0f);
-            const float cmh = c - hp;
-            const float F = fmaf(z, cmh, hp);
-            const float omz = 1.0f - z;
-            const float omc2 = fmaf(-c, c, 1.0f);
-            const float rr = fmaf(-r, r, r);
-            const float drh = fmaf(hp * rr, ur, r);
-            const float inner = fmaf(omz * uz, cmh, (omc2 * uc) * drh);
-            float J = fmaf(z, inner, omz);
-            float beta = F - hv[i];
+            float J, beta;
+            gru_map_scaled(gw, hp, xz[i], xr[i], xc[i], hv[i], J, beta);
             if (!FULL) {
                 J = val[i] ? J : 1.0f;
                 beta = val[i] ? beta : 0.0f;

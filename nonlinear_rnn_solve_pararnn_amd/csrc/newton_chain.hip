@@ -64,20 +64,9 @@ struct GruChain {
     float *h;
     bool runs;  // H == 1 with 16-byte aligned rows: whole runs move as float4
 
-    struct W {
-        float uz, ur, uc, uzs, urs, ucs;
-    };
+    using W = GruScaledW;
     __device__ W weights(int64_t j, bool ok) const {
-        W w{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-        if (ok) {
-            w.uz = uz[j];
-            w.ur = ur[j];
-            w.uc = uc[j];
-            w.uzs = kE1 * w.uz;
-            w.urs = kE1 * w.ur;
-            w.ucs = kE2 * w.uc;
-        }
-        return w;
+        return ok ? gru_scaled_weights(uz[j], ur[j], uc[j]) : gru_scaled_weights(0.0f, 0.0f, 0.0f);
     }
     __device__ float init(int64_t b, int64_t j, int64_t H) const {
         return h0 != nullptr ? h0[b * H + j] : 0.0f;
@@ -119,17 +108,9 @@ struct GruChain {
     }
     // Newton map of one position: delta -> J delta + (F - s), F and J at hp.
     __device__ Aff1 step(const W &w, float hp, float xz, float xr, float xc, float s) const {
-        const float z = fast_rcp(1.0f + fast_exp2(fmaf(w.uzs, hp, xz)));
-        const float r = fast_rcp(1.0f + fast_exp2(fmaf(w.urs, hp, xr)));
-        const float sc = fast_rcp(1.0f + fast_exp2(fmaf(w.ucs, r * hp, xc)));
-        const float c = fmaf(2.0f, sc, -1.0f);
-        const float cmh = c - hp;
-        const float F = fmaf(z, cmh, hp);
-        const float omz = 1.0f - z;
-        const float omc2 = fmaf(-c, c, 1.0f);
-        const float drh = fmaf(hp * fmaf(-r, r, r), w.ur, r);
-        const float inner = fmaf(omz * w.uz, cmh, (omc2 * w.uc) * drh);
-        return {fmaf(z, inner, omz), F - s};
+        Aff1 m;
+        gru_map_scaled(w, hp, xz, xr, xc, s, m.a, m.b);
+        return m;
     }
     template <int C>
     __device__ void store(int64_t base, int64_t H, const bool (&val)[C], bool whole, const float (&s)[C]) const {
@@ -200,18 +181,24 @@ struct LstmChain {
     }
     // Newton map of one position on the pre-scaled gate inputs (pi, pf, po by
     // -log2 e, pg by -2 log2 e): the arithmetic of lstm_f_j in cells.hpp with
-    // each gate's pre-activation one fma in the exp2 domain.
+    // each gate's pre-activation one fma in the exp2 domain, and the
+    // derivative terms rewritten on products the cell already forms
+    // (ig = i g, otc = o tanh c), each one multiply-add:
+    //   g i(1-i) = ig - ig i,  i(1-g^2) = i - ig g,
+    //   o(1-tanh^2 c) = o - otc tanh c,  o(1-o) tanh c = otc - otc o.
     __device__ Aff2 step(const W &w, float2s hp, float xi, float xf, float xo, float xg, float2s s) const {
         const float h = hp.y, cp = hp.x;
         const float i = fast_rcp(1.0f + fast_exp2(fmaf(w.uis, h, xi)));
         const float f = fast_rcp(1.0f + fast_exp2(fmaf(w.ufs, h, xf)));
         const float o = fast_rcp(1.0f + fast_exp2(fmaf(w.uos, h, xo)));
         const float g = fmaf(2.0f, fast_rcp(1.0f + fast_exp2(fmaf(w.ugs, h, xg))), -1.0f);
-        const float c = fmaf(f, cp, i * g);
+        const float ig = i * g;
+        const float c = fmaf(f, cp, ig);
         const float tc = fmaf(2.0f, fast_rcp(1.0f + fast_exp2(kE2 * c)), -1.0f);
-        const float odtc = o * fmaf(-tc, tc, 1.0f);
-        const float kappa = fmaf(cp * fmaf(-f, f, f), w.uf, fmaf(g * fmaf(-i, i, i), w.ui, i * fmaf(-g, g, 1.0f) * w.ug));
-        return {f, kappa, odtc * f, fmaf(fmaf(-o, o, o) * w.uo, tc, odtc * kappa), c - s.x, o * tc - s.y};
+        const float otc = o * tc;
+        const float odtc = fmaf(-otc, tc, o);
+        const float kappa = fmaf(cp * fmaf(-f, f, f), w.uf, fmaf(fmaf(-ig, i, ig), w.ui, fmaf(-ig, g, i) * w.ug));
+        return {f, kappa, odtc * f, fmaf(fmaf(-otc, o, otc), w.uo, odtc * kappa), c - s.x, otc - s.y};
     }
     template <int C>
     __device__ void store(int64_t base, int64_t H, const bool (&val)[C], bool, const float2s (&s)[C]) const {
