@@ -91,14 +91,14 @@ TRAFFIC = {
     "c2_gru_fused": {"bytes": 418748032 + 152030544,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
         "sha256": "f70485a8bc4a5ca2"},
-    "c3_lstm": {"bytes": 537187344 + 268440064,
+    "c3_lstm": {"bytes": 537172448 + 268439216,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "31cb93a4bc8aa18b"},
-    "c4_gru_long_fwd_adj": {"bytes": 544462192 + 269380452,
+        "sha256": "0f81def8b6310f06"},
+    "c4_gru_long_fwd_adj": {"bytes": 544162896 + 269411740,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp",
                     "newton_chain.hip", "adjoint.hip"],
-        "sha256": "933ddc3afe62b5fb"},
+        "sha256": "d84970d26ee849d9"},
     "x_linscan_blk2": {"bytes": 823221138 + 325722144,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
         "sha256": "824e51b5f0f2217b"},
@@ -112,10 +112,10 @@ TRAFFIC = {
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "adjoint.hip"],
         "sha256": "bfc84b6bd7a7c19f"},
-    "x_gru_long_fwd": {"bytes": 205119456 + 67770908,
+    "x_gru_long_fwd": {"bytes": 205229264 + 67798612,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "31cb93a4bc8aa18b"},
+        "sha256": "0f81def8b6310f06"},
     "x_hgru8_bwd": {"bytes": 445603493 + 296485243,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp",
                     "newton_iter.hpp", "hgru.hip"],
@@ -213,14 +213,14 @@ def roofline(name, elements, kernel_ms):
 #    transcendental wave instructions per element and iteration (the gfx950
 #    assembly of the loop gives 31.8 and 6; the rest is per-iteration work
 #    outside the cell loop);
-#  - LSTM whole chains, B=8 L=2048 H=2048, 4 iterations: 79.98 and 10.00;
+#  - LSTM whole chains, B=8 L=2048 H=2048, 4 iterations: 75.89 and 10.00;
 #  - long GRU forward (chained, time lanes), B=16 L=2^20 H=1, 3 iterations:
 #    41.42 and 6.08;
 #  - GRU with 8x8 heads, B=16 L=2048 NH=64, per launch of one iteration:
 #    366.37 and 6.04.
 ALU_SLOTS_PER_ELEMENT_ITER = {
     "c2_gru_fused": (36.34 - 6.02) + 6.02 * 4,
-    "c3_lstm": (79.98 - 10.00) + 10.00 * 4,
+    "c3_lstm": (75.89 - 10.00) + 10.00 * 4,
     "x_gru_long_fwd": (41.42 - 6.08) + 6.08 * 4,
     "x_hgru8_fwd": (366.37 - 6.04) + 6.04 * 4,
 }
@@ -232,12 +232,12 @@ PEAK_VALU_TOPS = 78.6
 # the probes show happens for pure multiply-add streams (2 per quad-cycle: the
 # 66.9 T rate) but hardly at all once transcendentals are mixed in (under 4%
 # of quad-cycles in a probe of 8 transcendentals and 4-36 multiply-adds per
-# step; 16% in the fused GRU, 9% in the LSTM).  The roof is then the
+# step; 16% in the fused GRU, 7% in the LSTM).  The roof is then the
 # single-issue rate, measured live with one wave per SIMD (alu_calibration,
 # "fma_1wave"), against the issue quad-cycles per element and iteration:
 ALU_ISSUE_PER_ELEMENT_ITER = {
     "c2_gru_fused": 42.35,
-    "c3_lstm": 89.98,
+    "c3_lstm": 85.89,
     "x_gru_long_fwd": 47.50,
     "x_hgru8_fwd": 372.41,
 }

@@ -518,9 +518,27 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
 #pragma unroll
         for (int i = 1; i < C; ++i) acc = M::then(acc, e[i]);
 
-        // exclusive prefix of this sub-chunk inside the chunk, and the chunk aggregate
+        // exclusive prefix of this sub-chunk inside the chunk, and the chunk
+        // aggregate; in the whole-chain form the delta entering the chunk is
+        // already known, so each thread instead carries that delta through
+        // the earlier sub-chunks' maps (a map applied to a state costs a third
+        // of a map composed with a map, for 2x2 blocks) and nothing is composed
         Map ex, tot;
-        if (CL) {
+        State din_sub;  // whole-chain form: the delta entering this sub-chunk
+        if (LOCAL) {
+            s_part[sub * CW + ch] = acc;
+            lds_barrier();
+            Map pv[NS - 1];
+#pragma unroll
+            for (int kk = 0; kk < NS - 1; ++kk)
+                if (kk < sub) pv[kk] = s_part[kk * CW + ch];
+            // the previous chunk's inclusive delta at k (zero once it has
+            // stopped)
+            din_sub = (q > 0 && k <= kprev) ? s_rec[((q - 1) & 1) * kRecHalf + (k - 1) * CW + ch] : M::zero();
+#pragma unroll
+            for (int kk = 0; kk < NS - 1; ++kk)
+                if (kk < sub) din_sub = M::apply(pv[kk], din_sub);
+        } else if (CL) {
             s_part[sub * CW + ch] = acc;
             lds_barrier();
             // the earlier sub-chunks' maps are all read before any is
@@ -554,10 +572,10 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
         // delta entering the chunk at iteration k
         State cin;
         if (LOCAL) {
-            // the previous chunk's inclusive delta at k (zero once it has
-            // stopped); the holder records this chunk's for the next chunk
-            cin = (q > 0 && k <= kprev) ? s_rec[((q - 1) & 1) * kRecHalf + (k - 1) * CW + ch] : M::zero();
-            if (holder) s_rec[(q & 1) * kRecHalf + (k - 1) * CW + ch] = M::apply(tot, cin);
+            // the holder records this chunk's inclusive delta for the next
+            // chunk; only sub-chunk 0 needs the delta entering the chunk (hb)
+            cin = din_sub;
+            if (holder) s_rec[(q & 1) * kRecHalf + (k - 1) * CW + ch] = M::apply(acc, din_sub);
         } else if (CL) {
             if (holder) {
                 State din = M::zero();
@@ -588,7 +606,7 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
 
         // apply: delta through the sub-chunk, s += delta
         if (sub == 0) hb = state_add(hb, cin);  // the previous chunk's last state at iterate k
-        State dlt = M::apply(ex, cin);
+        State dlt = LOCAL ? din_sub : M::apply(ex, cin);
         uint32_t mx = 0;
         // With time lanes, a thread whose positions all lie inside the
         // sequence (every thread but those of a chain's last chunk) takes
