@@ -90,15 +90,15 @@ TRAFFIC = {
         "sha256": "824e51b5f0f2217b"},
     "c2_gru_fused": {"bytes": 418748032 + 152030544,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
-        "sha256": "f70485a8bc4a5ca2"},
-    "c3_lstm": {"bytes": 537172448 + 268439216,
+        "sha256": "0f1e7fd137ff245b"},
+    "c3_lstm": {"bytes": 537166944 + 268441556,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "0f81def8b6310f06"},
-    "c4_gru_long_fwd_adj": {"bytes": 544162896 + 269411740,
+        "sha256": "a2e4835b2c822ab6"},
+    "c4_gru_long_fwd_adj": {"bytes": 544305376 + 269409900,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp",
                     "newton_chain.hip", "adjoint.hip"],
-        "sha256": "d84970d26ee849d9"},
+        "sha256": "a93624ffe2e256d8"},
     "x_linscan_blk2": {"bytes": 823221138 + 325722144,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
         "sha256": "824e51b5f0f2217b"},
@@ -111,21 +111,21 @@ TRAFFIC = {
     "x_lstm_adjoint": {"bytes": 1127667803 + 597172256,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "adjoint.hip"],
-        "sha256": "bfc84b6bd7a7c19f"},
-    "x_gru_long_fwd": {"bytes": 205229264 + 67798612,
+        "sha256": "7db2b305e6b9d39a"},
+    "x_gru_long_fwd": {"bytes": 205109136 + 67751176,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "0f81def8b6310f06"},
+        "sha256": "a2e4835b2c822ab6"},
     "x_hgru8_bwd": {"bytes": 445603493 + 296485243,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp",
                     "newton_iter.hpp", "hgru.hip"],
         "sha256": "2a02d50e4da835a7"},
     "x_gru_seq": {"bytes": 402868535 + 134217728,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
-        "sha256": "4a1c026d3ab8d36c"},
+        "sha256": "7e85cffc4dbacda6"},
     "x_lstm_seq": {"bytes": 537126802 + 268435456,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
-        "sha256": "4a1c026d3ab8d36c"},
+        "sha256": "7e85cffc4dbacda6"},
     # per step: the launches of the iterations that ran (the launches after
     # convergence read and write almost nothing)
     "x_hgru8_fwd": {"bytes": 1426876272 + 504170704,

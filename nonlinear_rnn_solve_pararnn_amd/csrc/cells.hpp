@@ -82,6 +82,21 @@ __device__ __forceinline__ void gru_map_scaled(const GruScaledW &w, float hp, fl
     J = fmaf(z, fmaf(fmaf(-z, w.uz, w.uz), cmh, v), 1.0f);
 }
 
+// gru_map_scaled at hp = 0 and s = 0: Newton's first iteration from the
+// zero iterate at every position whose previous state is that iterate's.
+// The terms that vanish are dropped, so it gives the same bits as
+// gru_map_scaled there (fma(w, 0, x) = x, fma(-0 r, ., r) = r, ...).
+__device__ __forceinline__ void gru_map_scaled0(const GruScaledW &w, float xz, float xr, float xc, float &J,
+                                                float &beta) {
+    const float z = fast_rcp(1.0f + fast_exp2(xz));
+    const float r = fast_rcp(1.0f + fast_exp2(xr));
+    const float sc = fast_rcp(1.0f + fast_exp2(xc));
+    const float c = fmaf(2.0f, sc, -1.0f);
+    beta = z * c;
+    const float v = fmaf(fmaf(-sc, sc, sc) * w.uc4, r, -1.0f);
+    J = fmaf(z, fmaf(fmaf(-z, w.uz, w.uz), c, v), 1.0f);
+}
+
 struct Lstm2 {
     float Fc, Fh;
     float j00, j01, j10, j11;

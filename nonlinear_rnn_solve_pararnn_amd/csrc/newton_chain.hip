@@ -112,6 +112,12 @@ struct GruChain {
         gru_map_scaled(w, hp, xz, xr, xc, s, m.a, m.b);
         return m;
     }
+    // step at hp = 0 and s = 0 (the first iteration from the zero iterate)
+    __device__ Aff1 step0(const W &w, float xz, float xr, float xc) const {
+        Aff1 m;
+        gru_map_scaled0(w, xz, xr, xc, m.a, m.b);
+        return m;
+    }
     template <int C>
     __device__ void store(int64_t base, int64_t H, const bool (&val)[C], bool whole, const float (&s)[C]) const {
         if constexpr (C % 4 == 0) {
@@ -498,8 +504,24 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
         // the records of the last chunk (which no chunk reads) and states that
         // are neither stored nor counted in max|delta|.
         Map e[C];
+        const auto cells = [&]() {
 #pragma unroll
-        for (int i = 1; i < C; ++i) e[i] = cell_step<Cell, C>(cell, wts, s[i - 1], x, i, s[i]);
+            for (int i = 1; i < C; ++i) e[i] = cell_step<Cell, C>(cell, wts, s[i - 1], x, i, s[i]);
+        };
+        if constexpr (LOCAL && S == 1) {
+            // From the zero iterate, positions 1.. see a zero previous state.
+            // Only the GRU's whole-chain form takes this: in the other forms
+            // the second copy of the cell loop costs registers, spills or
+            // occupancy.
+            if (k == 1 && !warm) {
+#pragma unroll
+                for (int i = 1; i < C; ++i) e[i] = cell.step0(wts, x[0][i], x[1][i], x[2][i]);
+            } else {
+                cells();
+            }
+        } else {
+            cells();
+        }
         State hp = M::zero();
         State nb = M::zero();
         if (!CL) nb = shfl_up_s(s[C - 1], 1);  // every lane active for the shuffle
