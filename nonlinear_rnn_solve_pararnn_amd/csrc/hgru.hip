@@ -79,21 +79,21 @@ __device__ __forceinline__ void hgru_row(float hp, float xz, float xr, float xc,
     float ac = xc;
     xor_terms_sum<K>(r * hp, uc, ac);
     const float cc = tanh_fast(ac);
-    const float a1 = (cc - hp) * (z - z * z);
+    const float a1 = (cc - hp) * fmaf(-z, z, z);
     const float a2 = z * fmaf(-cc, cc, 1.0f);
     float wx[K];
-    xor_lanes<K>(hp * (r - r * r), wx);  // h_m r_m (1 - r_m) of lane c ^ q
-    float vq[K], t[K], rx[K];
+    xor_lanes<K>(hp * fmaf(-r, r, r), wx);  // h_m r_m (1 - r_m) of lane c ^ q
+    // The row accumulates in place: a1 Uz[c][c ^ p] (+ 1 - z at p = 0), then
+    // the two Uc terms with a2 already folded into the row of Uc.
+    float a2uc[K], vq[K];
 #pragma unroll
     for (int q = 0; q < K; ++q) {
-        vq[q] = uc[q] * wx[q];
-        t[q] = 0.0f;
-        rx[q] = 0.0f;
+        a2uc[q] = a2 * uc[q];
+        vq[q] = a2uc[q] * wx[q];
+        o.a[q] = q == 0 ? fmaf(a1, uz[q], 1.0f - z) : a1 * uz[q];
     }
-    ur_terms<K, 0>(ur, vq, t);   // t[p] = sum_m Uc[c][m] w_m Ur[m][c ^ p]
-    xor_terms<K, 0>(r, uc, rx);  // rx[p] = Uc[c][c ^ p] r_{c ^ p}
-#pragma unroll
-    for (int q = 0; q < K; ++q) o.a[q] = fmaf(a1, uz[q], a2 * (rx[q] + t[q])) + (q == 0 ? 1.0f - z : 0.0f);
+    ur_terms<K, 0>(ur, vq, o.a);    // += a2 sum_m Uc[c][m] w_m Ur[m][c ^ p]
+    xor_terms<K, 0>(r, a2uc, o.a);  // += a2 Uc[c][c ^ p] r_{c ^ p}
     o.z = z;
     o.r = r;
     o.cc = cc;
