@@ -59,6 +59,7 @@ constexpr float kE1 = -kLog2e, kE2 = -2.0f * kLog2e;
 // -2 log2 e), the same arithmetic as the fused kernel.
 struct GruChain {
     static constexpr int S = 1, NG = 3;
+    static constexpr bool kZeroMapOutside = false;  // positions outside are masked
     const float *pz, *pr, *pc, *uz, *ur, *uc, *h0;
     const float *h_init;  // initial iterate [B, L, H], or null for zeros
     float *h;
@@ -135,6 +136,7 @@ struct GruChain {
 // LSTM-style cell; state (c, h) as (x, y).
 struct LstmChain {
     static constexpr int S = 2, NG = 4;
+    static constexpr bool kZeroMapOutside = true;  // see load()
     const float *pi, *pf, *po, *pg, *ui, *uf, *uo, *ug, *h0, *c0;
     const float *h_init, *c_init;  // initial iterates [B, L, H]; a null one is zero
     float *h, *c;
@@ -177,11 +179,16 @@ struct LstmChain {
             x[2][i] = ld_once(po + e);
             x[3][i] = ld_once(pg + e);
         }
+        // A position outside takes i = f = o = 0 (pre-scaled input +inf:
+        // exp2 gives +inf, the reciprocal 0), which makes its Newton map
+        // exactly zero (J = 0, F - s = 0 - 0), so its delta is 0 and
+        // max|delta| needs no mask (kZeroMapOutside).
+        constexpr float kOff = __builtin_inff();
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            x[0][i] = val[i] ? kE1 * x[0][i] : 0.0f;
-            x[1][i] = val[i] ? kE1 * x[1][i] : 0.0f;
-            x[2][i] = val[i] ? kE1 * x[2][i] : 0.0f;
+            x[0][i] = val[i] ? kE1 * x[0][i] : kOff;
+            x[1][i] = val[i] ? kE1 * x[1][i] : kOff;
+            x[2][i] = val[i] ? kE1 * x[2][i] : kOff;
             x[3][i] = val[i] ? kE2 * x[3][i] : 0.0f;
         }
     }
@@ -499,10 +506,12 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
         // come from the previous chunk
         // Every position is evaluated, with no branch per position, so the
         // compiler can interleave the independent cells.  A position past the
-        // end of the sequence or a channel past H runs on zero inputs; its map
-        // reaches only later positions of the same chunk (also past the end),
-        // the records of the last chunk (which no chunk reads) and states that
-        // are neither stored nor counted in max|delta|.
+        // end of the sequence or a channel past H runs on inputs the cell
+        // chooses (zero for the GRU; for the LSTM ones that make its map zero);
+        // its map reaches only later positions of the same chunk (also past
+        // the end), the records of the last chunk (which no chunk reads) and
+        // states that are never stored (nor, for the GRU, counted in
+        // max|delta|; the LSTM's are zero).
         Map e[C];
         const auto cells = [&]() {
 #pragma unroll
@@ -650,10 +659,14 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
                 mx = a > mx ? a : mx;
             }
         };
-        if (!CL && whole)
-            apply_all(std::false_type{});
-        else
-            apply_all(std::true_type{});
+        if constexpr (Cell::kZeroMapOutside) {
+            apply_all(std::false_type{});  // positions outside have delta 0
+        } else {
+            if (!CL && whole)
+                apply_all(std::false_type{});
+            else
+                apply_all(std::true_type{});
+        }
         mx = clamp_nan_to_inf(mx);
         if (CL)
             s_last[sub * CW + ch] = s[C - 1];
