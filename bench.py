@@ -58,11 +58,11 @@ ALG_BYTES = {
     "x_hgru8_bwd": 256,          # pz, pr, pc, h, g (8 each) in; dpz, dpr, dpc (8 each) out, per (batch, position, head)
 }
 DOMINANT = {
-    "c1_linscan": "diag_pf_kernel<16,16,2> (chunked scan, next tile prefetched)",
+    "c1_linscan": "scan_pf_kernel<LinDiagOp,16,16,2> (chunked scan, next tile prefetched)",
     "c2_gru_fused": "gru_fused_kernel<16>",
     "c3_lstm": "newton_local_kernel<LstmChain> (one launch for every iteration; each workgroup owns whole chains)",
     "c4_gru_long_fwd_adj": "newton_chain_kernel<GruChain> + chunk_scan_kernel<GruAdjOp> (whole step)",
-    "x_linscan_blk2": "chunk_scan_kernel<LinBlk2Op>",
+    "x_linscan_blk2": "scan_pf_kernel<LinBlk2Op,8,12,1> (chunked scan, next tile prefetched)",
     "x_lstm_adjoint": "chunk_scan_kernel<LstmAdjOp> + reduce_u_kernel (whole step)",
     "x_lstm_step": "chunk_scan_kernel<LstmStepOp> (one launch per iteration up to the cap; "
                    "launches after convergence exit at once)",
@@ -85,53 +85,53 @@ DOMINANT = {
 # taken on: the sha256 prefix of those sources is checked at run time and the
 # figure is dropped (null) once any of them has changed.
 TRAFFIC = {
-    "c1_linscan": {"bytes": 551301358 + 289021984,
+    "c1_linscan": {"bytes": 551225435 + 289021984,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-        "sha256": "824e51b5f0f2217b"},
-    "c2_gru_fused": {"bytes": 418748032 + 152030544,
+        "sha256": "a155fe72a65b029c"},
+    "c2_gru_fused": {"bytes": 418677664 + 151870328,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
-        "sha256": "0f1e7fd137ff245b"},
-    "c3_lstm": {"bytes": 537167216 + 268440176,
+        "sha256": "21b6cb6480f857e0"},
+    "c3_lstm": {"bytes": 537166576 + 268441296,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "c536b3c6a4ff49b9"},
-    "c4_gru_long_fwd_adj": {"bytes": 544355312 + 269399100,
+        "sha256": "ead979d6acdf53f7"},
+    "c4_gru_long_fwd_adj": {"bytes": 544031216 + 269397744,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp",
                     "newton_chain.hip", "adjoint.hip"],
-        "sha256": "afba726cee5ca8b0"},
-    "x_linscan_blk2": {"bytes": 823221138 + 325722144,
+        "sha256": "c3c7e41078f2c83c"},
+    "x_linscan_blk2": {"bytes": 829594368 + 345952325,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-        "sha256": "824e51b5f0f2217b"},
-    "x_linscan_blk4": {"bytes": 695774939 + 159006752,
+        "sha256": "a155fe72a65b029c"},
+    "x_linscan_blk4": {"bytes": 695805074 + 159006752,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "blkrow.hip"],
-        "sha256": "94389dbd5e94023c"},
-    "x_linscan_blk8": {"bytes": 677625033 + 115343392,
+        "sha256": "4e182ba4bf45e422"},
+    "x_linscan_blk8": {"bytes": 678158135 + 115343392,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "blkrow.hip"],
-        "sha256": "94389dbd5e94023c"},
-    "x_lstm_adjoint": {"bytes": 1127667803 + 597172256,
+        "sha256": "4e182ba4bf45e422"},
+    "x_lstm_adjoint": {"bytes": 1127551689 + 597172256,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "adjoint.hip"],
-        "sha256": "7db2b305e6b9d39a"},
-    "x_gru_long_fwd": {"bytes": 204941440 + 67773052,
+        "sha256": "7621327f970f43b0"},
+    "x_gru_long_fwd": {"bytes": 204860880 + 67792476,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "c536b3c6a4ff49b9"},
-    "x_hgru8_bwd": {"bytes": 444640859 + 296485810,
+        "sha256": "ead979d6acdf53f7"},
+    "x_hgru8_bwd": {"bytes": 444827227 + 296485134,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp",
                     "newton_iter.hpp", "hgru.hip"],
-        "sha256": "5217201cf5ccf07c"},
-    "x_gru_seq": {"bytes": 402868535 + 134217728,
+        "sha256": "df370851e1601e32"},
+    "x_gru_seq": {"bytes": 402868864 + 134217728,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
-        "sha256": "7e85cffc4dbacda6"},
-    "x_lstm_seq": {"bytes": 537126802 + 268435456,
+        "sha256": "f3430fb8a98878ef"},
+    "x_lstm_seq": {"bytes": 537126857 + 268435456,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "rollout.hip"],
-        "sha256": "7e85cffc4dbacda6"},
+        "sha256": "f3430fb8a98878ef"},
     # per step: the launches of the iterations that ran (the launches after
     # convergence read and write almost nothing)
-    "x_hgru8_fwd": {"bytes": 1415838624 + 504171624,
+    "x_hgru8_fwd": {"bytes": 1415263968 + 504173012,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp",
                     "newton_iter.hpp", "hgru.hip"],
-        "sha256": "5217201cf5ccf07c"},
+        "sha256": "df370851e1601e32"},
 }
 DESCRIBE = {
     "c1_linscan": "linear diagonal recurrence h_t = a_t h_{t-1} + b_t, B=16 L=4096 H=1024, "

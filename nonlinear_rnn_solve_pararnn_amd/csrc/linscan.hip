@@ -94,161 +94,6 @@ struct LinDiagOp {
     }
 };
 
-// ---------------------------------------------------------------- diag scan, prefetching
-// The diagonal scan with channel lanes, as a persistent kernel that keeps the
-// next tile's inputs in flight while the current tile finishes.  A tile is
-// the scan_core.hpp channel-lane tile (NWC groups of 64 channels x NW/NWC
-// sub-chunks of C positions).  Each workgroup draws its next ticket while it
-// composes the current tile; after the first barrier every wave issues the
-// loads of the next tile into a second register set, so they overlap the
-// look-back, the second barrier, the carry-in and the stores of the current
-// one.  The holder waves issue theirs after their look-back: loads complete in
-// issue order, so look-back loads queued behind them would wait for them.
-// The two register sets alternate by unrolling the tile loop twice.  Every
-// wait is still on a smaller ticket (a workgroup finishes its tiles in ticket
-// order), and each workgroup draws exactly one ticket past the last tile.
-struct DiagTilePos {
-    int64_t q, b, j, pos0, base;
-    bool ok;
-};
-
-template <int NW, int C, int NWC>
-__device__ __forceinline__ DiagTilePos diag_tile_pos(const ScanGeo &g, int64_t ticket) {
-    constexpr int NWT = NW / NWC;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int cw = w % NWC, tw = w / NWC;
-    DiagTilePos p;
-    const int64_t per_q = g.B * g.ncb;
-    p.q = ticket / per_q;
-    const int64_t rest = ticket - p.q * per_q;
-    p.b = rest / g.ncb;
-    const int64_t cb = rest - p.b * g.ncb;
-    p.j = (cb * NWC + cw) * 64 + lane;
-    p.ok = p.j < g.H;
-    p.pos0 = p.q * ((int64_t)NWT * C) + (int64_t)tw * C;
-    p.base = idx3(p.b, p.pos0, p.ok ? p.j : 0, g.L, g.H);
-    return p;
-}
-
-template <int C>
-__device__ __forceinline__ void diag_tile_load(const LinDiagOp &op, const DiagTilePos &p, float (&ea)[C],
-                                               float (&eb)[C]) {
-    if (p.ok && p.pos0 + C <= op.L) {
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            ea[i] = ld_once(op.a + p.base + i * op.H);
-            eb[i] = ld_once(op.b + p.base + i * op.H);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            const bool v = p.ok && p.pos0 + i < op.L;
-            ea[i] = v ? ld_once(op.a + p.base + i * op.H) : 1.0f;
-            eb[i] = v ? ld_once(op.b + p.base + i * op.H) : 0.0f;
-        }
-    }
-}
-
-// One tile (inputs already in ea/eb); prefetches the next ticket's tile into
-// na/nb.  Returns whether there is a next tile.
-template <int NW, int C, int NWC>
-__device__ __forceinline__ bool diag_pf_tile(const LinDiagOp &op, const ScanGeo &g, uint32_t draws,
-                                             const DiagTilePos &p, uint32_t tag, float (&ea)[C],
-                                             float (&eb)[C], Ticket *s_next, Aff1 *s_part, float *s_carry,
-                                             DiagTilePos &pn, float (&na)[C], float (&nb)[C],
-                                             Ticket &tn) {
-    using M = MonoidT<1>;
-    using D = Desc<1>;
-    constexpr int NWT = NW / NWC;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int cw = w % NWC, tw = w / NWC;
-    const bool holder = tw == NWT - 1;
-    const int cslot = cw * 64 + lane;
-
-    Aff1 acc = M::id();
-#pragma unroll
-    for (int i = 0; i < C; ++i) acc = M::then(acc, Aff1{ea[i], eb[i]});
-    if (tid == 0) *s_next = draw_ticket(g.ws.hdr, draws);
-    s_part[w * 64 + lane] = acc;
-    lds_barrier();
-    tn = *s_next;
-    const bool more = tn.index < g.ntiles;
-    if (more) pn = diag_tile_pos<NW, C, NWC>(g, tn.index);
-    if (more && !holder) diag_tile_load<C>(op, pn, na, nb);
-
-    Aff1 ex = M::id();
-    for (int k = 0; k < tw; ++k) ex = M::then(ex, s_part[(k * NWC + cw) * 64 + lane]);
-    if (holder) {
-        const Aff1 tot = M::then(ex, acc);
-        const int64_t stride = g.B * g.H, slot = p.b * g.H + p.j;
-        const int64_t dsc = p.q * stride + slot;
-        float xin = 0.0f;
-        if (p.ok) {
-            if (p.q == 0) {
-                xin = op.h0 != nullptr ? op.h0[p.b * g.H + p.j] : 0.0f;
-            } else {
-                D::put_agg(g.agg + dsc * D::kAggWords, tot, tag);
-                xin = lane_lookback<1>(g, tag, p.q, stride, slot);
-            }
-            D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin), tag);
-        }
-        s_carry[cslot] = xin;
-        if (more) diag_tile_load<C>(op, pn, na, nb);
-    }
-    lds_barrier();
-
-    float x = M::apply(ex, s_carry[cslot]);
-    if (p.ok && p.pos0 + C <= op.L) {
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            x = fmaf(ea[i], x, eb[i]);
-            op.h[p.base + i * op.H] = x;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            x = fmaf(ea[i], x, eb[i]);
-            if (p.ok && p.pos0 + i < op.L) op.h[p.base + i * op.H] = x;
-        }
-    }
-    return more;
-}
-
-template <int NW, int C, int NWC>
-__global__ __launch_bounds__(NW * 64) void diag_pf_kernel(LinDiagOp op, ScanGeo g) {
-    static_assert(NW % NWC == 0, "channel groups tile the waves");
-    __shared__ Aff1 s_part[NW * 64];
-    __shared__ float s_carry[64 * NWC];
-    __shared__ Ticket s_tk[2];
-    const uint32_t draws = (uint32_t)(g.ntiles + gridDim.x);  // one draw past the end per workgroup
-    if (threadIdx.x == 0) s_tk[0] = draw_ticket(g.ws.hdr, draws);
-    __syncthreads();
-    Ticket tx = s_tk[0], ty;
-    if (tx.index >= g.ntiles) {
-        finish_launch(tx, g.ws);
-        return;
-    }
-    DiagTilePos px = diag_tile_pos<NW, C, NWC>(g, tx.index), py;
-    float xa[C], xb[C], ya[C], yb[C];
-    diag_tile_load<C>(op, px, xa, xb);
-    for (;;) {
-        if (!diag_pf_tile<NW, C, NWC>(op, g, draws, px, tx.tag, xa, xb, &s_tk[1], s_part, s_carry, py, ya, yb, ty))
-            break;
-        if (!diag_pf_tile<NW, C, NWC>(op, g, draws, py, ty.tag, ya, yb, &s_tk[0], s_part, s_carry, px, xa, xb, tx))
-            break;
-    }
-    finish_launch(tx, g.ws);  // every draw of a launch carries the same epoch
-}
-
-template <int NW, int C, int NWC>
-static hipError_t launch_diag_pf(const LinDiagOp &op, const ScanGeo &g, hipStream_t s) {
-    static const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(diag_pf_kernel<NW, C, NWC>), NW * 64);
-    const int64_t slots = (int64_t)per_cu * device_cu_count();
-    const int64_t grid = g.ntiles < slots ? g.ntiles : slots;
-    hipLaunchKernelGGL((diag_pf_kernel<NW, C, NWC>), dim3((unsigned)grid), dim3(NW * 64), 0, s, op, g);
-    return hipGetLastError();
-}
-
 // ---------------------------------------------------------------- 2x2 scan
 // h_t = A_t h_{t-1} + b_t with A_t a 2x2 block per (batch, channel).  VEC:
 // A 16-byte aligned, b, h and h0 8-byte aligned, so a block moves as one
@@ -332,6 +177,199 @@ struct LinBlk2Op {
         }
     }
 };
+
+// ---------------------------------------------------------------- scans, prefetching
+// The diagonal and 2x2 scans with channel lanes, as a persistent kernel that
+// keeps the next tile's inputs in flight while the current tile finishes.  A
+// tile is the scan_core.hpp channel-lane tile (NWC groups of 64 channels x
+// NW/NWC sub-chunks of C positions).  Each workgroup draws its next ticket
+// while it composes the current tile; after the first barrier every wave
+// issues the loads of the next tile into a second register set, so they
+// overlap the look-back, the second barrier, the carry-in and the stores of
+// the current one.  The holder waves issue theirs after their look-back:
+// loads complete in issue order, so look-back loads queued behind them would
+// wait for them.  The two register sets alternate by unrolling the tile loop
+// twice.  Every wait is still on a smaller ticket (a workgroup finishes its
+// tiles in ticket order), and each workgroup draws exactly one ticket past the
+// last tile.
+struct PfTilePos {
+    int64_t q, b, j, pos0, base;
+    bool ok;
+};
+
+template <int NW, int C, int NWC>
+__device__ __forceinline__ PfTilePos pf_tile_pos(const ScanGeo &g, int64_t ticket) {
+    constexpr int NWT = NW / NWC;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int cw = w % NWC, tw = w / NWC;
+    PfTilePos p;
+    const int64_t per_q = g.B * g.ncb;
+    p.q = ticket / per_q;
+    const int64_t rest = ticket - p.q * per_q;
+    p.b = rest / g.ncb;
+    const int64_t cb = rest - p.b * g.ncb;
+    p.j = (cb * NWC + cw) * 64 + lane;
+    p.ok = p.j < g.H;
+    p.pos0 = p.q * ((int64_t)NWT * C) + (int64_t)tw * C;
+    p.base = idx3(p.b, p.pos0, p.ok ? p.j : 0, g.L, g.H);
+    return p;
+}
+
+// The op-specific pieces: a tile's maps (the identity outside the sequence),
+// the state before the first chunk, and the stores.
+template <int C>
+__device__ __forceinline__ void pf_load(const LinDiagOp &op, const PfTilePos &p, Aff1 (&m)[C]) {
+    if (p.ok && p.pos0 + C <= op.L) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            m[i].a = ld_once(op.a + p.base + i * op.H);
+            m[i].b = ld_once(op.b + p.base + i * op.H);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const bool v = p.ok && p.pos0 + i < op.L;
+            m[i].a = v ? ld_once(op.a + p.base + i * op.H) : 1.0f;
+            m[i].b = v ? ld_once(op.b + p.base + i * op.H) : 0.0f;
+        }
+    }
+}
+__device__ __forceinline__ float pf_init(const LinDiagOp &op, const PfTilePos &p) {
+    return op.h0 != nullptr ? op.h0[p.b * op.H + p.j] : 0.0f;
+}
+__device__ __forceinline__ void pf_store(const LinDiagOp &op, int64_t e, float x) { op.h[e] = x; }
+
+template <int C, bool VEC>
+__device__ __forceinline__ void pf_load(const LinBlk2Op<VEC> &op, const PfTilePos &p, Aff2 (&m)[C]) {
+    if (p.ok && p.pos0 + C <= op.L) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) op.load_elem(p.base + i * op.H, m[i]);
+    } else {
+        // every load issued, none behind a branch (a position outside reads
+        // element 0 and takes the identity by selects)
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const bool v = p.ok && p.pos0 + i < op.L;
+            op.load_elem(v ? p.base + i * op.H : 0, m[i]);
+            const Aff2 id = MonoidT<2>::id();
+            m[i] = {v ? m[i].a00 : id.a00, v ? m[i].a01 : id.a01, v ? m[i].a10 : id.a10,
+                    v ? m[i].a11 : id.a11, v ? m[i].b0 : id.b0,   v ? m[i].b1 : id.b1};
+        }
+    }
+}
+template <bool VEC>
+__device__ __forceinline__ float2s pf_init(const LinBlk2Op<VEC> &op, const PfTilePos &p) {
+    TilePos tp{};
+    tp.b = p.b;
+    tp.j = p.j;
+    tp.ok = true;
+    return op.init_state(tp);
+}
+template <bool VEC>
+__device__ __forceinline__ void pf_store(const LinBlk2Op<VEC> &op, int64_t e, float2s x) {
+    op.store_state(e, x);
+}
+
+// One tile (inputs already in m); prefetches the next ticket's tile into nm.
+// Returns whether there is a next tile.
+template <class Op, int NW, int C, int NWC>
+__device__ __forceinline__ bool pf_tile(const Op &op, const ScanGeo &g, uint32_t draws, const PfTilePos &p,
+                                        uint32_t tag, typename MonoidT<Op::S>::Map (&m)[C], Ticket *s_next,
+                                        typename MonoidT<Op::S>::Map *s_part,
+                                        typename MonoidT<Op::S>::State *s_carry, PfTilePos &pn,
+                                        typename MonoidT<Op::S>::Map (&nm)[C], Ticket &tn) {
+    using M = MonoidT<Op::S>;
+    using D = Desc<Op::S>;
+    using Map = typename M::Map;
+    using State = typename M::State;
+    constexpr int NWT = NW / NWC;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int cw = w % NWC, tw = w / NWC;
+    const bool holder = tw == NWT - 1;
+    const int cslot = cw * 64 + lane;
+
+    Map acc = M::id();
+#pragma unroll
+    for (int i = 0; i < C; ++i) acc = M::then(acc, m[i]);
+    if (tid == 0) *s_next = draw_ticket(g.ws.hdr, draws);
+    s_part[w * 64 + lane] = acc;
+    lds_barrier();
+    tn = *s_next;
+    const bool more = tn.index < g.ntiles;
+    if (more) pn = pf_tile_pos<NW, C, NWC>(g, tn.index);
+    if (more && !holder) pf_load<C>(op, pn, nm);
+
+    Map ex = M::id();
+    for (int k = 0; k < tw; ++k) ex = M::then(ex, s_part[(k * NWC + cw) * 64 + lane]);
+    if (holder) {
+        const Map tot = M::then(ex, acc);
+        const int64_t stride = g.B * g.H, slot = p.b * g.H + p.j;
+        const int64_t dsc = p.q * stride + slot;
+        State xin = M::zero();
+        if (p.ok) {
+            if (p.q == 0) {
+                xin = pf_init(op, p);
+            } else {
+                D::put_agg(g.agg + dsc * D::kAggWords, tot, tag);
+                xin = lane_lookback<Op::S>(g, tag, p.q, stride, slot);
+            }
+            D::put_inc(g.inc + dsc * D::kIncWords, M::apply(tot, xin), tag);
+        }
+        s_carry[cslot] = xin;
+        if (more) pf_load<C>(op, pn, nm);
+    }
+    lds_barrier();
+
+    State x = M::apply(ex, s_carry[cslot]);
+    if (p.ok && p.pos0 + C <= op.L) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            x = M::apply(m[i], x);
+            pf_store(op, p.base + i * op.H, x);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            x = M::apply(m[i], x);
+            if (p.ok && p.pos0 + i < op.L) pf_store(op, p.base + i * op.H, x);
+        }
+    }
+    return more;
+}
+
+template <class Op, int NW, int C, int NWC>
+__global__ __launch_bounds__(NW * 64) void scan_pf_kernel(Op op, ScanGeo g) {
+    static_assert(NW % NWC == 0, "channel groups tile the waves");
+    using M = MonoidT<Op::S>;
+    __shared__ typename M::Map s_part[NW * 64];
+    __shared__ typename M::State s_carry[64 * NWC];
+    __shared__ Ticket s_tk[2];
+    const uint32_t draws = (uint32_t)(g.ntiles + gridDim.x);  // one draw past the end per workgroup
+    if (threadIdx.x == 0) s_tk[0] = draw_ticket(g.ws.hdr, draws);
+    __syncthreads();
+    Ticket tx = s_tk[0], ty;
+    if (tx.index >= g.ntiles) {
+        finish_launch(tx, g.ws);
+        return;
+    }
+    PfTilePos px = pf_tile_pos<NW, C, NWC>(g, tx.index), py;
+    typename M::Map xm[C], ym[C];
+    pf_load<C>(op, px, xm);
+    for (;;) {
+        if (!pf_tile<Op, NW, C, NWC>(op, g, draws, px, tx.tag, xm, &s_tk[1], s_part, s_carry, py, ym, ty)) break;
+        if (!pf_tile<Op, NW, C, NWC>(op, g, draws, py, ty.tag, ym, &s_tk[0], s_part, s_carry, px, xm, tx)) break;
+    }
+    finish_launch(tx, g.ws);  // every draw of a launch carries the same epoch
+}
+
+template <class Op, int NW, int C, int NWC>
+static hipError_t launch_scan_pf(const Op &op, const ScanGeo &g, hipStream_t s) {
+    static const int per_cu = blocks_per_cu(reinterpret_cast<const void *>(scan_pf_kernel<Op, NW, C, NWC>), NW * 64);
+    const int64_t slots = (int64_t)per_cu * device_cu_count();
+    const int64_t grid = g.ntiles < slots ? g.ntiles : slots;
+    hipLaunchKernelGGL((scan_pf_kernel<Op, NW, C, NWC>), dim3((unsigned)grid), dim3(NW * 64), 0, s, op, g);
+    return hipGetLastError();
+}
 
 // ---------------------------------------------------------------- k x k scan
 // h_t = A_t h_{t-1} + b_t with A_t a dense k x k block per (batch, channel):
@@ -484,25 +522,30 @@ static hipError_t run_scan(const TileCfg &cfg, const Op &op, int64_t B, int64_t 
                               : launch_chunk_scan<Op, NWT, CT, false>(op, g, s);
 }
 
+// The prefetching form (channel lanes only) on the same workspace layout.
+template <class Op, int NW, int C, int NWC>
+static hipError_t run_scan_pf(const TileCfg &cfg, const Op &op, int64_t B, int64_t L, int64_t H, const Ws &ws,
+                              hipStream_t s) {
+    const ScanWs w = scan_ws(cfg, Op::S, B, L, H);
+    ScanGeo g;
+    g.B = B;
+    g.L = L;
+    g.H = H;
+    g.ncb = w.sh.ncb;
+    g.nq = w.sh.nq;
+    g.ntiles = w.sh.ntiles;
+    g.ws = ws_span(ws);
+    g.agg = reinterpret_cast<uint64_t *>(ws.p + w.agg);
+    g.inc = reinterpret_cast<uint64_t *>(ws.p + w.inc);
+    return launch_scan_pf<Op, NW, C, NWC>(op, g, s);
+}
+
 
 hipError_t linscan_diag(int64_t B, int64_t L, int64_t H, const float *a, const float *b,
                         const float *h0, float *h, const Ws &ws, hipStream_t s) {
     LinDiagOp op{a, b, h0, h, L, H};
     constexpr TileCfg c = kCfgLinDiag;
-    if (kDiagPrefetch && H >= kChannelLanesMinH) {
-        const ScanWs w = scan_ws(c, 1, B, L, H);
-        ScanGeo g;
-        g.B = B;
-        g.L = L;
-        g.H = H;
-        g.ncb = w.sh.ncb;
-        g.nq = w.sh.nq;
-        g.ntiles = w.sh.ntiles;
-        g.ws = ws_span(ws);
-        g.agg = reinterpret_cast<uint64_t *>(ws.p + w.agg);
-        g.inc = reinterpret_cast<uint64_t *>(ws.p + w.inc);
-        return launch_diag_pf<c.nw_cl, c.c_cl, c.ncw_cl>(op, g, s);
-    }
+    if (kDiagPrefetch && H >= kChannelLanesMinH) return run_scan_pf<LinDiagOp, c.nw_cl, c.c_cl, c.ncw_cl>(c, op, B, L, H, ws, s);
     return run_scan<LinDiagOp, 1, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
 }
 
@@ -510,11 +553,14 @@ hipError_t linscan_blk2(int64_t B, int64_t L, int64_t H, const float *A, const f
                         const float *h0, float *h, const Ws &ws, hipStream_t s) {
     constexpr TileCfg c = kCfgLinBlk2;
     const bool vec = aligned16(A) && aligned_to(b, 8) && aligned_to(h, 8) && (h0 == nullptr || aligned_to(h0, 8));
+    const bool pf = kBlk2Prefetch && H >= kChannelLanesMinH;
     if (vec) {
         LinBlk2Op<true> op{A, b, h0, h, L, H};
+        if (pf) return run_scan_pf<LinBlk2Op<true>, c.nw_cl, c.c_cl, c.ncw_cl>(c, op, B, L, H, ws, s);
         return run_scan<LinBlk2Op<true>, 2, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
     }
     LinBlk2Op<false> op{A, b, h0, h, L, H};
+    if (pf) return run_scan_pf<LinBlk2Op<false>, c.nw_cl, c.c_cl, c.ncw_cl>(c, op, B, L, H, ws, s);
     return run_scan<LinBlk2Op<false>, 2, c.nw_cl, c.c_cl, c.nw_tl, c.c_tl, c.ncw_cl>(c, op, B, L, H, ws, s);
 }
 

@@ -19,7 +19,9 @@ struct TileCfg {
 constexpr TileCfg kCfgLinDiag{16, 16, 4, 16, 2};
 // The diagonal scan with channel lanes prefetches the next tile (linscan.hip).
 constexpr bool kDiagPrefetch = true;
-constexpr TileCfg kCfgLinBlk2{16, 8, 4, 8, 1};
+constexpr TileCfg kCfgLinBlk2{8, 12, 4, 8, 1};
+// The 2x2 scan with channel lanes prefetches the next tile too.
+constexpr bool kBlk2Prefetch = true;
 // 4x4 blocks (the maps hold 20 floats per position)
 constexpr TileCfg kCfgLinBlk4{8, 4, 4, 2, 1};
 constexpr TileCfg kCfgGruStep{4, 16, 8, 16};
