@@ -87,7 +87,7 @@ DOMINANT = {
 TRAFFIC = {
     "c1_linscan": {"bytes": 551225435 + 289021984,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-        "sha256": "a155fe72a65b029c"},
+        "sha256": "3eb66f7d7ef182f5"},
     "c2_gru_fused": {"bytes": 418677664 + 151870328,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "gru_fused.hip"],
         "sha256": "21b6cb6480f857e0"},
@@ -101,7 +101,7 @@ TRAFFIC = {
         "sha256": "c3c7e41078f2c83c"},
     "x_linscan_blk2": {"bytes": 829594368 + 345952325,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
-        "sha256": "a155fe72a65b029c"},
+        "sha256": "3eb66f7d7ef182f5"},
     "x_linscan_blk4": {"bytes": 695805074 + 159006752,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp", "blkrow.hip"],
         "sha256": "4e182ba4bf45e422"},

@@ -110,9 +110,10 @@ struct LinBlk2Op {
         Aff2 m;
     };
     __device__ bool active() const { return true; }
-    __device__ float2s init_state(const TilePos &tp) const {
-        if (h0 != nullptr && tp.ok) {
-            const int64_t e = tp.b * H + tp.j;
+    // the state before the first chunk of (batch row b, channel j)
+    __device__ float2s init_at(int64_t b, int64_t j) const {
+        if (h0 != nullptr) {
+            const int64_t e = b * H + j;
             if (VEC) {
                 const float2 v = reinterpret_cast<const float2 *>(h0)[e];
                 return {v.x, v.y};
@@ -120,6 +121,9 @@ struct LinBlk2Op {
             return {h0[2 * e], h0[2 * e + 1]};
         }
         return {0.0f, 0.0f};
+    }
+    __device__ float2s init_state(const TilePos &tp) const {
+        return tp.ok ? init_at(tp.b, tp.j) : float2s{0.0f, 0.0f};
     }
     __device__ void load_elem(int64_t e, Aff2 &m) const {
         if (VEC) {
@@ -259,11 +263,7 @@ __device__ __forceinline__ void pf_load(const LinBlk2Op<VEC> &op, const PfTilePo
 }
 template <bool VEC>
 __device__ __forceinline__ float2s pf_init(const LinBlk2Op<VEC> &op, const PfTilePos &p) {
-    TilePos tp{};
-    tp.b = p.b;
-    tp.j = p.j;
-    tp.ok = true;
-    return op.init_state(tp);
+    return op.init_at(p.b, p.j);
 }
 template <bool VEC>
 __device__ __forceinline__ void pf_store(const LinBlk2Op<VEC> &op, int64_t e, float2s x) {
