@@ -48,6 +48,30 @@ def test_shapes_match_rollout(orc, B, L, H):
     assert max_abs(h, hr) <= FWD_ATOL and max_abs(c, cr) <= FWD_ATOL
 
 
+def test_non_convergence_and_nan_reported():
+    d = synth.lstm_inputs(2, 200, 40, seed=75, h0=True)
+    _, _, info = _run(d, 0.0, 1)
+    assert list(info) == [1, 0]
+    d["pi"][1, 50, 3] = float("nan")
+    _, _, info = _run(d, 1e-4, 6)
+    assert list(info) == [6, 0]
+
+
+# Positions past the end of the sequence (ragged last chunks) and channels past
+# H (ragged channel blocks) must not change when Newton stops: the count is
+# that of Newton over the whole sequence (R4), within one of the oracle's
+# where the last update is within rounding of tol (R5).
+@pytest.mark.parametrize("B,L,H", [(2, 700, 33), (3, 257, 70), (2, 3001, 1)])
+def test_ragged_stop_matches_oracle_count(orc, B, L, H):
+    d = synth.lstm_inputs(B, L, H, seed=76 + H, h0=True)
+    h, c, info = _run(d, 1e-4, 32)
+    hr, cr, it, conv, _ = orc.lstm_newton(*lstm_args(d), h0=d["h0"], c0=d["c0"], tol=1e-4, cap=32)
+    say("lstm ragged", B, L, H, "gpu", list(info), "oracle", it, conv)
+    assert info[1] == 1 and conv == 1
+    assert abs(int(info[0]) - int(it)) <= 1
+    assert max_abs(h, hr) <= FWD_ATOL and max_abs(c, cr) <= FWD_ATOL
+
+
 def test_u0_converges_in_three_updates(orc):
     d = synth.lstm_inputs(2, 500, 40, seed=72, zero_u=True)
     h, c, info = _run(d, 1e-6, 10, with_init=False)
