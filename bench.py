@@ -485,6 +485,47 @@ def alu_calibration(dev):
     return res
 
 
+def compose_probe(dev):
+    """Dense 8x8 map compositions per second, vector lane groups (the block
+    scans' row_then) against the matrix cores (v_mfma_f32_16x16x4_f32 on
+    block-diagonal pairs of maps, an upper bound: no operand permutes, no b
+    part), alu_probe.hip, HIP events on the launch stream."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "nonlinear_rnn_solve_pararnn_amd", "libpararnn_probe.so"))
+    for f in (lib.alu_probe_lg8_compose, lib.alu_probe_mfma):
+        f.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+        f.restype = ctypes.c_int
+    tpb = lib.alu_probe_threads_per_block()
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks = ncu * 8  # eight workgroups of 4 waves per CU: 8 waves per SIMD
+    out = torch.empty(blocks * tpb, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, iters):
+        for _ in range(2):
+            assert fn(blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream)) == 0
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        assert fn(blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(stream.cuda_stream)) == 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3
+
+    it_v, it_m = 512, 2048
+    tv = timed(lib.alu_probe_lg8_compose, it_v)
+    vec = blocks * (tpb // 8) * it_v * lib.alu_probe_lg8_compose_per_group_iter() / tv
+    tm = timed(lib.alu_probe_mfma, it_m)
+    instr = blocks * (tpb // 64) * it_m * lib.alu_probe_mfma_per_wave_iter() / tm
+    return {"vector_compositions_per_s": vec, "vector_ms": tv * 1e3,
+            "mfma_instructions_per_s": instr, "mfma_tflops": instr * 2048 / 1e12, "mfma_ms": tm * 1e3,
+            "mfma_compositions_per_s_bound": instr / 2, "vector_over_mfma_bound": vec / (instr / 2),
+            "what": "8x8 affine maps; vector: lane groups of 8 with DPP multiply-adds, 4 chains per group; "
+                    "mfma: 16x16x4 fp32, 4 instructions per 16x16x16 product = 2 compositions of A only; "
+                    "%d workgroups of %d threads" % (blocks, tpb)}
+
+
 def issue_probe(dev):
     """How a SIMD shares its issue between waves (alu_probe.hip): the
     multiply-add chains at 1, 2, 4 and 8 waves per SIMD (1, 2, 4, 8
@@ -814,6 +855,8 @@ def main():
                     help="leave out the modality sweep and residual traces")
     ap.add_argument("--modalities", action="store_true",
                     help="only the modality sweep and residual traces (one JSON line)")
+    ap.add_argument("--compose-probe", action="store_true",
+                    help="print 8x8 map compositions per second, vector lane groups against the matrix cores")
     ap.add_argument("--issue-probe", action="store_true",
                     help="print the issue-sharing probe table (alu_probe.hip) and exit")
     ap.add_argument("--alu-calibration", action="store_true",
@@ -836,6 +879,9 @@ def main():
         print(json.dumps(modalities(dev)), flush=True)
         return
 
+    if args.compose_probe:
+        print(json.dumps(compose_probe(dev)))
+        return
     if args.issue_probe:
         for row in issue_probe(dev):
             print(json.dumps(row), flush=True)

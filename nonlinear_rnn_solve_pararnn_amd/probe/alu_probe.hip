@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../csrc/lanegroup.hpp"
+
 namespace {
 
 constexpr int kThreads = 256;
@@ -79,6 +81,68 @@ __global__ __launch_bounds__(kThreads) void mix_probe_kernel(int iters, float *o
     out[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
 }
 
+// ---------------------------------------------------------------- 8x8 maps
+// The block scans compose dense 8x8 affine maps (A, b), one per position.
+// Vector form, as the scans do it (lanegroup.hpp): lane c of a group of 8
+// lanes holds row c of a map in xor order and a composition is row_then,
+// multiply-adds with DPP operands.  Four independent chains per lane group;
+// the fixed map contracts, so the values stay small.
+constexpr int kComposeChains = 4, kComposeUnroll = 4;
+__global__ __launch_bounds__(kThreads) void lg8_compose_probe_kernel(int iters, float *out) {
+    using prn::lg::RowK;
+    RowK<8> m;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) m.a[p] = p == 0 ? 0.5f : 1e-3f * (float)((threadIdx.x + p) & 7);
+    m.b = 1e-3f;
+    RowK<8> acc[kComposeChains];
+#pragma unroll
+    for (int k = 0; k < kComposeChains; ++k) {
+        acc[k] = m;
+        acc[k].b = 1e-3f * (float)(k + 1);
+    }
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int u = 0; u < kComposeUnroll; ++u) {
+#pragma unroll
+            for (int k = 0; k < kComposeChains; ++k) acc[k] = prn::lg::row_then<8>(acc[k], m);
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kComposeChains; ++k) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) s += acc[k].a[p];
+        s += acc[k].b;
+    }
+    out[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
+// Matrix-core bound for the same work: v_mfma_f32_16x16x4_f32 (a 16x4 by
+// 4x16 fp32 product per wave).  Two 8x8 maps packed block-diagonally into a
+// 16x16 matrix compose with another such pair in one 16x16x16 product, four
+// of these instructions.  Eight independent accumulators per wave, operands
+// held in registers: the lane permutes a chain of products would need between
+// steps (the product's layout is not the next operand's) are left out, and
+// so is the b part of the maps, so this bounds the matrix cores from above.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(kThreads) void mfma_probe_kernel(int iters, float *out) {
+    const float a = 1e-3f * (float)(threadIdx.x & 63), b = 1e-3f;
+    f32x4 acc[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[k], 0, 0, 0);
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += acc[k].x + acc[k].y + acc[k].z + acc[k].w;
+    out[(size_t)blockIdx.x * kThreads + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,6 +180,25 @@ int alu_probe_mix(int64_t blocks, int32_t iters, int32_t m, float *out, void *st
         case 32: hipLaunchKernelGGL(mix_probe_kernel<32>, g, b, 0, s, iters, out); break;
         default: return -1;
     }
+    return (int)hipGetLastError();
+}
+
+// 8x8 compositions per thread and iteration of the vector probe (each lane
+// group of 8 threads composes kComposeChains maps kComposeUnroll times per
+// iteration: per lane group, 8 times this); MFMA instructions per wave and
+// iteration of the matrix-core probe (2048 flops each).
+int alu_probe_lg8_compose_per_group_iter(void) { return kComposeChains * kComposeUnroll; }
+int alu_probe_mfma_per_wave_iter(void) { return kUnroll * 8; }
+
+int alu_probe_lg8_compose(int64_t blocks, int32_t iters, float *out, void *stream) {
+    hipLaunchKernelGGL(lg8_compose_probe_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), iters, out);
+    return (int)hipGetLastError();
+}
+
+int alu_probe_mfma(int64_t blocks, int32_t iters, float *out, void *stream) {
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), iters, out);
     return (int)hipGetLastError();
 }
 
