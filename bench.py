@@ -94,11 +94,11 @@ TRAFFIC = {
     "c3_lstm": {"bytes": 537166576 + 268441296,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "ead979d6acdf53f7"},
+        "sha256": "284394b7d1def984"},
     "c4_gru_long_fwd_adj": {"bytes": 544031216 + 269397744,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp",
                     "newton_chain.hip", "adjoint.hip"],
-        "sha256": "c3c7e41078f2c83c"},
+        "sha256": "79354152ed395f4d"},
     "x_linscan_blk2": {"bytes": 829594368 + 345952325,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "scan_core.hpp", "linscan.hip"],
         "sha256": "3eb66f7d7ef182f5"},
@@ -115,7 +115,7 @@ TRAFFIC = {
     "x_gru_long_fwd": {"bytes": 204860880 + 67792476,
         "sources": ["common.hpp", "tags.hpp", "cells.hpp", "plan.hpp", "launch.hpp",
                     "scan_core.hpp", "newton_chain.hip"],
-        "sha256": "ead979d6acdf53f7"},
+        "sha256": "284394b7d1def984"},
     "x_hgru8_bwd": {"bytes": 444827227 + 296485134,
         "sources": ["common.hpp", "tags.hpp", "plan.hpp", "launch.hpp", "lanegroup.hpp",
                     "newton_iter.hpp", "hgru.hip"],

@@ -639,15 +639,15 @@ __device__ __forceinline__ void chain_tile(const Cell &cell, const ChainGeo &g, 
         if (sub == 0) hb = state_add(hb, cin);  // the previous chunk's last state at iterate k
         State dlt = LOCAL ? din_sub : M::apply(ex, cin);
         uint32_t mx = 0;
-        // With time lanes, a thread whose positions all lie inside the
-        // sequence (every thread but those of a chain's last chunk) takes
-        // max|delta| with no per-position mask: the masks are lane masks in
-        // scalar registers, which that kernel keeps spilled, so each masked
-        // position would cost two reloads.  (With channel lanes the split
-        // measured slower.)
-        // With time lanes the per-position tests are taken here from nv,
-        // which the empty asm makes opaque, so that their lane masks are not
-        // hoisted out of the loop and kept live in scalar registers across it.
+        // max|delta| over the positions inside the sequence.  The LSTM needs
+        // no mask (a position outside has a zero map, so a zero delta).  For
+        // the GRU with time lanes, a thread whose positions all lie inside
+        // (every thread but those of a chain's last chunk) takes no mask
+        // either: the masks are lane masks in scalar registers, which that
+        // kernel keeps spilled, so each masked position would cost two
+        // reloads; the others test i < nv, which the empty asm makes opaque
+        // so that the masks are not hoisted out of the loop and kept live
+        // across it.  With channel lanes the split measured slower.
         if constexpr (!CL) asm volatile("" : "+v"(nv));
         const auto apply_all = [&](auto masked) {
 #pragma unroll
