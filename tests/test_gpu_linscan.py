@@ -13,6 +13,7 @@ pytestmark = pytest.mark.gpu
 DIAG_SHAPES = [
     (1, 1, 1), (2, 100, 3), (3, 257, 70), (2, 5000, 1), (1, 70000, 2),
     (4, 1000, 64), (2, 3001, 33), (1, 64, 4), (3, 130, 200), (2, 300, 31), (2, 300, 32),
+    (8, 3001, 300),  # more tiles than workgroup slots, ragged in L and in the channel block
 ]
 
 
@@ -82,7 +83,10 @@ def test_linscan_diag_repeatable_within_tolerance(orc):
         assert max_abs(host(api.linscan_diag(a, b)), h1) <= 1e-5
 
 
-BLK2_SHAPES = [(1, 1, 1), (2, 100, 3), (2, 3000, 1), (3, 257, 70), (2, 700, 33), (1, 9000, 40)]
+# (8, 3001, 300): more tiles than workgroup slots, so the prefetching kernel
+# runs several tiles per workgroup, alternating its two register sets, with a
+# ragged last chunk and a ragged channel block
+BLK2_SHAPES = [(1, 1, 1), (2, 100, 3), (2, 3000, 1), (3, 257, 70), (2, 700, 33), (1, 9000, 40), (8, 3001, 300)]
 
 
 @pytest.mark.parametrize("B,L,H", BLK2_SHAPES)
