@@ -181,6 +181,24 @@ __device__ __forceinline__ void xor_terms_sum(float v, const float (&mul)[K], fl
     }
 }
 
+// o[p ^ Q] = mul[p] * (v of lane (lane ^ p)): the first exchange of a sum,
+// which sets the terms instead of adding to zeroed ones.  Written with the
+// DPP move builtins, which the compiler folds into the multiplies.
+template <int K, int Q>
+__device__ __forceinline__ void xor_terms_set(float v, const float (&mul)[K], float (&o)[K]) {
+    o[Q] = mul[0] * v;
+    o[Q ^ 1] = mul[1] * dpp_f<kQpXor1>(v);
+    o[Q ^ 2] = mul[2] * dpp_f<kQpXor2>(v);
+    o[Q ^ 3] = mul[3] * dpp_f<kQpXor3>(v);
+    if constexpr (K == 8) {
+        const float m = dpp_f<kHalfRowMirror>(v);  // lane ^ 7
+        o[Q ^ 7] = mul[7] * m;
+        o[Q ^ 6] = mul[6] * dpp_f<kQpXor1>(m);
+        o[Q ^ 5] = mul[5] * dpp_f<kQpXor2>(m);
+        o[Q ^ 4] = mul[4] * dpp_f<kQpXor3>(m);
+    }
+}
+
 template <int K, int Q = 0>
 __device__ __forceinline__ void then_cols(const RowK<K> &m1, const RowK<K> &m2, RowK<K> &r) {
     if constexpr (Q < K) {
@@ -193,9 +211,8 @@ __device__ __forceinline__ void then_cols(const RowK<K> &m1, const RowK<K> &m2, 
 template <int K>
 __device__ __forceinline__ RowK<K> row_then(const RowK<K> &m1, const RowK<K> &m2) {
     RowK<K> r;
-#pragma unroll
-    for (int p = 0; p < K; ++p) r.a[p] = 0.0f;
-    then_cols<K>(m1, m2, r);
+    xor_terms_set<K, 0>(m1.a[0], m2.a, r.a);
+    then_cols<K, 1>(m1, m2, r);
     r.b = m2.b;
     xor_terms_sum<K>(m1.b, m2.a, r.b);
     return r;
