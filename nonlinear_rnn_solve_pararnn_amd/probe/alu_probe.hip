@@ -3,9 +3,11 @@
 // (exp2, reciprocal) that the Newton kernels are built from, measured on the
 // device with the same compiler flags (packed fp32 disabled), so the
 // arithmetic rooflines can be given against a measured basis beside the
-// published fp32 vector peak.  Each thread runs 8 independent chains held in
-// registers; nothing is read from memory and one float per thread is written
-// so the chains are kept.
+// published fp32 vector peak; and the rate of dense 8x8 map compositions in
+// the block scans' vector form against the matrix cores' bound for the same
+// work.  Each thread runs independent chains held in registers; nothing is
+// read from memory and one float per thread is written so the chains are
+// kept.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
